@@ -1,0 +1,190 @@
+#!/usr/bin/env python3
+"""Benchmark of the routed-expert MoE layer on one MI355X.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload N]
+
+One step is one pass of the whole layer (router, dispatch, expert gate/up +
+activation, expert down, shared experts, combine) over one batch of tokens,
+with weights and tokens already resident in HBM.  Default workload: the
+Kimi-K3-shaped layer at decode T=1 (E=896 routed experts in MXFP4, top-16,
+2 bf16 shared experts, d=3584, F=3072).  Steps cycle through a pool of 32
+distinct token batches so consecutive steps pick different experts (no
+cache reuse of one fixed selection).
+
+Prints one JSON line: throughput (tok/s), the roofline of the dominant kernel
+(algorithmic bytes / its average duration, timed live with the HIP events of
+moe_layer_timed on the launch stream), and the CPU oracle timed on a bounded
+sample of the same workload on this host.
+"""
+import argparse
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+import numpy as np  # noqa: E402
+
+PEAK_HBM_GBS = 8000.0      # MI355X HBM3E, GB/s
+PEAK_BF16_TFLOPS = 2500.0  # MI355X dense bf16 MFMA, TFLOP/s
+METRIC = "MoE layer decode tok/s + HBM GB/s vs peak; prefill TFLOP/s vs MFMA peak"
+PHASES = ("router_logits", "topk_dispatch", "expert_gate_up", "expert_down", "combine")
+KERNELS = {"router_logits": "k_router_logits", "topk_dispatch": "k_dispatch_small/k_topk+k_dispatch_*",
+           "expert_gate_up": "k_gemv_gateup", "expert_down": "k_gemv_down", "combine": "k_combine"}
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def phase_bytes(shape, T, counts):
+    """Algorithmic HBM bytes of each phase for one step (every touched expert
+    read once; shared, router, tokens and outputs once; workspace excluded)."""
+    d, F, S, E, k = shape.d_model, shape.d_ffn, shape.n_shared, shape.n_experts, shape.top_k
+    active = int((counts > 0).sum())
+    w13 = 2 * (F * d // 2 + F * d // 32)
+    w2 = d * F // 2 + d * F // 32
+    return {
+        "router_logits": E * d * 4 + T * d * 2,
+        "topk_dispatch": 0,
+        "expert_gate_up": active * w13 + S * 2 * F * d * 2 + T * d * 2,
+        "expert_down": active * w2 + S * d * F * 2,
+        "combine": T * d * 2,
+    }
+
+
+def flops(shape, T):
+    d, F, S, E, k = shape.d_model, shape.d_ffn, shape.n_shared, shape.n_experts, shape.top_k
+    return T * (k * 6 * d * F + S * 6 * d * F + 2 * E * d)
+
+
+def cpu_baseline(shape, seed, layer, zipf, pool, budget_s):
+    """The oracle, as it is, on a bounded sample of the workload's tokens:
+    routing plus the expert mixture per token (expert generation untimed)."""
+    import oracle
+    import synth
+    rw = synth.router_weight(shape, seed, layer)
+    bias = synth.zipf_bias(shape, seed) if zipf else None
+    sh = synth.shared_weights(shape, seed, layer)
+    toks = pool.reshape(-1, shape.d_model)
+    done, spent = 0, 0.0
+    for t in range(toks.shape[0]):
+        x = toks[t:t + 1]
+        t0 = time.perf_counter()
+        ids, w, _ = oracle.route(x, rw, bias, shape.top_k)
+        spent += time.perf_counter() - t0
+        held = synth.host_layer(shape, seed, layer, zipf=zipf, experts=np.unique(ids))
+        pos = {int(e): i for i, e in enumerate(held.experts)}
+        slot = np.array([[pos[int(e)] for e in ids[0]]], dtype=np.int32)
+        t0 = time.perf_counter()
+        oracle.forward(x, slot, w, oracle.held_arrays(held), sh)
+        spent += time.perf_counter() - t0
+        done += 1
+        if spent >= budget_s:
+            break
+    return {"value": done / spent, "unit": "tok/s", "cores": oracle.threads(), "kind": "oracle",
+            "sample": f"{done} tokens of the workload, one at a time (router over all "
+                      f"{shape.n_experts} experts + {shape.top_k} routed + {shape.n_shared} "
+                      f"shared expert FFNs each), {spent:.1f} s of oracle time"}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--workload", type=int, default=1, help="index into synth.WORKLOADS (1..3)")
+    ap.add_argument("--pool", type=int, default=32, help="distinct token batches cycled over")
+    ap.add_argument("--cpu-seconds", type=float, default=15.0)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU: this layer's path is built and measured on a single "
+              f"MI355X (--gpus {args.gpus} is not supported)", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    import synth
+    import synth.device as sdev
+    import quantized_expert_gemv_sigmoid_amd as moe
+
+    wl = synth.WORKLOADS[args.workload]
+    if wl.layers != 1:
+        print("bench.py: the stacked workload is timed with --workload 1..3 per layer", file=sys.stderr)
+        sys.exit(2)
+    shape, T = wl.shape, wl.tokens
+    torch.cuda.set_device(0)
+    log(f"bench: {wl.name}: uploading {shape.n_experts} experts "
+        f"({shape.n_experts * shape.expert_bytes / 1e9:.2f} GB MXFP4)")
+    t = sdev.upload_layer(shape, wl.seed, 0, zipf=wl.zipf_bias)
+    desc = moe.make_desc(shape.n_experts, shape.top_k, shape.d_model, shape.d_ffn, shape.n_shared, t)
+    npool = max(1, min(args.pool, (1 << 16) // T))
+    pool = synth.x_tokens(shape, wl.seed, 0, npool * T).reshape(npool, T, shape.d_model)
+    xs = sdev.tokens_to_device(pool.reshape(npool * T, shape.d_model)).view(npool, T, shape.d_model)
+    ws = torch.empty(moe.workspace_bytes(desc, T), dtype=torch.uint8, device="cuda")
+    out = torch.empty((T, shape.d_model), dtype=torch.int16, device="cuda")
+    ids = torch.empty((T, shape.top_k), dtype=torch.int32, device="cuda")
+    wts = torch.empty((T, shape.top_k), dtype=torch.float32, device="cuda")
+    cnt = torch.empty(shape.n_experts, dtype=torch.int32, device="cuda")
+    counts = []
+    for i in range(npool):
+        moe.route(desc, xs[i], T, ids, wts, cnt, ws)
+        torch.cuda.synchronize()
+        counts.append(cnt.cpu().numpy().copy())
+    path = moe.path_for(desc, T)
+
+    stream = torch.cuda.current_stream()
+    for i in range(args.warmup):
+        moe.layer(desc, xs[i % npool], T, out, None, moe.OUT_BF16, ws)
+    torch.cuda.synchronize()
+
+    K = args.steps
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(moe.TIMED_EVENTS)] for _ in range(K)]
+    start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    start.record(stream)
+    for i in range(K):
+        moe.layer_timed(desc, xs[i % npool], T, out, None, moe.OUT_BF16, ws, evs[i], stream=stream)
+    end.record(stream)
+    torch.cuda.synchronize()
+    ms = start.elapsed_time(end) / K
+
+    ph_ms = {p: float(np.mean([evs[i][j].elapsed_time(evs[i][j + 1]) for i in range(K)]))
+             for j, p in enumerate(PHASES)}
+    ph_bytes = {p: float(np.mean([phase_bytes(shape, T, counts[i % npool])[p] for i in range(K)]))
+                for p in PHASES}
+    step_bytes = sum(ph_bytes.values())
+    dom = max(("expert_gate_up", "expert_down"), key=lambda p: ph_ms[p])
+    achieved = ph_bytes[dom] / (ph_ms[dom] * 1e-3) / 1e9
+    roofline = {"bound": "hbm", "achieved": round(achieved, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
+                "frac": round(achieved / PEAK_HBM_GBS, 4), "traffic": None,
+                "kernel": KERNELS[dom], "bytes_per_launch": int(ph_bytes[dom]),
+                "avg_launch_us": round(ph_ms[dom] * 1e3, 2)}
+    tok_s = T / (ms * 1e-3)
+    layer_gbs = step_bytes / (ms * 1e-3) / 1e9
+    result = {
+        "metric": METRIC, "value": round(tok_s, 2), "unit": "tok/s", "n_gpus": 1, "steps": K,
+        "warmup": args.warmup, "ms_per_step": round(ms, 5), "higher_is_better": True,
+        "scaling": "weak", "vs_baseline": None, "dtype": "fp32",
+        "data": "synthetic",
+        "config": {"workload": wl.name, "n_experts": shape.n_experts, "top_k": shape.top_k,
+                   "n_shared": shape.n_shared, "d_model": shape.d_model, "d_ffn": shape.d_ffn,
+                   "tokens": T, "weights": "mxfp4 (e2m1 + e8m0/32) routed, bf16 shared",
+                   "path": {1: "gemv", 2: "mfma"}[path], "token_pool": npool},
+        "layer_hbm_gbs": round(layer_gbs, 1), "layer_hbm_frac": round(layer_gbs / PEAK_HBM_GBS, 4),
+        "layer_tflops": round(flops(shape, T) / (ms * 1e-3) / 1e12, 3),
+        "phase_us": {p: round(v * 1e3, 2) for p, v in ph_ms.items()},
+        "roofline": roofline,
+    }
+    if not args.no_cpu_baseline:
+        log("bench: timing the CPU oracle on a bounded sample")
+        result["cpu_baseline"] = cpu_baseline(shape, wl.seed, 0, wl.zipf_bias, pool,
+                                              args.cpu_seconds)
+    print(json.dumps(result), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,151 @@
+/*
+ * moe.h -- C ABI of the routed-expert MoE layer on MI355X (gfx950).
+ *
+ * The layer (pages: "kimi-k3-in-c", section 4 "Reduction one: the experts
+ * already ship at half a byte", section 9 "Picking 16 experts of 896" and
+ * "Three invariants"; "Part 4 - Lecture 01", section 1 model table):
+ *
+ *   route:   logit[t][e] = sum_i x[t][i] * Wr[e][i];  s = sigmoid(logit);
+ *            pick the k experts with the largest s + bias (ties -> lower id);
+ *            weight_j = s[id_j] / sum_j s[id_j] (if renorm) * routed_scale.
+ *            The bias steers selection only; weights use the unbiased s.
+ *   experts: for each chosen expert e: g = W1_e x, u = W3_e x, h = act(g, u),
+ *            y = W2_e h, with W1, W3, W2 in MXFP4 (E2M1 code per weight,
+ *            E8M0 scale byte per 32 consecutive weights of a row).
+ *   combine: out[t] = sum_j weight_j * y_j + sum_s FFN_shared_s(x[t]), the
+ *            shared experts bf16, on the same x, added unweighted.
+ *   act:     SiTU-GLU  h = b1*tanh(g/b1)*sigmoid(g) * b2*tanh(u/b2)
+ *            (sigmoid of the uncapped g; K3 uses b1 = 4, b2 = 25), or
+ *            SwiGLU    h = g*sigmoid(g)*u.
+ *
+ * Conventions (every call):
+ *  - All pointers are DEVICE pointers owned by the caller; the library
+ *    allocates nothing, keeps no state between calls and never synchronises
+ *    the host.  Work is enqueued on `stream` (a hipStream_t; NULL = the null
+ *    stream) and may be captured into a HIP graph (no memset, no allocation).
+ *  - Arguments are validated before anything is launched; on any error
+ *    nothing is enqueued and a negative moe_status is returned.
+ *  - T = 0 is a valid no-op.
+ *  - Calls that share a workspace must not overlap in time.
+ */
+#ifndef MOE_H
+#define MOE_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+    MOE_OK = 0,
+    MOE_EINVAL = -1,        /* a null/misaligned pointer, a bad size or enum      */
+    MOE_EUNSUPPORTED = -2,  /* valid but outside the supported shape range below  */
+    MOE_EWORKSPACE = -3,    /* ws_bytes < moe_workspace_bytes(desc, T)            */
+    MOE_EHIP = -4           /* a HIP launch failed (hipGetLastError != success)   */
+} moe_status;
+
+typedef enum { MOE_ACT_SITU = 0, MOE_ACT_SWIGLU = 1 } moe_act;
+
+/* which outputs moe_expert_forward / moe_layer write */
+typedef enum { MOE_OUT_BF16 = 0, MOE_OUT_F32 = 1, MOE_OUT_BOTH = 2 } moe_out_mode;
+
+/* which expert kernels run: AUTO picks the dequant-fused GEMV for small token
+ * counts and the grouped MFMA GEMM for large ones (moe_path_for reports it) */
+typedef enum { MOE_PATH_AUTO = 0, MOE_PATH_GEMV = 1, MOE_PATH_MFMA = 2 } moe_path;
+
+/*
+ * One layer.  Every field is required (there are no defaults).
+ * Shapes: E = n_experts, k = top_k, d = d_model, F = d_ffn, S = n_shared.
+ * Supported: 1 <= k <= E <= 1024, k <= 64, d and F multiples of 32 in
+ * [32, 4096], 0 <= S <= 8; otherwise MOE_EUNSUPPORTED.
+ *
+ * MXFP4 tensors are in the checkpoint layout, row-major per expert: codes
+ * [E][rows][cols/2] bytes, the low nibble of byte c/2 holding column c when c
+ * is even and the high nibble column c+1; scales [E][rows][cols/32] E8M0 bytes
+ * (value 2^(b-127); byte 255 makes its 32 weights contribute zero).
+ * W1 (gate) and W3 (up) are [F rows][d cols]; W2 (down) is [d rows][F cols].
+ * Code arrays must be 16-byte aligned; scale arrays need no alignment.
+ */
+typedef struct {
+    int32_t n_experts, top_k, d_model, d_ffn, n_shared;
+    int32_t renorm;          /* 1: weights renormalised to sum to 1 (K3: 1)      */
+    float routed_scale;      /* multiplies every routed weight (K3: 1.0)         */
+    int32_t act;             /* moe_act                                         */
+    float situ_b1, situ_b2;  /* SiTU betas (K3: 4.0, 25.0); unused for SwiGLU     */
+    int32_t path;            /* moe_path                                        */
+    const float *router_w;   /* [E][d] fp32, 16-byte aligned                     */
+    const float *router_bias;/* [E] fp32 selection bias, or NULL for none        */
+    const uint8_t *w1_q, *w1_s;  /* gate: [E][F][d/2], [E][F][d/32]             */
+    const uint8_t *w3_q, *w3_s;  /* up:   [E][F][d/2], [E][F][d/32]             */
+    const uint8_t *w2_q, *w2_s;  /* down: [E][d][F/2], [E][d][F/32]             */
+    const uint16_t *sh_w1;   /* shared gate [S][F][d] bf16 bits, 16-byte aligned  */
+    const uint16_t *sh_w3;   /* shared up   [S][F][d] bf16                        */
+    const uint16_t *sh_w2;   /* shared down [S][d][F] bf16                        */
+} moe_layer_desc;
+
+/* Workspace bytes a call with up to max_tokens tokens needs (0 if the
+ * descriptor is invalid or unsupported).  Pass a buffer of at least this
+ * size, 256-byte aligned, to the calls below. */
+size_t moe_workspace_bytes(const moe_layer_desc *desc, int32_t max_tokens);
+
+/* The expert path (MOE_PATH_GEMV or MOE_PATH_MFMA) a call with T tokens
+ * takes; a negative moe_status if desc is invalid. */
+int32_t moe_path_for(const moe_layer_desc *desc, int32_t T);
+
+/*
+ * Router only.  x: [T][d] bf16 bits (16-byte aligned).
+ * ids: [T][k] int32 -- each token's experts in descending selection score
+ *      (s + bias), ties to the lower id.
+ * weights: [T][k] fp32 -- the routing weights of those experts, same order.
+ * counts: [E] int32 or NULL -- counts[e] = number of tokens that picked e.
+ */
+moe_status moe_route(const moe_layer_desc *desc, const uint16_t *x, int32_t T,
+                     int32_t *ids, float *weights, int32_t *counts,
+                     void *ws, size_t ws_bytes, void *stream);
+
+/*
+ * Experts for a given routing (ids/weights as moe_route writes them).
+ * Ids must be distinct within a token; an id outside [0, E) drops that term.
+ * include_shared: 1 adds the shared experts, 0 leaves them out.
+ * out_mode picks the outputs: out_bf16 [T][d] bf16 bits (round to nearest
+ * even of the fp32 result) and/or out_f32 [T][d] fp32; the one not asked
+ * for may be NULL.  moe_route followed by moe_expert_forward(include_shared
+ * = 1) gives bit-for-bit the results of moe_layer.
+ */
+moe_status moe_expert_forward(const moe_layer_desc *desc, const uint16_t *x, int32_t T,
+                              const int32_t *ids, const float *weights,
+                              int32_t include_shared, uint16_t *out_bf16, float *out_f32,
+                              int32_t out_mode, void *ws, size_t ws_bytes, void *stream);
+
+/*
+ * Whole layer: route, experts, shared experts, combine.  ids_opt/weights_opt
+ * ([T][k]) and counts_opt ([E]) receive the routing when non-NULL.
+ */
+moe_status moe_layer(const moe_layer_desc *desc, const uint16_t *x, int32_t T,
+                     uint16_t *out_bf16, float *out_f32, int32_t out_mode,
+                     int32_t *ids_opt, float *weights_opt, int32_t *counts_opt,
+                     void *ws, size_t ws_bytes, void *stream);
+
+/*
+ * moe_layer with phase timing: records the caller's HIP events (hipEvent_t
+ * handles, exactly MOE_TIMED_EVENTS of them) on `stream` at the phase
+ * boundaries: events[0] before the router, [1] after the router logits,
+ * [2] after top-k and dispatch, [3] after the expert gate/up kernel (with the
+ * activation and the shared experts' gate/up), [4] after the expert down
+ * kernel, [5] after the combine.  hipEventElapsedTime of consecutive events
+ * gives each phase's device time.  Results equal moe_layer's bit for bit.
+ */
+#define MOE_TIMED_EVENTS 6
+moe_status moe_layer_timed(const moe_layer_desc *desc, const uint16_t *x, int32_t T,
+                           uint16_t *out_bf16, float *out_f32, int32_t out_mode,
+                           void *ws, size_t ws_bytes, void *stream, void *const *events);
+
+/* Static text for a status code. */
+const char *moe_status_str(int32_t status);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* MOE_H */

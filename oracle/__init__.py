@@ -73,6 +73,8 @@ def lib():
         L.orc_forward.argtypes = [vp, vp, i, i, i, i, vp, vp, vp, vp, vp, vp, vp, vp,
                                   i, vp, vp, vp, i, i, f, f]
         L.orc_counts.argtypes = [vp, vp, i, i, i]
+        L.orc_threads.restype = i
+        L.orc_threads.argtypes = []
         _lib = L
     return _lib
 
@@ -165,6 +167,10 @@ def route(x_bf16: np.ndarray, router_w: np.ndarray, bias: Optional[np.ndarray], 
     lib().orc_route(_p(ids), _p(w), _p(gap), _p(sc), _p(x), T, _p(Wr), _p(b), E, d, k,
                     renorm, routed_scale)
     return (ids, w, gap, sc) if want_scores else (ids, w, gap)
+
+
+def threads() -> int:
+    return int(lib().orc_threads())
 
 
 def counts(ids: np.ndarray, E: int) -> np.ndarray:

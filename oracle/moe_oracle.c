@@ -19,6 +19,7 @@
  * Every function here is pinned by a CPU test (tests/test_oracle_*.py).
  */
 #include <math.h>
+#include <omp.h>
 #include <stdint.h>
 #include <stdlib.h>
 #include <string.h>
@@ -289,3 +290,6 @@ void orc_counts(int32_t *counts, const int32_t *ids, int T, int k, int E)
     for (int e = 0; e < E; e++) counts[e] = 0;
     for (size_t i = 0; i < (size_t)T * k; i++) counts[ids[i]]++;
 }
+
+/* number of OpenMP threads the parallel loops above use */
+int orc_threads(void) { return omp_get_max_threads(); }

@@ -1,0 +1,191 @@
+// Internal definitions shared by the HIP kernels of the MoE layer (gfx950).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+#define MOE_WAVE 64
+
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+typedef float f32x2_t __attribute__((ext_vector_type(2)));
+typedef float f32x4_t __attribute__((ext_vector_type(4)));
+
+namespace moe {
+
+// Limits the kernels are written for (checked on the host before launch).
+constexpr int kMaxExperts = 1024;  // router top-k keeps E/64 scores per lane
+constexpr int kMaxTopK = 64;
+constexpr int kMaxDim = 4096;      // d and F: GEMV lanes hold <= 2 MXFP4 blocks
+constexpr int kMaxShared = 8;
+constexpr int kDispatchTokens = 64;  // tokens per dispatch block (one 64-bit mask)
+
+// Device views of the workspace of one call (see carve_workspace).
+struct Work {
+    float *logits;     // [T][E]  router logits
+    int32_t *ids;      // [T][k]  routing (when the caller passed none)
+    float *wts;        // [T][k]
+    int32_t *counts;   // [E]
+    int32_t *offsets;  // [E+1]   exclusive scan of counts
+    int32_t *active;   // [E]     experts with a nonzero count, ascending
+    int32_t *meta;     // [4]     meta[0] = number of active experts
+    uint64_t *masks;   // [nblk][E] token bitmaps per 64-token block
+    int32_t *blk_base; // [nblk][E]
+    int32_t *pos_tok;  // [T*k]   token of the slot at each expert-grouped position
+    float *pos_w;      // [T*k]   its routing weight
+    int32_t *tok_pos;  // [T][k]  positions of a token's slots, ascending expert id
+    void *H;           // [T*k][F] gate/up activations (fp32 or fp16)
+    float *Hs;         // [T][S*F] shared activations (fp32)
+    float *Y;          // [T*k][d] weighted expert outputs
+    float *Ysh;        // [T][d]  shared expert output
+};
+
+struct Shape {
+    int T, E, k, d, F, S;
+    int act;
+    float b1, b2;
+    int renorm;
+    float routed_scale;
+};
+
+// ------------------------------------------------------------------ helpers
+
+__device__ __forceinline__ float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }
+__device__ __forceinline__ float bf16_hi(uint32_t w) { return __uint_as_float(w & 0xffff0000u); }
+
+// fp32 -> bf16 bits, round to nearest even; NaN stays a quiet NaN
+__device__ __forceinline__ uint16_t f32_to_bf16_rne(float f)
+{
+    uint32_t u = __float_as_uint(f);
+    if ((u & 0x7f800000u) == 0x7f800000u)
+        return (uint16_t)((u >> 16) | ((u & 0x007fffffu) ? 0x40u : 0u));
+    u += 0x7fffu + ((u >> 16) & 1u);
+    return (uint16_t)(u >> 16);
+}
+
+// E8M0 byte -> 2^(b-127) as fp32; b == 0 is the subnormal 2^-127; b == 255
+// (NaN in the format) -> 0 so the group contributes nothing.
+__device__ __forceinline__ float e8m0_to_f32(uint32_t b)
+{
+    const uint32_t bits = b == 0 ? 0x00400000u : (b << 23);
+    return b == 255 ? 0.0f : __uint_as_float(bits);
+}
+
+__device__ __forceinline__ float sigmoidf_(float v) { return 1.0f / (1.0f + expf(-v)); }
+
+// gated activation of one (gate, up) pair: 0 = SiTU-GLU, 1 = SwiGLU
+__device__ __forceinline__ float gated_act(float g, float u, int act, float b1, float b2)
+{
+    if (act == 1) return g * sigmoidf_(g) * u;
+    const float a = b1 * tanhf(g / b1) * sigmoidf_(g);
+    const float v = b2 * tanhf(u / b2);
+    return a * v;
+}
+
+// butterfly sum over the 64 lanes of a wave: every lane gets the total
+__device__ __forceinline__ float wave_sum(float v)
+{
+#pragma unroll
+    for (int m = 32; m >= 1; m >>= 1) v += __shfl_xor(v, m, MOE_WAVE);
+    return v;
+}
+
+// One MXFP4 block: 16 bytes = 32 E2M1 codes (byte j holds columns 2j (low
+// nibble) and 2j+1 (high nibble)), dotted with 32 bf16 inputs packed two per
+// dword in column order.  Returns the unscaled partial sum; the caller
+// multiplies by the block's E8M0 scale.
+__device__ __forceinline__ float fp4x32_dot_bf16(const uint4 q, const uint32_t *xp)
+{
+    const uint32_t w[4] = {q.x, q.y, q.z, q.w};
+    float p0 = 0.0f, p1 = 0.0f;
+#pragma unroll
+    for (int i = 0; i < 4; i++) {
+        const bf16x2_t a0 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(w[i], 1.0f, 0);
+        const bf16x2_t a1 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(w[i], 1.0f, 1);
+        const bf16x2_t a2 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(w[i], 1.0f, 2);
+        const bf16x2_t a3 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(w[i], 1.0f, 3);
+        p0 = __builtin_amdgcn_fdot2_f32_bf16(a0, __builtin_bit_cast(bf16x2_t, xp[4 * i + 0]), p0, false);
+        p1 = __builtin_amdgcn_fdot2_f32_bf16(a1, __builtin_bit_cast(bf16x2_t, xp[4 * i + 1]), p1, false);
+        p0 = __builtin_amdgcn_fdot2_f32_bf16(a2, __builtin_bit_cast(bf16x2_t, xp[4 * i + 2]), p0, false);
+        p1 = __builtin_amdgcn_fdot2_f32_bf16(a3, __builtin_bit_cast(bf16x2_t, xp[4 * i + 3]), p1, false);
+    }
+    return p0 + p1;
+}
+
+// One MXFP4 block dotted with 32 fp32 inputs; unscaled partial sum.
+__device__ __forceinline__ float fp4x32_dot_f32(const uint4 q, const float *h)
+{
+    const uint32_t w[4] = {q.x, q.y, q.z, q.w};
+    float p0 = 0.0f, p1 = 0.0f;
+#pragma unroll
+    for (int i = 0; i < 4; i++) {
+#pragma unroll
+        for (int b = 0; b < 4; b++) {
+            f32x2_t v;
+            switch (b) {
+            case 0: v = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(w[i], 1.0f, 0); break;
+            case 1: v = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(w[i], 1.0f, 1); break;
+            case 2: v = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(w[i], 1.0f, 2); break;
+            default: v = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(w[i], 1.0f, 3); break;
+            }
+            p0 = fmaf(v.x, h[8 * i + 2 * b], p0);
+            p1 = fmaf(v.y, h[8 * i + 2 * b + 1], p1);
+        }
+    }
+    return p0 + p1;
+}
+
+// 8 bf16 weights (16 bytes) dotted with 8 bf16 inputs (4 dwords)
+__device__ __forceinline__ float bf16x8_dot_bf16(const uint4 w, const uint32_t *xp, float acc)
+{
+    acc = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, w.x), __builtin_bit_cast(bf16x2_t, xp[0]), acc, false);
+    acc = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, w.y), __builtin_bit_cast(bf16x2_t, xp[1]), acc, false);
+    acc = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, w.z), __builtin_bit_cast(bf16x2_t, xp[2]), acc, false);
+    acc = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, w.w), __builtin_bit_cast(bf16x2_t, xp[3]), acc, false);
+    return acc;
+}
+
+// 8 bf16 weights dotted with 8 fp32 inputs
+__device__ __forceinline__ float bf16x8_dot_f32(const uint4 w, const float *h, float acc)
+{
+    acc = fmaf(bf16_lo(w.x), h[0], acc);
+    acc = fmaf(bf16_hi(w.x), h[1], acc);
+    acc = fmaf(bf16_lo(w.y), h[2], acc);
+    acc = fmaf(bf16_hi(w.y), h[3], acc);
+    acc = fmaf(bf16_lo(w.z), h[4], acc);
+    acc = fmaf(bf16_hi(w.z), h[5], acc);
+    acc = fmaf(bf16_lo(w.w), h[6], acc);
+    acc = fmaf(bf16_hi(w.w), h[7], acc);
+    return acc;
+}
+
+}  // namespace moe
+
+// ------------------------------------------------------------ host launchers
+// Each returns hipGetLastError() after enqueueing on `stream`.
+
+namespace moe {
+
+// router logits for T tokens (VALU, fp32 accumulate)
+hipError_t launch_router_logits(const Shape &s, const uint16_t *x, const float *Wr,
+                                float *logits, hipStream_t stream);
+
+// top-k + renormalised weights; then histogram / scan / stable permutation.
+// do_topk = 0 takes ids/wts as given.
+hipError_t launch_dispatch(const Shape &s, int do_topk, const float *logits, const float *bias,
+                           int32_t *ids, float *wts, int32_t *counts_out, const Work &w,
+                           hipStream_t stream);
+
+// dequant-fused GEMV path: gate/up + activation, then down + weight
+// ev2 (optional): two events recorded after the gate/up and the down launch
+hipError_t launch_gemv_experts(const Shape &s, const uint16_t *x, const uint8_t *w1q,
+                               const uint8_t *w1s, const uint8_t *w3q, const uint8_t *w3s,
+                               const uint8_t *w2q, const uint8_t *w2s, const uint16_t *sh1,
+                               const uint16_t *sh3, const uint16_t *sh2, int include_shared,
+                               const Work &w, hipStream_t stream, hipEvent_t const *ev2);
+
+// combine: out[t] = sum over the token's slots (ascending expert id) + shared
+hipError_t launch_combine(const Shape &s, int include_shared, const Work &w, uint16_t *out_bf16,
+                          float *out_f32, hipStream_t stream);
+
+}  // namespace moe

@@ -1,0 +1,289 @@
+// C ABI of the MoE layer: argument validation, workspace carving and the
+// launch sequence of each entry point (see include/moe.h).
+#include <math.h>
+#include <string.h>
+
+#include "../../include/moe.h"
+#include "common.h"
+
+namespace moe {
+hipError_t launch_mfma_experts(const Shape &s, const uint16_t *x, const moe_layer_desc *d,
+                               int include_shared, const Work &w, hipStream_t stream,
+                               hipEvent_t const *ev2);
+size_t mfma_extra_workspace(const Shape &s);
+bool mfma_supported(const Shape &s);
+}  // namespace moe
+
+namespace {
+
+using moe::Shape;
+using moe::Work;
+
+constexpr int32_t kMaxTokens = 1 << 20;
+constexpr int32_t kGemvMaxTokens = 128;  // AUTO: GEMV up to here, MFMA above
+
+bool aligned(const void *p, size_t a) { return ((uintptr_t)p % a) == 0; }
+
+moe_status check_desc(const moe_layer_desc *d)
+{
+    if (!d) return MOE_EINVAL;
+    if (d->n_experts < 1 || d->top_k < 1 || d->top_k > d->n_experts) return MOE_EINVAL;
+    if (d->d_model < 32 || d->d_model % 32 || d->d_ffn < 32 || d->d_ffn % 32) return MOE_EINVAL;
+    if (d->n_shared < 0) return MOE_EINVAL;
+    if (d->act != MOE_ACT_SITU && d->act != MOE_ACT_SWIGLU) return MOE_EINVAL;
+    if (d->path != MOE_PATH_AUTO && d->path != MOE_PATH_GEMV && d->path != MOE_PATH_MFMA)
+        return MOE_EINVAL;
+    if (d->renorm != 0 && d->renorm != 1) return MOE_EINVAL;
+    if (!isfinite(d->routed_scale)) return MOE_EINVAL;
+    if (d->act == MOE_ACT_SITU &&
+        !(isfinite(d->situ_b1) && isfinite(d->situ_b2) && d->situ_b1 > 0 && d->situ_b2 > 0))
+        return MOE_EINVAL;
+    if (!d->router_w || !d->w1_q || !d->w1_s || !d->w3_q || !d->w3_s || !d->w2_q || !d->w2_s)
+        return MOE_EINVAL;
+    if (d->n_shared > 0 && (!d->sh_w1 || !d->sh_w3 || !d->sh_w2)) return MOE_EINVAL;
+    if (!aligned(d->router_w, 16) || !aligned(d->w1_q, 16) || !aligned(d->w3_q, 16) ||
+        !aligned(d->w2_q, 16))
+        return MOE_EINVAL;
+    if (d->n_shared > 0 && (!aligned(d->sh_w1, 16) || !aligned(d->sh_w3, 16) || !aligned(d->sh_w2, 16)))
+        return MOE_EINVAL;
+    if (d->n_experts > moe::kMaxExperts || d->top_k > moe::kMaxTopK || d->d_model > moe::kMaxDim ||
+        d->d_ffn > moe::kMaxDim || d->n_shared > moe::kMaxShared)
+        return MOE_EUNSUPPORTED;
+    return MOE_OK;
+}
+
+Shape shape_of(const moe_layer_desc *d, int32_t T)
+{
+    Shape s;
+    s.T = T;
+    s.E = d->n_experts;
+    s.k = d->top_k;
+    s.d = d->d_model;
+    s.F = d->d_ffn;
+    s.S = d->n_shared;
+    s.act = d->act;
+    s.b1 = d->situ_b1;
+    s.b2 = d->situ_b2;
+    s.renorm = d->renorm;
+    s.routed_scale = d->routed_scale;
+    return s;
+}
+
+Shape shape_of(const moe_layer_desc *d, int32_t T);
+
+int path_of(const moe_layer_desc *d, int32_t T)
+{
+    if (d->path == MOE_PATH_GEMV || d->path == MOE_PATH_MFMA) return d->path;
+    return (T > kGemvMaxTokens && moe::mfma_supported(shape_of(d, T))) ? MOE_PATH_MFMA
+                                                                       : MOE_PATH_GEMV;
+}
+
+// Lay the workspace out for T tokens; returns the bytes used.  With base ==
+// nullptr only the size is computed.
+size_t carve(const Shape &s, char *base, Work *w)
+{
+    size_t off = 0;
+    auto take = [&](size_t bytes) -> char * {
+        char *p = base ? base + off : nullptr;
+        off += (bytes + 255) & ~(size_t)255;
+        return p;
+    };
+    const size_t T = (size_t)s.T, E = (size_t)s.E, k = (size_t)s.k;
+    const size_t nblk = (T + moe::kDispatchTokens - 1) / moe::kDispatchTokens;
+    Work v;
+    v.logits = (float *)take(T * E * 4);
+    v.ids = (int32_t *)take(T * k * 4);
+    v.wts = (float *)take(T * k * 4);
+    v.counts = (int32_t *)take(E * 4);
+    v.offsets = (int32_t *)take((E + 1) * 4);
+    v.active = (int32_t *)take(E * 4);
+    v.meta = (int32_t *)take(16);
+    v.masks = (uint64_t *)take(nblk * E * 8);
+    v.blk_base = (int32_t *)take(nblk * E * 4);
+    v.pos_tok = (int32_t *)take(T * k * 4);
+    v.pos_w = (float *)take(T * k * 4);
+    v.tok_pos = (int32_t *)take(T * k * 4);
+    v.H = (void *)take(T * k * (size_t)s.F * 4);
+    v.Hs = (float *)take(T * (size_t)s.S * s.F * 4);
+    v.Y = (float *)take(T * k * (size_t)s.d * 4);
+    v.Ysh = (float *)take(T * (size_t)s.d * 4);
+    if (w) *w = v;
+    return off;
+}
+
+size_t ws_needed(const moe_layer_desc *d, int32_t T)
+{
+    const Shape s = shape_of(d, T < 1 ? 1 : T);
+    size_t n = carve(s, nullptr, nullptr);
+    n += moe::mfma_extra_workspace(s);
+    return n;
+}
+
+moe_status check_call(const moe_layer_desc *d, const uint16_t *x, int32_t T, void *ws,
+                      size_t ws_bytes, bool experts)
+{
+    const moe_status st = check_desc(d);
+    if (st != MOE_OK) return st;
+    if (T < 0) return MOE_EINVAL;
+    if (T > kMaxTokens) return MOE_EUNSUPPORTED;
+    if (T == 0) return MOE_OK;
+    if (!x || !aligned(x, 16)) return MOE_EINVAL;
+    if (!ws || !aligned(ws, 256)) return MOE_EINVAL;
+    if (experts && path_of(d, T) == MOE_PATH_MFMA && !moe::mfma_supported(shape_of(d, T)))
+        return MOE_EUNSUPPORTED;
+    if (ws_bytes < ws_needed(d, T)) return MOE_EWORKSPACE;
+    return MOE_OK;
+}
+
+moe_status check_out(int32_t out_mode, const uint16_t *out_bf16, const float *out_f32)
+{
+    if (out_mode != MOE_OUT_BF16 && out_mode != MOE_OUT_F32 && out_mode != MOE_OUT_BOTH)
+        return MOE_EINVAL;
+    const bool want_b = out_mode != MOE_OUT_F32, want_f = out_mode != MOE_OUT_BF16;
+    if (want_b && (!out_bf16 || !aligned(out_bf16, 16))) return MOE_EINVAL;
+    if (want_f && (!out_f32 || !aligned(out_f32, 16))) return MOE_EINVAL;
+    return MOE_OK;
+}
+
+#define MOE_TRY(expr)                                   \
+    do {                                                \
+        if ((expr) != hipSuccess) return MOE_EHIP;      \
+    } while (0)
+
+// records events[i] (if any) on the stream
+hipError_t mark(hipEvent_t const *ev, int i, hipStream_t st)
+{
+    return ev ? hipEventRecord(ev[i], st) : hipSuccess;
+}
+
+moe_status run_experts(const moe_layer_desc *d, const Shape &s, const uint16_t *x,
+                       int include_shared, const Work &w, int32_t out_mode, uint16_t *out_bf16,
+                       float *out_f32, hipStream_t st, hipEvent_t const *ev = nullptr)
+{
+    const int path = path_of(d, s.T);
+    if (path == MOE_PATH_GEMV) {
+        MOE_TRY(moe::launch_gemv_experts(s, x, d->w1_q, d->w1_s, d->w3_q, d->w3_s, d->w2_q,
+                                         d->w2_s, d->sh_w1, d->sh_w3, d->sh_w2, include_shared, w,
+                                         st, ev ? ev + 3 : nullptr));
+    } else {
+        MOE_TRY(moe::launch_mfma_experts(s, x, d, include_shared, w, st, ev ? ev + 3 : nullptr));
+    }
+    MOE_TRY(moe::launch_combine(s, include_shared && s.S > 0, w,
+                                out_mode != MOE_OUT_F32 ? out_bf16 : nullptr,
+                                out_mode != MOE_OUT_BF16 ? out_f32 : nullptr, st));
+    MOE_TRY(mark(ev, 5, st));
+    return MOE_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+size_t moe_workspace_bytes(const moe_layer_desc *desc, int32_t max_tokens)
+{
+    if (check_desc(desc) != MOE_OK || max_tokens < 0 || max_tokens > kMaxTokens) return 0;
+    return ws_needed(desc, max_tokens);
+}
+
+int32_t moe_path_for(const moe_layer_desc *desc, int32_t T)
+{
+    const moe_status st = check_desc(desc);
+    if (st != MOE_OK) return st;
+    return path_of(desc, T);
+}
+
+moe_status moe_route(const moe_layer_desc *desc, const uint16_t *x, int32_t T, int32_t *ids,
+                     float *weights, int32_t *counts, void *ws, size_t ws_bytes, void *stream)
+{
+    moe_status st = check_call(desc, x, T, ws, ws_bytes, false);
+    if (st != MOE_OK || T == 0) return st;
+    if (!ids || !weights) return MOE_EINVAL;
+    (void)hipGetLastError();
+    const Shape s = shape_of(desc, T);
+    Work w;
+    carve(s, (char *)ws, &w);
+    hipStream_t hs = (hipStream_t)stream;
+    MOE_TRY(moe::launch_router_logits(s, x, desc->router_w, w.logits, hs));
+    MOE_TRY(moe::launch_dispatch(s, 1, w.logits, desc->router_bias, ids, weights, counts, w, hs));
+    return MOE_OK;
+}
+
+moe_status moe_expert_forward(const moe_layer_desc *desc, const uint16_t *x, int32_t T,
+                              const int32_t *ids, const float *weights, int32_t include_shared,
+                              uint16_t *out_bf16, float *out_f32, int32_t out_mode, void *ws,
+                              size_t ws_bytes, void *stream)
+{
+    moe_status st = check_call(desc, x, T, ws, ws_bytes, true);
+    if (st != MOE_OK) return st;
+    if (include_shared != 0 && include_shared != 1) return MOE_EINVAL;
+    st = check_out(out_mode, out_bf16, out_f32);
+    if (st != MOE_OK || T == 0) return st;
+    if (!ids || !weights) return MOE_EINVAL;
+    (void)hipGetLastError();
+    const Shape s = shape_of(desc, T);
+    Work w;
+    carve(s, (char *)ws, &w);
+    hipStream_t hs = (hipStream_t)stream;
+    MOE_TRY(moe::launch_dispatch(s, 0, nullptr, nullptr, const_cast<int32_t *>(ids),
+                                 const_cast<float *>(weights), nullptr, w, hs));
+    return run_experts(desc, s, x, include_shared, w, out_mode, out_bf16, out_f32, hs);
+}
+
+moe_status moe_layer(const moe_layer_desc *desc, const uint16_t *x, int32_t T, uint16_t *out_bf16,
+                     float *out_f32, int32_t out_mode, int32_t *ids_opt, float *weights_opt,
+                     int32_t *counts_opt, void *ws, size_t ws_bytes, void *stream)
+{
+    moe_status st = check_call(desc, x, T, ws, ws_bytes, true);
+    if (st != MOE_OK) return st;
+    st = check_out(out_mode, out_bf16, out_f32);
+    if (st != MOE_OK || T == 0) return st;
+    (void)hipGetLastError();
+    const Shape s = shape_of(desc, T);
+    Work w;
+    carve(s, (char *)ws, &w);
+    int32_t *ids = ids_opt ? ids_opt : w.ids;
+    float *wts = weights_opt ? weights_opt : w.wts;
+    hipStream_t hs = (hipStream_t)stream;
+    MOE_TRY(moe::launch_router_logits(s, x, desc->router_w, w.logits, hs));
+    MOE_TRY(moe::launch_dispatch(s, 1, w.logits, desc->router_bias, ids, wts, counts_opt, w, hs));
+    return run_experts(desc, s, x, 1, w, out_mode, out_bf16, out_f32, hs);
+}
+
+moe_status moe_layer_timed(const moe_layer_desc *desc, const uint16_t *x, int32_t T,
+                           uint16_t *out_bf16, float *out_f32, int32_t out_mode, void *ws,
+                           size_t ws_bytes, void *stream, void *const *events)
+{
+    moe_status st = check_call(desc, x, T, ws, ws_bytes, true);
+    if (st != MOE_OK) return st;
+    st = check_out(out_mode, out_bf16, out_f32);
+    if (st != MOE_OK || T == 0) return st;
+    if (!events) return MOE_EINVAL;
+    for (int i = 0; i < MOE_TIMED_EVENTS; i++)
+        if (!events[i]) return MOE_EINVAL;
+    (void)hipGetLastError();
+    hipEvent_t const *ev = reinterpret_cast<hipEvent_t const *>(events);
+    const Shape s = shape_of(desc, T);
+    Work w;
+    carve(s, (char *)ws, &w);
+    hipStream_t hs = (hipStream_t)stream;
+    MOE_TRY(mark(ev, 0, hs));
+    MOE_TRY(moe::launch_router_logits(s, x, desc->router_w, w.logits, hs));
+    MOE_TRY(mark(ev, 1, hs));
+    MOE_TRY(moe::launch_dispatch(s, 1, w.logits, desc->router_bias, w.ids, w.wts, nullptr, w, hs));
+    MOE_TRY(mark(ev, 2, hs));
+    return run_experts(desc, s, x, 1, w, out_mode, out_bf16, out_f32, hs, ev);
+}
+
+const char *moe_status_str(int32_t status)
+{
+    switch (status) {
+    case MOE_OK: return "ok";
+    case MOE_EINVAL: return "invalid argument";
+    case MOE_EUNSUPPORTED: return "unsupported shape";
+    case MOE_EWORKSPACE: return "workspace too small";
+    case MOE_EHIP: return "HIP launch failed";
+    default: return "unknown status";
+    }
+}
+
+}  // extern "C"

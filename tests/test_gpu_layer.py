@@ -1,0 +1,196 @@
+"""GPU parity of the whole layer through the C ABI against the CPU oracle.
+
+Ids (as per-token sets) and per-expert counts must be bit-exact, fp32 outputs
+within relative L2 <= 2e-3 and max-abs <= 1e-2 * rms, bf16 outputs the
+round-to-nearest-even of the fp32 outputs bit for bit, moe_route +
+moe_expert_forward bit-identical to moe_layer, and two runs bit-identical.
+"""
+import gc
+
+import numpy as np
+import pytest
+
+import oracle
+import synth
+from support import (assert_close, bf16_rne, check_routing, log, make_gpu_layer, oracle_outputs,
+                     run_layer, tokens)
+
+pytestmark = pytest.mark.gpu
+
+torch = pytest.importorskip("torch")
+
+
+@pytest.fixture(autouse=True)
+def _free_memory():
+    yield
+    gc.collect()
+    torch.cuda.empty_cache()
+
+
+def _full_check(gl, T, act=0, screened=True, first_token=0):
+    x, rw, bias = tokens(gl, T, screened=screened, first_token=first_token)
+    out_f, out_b, ids, w, cnt = run_layer(gl, x)
+    rids, rw_, gap, rout = oracle_outputs(gl, x, rw, bias, np.arange(T), act=act)
+    check_routing(ids, w, cnt, rids, rw_, gl.shape.n_experts, "routing")
+    assert_close(out_f, rout, f"T={T}")
+    assert np.array_equal(out_b, bf16_rne(out_f)), "bf16 output is not RNE(fp32 output)"
+    return x, out_f, out_b, ids, w, cnt
+
+
+def test_tiny_workload_situ():
+    w = synth.WORKLOADS[0]
+    log(f"case: {w.name} seed={w.seed}")
+    gl = make_gpu_layer(w.shape, w.seed)
+    x, out_f, out_b, ids, wts, cnt = _full_check(gl, w.tokens)
+    # deterministic: a second run gives the same bits
+    out_f2, out_b2, ids2, _, _ = run_layer(gl, x)
+    assert np.array_equal(out_f, out_f2) and np.array_equal(out_b, out_b2) and np.array_equal(ids, ids2)
+
+
+def test_tiny_workload_swiglu():
+    w = synth.WORKLOADS[0]
+    log(f"case: {w.name} swiglu")
+    gl = make_gpu_layer(w.shape, w.seed, act=oracle.ACT_SWIGLU)
+    _full_check(gl, w.tokens, act=oracle.ACT_SWIGLU)
+
+
+def test_route_then_forward_equals_layer():
+    import quantized_expert_gemv_sigmoid_amd as moe
+    import synth.device as sdev
+    shape = synth.LayerShape(n_experts=40, top_k=6, n_shared=2, d_model=320, d_ffn=416)
+    gl = make_gpu_layer(shape, 7)
+    for T in (3, 70):
+        log(f"case: route+forward vs layer T={T}")
+        x, _, _ = tokens(gl, T)
+        out_f, out_b, ids, w, cnt = run_layer(gl, x)
+        xd = sdev.tokens_to_device(x)
+        ids2 = torch.empty((T, 6), dtype=torch.int32, device="cuda")
+        w2 = torch.empty((T, 6), dtype=torch.float32, device="cuda")
+        c2 = torch.empty(40, dtype=torch.int32, device="cuda")
+        ws = torch.empty(moe.workspace_bytes(gl.desc, T), dtype=torch.uint8, device="cuda")
+        moe.route(gl.desc, xd, T, ids2, w2, c2, ws)
+        of = torch.empty((T, 320), dtype=torch.float32, device="cuda")
+        ob = torch.empty((T, 320), dtype=torch.int16, device="cuda")
+        moe.expert_forward(gl.desc, xd, T, ids2, w2, 1, ob, of, moe.OUT_BOTH, ws)
+        torch.cuda.synchronize()
+        assert np.array_equal(ids2.cpu().numpy(), ids)
+        assert np.array_equal(w2.cpu().numpy(), w)
+        assert np.array_equal(c2.cpu().numpy(), cnt)
+        assert np.array_equal(of.cpu().numpy(), out_f)
+        assert np.array_equal(ob.cpu().numpy().view(np.uint16), out_b)
+        # experts only, without the shared experts
+        moe.expert_forward(gl.desc, xd, T, ids2, w2, 0, None, of, moe.OUT_F32, ws)
+        torch.cuda.synchronize()
+        held = gl.host
+        ref = oracle.forward(x, ids, w, oracle.held_arrays(held), oracle.shared_arrays(held),
+                             include_shared=False)
+        assert_close(of.cpu().numpy(), ref, f"no-shared T={T}")
+
+
+@pytest.mark.parametrize("T", [1, 5, 37, 64, 65, 130])
+def test_ragged_shapes(T):
+    # d = 320 -> 10 MX blocks per row (lanes partly idle); F = 416 -> 13 blocks;
+    # T > 64 takes the multi-block dispatch; odd T exercises the token chunk tail
+    shape = synth.LayerShape(n_experts=40, top_k=6, n_shared=2, d_model=320, d_ffn=416)
+    log(f"case: ragged E40 k6 S2 d320 F416 T={T}")
+    gl = make_gpu_layer(shape, 11)
+    _full_check(gl, T)
+
+
+def test_topk_equals_experts_dense_mixture():
+    shape = synth.LayerShape(n_experts=8, top_k=8, n_shared=1, d_model=64, d_ffn=96)
+    log("case: k = E = 8")
+    gl = make_gpu_layer(shape, 21)
+    _full_check(gl, 9, screened=False)
+
+
+def test_no_shared_experts_and_single_expert():
+    for shape in (synth.LayerShape(n_experts=16, top_k=3, n_shared=0, d_model=128, d_ffn=256),
+                  synth.LayerShape(n_experts=1, top_k=1, n_shared=1, d_model=96, d_ffn=64)):
+        log(f"case: {shape}")
+        gl = make_gpu_layer(shape, 31)
+        _full_check(gl, 6)
+
+
+def test_nan_scale_groups_contribute_zero():
+    shape = synth.LayerShape(n_experts=12, top_k=4, n_shared=1, d_model=256, d_ffn=192)
+    h = synth.host_layer(shape, 41, 0)
+    rng = np.random.default_rng(0)
+    for s in (h.w1s, h.w3s, h.w2s):
+        s[rng.random(s.shape) < 0.05] = 255
+    log("case: 5% of scale bytes = 255")
+    gl = make_gpu_layer(shape, 41, host=h)
+    _full_check(gl, 8)
+
+
+def test_extreme_scales_exact_window():
+    # scale bytes across 100..150 (beyond the workload's 119..122)
+    shape = synth.LayerShape(n_experts=12, top_k=4, n_shared=1, d_model=256, d_ffn=192)
+    h = synth.host_layer(shape, 43, 0)
+    rng = np.random.default_rng(1)
+    for s in (h.w1s, h.w3s, h.w2s):
+        s[...] = rng.integers(112, 126, size=s.shape, dtype=np.uint8)
+    log("case: scale bytes 112..125")
+    gl = make_gpu_layer(shape, 43, host=h)
+    _full_check(gl, 8)
+
+
+def test_zero_tokens_is_noop():
+    import quantized_expert_gemv_sigmoid_amd as moe
+    w = synth.WORKLOADS[0]
+    gl = make_gpu_layer(w.shape, w.seed)
+    out = torch.full((2, w.shape.d_model), 7.0, device="cuda")
+    ws = torch.empty(moe.workspace_bytes(gl.desc, 1), dtype=torch.uint8, device="cuda")
+    x = torch.zeros((1, w.shape.d_model), dtype=torch.int16, device="cuda")
+    moe.layer(gl.desc, x, 0, None, out, moe.OUT_F32, ws)
+    torch.cuda.synchronize()
+    assert (out == 7.0).all()
+
+
+# ------------------------------------------------------------- full sizes
+
+def _k3(widx, zipf=False):
+    w = synth.WORKLOADS[widx]
+    log(f"case: {w.name} seed={w.seed} (uploading {w.shape.n_experts} experts)")
+    return w, make_gpu_layer(w.shape, w.seed, zipf=zipf)
+
+
+def test_k3_decode_T1():
+    w, gl = _k3(1)
+    x, out_f, out_b, ids, wts, cnt = _full_check(gl, 1)
+    assert cnt.sum() == 16 and (cnt <= 1).all()
+    del gl
+
+
+def test_k3_decode_T1_zipf_bias():
+    w = synth.WORKLOADS[4]
+    log(f"case: {w.name} layer 0 (one layer of the stack)")
+    gl = make_gpu_layer(w.shape, w.seed, zipf=True)
+    _full_check(gl, 4)
+    del gl
+
+
+def test_k3_decode_T64_sampled():
+    w, gl = _k3(2)
+    x, rw, bias = tokens(gl, w.tokens)
+    out_f, out_b, ids, wts, cnt = run_layer(gl, x)
+    sample = np.array([0, 1, 7, 15, 16, 31, 32, 40, 47, 48, 55, 62, 63])
+    rids, rw_, gap, rout = oracle_outputs(gl, x, rw, bias, sample)
+    check_routing(ids, wts, cnt, rids, rw_, w.shape.n_experts, "T64")
+    log(f"  distinct experts touched: {(cnt > 0).sum()}")
+    assert_close(out_f[sample], rout, "T64 sampled")
+    assert np.array_equal(out_b, bf16_rne(out_f))
+    del gl
+
+
+def test_k3_prefill_T4096_sampled():
+    w, gl = _k3(3)
+    x, rw, bias = tokens(gl, w.tokens)
+    out_f, out_b, ids, wts, cnt = run_layer(gl, x)
+    sample = np.array([0, 1, 63, 64, 1000, 2047, 2048, 3001, 4030, 4095])
+    rids, rw_, gap, rout = oracle_outputs(gl, x, rw, bias, sample)
+    check_routing(ids, wts, cnt, rids, rw_, w.shape.n_experts, "T4096")
+    log(f"  experts touched: {(cnt > 0).sum()}, tokens/expert {cnt.mean():.1f} +- {cnt.std():.1f}")
+    assert_close(out_f[sample], rout, "T4096 sampled")
+    assert np.array_equal(out_b, bf16_rne(out_f))
+    del gl
