@@ -144,6 +144,9 @@ def main():
     K = args.steps
     evs = [[torch.cuda.Event(enable_timing=True) for _ in range(moe.TIMED_EVENTS)] for _ in range(K)]
     start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    for row in evs:  # torch creates an event's HIP handle at its first record
+        for e in row:
+            e.record(stream)
     torch.cuda.synchronize()
     start.record(stream)
     for i in range(K):

@@ -153,6 +153,9 @@ def layer_timed(desc: LayerDesc, x, T: int, out_bf16, out_f32, out_mode: int, ws
     """moe_layer recording the 6 phase-boundary events (torch.cuda.Event with
     enable_timing) on the stream."""
     assert len(events) == TIMED_EVENTS
+    for e in events:
+        if not e.cuda_event:  # torch creates the HIP event at its first record
+            e.record(stream)
     arr = (ctypes.c_void_p * TIMED_EVENTS)(*[e.cuda_event for e in events])
     wp, wn = _ws(ws)
     _check(lib().moe_layer_timed(ctypes.byref(desc), _ptr(x), T, _ptr(out_bf16), _ptr(out_f32),
