@@ -100,6 +100,7 @@ def main():
     ap.add_argument("--pool", type=int, default=32, help="distinct token batches cycled over")
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-graph", action="store_true", help="time eager launches instead of HIP graph replays")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py measures one GPU: this layer's path is built and measured on a single "
@@ -142,8 +143,28 @@ def main():
     torch.cuda.synchronize()
 
     K = args.steps
-    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(moe.TIMED_EVENTS)] for _ in range(K)]
     start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    graph_ms = None
+    if not args.no_graph:
+        # one HIP graph per token batch of the pool (the batch's address is
+        # baked into its graph, as a decode loop's fixed input buffer would be)
+        graphs = []
+        for i in range(npool):
+            g = torch.cuda.CUDAGraph()
+            with torch.cuda.graph(g):
+                moe.layer(desc, xs[i], T, out, None, moe.OUT_BF16, ws)
+            graphs.append(g)
+        for i in range(args.warmup):
+            graphs[i % npool].replay()
+        torch.cuda.synchronize()
+        start.record(stream)
+        for i in range(K):
+            graphs[i % npool].replay()
+        end.record(stream)
+        torch.cuda.synchronize()
+        graph_ms = start.elapsed_time(end) / K
+
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(moe.TIMED_EVENTS)] for _ in range(K)]
     for row in evs:  # torch creates an event's HIP handle at its first record
         for e in row:
             e.record(stream)
@@ -153,7 +174,8 @@ def main():
         moe.layer_timed(desc, xs[i % npool], T, out, None, moe.OUT_BF16, ws, evs[i], stream=stream)
     end.record(stream)
     torch.cuda.synchronize()
-    ms = start.elapsed_time(end) / K
+    eager_ms = start.elapsed_time(end) / K
+    ms = graph_ms if graph_ms is not None else eager_ms
 
     ph_ms = {p: float(np.mean([evs[i][j].elapsed_time(evs[i][j + 1]) for i in range(K)]))
              for j, p in enumerate(PHASES)}
@@ -176,7 +198,9 @@ def main():
         "config": {"workload": wl.name, "n_experts": shape.n_experts, "top_k": shape.top_k,
                    "n_shared": shape.n_shared, "d_model": shape.d_model, "d_ffn": shape.d_ffn,
                    "tokens": T, "weights": "mxfp4 (e2m1 + e8m0/32) routed, bf16 shared",
-                   "path": {1: "gemv", 2: "mfma"}[path], "token_pool": npool},
+                   "path": {1: "gemv", 2: "mfma"}[path], "token_pool": npool,
+                   "launch": "hip graph replay" if graph_ms is not None else "eager"},
+        "ms_per_step_eager": round(eager_ms, 5),
         "layer_hbm_gbs": round(layer_gbs, 1), "layer_hbm_frac": round(layer_gbs / PEAK_HBM_GBS, 4),
         "layer_tflops": round(flops(shape, T) / (ms * 1e-3) / 1e12, 3),
         "phase_us": {p: round(v * 1e3, 2) for p, v in ph_ms.items()},

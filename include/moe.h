@@ -131,10 +131,11 @@ moe_status moe_layer(const moe_layer_desc *desc, const uint16_t *x, int32_t T,
 /*
  * moe_layer with phase timing: records the caller's HIP events (hipEvent_t
  * handles, exactly MOE_TIMED_EVENTS of them) on `stream` at the phase
- * boundaries: events[0] before the router, [1] after the router logits,
+ * boundaries: events[0] before the router, [1] after the router logits (and,
+ * on the GEMV path, the shared experts' gate/up, which share that launch),
  * [2] after top-k and dispatch, [3] after the expert gate/up kernel (with the
- * activation and the shared experts' gate/up), [4] after the expert down
- * kernel, [5] after the combine.  hipEventElapsedTime of consecutive events
+ * activation; on the GEMV path also the shared experts' down), [4] after the
+ * expert down kernel, [5] after the combine.  hipEventElapsedTime of consecutive events
  * gives each phase's device time.  Results equal moe_layer's bit for bit.
  */
 #define MOE_TIMED_EVENTS 6

@@ -37,7 +37,7 @@ struct Work {
     void *H;           // [T*k][F] gate/up activations (fp32 or fp16)
     float *Hs;         // [T][S*F] shared activations (fp32)
     float *Y;          // [T*k][d] weighted expert outputs
-    float *Ysh;        // [T][d]  shared expert output
+    float *Ysh;        // [S][T][d] shared experts' outputs
 };
 
 struct Shape {
@@ -94,9 +94,19 @@ __device__ __forceinline__ float wave_sum(float v)
 // nibble) and 2j+1 (high nibble)), dotted with 32 bf16 inputs packed two per
 // dword in column order.  Returns the unscaled partial sum; the caller
 // multiplies by the block's E8M0 scale.
+// Opaque copy of 4 packed words: the decode below then stays at its point of
+// use instead of being hoisted out of token loops (where its 32 results per
+// block would stay live and exhaust the register file).
+__device__ __forceinline__ void opaque4(uint32_t (&w)[4], const uint4 q)
+{
+    w[0] = q.x; w[1] = q.y; w[2] = q.z; w[3] = q.w;
+    asm volatile("" : "+v"(w[0]), "+v"(w[1]), "+v"(w[2]), "+v"(w[3]));
+}
+
 __device__ __forceinline__ float fp4x32_dot_bf16(const uint4 q, const uint32_t *xp)
 {
-    const uint32_t w[4] = {q.x, q.y, q.z, q.w};
+    uint32_t w[4];
+    opaque4(w, q);
     float p0 = 0.0f, p1 = 0.0f;
 #pragma unroll
     for (int i = 0; i < 4; i++) {
@@ -115,7 +125,8 @@ __device__ __forceinline__ float fp4x32_dot_bf16(const uint4 q, const uint32_t *
 // One MXFP4 block dotted with 32 fp32 inputs; unscaled partial sum.
 __device__ __forceinline__ float fp4x32_dot_f32(const uint4 q, const float *h)
 {
-    const uint32_t w[4] = {q.x, q.y, q.z, q.w};
+    uint32_t w[4];
+    opaque4(w, q);
     float p0 = 0.0f, p1 = 0.0f;
 #pragma unroll
     for (int i = 0; i < 4; i++) {
@@ -166,25 +177,32 @@ __device__ __forceinline__ float bf16x8_dot_f32(const uint4 w, const float *h, f
 
 namespace moe {
 
-// router logits for T tokens (VALU, fp32 accumulate)
-hipError_t launch_router_logits(const Shape &s, const uint16_t *x, const float *Wr,
-                                float *logits, hipStream_t stream);
+// device pointers of one layer's weights
+struct Weights {
+    const float *router_w, *router_bias;
+    const uint8_t *w1q, *w1s, *w3q, *w3s, *w2q, *w2s;
+    const uint16_t *sh1, *sh3, *sh2;
+};
 
-// top-k + renormalised weights; then histogram / scan / stable permutation.
-// do_topk = 0 takes ids/wts as given.
+// decode front: shared experts' gate/up + activation (if include_shared) and
+// the router logits (if do_router), in one launch
+hipError_t launch_front(const Shape &s, const uint16_t *x, const Weights &wt, int do_router,
+                        int include_shared, const Work &w, hipStream_t stream);
+
+// top-k + renormalised weights (do_topk), then histogram / scan / stable
+// permutation of the slots; do_topk = 0 takes ids/wts as given.
 hipError_t launch_dispatch(const Shape &s, int do_topk, const float *logits, const float *bias,
                            int32_t *ids, float *wts, int32_t *counts_out, const Work &w,
                            hipStream_t stream);
 
-// dequant-fused GEMV path: gate/up + activation, then down + weight
-// ev2 (optional): two events recorded after the gate/up and the down launch
-hipError_t launch_gemv_experts(const Shape &s, const uint16_t *x, const uint8_t *w1q,
-                               const uint8_t *w1s, const uint8_t *w3q, const uint8_t *w3s,
-                               const uint8_t *w2q, const uint8_t *w2s, const uint16_t *sh1,
-                               const uint16_t *sh3, const uint16_t *sh2, int include_shared,
-                               const Work &w, hipStream_t stream, hipEvent_t const *ev2);
+// dequant-fused GEMV experts: shared down + routed gate/up + activation, then
+// routed down + weight.  ev2 (optional): events recorded after each launch.
+hipError_t launch_gemv_experts(const Shape &s, const uint16_t *x, const Weights &wt,
+                               int include_shared, const Work &w, hipStream_t stream,
+                               hipEvent_t const *ev2);
 
-// combine: out[t] = sum over the token's slots (ascending expert id) + shared
+// combine: out[t] = sum of the token's slot rows (ascending expert id)
+//                 + sum over shared experts of Ysh[s][t]
 hipError_t launch_combine(const Shape &s, int include_shared, const Work &w, uint16_t *out_bf16,
                           float *out_f32, hipStream_t stream);
 

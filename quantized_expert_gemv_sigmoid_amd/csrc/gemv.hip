@@ -1,201 +1,112 @@
 // Dequant-fused GEMV path for small token counts (decode).
 //
-// Every selected expert's MXFP4 bytes are read once with 16-byte loads: a
-// lane's load is exactly one 32-weight block (kimi-k3-in-c section 4: codes
-// two per byte, low nibble = even column, one E8M0 scale byte per 32), which
-// is decoded in registers (v_cvt_scalef32_pk_bf16/f32_fp4) and never written
-// back.  One wave works on one row at a time across all 64 lanes: lane l
-// holds MX blocks l and l + 64 of the row, so the input vector of the wave's
-// tokens stays in registers for every row the wave visits.
+// Every selected expert's MXFP4 bytes are read once with 16-byte loads: one
+// lane load is exactly one 32-weight block (kimi-k3-in-c section 4: two codes
+// per byte, low nibble = even column, one E8M0 scale byte per 32 weights).
+// It is decoded in registers (v_cvt_scalef32_pk_{bf16,f32}_fp4) and never
+// written back.  A row is spread over L lanes (L = 16, 32 or 64), lane g of
+// the row holding MX blocks g, g + L, ..., so the input vector of the wave's
+// tokens is loaded into registers once and reused for every row it visits.
 //
-//  k_gemv_gateup: g = W1_e x, u = W3_e x for the tokens routed to e, then the
-//                 gated activation, h -> H[position][F] (fp32).  The shared
-//                 experts' bf16 gate/up rows run as extra blocks of the same
-//                 launch (all tokens), h -> Hs[t][s*F + row].
-//  k_gemv_down:   y = weight * (W2_e h) -> Y[position][d]; shared experts'
-//                 down rows (summed over s, unweighted) -> Ysh[t][d].
+// Three launches, each scheduling its biggest independent work first:
+//   k_front       shared experts' gate/up (bf16) + router logits
+//   k_gemv_gateup shared experts' down (bf16) + routed gate/up + activation
+//   k_gemv_down   routed down, times the routing weight -> slot rows
 #include "common.h"
+#include "router_dev.h"
 
 namespace moe {
 
-constexpr int kWaves = 4;         // waves per block
-constexpr int kRowsPerWave = 8;   // rows a wave owns in a block
-constexpr int kRowsPerBlock = kWaves * kRowsPerWave;
-constexpr int kR = 4;             // MXFP4 rows whose loads are in flight together
-constexpr int kXB = 2;            // MXFP4 blocks per lane per row (row width <= 4096)
-constexpr int kSB = 8;            // bf16 16-byte blocks per lane per row (<= 4096)
+constexpr int kWaves = 4;  // waves per block (256 threads)
+constexpr int kSB = 8;     // bf16 16-byte blocks per lane per row (row width <= 4096)
 
 struct GemvParams {
     Shape s;
     const uint16_t *x;
+    const float *Wr;
     const uint8_t *w1q, *w1s, *w3q, *w3s, *w2q, *w2s;
     const uint16_t *sh1, *sh3, *sh2;
     Work w;
-    int include_shared;
-    int tiles13;        // row tiles per routed expert, gate/up (F rows)
-    int tiles2;         // row tiles per routed expert, down (d rows)
-    int routed_blocks;  // max_active * tiles
+    int n_sh13;   // shared gate/up blocks (front kernel)
+    int n_router; // router blocks (front kernel)
+    int n_sh2;    // shared down blocks (gate/up kernel)
+    int tiles13;  // routed gate/up row tiles per expert
+    int tiles2;   // routed down row tiles per expert
 };
 
 __device__ __forceinline__ uint4 ld16(const void *p) { return *reinterpret_cast<const uint4 *>(p); }
 
-// lane's two MX blocks of bf16 input row `src` (d wide) -> 2 x 16 dwords
-__device__ __forceinline__ void load_x_fp4cols(const uint16_t *src, int nb, int lane,
-                                               uint32_t (&xr)[kXB][16])
+template <int CTRL>
+__device__ __forceinline__ float dppf(float v)
 {
-#pragma unroll
-    for (int b = 0; b < kXB; b++) {
-        const int blk = lane + 64 * b;
-        if (src && blk < nb) {
-            const uint4 *p = reinterpret_cast<const uint4 *>(src + blk * 32);
-#pragma unroll
-            for (int c = 0; c < 4; c++) {
-                const uint4 v = p[c];
-                xr[b][4 * c + 0] = v.x;
-                xr[b][4 * c + 1] = v.y;
-                xr[b][4 * c + 2] = v.z;
-                xr[b][4 * c + 3] = v.w;
-            }
-        } else {
-#pragma unroll
-            for (int c = 0; c < 16; c++) xr[b][c] = 0u;
-        }
-    }
+    return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), CTRL, 0xF, 0xF, true));
 }
 
-// ------------------------------------------------------------ gate / up
-
-template <int NT>
-__device__ __forceinline__ void gateup_routed(const GemvParams &p, int blk)
+// all-reduce sum over groups of L consecutive lanes (L = 16, 32, 64)
+template <int L>
+__device__ __forceinline__ float group_sum(float v)
 {
-    const Shape &s = p.s;
-    const int slot = blk / p.tiles13, tile = blk % p.tiles13;
-    if (slot >= p.w.meta[0]) return;
-    const int e = p.w.active[slot];
-    const int n = p.w.counts[e], base = p.w.offsets[e];
-    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-    const int d = s.d, F = s.F, nb = d / 32;
-    const size_t qrow = (size_t)d / 2, srow = (size_t)d / 32;
-    const uint8_t *q1 = p.w1q + (size_t)e * F * qrow, *s1 = p.w1s + (size_t)e * F * srow;
-    const uint8_t *q3 = p.w3q + (size_t)e * F * qrow, *s3 = p.w3s + (size_t)e * F * srow;
-    float *H = reinterpret_cast<float *>(p.w.H);
-    const int rbeg = tile * kRowsPerBlock + wave * kRowsPerWave;
-    for (int c0 = 0; c0 < n; c0 += NT) {
-        uint32_t xr[NT][kXB][16];
-#pragma unroll
-        for (int tt = 0; tt < NT; tt++) {
-            const int i = c0 + tt;
-            const uint16_t *src = i < n ? p.x + (size_t)p.w.pos_tok[base + i] * d : nullptr;
-            load_x_fp4cols(src, nb, lane, xr[tt]);
-        }
-        for (int r0 = rbeg; r0 < rbeg + kRowsPerWave; r0 += kR) {
-            uint4 qa[kR][kXB], qb[kR][kXB];
-            uint32_t sa[kR][kXB], sb[kR][kXB];
-#pragma unroll
-            for (int rr = 0; rr < kR; rr++) {
-                const int row = r0 + rr;
-#pragma unroll
-                for (int b = 0; b < kXB; b++) {
-                    const int bc = lane + 64 * b;
-                    if (row < F && bc < nb) {
-                        qa[rr][b] = ld16(q1 + row * qrow + bc * 16);
-                        qb[rr][b] = ld16(q3 + row * qrow + bc * 16);
-                        sa[rr][b] = s1[row * srow + bc];
-                        sb[rr][b] = s3[row * srow + bc];
-                    } else {
-                        qa[rr][b] = qb[rr][b] = make_uint4(0, 0, 0, 0);
-                        sa[rr][b] = sb[rr][b] = 255u;
-                    }
-                }
-            }
-            float g[kR][NT], u[kR][NT];
-#pragma unroll
-            for (int rr = 0; rr < kR; rr++) {
-#pragma unroll
-                for (int tt = 0; tt < NT; tt++) {
-                    float ga = 0.0f, ua = 0.0f;
-#pragma unroll
-                    for (int b = 0; b < kXB; b++) {
-                        const float pg = fp4x32_dot_bf16(qa[rr][b], xr[tt][b]);
-                        const float pu = fp4x32_dot_bf16(qb[rr][b], xr[tt][b]);
-                        ga = sa[rr][b] == 255u ? ga : fmaf(pg, e8m0_to_f32(sa[rr][b]), ga);
-                        ua = sb[rr][b] == 255u ? ua : fmaf(pu, e8m0_to_f32(sb[rr][b]), ua);
-                    }
-                    g[rr][tt] = wave_sum(ga);
-                    u[rr][tt] = wave_sum(ua);
-                }
-            }
-            // lane rr*NT + tt owns output (rr, tt)
-            float gv = 0.0f, uv = 0.0f;
-#pragma unroll
-            for (int rr = 0; rr < kR; rr++)
-#pragma unroll
-                for (int tt = 0; tt < NT; tt++)
-                    if (lane == rr * NT + tt) {
-                        gv = g[rr][tt];
-                        uv = u[rr][tt];
-                    }
-            if (lane < kR * NT) {
-                const int rr = lane / NT, tt = lane % NT;
-                const int row = r0 + rr, i = c0 + tt;
-                if (row < F && i < n)
-                    H[(size_t)(base + i) * F + row] = gated_act(gv, uv, s.act, s.b1, s.b2);
-            }
-        }
-    }
+    v += dppf<0xB1>(v);   // quad_perm [1,0,3,2]
+    v += dppf<0x4E>(v);   // quad_perm [2,3,0,1]
+    v += dppf<0x141>(v);  // row_half_mirror
+    v += dppf<0x140>(v);  // row_mirror
+    if (L >= 32) v += __shfl_xor(v, 16, 64);
+    if (L >= 64) v += __shfl_xor(v, 32, 64);
+    return v;
 }
 
+// ------------------------------------------------------------ shared experts
+
+// gate/up of shared expert sidx, 2 rows per wave (8 per block), NT tokens at a time
 template <int NT>
-__device__ __forceinline__ void gateup_shared(const GemvParams &p, int blk)
+__device__ __forceinline__ void shared_gateup_tile(const GemvParams &p, int blk)
 {
     const Shape &s = p.s;
-    const int tiles = (s.F + kRowsPerBlock - 1) / kRowsPerBlock;
+    const int tiles = (s.F + 7) / 8;
     const int sidx = blk / tiles, tile = blk % tiles;
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-    const int d = s.d, F = s.F, T = s.T, nb = d / 8;
+    const int d = s.d, F = s.F, T = s.T, nb = d / 8, SF = s.S * F;
     const uint16_t *w1 = p.sh1 + (size_t)sidx * F * d;
     const uint16_t *w3 = p.sh3 + (size_t)sidx * F * d;
-    const int rbeg = tile * kRowsPerBlock + wave * kRowsPerWave;
-    const int SF = s.S * F;
+    const int r0 = tile * 8 + wave * 2;
+    uint4 wa[2][kSB], wb[2][kSB];
+#pragma unroll
+    for (int rr = 0; rr < 2; rr++) {
+        const int row = r0 + rr;
+#pragma unroll
+        for (int b = 0; b < kSB; b++) {
+            const int bc = lane + 64 * b;
+            const bool ok = row < F && bc < nb;
+            wa[rr][b] = ok ? ld16(w1 + (size_t)row * d + bc * 8) : make_uint4(0, 0, 0, 0);
+            wb[rr][b] = ok ? ld16(w3 + (size_t)row * d + bc * 8) : make_uint4(0, 0, 0, 0);
+        }
+    }
     for (int c0 = 0; c0 < T; c0 += NT) {
         uint32_t xr[NT][kSB][4];
 #pragma unroll
         for (int tt = 0; tt < NT; tt++) {
-            const int t = c0 + tt;
 #pragma unroll
             for (int b = 0; b < kSB; b++) {
                 const int bc = lane + 64 * b;
-                if (t < T && bc < nb) {
-                    const uint4 v = ld16(p.x + (size_t)t * d + bc * 8);
-                    xr[tt][b][0] = v.x; xr[tt][b][1] = v.y; xr[tt][b][2] = v.z; xr[tt][b][3] = v.w;
-                } else {
-                    xr[tt][b][0] = xr[tt][b][1] = xr[tt][b][2] = xr[tt][b][3] = 0u;
-                }
+                uint4 v = make_uint4(0, 0, 0, 0);
+                if (c0 + tt < T && bc < nb) v = ld16(p.x + (size_t)(c0 + tt) * d + bc * 8);
+                xr[tt][b][0] = v.x; xr[tt][b][1] = v.y; xr[tt][b][2] = v.z; xr[tt][b][3] = v.w;
             }
         }
-        for (int row = rbeg; row < rbeg + kRowsPerWave; row++) {
-            uint4 wa[kSB], wb[kSB];
 #pragma unroll
-            for (int b = 0; b < kSB; b++) {
-                const int bc = lane + 64 * b;
-                if (row < F && bc < nb) {
-                    wa[b] = ld16(w1 + (size_t)row * d + bc * 8);
-                    wb[b] = ld16(w3 + (size_t)row * d + bc * 8);
-                } else {
-                    wa[b] = wb[b] = make_uint4(0, 0, 0, 0);
-                }
-            }
+        for (int rr = 0; rr < 2; rr++) {
+            const int row = r0 + rr;
             float gv = 0.0f, uv = 0.0f;
 #pragma unroll
             for (int tt = 0; tt < NT; tt++) {
                 float ga = 0.0f, ua = 0.0f;
 #pragma unroll
                 for (int b = 0; b < kSB; b++) {
-                    ga = bf16x8_dot_bf16(wa[b], xr[tt][b], ga);
-                    ua = bf16x8_dot_bf16(wb[b], xr[tt][b], ua);
+                    ga = bf16x8_dot_bf16(wa[rr][b], xr[tt][b], ga);
+                    ua = bf16x8_dot_bf16(wb[rr][b], xr[tt][b], ua);
                 }
-                ga = wave_sum(ga);
-                ua = wave_sum(ua);
+                ga = group_sum<64>(ga);
+                ua = group_sum<64>(ua);
                 if (lane == tt) {
                     gv = ga;
                     uv = ua;
@@ -208,204 +119,333 @@ __device__ __forceinline__ void gateup_shared(const GemvParams &p, int blk)
     }
 }
 
+// down of shared expert sidx, 2 rows per wave (8 per block) -> Ysh[sidx][t][row]
 template <int NT>
-__global__ __launch_bounds__(256) void k_gemv_gateup(GemvParams p)
+__device__ __forceinline__ void shared_down_tile(const GemvParams &p, int blk)
 {
-    const int blk = blockIdx.x;
-    if (blk < p.routed_blocks) gateup_routed<NT>(p, blk);
-    else gateup_shared<NT>(p, blk - p.routed_blocks);
+    const Shape &s = p.s;
+    const int tiles = (s.d + 7) / 8;
+    const int sidx = blk / tiles, tile = blk % tiles;
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const int d = s.d, F = s.F, T = s.T, nb = F / 8, SF = s.S * F;
+    const uint16_t *w2 = p.sh2 + (size_t)sidx * d * F;
+    const int r0 = tile * 8 + wave * 2;
+    float *ysh = p.w.Ysh + (size_t)sidx * T * d;
+    uint4 wv[2][kSB];
+#pragma unroll
+    for (int rr = 0; rr < 2; rr++) {
+        const int row = r0 + rr;
+#pragma unroll
+        for (int b = 0; b < kSB; b++) {
+            const int bc = lane + 64 * b;
+            wv[rr][b] = (row < d && bc < nb) ? ld16(w2 + (size_t)row * F + bc * 8) : make_uint4(0, 0, 0, 0);
+        }
+    }
+    for (int c0 = 0; c0 < T; c0 += NT) {
+        float hr[NT][kSB][8];
+#pragma unroll
+        for (int tt = 0; tt < NT; tt++) {
+#pragma unroll
+            for (int b = 0; b < kSB; b++) {
+                const int bc = lane + 64 * b;
+                if (c0 + tt < T && bc < nb) {
+                    const float4 *src = reinterpret_cast<const float4 *>(
+                        p.w.Hs + (size_t)(c0 + tt) * SF + (size_t)sidx * F + bc * 8);
+                    const float4 v0 = src[0], v1 = src[1];
+                    hr[tt][b][0] = v0.x; hr[tt][b][1] = v0.y; hr[tt][b][2] = v0.z; hr[tt][b][3] = v0.w;
+                    hr[tt][b][4] = v1.x; hr[tt][b][5] = v1.y; hr[tt][b][6] = v1.z; hr[tt][b][7] = v1.w;
+                } else {
+#pragma unroll
+                    for (int c = 0; c < 8; c++) hr[tt][b][c] = 0.0f;
+                }
+            }
+        }
+#pragma unroll
+        for (int rr = 0; rr < 2; rr++) {
+            const int row = r0 + rr;
+            float yv = 0.0f;
+#pragma unroll
+            for (int tt = 0; tt < NT; tt++) {
+                float a = 0.0f;
+#pragma unroll
+                for (int b = 0; b < kSB; b++) a = bf16x8_dot_f32(wv[rr][b], hr[tt][b], a);
+                a = group_sum<64>(a);
+                if (lane == tt) yv = a;
+            }
+            if (lane < NT && row < d && c0 + lane < T) ysh[(size_t)(c0 + lane) * d + row] = yv;
+        }
+    }
 }
 
-// ------------------------------------------------------------------ down
+// ------------------------------------------------------------ routed experts
 
-template <int NT>
-__device__ __forceinline__ void down_routed(const GemvParams &p, int blk)
+// Gate/up of one routed expert for a tile of rows.  L lanes per row, so a
+// wave covers 64/L rows per load instruction; G such row groups are loaded
+// at once, before the token loop.  Lane g of a row holds MX blocks g + L*i.
+template <int NT, int L, int BPL, int G>
+__device__ __forceinline__ void routed_gateup_tile(const GemvParams &p, int blk)
 {
+    constexpr int RPI = 64 / L;        // rows per load instruction
+    constexpr int RPW = RPI * G;       // rows per wave
+    constexpr int RPB = RPW * kWaves;  // rows per block
+    const Shape &s = p.s;
+    const int slot = blk / p.tiles13, tile = blk % p.tiles13;
+    if (slot >= p.w.meta[0]) return;
+    const int e = p.w.active[slot];
+    const int n = p.w.counts[e], base = p.w.offsets[e];
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const int g = lane % L, rsub = lane / L;
+    const int d = s.d, F = s.F, nb = d / 32;
+    const size_t qrow = (size_t)d / 2, srow = (size_t)d / 32;
+    const uint8_t *q1 = p.w1q + (size_t)e * F * qrow, *s1 = p.w1s + (size_t)e * F * srow;
+    const uint8_t *q3 = p.w3q + (size_t)e * F * qrow, *s3 = p.w3s + (size_t)e * F * srow;
+    float *H = reinterpret_cast<float *>(p.w.H);
+    const int rw0 = tile * RPB + wave * RPW;
+    uint4 qa[G][BPL], qb[G][BPL];
+    uint32_t sa[G][BPL], sb[G][BPL];
+#pragma unroll
+    for (int gi = 0; gi < G; gi++) {
+        const int row = rw0 + gi * RPI + rsub;
+#pragma unroll
+        for (int i = 0; i < BPL; i++) {
+            const int bc = g + L * i;
+            const bool ok = row < F && bc < nb;
+            qa[gi][i] = ok ? ld16(q1 + row * qrow + bc * 16) : make_uint4(0, 0, 0, 0);
+            qb[gi][i] = ok ? ld16(q3 + row * qrow + bc * 16) : make_uint4(0, 0, 0, 0);
+            sa[gi][i] = ok ? s1[row * srow + bc] : 255u;
+            sb[gi][i] = ok ? s3[row * srow + bc] : 255u;
+        }
+    }
+    for (int c0 = 0; c0 < n; c0 += NT) {
+        uint32_t xr[NT][BPL][16];
+#pragma unroll
+        for (int tt = 0; tt < NT; tt++) {
+            const int i0 = c0 + tt;
+            const uint16_t *src = i0 < n ? p.x + (size_t)p.w.pos_tok[base + i0] * d : nullptr;
+#pragma unroll
+            for (int i = 0; i < BPL; i++) {
+                const int bc = g + L * i;
+                if (src && bc < nb) {
+                    const uint4 *q = reinterpret_cast<const uint4 *>(src + bc * 32);
+#pragma unroll
+                    for (int c = 0; c < 4; c++) {
+                        const uint4 v = q[c];
+                        xr[tt][i][4 * c + 0] = v.x; xr[tt][i][4 * c + 1] = v.y;
+                        xr[tt][i][4 * c + 2] = v.z; xr[tt][i][4 * c + 3] = v.w;
+                    }
+                } else {
+#pragma unroll
+                    for (int c = 0; c < 16; c++) xr[tt][i][c] = 0u;
+                }
+            }
+        }
+#pragma unroll
+        for (int gi = 0; gi < G; gi++) {
+            const int row = rw0 + gi * RPI + rsub;
+            float gv = 0.0f, uv = 0.0f;
+#pragma unroll
+            for (int tt = 0; tt < NT; tt++) {
+                float ga = 0.0f, ua = 0.0f;
+#pragma unroll
+                for (int i = 0; i < BPL; i++) {
+                    const float pg = fp4x32_dot_bf16(qa[gi][i], xr[tt][i]);
+                    const float pu = fp4x32_dot_bf16(qb[gi][i], xr[tt][i]);
+                    ga = sa[gi][i] == 255u ? ga : fmaf(pg, e8m0_to_f32(sa[gi][i]), ga);
+                    ua = sb[gi][i] == 255u ? ua : fmaf(pu, e8m0_to_f32(sb[gi][i]), ua);
+                    // keep each block's decode next to its use (register pressure)
+                    __builtin_amdgcn_sched_barrier(0);
+                }
+                ga = group_sum<L>(ga);
+                ua = group_sum<L>(ua);
+                if (g == tt) {
+                    gv = ga;
+                    uv = ua;
+                }
+            }
+            if (g < NT && row < F && c0 + g < n)
+                H[(size_t)(base + c0 + g) * F + row] = gated_act(gv, uv, s.act, s.b1, s.b2);
+        }
+    }
+}
+
+// Down of one routed expert for a tile of rows, times the routing weight.
+template <int NT, int L, int BPL, int G>
+__device__ __forceinline__ void routed_down_tile(const GemvParams &p, int blk)
+{
+    constexpr int RPI = 64 / L;
+    constexpr int RPW = RPI * G;
+    constexpr int RPB = RPW * kWaves;
     const Shape &s = p.s;
     const int slot = blk / p.tiles2, tile = blk % p.tiles2;
     if (slot >= p.w.meta[0]) return;
     const int e = p.w.active[slot];
     const int n = p.w.counts[e], base = p.w.offsets[e];
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const int g = lane % L, rsub = lane / L;
     const int d = s.d, F = s.F, nb = F / 32;
     const size_t qrow = (size_t)F / 2, srow = (size_t)F / 32;
     const uint8_t *q2 = p.w2q + (size_t)e * d * qrow, *s2 = p.w2s + (size_t)e * d * srow;
     const float *H = reinterpret_cast<const float *>(p.w.H);
-    const int rbeg = tile * kRowsPerBlock + wave * kRowsPerWave;
+    const int rw0 = tile * RPB + wave * RPW;
+    uint4 q[G][BPL];
+    uint32_t sc[G][BPL];
+#pragma unroll
+    for (int gi = 0; gi < G; gi++) {
+        const int row = rw0 + gi * RPI + rsub;
+#pragma unroll
+        for (int i = 0; i < BPL; i++) {
+            const int bc = g + L * i;
+            const bool ok = row < d && bc < nb;
+            q[gi][i] = ok ? ld16(q2 + row * qrow + bc * 16) : make_uint4(0, 0, 0, 0);
+            sc[gi][i] = ok ? s2[row * srow + bc] : 255u;
+        }
+    }
     for (int c0 = 0; c0 < n; c0 += NT) {
-        float hr[NT][kXB][32];
+        float hr[NT][BPL][32];
         float wt[NT];
 #pragma unroll
         for (int tt = 0; tt < NT; tt++) {
-            const int i = c0 + tt;
-            wt[tt] = i < n ? p.w.pos_w[base + i] : 0.0f;
+            const int i0 = c0 + tt;
+            wt[tt] = i0 < n ? p.w.pos_w[base + i0] : 0.0f;
 #pragma unroll
-            for (int b = 0; b < kXB; b++) {
-                const int bc = lane + 64 * b;
-                if (i < n && bc < nb) {
-                    const float4 *src = reinterpret_cast<const float4 *>(H + (size_t)(base + i) * F + bc * 32);
+            for (int i = 0; i < BPL; i++) {
+                const int bc = g + L * i;
+                if (i0 < n && bc < nb) {
+                    const float4 *src = reinterpret_cast<const float4 *>(H + (size_t)(base + i0) * F + bc * 32);
 #pragma unroll
                     for (int c = 0; c < 8; c++) {
                         const float4 v = src[c];
-                        hr[tt][b][4 * c + 0] = v.x;
-                        hr[tt][b][4 * c + 1] = v.y;
-                        hr[tt][b][4 * c + 2] = v.z;
-                        hr[tt][b][4 * c + 3] = v.w;
+                        hr[tt][i][4 * c + 0] = v.x; hr[tt][i][4 * c + 1] = v.y;
+                        hr[tt][i][4 * c + 2] = v.z; hr[tt][i][4 * c + 3] = v.w;
                     }
                 } else {
 #pragma unroll
-                    for (int c = 0; c < 32; c++) hr[tt][b][c] = 0.0f;
+                    for (int c = 0; c < 32; c++) hr[tt][i][c] = 0.0f;
                 }
             }
         }
-        for (int r0 = rbeg; r0 < rbeg + kRowsPerWave; r0 += kR) {
-            uint4 q[kR][kXB];
-            uint32_t sc[kR][kXB];
 #pragma unroll
-            for (int rr = 0; rr < kR; rr++) {
-                const int row = r0 + rr;
-#pragma unroll
-                for (int b = 0; b < kXB; b++) {
-                    const int bc = lane + 64 * b;
-                    if (row < d && bc < nb) {
-                        q[rr][b] = ld16(q2 + row * qrow + bc * 16);
-                        sc[rr][b] = s2[row * srow + bc];
-                    } else {
-                        q[rr][b] = make_uint4(0, 0, 0, 0);
-                        sc[rr][b] = 255u;
-                    }
-                }
-            }
+        for (int gi = 0; gi < G; gi++) {
+            const int row = rw0 + gi * RPI + rsub;
             float yv = 0.0f;
 #pragma unroll
-            for (int rr = 0; rr < kR; rr++) {
+            for (int tt = 0; tt < NT; tt++) {
+                float a = 0.0f;
 #pragma unroll
-                for (int tt = 0; tt < NT; tt++) {
-                    float a = 0.0f;
-#pragma unroll
-                    for (int b = 0; b < kXB; b++) {
-                        const float pp = fp4x32_dot_f32(q[rr][b], hr[tt][b]);
-                        a = sc[rr][b] == 255u ? a : fmaf(pp, e8m0_to_f32(sc[rr][b]), a);
-                    }
-                    a = wave_sum(a);
-                    if (lane == rr * NT + tt) yv = a;
+                for (int i = 0; i < BPL; i++) {
+                    const float pp = fp4x32_dot_f32(q[gi][i], hr[tt][i]);
+                    a = sc[gi][i] == 255u ? a : fmaf(pp, e8m0_to_f32(sc[gi][i]), a);
+                    __builtin_amdgcn_sched_barrier(0);
                 }
+                a = group_sum<L>(a);
+                if (g == tt) yv = a * wt[tt];
             }
-            if (lane < kR * NT) {
-                const int rr = lane / NT, tt = lane % NT;
-                const int row = r0 + rr, i = c0 + tt;
-                if (row < d && i < n) p.w.Y[(size_t)(base + i) * d + row] = wt[tt] * yv;
-            }
+            if (g < NT && row < d && c0 + g < n) p.w.Y[(size_t)(base + c0 + g) * d + row] = yv;
         }
     }
 }
 
-template <int NT>
-__device__ __forceinline__ void down_shared(const GemvParams &p, int tile)
-{
-    const Shape &s = p.s;
-    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-    const int d = s.d, F = s.F, T = s.T, nb = F / 8, SF = s.S * F;
-    const int rbeg = tile * kRowsPerBlock + wave * kRowsPerWave;
-    for (int c0 = 0; c0 < T; c0 += NT) {
-        float acc[kRowsPerWave][NT];
-#pragma unroll
-        for (int r = 0; r < kRowsPerWave; r++)
-#pragma unroll
-            for (int tt = 0; tt < NT; tt++) acc[r][tt] = 0.0f;
-        for (int si = 0; si < s.S; si++) {
-            float hr[NT][kSB][8];
-#pragma unroll
-            for (int tt = 0; tt < NT; tt++) {
-                const int t = c0 + tt;
-#pragma unroll
-                for (int b = 0; b < kSB; b++) {
-                    const int bc = lane + 64 * b;
-                    if (t < T && bc < nb) {
-                        const float4 *src = reinterpret_cast<const float4 *>(p.w.Hs + (size_t)t * SF + (size_t)si * F + bc * 8);
-                        const float4 v0 = src[0], v1 = src[1];
-                        hr[tt][b][0] = v0.x; hr[tt][b][1] = v0.y; hr[tt][b][2] = v0.z; hr[tt][b][3] = v0.w;
-                        hr[tt][b][4] = v1.x; hr[tt][b][5] = v1.y; hr[tt][b][6] = v1.z; hr[tt][b][7] = v1.w;
-                    } else {
-#pragma unroll
-                        for (int c = 0; c < 8; c++) hr[tt][b][c] = 0.0f;
-                    }
-                }
-            }
-            const uint16_t *w2 = p.sh2 + (size_t)si * d * F;
-#pragma unroll 2
-            for (int r = 0; r < kRowsPerWave; r++) {
-                const int row = rbeg + r;
-                uint4 wv[kSB];
-#pragma unroll
-                for (int b = 0; b < kSB; b++) {
-                    const int bc = lane + 64 * b;
-                    wv[b] = (row < d && bc < nb) ? ld16(w2 + (size_t)row * F + bc * 8) : make_uint4(0, 0, 0, 0);
-                }
-#pragma unroll
-                for (int tt = 0; tt < NT; tt++) {
-                    float a = 0.0f;
-#pragma unroll
-                    for (int b = 0; b < kSB; b++) a = bf16x8_dot_f32(wv[b], hr[tt][b], a);
-                    acc[r][tt] += a;  // per-lane partial; reduced once below
-                }
-            }
-        }
-#pragma unroll
-        for (int r = 0; r < kRowsPerWave; r++) {
-            const int row = rbeg + r;
-#pragma unroll
-            for (int tt = 0; tt < NT; tt++) {
-                const float v = wave_sum(acc[r][tt]);
-                if (lane == 0 && row < d && c0 + tt < T) p.w.Ysh[(size_t)(c0 + tt) * d + row] = v;
-            }
-        }
-    }
-}
+// ---------------------------------------------------------------- kernels
 
 template <int NT>
-__global__ __launch_bounds__(256) void k_gemv_down(GemvParams p)
+__global__ __launch_bounds__(256) void k_front(GemvParams p)
 {
     const int blk = blockIdx.x;
-    if (blk < p.routed_blocks) down_routed<NT>(p, blk);
-    else down_shared<NT>(p, blk - p.routed_blocks);
+    if (blk < p.n_sh13) {
+        shared_gateup_tile<NT>(p, blk);
+    } else {
+        const int e = (blk - p.n_sh13) * kWaves + (threadIdx.x >> 6);
+        if (e < p.s.E) router_row(p.s.T, p.s.E, p.s.d, p.x, p.Wr, p.w.logits, e);
+    }
 }
 
-template <int NT>
-static void launch_nt(const GemvParams &base, hipStream_t stream, hipEvent_t const *ev2)
+template <int NT, int L, int BPL, int G>
+__global__ __launch_bounds__(256) void k_gemv_gateup(GemvParams p)
 {
-    const Shape &s = base.s;
-    const int max_active = min(s.E, s.T * s.k);
-    GemvParams p = base;
-    p.tiles13 = (s.F + kRowsPerBlock - 1) / kRowsPerBlock;
-    p.tiles2 = (s.d + kRowsPerBlock - 1) / kRowsPerBlock;
-    const int shared13 = p.include_shared ? s.S * p.tiles13 : 0;
-    const int shared2 = (p.include_shared && s.S > 0) ? p.tiles2 : 0;
-    p.routed_blocks = max_active * p.tiles13;
-    if (p.routed_blocks + shared13 > 0)
-        k_gemv_gateup<NT><<<p.routed_blocks + shared13, 256, 0, stream>>>(p);
-    if (ev2) (void)hipEventRecord(ev2[0], stream);
-    p.routed_blocks = max_active * p.tiles2;
-    if (p.routed_blocks + shared2 > 0)
-        k_gemv_down<NT><<<p.routed_blocks + shared2, 256, 0, stream>>>(p);
-    if (ev2) (void)hipEventRecord(ev2[1], stream);
+    const int blk = blockIdx.x;
+    if (blk < p.n_sh2) shared_down_tile<NT>(p, blk);
+    else routed_gateup_tile<NT, L, BPL, G>(p, blk - p.n_sh2);
 }
 
-hipError_t launch_gemv_experts(const Shape &s, const uint16_t *x, const uint8_t *w1q,
-                               const uint8_t *w1s, const uint8_t *w3q, const uint8_t *w3s,
-                               const uint8_t *w2q, const uint8_t *w2s, const uint16_t *sh1,
-                               const uint16_t *sh3, const uint16_t *sh2, int include_shared,
-                               const Work &w, hipStream_t stream, hipEvent_t const *ev2)
+template <int NT, int L, int BPL, int G>
+__global__ __launch_bounds__(256) void k_gemv_down(GemvParams p)
+{
+    routed_down_tile<NT, L, BPL, G>(p, blockIdx.x);
+}
+
+// ---------------------------------------------------------------- launches
+
+static GemvParams make_params(const Shape &s, const uint16_t *x, const Weights &wt, const Work &w)
 {
     GemvParams p;
     p.s = s;
     p.x = x;
-    p.w1q = w1q; p.w1s = w1s; p.w3q = w3q; p.w3s = w3s; p.w2q = w2q; p.w2s = w2s;
-    p.sh1 = sh1; p.sh3 = sh3; p.sh2 = sh2;
+    p.Wr = wt.router_w;
+    p.w1q = wt.w1q; p.w1s = wt.w1s; p.w3q = wt.w3q; p.w3s = wt.w3s; p.w2q = wt.w2q; p.w2s = wt.w2s;
+    p.sh1 = wt.sh1; p.sh3 = wt.sh3; p.sh2 = wt.sh2;
     p.w = w;
-    p.include_shared = include_shared && s.S > 0;
-    if (s.T == 1) launch_nt<1>(p, stream, ev2);
-    else launch_nt<2>(p, stream, ev2);
+    p.n_sh13 = p.n_router = p.n_sh2 = 0;
+    p.tiles13 = p.tiles2 = 0;
+    return p;
+}
+
+hipError_t launch_front(const Shape &s, const uint16_t *x, const Weights &wt, int do_router,
+                        int include_shared, const Work &w, hipStream_t stream)
+{
+    GemvParams p = make_params(s, x, wt, w);
+    p.n_sh13 = (include_shared && s.S > 0) ? s.S * ((s.F + 7) / 8) : 0;
+    p.n_router = do_router ? (s.E + kWaves - 1) / kWaves : 0;
+    const int nblk = p.n_sh13 + p.n_router;
+    if (nblk == 0) return hipSuccess;
+    if (s.T == 1) k_front<1><<<nblk, 256, 0, stream>>>(p);
+    else k_front<2><<<nblk, 256, 0, stream>>>(p);
+    return hipGetLastError();
+}
+
+template <int NT, int L, int BPL, int G>
+static void gateup_launch(GemvParams p, int max_active, hipStream_t stream)
+{
+    constexpr int RPB = (64 / L) * G * kWaves;
+    p.tiles13 = (p.s.F + RPB - 1) / RPB;
+    const int nblk = p.n_sh2 + max_active * p.tiles13;
+    if (nblk > 0) k_gemv_gateup<NT, L, BPL, G><<<nblk, 256, 0, stream>>>(p);
+}
+
+template <int NT, int L, int BPL, int G>
+static void down_launch(GemvParams p, int max_active, hipStream_t stream)
+{
+    constexpr int RPB = (64 / L) * G * kWaves;
+    p.tiles2 = (p.s.d + RPB - 1) / RPB;
+    const int nblk = max_active * p.tiles2;
+    if (nblk > 0) k_gemv_down<NT, L, BPL, G><<<nblk, 256, 0, stream>>>(p);
+}
+
+hipError_t launch_gemv_experts(const Shape &s, const uint16_t *x, const Weights &wt,
+                               int include_shared, const Work &w, hipStream_t stream,
+                               hipEvent_t const *ev2)
+{
+    GemvParams p = make_params(s, x, wt, w);
+    const int max_active = min(s.E, s.T * s.k);
+    p.n_sh2 = (include_shared && s.S > 0) ? s.S * ((s.d + 7) / 8) : 0;
+    const int nb13 = s.d / 32, nb2 = s.F / 32;
+    // The weights of a tile are loaded into registers once; tokens routed to
+    // the expert are then processed one at a time (inputs through the cache).
+    // gate/up: 16 lanes per row, ceil(nb/16) MX blocks per lane
+    const int bpl = (nb13 + 15) / 16;
+    if (bpl <= 1) gateup_launch<1, 16, 1, 1>(p, max_active, stream);
+    else if (bpl <= 2) gateup_launch<1, 16, 2, 1>(p, max_active, stream);
+    else if (bpl <= 4) gateup_launch<1, 16, 4, 1>(p, max_active, stream);
+    else if (bpl <= 6) gateup_launch<1, 16, 6, 1>(p, max_active, stream);
+    else if (bpl <= 7) gateup_launch<1, 16, 7, 1>(p, max_active, stream);
+    else gateup_launch<1, 16, 8, 1>(p, max_active, stream);
+    if (ev2) (void)hipEventRecord(ev2[0], stream);
+    // down: 32 lanes per row, ceil(nb/32) MX blocks per lane, 4 row pairs per wave
+    const int bpl2 = (nb2 + 31) / 32;
+    if (bpl2 <= 1) down_launch<1, 32, 1, 4>(p, max_active, stream);
+    else if (bpl2 <= 2) down_launch<1, 32, 2, 4>(p, max_active, stream);
+    else if (bpl2 <= 3) down_launch<1, 32, 3, 4>(p, max_active, stream);
+    else down_launch<1, 32, 4, 4>(p, max_active, stream);
+    if (ev2) (void)hipEventRecord(ev2[1], stream);
     return hipGetLastError();
 }
 

@@ -106,7 +106,7 @@ size_t carve(const Shape &s, char *base, Work *w)
     v.H = (void *)take(T * k * (size_t)s.F * 4);
     v.Hs = (float *)take(T * (size_t)s.S * s.F * 4);
     v.Y = (float *)take(T * k * (size_t)s.d * 4);
-    v.Ysh = (float *)take(T * (size_t)s.d * 4);
+    v.Ysh = (float *)take((size_t)s.S * T * s.d * 4);
     if (w) *w = v;
     return off;
 }
@@ -135,6 +135,17 @@ moe_status check_call(const moe_layer_desc *d, const uint16_t *x, int32_t T, voi
     return MOE_OK;
 }
 
+moe::Weights weights_of(const moe_layer_desc *d)
+{
+    moe::Weights w;
+    w.router_w = d->router_w;
+    w.router_bias = d->router_bias;
+    w.w1q = d->w1_q; w.w1s = d->w1_s; w.w3q = d->w3_q; w.w3s = d->w3_s;
+    w.w2q = d->w2_q; w.w2s = d->w2_s;
+    w.sh1 = d->sh_w1; w.sh3 = d->sh_w3; w.sh2 = d->sh_w2;
+    return w;
+}
+
 moe_status check_out(int32_t out_mode, const uint16_t *out_bf16, const float *out_f32)
 {
     if (out_mode != MOE_OUT_BF16 && out_mode != MOE_OUT_F32 && out_mode != MOE_OUT_BOTH)
@@ -156,20 +167,35 @@ hipError_t mark(hipEvent_t const *ev, int i, hipStream_t st)
     return ev ? hipEventRecord(ev[i], st) : hipSuccess;
 }
 
-moe_status run_experts(const moe_layer_desc *d, const Shape &s, const uint16_t *x,
-                       int include_shared, const Work &w, int32_t out_mode, uint16_t *out_bf16,
-                       float *out_f32, hipStream_t st, hipEvent_t const *ev = nullptr)
+// The launch sequence shared by every entry point:
+//   front    router logits (do_router) + shared experts' gate/up (GEMV path)
+//   dispatch top-k (do_topk) + histogram / scan / permutation
+//   experts  gate/up + activation, down + routing weight (GEMV or MFMA path)
+//   combine  fp32 and/or bf16 output
+// ev (optional, 6 events) marks the phase boundaries.
+moe_status run_layer(const moe_layer_desc *d, const Shape &s, const uint16_t *x, int do_router,
+                     int include_shared, int32_t *ids, float *wts, int32_t *counts_out,
+                     const Work &w, int32_t out_mode, uint16_t *out_bf16, float *out_f32,
+                     hipStream_t st, hipEvent_t const *ev, bool experts)
 {
     const int path = path_of(d, s.T);
+    const moe::Weights wt = weights_of(d);
+    const int shared = include_shared && s.S > 0;
+    MOE_TRY(mark(ev, 0, st));
+    if (do_router || (experts && shared && path == MOE_PATH_GEMV))
+        MOE_TRY(moe::launch_front(s, x, wt, do_router, experts && shared && path == MOE_PATH_GEMV,
+                                  w, st));
+    MOE_TRY(mark(ev, 1, st));
+    MOE_TRY(moe::launch_dispatch(s, do_router, w.logits, d->router_bias, ids, wts, counts_out, w,
+                                 st));
+    MOE_TRY(mark(ev, 2, st));
+    if (!experts) return MOE_OK;
     if (path == MOE_PATH_GEMV) {
-        MOE_TRY(moe::launch_gemv_experts(s, x, d->w1_q, d->w1_s, d->w3_q, d->w3_s, d->w2_q,
-                                         d->w2_s, d->sh_w1, d->sh_w3, d->sh_w2, include_shared, w,
-                                         st, ev ? ev + 3 : nullptr));
+        MOE_TRY(moe::launch_gemv_experts(s, x, wt, shared, w, st, ev ? ev + 3 : nullptr));
     } else {
-        MOE_TRY(moe::launch_mfma_experts(s, x, d, include_shared, w, st, ev ? ev + 3 : nullptr));
+        MOE_TRY(moe::launch_mfma_experts(s, x, d, shared, w, st, ev ? ev + 3 : nullptr));
     }
-    MOE_TRY(moe::launch_combine(s, include_shared && s.S > 0, w,
-                                out_mode != MOE_OUT_F32 ? out_bf16 : nullptr,
+    MOE_TRY(moe::launch_combine(s, shared, w, out_mode != MOE_OUT_F32 ? out_bf16 : nullptr,
                                 out_mode != MOE_OUT_BF16 ? out_f32 : nullptr, st));
     MOE_TRY(mark(ev, 5, st));
     return MOE_OK;
@@ -202,10 +228,8 @@ moe_status moe_route(const moe_layer_desc *desc, const uint16_t *x, int32_t T, i
     const Shape s = shape_of(desc, T);
     Work w;
     carve(s, (char *)ws, &w);
-    hipStream_t hs = (hipStream_t)stream;
-    MOE_TRY(moe::launch_router_logits(s, x, desc->router_w, w.logits, hs));
-    MOE_TRY(moe::launch_dispatch(s, 1, w.logits, desc->router_bias, ids, weights, counts, w, hs));
-    return MOE_OK;
+    return run_layer(desc, s, x, 1, 0, ids, weights, counts, w, MOE_OUT_F32, nullptr, nullptr,
+                     (hipStream_t)stream, nullptr, false);
 }
 
 moe_status moe_expert_forward(const moe_layer_desc *desc, const uint16_t *x, int32_t T,
@@ -223,10 +247,9 @@ moe_status moe_expert_forward(const moe_layer_desc *desc, const uint16_t *x, int
     const Shape s = shape_of(desc, T);
     Work w;
     carve(s, (char *)ws, &w);
-    hipStream_t hs = (hipStream_t)stream;
-    MOE_TRY(moe::launch_dispatch(s, 0, nullptr, nullptr, const_cast<int32_t *>(ids),
-                                 const_cast<float *>(weights), nullptr, w, hs));
-    return run_experts(desc, s, x, include_shared, w, out_mode, out_bf16, out_f32, hs);
+    return run_layer(desc, s, x, 0, include_shared, const_cast<int32_t *>(ids),
+                     const_cast<float *>(weights), nullptr, w, out_mode, out_bf16, out_f32,
+                     (hipStream_t)stream, nullptr, true);
 }
 
 moe_status moe_layer(const moe_layer_desc *desc, const uint16_t *x, int32_t T, uint16_t *out_bf16,
@@ -241,12 +264,8 @@ moe_status moe_layer(const moe_layer_desc *desc, const uint16_t *x, int32_t T, u
     const Shape s = shape_of(desc, T);
     Work w;
     carve(s, (char *)ws, &w);
-    int32_t *ids = ids_opt ? ids_opt : w.ids;
-    float *wts = weights_opt ? weights_opt : w.wts;
-    hipStream_t hs = (hipStream_t)stream;
-    MOE_TRY(moe::launch_router_logits(s, x, desc->router_w, w.logits, hs));
-    MOE_TRY(moe::launch_dispatch(s, 1, w.logits, desc->router_bias, ids, wts, counts_opt, w, hs));
-    return run_experts(desc, s, x, 1, w, out_mode, out_bf16, out_f32, hs);
+    return run_layer(desc, s, x, 1, 1, ids_opt ? ids_opt : w.ids, weights_opt ? weights_opt : w.wts,
+                     counts_opt, w, out_mode, out_bf16, out_f32, (hipStream_t)stream, nullptr, true);
 }
 
 moe_status moe_layer_timed(const moe_layer_desc *desc, const uint16_t *x, int32_t T,
@@ -261,17 +280,11 @@ moe_status moe_layer_timed(const moe_layer_desc *desc, const uint16_t *x, int32_
     for (int i = 0; i < MOE_TIMED_EVENTS; i++)
         if (!events[i]) return MOE_EINVAL;
     (void)hipGetLastError();
-    hipEvent_t const *ev = reinterpret_cast<hipEvent_t const *>(events);
     const Shape s = shape_of(desc, T);
     Work w;
     carve(s, (char *)ws, &w);
-    hipStream_t hs = (hipStream_t)stream;
-    MOE_TRY(mark(ev, 0, hs));
-    MOE_TRY(moe::launch_router_logits(s, x, desc->router_w, w.logits, hs));
-    MOE_TRY(mark(ev, 1, hs));
-    MOE_TRY(moe::launch_dispatch(s, 1, w.logits, desc->router_bias, w.ids, w.wts, nullptr, w, hs));
-    MOE_TRY(mark(ev, 2, hs));
-    return run_experts(desc, s, x, 1, w, out_mode, out_bf16, out_f32, hs, ev);
+    return run_layer(desc, s, x, 1, 1, w.ids, w.wts, nullptr, w, out_mode, out_bf16, out_f32,
+                     (hipStream_t)stream, reinterpret_cast<hipEvent_t const *>(events), true);
 }
 
 const char *moe_status_str(int32_t status)

@@ -194,3 +194,35 @@ def test_k3_prefill_T4096_sampled():
     assert_close(out_f[sample], rout, "T4096 sampled")
     assert np.array_equal(out_b, bf16_rne(out_f))
     del gl
+
+
+def test_graph_replay_matches_eager():
+    """The layer captured in a HIP graph gives the eager result on every replay
+    (replays interleaved with eager calls on other inputs)."""
+    import quantized_expert_gemv_sigmoid_amd as moe
+    import synth.device as sdev
+    shape = synth.LayerShape(n_experts=40, top_k=6, n_shared=2, d_model=320, d_ffn=416)
+    gl = make_gpu_layer(shape, 51)
+    T = 3
+    xa, _, _ = tokens(gl, T)
+    xb = synth.x_tokens(shape, 51, 0, T, first_token=100)
+    ref_a, _, _, _, _ = run_layer(gl, xa)
+    ref_b, _, _, _, _ = run_layer(gl, xb)
+    xd = sdev.tokens_to_device(xa)
+    xo = sdev.tokens_to_device(xb)
+    ws = torch.empty(moe.workspace_bytes(gl.desc, T), dtype=torch.uint8, device="cuda")
+    out = torch.empty((T, shape.d_model), dtype=torch.float32, device="cuda")
+    out_o = torch.empty_like(out)
+    moe.layer(gl.desc, xd, T, None, out, moe.OUT_F32, ws)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        moe.layer(gl.desc, xd, T, None, out, moe.OUT_F32, ws)
+    for r in range(4):
+        out.zero_()
+        g.replay()
+        torch.cuda.synchronize()
+        assert np.array_equal(out.cpu().numpy(), ref_a), f"replay {r} differs from eager"
+        moe.layer(gl.desc, xo, T, None, out_o, moe.OUT_F32, ws)  # eager work in between
+        torch.cuda.synchronize()
+        assert np.array_equal(out_o.cpu().numpy(), ref_b)
