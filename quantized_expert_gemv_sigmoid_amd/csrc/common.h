@@ -38,6 +38,7 @@ struct Work {
     float *Hs;         // [T][S*F] shared activations (fp32)
     float *Y;          // [T*k][d] weighted expert outputs
     float *Ysh;        // [S][T][d] shared experts' outputs
+    void *extra;       // MFMA path: router weights split into 3 bf16 parts [E][3d]
 };
 
 struct Shape {
@@ -198,6 +199,16 @@ hipError_t launch_dispatch(const Shape &s, int do_topk, const float *logits, con
 // dequant-fused GEMV experts: shared down + routed gate/up + activation, then
 // routed down + weight.  ev2 (optional): events recorded after each launch.
 hipError_t launch_gemv_experts(const Shape &s, const uint16_t *x, const Weights &wt,
+                               int include_shared, const Work &w, hipStream_t stream,
+                               hipEvent_t const *ev2);
+
+// grouped MFMA GEMM path (prefill): router logits via 3-part bf16 split of
+// the router weights, and the experts (shared + routed gate/up, then down)
+bool mfma_supported(const Shape &s);
+size_t mfma_extra_workspace(const Shape &s);
+hipError_t launch_mfma_router(const Shape &s, const uint16_t *x, const Weights &wt, const Work &w,
+                              hipStream_t stream);
+hipError_t launch_mfma_experts(const Shape &s, const uint16_t *x, const Weights &wt,
                                int include_shared, const Work &w, hipStream_t stream,
                                hipEvent_t const *ev2);
 

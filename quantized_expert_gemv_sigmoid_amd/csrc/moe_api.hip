@@ -6,14 +6,6 @@
 #include "../../include/moe.h"
 #include "common.h"
 
-namespace moe {
-hipError_t launch_mfma_experts(const Shape &s, const uint16_t *x, const moe_layer_desc *d,
-                               int include_shared, const Work &w, hipStream_t stream,
-                               hipEvent_t const *ev2);
-size_t mfma_extra_workspace(const Shape &s);
-bool mfma_supported(const Shape &s);
-}  // namespace moe
-
 namespace {
 
 using moe::Shape;
@@ -107,6 +99,7 @@ size_t carve(const Shape &s, char *base, Work *w)
     v.Hs = (float *)take(T * (size_t)s.S * s.F * 4);
     v.Y = (float *)take(T * k * (size_t)s.d * 4);
     v.Ysh = (float *)take((size_t)s.S * T * s.d * 4);
+    v.extra = (void *)take(moe::mfma_extra_workspace(s));
     if (w) *w = v;
     return off;
 }
@@ -114,9 +107,7 @@ size_t carve(const Shape &s, char *base, Work *w)
 size_t ws_needed(const moe_layer_desc *d, int32_t T)
 {
     const Shape s = shape_of(d, T < 1 ? 1 : T);
-    size_t n = carve(s, nullptr, nullptr);
-    n += moe::mfma_extra_workspace(s);
-    return n;
+    return carve(s, nullptr, nullptr);
 }
 
 moe_status check_call(const moe_layer_desc *d, const uint16_t *x, int32_t T, void *ws,
@@ -182,9 +173,12 @@ moe_status run_layer(const moe_layer_desc *d, const Shape &s, const uint16_t *x,
     const moe::Weights wt = weights_of(d);
     const int shared = include_shared && s.S > 0;
     MOE_TRY(mark(ev, 0, st));
-    if (do_router || (experts && shared && path == MOE_PATH_GEMV))
-        MOE_TRY(moe::launch_front(s, x, wt, do_router, experts && shared && path == MOE_PATH_GEMV,
-                                  w, st));
+    const int front_shared = experts && shared && path == MOE_PATH_GEMV;
+    if (do_router && path == MOE_PATH_MFMA) {
+        MOE_TRY(moe::launch_mfma_router(s, x, wt, w, st));
+    } else if (do_router || front_shared) {
+        MOE_TRY(moe::launch_front(s, x, wt, do_router, front_shared, w, st));
+    }
     MOE_TRY(mark(ev, 1, st));
     MOE_TRY(moe::launch_dispatch(s, do_router, w.logits, d->router_bias, ids, wts, counts_out, w,
                                  st));
@@ -193,7 +187,7 @@ moe_status run_layer(const moe_layer_desc *d, const Shape &s, const uint16_t *x,
     if (path == MOE_PATH_GEMV) {
         MOE_TRY(moe::launch_gemv_experts(s, x, wt, shared, w, st, ev ? ev + 3 : nullptr));
     } else {
-        MOE_TRY(moe::launch_mfma_experts(s, x, d, shared, w, st, ev ? ev + 3 : nullptr));
+        MOE_TRY(moe::launch_mfma_experts(s, x, wt, shared, w, st, ev ? ev + 3 : nullptr));
     }
     MOE_TRY(moe::launch_combine(s, shared, w, out_mode != MOE_OUT_F32 ? out_bf16 : nullptr,
                                 out_mode != MOE_OUT_BF16 ? out_f32 : nullptr, st));

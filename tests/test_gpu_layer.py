@@ -226,3 +226,58 @@ def test_graph_replay_matches_eager():
         moe.layer(gl.desc, xo, T, None, out_o, moe.OUT_F32, ws)  # eager work in between
         torch.cuda.synchronize()
         assert np.array_equal(out_o.cpu().numpy(), ref_b)
+
+
+# ------------------------------------------------------------- MFMA path
+
+MFMA_SHAPE = synth.LayerShape(n_experts=40, top_k=6, n_shared=2, d_model=512, d_ffn=768)
+
+
+@pytest.mark.parametrize("T", [1, 17, 130, 300])
+def test_mfma_path_parity(T):
+    import quantized_expert_gemv_sigmoid_amd as moe
+    log(f"case: MFMA path E40 k6 S2 d512 F768 T={T}")
+    gl = make_gpu_layer(MFMA_SHAPE, 61, path=moe.PATH_MFMA)
+    assert moe.path_for(gl.desc, T) == moe.PATH_MFMA
+    _full_check(gl, T)
+
+
+def test_mfma_auto_threshold_and_gemv_agree():
+    import quantized_expert_gemv_sigmoid_amd as moe
+    h = synth.host_layer(MFMA_SHAPE, 62, 0)
+    g_auto = make_gpu_layer(MFMA_SHAPE, 62, host=h)
+    g_gemv = make_gpu_layer(MFMA_SHAPE, 62, host=h, path=moe.PATH_GEMV)
+    assert moe.path_for(g_auto.desc, 128) == moe.PATH_GEMV
+    assert moe.path_for(g_auto.desc, 129) == moe.PATH_MFMA
+    T = 200
+    x, rw, bias = tokens(g_auto, T)
+    a = run_layer(g_auto, x)
+    b = run_layer(g_gemv, x)
+    assert np.array_equal(a[2], b[2]) or (np.sort(a[2], 1) == np.sort(b[2], 1)).all()
+    rids, rw_, gap, rout = oracle_outputs(g_auto, x, rw, bias, np.arange(T))
+    assert_close(a[0], rout, "auto(MFMA) T=200")
+    assert_close(b[0], rout, "GEMV T=200")
+
+
+def test_mfma_skewed_routing_many_tokens_per_expert():
+    # a selection bias that sends every token to experts 0..5: 300 tokens per
+    # expert, three M passes of 128 rows
+    import quantized_expert_gemv_sigmoid_amd as moe
+    h = synth.host_layer(MFMA_SHAPE, 63, 0)
+    h.router_bias = np.zeros(MFMA_SHAPE.n_experts, dtype=np.float32)
+    h.router_bias[:6] = [6.0, 5.0, 4.0, 3.0, 2.0, 1.0]
+    gl = make_gpu_layer(MFMA_SHAPE, 63, host=h, path=moe.PATH_MFMA)
+    x, out_f, out_b, ids, w, cnt = _full_check(gl, 300, screened=False)
+    assert (cnt[:6] == 300).all() and cnt[6:].sum() == 0
+
+
+def test_mfma_down_projection_out_of_fp16_window():
+    # W2 scale bytes outside [104, 140] take the exact bf16 split fallback
+    import quantized_expert_gemv_sigmoid_amd as moe
+    h = synth.host_layer(MFMA_SHAPE, 64, 0)
+    rng = np.random.default_rng(5)
+    h.w2s[...] = rng.integers(100, 104, size=h.w2s.shape, dtype=np.uint8)
+    h.w2s[:, :, 0] = 141
+    h.w2s[rng.random(h.w2s.shape) < 0.03] = 255
+    gl = make_gpu_layer(MFMA_SHAPE, 64, host=h, path=moe.PATH_MFMA)
+    _full_check(gl, 150)
