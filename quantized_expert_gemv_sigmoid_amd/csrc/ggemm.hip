@@ -33,6 +33,8 @@
 #include "../../include/moe.h"
 #include "common.h"
 
+#include <type_traits>
+
 namespace moe {
 
 typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
@@ -66,6 +68,24 @@ struct GemmParams {
 
 __device__ __forceinline__ uint4 gld16(const void *p) { return *reinterpret_cast<const uint4 *>(p); }
 
+// LDS pointers keep their address space through every helper (generic
+// pointers would let the compiler fall back to flat instructions)
+#define LDS __attribute__((address_space(3)))
+typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2_t __attribute__((ext_vector_type(2)));
+__device__ __forceinline__ uint4 lds_ld16(const LDS uint8_t *p)
+{
+    return __builtin_bit_cast(uint4, *reinterpret_cast<const LDS u32x4_t *>(p));
+}
+__device__ __forceinline__ void lds_st16(LDS uint8_t *p, uint4 v)
+{
+    *reinterpret_cast<LDS u32x4_t *>(p) = __builtin_bit_cast(u32x4_t, v);
+}
+__device__ __forceinline__ void lds_st8(LDS uint8_t *p, uint2 v)
+{
+    *reinterpret_cast<LDS u32x2_t *>(p) = __builtin_bit_cast(u32x2_t, v);
+}
+
 // Workgroup barrier for the LDS stages only: waits for this wave's LDS
 // writes (lgkmcnt 0), not for its outstanding global loads, so prefetches
 // stay in flight across it (__syncthreads would also wait for vmcnt 0).
@@ -90,35 +110,6 @@ __device__ __forceinline__ float e8m0f(uint32_t b)
     return __uint_as_float(b == 0 ? 0x00400000u : (b << 23));
 }
 
-// 8 E2M1 codes (one dword) -> 8 bf16 values times 2^(b-127); b == 255 -> 0
-__device__ __forceinline__ bf16x8_t dec_bf16(uint32_t w, uint32_t b)
-{
-    w = b == 255u ? 0u : w;
-    const float sc = e8m0f(b == 255u ? 127u : b);
-    const bf16x2v_t p0 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(w, sc, 0);
-    const bf16x2v_t p1 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(w, sc, 1);
-    const bf16x2v_t p2 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(w, sc, 2);
-    const bf16x2v_t p3 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(w, sc, 3);
-    bf16x8_t r;
-    r[0] = p0.x; r[1] = p0.y; r[2] = p1.x; r[3] = p1.y;
-    r[4] = p2.x; r[5] = p2.y; r[6] = p3.x; r[7] = p3.y;
-    return r;
-}
-
-__device__ __forceinline__ f16x8_t dec_f16(uint32_t w, uint32_t b)
-{
-    w = b == 255u ? 0u : w;
-    const float sc = e8m0f(b == 255u ? 127u : b);
-    const f16x2v_t p0 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w, sc, 0);
-    const f16x2v_t p1 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w, sc, 1);
-    const f16x2v_t p2 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w, sc, 2);
-    const f16x2v_t p3 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w, sc, 3);
-    f16x8_t r;
-    r[0] = p0.x; r[1] = p0.y; r[2] = p1.x; r[3] = p1.y;
-    r[4] = p2.x; r[5] = p2.y; r[6] = p3.x; r[7] = p3.y;
-    return r;
-}
-
 // fp16 x8 -> (hi, lo) bf16 x8 with hi + lo == value exactly
 __device__ __forceinline__ void split_f16(const f16x8_t a, bf16x8_t &hi, bf16x8_t &lo)
 {
@@ -140,372 +131,529 @@ struct Cfg {
     static constexpr bool kFp4 = (MODE == M_G13 || MODE == M_D2);
     static constexpr bool kGated = (MODE == M_G13 || MODE == M_S13);
     // K per A stage and per B stage.  A B stage holds 128 bytes of every
-    // column (256 fp4 codes or 64 bf16 values), loaded as 128-byte runs.
+    // column (256 fp4 codes = 8 MX blocks, or 64 bf16 values), loaded as
+    // 128-byte runs.
     static constexpr int KCA = kFp4 ? 128 : 64;
     static constexpr int KCB = kFp4 ? 256 : 64;
     static constexpr int R = KCB / KCA;                 // A stages per B stage
-    static constexpr int BROW = 128;                    // bytes per column per B stage
+    static constexpr int STEPS = KCA / 32;              // MFMA K steps per A stage
+    static constexpr int QPR = KCA / 8;                 // 16-byte A pieces per row of a stage
+    static constexpr int RPP = 256 / QPR;               // A rows staged per pass
     static constexpr int BSC = kFp4 ? KCB / 32 : 0;     // scale bytes per column per B stage
+    static constexpr int BPASS = GN / 32;               // B staging passes (32 columns each)
 };
+
+// K order inside an A stage: MFMA step st, lane group kg (lane / 16) and
+// element i (0..7) of a fragment multiply K index kg * (KCA / 4) + st * 8 + i
+// of the stage, for A and B alike.  A lane's fragments over the stage's
+// steps are then one contiguous run of K: for MXFP4 exactly one MX block (32
+// codes, one scale), read from LDS as one 16-byte piece.  A-stage piece q
+// (8 elements) is kg * STEPS + st.
 
 // byte offset of 16-byte piece p of column c inside a B stage (8 pieces per
 // column, XOR-swizzled so the fragment reads of 16 columns hit distinct banks)
 __device__ __forceinline__ int b_off(int c, int p) { return c * 128 + ((p ^ ((c >> 1) & 7)) << 4); }
 
-// ---------------------------------------------------------------- kernel
+// 8 E2M1 codes (one dword, low nibble first) times the scale sc (a power of
+// two) -> 8 bf16 / fp16 values
+__device__ __forceinline__ bf16x8_t cvt8_bf16(uint32_t w, float sc)
+{
+    const bf16x2v_t p0 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(w, sc, 0);
+    const bf16x2v_t p1 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(w, sc, 1);
+    const bf16x2v_t p2 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(w, sc, 2);
+    const bf16x2v_t p3 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(w, sc, 3);
+    bf16x8_t r;
+    r[0] = p0.x; r[1] = p0.y; r[2] = p1.x; r[3] = p1.y;
+    r[4] = p2.x; r[5] = p2.y; r[6] = p3.x; r[7] = p3.y;
+    return r;
+}
+
+__device__ __forceinline__ f16x8_t cvt8_f16(uint32_t w, float sc)
+{
+    const f16x2v_t p0 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w, sc, 0);
+    const f16x2v_t p1 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w, sc, 1);
+    const f16x2v_t p2 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w, sc, 2);
+    const f16x2v_t p3 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w, sc, 3);
+    f16x8_t r;
+    r[0] = p0.x; r[1] = p0.y; r[2] = p1.x; r[3] = p1.y;
+    r[4] = p2.x; r[5] = p2.y; r[6] = p3.x; r[7] = p3.y;
+    return r;
+}
+
+__device__ __forceinline__ uint32_t u4at(const uint4 &q, int i)
+{
+    return i == 0 ? q.x : (i == 1 ? q.y : (i == 2 ? q.z : q.w));
+}
+
+// Per-block geometry: which group (expert / shared expert / router) and
+// which 256-column tile this block computes.
+struct Blk {
+    int group, tile, mb;
+    int M, base, e, K, nA, nB, ncols;
+};
+
+// Global sources of this thread's B staging copies: 16-byte piece (t % 8)
+// of block columns ps * 32 + t / 8 (ps < BPASS), and (MXFP4) the scales of
+// column t.  Bases are uniform over the block, offsets are 32-bit bytes, so
+// the loads take the scalar-base + vector-offset form.  Every column of an
+// expert's tile is in range (the path requires d and F to be multiples of
+// 256); the router's columns past E re-read row E - 1 and are never stored.
+template <int MODE>
+struct BSrc {
+    const uint8_t *base0, *base1;  // gated: gate / up weights (even / odd passes)
+    uint32_t off;                  // this thread's pass-0 column row + piece
+    uint32_t pstride;              // bytes between the rows of consecutive passes (gated: pass pairs)
+    uint32_t roff[MODE == M_R ? Cfg<MODE>::BPASS : 1];  // router: clamped per-pass rows
+    const uint8_t *sbase;          // MXFP4 scales of column t: sbase + soff
+    uint32_t soff;
+};
+
+template <int MODE>
+__device__ __forceinline__ BSrc<MODE> make_bsrc(const GemmParams &p, const Blk &b)
+{
+    using C = Cfg<MODE>;
+    const Shape &s = p.s;
+    const int t = threadIdx.x;
+    const uint32_t piece = (t & 7) * 16;
+    BSrc<MODE> r;
+    r.base1 = nullptr;
+    r.sbase = nullptr;
+    r.soff = 0;
+    r.roff[0] = 0;
+    if constexpr (C::kGated) {
+        // block column cc = ps * 32 + t / 8: wave part ps / 2, up if ps is odd,
+        // feature tile * 128 + (ps / 2) * 32 + ((t / 128) & 1) * 16 + (t / 8) % 16
+        const uint32_t f0 = b.tile * 128 + ((t >> 7) & 1) * 16 + ((t >> 3) & 15);
+        if constexpr (MODE == M_G13) {
+            const size_t eo = (size_t)b.e * s.F * (s.d / 2);
+            r.base0 = p.w1q + eo;
+            r.base1 = p.w3q + eo;
+            r.off = f0 * (s.d / 2) + piece;
+            r.pstride = 32 * (s.d / 2);
+            // scales of block column t
+            const int fs = b.tile * 128 + (t >> 6) * 32 + ((t >> 4) & 1) * 16 + (t & 15);
+            r.sbase = (((t >> 5) & 1) ? p.w3s : p.w1s) + (size_t)b.e * s.F * (s.d / 32);
+            r.soff = fs * (s.d / 32);
+        } else {
+            const size_t go = (size_t)b.group * s.F * s.d * 2;
+            r.base0 = reinterpret_cast<const uint8_t *>(p.sh1) + go;
+            r.base1 = reinterpret_cast<const uint8_t *>(p.sh3) + go;
+            r.off = f0 * (s.d * 2) + piece;
+            r.pstride = 32 * (s.d * 2);
+        }
+    } else if constexpr (MODE == M_D2) {
+        r.base0 = p.w2q + (size_t)b.e * s.d * (s.F / 2);
+        r.off = (b.tile * GN + (t >> 3)) * (s.F / 2) + piece;
+        r.pstride = 32 * (s.F / 2);
+        r.sbase = p.w2s + (size_t)b.e * s.d * (s.F / 32);
+        r.soff = (b.tile * GN + t) * (s.F / 32);
+    } else if constexpr (MODE == M_S2) {
+        r.base0 = reinterpret_cast<const uint8_t *>(p.sh2) + (size_t)b.group * s.d * s.F * 2;
+        r.off = (b.tile * GN + (t >> 3)) * (s.F * 2) + piece;
+        r.pstride = 32 * (s.F * 2);
+    } else {
+        r.base0 = reinterpret_cast<const uint8_t *>(p.wr3);
+        r.off = piece;
+        r.pstride = 0;
+#pragma unroll
+        for (int ps = 0; ps < C::BPASS; ps++) {
+            const int n = min(b.tile * GN + ps * 32 + (t >> 3), s.E - 1);
+            r.roff[ps] = (uint32_t)n * (3 * s.d * 2);
+        }
+    }
+    return r;
+}
+
+// One M pass of MT 16-row tiles (rows m0 .. m0 + mrows - 1 of the group)
+// over the whole K, then its epilogue.  la / lb / lbs: the LDS stages.
+template <int MODE, int MT, bool SPLIT = false>
+__device__ __forceinline__ void gemm_pass(const GemmParams &p, const Blk &bk, const BSrc<MODE> &bsrc,
+                                          int m0, int mrows, LDS uint16_t *la, LDS uint8_t *lb,
+                                          LDS uint8_t *lbs)
+{
+    using C = Cfg<MODE>;
+    constexpr int KCA = C::KCA, R = C::R, STEPS = C::STEPS, QPR = C::QPR, RPP = C::RPP;
+    constexpr int NPASS = (MT * 16 + RPP - 1) / RPP;  // A staging passes for MT tiles
+    constexpr int ASTAGE = GM * KCA;                  // elements per A stage
+    constexpr int BSTAGE = GN * 128;                  // bytes per B stage
+    constexpr int SSTAGE = GN * (C::kFp4 ? C::BSC : 1);
+    const Shape &s = p.s;
+    const int t = threadIdx.x;
+    const int lane = t & 63, wave = t >> 6;
+    const int col = lane & 15, kg = lane >> 4;
+    const int nA = bk.nA, nB = bk.nB;
+
+    // ---- A staging: this thread copies piece qa of rows ps * RPP + t / QPR
+    // (rows past the group's end re-read its last row; their results are
+    // never stored)
+    // byte offsets (32-bit: the host checks that every A operand is below 2 GiB)
+    const int qa = t % QPR;
+    uint32_t arow[NPASS];
+#pragma unroll
+    for (int ps = 0; ps < NPASS; ps++) {
+        const int r = min(ps * RPP + t / QPR, mrows - 1);
+        const int m = m0 + r;
+        uint32_t e;
+        if constexpr (MODE == M_G13) e = (uint32_t)p.w.pos_tok[bk.base + m] * s.d;
+        else if constexpr (MODE == M_D2) e = (uint32_t)(bk.base + m) * s.F;
+        else if constexpr (MODE == M_S2) e = (uint32_t)m * s.S * s.F + (uint32_t)bk.group * s.F;
+        else e = (uint32_t)m * s.d;
+        arow[ps] = (e + qa * 8) * 2;
+    }
+    auto load_a = [&](uint4 (&ar)[NPASS], int i) __attribute__((always_inline)) {
+        const int k0 = i * KCA;
+        const uint16_t *abase;
+        int kk = k0;
+        if constexpr (MODE == M_G13 || MODE == M_S13) {
+            abase = p.x;
+        } else if constexpr (MODE == M_D2) {
+            abase = reinterpret_cast<const uint16_t *>(p.w.H);
+        } else if constexpr (MODE == M_S2) {
+            abase = k0 < s.F ? p.hs_hi : p.hs_lo;  // K runs over [hi parts | lo parts]
+            kk = k0 % s.F;
+        } else {
+            abase = p.x;  // router: K runs over [x | x | x]
+            kk = k0 % s.d;
+        }
+        const uint8_t *ab = reinterpret_cast<const uint8_t *>(abase);
+#pragma unroll
+        for (int ps = 0; ps < NPASS; ps++) ar[ps] = gld16(ab + (arow[ps] + (uint32_t)kk * 2));
+    };
+    auto store_a = [&](const uint4 (&ar)[NPASS], int stage) __attribute__((always_inline)) {
+#pragma unroll
+        for (int ps = 0; ps < NPASS; ps++) {
+            const int r = ps * RPP + t / QPR;
+            lds_st16(reinterpret_cast<LDS uint8_t *>(la + stage * ASTAGE + lds_off<KCA>(r, qa)), ar[ps]);
+        }
+    };
+
+    // ---- B staging
+    const int bpiece = t & 7;  // 16-byte piece of a column this thread copies
+    struct BRegs {
+        uint4 v[C::BPASS];
+        uint2 sc;
+    };
+    auto load_b = [&](BRegs &br, int j) __attribute__((always_inline)) {
+        const int k0 = j * C::KCB;
+        uint32_t koff;  // byte offset of the stage in a weight row
+        if constexpr (C::kFp4) koff = k0 / 2;
+        else if constexpr (MODE == M_S2) koff = (k0 % s.F) * 2;  // B repeats for the hi / lo halves
+        else koff = k0 * 2;                                       // router row = [hi | mid | lo]
+#pragma unroll
+        for (int ps = 0; ps < C::BPASS; ps++) {
+            if constexpr (C::kGated)
+                br.v[ps] = gld16(((ps & 1) ? bsrc.base1 : bsrc.base0) + (bsrc.off + (ps >> 1) * bsrc.pstride + koff));
+            else if constexpr (MODE == M_R)
+                br.v[ps] = gld16(bsrc.base0 + (bsrc.roff[ps] + bsrc.off + koff));
+            else
+                br.v[ps] = gld16(bsrc.base0 + (bsrc.off + ps * bsrc.pstride + koff));
+        }
+        if constexpr (C::kFp4) br.sc = *reinterpret_cast<const uint2 *>(bsrc.sbase + (bsrc.soff + k0 / 32));
+    };
+    auto store_b = [&](const BRegs &br, int stage) __attribute__((always_inline)) {
+#pragma unroll
+        for (int ps = 0; ps < C::BPASS; ps++) {
+            const int cc = ps * 32 + (t >> 3);
+            lds_st16(lb + stage * BSTAGE + b_off(cc, bpiece), br.v[ps]);
+        }
+        if constexpr (C::kFp4) lds_st8(lbs + stage * SSTAGE + t * C::BSC, br.sc);
+    };
+
+    f32x4_t acc[MT][GNS];
+#pragma unroll
+    for (int mt = 0; mt < MT; mt++)
+#pragma unroll
+        for (int j = 0; j < GNS; j++) acc[mt][j] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+
+    auto a_frag = [&](const LDS uint16_t *A, int mt, int st) __attribute__((always_inline)) -> uint4 {
+        return lds_ld16(reinterpret_cast<const LDS uint8_t *>(A + lds_off<KCA>(mt * 16 + col, kg * STEPS + st)));
+    };
+
+    // One A stage (STEPS MFMA K steps) against sub-stage `sub` of a B stage.
+    // Software pipelined: the A fragments and decoded B fragments of step
+    // st + 1 are read / decoded while the MFMAs of step st run (the
+    // scheduling fences keep the compiler from sinking the reads back next
+    // to their uses).
+    auto compute = [&](int sa, int sb, int sub) __attribute__((always_inline)) {
+        const LDS uint16_t *A = la + sa * ASTAGE;
+        const LDS uint8_t *B = lb + sb * BSTAGE;
+        uint4 af[2][MT];
+        if constexpr (C::kFp4) {
+            using BT = typename std::conditional<MODE == M_D2, f16x8_t, bf16x8_t>::type;
+            // this lane's MX block of each of its 4 columns: 16 bytes + scale
+            uint4 q[GNS];
+            uint32_t sc[GNS];
+#pragma unroll
+            for (int j = 0; j < GNS; j++) {
+                const int cc = wave * 64 + j * 16 + col;
+                q[j] = lds_ld16(B + b_off(cc, sub * 4 + kg));
+                sc[j] = lbs[sb * SSTAGE + cc * C::BSC + sub * 4 + kg];
+            }
+            float scf[GNS];
+#pragma unroll
+            for (int j = 0; j < GNS; j++) {
+                // NaN scale (255): the block contributes 0
+                const uint32_t keep = sc[j] == 255u ? 0u : ~0u;
+                q[j].x &= keep; q[j].y &= keep; q[j].z &= keep; q[j].w &= keep;
+                scf[j] = e8m0f(sc[j] == 255u ? 127u : sc[j]);
+            }
+            if constexpr (!SPLIT) {
+                // fragments of the first PF tiles are prefetched one step
+                // ahead, the rest (large tiles only) read in their step
+                constexpr int PF = MT <= 6 ? MT : 4;
+#pragma unroll
+                for (int mt = 0; mt < PF; mt++) af[0][mt] = a_frag(A, mt, 0);
+                BT b[2][GNS];
+                auto decode = [&](BT (&bb)[GNS], int st) __attribute__((always_inline)) {
+#pragma unroll
+                    for (int j = 0; j < GNS; j++) {
+                        if constexpr (MODE == M_D2) bb[j] = cvt8_f16(u4at(q[j], st), scf[j]);
+                        else bb[j] = cvt8_bf16(u4at(q[j], st), scf[j]);
+                    }
+                };
+                decode(b[0], 0);
+#pragma unroll
+                for (int st = 0; st < STEPS; st++) {
+                    const int cur = st & 1, nxt = cur ^ 1;
+                    if (st + 1 < STEPS) {
+#pragma unroll
+                        for (int mt = 0; mt < PF; mt++) af[nxt][mt] = a_frag(A, mt, st + 1);
+                        decode(b[nxt], st + 1);
+                    }
+#pragma unroll
+                    for (int mt = 0; mt < MT; mt++) {
+                        const uint4 a = mt < PF ? af[cur][mt] : a_frag(A, mt, st);
+#pragma unroll
+                        for (int j = 0; j < GNS; j++) {
+                            if constexpr (MODE == M_D2)
+                                acc[mt][j] = __builtin_amdgcn_mfma_f32_16x16x32_f16(
+                                    __builtin_bit_cast(f16x8_t, a), b[cur][j], acc[mt][j], 0, 0, 0);
+                            else
+                                acc[mt][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
+                                    __builtin_bit_cast(bf16x8_t, a), b[cur][j], acc[mt][j], 0, 0, 0);
+                        }
+                    }
+                    __builtin_amdgcn_sched_barrier(0);
+                }
+            } else {
+                // exact fallback: bf16 weights, fp16 inputs split in two bf16 parts
+#pragma unroll
+                for (int st = 0; st < STEPS; st++) {
+                    bf16x8_t b[GNS];
+#pragma unroll
+                    for (int j = 0; j < GNS; j++) b[j] = cvt8_bf16(u4at(q[j], st), scf[j]);
+#pragma unroll
+                    for (int mt = 0; mt < MT; mt++) {
+                        // one fragment at a time (a rare path; keeps its registers few)
+                        bf16x8_t ah, al;
+                        split_f16(__builtin_bit_cast(f16x8_t, a_frag(A, mt, st)), ah, al);
+#pragma unroll
+                        for (int j = 0; j < GNS; j++) {
+                            acc[mt][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ah, b[j], acc[mt][j], 0, 0, 0);
+                            acc[mt][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(al, b[j], acc[mt][j], 0, 0, 0);
+                        }
+                        __builtin_amdgcn_sched_barrier(0);
+                    }
+                    __builtin_amdgcn_sched_barrier(0);
+                }
+            }
+        } else {
+            uint4 b[2][GNS];
+            auto read_b = [&](uint4 (&bb)[GNS], int st) __attribute__((always_inline)) {
+#pragma unroll
+                for (int j = 0; j < GNS; j++) {
+                    const int cc = wave * 64 + j * 16 + col;
+                    bb[j] = lds_ld16(B + b_off(cc, kg * STEPS + st));
+                }
+            };
+            read_b(b[0], 0);
+#pragma unroll
+            for (int mt = 0; mt < MT; mt++) af[0][mt] = a_frag(A, mt, 0);
+#pragma unroll
+            for (int st = 0; st < STEPS; st++) {
+                const int cur = st & 1, nxt = cur ^ 1;
+                if (st + 1 < STEPS) {
+                    read_b(b[nxt], st + 1);
+#pragma unroll
+                    for (int mt = 0; mt < MT; mt++) af[nxt][mt] = a_frag(A, mt, st + 1);
+                }
+#pragma unroll
+                for (int mt = 0; mt < MT; mt++)
+#pragma unroll
+                    for (int j = 0; j < GNS; j++)
+                        acc[mt][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
+                            __builtin_bit_cast(bf16x8_t, af[cur][mt]), __builtin_bit_cast(bf16x8_t, b[cur][j]),
+                            acc[mt][j], 0, 0, 0);
+                __builtin_amdgcn_sched_barrier(0);
+            }
+        }
+    };
+
+    // ---- K loop, two A stages per trip (every K here is a multiple of
+    // 2 * KCA).  A stage i sits in LDS stage i & 1 and was loaded into
+    // registers two stages before it is stored (register sets ar0 / ar1), B
+    // stage j in LDS stage j & 1, loaded R stages ahead (fp4: one B stage per
+    // trip).  Loads past the end re-read the last stage (harmless) so every
+    // trip is identical.
+    uint4 ar0[NPASS], ar1[NPASS];
+    BRegs br;
+    load_a(ar0, 0);
+    load_b(br, 0);
+    store_a(ar0, 0);
+    store_b(br, 0);
+    load_a(ar1, min(1, nA - 1));
+    load_a(ar0, min(2, nA - 1));
+    load_b(br, min(1, nB - 1));
+    lds_barrier();
+    for (int i = 0; i < nA; i += 2) {
+        compute(0, (i / R) & 1, i % R);
+        store_a(ar1, 1);  // A stage i + 1
+        if constexpr (R == 1) store_b(br, 1);
+        lds_barrier();
+        load_a(ar1, min(i + 3, nA - 1));
+        if constexpr (R == 1) load_b(br, min(i + 2, nB - 1));
+
+        compute(1, ((i + 1) / R) & 1, (i + 1) % R);
+        store_a(ar0, 0);  // A stage i + 2
+        store_b(br, ((i + 1) / R + 1) & 1);
+        lds_barrier();
+        load_a(ar0, min(i + 4, nA - 1));
+        load_b(br, min((i + 1) / R + 2, nB - 1));
+    }
+
+    // ---- epilogue (D lane layout: register i of tile (mt, j) holds row
+    // mt * 16 + 4 * kg + i, column j * 16 + col of the wave's 64)
+#pragma unroll
+    for (int mt = 0; mt < MT; mt++) {
+#pragma unroll
+        for (int i = 0; i < 4; i++) {
+            const int r = mt * 16 + kg * 4 + i;
+            if (r >= mrows) continue;
+            const int m = m0 + r;
+            if constexpr (C::kGated) {
+#pragma unroll
+                for (int j = 0; j < 2; j++) {
+                    const int f = bk.tile * 128 + wave * 32 + j * 16 + col;
+                    if (f >= s.F) continue;
+                    const float h = gated_act(acc[mt][j][i], acc[mt][j + 2][i], s.act, s.b1, s.b2);
+                    if constexpr (MODE == M_G13) {
+                        _Float16 *H = reinterpret_cast<_Float16 *>(p.w.H);
+                        H[(size_t)(bk.base + m) * s.F + f] = (_Float16)h;
+                    } else {
+                        const uint16_t hi = f32_to_bf16_rne(h);
+                        const uint16_t lo = f32_to_bf16_rne(h - __uint_as_float((uint32_t)hi << 16));
+                        const size_t o = (size_t)m * s.S * s.F + (size_t)bk.group * s.F + f;
+                        p.hs_hi_w[o] = hi;
+                        p.hs_lo_w[o] = lo;
+                    }
+                }
+            } else {
+                float wrow = 1.0f;
+                if constexpr (MODE == M_D2) wrow = p.w.pos_w[bk.base + m];
+#pragma unroll
+                for (int j = 0; j < GNS; j++) {
+                    const int n = bk.tile * GN + wave * 64 + j * 16 + col;
+                    if (n >= bk.ncols) continue;
+                    const float v = acc[mt][j][i];
+                    if constexpr (MODE == M_D2) p.w.Y[(size_t)(bk.base + m) * s.d + n] = v * wrow;
+                    else if constexpr (MODE == M_S2) p.w.Ysh[((size_t)bk.group * s.T + m) * s.d + n] = v;
+                    else p.w.logits[(size_t)m * s.E + n] = v;
+                }
+            }
+        }
+    }
+}
 
 template <int MODE>
 __global__ __launch_bounds__(256) void k_ggemm(GemmParams p)
 {
     using C = Cfg<MODE>;
-    constexpr int KCA = C::KCA, KCB = C::KCB, R = C::R;
-    constexpr int QPR = KCA / 8;          // 16-byte A pieces per row of a stage
-    constexpr int RPP = 256 / QPR;        // A rows staged per pass
-    constexpr int SPASS = GM / RPP;       // A staging passes per stage
-    constexpr int STEPS = KCA / 32;       // MFMA K steps per A stage
-    constexpr int BPASS = GN / 32;        // B staging passes (32 columns x 128 B each)
-    __shared__ __attribute__((aligned(16))) uint16_t lds_a[2][GM * KCA];
-    __shared__ __attribute__((aligned(16))) uint8_t lds_b[2][GN * C::BROW];
-    __shared__ __attribute__((aligned(16))) uint8_t lds_bs[2][C::kFp4 ? GN * C::BSC : 16];
+    __shared__ __attribute__((aligned(16))) uint16_t lds_a[2 * GM * C::KCA];
+    __shared__ __attribute__((aligned(16))) uint8_t lds_b[2 * GN * 128];
+    __shared__ __attribute__((aligned(16))) uint8_t lds_bs[2 * GN * (C::kFp4 ? C::BSC : 1)];
 
+    LDS uint16_t *la = (LDS uint16_t *)lds_a;
+    LDS uint8_t *lb = (LDS uint8_t *)lds_b;
+    LDS uint8_t *lbs = (LDS uint8_t *)lds_bs;
     const Shape &s = p.s;
-    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-    const int col = lane & 15, kg = lane >> 4;
-
-    // ---- block -> (m block, group, column tile); groups of one XCD together
+    Blk b;
+    // ---- block -> (m block, group, column tile); consecutive groups of
+    // tiles go to one XCD (blocks are dealt to the 8 XCDs round robin)
     int x = blockIdx.x;
     const int gt = p.groups * p.n_tiles;
-    int mb = 0;
+    b.mb = 0;
     if (p.m_blocks > 1) {
-        mb = x / gt;
+        b.mb = x / gt;
         x = x % gt;
     }
-    int group, tile;
     if (p.groups >= 8) {
         const int xcd = x & 7, j = x >> 3;
-        group = (j / p.n_tiles) * 8 + xcd;
-        tile = j % p.n_tiles;
+        b.group = (j / p.n_tiles) * 8 + xcd;
+        b.tile = j % p.n_tiles;
     } else {
-        group = x / p.n_tiles;
-        tile = x % p.n_tiles;
+        b.group = x / p.n_tiles;
+        b.tile = x % p.n_tiles;
     }
-    if (group >= p.groups) return;
+    if (b.group >= p.groups) return;
 
-    // ---- group geometry
-    int M, base = 0, e = 0, K;
+    b.base = 0;
+    b.e = 0;
     if constexpr (MODE == M_G13 || MODE == M_D2) {
-        if (group >= p.w.meta[0]) return;
-        e = p.w.active[group];
-        M = p.w.counts[e];
-        base = p.w.offsets[e];
-        K = MODE == M_G13 ? s.d : s.F;
+        if (b.group >= p.w.meta[0]) return;
+        b.e = p.w.active[b.group];
+        b.M = p.w.counts[b.e];
+        b.base = p.w.offsets[b.e];
+        b.K = MODE == M_G13 ? s.d : s.F;
     } else {
-        M = s.T;
-        K = MODE == M_S13 ? s.d : (MODE == M_S2 ? 2 * s.F : 3 * s.d);
+        b.M = s.T;
+        b.K = MODE == M_S13 ? s.d : (MODE == M_S2 ? 2 * s.F : 3 * s.d);
     }
-    const int nA = K / KCA, nB = K / KCB;
-    const int ncols = C::kGated ? s.F : (MODE == M_R ? s.E : s.d);
+    b.nA = b.K / C::KCA;
+    b.nB = b.K / C::KCB;
+    b.ncols = C::kGated ? s.F : (MODE == M_R ? s.E : s.d);
+    const BSrc<MODE> bsrc = make_bsrc<MODE>(p, b);
 
-    // ---- B staging: thread t copies 16-byte piece (t % 8) of columns
-    // ps * 32 + t / 8 (ps < BPASS); with fp4 also the scales of column t
-    const int bpiece = threadIdx.x & 7;
-    auto col_global = [&](int cc, bool &valid) -> int {
-        // block column cc (0..255) -> output column (or gated feature)
-        int n;
-        if constexpr (C::kGated) n = tile * 128 + (cc >> 6) * 32 + ((cc >> 4) & 1) * 16 + (cc & 15);
-        else n = tile * GN + cc;
-        valid = n < ncols;
-        return valid ? n : 0;
-    };
-    // row base pointer (bytes) of block column cc in the weight matrix
-    auto b_row = [&](int cc, bool &valid) -> const uint8_t * {
-        const int n = col_global(cc, valid);
-        if constexpr (MODE == M_G13) {
-            const uint8_t *q = ((cc >> 5) & 1) ? p.w3q : p.w1q;  // columns 32..63 of a wave: up
-            return q + ((size_t)e * s.F + n) * (s.d / 2);
-        } else if constexpr (MODE == M_D2) {
-            return p.w2q + ((size_t)e * s.d + n) * (s.F / 2);
-        } else if constexpr (MODE == M_S13) {
-            const uint16_t *w = ((cc >> 5) & 1) ? p.sh3 : p.sh1;
-            return reinterpret_cast<const uint8_t *>(w + ((size_t)group * s.F + n) * s.d);
-        } else if constexpr (MODE == M_S2) {
-            return reinterpret_cast<const uint8_t *>(p.sh2 + ((size_t)group * s.d + n) * s.F);
-        } else {
-            return reinterpret_cast<const uint8_t *>(p.wr3 + (size_t)n * 3 * s.d);
-        }
-    };
-    auto b_scale_row = [&](int cc) -> const uint8_t * {
-        bool v;
-        const int n = col_global(cc, v);
-        if constexpr (MODE == M_G13) {
-            const uint8_t *sc = ((cc >> 5) & 1) ? p.w3s : p.w1s;
-            return sc + ((size_t)e * s.F + n) * (s.d / 32);
-        } else {
-            return p.w2s + ((size_t)e * s.d + n) * (s.F / 32);
-        }
-    };
-    const uint8_t *brow[BPASS];
-    bool bval[BPASS];
+    if constexpr (MODE == M_D2) {
+        // The down projection multiplies fp16 H by W2 decoded to fp16, which
+        // is exact for scale bytes 104..140 (and 255, which decodes to 0).
+        // A block whose W2 scales leave that range takes the exact split
+        // path (bf16 weights, H split into two bf16 parts) for all its rows.
+        const uint8_t *sc = bsrc.sbase + bsrc.soff;  // scales of block column t
+        bool ok = true;
+        for (int i = 0; i < s.F / 32; i += 8) {
+            const uint2 v = *reinterpret_cast<const uint2 *>(sc + i);
 #pragma unroll
-    for (int ps = 0; ps < BPASS; ps++) brow[ps] = b_row(ps * 32 + (threadIdx.x >> 3), bval[ps]);
-    const uint8_t *bsrow = nullptr;
-    if constexpr (C::kFp4) bsrow = b_scale_row(threadIdx.x);
-
-    struct BRegs {
-        uint4 v[BPASS];
-        uint2 sc;
-    };
-    auto load_b = [&](BRegs &br, int j) {
-        const int k0 = j * KCB;
-        size_t koff;  // byte offset of the stage in a row
-        if constexpr (C::kFp4) koff = (size_t)k0 / 2;
-        else if constexpr (MODE == M_S2) koff = (size_t)(k0 % s.F) * 2;  // B repeats for the hi / lo halves
-        else koff = (size_t)k0 * 2;
-#pragma unroll
-        for (int ps = 0; ps < BPASS; ps++) br.v[ps] = gld16(brow[ps] + koff + bpiece * 16);
-        if constexpr (C::kFp4) br.sc = *reinterpret_cast<const uint2 *>(bsrow + k0 / 32);
-    };
-    auto store_b = [&](const BRegs &br, int stage) {
-#pragma unroll
-        for (int ps = 0; ps < BPASS; ps++) {
-            const int cc = ps * 32 + (threadIdx.x >> 3);
-            // a column past the edge stores zeros (fp4 codes 0 and scale 255 decode to 0)
-            *reinterpret_cast<uint4 *>(&lds_b[stage][b_off(cc, bpiece)]) =
-                bval[ps] ? br.v[ps] : make_uint4(0, 0, 0, 0);
-        }
-        if constexpr (C::kFp4) {
-            bool v;
-            col_global(threadIdx.x, v);
-            *reinterpret_cast<uint2 *>(&lds_bs[stage][threadIdx.x * C::BSC]) = v ? br.sc : make_uint2(~0u, ~0u);
-        }
-    };
-
-    // ---- M passes
-    const int m_first = (p.m_blocks > 1) ? mb * GM : 0;
-    const int m_step = (p.m_blocks > 1) ? M : GM;  // shared / router: one pass per block
-    for (int m0 = m_first; m0 < M; m0 += m_step) {
-        const int mrows = min(GM, M - m0);
-        const int mtiles = (mrows + 15) >> 4;
-
-        // A staging: element offset of the row each of this thread's pieces reads
-        // (rows past the group's end re-read its last row; results not stored)
-        size_t arow[SPASS];
-#pragma unroll
-        for (int ps = 0; ps < SPASS; ps++) {
-            const int r = min(ps * RPP + (int)threadIdx.x / QPR, mrows - 1);
-            const int m = m0 + r;
-            if constexpr (MODE == M_G13) arow[ps] = (size_t)p.w.pos_tok[base + m] * s.d;
-            else if constexpr (MODE == M_D2) arow[ps] = (size_t)(base + m) * s.F;
-            else if constexpr (MODE == M_S2) arow[ps] = (size_t)m * s.S * s.F + (size_t)group * s.F;
-            else arow[ps] = (size_t)m * s.d;
-        }
-        const int qa = threadIdx.x % QPR;
-        struct ARegs {
-            uint4 v[SPASS];
-        };
-        auto load_a = [&](ARegs &ar, int i) {
-            const int k0 = i * KCA;
-            const uint16_t *abase;
-            int kk = k0;
-            if constexpr (MODE == M_G13 || MODE == M_S13) {
-                abase = p.x;
-            } else if constexpr (MODE == M_D2) {
-                abase = reinterpret_cast<const uint16_t *>(p.w.H);
-            } else if constexpr (MODE == M_S2) {
-                abase = k0 < s.F ? p.hs_hi : p.hs_lo;
-                kk = k0 % s.F;
-            } else {
-                abase = p.x;
-                kk = k0 % s.d;
-            }
-#pragma unroll
-            for (int ps = 0; ps < SPASS; ps++) ar.v[ps] = gld16(abase + arow[ps] + kk + qa * 8);
-        };
-        auto store_a = [&](const ARegs &ar, int stage) {
-#pragma unroll
-            for (int ps = 0; ps < SPASS; ps++) {
-                const int r = ps * RPP + threadIdx.x / QPR;
-                *reinterpret_cast<uint4 *>(&lds_a[stage][lds_off<KCA>(r, qa)]) = ar.v[ps];
-            }
-        };
-
-        f32x4_t acc[GMT][GNS];
-#pragma unroll
-        for (int mt = 0; mt < GMT; mt++)
-#pragma unroll
-            for (int j = 0; j < GNS; j++) acc[mt][j] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-
-        // ---- fragments
-        auto a_frag = [&](int stage, int mt, int st) -> uint4 {
-            const int r = mt * 16 + col;
-            const int q = (st * 32 + kg * 8) >> 3;
-            return *reinterpret_cast<const uint4 *>(&lds_a[stage][lds_off<KCA>(r, q)]);
-        };
-        // fp4: 8 codes (4 bytes) + scale of column cc at K offset kb of the B stage
-        auto b_codes = [&](int stage, int cc, int kb) -> uint32_t {
-            const int byte = kb / 2;
-            return *reinterpret_cast<const uint32_t *>(&lds_b[stage][b_off(cc, byte >> 4) + (byte & 15)]);
-        };
-        auto b_scale = [&](int stage, int cc, int kb) -> uint32_t {
-            return lds_bs[stage][cc * C::BSC + kb / 32];
-        };
-        auto b_bf16 = [&](int stage, int cc, int kb) -> uint4 {
-            const int byte = kb * 2;
-            return *reinterpret_cast<const uint4 *>(&lds_b[stage][b_off(cc, byte >> 4)]);
-        };
-
-        // one A stage (STEPS MFMA K steps) against the matching part of a B stage
-        auto compute = [&](int sa, int sb, int sub) {
-            bool fp16_ok = true;
-            if constexpr (MODE == M_D2) {
-                // fp16 decode is exact for scale bytes 104..140 (and 255 -> 0)
-                bool mine = true;
-#pragma unroll
-                for (int st = 0; st < STEPS; st++)
-#pragma unroll
-                    for (int j = 0; j < GNS; j++) {
-                        const uint32_t b = b_scale(sb, wave * 64 + j * 16 + col, sub * KCA + st * 32 + kg * 8);
-                        mine = mine && (b == 255u || (b >= 104u && b <= 140u));
-                    }
-                fp16_ok = __all(mine);
-            }
-#pragma unroll
-            for (int st = 0; st < STEPS; st++) {
-                const int kb = sub * KCA + st * 32 + kg * 8;  // K of this lane's 8 values in the B stage
-                if constexpr (MODE == M_D2) {
-                    if (fp16_ok) {
-                        f16x8_t b[GNS];
-#pragma unroll
-                        for (int j = 0; j < GNS; j++) {
-                            const int cc = wave * 64 + j * 16 + col;
-                            b[j] = dec_f16(b_codes(sb, cc, kb), b_scale(sb, cc, kb));
-                        }
-#pragma unroll
-                        for (int mt = 0; mt < GMT; mt++) {
-                            if (mt < mtiles) {
-                                const f16x8_t a = __builtin_bit_cast(f16x8_t, a_frag(sa, mt, st));
-#pragma unroll
-                                for (int j = 0; j < GNS; j++)
-                                    acc[mt][j] = __builtin_amdgcn_mfma_f32_16x16x32_f16(a, b[j], acc[mt][j], 0, 0, 0);
-                            }
-                        }
-                    } else {
-                        // exact fallback: bf16 weights, fp16 inputs split in two bf16 parts
-                        bf16x8_t b[GNS];
-#pragma unroll
-                        for (int j = 0; j < GNS; j++) {
-                            const int cc = wave * 64 + j * 16 + col;
-                            b[j] = dec_bf16(b_codes(sb, cc, kb), b_scale(sb, cc, kb));
-                        }
-#pragma unroll
-                        for (int mt = 0; mt < GMT; mt++) {
-                            if (mt < mtiles) {
-                                bf16x8_t ah, al;
-                                split_f16(__builtin_bit_cast(f16x8_t, a_frag(sa, mt, st)), ah, al);
-#pragma unroll
-                                for (int j = 0; j < GNS; j++) {
-                                    acc[mt][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ah, b[j], acc[mt][j], 0, 0, 0);
-                                    acc[mt][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(al, b[j], acc[mt][j], 0, 0, 0);
-                                }
-                            }
-                        }
-                    }
-                } else {
-                    bf16x8_t b[GNS];
-#pragma unroll
-                    for (int j = 0; j < GNS; j++) {
-                        const int cc = wave * 64 + j * 16 + col;
-                        if constexpr (C::kFp4) b[j] = dec_bf16(b_codes(sb, cc, kb), b_scale(sb, cc, kb));
-                        else b[j] = __builtin_bit_cast(bf16x8_t, b_bf16(sb, cc, kb));
-                    }
-#pragma unroll
-                    for (int mt = 0; mt < GMT; mt++) {
-                        if (mt < mtiles) {
-                            const bf16x8_t a = __builtin_bit_cast(bf16x8_t, a_frag(sa, mt, st));
-#pragma unroll
-                            for (int j = 0; j < GNS; j++)
-                                acc[mt][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b[j], acc[mt][j], 0, 0, 0);
-                        }
-                    }
-                }
-                __builtin_amdgcn_sched_barrier(0);
-            }
-        };
-
-        // ---- K loop.  Iteration i multiplies A stage i (LDS stage i & 1)
-        // against B stage i / R (LDS stage (i / R) & 1), then writes A(i + 1)
-        // and, at a B boundary, B(i / R + 1) into LDS, then issues the loads
-        // of A(i + 2) and only after them of B(i / R + 2): the wait for an A
-        // load never has to wait for a B load issued later, so each B load
-        // has R iterations to arrive and each A load one.  Loads past the end
-        // re-read the last stage (harmless) so every iteration is identical.
-        ARegs ar;
-        BRegs br;
-        load_a(ar, 0);
-        load_b(br, 0);
-        store_a(ar, 0);
-        store_b(br, 0);
-        load_a(ar, min(1, nA - 1));
-        load_b(br, min(1, nB - 1));
-        lds_barrier();
-        for (int i = 0; i < nA; i++) {
-            const int jb = i / R, sub = i % R;
-            compute(i & 1, jb & 1, sub);
-            store_a(ar, (i + 1) & 1);
-            const bool bnd = sub == R - 1;  // the next iteration starts a new B stage
-            if (bnd) store_b(br, (jb + 1) & 1);
-            lds_barrier();
-            load_a(ar, min(i + 2, nA - 1));
-            if (bnd) load_b(br, min(jb + 2, nB - 1));
-        }
-
-        // ---- epilogue
-#pragma unroll
-        for (int mt = 0; mt < GMT; mt++) {
-            if (mt >= mtiles) continue;
-#pragma unroll
-            for (int i = 0; i < 4; i++) {
-                const int r = mt * 16 + kg * 4 + i;
-                if (r >= mrows) continue;
-                const int m = m0 + r;
-                if constexpr (C::kGated) {
-#pragma unroll
-                    for (int j = 0; j < 2; j++) {
-                        const int f = tile * 128 + wave * 32 + j * 16 + col;
-                        if (f >= s.F) continue;
-                        const float h = gated_act(acc[mt][j][i], acc[mt][j + 2][i], s.act, s.b1, s.b2);
-                        if constexpr (MODE == M_G13) {
-                            _Float16 *H = reinterpret_cast<_Float16 *>(p.w.H);
-                            H[(size_t)(base + m) * s.F + f] = (_Float16)h;
-                        } else {
-                            const uint16_t hi = f32_to_bf16_rne(h);
-                            const uint16_t lo = f32_to_bf16_rne(h - __uint_as_float((uint32_t)hi << 16));
-                            const size_t o = (size_t)m * s.S * s.F + (size_t)group * s.F + f;
-                            p.hs_hi_w[o] = hi;
-                            p.hs_lo_w[o] = lo;
-                        }
-                    }
-                } else {
-                    float wrow = 1.0f;
-                    if constexpr (MODE == M_D2) wrow = p.w.pos_w[base + m];
-#pragma unroll
-                    for (int j = 0; j < GNS; j++) {
-                        const int n = tile * GN + wave * 64 + j * 16 + col;
-                        if (n >= ncols) continue;
-                        const float v = acc[mt][j][i];
-                        if constexpr (MODE == M_D2) {
-                            p.w.Y[(size_t)(base + m) * s.d + n] = v * wrow;
-                        } else if constexpr (MODE == M_S2) {
-                            p.w.Ysh[((size_t)group * s.T + m) * s.d + n] = v;
-                        } else {
-                            p.w.logits[(size_t)m * s.E + n] = v;
-                        }
-                    }
-                }
+            for (int k = 0; k < 8; k++) {
+                const uint32_t by = ((k < 4 ? v.x : v.y) >> (8 * (k & 3))) & 0xffu;
+                ok = ok && (by == 255u || (by - 104u) <= 36u);
             }
         }
-        if (p.m_blocks > 1) break;
-        lds_barrier();  // LDS reuse by the next M pass
+        if (!__syncthreads_and(ok)) {
+            for (int m0 = 0; m0 < b.M; m0 += GM)
+                gemm_pass<MODE, GMT, true>(p, b, bsrc, m0, min(GM, b.M - m0), la, lb, lbs);
+            return;
+        }
+    }
+    if constexpr (C::kFp4) {
+        // routed experts: all of the group's rows, in passes of up to 128
+        for (int m0 = 0; m0 < b.M; m0 += GM) {
+            const int mrows = min(GM, b.M - m0);
+            switch ((mrows + 15) >> 4) {
+            case 1: gemm_pass<MODE, 1>(p, b, bsrc, m0, mrows, la, lb, lbs); break;
+            case 2: gemm_pass<MODE, 2>(p, b, bsrc, m0, mrows, la, lb, lbs); break;
+            case 3: gemm_pass<MODE, 3>(p, b, bsrc, m0, mrows, la, lb, lbs); break;
+            case 4: gemm_pass<MODE, 4>(p, b, bsrc, m0, mrows, la, lb, lbs); break;
+            case 5: gemm_pass<MODE, 5>(p, b, bsrc, m0, mrows, la, lb, lbs); break;
+            case 6: gemm_pass<MODE, 6>(p, b, bsrc, m0, mrows, la, lb, lbs); break;
+            case 7: gemm_pass<MODE, 7>(p, b, bsrc, m0, mrows, la, lb, lbs); break;
+            default: gemm_pass<MODE, 8>(p, b, bsrc, m0, mrows, la, lb, lbs); break;
+            }
+        }
+    } else {
+        // shared experts / router: one 128-row pass per block (a short last
+        // pass computes clamped copies of its last row, never stored)
+        const int m0 = b.mb * GM;
+        if (m0 < b.M) gemm_pass<MODE, GMT>(p, b, bsrc, m0, min(GM, b.M - m0), la, lb, lbs);
     }
 }
 
@@ -534,15 +682,18 @@ __global__ __launch_bounds__(256) void k_split_router(int E, int d, const float 
 
 bool mfma_supported(const Shape &s)
 {
-    // K of every GEMM a multiple of the 256-wide B stage; the 8 scale bytes of
-    // a column per stage are read as one 8-byte-aligned load
-    return s.d % 256 == 0 && s.F % 256 == 0;
+    // K of every GEMM a multiple of the 256-wide B stage (the 8 scale bytes of
+    // a column per stage are read as one 8-byte-aligned load) and every
+    // column tile full; activation operands addressed with 32-bit offsets
+    const size_t lim = (size_t)1 << 31;
+    return s.d % 256 == 0 && s.F % 256 == 0 && (size_t)s.T * s.k * s.F * 2 < lim &&
+           (size_t)s.T * s.d * 2 < lim && (size_t)s.T * s.S * s.F * 2 < lim;
 }
 
 // extra workspace of the MFMA path: router weights split in 3 bf16 parts
 size_t mfma_extra_workspace(const Shape &s)
 {
-    if (!mfma_supported(s)) return 0;
+    if (s.d % 256 != 0 || s.F % 256 != 0) return 0;  // independent of T: sizes stay monotone
     return (((size_t)s.E * 3 * s.d * 2) + 255) & ~(size_t)255;
 }
 

@@ -233,7 +233,7 @@ def test_graph_replay_matches_eager():
 MFMA_SHAPE = synth.LayerShape(n_experts=40, top_k=6, n_shared=2, d_model=512, d_ffn=768)
 
 
-@pytest.mark.parametrize("T", [1, 17, 130, 300])
+@pytest.mark.parametrize("T", [1, 17, 130, 300, 700])
 def test_mfma_path_parity(T):
     import quantized_expert_gemv_sigmoid_amd as moe
     log(f"case: MFMA path E40 k6 S2 d512 F768 T={T}")
@@ -281,3 +281,30 @@ def test_mfma_down_projection_out_of_fp16_window():
     h.w2s[rng.random(h.w2s.shape) < 0.03] = 255
     gl = make_gpu_layer(MFMA_SHAPE, 64, host=h, path=moe.PATH_MFMA)
     _full_check(gl, 150)
+
+
+def test_mfma_down_projection_mixed_blocks():
+    # Only the second 256-row tile of W2 of expert 3 leaves the fp16 window:
+    # row 400 has scale byte 141 everywhere (codes of magnitude >= 4 would
+    # overflow an fp16 decode) and row 300 one block at 90.  That block takes
+    # the split path, every other block the fp16 one.  Column 400 is ~2^20
+    # times larger than the rest, so it is compared on its own.
+    import quantized_expert_gemv_sigmoid_amd as moe
+    log("case: MFMA E40 k6 d512 F768 T=200, one W2 tile out of the fp16 window")
+    h = synth.host_layer(MFMA_SHAPE, 65, 0)
+    h.w2s[3, 400, :] = 141
+    h.w2s[3, 300, 5] = 90
+    h.router_bias = np.zeros(MFMA_SHAPE.n_experts, dtype=np.float32)
+    h.router_bias[3] = 4.0  # every token uses expert 3
+    gl = make_gpu_layer(MFMA_SHAPE, 65, host=h, path=moe.PATH_MFMA)
+    T = 200
+    x, rw, bias = tokens(gl, T, screened=False)
+    out_f, out_b, ids, w, cnt = run_layer(gl, x)
+    rids, rw_, gap, rout = oracle_outputs(gl, x, rw, bias, np.arange(T))
+    check_routing(ids, w, cnt, rids, rw_, gl.shape.n_experts, "routing")
+    assert cnt[3] == T
+    assert np.isfinite(out_f).all()
+    other = np.ones(MFMA_SHAPE.d_model, dtype=bool)
+    other[400] = False
+    assert_close(out_f[:, other], rout[:, other], "columns other than 400")
+    assert_close(out_f[:, 400:401], rout[:, 400:401], "column 400 (scale byte 141)")
