@@ -74,12 +74,32 @@ __device__ __forceinline__ float e8m0_to_f32(uint32_t b)
 
 __device__ __forceinline__ float sigmoidf_(float v) { return 1.0f / (1.0f + expf(-v)); }
 
+// exp(x) and 1/x on the hardware's v_exp_f32 (2^x) and v_rcp_f32, each
+// within about 1 ulp: a few instructions instead of a library expansion,
+// which keeps the activation epilogues of the unrolled GEMM tiles small
+__device__ __forceinline__ float exp_hw(float x) { return __builtin_amdgcn_exp2f(x * 1.44269504088896341f); }
+__device__ __forceinline__ float rcp_hw(float x) { return __builtin_amdgcn_rcpf(x); }
+__device__ __forceinline__ float sigmoid_hw(float x) { return rcp_hw(1.0f + exp_hw(-x)); }
+
+// tanh(x) = sign(x) (1 - e) / (1 + e) with e = exp(-2|x|); below |x| = 1/16
+// the odd Taylor polynomial to x^7 (next term < 3e-13 relative) replaces
+// the cancelling 1 - e
+__device__ __forceinline__ float tanh_hw(float x)
+{
+    const float ax = fabsf(x);
+    const float e = exp_hw(-2.0f * ax);
+    const float big = (1.0f - e) * rcp_hw(1.0f + e);
+    const float x2 = x * x;
+    const float small = ax * (1.0f + x2 * (-1.0f / 3.0f + x2 * (2.0f / 15.0f + x2 * (-17.0f / 315.0f))));
+    return copysignf(ax < 0.0625f ? small : big, x);
+}
+
 // gated activation of one (gate, up) pair: 0 = SiTU-GLU, 1 = SwiGLU
 __device__ __forceinline__ float gated_act(float g, float u, int act, float b1, float b2)
 {
-    if (act == 1) return g * sigmoidf_(g) * u;
-    const float a = b1 * tanhf(g / b1) * sigmoidf_(g);
-    const float v = b2 * tanhf(u / b2);
+    if (act == 1) return g * sigmoid_hw(g) * u;
+    const float a = b1 * tanh_hw(g / b1) * sigmoid_hw(g);
+    const float v = b2 * tanh_hw(u / b2);
     return a * v;
 }
 

@@ -12,22 +12,27 @@
 // experts (bf16) and the router (fp32) run through the same kernel as extra
 // groups.
 //
-// Block = 4 waves, 256 output columns (4 waves x 4 MFMA tiles of 16), all M
-// rows of the group in passes of 128 (8 MFMA tiles of 16).  K runs in chunks:
+// Block = 4 waves (one per SIMD), 256 output columns: wave w owns 64 of them
+// as two 32-column tiles of v_mfma_f32_32x32x16_{bf16,f16} (the 32x32 shape
+// sustains about twice the rate of 16x16x32 from one wave), and all M rows
+// of the group in passes of up to 128 (four 32-row tiles, the tile count a
+// compile-time parameter).  K runs in stages:
 //  - A (token rows, bf16 or fp16) is staged through LDS, double buffered, in
-//    16-byte pieces XOR-swizzled by row so the MFMA fragment reads are
-//    bank-conflict free;
-//  - B (weights) goes straight from HBM to registers (one 16-byte load per
-//    lane per chunk = one MX block of one column), is decoded there by
-//    v_cvt_scalef32_pk_{bf16,f16}_fp4 with its E8M0 scale (exact), and feeds
-//    v_mfma_f32_16x16x32_{bf16,f16} directly; the next chunk's loads are in
-//    flight while the current one is multiplied.
-// The K order inside a chunk is permuted identically for A and B (lane group
-// g of a column holds the chunk's g-th quarter of K), which is what lets one
-// lane load a whole MX block.
+//    16-byte pieces XOR-swizzled by row so the fragment reads are bank
+//    conflict free;
+//  - B (weights) is staged through LDS too, copied as 128-byte runs of each
+//    column; a lane reads its fragment for a whole A stage at once (two MX
+//    blocks), decodes it in registers with v_cvt_scalef32_pk_{bf16,f16}_fp4
+//    and its E8M0 scales (exact), and feeds the MFMAs;
+//  - global loads for stages ahead are in flight while a stage is multiplied,
+//    and the fragment reads / decodes of the next MFMA step overlap the
+//    current step's MFMAs.
+// The K order inside a stage is permuted identically for A and B (lane half
+// h of a column holds the stage's h-th half of K), which is what lets one
+// lane own whole MX blocks.
 //
 // Down projection precision: H is fp16 and W2 is decoded to fp16, exact for
-// scale bytes in [104, 140].  A chunk whose W2 scales fall outside takes an
+// scale bytes in [104, 140].  A block whose W2 scales fall outside takes an
 // exact fallback: W2 decoded to bf16 and each fp16 H value split into two
 // bf16 parts (hi + lo == h exactly), two bf16 MFMAs.
 #include "../../include/moe.h"
@@ -41,12 +46,12 @@ typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
 typedef _Float16 f16x8_t __attribute__((ext_vector_type(8)));
 typedef __bf16 bf16x2v_t __attribute__((ext_vector_type(2)));
 typedef _Float16 f16x2v_t __attribute__((ext_vector_type(2)));
+typedef float f32x16_t __attribute__((ext_vector_type(16)));
 
-constexpr int GW = 4;            // waves per block
-constexpr int GNS = 4;           // 16-column MFMA tiles per wave
-constexpr int GN = GW * GNS * 16;  // 256 output columns per block
-constexpr int GMT = 8;           // 16-row MFMA tiles per M pass
-constexpr int GM = GMT * 16;     // 128 rows per M pass
+constexpr int GT = 256;          // threads per block: 4 waves, one per SIMD
+constexpr int GN = 256;          // output columns per block (64 per wave: two 32-column tiles)
+constexpr int GMT = 4;           // 32-row MFMA tiles per M pass
+constexpr int GM = GMT * 32;     // 128 rows per M pass
 
 enum Mode { M_G13 = 0, M_D2 = 1, M_S13 = 2, M_S2 = 3, M_R = 4 };
 
@@ -72,7 +77,6 @@ __device__ __forceinline__ uint4 gld16(const void *p) { return *reinterpret_cast
 // pointers would let the compiler fall back to flat instructions)
 #define LDS __attribute__((address_space(3)))
 typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
-typedef uint32_t u32x2_t __attribute__((ext_vector_type(2)));
 __device__ __forceinline__ uint4 lds_ld16(const LDS uint8_t *p)
 {
     return __builtin_bit_cast(uint4, *reinterpret_cast<const LDS u32x4_t *>(p));
@@ -81,10 +85,7 @@ __device__ __forceinline__ void lds_st16(LDS uint8_t *p, uint4 v)
 {
     *reinterpret_cast<LDS u32x4_t *>(p) = __builtin_bit_cast(u32x4_t, v);
 }
-__device__ __forceinline__ void lds_st8(LDS uint8_t *p, uint2 v)
-{
-    *reinterpret_cast<LDS u32x2_t *>(p) = __builtin_bit_cast(u32x2_t, v);
-}
+__device__ __forceinline__ void lds_st4(LDS uint8_t *p, uint32_t v) { *reinterpret_cast<LDS uint32_t *>(p) = v; }
 
 // Workgroup barrier for the LDS stages only: waits for this wave's LDS
 // writes (lgkmcnt 0), not for its outstanding global loads, so prefetches
@@ -102,7 +103,7 @@ template <int KC>
 __device__ __forceinline__ int lds_off(int r, int q)
 {
     if constexpr (KC == 128) return r * KC + ((q ^ (r & 15)) << 3);
-    else return r * KC + ((q ^ ((r >> 1) & 7)) << 3);
+    else return r * KC + ((q ^ (r & 7)) << 3);
 }
 
 __device__ __forceinline__ float e8m0f(uint32_t b)
@@ -136,23 +137,24 @@ struct Cfg {
     static constexpr int KCA = kFp4 ? 128 : 64;
     static constexpr int KCB = kFp4 ? 256 : 64;
     static constexpr int R = KCB / KCA;                 // A stages per B stage
-    static constexpr int STEPS = KCA / 32;              // MFMA K steps per A stage
+    static constexpr int STEPS = KCA / 16;              // MFMA K steps per A stage
     static constexpr int QPR = KCA / 8;                 // 16-byte A pieces per row of a stage
-    static constexpr int RPP = 256 / QPR;               // A rows staged per pass
+    static constexpr int RPP = GT / QPR;                // A rows staged per pass
     static constexpr int BSC = kFp4 ? KCB / 32 : 0;     // scale bytes per column per B stage
-    static constexpr int BPASS = GN / 32;               // B staging passes (32 columns each)
+    static constexpr int BPASS = GN * 8 / GT;           // B staging passes (32 columns each)
 };
 
-// K order inside an A stage: MFMA step st, lane group kg (lane / 16) and
-// element i (0..7) of a fragment multiply K index kg * (KCA / 4) + st * 8 + i
-// of the stage, for A and B alike.  A lane's fragments over the stage's
-// steps are then one contiguous run of K: for MXFP4 exactly one MX block (32
-// codes, one scale), read from LDS as one 16-byte piece.  A-stage piece q
-// (8 elements) is kg * STEPS + st.
+// K order inside an A stage: MFMA step st, lane half kh (lane / 32) and
+// element i (0..7) of a fragment multiply K index kh * (KCA / 2) + st * 8 + i
+// of the stage, for A and B alike.  A lane's fragments over the stage are
+// then one contiguous run of K: for MXFP4 two whole MX blocks (64 codes, two
+// scales), read from LDS as two 16-byte pieces.  A-stage piece q (8
+// elements) is kh * STEPS + st.
 
 // byte offset of 16-byte piece p of column c inside a B stage (8 pieces per
-// column, XOR-swizzled so the fragment reads of 16 columns hit distinct banks)
-__device__ __forceinline__ int b_off(int c, int p) { return c * 128 + ((p ^ ((c >> 1) & 7)) << 4); }
+// column, XOR-swizzled so the fragment reads of 8 consecutive columns hit
+// distinct banks)
+__device__ __forceinline__ int b_off(int c, int p) { return c * 128 + ((p ^ (c & 7)) << 4); }
 
 // 8 E2M1 codes (one dword, low nibble first) times the scale sc (a power of
 // two) -> 8 bf16 / fp16 values
@@ -185,6 +187,15 @@ __device__ __forceinline__ uint32_t u4at(const uint4 &q, int i)
     return i == 0 ? q.x : (i == 1 ? q.y : (i == 2 ? q.z : q.w));
 }
 
+__device__ __forceinline__ f32x16_t mfma32(bf16x8_t a, bf16x8_t b, f32x16_t c)
+{
+    return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
+}
+__device__ __forceinline__ f32x16_t mfma32(f16x8_t a, f16x8_t b, f32x16_t c)
+{
+    return __builtin_amdgcn_mfma_f32_32x32x16_f16(a, b, c, 0, 0, 0);
+}
+
 // Per-block geometry: which group (expert / shared expert / router) and
 // which 256-column tile this block computes.
 struct Blk {
@@ -193,20 +204,26 @@ struct Blk {
 };
 
 // Global sources of this thread's B staging copies: 16-byte piece (t % 8)
-// of block columns ps * 32 + t / 8 (ps < BPASS), and (MXFP4) the scales of
-// column t.  Bases are uniform over the block, offsets are 32-bit bytes, so
-// the loads take the scalar-base + vector-offset form.  Every column of an
-// expert's tile is in range (the path requires d and F to be multiples of
-// 256); the router's columns past E re-read row E - 1 and are never stored.
+// of block columns ps * 32 + t / 8 (ps < BPASS), and (MXFP4) the 8 scale
+// bytes per stage of column t.  Offsets are 32-bit bytes from a 64-bit base.
+// Every column of an expert's tile is in range (the path requires d and F
+// to be multiples of 256); the router's columns past E re-read row E - 1
+// and are never stored.
 template <int MODE>
 struct BSrc {
     const uint8_t *base0, *base1;  // gated: gate / up weights (even / odd passes)
     uint32_t off;                  // this thread's pass-0 column row + piece
     uint32_t pstride;              // bytes between the rows of consecutive passes (gated: pass pairs)
     uint32_t roff[MODE == M_R ? Cfg<MODE>::BPASS : 1];  // router: clamped per-pass rows
-    const uint8_t *sbase;          // MXFP4 scales of column t: sbase + soff
+    const uint8_t *sbase;          // MXFP4 scales of column t: sbase + soff + stage offset
     uint32_t soff;
 };
+
+// block column c (0..255) of a gated tile -> feature and gate / up: wave
+// w = c / 64 holds features tile * 128 + w * 32 + 0..31, the gate ones in
+// its first 32 columns and the up ones in the next 32
+__device__ __forceinline__ int gated_feature(int tile, int c) { return tile * 128 + (c >> 6) * 32 + (c & 31); }
+__device__ __forceinline__ bool gated_up(int c) { return (c >> 5) & 1; }
 
 template <int MODE>
 __device__ __forceinline__ BSrc<MODE> make_bsrc(const GemmParams &p, const Blk &b)
@@ -215,25 +232,24 @@ __device__ __forceinline__ BSrc<MODE> make_bsrc(const GemmParams &p, const Blk &
     const Shape &s = p.s;
     const int t = threadIdx.x;
     const uint32_t piece = (t & 7) * 16;
+    const int c0 = t >> 3;  // block column of pass 0 (pass ps adds 32 ps)
     BSrc<MODE> r;
     r.base1 = nullptr;
     r.sbase = nullptr;
     r.soff = 0;
     r.roff[0] = 0;
     if constexpr (C::kGated) {
-        // block column cc = ps * 32 + t / 8: wave part ps / 2, up if ps is odd,
-        // feature tile * 128 + (ps / 2) * 32 + ((t / 128) & 1) * 16 + (t / 8) % 16
-        const uint32_t f0 = b.tile * 128 + ((t >> 7) & 1) * 16 + ((t >> 3) & 15);
+        // pass ps copies column ps * 32 + c0: wave part ps / 2, up if ps is
+        // odd, feature gated_feature(tile, c0) + (ps / 2) * 32
+        const uint32_t f0 = gated_feature(b.tile, c0);
         if constexpr (MODE == M_G13) {
             const size_t eo = (size_t)b.e * s.F * (s.d / 2);
             r.base0 = p.w1q + eo;
             r.base1 = p.w3q + eo;
             r.off = f0 * (s.d / 2) + piece;
             r.pstride = 32 * (s.d / 2);
-            // scales of block column t
-            const int fs = b.tile * 128 + (t >> 6) * 32 + ((t >> 4) & 1) * 16 + (t & 15);
-            r.sbase = (((t >> 5) & 1) ? p.w3s : p.w1s) + (size_t)b.e * s.F * (s.d / 32);
-            r.soff = fs * (s.d / 32);
+            r.sbase = (gated_up(t) ? p.w3s : p.w1s) + (size_t)b.e * s.F * (s.d / 32);
+            r.soff = gated_feature(b.tile, t) * (s.d / 32);
         } else {
             const size_t go = (size_t)b.group * s.F * s.d * 2;
             r.base0 = reinterpret_cast<const uint8_t *>(p.sh1) + go;
@@ -243,13 +259,13 @@ __device__ __forceinline__ BSrc<MODE> make_bsrc(const GemmParams &p, const Blk &
         }
     } else if constexpr (MODE == M_D2) {
         r.base0 = p.w2q + (size_t)b.e * s.d * (s.F / 2);
-        r.off = (b.tile * GN + (t >> 3)) * (s.F / 2) + piece;
+        r.off = (b.tile * GN + c0) * (s.F / 2) + piece;
         r.pstride = 32 * (s.F / 2);
         r.sbase = p.w2s + (size_t)b.e * s.d * (s.F / 32);
         r.soff = (b.tile * GN + t) * (s.F / 32);
     } else if constexpr (MODE == M_S2) {
         r.base0 = reinterpret_cast<const uint8_t *>(p.sh2) + (size_t)b.group * s.d * s.F * 2;
-        r.off = (b.tile * GN + (t >> 3)) * (s.F * 2) + piece;
+        r.off = (b.tile * GN + c0) * (s.F * 2) + piece;
         r.pstride = 32 * (s.F * 2);
     } else {
         r.base0 = reinterpret_cast<const uint8_t *>(p.wr3);
@@ -257,15 +273,16 @@ __device__ __forceinline__ BSrc<MODE> make_bsrc(const GemmParams &p, const Blk &
         r.pstride = 0;
 #pragma unroll
         for (int ps = 0; ps < C::BPASS; ps++) {
-            const int n = min(b.tile * GN + ps * 32 + (t >> 3), s.E - 1);
+            const int n = min(b.tile * GN + ps * 32 + c0, s.E - 1);
             r.roff[ps] = (uint32_t)n * (3 * s.d * 2);
         }
     }
     return r;
 }
 
-// One M pass of MT 16-row tiles (rows m0 .. m0 + mrows - 1 of the group)
-// over the whole K, then its epilogue.  la / lb / lbs: the LDS stages.
+// One M pass of MT 32-row tiles (rows m0 .. m0 + mrows - 1 of the group)
+// over the whole K, then its epilogue.  la / lb / lbs: the LDS stages.  Wave
+// w computes block columns 64 w .. 64 w + 63 as two 32-column MFMA tiles.
 template <int MODE, int MT, bool SPLIT = false>
 __device__ __forceinline__ void gemm_pass(const GemmParams &p, const Blk &bk, const BSrc<MODE> &bsrc,
                                           int m0, int mrows, LDS uint16_t *la, LDS uint8_t *lb,
@@ -273,20 +290,20 @@ __device__ __forceinline__ void gemm_pass(const GemmParams &p, const Blk &bk, co
 {
     using C = Cfg<MODE>;
     constexpr int KCA = C::KCA, R = C::R, STEPS = C::STEPS, QPR = C::QPR, RPP = C::RPP;
-    constexpr int NPASS = (MT * 16 + RPP - 1) / RPP;  // A staging passes for MT tiles
+    constexpr int NPASS = (MT * 32 + RPP - 1) / RPP;  // A staging passes for MT tiles
     constexpr int ASTAGE = GM * KCA;                  // elements per A stage
     constexpr int BSTAGE = GN * 128;                  // bytes per B stage
     constexpr int SSTAGE = GN * (C::kFp4 ? C::BSC : 1);
     const Shape &s = p.s;
     const int t = threadIdx.x;
     const int lane = t & 63, wave = t >> 6;
-    const int col = lane & 15, kg = lane >> 4;
+    const int col = lane & 31, kh = lane >> 5;
     const int nA = bk.nA, nB = bk.nB;
 
     // ---- A staging: this thread copies piece qa of rows ps * RPP + t / QPR
     // (rows past the group's end re-read its last row; their results are
-    // never stored)
-    // byte offsets (32-bit: the host checks that every A operand is below 2 GiB)
+    // never stored).  Byte offsets are 32-bit: the host checks that every A
+    // operand is below 2 GiB.
     const int qa = t % QPR;
     uint32_t arow[NPASS];
 #pragma unroll
@@ -356,59 +373,63 @@ __device__ __forceinline__ void gemm_pass(const GemmParams &p, const Blk &bk, co
             const int cc = ps * 32 + (t >> 3);
             lds_st16(lb + stage * BSTAGE + b_off(cc, bpiece), br.v[ps]);
         }
-        if constexpr (C::kFp4) lds_st8(lbs + stage * SSTAGE + t * C::BSC, br.sc);
+        if constexpr (C::kFp4) {
+            lds_st4(lbs + stage * SSTAGE + t * C::BSC, br.sc.x);
+            lds_st4(lbs + stage * SSTAGE + t * C::BSC + 4, br.sc.y);
+        }
     };
 
-    f32x4_t acc[MT][GNS];
+    f32x16_t acc[MT][2];
 #pragma unroll
-    for (int mt = 0; mt < MT; mt++)
-#pragma unroll
-        for (int j = 0; j < GNS; j++) acc[mt][j] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+    for (int i = 0; i < MT; i++) {
+        acc[i][0] = (f32x16_t)0.0f;
+        acc[i][1] = (f32x16_t)0.0f;
+    }
 
+    // A fragment of tile mt, step st: row mt * 32 + col, 8 values of piece kh * STEPS + st
     auto a_frag = [&](const LDS uint16_t *A, int mt, int st) __attribute__((always_inline)) -> uint4 {
-        return lds_ld16(reinterpret_cast<const LDS uint8_t *>(A + lds_off<KCA>(mt * 16 + col, kg * STEPS + st)));
+        return lds_ld16(reinterpret_cast<const LDS uint8_t *>(A + lds_off<KCA>(mt * 32 + col, kh * STEPS + st)));
     };
 
     // One A stage (STEPS MFMA K steps) against sub-stage `sub` of a B stage.
     // Software pipelined: the A fragments and decoded B fragments of step
-    // st + 1 are read / decoded while the MFMAs of step st run (the
-    // scheduling fences keep the compiler from sinking the reads back next
-    // to their uses).
+    // st + 1 are read / decoded while the MFMAs of step st run.
     auto compute = [&](int sa, int sb, int sub) __attribute__((always_inline)) {
         const LDS uint16_t *A = la + sa * ASTAGE;
         const LDS uint8_t *B = lb + sb * BSTAGE;
         uint4 af[2][MT];
         if constexpr (C::kFp4) {
             using BT = typename std::conditional<MODE == M_D2, f16x8_t, bf16x8_t>::type;
-            // this lane's MX block of each of its 4 columns: 16 bytes + scale
-            uint4 q[GNS];
-            uint32_t sc[GNS];
+            // this lane's two MX blocks (sub * 4 + kh * 2 + {0, 1}) of each of
+            // its 2 columns: 32 bytes + 2 scales
+            uint4 q[2][2];
+            float scf[2][2];
 #pragma unroll
-            for (int j = 0; j < GNS; j++) {
-                const int cc = wave * 64 + j * 16 + col;
-                q[j] = lds_ld16(B + b_off(cc, sub * 4 + kg));
-                sc[j] = lbs[sb * SSTAGE + cc * C::BSC + sub * 4 + kg];
-            }
-            float scf[GNS];
+            for (int nb = 0; nb < 2; nb++) {
+                const int cc = wave * 64 + nb * 32 + col;
+                const int blk = sub * 4 + kh * 2;
+                q[nb][0] = lds_ld16(B + b_off(cc, blk));
+                q[nb][1] = lds_ld16(B + b_off(cc, blk + 1));
+                const uint32_t s2 = *reinterpret_cast<const LDS uint16_t *>(lbs + sb * SSTAGE + cc * C::BSC + blk);
 #pragma unroll
-            for (int j = 0; j < GNS; j++) {
-                // NaN scale (255): the block contributes 0
-                const uint32_t keep = sc[j] == 255u ? 0u : ~0u;
-                q[j].x &= keep; q[j].y &= keep; q[j].z &= keep; q[j].w &= keep;
-                scf[j] = e8m0f(sc[j] == 255u ? 127u : sc[j]);
+                for (int h = 0; h < 2; h++) {
+                    // NaN scale (255): the block contributes 0
+                    const uint32_t sc = (s2 >> (8 * h)) & 0xffu;
+                    const uint32_t keep = sc == 255u ? 0u : ~0u;
+                    q[nb][h].x &= keep; q[nb][h].y &= keep; q[nb][h].z &= keep; q[nb][h].w &= keep;
+                    scf[nb][h] = e8m0f(sc == 255u ? 127u : sc);
+                }
             }
             if constexpr (!SPLIT) {
-                // fragments of the first PF tiles are prefetched one step
-                // ahead, the rest (large tiles only) read in their step
-                constexpr int PF = MT <= 6 ? MT : 4;
 #pragma unroll
-                for (int mt = 0; mt < PF; mt++) af[0][mt] = a_frag(A, mt, 0);
-                BT b[2][GNS];
-                auto decode = [&](BT (&bb)[GNS], int st) __attribute__((always_inline)) {
+                for (int mt = 0; mt < MT; mt++) af[0][mt] = a_frag(A, mt, 0);
+                BT b[2][2];
+                auto decode = [&](BT (&bb)[2], int st) __attribute__((always_inline)) {
 #pragma unroll
-                    for (int j = 0; j < GNS; j++) {
-                        if constexpr (MODE == M_D2) bb[j] = cvt8_f16(u4at(q[j], st), scf[j]);
-                        else bb[j] = cvt8_bf16(u4at(q[j], st), scf[j]);
+                    for (int nb = 0; nb < 2; nb++) {
+                        const uint32_t w = u4at(q[nb][st >> 2], st & 3);
+                        if constexpr (MODE == M_D2) bb[nb] = cvt8_f16(w, scf[nb][st >> 2]);
+                        else bb[nb] = cvt8_bf16(w, scf[nb][st >> 2]);
                     }
                 };
                 decode(b[0], 0);
@@ -417,21 +438,13 @@ __device__ __forceinline__ void gemm_pass(const GemmParams &p, const Blk &bk, co
                     const int cur = st & 1, nxt = cur ^ 1;
                     if (st + 1 < STEPS) {
 #pragma unroll
-                        for (int mt = 0; mt < PF; mt++) af[nxt][mt] = a_frag(A, mt, st + 1);
+                        for (int mt = 0; mt < MT; mt++) af[nxt][mt] = a_frag(A, mt, st + 1);
                         decode(b[nxt], st + 1);
                     }
 #pragma unroll
                     for (int mt = 0; mt < MT; mt++) {
-                        const uint4 a = mt < PF ? af[cur][mt] : a_frag(A, mt, st);
 #pragma unroll
-                        for (int j = 0; j < GNS; j++) {
-                            if constexpr (MODE == M_D2)
-                                acc[mt][j] = __builtin_amdgcn_mfma_f32_16x16x32_f16(
-                                    __builtin_bit_cast(f16x8_t, a), b[cur][j], acc[mt][j], 0, 0, 0);
-                            else
-                                acc[mt][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
-                                    __builtin_bit_cast(bf16x8_t, a), b[cur][j], acc[mt][j], 0, 0, 0);
-                        }
+                        for (int nb = 0; nb < 2; nb++) acc[mt][nb] = mfma32(__builtin_bit_cast(BT, af[cur][mt]), b[cur][nb], acc[mt][nb]);
                     }
                     __builtin_amdgcn_sched_barrier(0);
                 }
@@ -439,18 +452,18 @@ __device__ __forceinline__ void gemm_pass(const GemmParams &p, const Blk &bk, co
                 // exact fallback: bf16 weights, fp16 inputs split in two bf16 parts
 #pragma unroll
                 for (int st = 0; st < STEPS; st++) {
-                    bf16x8_t b[GNS];
+                    bf16x8_t b[2];
 #pragma unroll
-                    for (int j = 0; j < GNS; j++) b[j] = cvt8_bf16(u4at(q[j], st), scf[j]);
+                    for (int nb = 0; nb < 2; nb++) b[nb] = cvt8_bf16(u4at(q[nb][st >> 2], st & 3), scf[nb][st >> 2]);
 #pragma unroll
                     for (int mt = 0; mt < MT; mt++) {
                         // one fragment at a time (a rare path; keeps its registers few)
                         bf16x8_t ah, al;
                         split_f16(__builtin_bit_cast(f16x8_t, a_frag(A, mt, st)), ah, al);
 #pragma unroll
-                        for (int j = 0; j < GNS; j++) {
-                            acc[mt][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ah, b[j], acc[mt][j], 0, 0, 0);
-                            acc[mt][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(al, b[j], acc[mt][j], 0, 0, 0);
+                        for (int nb = 0; nb < 2; nb++) {
+                            acc[mt][nb] = mfma32(ah, b[nb], acc[mt][nb]);
+                            acc[mt][nb] = mfma32(al, b[nb], acc[mt][nb]);
                         }
                         __builtin_amdgcn_sched_barrier(0);
                     }
@@ -458,13 +471,10 @@ __device__ __forceinline__ void gemm_pass(const GemmParams &p, const Blk &bk, co
                 }
             }
         } else {
-            uint4 b[2][GNS];
-            auto read_b = [&](uint4 (&bb)[GNS], int st) __attribute__((always_inline)) {
+            uint4 b[2][2];
+            auto read_b = [&](uint4 (&bb)[2], int st) __attribute__((always_inline)) {
 #pragma unroll
-                for (int j = 0; j < GNS; j++) {
-                    const int cc = wave * 64 + j * 16 + col;
-                    bb[j] = lds_ld16(B + b_off(cc, kg * STEPS + st));
-                }
+                for (int nb = 0; nb < 2; nb++) bb[nb] = lds_ld16(B + b_off(wave * 64 + nb * 32 + col, kh * STEPS + st));
             };
             read_b(b[0], 0);
 #pragma unroll
@@ -480,10 +490,9 @@ __device__ __forceinline__ void gemm_pass(const GemmParams &p, const Blk &bk, co
 #pragma unroll
                 for (int mt = 0; mt < MT; mt++)
 #pragma unroll
-                    for (int j = 0; j < GNS; j++)
-                        acc[mt][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
-                            __builtin_bit_cast(bf16x8_t, af[cur][mt]), __builtin_bit_cast(bf16x8_t, b[cur][j]),
-                            acc[mt][j], 0, 0, 0);
+                    for (int nb = 0; nb < 2; nb++)
+                        acc[mt][nb] = mfma32(__builtin_bit_cast(bf16x8_t, af[cur][mt]),
+                                             __builtin_bit_cast(bf16x8_t, b[cur][nb]), acc[mt][nb]);
                 __builtin_amdgcn_sched_barrier(0);
             }
         }
@@ -521,40 +530,36 @@ __device__ __forceinline__ void gemm_pass(const GemmParams &p, const Blk &bk, co
         load_b(br, min((i + 1) / R + 2, nB - 1));
     }
 
-    // ---- epilogue (D lane layout: register i of tile (mt, j) holds row
-    // mt * 16 + 4 * kg + i, column j * 16 + col of the wave's 64)
+    // ---- epilogue (D lane layout: register e of tile (mt, nb) holds row
+    // mt * 32 + 8 (e / 4) + 4 kh + e % 4, column nb * 32 + col of the wave's 64)
 #pragma unroll
     for (int mt = 0; mt < MT; mt++) {
 #pragma unroll
-        for (int i = 0; i < 4; i++) {
-            const int r = mt * 16 + kg * 4 + i;
+        for (int e = 0; e < 16; e++) {
+            const int r = mt * 32 + 8 * (e >> 2) + 4 * kh + (e & 3);
             if (r >= mrows) continue;
             const int m = m0 + r;
             if constexpr (C::kGated) {
-#pragma unroll
-                for (int j = 0; j < 2; j++) {
-                    const int f = bk.tile * 128 + wave * 32 + j * 16 + col;
-                    if (f >= s.F) continue;
-                    const float h = gated_act(acc[mt][j][i], acc[mt][j + 2][i], s.act, s.b1, s.b2);
-                    if constexpr (MODE == M_G13) {
-                        _Float16 *H = reinterpret_cast<_Float16 *>(p.w.H);
-                        H[(size_t)(bk.base + m) * s.F + f] = (_Float16)h;
-                    } else {
-                        const uint16_t hi = f32_to_bf16_rne(h);
-                        const uint16_t lo = f32_to_bf16_rne(h - __uint_as_float((uint32_t)hi << 16));
-                        const size_t o = (size_t)m * s.S * s.F + (size_t)bk.group * s.F + f;
-                        p.hs_hi_w[o] = hi;
-                        p.hs_lo_w[o] = lo;
-                    }
+                const int f = bk.tile * 128 + wave * 32 + col;
+                const float hv = gated_act(acc[mt][0][e], acc[mt][1][e], s.act, s.b1, s.b2);
+                if constexpr (MODE == M_G13) {
+                    _Float16 *H = reinterpret_cast<_Float16 *>(p.w.H);
+                    H[(size_t)(bk.base + m) * s.F + f] = (_Float16)hv;
+                } else {
+                    const uint16_t hi = f32_to_bf16_rne(hv);
+                    const uint16_t lo = f32_to_bf16_rne(hv - __uint_as_float((uint32_t)hi << 16));
+                    const size_t o = (size_t)m * s.S * s.F + (size_t)bk.group * s.F + f;
+                    p.hs_hi_w[o] = hi;
+                    p.hs_lo_w[o] = lo;
                 }
             } else {
                 float wrow = 1.0f;
                 if constexpr (MODE == M_D2) wrow = p.w.pos_w[bk.base + m];
 #pragma unroll
-                for (int j = 0; j < GNS; j++) {
-                    const int n = bk.tile * GN + wave * 64 + j * 16 + col;
+                for (int nb = 0; nb < 2; nb++) {
+                    const int n = bk.tile * GN + wave * 64 + nb * 32 + col;
                     if (n >= bk.ncols) continue;
-                    const float v = acc[mt][j][i];
+                    const float v = acc[mt][nb][e];
                     if constexpr (MODE == M_D2) p.w.Y[(size_t)(bk.base + m) * s.d + n] = v * wrow;
                     else if constexpr (MODE == M_S2) p.w.Ysh[((size_t)bk.group * s.T + m) * s.d + n] = v;
                     else p.w.logits[(size_t)m * s.E + n] = v;
@@ -565,7 +570,7 @@ __device__ __forceinline__ void gemm_pass(const GemmParams &p, const Blk &bk, co
 }
 
 template <int MODE>
-__global__ __launch_bounds__(256) void k_ggemm(GemmParams p)
+__global__ __launch_bounds__(GT) void k_ggemm(GemmParams p)
 {
     using C = Cfg<MODE>;
     __shared__ __attribute__((aligned(16))) uint16_t lds_a[2 * GM * C::KCA];
@@ -618,13 +623,13 @@ __global__ __launch_bounds__(256) void k_ggemm(GemmParams p)
         // is exact for scale bytes 104..140 (and 255, which decodes to 0).
         // A block whose W2 scales leave that range takes the exact split
         // path (bf16 weights, H split into two bf16 parts) for all its rows.
-        const uint8_t *sc = bsrc.sbase + bsrc.soff;  // scales of block column t
+        const uint8_t *sc = p.w2s + ((size_t)b.e * s.d + b.tile * GN + threadIdx.x) * (s.F / 32);
         bool ok = true;
-        for (int i = 0; i < s.F / 32; i += 8) {
-            const uint2 v = *reinterpret_cast<const uint2 *>(sc + i);
+        for (int i = 0; i < s.F / 32; i += 4) {
+            const uint32_t v = *reinterpret_cast<const uint32_t *>(sc + i);
 #pragma unroll
-            for (int k = 0; k < 8; k++) {
-                const uint32_t by = ((k < 4 ? v.x : v.y) >> (8 * (k & 3))) & 0xffu;
+            for (int k = 0; k < 4; k++) {
+                const uint32_t by = (v >> (8 * k)) & 0xffu;
                 ok = ok && (by == 255u || (by - 104u) <= 36u);
             }
         }
@@ -638,15 +643,11 @@ __global__ __launch_bounds__(256) void k_ggemm(GemmParams p)
         // routed experts: all of the group's rows, in passes of up to 128
         for (int m0 = 0; m0 < b.M; m0 += GM) {
             const int mrows = min(GM, b.M - m0);
-            switch ((mrows + 15) >> 4) {
+            switch ((mrows + 31) >> 5) {
             case 1: gemm_pass<MODE, 1>(p, b, bsrc, m0, mrows, la, lb, lbs); break;
             case 2: gemm_pass<MODE, 2>(p, b, bsrc, m0, mrows, la, lb, lbs); break;
             case 3: gemm_pass<MODE, 3>(p, b, bsrc, m0, mrows, la, lb, lbs); break;
-            case 4: gemm_pass<MODE, 4>(p, b, bsrc, m0, mrows, la, lb, lbs); break;
-            case 5: gemm_pass<MODE, 5>(p, b, bsrc, m0, mrows, la, lb, lbs); break;
-            case 6: gemm_pass<MODE, 6>(p, b, bsrc, m0, mrows, la, lb, lbs); break;
-            case 7: gemm_pass<MODE, 7>(p, b, bsrc, m0, mrows, la, lb, lbs); break;
-            default: gemm_pass<MODE, 8>(p, b, bsrc, m0, mrows, la, lb, lbs); break;
+            default: gemm_pass<MODE, 4>(p, b, bsrc, m0, mrows, la, lb, lbs); break;
             }
         }
     } else {
@@ -706,7 +707,7 @@ static void launch_mode(const GemmParams &p0, int groups, int n_tiles, int m_blo
     p.m_blocks = m_blocks;
     const int padded = groups >= 8 ? (groups + 7) / 8 * 8 : groups;
     const int nblk = padded * n_tiles * m_blocks;
-    if (nblk > 0) k_ggemm<MODE><<<nblk, 256, 0, st>>>(p);
+    if (nblk > 0) k_ggemm<MODE><<<nblk, GT, 0, st>>>(p);
 }
 
 static GemmParams make_gemm_params(const Shape &s, const uint16_t *x, const Weights &wt, const Work &w)
