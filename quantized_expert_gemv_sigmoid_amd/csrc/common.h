@@ -103,6 +103,25 @@ __device__ __forceinline__ float gated_act(float g, float u, int act, float b1, 
     return a * v;
 }
 
+template <int CTRL>
+__device__ __forceinline__ float dppf(float v)
+{
+    return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), CTRL, 0xF, 0xF, true));
+}
+
+// all-reduce sum over groups of L consecutive lanes (L = 16, 32, 64)
+template <int L>
+__device__ __forceinline__ float group_sum(float v)
+{
+    v += dppf<0xB1>(v);   // quad_perm [1,0,3,2]
+    v += dppf<0x4E>(v);   // quad_perm [2,3,0,1]
+    v += dppf<0x141>(v);  // row_half_mirror
+    v += dppf<0x140>(v);  // row_mirror
+    if (L >= 32) v += __shfl_xor(v, 16, 64);
+    if (L >= 64) v += __shfl_xor(v, 32, 64);
+    return v;
+}
+
 // butterfly sum over the 64 lanes of a wave: every lane gets the total
 __device__ __forceinline__ float wave_sum(float v)
 {
@@ -236,5 +255,14 @@ hipError_t launch_mfma_experts(const Shape &s, const uint16_t *x, const Weights 
 //                 + sum over shared experts of Ysh[s][t]
 hipError_t launch_combine(const Shape &s, int include_shared, const Work &w, uint16_t *out_bf16,
                           float *out_f32, hipStream_t stream);
+
+// fused one-token decode after launch_front: top-k (do_topk) or the given
+// ids / weights, routed gate/up (+ shared down), routed down + combine into
+// out_bf16 / out_f32.  ev2 (optional): events after each of the two launches.
+bool decode1_supported(const Shape &s);
+hipError_t launch_decode1(const Shape &s, const uint16_t *x, const Weights &wt, const float *bias,
+                          int do_topk, int32_t *ids, float *wts, int32_t *counts_out, int shared,
+                          const Work &w, uint16_t *out_bf16, float *out_f32, hipStream_t stream,
+                          hipEvent_t const *ev2);
 
 }  // namespace moe

@@ -36,25 +36,6 @@ struct GemvParams {
 
 __device__ __forceinline__ uint4 ld16(const void *p) { return *reinterpret_cast<const uint4 *>(p); }
 
-template <int CTRL>
-__device__ __forceinline__ float dppf(float v)
-{
-    return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), CTRL, 0xF, 0xF, true));
-}
-
-// all-reduce sum over groups of L consecutive lanes (L = 16, 32, 64)
-template <int L>
-__device__ __forceinline__ float group_sum(float v)
-{
-    v += dppf<0xB1>(v);   // quad_perm [1,0,3,2]
-    v += dppf<0x4E>(v);   // quad_perm [2,3,0,1]
-    v += dppf<0x141>(v);  // row_half_mirror
-    v += dppf<0x140>(v);  // row_mirror
-    if (L >= 32) v += __shfl_xor(v, 16, 64);
-    if (L >= 64) v += __shfl_xor(v, 32, 64);
-    return v;
-}
-
 // ------------------------------------------------------------ shared experts
 
 // gate/up of shared expert sidx, 2 rows per wave (8 per block), NT tokens at a time

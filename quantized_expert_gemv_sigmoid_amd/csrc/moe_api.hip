@@ -180,6 +180,16 @@ moe_status run_layer(const moe_layer_desc *d, const Shape &s, const uint16_t *x,
         MOE_TRY(moe::launch_front(s, x, wt, do_router, front_shared, w, st));
     }
     MOE_TRY(mark(ev, 1, st));
+    if (experts && path == MOE_PATH_GEMV && moe::decode1_supported(s)) {
+        // one token: top-k, dispatch and combine fused into the expert kernels
+        MOE_TRY(mark(ev, 2, st));
+        MOE_TRY(moe::launch_decode1(s, x, wt, d->router_bias, do_router, ids, wts, counts_out, shared,
+                                    w, out_mode != MOE_OUT_F32 ? out_bf16 : nullptr,
+                                    out_mode != MOE_OUT_BF16 ? out_f32 : nullptr, st,
+                                    ev ? ev + 3 : nullptr));
+        MOE_TRY(mark(ev, 5, st));
+        return MOE_OK;
+    }
     MOE_TRY(moe::launch_dispatch(s, do_router, w.logits, d->router_bias, ids, wts, counts_out, w,
                                  st));
     MOE_TRY(mark(ev, 2, st));

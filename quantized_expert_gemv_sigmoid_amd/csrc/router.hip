@@ -26,39 +26,12 @@ __device__ __forceinline__ void topk_wave(int E, int k, const float *__restrict_
                                           float *__restrict__ w_out)
 {
     const int lane = threadIdx.x & 63;
-    uint64_t key[EPL];
-#pragma unroll
-    for (int i = 0; i < EPL; i++) {
-        // branch-free (a branch per element makes the compiler copy the whole array)
-        const int e = lane + 64 * i;
-        const int ec = e < E ? e : E - 1;
-        const float sc = sigmoidf_(lrow[ec]);
-        const uint64_t kk = select_key(sc + (bias ? bias[ec] : 0.0f), e);
-        key[i] = e < E ? kk : 0ull;  // padding is never selected: real keys are > 0
-    }
-    int my_id = 0;
-#pragma unroll 1
-    for (int j = 0; j < k; j++) {
-        uint64_t best = 0;
-#pragma unroll
-        for (int i = 0; i < EPL; i++) best = key[i] > best ? key[i] : best;
-        const uint64_t win = wave_max_u64(best);
-        const int e = (int)(~(uint32_t)win);
-        const bool mine = (e & 63) == lane;
-#pragma unroll
-        for (int i = 0; i < EPL; i++) key[i] = (mine && i == (e >> 6)) ? 0ull : key[i];
-        my_id = lane == j ? e : my_id;
-    }
-    // the unbiased score of each pick, recomputed from its logit (same fp32 op)
-    const float my_s = lane < k ? sigmoidf_(lrow[my_id]) : 0.0f;
-    float sum = 0.0f;  // fp32 sum in selection order
-    for (int j = 0; j < k; j++) sum += __shfl(my_s, j, 64);
-    float wj = my_s;
-    if (renorm && sum > 0.0f) wj = wj / sum;
-    wj *= routed_scale;
+    int id;
+    float wt;
+    topk_regs<EPL>(E, k, lrow, bias, renorm, routed_scale, id, wt);
     if (lane < k) {
-        ids_out[lane] = my_id;
-        w_out[lane] = wj;
+        ids_out[lane] = id;
+        w_out[lane] = wt;
     }
 }
 

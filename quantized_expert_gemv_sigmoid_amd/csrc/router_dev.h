@@ -47,6 +47,52 @@ __device__ __forceinline__ uint64_t wave_max_u64(uint64_t v)
     return r;
 }
 
+// Top-k of one token's logits row by one wave (kimi-k3-in-c section 9,
+// "Picking 16 experts of 896"): lane j < k ends with the j-th pick (descending
+// selection score sigmoid(logit) + bias, ties to the lower id) in id and its
+// routing weight in wt: the unbiased score, renormalised over the k picks (fp32
+// sum in selection order) if renorm, times routed_scale.  Each lane keeps
+// EPL >= E / 64 keys; k rounds of a wave-wide 64-bit max.
+template <int EPL>
+__device__ __forceinline__ void topk_regs(int E, int k, const float *__restrict__ lrow,
+                                          const float *__restrict__ bias, int renorm,
+                                          float routed_scale, int &id, float &wt)
+{
+    const int lane = threadIdx.x & 63;
+    uint64_t key[EPL];
+#pragma unroll
+    for (int i = 0; i < EPL; i++) {
+        // branch-free (a branch per element makes the compiler copy the whole array)
+        const int e = lane + 64 * i;
+        const int ec = e < E ? e : E - 1;
+        const float sc = sigmoidf_(lrow[ec]);
+        const uint64_t kk = select_key(sc + (bias ? bias[ec] : 0.0f), e);
+        key[i] = e < E ? kk : 0ull;  // padding is never selected: real keys are > 0
+    }
+    int my_id = 0;
+#pragma unroll 1
+    for (int j = 0; j < k; j++) {
+        uint64_t best = 0;
+#pragma unroll
+        for (int i = 0; i < EPL; i++) best = key[i] > best ? key[i] : best;
+        const uint64_t win = wave_max_u64(best);
+        const int e = (int)(~(uint32_t)win);
+        const bool mine = (e & 63) == lane;
+#pragma unroll
+        for (int i = 0; i < EPL; i++) key[i] = (mine && i == (e >> 6)) ? 0ull : key[i];
+        my_id = lane == j ? e : my_id;
+    }
+    // the unbiased score of each pick, recomputed from its logit (same fp32 op)
+    const float my_s = lane < k ? sigmoidf_(lrow[my_id]) : 0.0f;
+    float sum = 0.0f;  // fp32 sum in selection order
+    for (int j = 0; j < k; j++) sum += __shfl(my_s, j, 64);
+    float wj = my_s;
+    if (renorm && sum > 0.0f) wj = wj / sum;
+    wj *= routed_scale;
+    id = lane < k ? my_id : -1;
+    wt = lane < k ? wj : 0.0f;
+}
+
 // One wave: logits of router row e for tokens [0, T) of x.  The row (d fp32,
 // d <= 4096) is loaded once into registers (16 float4 per lane at most) and
 // reused for every token; x is read through the cache, 8 tokens at a time.
