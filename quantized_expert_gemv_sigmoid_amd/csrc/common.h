@@ -103,6 +103,17 @@ __device__ __forceinline__ float gated_act(float g, float u, int act, float b1, 
     return a * v;
 }
 
+// Workgroup barrier for LDS traffic only: waits for this wave's LDS
+// accesses (lgkmcnt 0) but not for its global loads, so prefetches stay in
+// flight across it (__syncthreads would also wait for vmcnt 0).
+__device__ __forceinline__ void lds_barrier()
+{
+    asm volatile("" ::: "memory");
+    __builtin_amdgcn_s_waitcnt(0xC07F);  // vmcnt 63 (no wait), expcnt 7, lgkmcnt 0
+    __builtin_amdgcn_s_barrier();
+    asm volatile("" ::: "memory");
+}
+
 template <int CTRL>
 __device__ __forceinline__ float dppf(float v)
 {

@@ -1,14 +1,16 @@
 // Fused decode path for one token (T = 1), three launches in all:
 //
 //   k_front (gemv.hip)  router logits + shared experts' gate/up
-//   k_dec1_gateup       top-k (kimi-k3-in-c section 9, "Picking 16 experts
-//                       of 896"), recomputed by one wave of every block from
-//                       the logits while the block's other waves stream the
-//                       shared experts' down rows; then the routed experts'
-//                       gate/up + activation -> H (fp16, picks in ascending id)
-//   k_dec1_down         routed down of every pick, times its routing weight,
-//                       summed over the picks, plus the shared experts'
-//                       outputs -> out (the weighted combine of section 9)
+//   k_dec1_gateup       one block of 8 waves per CU: the top-k (kimi-k3-in-c
+//                       section 9, "Picking 16 experts of 896"), recomputed by
+//                       every block from the logits, while the loads of the
+//                       shared experts' down rows are in flight; those rows;
+//                       then the routed experts' gate/up + activation -> H
+//                       (fp16, picks in ascending id)
+//   k_dec1_down         per output row: the routed down of every pick times
+//                       its routing weight, summed over the picks, plus the
+//                       shared experts' outputs -> out (the weighted combine
+//                       of section 9)
 //
 // No dispatch kernel and no combine kernel: with one token the dispatch is
 // the ascending sort of 16 ids, and the combine is a sum over the picks that
@@ -17,11 +19,10 @@
 // Weight streaming (kimi-k3-in-c section 4: MXFP4 = E2M1 codes two per byte,
 // low nibble first, one E8M0 scale per 32 weights): a row is spread over the
 // 64 lanes of a wave, lane l holding MX blocks 2l and 2l + 1 (32 contiguous
-// code bytes + 2 scale bytes), so one 16-byte load instruction reads 1 KB of
-// one row.  Every wave keeps two units of loads in flight (the next unit is
-// issued before the current one is multiplied); the lane's 64 inputs of the
-// token stay in registers (gate/up) or are read from LDS (down: the fp16 H of
-// all picks, staged once per block).
+// code bytes + 2 scale bytes).  Every wave keeps two units of loads in flight
+// (the next unit is issued before the current one is multiplied); the lane's
+// 64 inputs stay in registers (gate/up) or are read from LDS (down: the fp16
+// H of all picks, staged once per block).
 #include "common.h"
 #include "router_dev.h"
 
@@ -43,13 +44,17 @@ struct Dec1Params {
     float *out_f32;
 };
 
-constexpr int kGuRows = 4;   // rows of W1 and of W3 per gate/up unit
-constexpr int kShRows = 4;   // rows of a shared down matrix per unit
-constexpr int kDnWaves = 7;  // waves per down block
-constexpr int kDnRows = 2;   // output rows per down wave
+constexpr int kGuWaves = 8;             // waves per gate/up block (one block per CU)
+constexpr int kGuRows = 4;              // rows of W1 and of W3 per gate/up unit
+constexpr int kGuMaxBlockUnits = 1024;  // gate/up units of one block (activations staged in LDS)
+constexpr int kShRows = 2;              // shared down rows per unit
+constexpr int kShMaxBlockUnits = 512;   // shared down units of one block (outputs staged in LDS)
+constexpr int kShMaxChunks = 8;         // 16-byte chunks per lane of a shared down row (F <= 4096)
+constexpr int kShMaxHs = 8192;          // shared activations S * F (fp32) staged in LDS
+constexpr int kDnWaves = 7;             // waves per down block
+constexpr int kDnRows = 2;              // output rows per down wave
 constexpr int kDnBlockRows = kDnWaves * kDnRows;
-constexpr int kDnMaxH = 128 * 1024;  // LDS bytes for the fp16 H of all picks
-constexpr int kMaxUnitsPerWave = 64; // gate/up units a wave may take (the grid is sized for it)
+constexpr int kDnMaxH = 150 * 1024;     // LDS bytes for the fp16 H of the picks
 
 __device__ __forceinline__ uint4 gl16(const void *p) { return *reinterpret_cast<const uint4 *>(p); }
 
@@ -65,6 +70,10 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t brsrc(const void *base, uint32
 __device__ __forceinline__ uint4 bld16(__amdgpu_buffer_rsrc_t r, uint32_t voff, uint32_t soff)
 {
     return __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(r, (int)voff, (int)soff, 0));
+}
+__device__ __forceinline__ uint32_t bld4(__amdgpu_buffer_rsrc_t r, uint32_t voff, uint32_t soff)
+{
+    return __builtin_amdgcn_raw_buffer_load_b32(r, (int)voff, (int)soff, 0);
 }
 __device__ __forceinline__ uint16_t bld2(__amdgpu_buffer_rsrc_t r, uint32_t voff, uint32_t soff)
 {
@@ -117,142 +126,378 @@ __device__ __forceinline__ float scaled2(float a0, float a1, uint32_t s2)
     return v;
 }
 
-// ------------------------------------------------------------ shared down
+// ------------------------------------------------------------ block top-k
 
-// rows [4u', 4u' + 4) of shared expert u / (d / 4): Ysh[s][0][n] = W2sh[n] . Hs[s]
-__device__ __forceinline__ void shared_down_unit(const Dec1Params &p, int u)
+constexpr int kTkWaves = 4;  // waves of a gate/up block that key the experts (one per SIMD)
+
+// order-preserving 32-bit image of a selection score
+__device__ __forceinline__ uint32_t score_bits(float ch)
 {
-    const Shape &s = p.s;
-    const int lane = threadIdx.x & 63;
-    const int d = s.d, F = s.F;
-    const int per = d / kShRows;
-    const int si = u / per, n0 = (u % per) * kShRows;
-    const int nc = F / 8;                  // 16-byte chunks per row (bf16)
-    const int chunks = (nc + 63) / 64;     // per lane
-    const uint16_t *w2 = p.sh2 + (size_t)si * d * F;
-    const float *h = p.w.Hs + (size_t)si * F;  // T = 1: Hs[0][si * F + f]
-    float acc[kShRows];
-#pragma unroll
-    for (int r = 0; r < kShRows; r++) acc[r] = 0.0f;
-    for (int c = 0; c < chunks; c++) {
-        const int ci = lane + 64 * c;
-        const bool ok = ci < nc;
-        const int cc = ok ? ci : nc - 1;
-        const float4 h0 = reinterpret_cast<const float4 *>(h + cc * 8)[0];
-        const float4 h1 = reinterpret_cast<const float4 *>(h + cc * 8)[1];
-        const float hv[8] = {h0.x, h0.y, h0.z, h0.w, h1.x, h1.y, h1.z, h1.w};
-        uint4 wv[kShRows];
-#pragma unroll
-        for (int r = 0; r < kShRows; r++) wv[r] = gl16(w2 + (size_t)(n0 + r) * F + cc * 8);
-#pragma unroll
-        for (int r = 0; r < kShRows; r++) {
-            const float a = bf16x8_dot_f32(wv[r], hv, 0.0f);
-            acc[r] += ok ? a : 0.0f;
-        }
-    }
-#pragma unroll
-    for (int r = 0; r < kShRows; r++) {
-        const float v = wave_total(acc[r]);
-        if (lane == r) p.w.Ysh[(size_t)si * d + n0 + r] = v;
-    }
+    const uint32_t u = __float_as_uint(ch);
+    return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
 }
 
-// ------------------------------------------------------------ routed gate/up
+template <int CTRL>
+__device__ __forceinline__ uint32_t dppu(uint32_t v)
+{
+    return (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, CTRL, 0xF, 0xF, true);
+}
+
+// LDS flags between the waves of a block (no workgroup barrier: the other
+// waves keep streaming meanwhile).  The LDS performs one wave's accesses in
+// issue order, so a flag raised after a wave's writes is seen after them.
+__device__ __forceinline__ int lds_peek(const int *p)
+{
+    return __builtin_amdgcn_readfirstlane(*reinterpret_cast<const volatile int *>(p));
+}
+__device__ __forceinline__ void spin_until(const int *p, int target)
+{
+    while (lds_peek(p) < target) __builtin_amdgcn_s_sleep(1);
+}
+__device__ __forceinline__ void flag_add(int *p)
+{
+    asm volatile("" ::: "memory");
+    if ((threadIdx.x & 63) == 0) atomicAdd(p, 1);
+    asm volatile("" ::: "memory");
+}
+
+// Top-k of one token, part 1 (kimi-k3-in-c section 9, "Picking 16 experts
+// of 896"; the same selection as topk_regs): keying wave w < 4 takes experts
+// [w * EQ, (w + 1) * EQ), EQ = ceil(E / 4) <= 256 (slot i of lane l is
+// expert w * EQ + 64 i + l), from the logits and biases the caller loaded,
+// stores their unbiased scores, and writes its k best as 64-bit keys (score
+// bits, then the inverted id: distinct) to cand[w * k, (w + 1) * k), found
+// in k rounds: a 32-bit max over the wave (DPP inside rows of 16, readlane
+// across them), then the lowest id holding it (first slot with a match,
+// lowest lane).  Rounds past the wave's real experts give key 0.
+__device__ __forceinline__ void topk_candidates(int E, int k, int wave, const float (&lg)[4],
+                                                const float (&bs)[4], uint64_t *cand, float *score)
+{
+    const int lane = threadIdx.x & 63;
+    const int EQ = (E + kTkWaves - 1) / kTkWaves;
+    const int base = wave * EQ;
+    uint32_t key[4];
+#pragma unroll
+    for (int i = 0; i < 4; i++) {
+        const int li = lane + 64 * i;
+        const int e = base + li;
+        const bool ok = li < EQ && e < E;
+        const float sc = sigmoidf_(lg[i]);
+        if (ok) score[e] = sc;  // the unbiased score, for the weights
+        // padding is never selected: real keys are > 0
+        key[i] = ok ? score_bits(sc + bs[i]) : 0u;
+    }
+    uint64_t mine = 0;
+#pragma unroll 1
+    for (int j = 0; j < k; j++) {
+        uint32_t m = max(max(key[0], key[1]), max(key[2], key[3]));
+        m = max(m, dppu<0xB1>(m));   // quad_perm [1,0,3,2]
+        m = max(m, dppu<0x4E>(m));   // quad_perm [2,3,0,1]
+        m = max(m, dppu<0x141>(m));  // row_half_mirror
+        m = max(m, dppu<0x140>(m));  // row_mirror
+        const uint32_t w = max(max((uint32_t)__builtin_amdgcn_readlane((int)m, 0), (uint32_t)__builtin_amdgcn_readlane((int)m, 16)),
+                               max((uint32_t)__builtin_amdgcn_readlane((int)m, 32), (uint32_t)__builtin_amdgcn_readlane((int)m, 48)));
+        const uint64_t b0 = __builtin_amdgcn_ballot_w64(key[0] == w);
+        const uint64_t b1 = __builtin_amdgcn_ballot_w64(key[1] == w);
+        const uint64_t b2 = __builtin_amdgcn_ballot_w64(key[2] == w);
+        const uint64_t b3 = __builtin_amdgcn_ballot_w64(key[3] == w);
+        const int sl = b0 ? 0 : b1 ? 1 : b2 ? 2 : 3;
+        const uint64_t bm = b0 ? b0 : b1 ? b1 : b2 ? b2 : b3;
+        const int l = (int)__builtin_ctzll(bm | (1ull << 63));
+        const int e = base + 64 * sl + l;
+        const bool me = lane == l;
+#pragma unroll
+        for (int i = 0; i < 4; i++) key[i] = (me && sl == i) ? 0u : key[i];
+        const uint64_t ck = w ? (((uint64_t)w << 32) | (uint32_t)(~(uint32_t)e)) : 0ull;
+        mine = lane == j ? ck : mine;
+    }
+    if (lane < k) cand[wave * k + lane] = mine;
+}
+
+// Part 2, one wave: the 4k candidates hold the global top k.  A candidate's
+// rank among them (distinct keys: a permutation) is the count of larger
+// ones; rank j < k makes it pick j (zero keys rank at least at the number
+// of real candidates, >= k).  Lanes j < k end with pick j (id) and its weight
+// (wt): the unbiased score, renormalised over the picks (fp32 sum in
+// selection order) if renorm, times routed_scale.
+__device__ __forceinline__ void topk_merge(int k, int renorm, float routed_scale, const uint64_t *cand,
+                                           uint64_t *sel, const float *score, int &id, float &wt)
+{
+    const int lane = threadIdx.x & 63;
+    const int nc = kTkWaves * k;  // <= 256: at most 4 per lane
+    uint64_t c[4];
+    int rank[4];
+#pragma unroll
+    for (int m = 0; m < 4; m++) {
+        c[m] = lane + 64 * m < nc ? cand[lane + 64 * m] : 0ull;
+        rank[m] = 0;
+    }
+#pragma unroll 8
+    for (int i = 0; i < nc; i++) {
+        const uint64_t o = cand[i];  // same address for all lanes: a broadcast
+#pragma unroll
+        for (int m = 0; m < 4; m++) rank[m] += o > c[m] ? 1 : 0;
+    }
+#pragma unroll
+    for (int m = 0; m < 4; m++)
+        if (lane + 64 * m < nc && rank[m] < k) sel[rank[m]] = c[m];
+    // (one wave: its LDS accesses are performed in order)
+    const uint64_t kk = lane < k ? sel[lane] : 0ull;
+    const int my_id = lane < k ? (int)(~(uint32_t)kk) : 0;
+    const float my_s = lane < k ? score[my_id] : 0.0f;
+    float sum = 0.0f;  // fp32 sum in selection order
+    for (int j = 0; j < k; j++) sum += __int_as_float(__builtin_amdgcn_readlane(__float_as_int(my_s), j));
+    float wj = my_s;
+    if (renorm && sum > 0.0f) wj = wj / sum;
+    wj *= routed_scale;
+    id = lane < k ? my_id : -1;
+    wt = lane < k ? wj : 0.0f;
+}
+
+// ------------------------------------------------------------ gate/up kernel
 
 struct GuLoads {
     uint4 c[kGuRows][2][2];  // [row][gate, up][block 2l, 2l + 1]
     uint16_t sc[kGuRows][2]; // [row][gate, up] two scale bytes (widened at use)
 };
 
-template <int EPL>
-__global__ __launch_bounds__(256) void k_dec1_gateup(Dec1Params p)
+// Work queue of a block: local units [0, n) taken in order by its waves,
+// one grab ahead of use, so that waves the memory system serves faster take
+// more of them (of the two waves sharing a SIMD the older is served first).
+// Every lane adds 1 to the LDS counter (it moves by 64 per grab; any lane's
+// old value / 64 is the grab's index).  Written out so that the unit loop
+// holds no branch and no extra register for it; the wait covers the LDS
+// return.
+__device__ __forceinline__ int grab(uint32_t lds_addr)
 {
+    int v;
+    asm volatile("ds_add_rtn_u32 %0, %1, %2\n\ts_waitcnt lgkmcnt(0)" : "=v"(v) : "v"(lds_addr), "v"(1) : "memory");
+    return __builtin_amdgcn_readfirstlane(v) >> 6;
+}
+
+// One block of 8 waves per CU.  Waves 0-3 pick the experts (top-k) while
+// waves 4-7 stream the shared experts' down rows (a work queue of their
+// own); then every wave takes routed gate/up units from the block's queue.
+// SHC: 16-byte chunks per lane of a shared down row (ceil(F / 512)).
+template <int SHC>
+__global__ __launch_bounds__(kGuWaves * 64) void k_dec1_gateup(Dec1Params p)
+{
+    __shared__ uint64_t s_cand[kTkWaves * kMaxTopK];
+    __shared__ uint64_t s_sel[kMaxTopK];
     __shared__ int s_eid[kMaxTopK];      // picks in ascending id (-1: no pick)
     __shared__ float s_wt[kMaxTopK];
-    __shared__ int s_cnt[kMaxExperts];
-    // each wave's activations, written to H after its last unit (a global
-    // store inside the unit loop would make the next register reuse wait for
-    // every load in flight: stores and loads share one counter)
-    __shared__ _Float16 s_hout[4][kMaxUnitsPerWave][kGuRows];
+    __shared__ float s_score[kMaxExperts];  // unbiased scores; then block 0's counts
+    __shared__ __attribute__((aligned(16))) float s_hs[kShMaxHs];  // shared activations [S][F]
+    // the block's results, written out after its last unit (a global store
+    // inside a unit loop would make the next register reuse wait for every
+    // load in flight: stores and loads share one counter)
+    __shared__ __attribute__((aligned(8))) _Float16 s_hout[kGuMaxBlockUnits][kGuRows];
+    __shared__ __attribute__((aligned(8))) float s_ysh[kShMaxBlockUnits][kShRows];
+    // [0], [1]: work queues (routed, shared); [2]: keying waves whose
+    // candidates are written; [3]: picks ready
+    __shared__ int s_ctl[4];
     const Shape &s = p.s;
     const int lane = threadIdx.x & 63;
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int d = s.d, F = s.F, E = s.E, k = s.k;
+    const int S = p.shared ? s.S : 0;
 
-    if (wave == 0) {
-        int id = -1;
-        float wt = 0.0f;
-        if (p.do_topk) {
-            topk_regs<EPL>(E, k, p.w.logits, p.bias, s.renorm, s.routed_scale, id, wt);
-        } else if (lane < k) {
-            id = p.ids[lane];
-            wt = p.wts[lane];
-        }
-        // rank among the valid ids (an id outside [0, E) drops its term)
-        const bool valid = lane < k && id >= 0 && id < E;
-        int rank = 0;
-        for (int j = 0; j < k; j++) {
-            const int o = __shfl(id, j, 64);
-            rank += (o >= 0 && o < E && o < id) ? 1 : 0;
-        }
-        if (lane < k) {
-            s_eid[lane] = -1;
-            s_wt[lane] = 0.0f;
-        }
-        // (one wave: its LDS accesses are performed in order)
-        if (valid) {
-            s_eid[rank] = id;
-            s_wt[rank] = wt;
-        }
-        if (blockIdx.x == 0) {
-            if (p.do_topk && lane < k) {
-                p.ids[lane] = id;
-                p.wts[lane] = wt;
-            }
-            if (lane < k) {
-                p.w.active[lane] = s_eid[lane];
-                p.w.pos_w[lane] = s_wt[lane];
-            }
-            if (p.counts_out) {
-                for (int e = lane; e < E; e += 64) s_cnt[e] = 0;
-                if (valid) s_cnt[id] = 1;
-                for (int e = lane; e < E; e += 64) p.counts_out[e] = s_cnt[e];
-            }
-        }
-    } else if (p.shared) {
-        const int nsw = gridDim.x * 3, sw = blockIdx.x * 3 + (wave - 1);
-        const int units = s.S * (d / kShRows);
-        for (int u = sw; u < units; u += nsw) shared_down_unit(p, u);
+    // ---- loads, in the order they are waited for (reads past a resource's
+    // size return 0, so none of them is conditional)
+    // the router logits and biases of this thread's four experts (keying
+    // waves), or the given picks
+    const bool keyer = p.do_topk && wave < kTkWaves;
+    const int EQ = (E + kTkWaves - 1) / kTkWaves;
+    const auto rlg = brsrc(p.w.logits, keyer ? (uint32_t)E * 4 : 0u);
+    const auto rbs = brsrc(p.bias, keyer && p.bias ? (uint32_t)E * 4 : 0u);
+    const auto rid = brsrc(p.ids, p.do_topk || wave ? 0u : (uint32_t)k * 4);
+    const auto rwt = brsrc(p.wts, p.do_topk || wave ? 0u : (uint32_t)k * 4);
+    float lg[4], bs[4];
+#pragma unroll
+    for (int i = 0; i < 4; i++) {
+        const uint32_t e = (uint32_t)(min(wave, kTkWaves - 1) * EQ + lane + 64 * i);
+        lg[i] = __uint_as_float(bld4(rlg, e * 4, 0));
+        bs[i] = __uint_as_float(bld4(rbs, e * 4, 0));
     }
-    __syncthreads();
-
-    // ---- routed gate/up units: (pick j, rows [4 rg, 4 rg + 4)) of W1 and W3
+    const int gid = (int)bld4(rid, lane * 4u, 0);
+    const float gwt = __uint_as_float(bld4(rwt, lane * 4u, 0));
+    // the shared activations (S * F fp32, to LDS)
+    constexpr int kHsRounds = kShMaxHs / 4 / (kGuWaves * 64);
+    const auto rhs = brsrc(p.w.Hs, (uint32_t)(S * F * 4));
+    uint4 hsv[kHsRounds];
+#pragma unroll
+    for (int i = 0; i < kHsRounds; i++) hsv[i] = bld16(rhs, (threadIdx.x + i * kGuWaves * 64) * 16u, 0);
+    __builtin_amdgcn_sched_barrier(0);
+    // the token's 64 inputs of this lane (blocks 2l, 2l + 1)
     const int nbp = d / 64;                      // MX block pairs per row = lanes in use
     const int lp = lane < nbp ? lane : nbp - 1;  // idle lanes re-read a valid pair
     const float lmask = lane < nbp ? 1.0f : 0.0f;
-    const size_t qrow = (size_t)d / 2, srow = (size_t)d / 32;
-    // the token's 64 inputs of this lane (blocks 2l, 2l + 1)
     uint32_t xr[32];
 #pragma unroll
     for (int i = 0; i < 8; i++) {
         const uint4 v = gl16(p.x + (size_t)lp * 64 + i * 8);
         xr[4 * i + 0] = v.x; xr[4 * i + 1] = v.y; xr[4 * i + 2] = v.z; xr[4 * i + 3] = v.w;
     }
+    // the shared activations to LDS (unconditional: past S * F the loads
+    // returned 0), the queues and flags cleared; the one workgroup barrier
+    // before the last
+#pragma unroll
+    for (int i = 0; i < kHsRounds; i++) reinterpret_cast<uint4 *>(s_hs)[threadIdx.x + i * kGuWaves * 64] = hsv[i];
+    if (threadIdx.x < 4) s_ctl[threadIdx.x] = 0;
+    lds_barrier();
+
+    const uint32_t q_addr = (uint32_t)(uintptr_t)(__attribute__((address_space(3))) int *)&s_ctl[0];
+    const uint32_t s_addr = q_addr + 4;
+
+    // ---- shared experts' down rows [2 n', 2 n' + 2) of expert si: unit
+    // u = si * d / 2 + n' writes Ysh[2u, 2u + 2) (T = 1).  The block owns
+    // units [sbeg, sbeg + nsloc), streamed by waves 4-7 from their queue.
+    const int per_sh = d / kShRows;
+    const int nsh = S * per_sh;
+    const int sper = (nsh + gridDim.x - 1) / gridDim.x;
+    const int sbeg = blockIdx.x * sper;
+    const int nsloc = max(min(nsh - sbeg, sper), 0);
+    const int nch = F / 8;  // 16-byte chunks of a bf16 row
+    auto load_sh = [&](uint4 (&w)[kShRows][SHC], int v) __attribute__((always_inline)) {
+        const bool ok = v < nsloc;
+        const int u = ok ? sbeg + v : 0;
+        const int si = u / per_sh, n0 = (u % per_sh) * kShRows;
+        const auto r = brsrc(p.sh2 + (size_t)si * d * F, ok ? (uint32_t)((size_t)d * F * 2) : 0u);
+#pragma unroll
+        for (int rr = 0; rr < kShRows; rr++)
+#pragma unroll
+            for (int c = 0; c < SHC; c++) {
+                const int ch = min(lane + 64 * c, nch - 1);
+                w[rr][c] = bld16(r, (uint32_t)ch * 16, (uint32_t)((n0 + rr) * F * 2));
+            }
+        __builtin_amdgcn_sched_barrier(0);
+    };
+    auto dot_sh = [&](const uint4 (&w)[kShRows][SHC], int v) __attribute__((always_inline)) {
+        const int si = (sbeg + v) / per_sh;
+        float acc[kShRows];
+#pragma unroll
+        for (int rr = 0; rr < kShRows; rr++) acc[rr] = 0.0f;
+#pragma unroll
+        for (int c = 0; c < SHC; c++) {
+            const int ch = lane + 64 * c;
+            const bool ok = ch < nch;
+            const float4 *h4 = reinterpret_cast<const float4 *>(s_hs + (size_t)si * F + (size_t)min(ch, nch - 1) * 8);
+            const float4 a = h4[0], b = h4[1];
+            const float hv[8] = {a.x, a.y, a.z, a.w, b.x, b.y, b.z, b.w};
+#pragma unroll
+            for (int rr = 0; rr < kShRows; rr++) {
+                const float t = bf16x8_dot_f32(w[rr][c], hv, 0.0f);
+                acc[rr] += ok ? t : 0.0f;
+            }
+        }
+        float o = 0.0f;
+#pragma unroll
+        for (int rr = 0; rr < kShRows; rr++) {
+            const float t = wave_total(acc[rr]);
+            o = lane == rr ? t : o;
+        }
+        if (lane < kShRows) s_ysh[v][lane] = o;
+    };
+
+    if (wave < kTkWaves) {
+        // ---- the picks
+        int id = -1;
+        float wt = 0.0f;
+        if (p.do_topk) {
+            topk_candidates(E, k, wave, lg, bs, s_cand, s_score);
+            flag_add(&s_ctl[2]);
+            if (wave == 0) {
+                spin_until(&s_ctl[2], kTkWaves);
+                topk_merge(k, s.renorm, s.routed_scale, s_cand, s_sel, s_score, id, wt);
+            }
+        } else {
+            id = lane < k ? gid : -1;
+            wt = lane < k ? gwt : 0.0f;
+        }
+        if (wave == 0) {
+            // rank among the valid ids (an id outside [0, E) drops its term)
+            const bool valid = lane < k && id >= 0 && id < E;
+            int rank = 0;
+            for (int j = 0; j < k; j++) {
+                const int o = __builtin_amdgcn_readlane(id, j);
+                rank += (o >= 0 && o < E && o < id) ? 1 : 0;
+            }
+            if (lane < k) {
+                s_eid[lane] = -1;
+                s_wt[lane] = 0.0f;
+            }
+            // (one wave: its LDS accesses are performed in order)
+            if (valid) {
+                s_eid[rank] = id;
+                s_wt[rank] = wt;
+            }
+            if (blockIdx.x == 0) {
+                if (p.do_topk && lane < k) {
+                    p.ids[lane] = id;
+                    p.wts[lane] = wt;
+                }
+                if (lane < k) {
+                    p.w.active[lane] = s_eid[lane];
+                    p.w.pos_w[lane] = s_wt[lane];
+                }
+                if (p.counts_out) {
+                    // (the scores are no longer read: the merge is done)
+                    int *cnt = reinterpret_cast<int *>(s_score);
+                    for (int e = lane; e < E; e += 64) cnt[e] = 0;
+                    if (valid) cnt[id] = 1;
+                    for (int e = lane; e < E; e += 64) p.counts_out[e] = cnt[e];
+                }
+            }
+            flag_add(&s_ctl[3]);
+        }
+    } else if (nsloc > 0) {
+        // ---- the shared rows, two units in flight per wave
+        int v0 = grab(s_addr), v1 = grab(s_addr);
+        if (v0 < nsloc) {
+            uint4 sa[kShRows][SHC], sb[kShRows][SHC];
+            load_sh(sa, v0);
+            for (;;) {
+                const int v2 = grab(s_addr);
+                load_sh(sb, v1);
+                dot_sh(sa, v0);
+                if (v1 >= nsloc) break;
+                const int v3 = grab(s_addr);
+                load_sh(sa, v2);
+                dot_sh(sb, v1);
+                if (v2 >= nsloc) break;
+                v0 = v2;
+                v1 = v3;
+            }
+        }
+    }
+    spin_until(&s_ctl[3], 1);
+
+    // ---- routed gate/up units: (pick j, rows [4 rg, 4 rg + 4)) of W1 and W3.
+    // Unit u = j * F / 4 + rg writes H[4u, 4u + 4).  The block owns units
+    // [ubeg, ubeg + nloc) (contiguous rows of one or two picks).
+    const size_t qrow = (size_t)d / 2, srow = (size_t)d / 32;
+    const uint32_t voq = (uint32_t)lp * 32, vos = (uint32_t)lp * 2;
     const int upr = F / kGuRows;  // units per pick
     const int units = k * upr;
-    const int nw = gridDim.x * 4, gw = blockIdx.x * 4 + wave;
-    _Float16 *H = reinterpret_cast<_Float16 *>(p.w.H);
-
-    const uint32_t voq = (uint32_t)lp * 32, vos = (uint32_t)lp * 2;
+    const int per = (units + gridDim.x - 1) / gridDim.x;
+    const int ubeg = blockIdx.x * per;
+    const int nloc = max(min(units - ubeg, per), 0);
     // lane j holds pick j; a unit's expert comes out through readlane (a
-    // scalar), so the unit loop needs no VGPR temporary and no LDS read
+    // scalar), so the unit loop needs no vector temporary and no LDS read
     const int my_e = lane < k ? s_eid[lane] : -1;
-    auto load = [&](GuLoads &g, int u) __attribute__((always_inline)) {
+
+    // loads of local unit v; past the block's range they read nothing (zero
+    // sized resources) but are still issued, so that the wait before a unit's
+    // arithmetic counts exactly the next unit's loads
+    auto load = [&](GuLoads &g, int v) __attribute__((always_inline)) {
+        const bool ok = v < nloc;
+        const int u = ok ? ubeg + v : 0;
         const int j = u / upr, f0 = (u % upr) * kGuRows;
         const int e = max(__builtin_amdgcn_readlane(my_e, j), 0);  // no pick: expert 0, never used
-        const uint32_t qbytes = (uint32_t)(F * qrow), sbytes = (uint32_t)(F * srow);
-        const auto r1 = brsrc(p.w1q + (size_t)e * qbytes, qbytes), r3 = brsrc(p.w3q + (size_t)e * qbytes, qbytes);
-        const auto t1 = brsrc(p.w1s + (size_t)e * sbytes, sbytes), t3 = brsrc(p.w3s + (size_t)e * sbytes, sbytes);
+        const uint32_t qbytes = ok ? (uint32_t)(F * qrow) : 0u, sbytes = ok ? (uint32_t)(F * srow) : 0u;
+        const size_t qe = (size_t)e * F * qrow, se = (size_t)e * F * srow;
+        const auto r1 = brsrc(p.w1q + qe, qbytes), r3 = brsrc(p.w3q + qe, qbytes);
+        const auto t1 = brsrc(p.w1s + se, sbytes), t3 = brsrc(p.w3s + se, sbytes);
 #pragma unroll
         for (int r = 0; r < kGuRows; r++) {
             const uint32_t so = (uint32_t)((f0 + r) * qrow), ss = (uint32_t)((f0 + r) * srow);
@@ -263,8 +508,10 @@ __global__ __launch_bounds__(256) void k_dec1_gateup(Dec1Params p)
             g.sc[r][0] = bld2(t1, vos, ss);
             g.sc[r][1] = bld2(t3, vos, ss);
         }
+        // (all of them issued before the arithmetic that follows)
+        __builtin_amdgcn_sched_barrier(0);
     };
-    auto compute = [&](const GuLoads &g, int it) __attribute__((always_inline)) {
+    auto compute = [&](const GuLoads &g, int v) __attribute__((always_inline)) {
         float gv[kGuRows], uv[kGuRows];
 #pragma unroll
         for (int r = 0; r < kGuRows; r++) {
@@ -280,43 +527,48 @@ __global__ __launch_bounds__(256) void k_dec1_gateup(Dec1Params p)
 #pragma unroll
             for (int r = 0; r < kGuRows; r++)
                 if (lane == r) hv = gated_act(gv[r], uv[r], s.act, s.b1, s.b2);
-            s_hout[wave][it][lane] = (_Float16)hv;
+            s_hout[v][lane] = (_Float16)hv;
         }
     };
 
-    // Two units in flight per wave.  The loads are unconditional (past the
-    // end they re-read the last unit, an L2 hit) so that the wait before a
-    // unit's arithmetic counts exactly the next unit's loads.
-    const int last = units - 1;
-    int u = gw, it = 0;
-    if (u < units) {
-        GuLoads ga, gb;
-        load(ga, u);
-        for (;;) {
-            const int un = u + nw;
-            load(gb, min(un, last));
-            compute(ga, it);
-            if (un >= units) break;
-            const int unn = un + nw;
-            load(ga, min(unn, last));
-            compute(gb, it + 1);
-            if (unn >= units) break;
-            u = unn;
-            it += 2;
+    {
+        int v0 = grab(q_addr), v1 = grab(q_addr);
+        if (v0 < nloc) {
+            GuLoads ga, gb;
+            load(ga, v0);
+            for (;;) {
+                // v0 (in ga) is multiplied now, v1 loaded, v2 grabbed
+                const int v2 = grab(q_addr);
+                load(gb, v1);
+                compute(ga, v0);
+                if (v1 >= nloc) break;
+                const int v3 = grab(q_addr);
+                load(ga, v2);
+                compute(gb, v1);
+                if (v2 >= nloc) break;
+                v0 = v2;
+                v1 = v3;
+            }
         }
     }
-    // this wave's units were gw, gw + nw, ...: lane r of unit i writes row r
-    const int nu = gw < units ? (units - 1 - gw) / nw + 1 : 0;
-    for (int i = lane / kGuRows; i < nu; i += 64 / kGuRows) {
-        const int uu = gw + i * nw, j = uu / upr, f0 = (uu % upr) * kGuRows;
-        if (s_eid[j] >= 0) H[(size_t)j * F + f0 + lane % kGuRows] = s_hout[wave][i][lane % kGuRows];
+
+    lds_barrier();
+    // the block's results: routed activations to H (4 fp16 per unit, skipped
+    // where no pick), shared outputs to Ysh
+    _Float16 *H = reinterpret_cast<_Float16 *>(p.w.H);
+    for (int i = threadIdx.x; i < nloc; i += kGuWaves * 64) {
+        const int u = ubeg + i;
+        if (s_eid[u / upr] >= 0)
+            *reinterpret_cast<uint2 *>(H + (size_t)u * kGuRows) = *reinterpret_cast<const uint2 *>(s_hout[i]);
     }
+    for (int i = threadIdx.x; i < nsloc; i += kGuWaves * 64)
+        *reinterpret_cast<float2 *>(p.w.Ysh + (size_t)(sbeg + i) * kShRows) = *reinterpret_cast<const float2 *>(s_ysh[i]);
 }
 
 // ------------------------------------------------------------ routed down + combine
 
 struct DnLoads {
-    uint4 c[2][kDnRows][2];  // [pick of the pair][row][block 2l, 2l + 1]
+    uint4 c[2][kDnRows][2];   // [pick of the pair][row][block 2l, 2l + 1]
     uint16_t sc[2][kDnRows];
 };
 
@@ -446,7 +698,9 @@ __global__ __launch_bounds__(kDnWaves * 64) void k_dec1_down(Dec1Params p)
 
 bool decode1_supported(const Shape &s)
 {
-    return s.T == 1 && s.d % 64 == 0 && s.F % 64 == 0 && (size_t)s.k * s.F * 2 <= kDnMaxH;
+    return s.T == 1 && s.d % 64 == 0 && s.d <= 4096 && s.F % 64 == 0 && s.F <= 512 * kShMaxChunks &&
+           s.E <= kMaxExperts && s.k <= kMaxTopK && (size_t)s.k * s.F * 2 <= kDnMaxH &&
+           (size_t)s.S * s.F <= kShMaxHs;
 }
 
 static int cu_count()
@@ -456,15 +710,6 @@ static int cu_count()
     if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0) return 256;
     return n;
 }
-
-#define MOE_EPL_SWITCH1(epl, CALL)      \
-    do {                                \
-        if ((epl) <= 1) CALL(1);        \
-        else if ((epl) <= 2) CALL(2);   \
-        else if ((epl) <= 4) CALL(4);   \
-        else if ((epl) <= 8) CALL(8);   \
-        else CALL(16);                  \
-    } while (0)
 
 hipError_t launch_decode1(const Shape &s, const uint16_t *x, const Weights &wt, const float *bias,
                           int do_topk, int32_t *ids, float *wts, int32_t *counts_out, int shared,
@@ -485,13 +730,16 @@ hipError_t launch_decode1(const Shape &s, const uint16_t *x, const Weights &wt, 
     p.shared = shared && s.S > 0;
     p.out_bf16 = out_bf16;
     p.out_f32 = out_f32;
-    // two blocks per CU, more if needed to keep a wave's units within its LDS record
+    // one block per CU, more if a block's ranges would not fit its LDS records
     const int units = s.k * (s.F / kGuRows);
-    const int nblk = max(2 * cu_count(), (units + 4 * kMaxUnitsPerWave - 1) / (4 * kMaxUnitsPerWave));
-    const int epl = (s.E + 63) / 64;
-#define CALL_GU(N) k_dec1_gateup<N><<<nblk, 256, 0, stream>>>(p)
-    MOE_EPL_SWITCH1(epl, CALL_GU);
-#undef CALL_GU
+    const int sh_units = p.shared ? s.S * (s.d / kShRows) : 0;
+    const int nblk = max(cu_count(), max((units + kGuMaxBlockUnits - 1) / kGuMaxBlockUnits,
+                                         (sh_units + kShMaxBlockUnits - 1) / kShMaxBlockUnits));
+    const int shc = (s.F / 8 + 63) / 64;  // 16-byte chunks per lane of a shared down row
+    if (shc <= 2) k_dec1_gateup<2><<<nblk, kGuWaves * 64, 0, stream>>>(p);
+    else if (shc <= 4) k_dec1_gateup<4><<<nblk, kGuWaves * 64, 0, stream>>>(p);
+    else if (shc <= 6) k_dec1_gateup<6><<<nblk, kGuWaves * 64, 0, stream>>>(p);
+    else k_dec1_gateup<8><<<nblk, kGuWaves * 64, 0, stream>>>(p);
     if (ev2) (void)hipEventRecord(ev2[0], stream);
     const int nd = (s.d + kDnBlockRows - 1) / kDnBlockRows;
     k_dec1_down<<<nd, kDnWaves * 64, (size_t)s.k * s.F * 2, stream>>>(p);

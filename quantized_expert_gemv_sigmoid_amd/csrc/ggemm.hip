@@ -87,16 +87,6 @@ __device__ __forceinline__ void lds_st16(LDS uint8_t *p, uint4 v)
 }
 __device__ __forceinline__ void lds_st4(LDS uint8_t *p, uint32_t v) { *reinterpret_cast<LDS uint32_t *>(p) = v; }
 
-// Workgroup barrier for the LDS stages only: waits for this wave's LDS
-// writes (lgkmcnt 0), not for its outstanding global loads, so prefetches
-// stay in flight across it (__syncthreads would also wait for vmcnt 0).
-__device__ __forceinline__ void lds_barrier()
-{
-    asm volatile("" ::: "memory");
-    __builtin_amdgcn_s_waitcnt(0xC07F);  // vmcnt 63 (no wait), expcnt 7, lgkmcnt 0
-    __builtin_amdgcn_s_barrier();
-    asm volatile("" ::: "memory");
-}
 
 // element offset of 16-byte piece q of row r in an LDS stage of KC columns
 template <int KC>
