@@ -103,6 +103,42 @@ __device__ __forceinline__ float gated_act(float g, float u, int act, float b1, 
     return a * v;
 }
 
+typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
+typedef _Float16 f16x8_t __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x2v_t __attribute__((ext_vector_type(2)));
+typedef _Float16 f16x2v_t __attribute__((ext_vector_type(2)));
+
+// 8 E2M1 codes (one dword, low nibble first) times the scale sc (a power of
+// two) -> 8 bf16 / fp16 values
+__device__ __forceinline__ bf16x8_t cvt8_bf16(uint32_t w, float sc)
+{
+    const bf16x2v_t p0 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(w, sc, 0);
+    const bf16x2v_t p1 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(w, sc, 1);
+    const bf16x2v_t p2 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(w, sc, 2);
+    const bf16x2v_t p3 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(w, sc, 3);
+    bf16x8_t r;
+    r[0] = p0.x; r[1] = p0.y; r[2] = p1.x; r[3] = p1.y;
+    r[4] = p2.x; r[5] = p2.y; r[6] = p3.x; r[7] = p3.y;
+    return r;
+}
+
+__device__ __forceinline__ f16x8_t cvt8_f16(uint32_t w, float sc)
+{
+    const f16x2v_t p0 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w, sc, 0);
+    const f16x2v_t p1 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w, sc, 1);
+    const f16x2v_t p2 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w, sc, 2);
+    const f16x2v_t p3 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w, sc, 3);
+    f16x8_t r;
+    r[0] = p0.x; r[1] = p0.y; r[2] = p1.x; r[3] = p1.y;
+    r[4] = p2.x; r[5] = p2.y; r[6] = p3.x; r[7] = p3.y;
+    return r;
+}
+
+__device__ __forceinline__ uint32_t u4at(const uint4 &q, int i)
+{
+    return i == 0 ? q.x : (i == 1 ? q.y : (i == 2 ? q.z : q.w));
+}
+
 // Workgroup barrier for LDS traffic only: waits for this wave's LDS
 // accesses (lgkmcnt 0) but not for its global loads, so prefetches stay in
 // flight across it (__syncthreads would also wait for vmcnt 0).

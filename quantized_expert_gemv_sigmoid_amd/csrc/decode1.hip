@@ -45,8 +45,14 @@ struct Dec1Params {
 };
 
 constexpr int kGuWaves = 8;             // waves per gate/up block (one block per CU)
-constexpr int kGuRows = 4;              // rows of W1 and of W3 per gate/up unit
-constexpr int kGuMaxBlockUnits = 1024;  // gate/up units of one block (activations staged in LDS)
+constexpr int kGuFeat = 16;             // features (rows of W1 and of W3) per gate/up unit
+constexpr int kGuWin = 4;               // 128-wide K windows per gate/up work item
+constexpr int kGuMaxBlockUnits = 32;    // gate/up units of one block (partial sums staged in LDS)
+constexpr int kGuMaxStages = 8;         // K slices per unit (d <= 4096)
+constexpr int kMaxD = 4096;             // token width of the one-token path
+constexpr int kXPad = kMaxD + kGuWin * 128;  // token length padded to whole gate/up stages
+constexpr int kX8Lo = kXPad + 256 + 128;     // LDS offset of the residual part (other banks)
+constexpr int kXsLo = kXPad / 32;            // offset of the residual's scales
 constexpr int kShRows = 2;              // shared down rows per unit
 constexpr int kShMaxBlockUnits = 512;   // shared down units of one block (outputs staged in LDS)
 constexpr int kShMaxChunks = 8;         // 16-byte chunks per lane of a shared down row (F <= 4096)
@@ -74,6 +80,10 @@ __device__ __forceinline__ uint4 bld16(__amdgpu_buffer_rsrc_t r, uint32_t voff, 
 __device__ __forceinline__ uint32_t bld4(__amdgpu_buffer_rsrc_t r, uint32_t voff, uint32_t soff)
 {
     return __builtin_amdgcn_raw_buffer_load_b32(r, (int)voff, (int)soff, 0);
+}
+__device__ __forceinline__ uint32_t bld1(__amdgpu_buffer_rsrc_t r, uint32_t voff, uint32_t soff)
+{
+    return __builtin_amdgcn_raw_buffer_load_b8(r, (int)voff, (int)soff, 0);
 }
 __device__ __forceinline__ uint16_t bld2(__amdgpu_buffer_rsrc_t r, uint32_t voff, uint32_t soff)
 {
@@ -256,9 +266,11 @@ __device__ __forceinline__ void topk_merge(int k, int renorm, float routed_scale
 
 // ------------------------------------------------------------ gate/up kernel
 
-struct GuLoads {
-    uint4 c[kGuRows][2][2];  // [row][gate, up][block 2l, 2l + 1]
-    uint16_t sc[kGuRows][2]; // [row][gate, up] two scale bytes (widened at use)
+// one gate/up stage of a lane: per K window, its MX block of W1 and of W3
+// (16 bytes) and their scale bytes
+struct GuStage {
+    uint4 c[2][kGuWin];
+    uint32_t s[2][kGuWin];
 };
 
 // Work queue of a block: local units [0, n) taken in order by its waves,
@@ -273,6 +285,82 @@ __device__ __forceinline__ int grab(uint32_t lds_addr)
     int v;
     asm volatile("ds_add_rtn_u32 %0, %1, %2\n\ts_waitcnt lgkmcnt(0)" : "=v"(v) : "v"(lds_addr), "v"(1) : "memory");
     return __builtin_amdgcn_readfirstlane(v) >> 6;
+}
+
+typedef int i32x8_t __attribute__((ext_vector_type(8)));
+
+// fp32 -> OCP fp8 e4m3 code, rounded to nearest even (|v| < 448)
+__device__ __forceinline__ uint32_t e4m3_rne(float v)
+{
+    const uint32_t sgn = (__float_as_uint(v) >> 24) & 0x80u;
+    const float a = fabsf(v);
+    // below 2^-6: steps of 2^-9 (8 is the smallest normal, field 0x08)
+    const uint32_t fs = (uint32_t)__builtin_rintf(a * 512.0f);
+    const uint32_t ab = __float_as_uint(a);
+    const uint32_t m = ab & 0x7FFFFFu;
+    const uint32_t r = (m + 0x7FFFFu + ((m >> 20) & 1u)) >> 20;  // 3 mantissa bits (8: carry)
+    const uint32_t fn = (((ab >> 23) - 120u) << 3) + r;        // exponent field e - 127 + 7
+    return sgn | (a < 0.015625f ? fs : fn);
+}
+__device__ __forceinline__ float e4m3_val(uint32_t c)
+{
+    const uint32_t e = (c >> 3) & 15u, m = c & 7u;
+    const float v = e ? ldexpf((float)(8u + m), (int)e - 10) : ldexpf((float)m, -9);
+    return (c & 0x80u) ? -v : v;
+}
+// E8M0 exponent for a 32-block whose largest magnitude is mx: the values
+// divided by 2^s stay below 2^8 (e4m3 holds up to 448)
+__device__ __forceinline__ int block_exp(float mx)
+{
+    const int e = (int)((__float_as_uint(mx) >> 23) & 255u) - 127;
+    return mx > 0.0f ? max(e - 7, -127) : 0;
+}
+
+// The token as B operand of the fp4 x fp8 matrix-core products: each
+// 32-block of x split into a high part h = e4m3(x / 2^sh) and the residual
+// l = e4m3((x - h 2^sh) / 2^sl), x = h 2^sh + l 2^sl up to the residual's
+// rounding (x is bf16: the residual of its 8 significant bits keeps at most
+// 4, which e4m3 holds, unless it falls below the block's subnormal range).
+// Thread t converts elements [8t, 8t + 8) (v: 8 bf16); the four threads of
+// a block are one DPP quad.
+__device__ __forceinline__ void split_token8(uint4 v, int t, uint8_t *hi, uint8_t *lo, uint8_t *shi, uint8_t *slo)
+{
+    const uint32_t w[4] = {v.x, v.y, v.z, v.w};
+    float f[8];
+#pragma unroll
+    for (int i = 0; i < 4; i++) {
+        f[2 * i] = __uint_as_float(w[i] << 16);
+        f[2 * i + 1] = __uint_as_float(w[i] & 0xFFFF0000u);
+    }
+    float mx = 0.0f;
+#pragma unroll
+    for (int i = 0; i < 8; i++) mx = fmaxf(mx, fabsf(f[i]));
+    mx = fmaxf(mx, dppf<0xB1>(mx));  // quad_perm [1,0,3,2]
+    mx = fmaxf(mx, dppf<0x4E>(mx));  // quad_perm [2,3,0,1]
+    const int sh = block_exp(mx);
+    uint32_t ch[8];
+    float r[8], mr = 0.0f;
+#pragma unroll
+    for (int i = 0; i < 8; i++) {
+        ch[i] = e4m3_rne(ldexpf(f[i], -sh));
+        r[i] = f[i] - ldexpf(e4m3_val(ch[i]), sh);
+        mr = fmaxf(mr, fabsf(r[i]));
+    }
+    mr = fmaxf(mr, dppf<0xB1>(mr));
+    mr = fmaxf(mr, dppf<0x4E>(mr));
+    const int sl = block_exp(mr);
+    uint32_t ph[2] = {0, 0}, pl[2] = {0, 0};
+#pragma unroll
+    for (int i = 0; i < 8; i++) {
+        ph[i >> 2] |= ch[i] << (8 * (i & 3));
+        pl[i >> 2] |= e4m3_rne(ldexpf(r[i], -sl)) << (8 * (i & 3));
+    }
+    *reinterpret_cast<uint2 *>(hi + 8 * t) = make_uint2(ph[0], ph[1]);
+    *reinterpret_cast<uint2 *>(lo + 8 * t) = make_uint2(pl[0], pl[1]);
+    if ((t & 3) == 0) {
+        shi[t >> 2] = (uint8_t)(sh + 127);
+        slo[t >> 2] = (uint8_t)(sl + 127);
+    }
 }
 
 // One block of 8 waves per CU.  Waves 0-3 pick the experts (top-k) while
@@ -291,7 +379,13 @@ __global__ __launch_bounds__(kGuWaves * 64) void k_dec1_gateup(Dec1Params p)
     // the block's results, written out after its last unit (a global store
     // inside a unit loop would make the next register reuse wait for every
     // load in flight: stores and loads share one counter)
-    __shared__ __attribute__((aligned(8))) _Float16 s_hout[kGuMaxBlockUnits][kGuRows];
+    // per unit and K slice: the 16 gate and 16 up partial sums
+    __shared__ __attribute__((aligned(16))) float s_part[kGuMaxBlockUnits][kGuMaxStages][2 * kGuFeat];
+    // the token as two scaled fp8 (e4m3) parts, zero-padded to whole
+    // stages: high part at 0, residual at kX8Lo; their E8M0 scales per
+    // 32-block in s_xs (high, then residual at kXsLo)
+    __shared__ __attribute__((aligned(16))) uint8_t s_x8[kX8Lo + kXPad];
+    __shared__ uint8_t s_xs[2 * kXsLo];
     __shared__ __attribute__((aligned(8))) float s_ysh[kShMaxBlockUnits][kShRows];
     // [0], [1]: work queues (routed, shared); [2]: keying waves whose
     // candidates are written; [3]: picks ready
@@ -328,21 +422,22 @@ __global__ __launch_bounds__(kGuWaves * 64) void k_dec1_gateup(Dec1Params p)
 #pragma unroll
     for (int i = 0; i < kHsRounds; i++) hsv[i] = bld16(rhs, (threadIdx.x + i * kGuWaves * 64) * 16u, 0);
     __builtin_amdgcn_sched_barrier(0);
-    // the token's 64 inputs of this lane (blocks 2l, 2l + 1)
-    const int nbp = d / 64;                      // MX block pairs per row = lanes in use
-    const int lp = lane < nbp ? lane : nbp - 1;  // idle lanes re-read a valid pair
-    const float lmask = lane < nbp ? 1.0f : 0.0f;
-    uint32_t xr[32];
+    // the token (d bf16, 16 bytes per thread and round; zeros past d)
+    constexpr int kXRounds = (kXPad / 8 + kGuWaves * 64 - 1) / (kGuWaves * 64);
+    const auto rx = brsrc(p.x, (uint32_t)d * 2);
+    uint4 xv[kXRounds];
 #pragma unroll
-    for (int i = 0; i < 8; i++) {
-        const uint4 v = gl16(p.x + (size_t)lp * 64 + i * 8);
-        xr[4 * i + 0] = v.x; xr[4 * i + 1] = v.y; xr[4 * i + 2] = v.z; xr[4 * i + 3] = v.w;
-    }
+    for (int i = 0; i < kXRounds; i++) xv[i] = bld16(rx, (threadIdx.x + i * kGuWaves * 64) * 16u, 0);
     // the shared activations to LDS (unconditional: past S * F the loads
     // returned 0), the queues and flags cleared; the one workgroup barrier
     // before the last
 #pragma unroll
     for (int i = 0; i < kHsRounds; i++) reinterpret_cast<uint4 *>(s_hs)[threadIdx.x + i * kGuWaves * 64] = hsv[i];
+#pragma unroll
+    for (int i = 0; i < kXRounds; i++) {
+        const int t = threadIdx.x + i * kGuWaves * 64;  // elements [8t, 8t + 8); quads share a 32-block
+        if (8 * t < kXPad) split_token8(xv[i], t, s_x8, s_x8 + kX8Lo, s_xs, s_xs + kXsLo);
+    }
     if (threadIdx.x < 4) s_ctl[threadIdx.x] = 0;
     lds_barrier();
 
@@ -472,94 +567,149 @@ __global__ __launch_bounds__(kGuWaves * 64) void k_dec1_gateup(Dec1Params p)
     }
     spin_until(&s_ctl[3], 1);
 
-    // ---- routed gate/up units: (pick j, rows [4 rg, 4 rg + 4)) of W1 and W3.
-    // Unit u = j * F / 4 + rg writes H[4u, 4u + 4).  The block owns units
-    // [ubeg, ubeg + nloc) (contiguous rows of one or two picks).
-    const size_t qrow = (size_t)d / 2, srow = (size_t)d / 32;
-    const uint32_t voq = (uint32_t)lp * 32, vos = (uint32_t)lp * 2;
-    const int upr = F / kGuRows;  // units per pick
+    // ---- routed gate/up units on the matrix cores.  Unit u = j * F / 16 +
+    // fb covers features [16 fb, 16 fb + 16) of pick j.  Per 128-wide K
+    // window, one v_mfma_scale_f32_16x16x128_f8f6f4 per matrix multiplies
+    // the MXFP4 rows as they are stored (A: lane l holds row l % 16, MX block
+    // 4w + l / 16 -- one 16-byte load, the four lanes of a row reading 64
+    // contiguous bytes -- with its E8M0 scale) by the token split into two
+    // scaled fp8 parts (B: column 0 the high part, column 1 the residual; the
+    // other columns repeat column 0).  The matrix core applies both scales
+    // and sums exact products in fp32, so no weight is ever converted.  The
+    // work items are (unit, K slice of kGuWin windows), nloc * NS of them per
+    // block, taken from its queue (small items: a wave that the memory
+    // system serves late holds little when the queue runs dry); two items
+    // in flight per wave.  Rows end as D[row][0] + D[row][1]: lane 16 g'
+    // holds features [4 g', 4 g' + 4) in registers 0-3 and stores them as
+    // the item's partial sums; after the block's last item the slices are
+    // summed in order and the activations written to H[16 u, 16 u + 16).
+    const uint32_t qrow = (uint32_t)d / 2, srow = (uint32_t)d / 32;
+    const int upr = F / kGuFeat;  // units per pick
     const int units = k * upr;
-    const int per = (units + gridDim.x - 1) / gridDim.x;
-    const int ubeg = blockIdx.x * per;
-    const int nloc = max(min(units - ubeg, per), 0);
+    // local unit v is unit blockIdx.x + v * gridDim.x: at any time the blocks
+    // stream neighbouring units, one sweep through the picks' rows
+    const int nloc = units > (int)blockIdx.x ? (units - 1 - (int)blockIdx.x) / (int)gridDim.x + 1 : 0;
+    const int nblk_row = d / 32;                    // MX blocks per row
+    const int nwin = (d + 127) / 128;               // 128-wide K windows
+    const int NS = (nwin + kGuWin - 1) / kGuWin;    // stages per unit
+    const int mrow = lane & 15, grp = lane >> 4;
+    const uint32_t vo_w = (uint32_t)mrow * qrow + 16u * grp;  // + 64 w (window) + row offset
+    const uint32_t vo_s = (uint32_t)mrow * srow + grp;        // + 4 w
+    // B operand bytes of this lane: the residual for column 1, else the high part
+    const uint8_t *xb8 = s_x8 + (mrow == 1 ? kX8Lo : 0);
+    const uint8_t *xs8 = s_xs + (mrow == 1 ? kXsLo : 0);
     // lane j holds pick j; a unit's expert comes out through readlane (a
-    // scalar), so the unit loop needs no vector temporary and no LDS read
+    // scalar), so the loads need no vector temporary and no LDS read
     const int my_e = lane < k ? s_eid[lane] : -1;
 
-    // loads of local unit v; past the block's range they read nothing (zero
-    // sized resources) but are still issued, so that the wait before a unit's
-    // arithmetic counts exactly the next unit's loads
-    auto load = [&](GuLoads &g, int v) __attribute__((always_inline)) {
-        const bool ok = v < nloc;
-        const int u = ok ? ubeg + v : 0;
-        const int j = u / upr, f0 = (u % upr) * kGuRows;
+    // loads of stage st of local unit v (past the block's range: zero-sized
+    // resources, nothing read; still issued so that the waits count exactly)
+    const int nitems = nloc * NS;
+    auto load = [&](GuStage &g, int item) __attribute__((always_inline)) {
+        const bool ok = item < nitems;
+        const int v = item / NS, st = item - v * NS;
+        const int u = ok ? (int)blockIdx.x + v * (int)gridDim.x : 0;
+        const int j = u / upr, f0 = (u % upr) * kGuFeat;
         const int e = max(__builtin_amdgcn_readlane(my_e, j), 0);  // no pick: expert 0, never used
-        const uint32_t qbytes = ok ? (uint32_t)(F * qrow) : 0u, sbytes = ok ? (uint32_t)(F * srow) : 0u;
+        const uint32_t qbytes = ok ? (uint32_t)F * qrow : 0u, sbytes = ok ? (uint32_t)F * srow : 0u;
         const size_t qe = (size_t)e * F * qrow, se = (size_t)e * F * srow;
         const auto r1 = brsrc(p.w1q + qe, qbytes), r3 = brsrc(p.w3q + qe, qbytes);
         const auto t1 = brsrc(p.w1s + se, sbytes), t3 = brsrc(p.w3s + se, sbytes);
+        const uint32_t so = (uint32_t)f0 * qrow + (uint32_t)st * (kGuWin * 64);
+        const uint32_t ss = (uint32_t)f0 * srow + (uint32_t)st * (kGuWin * 4);
 #pragma unroll
-        for (int r = 0; r < kGuRows; r++) {
-            const uint32_t so = (uint32_t)((f0 + r) * qrow), ss = (uint32_t)((f0 + r) * srow);
-            g.c[r][0][0] = bld16(r1, voq, so);
-            g.c[r][0][1] = bld16(r1, voq + 16, so);
-            g.c[r][1][0] = bld16(r3, voq, so);
-            g.c[r][1][1] = bld16(r3, voq + 16, so);
-            g.sc[r][0] = bld2(t1, vos, ss);
-            g.sc[r][1] = bld2(t3, vos, ss);
+        for (int w = 0; w < kGuWin; w++) {
+            g.c[0][w] = bld16(r1, vo_w + 64u * w, so);
+            g.c[1][w] = bld16(r3, vo_w + 64u * w, so);
+        }
+#pragma unroll
+        for (int w = 0; w < kGuWin; w++) {
+            g.s[0][w] = bld1(t1, vo_s + 4u * w, ss);
+            g.s[1][w] = bld1(t3, vo_s + 4u * w, ss);
         }
         // (all of them issued before the arithmetic that follows)
         __builtin_amdgcn_sched_barrier(0);
     };
-    auto compute = [&](const GuLoads &g, int v) __attribute__((always_inline)) {
-        float gv[kGuRows], uv[kGuRows];
+    f32x4_t acc[2][2];  // [gate, up][even, odd window]
+    // multiply item `item` (valid) held in g, store its partial sums
+    auto compute = [&](const GuStage &g, int item) __attribute__((always_inline)) {
+        const int v = item / NS, st = item - v * NS;
 #pragma unroll
-        for (int r = 0; r < kGuRows; r++) {
-            const float g0 = fp4x32_dot_bf16(g.c[r][0][0], xr);
-            const float g1 = fp4x32_dot_bf16(g.c[r][0][1], xr + 16);
-            const float u0 = fp4x32_dot_bf16(g.c[r][1][0], xr);
-            const float u1 = fp4x32_dot_bf16(g.c[r][1][1], xr + 16);
-            gv[r] = wave_total(scaled2(g0, g1, g.sc[r][0]) * lmask);
-            uv[r] = wave_total(scaled2(u0, u1, g.sc[r][1]) * lmask);
+        for (int m = 0; m < 2; m++)
+#pragma unroll
+            for (int h = 0; h < 2; h++) acc[m][h] = f32x4_t{0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+        for (int w = 0; w < kGuWin; w++) {
+            const int wg = st * kGuWin + w;
+            // B: this lane's 32 codes (k = 128 wg + 16 grp + [0, 16) and
+            // 128 wg + 64 + 16 grp + [0, 16)) and the scale of block 4 wg + grp
+            const uint4 b0 = *reinterpret_cast<const uint4 *>(xb8 + wg * 128 + grp * 16);
+            const uint4 b1 = *reinterpret_cast<const uint4 *>(xb8 + wg * 128 + 64 + grp * 16);
+            const i32x8_t bv = {(int)b0.x, (int)b0.y, (int)b0.z, (int)b0.w, (int)b1.x, (int)b1.y, (int)b1.z, (int)b1.w};
+            const int bs = xs8[4 * wg + grp];
+            // A scales: a 255 byte (no value) or a block past the row counts as
+            // nothing (the smallest scale; the token is 0 past the row)
+            const bool okb = 4 * wg + grp < nblk_row;
+#pragma unroll
+            for (int m = 0; m < 2; m++) {
+                const uint32_t sb = g.s[m][w];
+                const int as = (okb && sb != 255u) ? (int)sb : 0;
+                const uint4 q = g.c[m][w];
+                const i32x8_t av = {(int)q.x, (int)q.y, (int)q.z, (int)q.w, 0, 0, 0, 0};
+                acc[m][w & 1] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(av, bv, acc[m][w & 1], 4, 0, 0, as, 0, bs);
+            }
         }
-        if (lane < kGuRows) {
-            float hv = 0.0f;
+        f32x4_t y[2];
 #pragma unroll
-            for (int r = 0; r < kGuRows; r++)
-                if (lane == r) hv = gated_act(gv[r], uv[r], s.act, s.b1, s.b2);
-            s_hout[v][lane] = (_Float16)hv;
+        for (int m = 0; m < 2; m++) {
+            y[m] = acc[m][0] + acc[m][1];
+            // + column 1 (the residual part): lane 16 g' + 1 -> lane 16 g'
+#pragma unroll
+            for (int i = 0; i < 4; i++) y[m][i] += dppf<0xB1>(y[m][i]);  // quad_perm [1,0,3,2]
+        }
+        if (mrow == 0) {
+            *reinterpret_cast<f32x4_t *>(&s_part[v][st][4 * grp]) = y[0];
+            *reinterpret_cast<f32x4_t *>(&s_part[v][st][kGuFeat + 4 * grp]) = y[1];
         }
     };
 
     {
-        int v0 = grab(q_addr), v1 = grab(q_addr);
-        if (v0 < nloc) {
-            GuLoads ga, gb;
-            load(ga, v0);
+        int ia = grab(q_addr);
+        if (ia < nitems) {
+            int ib = grab(q_addr);
+            GuStage ga, gb;
+            load(ga, ia);
+            load(gb, ib);
+            // (one exit, at the bottom: a second one makes the compiler
+            // merge the paths and wait for both buffers at the top)
             for (;;) {
-                // v0 (in ga) is multiplied now, v1 loaded, v2 grabbed
-                const int v2 = grab(q_addr);
-                load(gb, v1);
-                compute(ga, v0);
-                if (v1 >= nloc) break;
-                const int v3 = grab(q_addr);
-                load(ga, v2);
-                compute(gb, v1);
-                if (v2 >= nloc) break;
-                v0 = v2;
-                v1 = v3;
+                // ga holds item ia and is multiplied now; gb (ib) is in flight
+                compute(ga, ia);
+                const int ic = grab(q_addr);
+                load(ga, ic);
+                if (ib < nitems) compute(gb, ib);
+                const int id = grab(q_addr);
+                load(gb, id);
+                if (ic >= nitems) break;
+                ia = ic;
+                ib = id;
             }
         }
     }
 
     lds_barrier();
-    // the block's results: routed activations to H (4 fp16 per unit, skipped
-    // where no pick), shared outputs to Ysh
+    // the block's results: routed activations to H (the K slices summed in
+    // order; skipped where no pick), shared outputs to Ysh
     _Float16 *H = reinterpret_cast<_Float16 *>(p.w.H);
-    for (int i = threadIdx.x; i < nloc; i += kGuWaves * 64) {
-        const int u = ubeg + i;
-        if (s_eid[u / upr] >= 0)
-            *reinterpret_cast<uint2 *>(H + (size_t)u * kGuRows) = *reinterpret_cast<const uint2 *>(s_hout[i]);
+    for (int i = threadIdx.x; i < nloc * kGuFeat; i += kGuWaves * 64) {
+        const int v = i / kGuFeat, f = i - v * kGuFeat;
+        const int u = (int)blockIdx.x + v * (int)gridDim.x;
+        float g = 0.0f, up = 0.0f;
+        for (int st = 0; st < NS; st++) {
+            g += s_part[v][st][f];
+            up += s_part[v][st][kGuFeat + f];
+        }
+        if (s_eid[u / upr] >= 0) H[(size_t)u * kGuFeat + f] = (_Float16)gated_act(g, up, s.act, s.b1, s.b2);
     }
     for (int i = threadIdx.x; i < nsloc; i += kGuWaves * 64)
         *reinterpret_cast<float2 *>(p.w.Ysh + (size_t)(sbeg + i) * kShRows) = *reinterpret_cast<const float2 *>(s_ysh[i]);
@@ -731,7 +881,7 @@ hipError_t launch_decode1(const Shape &s, const uint16_t *x, const Weights &wt, 
     p.out_bf16 = out_bf16;
     p.out_f32 = out_f32;
     // one block per CU, more if a block's ranges would not fit its LDS records
-    const int units = s.k * (s.F / kGuRows);
+    const int units = s.k * (s.F / kGuFeat);
     const int sh_units = p.shared ? s.S * (s.d / kShRows) : 0;
     const int nblk = max(cu_count(), max((units + kGuMaxBlockUnits - 1) / kGuMaxBlockUnits,
                                          (sh_units + kShMaxBlockUnits - 1) / kShMaxBlockUnits));
