@@ -147,18 +147,17 @@ __device__ __forceinline__ uint32_t score_bits(float ch)
     return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
 }
 
-template <int CTRL>
-__device__ __forceinline__ uint32_t dppu(uint32_t v)
-{
-    return (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, CTRL, 0xF, 0xF, true);
-}
-
 // LDS flags between the waves of a block (no workgroup barrier: the other
 // waves keep streaming meanwhile).  The LDS performs one wave's accesses in
 // issue order, so a flag raised after a wave's writes is seen after them.
 __device__ __forceinline__ int lds_peek(const int *p)
 {
-    return __builtin_amdgcn_readfirstlane(*reinterpret_cast<const volatile int *>(p));
+    // (written out: a volatile read would also wait for every global load
+    // in flight)
+    int v;
+    const uint32_t a = (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) int *)p;
+    asm volatile("ds_read_b32 %0, %1\n\ts_waitcnt lgkmcnt(0)" : "=v"(v) : "v"(a) : "memory");
+    return __builtin_amdgcn_readfirstlane(v);
 }
 __device__ __forceinline__ void spin_until(const int *p, int target)
 {
@@ -176,10 +175,12 @@ __device__ __forceinline__ void flag_add(int *p)
 // [w * EQ, (w + 1) * EQ), EQ = ceil(E / 4) <= 256 (slot i of lane l is
 // expert w * EQ + 64 i + l), from the logits and biases the caller loaded,
 // stores their unbiased scores, and writes its k best as 64-bit keys (score
-// bits, then the inverted id: distinct) to cand[w * k, (w + 1) * k), found
-// in k rounds: a 32-bit max over the wave (DPP inside rows of 16, readlane
-// across them), then the lowest id holding it (first slot with a match,
-// lowest lane).  Rounds past the wave's real experts give key 0.
+// bits, then the inverted id: distinct) to cand[w * k, (w + 1) * k), in no
+// particular order.  The k-th largest 32-bit key t of the wave is found by
+// bisection (32 steps: is #{key >= t | bit} >= k?, counted with ballots);
+// the keys above t and then the keys equal to t in id order (slot, then
+// lane) fill the k places.  Padding keys are 0 (a wave with fewer than k
+// experts writes zeros, never picked).
 __device__ __forceinline__ void topk_candidates(int E, int k, int wave, const float (&lg)[4],
                                                 const float (&bs)[4], uint64_t *cand, float *score)
 {
@@ -197,61 +198,58 @@ __device__ __forceinline__ void topk_candidates(int E, int k, int wave, const fl
         // padding is never selected: real keys are > 0
         key[i] = ok ? score_bits(sc + bs[i]) : 0u;
     }
-    uint64_t mine = 0;
+    uint32_t t = 0;
 #pragma unroll 1
-    for (int j = 0; j < k; j++) {
-        uint32_t m = max(max(key[0], key[1]), max(key[2], key[3]));
-        m = max(m, dppu<0xB1>(m));   // quad_perm [1,0,3,2]
-        m = max(m, dppu<0x4E>(m));   // quad_perm [2,3,0,1]
-        m = max(m, dppu<0x141>(m));  // row_half_mirror
-        m = max(m, dppu<0x140>(m));  // row_mirror
-        const uint32_t w = max(max((uint32_t)__builtin_amdgcn_readlane((int)m, 0), (uint32_t)__builtin_amdgcn_readlane((int)m, 16)),
-                               max((uint32_t)__builtin_amdgcn_readlane((int)m, 32), (uint32_t)__builtin_amdgcn_readlane((int)m, 48)));
-        const uint64_t b0 = __builtin_amdgcn_ballot_w64(key[0] == w);
-        const uint64_t b1 = __builtin_amdgcn_ballot_w64(key[1] == w);
-        const uint64_t b2 = __builtin_amdgcn_ballot_w64(key[2] == w);
-        const uint64_t b3 = __builtin_amdgcn_ballot_w64(key[3] == w);
-        const int sl = b0 ? 0 : b1 ? 1 : b2 ? 2 : 3;
-        const uint64_t bm = b0 ? b0 : b1 ? b1 : b2 ? b2 : b3;
-        const int l = (int)__builtin_ctzll(bm | (1ull << 63));
-        const int e = base + 64 * sl + l;
-        const bool me = lane == l;
+    for (int bit = 31; bit >= 0; bit--) {
+        const uint32_t c = t | (1u << bit);
+        int n = 0;
 #pragma unroll
-        for (int i = 0; i < 4; i++) key[i] = (me && sl == i) ? 0u : key[i];
-        const uint64_t ck = w ? (((uint64_t)w << 32) | (uint32_t)(~(uint32_t)e)) : 0ull;
-        mine = lane == j ? ck : mine;
+        for (int i = 0; i < 4; i++) n += __builtin_popcountll(__builtin_amdgcn_ballot_w64(key[i] >= c));
+        t = n >= k ? c : t;
     }
-    if (lane < k) cand[wave * k + lane] = mine;
+    int above = 0;
+#pragma unroll
+    for (int i = 0; i < 4; i++) above += __builtin_popcountll(__builtin_amdgcn_ballot_w64(key[i] > t));
+    const int need_eq = k - above;
+    int pg = 0, pe = 0;
+#pragma unroll
+    for (int i = 0; i < 4; i++) {
+        const uint64_t mg = __builtin_amdgcn_ballot_w64(key[i] > t);
+        const uint64_t me = __builtin_amdgcn_ballot_w64(key[i] == t);
+        const int bg = pg + (int)__builtin_amdgcn_mbcnt_hi((uint32_t)(mg >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)mg, 0u));
+        const int be = pe + (int)__builtin_amdgcn_mbcnt_hi((uint32_t)(me >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)me, 0u));
+        const int e = base + 64 * i + lane;
+        const uint64_t ck = key[i] ? (((uint64_t)key[i] << 32) | (uint32_t)(~(uint32_t)e)) : 0ull;
+        if (key[i] > t) cand[wave * k + bg] = ck;
+        if (key[i] == t && be < need_eq) cand[wave * k + above + be] = ck;
+        pg += __builtin_popcountll(mg);
+        pe += __builtin_popcountll(me);
+    }
 }
 
-// Part 2, one wave: the 4k candidates hold the global top k.  A candidate's
-// rank among them (distinct keys: a permutation) is the count of larger
-// ones; rank j < k makes it pick j (zero keys rank at least at the number
-// of real candidates, >= k).  Lanes j < k end with pick j (id) and its weight
-// (wt): the unbiased score, renormalised over the picks (fp32 sum in
-// selection order) if renorm, times routed_scale.
-__device__ __forceinline__ void topk_merge(int k, int renorm, float routed_scale, const uint64_t *cand,
-                                           uint64_t *sel, const float *score, int &id, float &wt)
+// Part 2, every keying wave once all 4k candidates are written: the 4k
+// candidates hold the global top k.  A candidate's rank among them
+// (distinct keys: a permutation) is the count of larger ones; each wave
+// ranks its own k, and rank j < k makes it pick j (zero keys rank at least
+// at the number of real candidates, >= k).
+__device__ __forceinline__ void topk_rank(int k, int wave, const uint64_t *cand, uint64_t *sel)
 {
     const int lane = threadIdx.x & 63;
-    const int nc = kTkWaves * k;  // <= 256: at most 4 per lane
-    uint64_t c[4];
-    int rank[4];
-#pragma unroll
-    for (int m = 0; m < 4; m++) {
-        c[m] = lane + 64 * m < nc ? cand[lane + 64 * m] : 0ull;
-        rank[m] = 0;
-    }
+    const int nc = kTkWaves * k;  // <= 256
+    const uint64_t c = lane < k ? cand[wave * k + lane] : 0ull;
+    int r = 0;
 #pragma unroll 8
-    for (int i = 0; i < nc; i++) {
-        const uint64_t o = cand[i];  // same address for all lanes: a broadcast
-#pragma unroll
-        for (int m = 0; m < 4; m++) rank[m] += o > c[m] ? 1 : 0;
-    }
-#pragma unroll
-    for (int m = 0; m < 4; m++)
-        if (lane + 64 * m < nc && rank[m] < k) sel[rank[m]] = c[m];
-    // (one wave: its LDS accesses are performed in order)
+    for (int i = 0; i < nc; i++) r += cand[i] > c ? 1 : 0;  // same address for all lanes: a broadcast
+    if (lane < k && r < k) sel[r] = c;
+}
+
+// Part 3, one wave: lanes j < k end with pick j (id) and its weight (wt):
+// the unbiased score, renormalised over the picks (fp32 sum in selection
+// order) if renorm, times routed_scale.
+__device__ __forceinline__ void topk_weights(int k, int renorm, float routed_scale, const uint64_t *sel,
+                                             const float *score, int &id, float &wt)
+{
+    const int lane = threadIdx.x & 63;
     const uint64_t kk = lane < k ? sel[lane] : 0ull;
     const int my_id = lane < k ? (int)(~(uint32_t)kk) : 0;
     const float my_s = lane < k ? score[my_id] : 0.0f;
@@ -268,9 +266,21 @@ __device__ __forceinline__ void topk_merge(int k, int renorm, float routed_scale
 
 // one gate/up stage of a lane: per K window, its MX block of W1 and of W3
 // (16 bytes) and their scale bytes
-struct GuStage {
+// (SA: the 16 scale bytes of a row's item in one aligned 16-byte load,
+// byte 4 w + g for window w of lane group g; else one byte load each)
+template <bool SA> struct GuStage;
+template <> struct GuStage<true> {
+    uint4 c[2][kGuWin];
+    uint4 s[2];
+    __device__ __forceinline__ uint32_t scale(int m, int w, int grp) const
+    {
+        return (u4at(s[m], w) >> (8 * grp)) & 0xFFu;
+    }
+};
+template <> struct GuStage<false> {
     uint4 c[2][kGuWin];
     uint32_t s[2][kGuWin];
+    __device__ __forceinline__ uint32_t scale(int m, int w, int) const { return s[m][w]; }
 };
 
 // Work queue of a block: local units [0, n) taken in order by its waves,
@@ -367,7 +377,8 @@ __device__ __forceinline__ void split_token8(uint4 v, int t, uint8_t *hi, uint8_
 // waves 4-7 stream the shared experts' down rows (a work queue of their
 // own); then every wave takes routed gate/up units from the block's queue.
 // SHC: 16-byte chunks per lane of a shared down row (ceil(F / 512)).
-template <int SHC>
+// SA: a row's scale bytes are 16-byte aligned (d % 512 == 0).
+template <int SHC, bool SA>
 __global__ __launch_bounds__(kGuWaves * 64) void k_dec1_gateup(Dec1Params p)
 {
     __shared__ uint64_t s_cand[kTkWaves * kMaxTopK];
@@ -388,8 +399,10 @@ __global__ __launch_bounds__(kGuWaves * 64) void k_dec1_gateup(Dec1Params p)
     __shared__ uint8_t s_xs[2 * kXsLo];
     __shared__ __attribute__((aligned(8))) float s_ysh[kShMaxBlockUnits][kShRows];
     // [0], [1]: work queues (routed, shared); [2]: keying waves whose
-    // candidates are written; [3]: picks ready
-    __shared__ int s_ctl[4];
+    // candidates are written; [3]: picks ready; [4]: keying waves whose
+    // candidates are ranked; [5]: waves 4-7 whose part of the token and of
+    // the shared activations is staged
+    __shared__ int s_ctl[6];
     const Shape &s = p.s;
     const int lane = threadIdx.x & 63;
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -415,38 +428,26 @@ __global__ __launch_bounds__(kGuWaves * 64) void k_dec1_gateup(Dec1Params p)
     }
     const int gid = (int)bld4(rid, lane * 4u, 0);
     const float gwt = __uint_as_float(bld4(rwt, lane * 4u, 0));
-    // the shared activations (S * F fp32, to LDS)
-    constexpr int kHsRounds = kShMaxHs / 4 / (kGuWaves * 64);
-    const auto rhs = brsrc(p.w.Hs, (uint32_t)(S * F * 4));
+    __builtin_amdgcn_sched_barrier(0);
+    // waves 4-7 (thread st of 256) stage the shared activations (S * F
+    // fp32) and the token (d bf16; zeros past d), 16 bytes per round
+    const bool stager = wave >= kTkWaves;
+    const int st = (int)threadIdx.x - kTkWaves * 64;
+    constexpr int kStThreads = (kGuWaves - kTkWaves) * 64;
+    constexpr int kHsRounds = kShMaxHs / 4 / kStThreads;
+    const auto rhs = brsrc(p.w.Hs, stager ? (uint32_t)(S * F * 4) : 0u);
     uint4 hsv[kHsRounds];
 #pragma unroll
-    for (int i = 0; i < kHsRounds; i++) hsv[i] = bld16(rhs, (threadIdx.x + i * kGuWaves * 64) * 16u, 0);
-    __builtin_amdgcn_sched_barrier(0);
-    // the token (d bf16, 16 bytes per thread and round; zeros past d)
-    constexpr int kXRounds = (kXPad / 8 + kGuWaves * 64 - 1) / (kGuWaves * 64);
-    const auto rx = brsrc(p.x, (uint32_t)d * 2);
+    for (int i = 0; i < kHsRounds; i++) hsv[i] = bld16(rhs, (uint32_t)(st + i * kStThreads) * 16u, 0);
+    constexpr int kXRounds = (kXPad / 8 + kStThreads - 1) / kStThreads;
+    const auto rx = brsrc(p.x, stager ? (uint32_t)d * 2 : 0u);
     uint4 xv[kXRounds];
 #pragma unroll
-    for (int i = 0; i < kXRounds; i++) xv[i] = bld16(rx, (threadIdx.x + i * kGuWaves * 64) * 16u, 0);
-    // the shared activations to LDS (unconditional: past S * F the loads
-    // returned 0), the queues and flags cleared; the one workgroup barrier
-    // before the last
-#pragma unroll
-    for (int i = 0; i < kHsRounds; i++) reinterpret_cast<uint4 *>(s_hs)[threadIdx.x + i * kGuWaves * 64] = hsv[i];
-#pragma unroll
-    for (int i = 0; i < kXRounds; i++) {
-        const int t = threadIdx.x + i * kGuWaves * 64;  // elements [8t, 8t + 8); quads share a 32-block
-        if (8 * t < kXPad) split_token8(xv[i], t, s_x8, s_x8 + kX8Lo, s_xs, s_xs + kXsLo);
-    }
-    if (threadIdx.x < 4) s_ctl[threadIdx.x] = 0;
-    lds_barrier();
-
-    const uint32_t q_addr = (uint32_t)(uintptr_t)(__attribute__((address_space(3))) int *)&s_ctl[0];
-    const uint32_t s_addr = q_addr + 4;
-
+    for (int i = 0; i < kXRounds; i++) xv[i] = bld16(rx, (uint32_t)(st + i * kStThreads) * 16u, 0);
     // ---- shared experts' down rows [2 n', 2 n' + 2) of expert si: unit
     // u = si * d / 2 + n' writes Ysh[2u, 2u + 2) (T = 1).  The block owns
-    // units [sbeg, sbeg + nsloc), streamed by waves 4-7 from their queue.
+    // units [sbeg, sbeg + nsloc), streamed by waves 4-7 from their queue
+    // (the first four at once, before the top-k's inputs are even in).
     const int per_sh = d / kShRows;
     const int nsh = S * per_sh;
     const int sper = (nsh + gridDim.x - 1) / gridDim.x;
@@ -494,16 +495,34 @@ __global__ __launch_bounds__(kGuWaves * 64) void k_dec1_gateup(Dec1Params p)
         if (lane < kShRows) s_ysh[v][lane] = o;
     };
 
+    // waves 4-7: local shared units 0-3, loaded now (for waves 0-3 the
+    // resources are empty: nothing read, and the same program for all)
+    uint4 sa[kShRows][SHC];
+    load_sh(sa, wave >= kTkWaves ? wave - kTkWaves : nsloc);
+
+    // the queues and flags cleared: the one workgroup barrier before the
+    // last (the loads above stay in flight; the shared queue starts past
+    // the four units already loaded)
+    if (threadIdx.x < 6) s_ctl[threadIdx.x] = threadIdx.x == 1 ? kTkWaves * 64 : 0;
+    lds_barrier();
+
+    const uint32_t q_addr = (uint32_t)(uintptr_t)(__attribute__((address_space(3))) int *)&s_ctl[0];
+    const uint32_t s_addr = q_addr + 4;
+
     if (wave < kTkWaves) {
-        // ---- the picks
+        // ---- the picks (ahead of the streaming waves on the same SIMD)
+        __builtin_amdgcn_s_setprio(2);
         int id = -1;
         float wt = 0.0f;
         if (p.do_topk) {
             topk_candidates(E, k, wave, lg, bs, s_cand, s_score);
             flag_add(&s_ctl[2]);
+            spin_until(&s_ctl[2], kTkWaves);
+            topk_rank(k, wave, s_cand, s_sel);
+            flag_add(&s_ctl[4]);
             if (wave == 0) {
-                spin_until(&s_ctl[2], kTkWaves);
-                topk_merge(k, s.renorm, s.routed_scale, s_cand, s_sel, s_score, id, wt);
+                spin_until(&s_ctl[4], kTkWaves);
+                topk_weights(k, s.renorm, s.routed_scale, s_sel, s_score, id, wt);
             }
         } else {
             id = lane < k ? gid : -1;
@@ -545,27 +564,42 @@ __global__ __launch_bounds__(kGuWaves * 64) void k_dec1_gateup(Dec1Params p)
             }
             flag_add(&s_ctl[3]);
         }
-    } else if (nsloc > 0) {
-        // ---- the shared rows, two units in flight per wave
-        int v0 = grab(s_addr), v1 = grab(s_addr);
-        if (v0 < nsloc) {
-            uint4 sa[kShRows][SHC], sb[kShRows][SHC];
-            load_sh(sa, v0);
+        __builtin_amdgcn_s_setprio(0);
+    } else {
+        // ---- staging: the shared activations to LDS (unconditional: past
+        // S * F the loads returned 0), the token split into its two fp8
+        // parts; then all four staging waves are waited for
+#pragma unroll
+        for (int i = 0; i < kHsRounds; i++) reinterpret_cast<uint4 *>(s_hs)[st + i * kStThreads] = hsv[i];
+#pragma unroll
+        for (int i = 0; i < kXRounds; i++) {
+            const int t = st + i * kStThreads;  // elements [8t, 8t + 8); quads share a 32-block
+            if (8 * t < kXPad) split_token8(xv[i], t, s_x8, s_x8 + kX8Lo, s_xs, s_xs + kXsLo);
+        }
+        flag_add(&s_ctl[5]);
+        spin_until(&s_ctl[5], kGuWaves - kTkWaves);
+        // ---- the shared rows, two units in flight per wave (unit va is in sa)
+        int va = wave - kTkWaves;
+        if (va < nsloc) {
+            uint4 sb[kShRows][SHC];
+            int vb = grab(s_addr);
+            load_sh(sb, vb);
+            // (one exit, at the bottom)
             for (;;) {
-                const int v2 = grab(s_addr);
-                load_sh(sb, v1);
-                dot_sh(sa, v0);
-                if (v1 >= nsloc) break;
-                const int v3 = grab(s_addr);
-                load_sh(sa, v2);
-                dot_sh(sb, v1);
-                if (v2 >= nsloc) break;
-                v0 = v2;
-                v1 = v3;
+                dot_sh(sa, va);
+                const int vc = grab(s_addr);
+                load_sh(sa, vc);
+                if (vb < nsloc) dot_sh(sb, vb);
+                const int vd = grab(s_addr);
+                load_sh(sb, vd);
+                if (vc >= nsloc) break;
+                va = vc;
+                vb = vd;
             }
         }
     }
     spin_until(&s_ctl[3], 1);
+    spin_until(&s_ctl[5], kGuWaves - kTkWaves);
 
     // ---- routed gate/up units on the matrix cores.  Unit u = j * F / 16 +
     // fb covers features [16 fb, 16 fb + 16) of pick j.  Per 128-wide K
@@ -595,6 +629,7 @@ __global__ __launch_bounds__(kGuWaves * 64) void k_dec1_gateup(Dec1Params p)
     const int mrow = lane & 15, grp = lane >> 4;
     const uint32_t vo_w = (uint32_t)mrow * qrow + 16u * grp;  // + 64 w (window) + row offset
     const uint32_t vo_s = (uint32_t)mrow * srow + grp;        // + 4 w
+    const uint32_t vo_s16 = (uint32_t)mrow * srow;            // the row's 16 bytes of the item
     // B operand bytes of this lane: the residual for column 1, else the high part
     const uint8_t *xb8 = s_x8 + (mrow == 1 ? kX8Lo : 0);
     const uint8_t *xs8 = s_xs + (mrow == 1 ? kXsLo : 0);
@@ -605,7 +640,7 @@ __global__ __launch_bounds__(kGuWaves * 64) void k_dec1_gateup(Dec1Params p)
     // loads of stage st of local unit v (past the block's range: zero-sized
     // resources, nothing read; still issued so that the waits count exactly)
     const int nitems = nloc * NS;
-    auto load = [&](GuStage &g, int item) __attribute__((always_inline)) {
+    auto load = [&](GuStage<SA> &g, int item) __attribute__((always_inline)) {
         const bool ok = item < nitems;
         const int v = item / NS, st = item - v * NS;
         const int u = ok ? (int)blockIdx.x + v * (int)gridDim.x : 0;
@@ -622,17 +657,22 @@ __global__ __launch_bounds__(kGuWaves * 64) void k_dec1_gateup(Dec1Params p)
             g.c[0][w] = bld16(r1, vo_w + 64u * w, so);
             g.c[1][w] = bld16(r3, vo_w + 64u * w, so);
         }
+        if constexpr (SA) {
+            g.s[0] = bld16(t1, vo_s16, ss);
+            g.s[1] = bld16(t3, vo_s16, ss);
+        } else {
 #pragma unroll
-        for (int w = 0; w < kGuWin; w++) {
-            g.s[0][w] = bld1(t1, vo_s + 4u * w, ss);
-            g.s[1][w] = bld1(t3, vo_s + 4u * w, ss);
+            for (int w = 0; w < kGuWin; w++) {
+                g.s[0][w] = bld1(t1, vo_s + 4u * w, ss);
+                g.s[1][w] = bld1(t3, vo_s + 4u * w, ss);
+            }
         }
         // (all of them issued before the arithmetic that follows)
         __builtin_amdgcn_sched_barrier(0);
     };
     f32x4_t acc[2][2];  // [gate, up][even, odd window]
     // multiply item `item` (valid) held in g, store its partial sums
-    auto compute = [&](const GuStage &g, int item) __attribute__((always_inline)) {
+    auto compute = [&](const GuStage<SA> &g, int item) __attribute__((always_inline)) {
         const int v = item / NS, st = item - v * NS;
 #pragma unroll
         for (int m = 0; m < 2; m++)
@@ -652,7 +692,7 @@ __global__ __launch_bounds__(kGuWaves * 64) void k_dec1_gateup(Dec1Params p)
             const bool okb = 4 * wg + grp < nblk_row;
 #pragma unroll
             for (int m = 0; m < 2; m++) {
-                const uint32_t sb = g.s[m][w];
+                const uint32_t sb = g.scale(m, w, grp);
                 const int as = (okb && sb != 255u) ? (int)sb : 0;
                 const uint4 q = g.c[m][w];
                 const i32x8_t av = {(int)q.x, (int)q.y, (int)q.z, (int)q.w, 0, 0, 0, 0};
@@ -677,7 +717,7 @@ __global__ __launch_bounds__(kGuWaves * 64) void k_dec1_gateup(Dec1Params p)
         int ia = grab(q_addr);
         if (ia < nitems) {
             int ib = grab(q_addr);
-            GuStage ga, gb;
+            GuStage<SA> ga, gb;
             load(ga, ia);
             load(gb, ib);
             // (one exit, at the bottom: a second one makes the compiler
@@ -886,10 +926,17 @@ hipError_t launch_decode1(const Shape &s, const uint16_t *x, const Weights &wt, 
     const int nblk = max(cu_count(), max((units + kGuMaxBlockUnits - 1) / kGuMaxBlockUnits,
                                          (sh_units + kShMaxBlockUnits - 1) / kShMaxBlockUnits));
     const int shc = (s.F / 8 + 63) / 64;  // 16-byte chunks per lane of a shared down row
-    if (shc <= 2) k_dec1_gateup<2><<<nblk, kGuWaves * 64, 0, stream>>>(p);
-    else if (shc <= 4) k_dec1_gateup<4><<<nblk, kGuWaves * 64, 0, stream>>>(p);
-    else if (shc <= 6) k_dec1_gateup<6><<<nblk, kGuWaves * 64, 0, stream>>>(p);
-    else k_dec1_gateup<8><<<nblk, kGuWaves * 64, 0, stream>>>(p);
+    const bool sa = s.d % 512 == 0;
+#define MOE_DEC1_GU(C)                                                                   \
+    do {                                                                                 \
+        if (sa) k_dec1_gateup<C, true><<<nblk, kGuWaves * 64, 0, stream>>>(p);           \
+        else k_dec1_gateup<C, false><<<nblk, kGuWaves * 64, 0, stream>>>(p);            \
+    } while (0)
+    if (shc <= 2) MOE_DEC1_GU(2);
+    else if (shc <= 4) MOE_DEC1_GU(4);
+    else if (shc <= 6) MOE_DEC1_GU(6);
+    else MOE_DEC1_GU(8);
+#undef MOE_DEC1_GU
     if (ev2) (void)hipEventRecord(ev2[0], stream);
     const int nd = (s.d + kDnBlockRows - 1) / kDnBlockRows;
     k_dec1_down<<<nd, kDnWaves * 64, (size_t)s.k * s.F * 2, stream>>>(p);
