@@ -32,33 +32,65 @@ PEAK_HBM_GBS = 8000.0      # MI355X HBM3E, GB/s
 PEAK_BF16_TFLOPS = 2500.0  # MI355X dense bf16 MFMA, TFLOP/s
 METRIC = "MoE layer decode tok/s + HBM GB/s vs peak; prefill TFLOP/s vs MFMA peak"
 PHASES = ("router_logits", "topk_dispatch", "expert_gate_up", "expert_down", "combine")
-KERNELS = {"router_logits": "k_router_logits", "topk_dispatch": "k_dispatch_small/k_topk+k_dispatch_*",
-           "expert_gate_up": "k_gemv_gateup", "expert_down": "k_gemv_down", "combine": "k_combine"}
+# kernels of each phase, per path: the fused one-token path (top-k, dispatch
+# and combine folded into the expert kernels), the GEMV path (small T), the
+# MFMA path (grouped GEMM over expert-sorted tokens)
+KERNELS = {
+    "decode1": {"router_logits": "k_front (router + shared gate/up)", "topk_dispatch": "-",
+                "expert_gate_up": "k_dec1_gateup", "expert_down": "k_dec1_down", "combine": "-"},
+    "gemv": {"router_logits": "k_front", "topk_dispatch": "k_dispatch_small/k_topk+k_dispatch_*",
+             "expert_gate_up": "k_gemv_gateup", "expert_down": "k_gemv_down", "combine": "k_combine"},
+    "mfma": {"router_logits": "k_split_router + k_ggemm<M_R>", "topk_dispatch": "k_topk + k_dispatch_*",
+             "expert_gate_up": "k_ggemm<M_S13> + k_ggemm<M_G13>", "expert_down": "k_ggemm<M_S2> + k_ggemm<M_D2>",
+             "combine": "k_combine"},
+}
+
+
+# HBM bytes per dispatch measured by rocprofv3 (FETCH_SIZE and WRITE_SIZE,
+# each scaled by what the counter reads for a plain 256 MiB copy), for the
+# kernel as it stands; the summary and the commands are in
+# profiles/moe_layer_kernels__k3-moe-decode-T1.md.  A kernel changed since
+# its counters were taken has no entry here (traffic: null).
+MEASURED_TRAFFIC = {"k_dec1_gateup": 233524098}
 
 
 def log(*a):
     print(*a, file=sys.stderr, flush=True)
 
 
-def phase_bytes(shape, T, counts):
+def phase_bytes(shape, T, counts, kind):
     """Algorithmic HBM bytes of each phase for one step (every touched expert
-    read once; shared, router, tokens and outputs once; workspace excluded)."""
+    read once; shared, router, tokens and outputs once; workspace excluded).
+    On the fused one-token path the shared experts' gate/up runs in the front
+    kernel and their down in the gate/up kernel."""
     d, F, S, E, k = shape.d_model, shape.d_ffn, shape.n_shared, shape.n_experts, shape.top_k
     active = int((counts > 0).sum())
     w13 = 2 * (F * d // 2 + F * d // 32)
     w2 = d * F // 2 + d * F // 32
+    sh13, sh2 = S * 2 * F * d * 2, S * d * F * 2
+    if kind == "decode1":
+        return {"router_logits": E * d * 4 + sh13 + T * d * 2, "topk_dispatch": 0,
+                "expert_gate_up": active * w13 + sh2 + T * d * 2,
+                "expert_down": active * w2 + T * d * 2, "combine": 0}
     return {
         "router_logits": E * d * 4 + T * d * 2,
         "topk_dispatch": 0,
-        "expert_gate_up": active * w13 + S * 2 * F * d * 2 + T * d * 2,
-        "expert_down": active * w2 + S * d * F * 2,
+        "expert_gate_up": active * w13 + sh13 + T * d * 2,
+        "expert_down": active * w2 + sh2,
         "combine": T * d * 2,
     }
 
 
-def flops(shape, T):
+def phase_flops(shape, T):
+    """Algorithmic flops of each phase (2 per multiply-add)."""
     d, F, S, E, k = shape.d_model, shape.d_ffn, shape.n_shared, shape.n_experts, shape.top_k
-    return T * (k * 6 * d * F + S * 6 * d * F + 2 * E * d)
+    return {"router_logits": 2 * T * E * d, "topk_dispatch": 0,
+            "expert_gate_up": 4 * T * (k + S) * d * F, "expert_down": 2 * T * (k + S) * d * F,
+            "combine": 0}
+
+
+def flops(shape, T):
+    return sum(phase_flops(shape, T).values())
 
 
 def cpu_baseline(shape, seed, layer, zipf, pool, budget_s):
@@ -101,6 +133,9 @@ def main():
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-graph", action="store_true", help="time eager launches instead of HIP graph replays")
+    ap.add_argument("--copy-mib", type=int, default=0,
+                    help="only run a plain device copy of this many MiB, --steps times (the known-size "
+                         "kernel that scales the FETCH_SIZE / WRITE_SIZE counters)")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py measures one GPU: this layer's path is built and measured on a single "
@@ -108,6 +143,15 @@ def main():
         sys.exit(2)
 
     import torch
+    if args.copy_mib:
+        n = args.copy_mib << 20
+        src = torch.ones(n, dtype=torch.uint8, device="cuda")
+        dst = torch.empty_like(src)
+        for _ in range(args.steps):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        print(json.dumps({"copy_bytes": n, "steps": args.steps}), flush=True)
+        return
     import synth
     import synth.device as sdev
     import quantized_expert_gemv_sigmoid_amd as moe
@@ -136,6 +180,8 @@ def main():
         torch.cuda.synchronize()
         counts.append(cnt.cpu().numpy().copy())
     path = moe.path_for(desc, T)
+    # (the fused one-token kernels serve T = 1 on the GEMV path)
+    kind = "decode1" if (path == 1 and T == 1) else {1: "gemv", 2: "mfma"}[path]
 
     stream = torch.cuda.current_stream()
     for i in range(args.warmup):
@@ -179,15 +225,26 @@ def main():
 
     ph_ms = {p: float(np.mean([evs[i][j].elapsed_time(evs[i][j + 1]) for i in range(K)]))
              for j, p in enumerate(PHASES)}
-    ph_bytes = {p: float(np.mean([phase_bytes(shape, T, counts[i % npool])[p] for i in range(K)]))
+    ph_bytes = {p: float(np.mean([phase_bytes(shape, T, counts[i % npool], kind)[p] for i in range(K)]))
                 for p in PHASES}
+    ph_flops = phase_flops(shape, T)
     step_bytes = sum(ph_bytes.values())
     dom = max(("expert_gate_up", "expert_down"), key=lambda p: ph_ms[p])
-    achieved = ph_bytes[dom] / (ph_ms[dom] * 1e-3) / 1e9
-    roofline = {"bound": "hbm", "achieved": round(achieved, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
-                "frac": round(achieved / PEAK_HBM_GBS, 4), "traffic": None,
-                "kernel": KERNELS[dom], "bytes_per_launch": int(ph_bytes[dom]),
-                "avg_launch_us": round(ph_ms[dom] * 1e3, 2)}
+    if kind == "mfma":
+        # a dense contraction on the matrix cores (bf16 after the in-register
+        # MXFP4 decode): against the bf16 MFMA peak
+        achieved = ph_flops[dom] / (ph_ms[dom] * 1e-3) / 1e12
+        roofline = {"bound": "mfma", "achieved": round(achieved, 1), "peak": PEAK_BF16_TFLOPS,
+                    "unit": "TFLOP/s", "frac": round(achieved / PEAK_BF16_TFLOPS, 4), "traffic": None,
+                    "kernel": KERNELS[kind][dom], "flops_per_launch": int(ph_flops[dom]),
+                    "avg_launch_us": round(ph_ms[dom] * 1e3, 2)}
+    else:
+        achieved = ph_bytes[dom] / (ph_ms[dom] * 1e-3) / 1e9
+        roofline = {"bound": "hbm", "achieved": round(achieved, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
+                    "frac": round(achieved / PEAK_HBM_GBS, 4),
+                    "traffic": MEASURED_TRAFFIC.get(KERNELS[kind][dom]),
+                    "kernel": KERNELS[kind][dom], "bytes_per_launch": int(ph_bytes[dom]),
+                    "avg_launch_us": round(ph_ms[dom] * 1e3, 2)}
     tok_s = T / (ms * 1e-3)
     layer_gbs = step_bytes / (ms * 1e-3) / 1e9
     result = {
@@ -198,7 +255,7 @@ def main():
         "config": {"workload": wl.name, "n_experts": shape.n_experts, "top_k": shape.top_k,
                    "n_shared": shape.n_shared, "d_model": shape.d_model, "d_ffn": shape.d_ffn,
                    "tokens": T, "weights": "mxfp4 (e2m1 + e8m0/32) routed, bf16 shared",
-                   "path": {1: "gemv", 2: "mfma"}[path], "token_pool": npool,
+                   "path": kind, "token_pool": npool,
                    "launch": "hip graph replay" if graph_ms is not None else "eager"},
         "ms_per_step_eager": round(eager_ms, 5),
         "layer_hbm_gbs": round(layer_gbs, 1), "layer_hbm_frac": round(layer_gbs / PEAK_HBM_GBS, 4),
