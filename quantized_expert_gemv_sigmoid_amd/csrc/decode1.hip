@@ -50,9 +50,7 @@ constexpr int kGuWin = 4;               // 128-wide K windows per gate/up work i
 constexpr int kGuMaxBlockUnits = 32;    // gate/up units of one block (partial sums staged in LDS)
 constexpr int kGuMaxStages = 8;         // K slices per unit (d <= 4096)
 constexpr int kMaxD = 4096;             // token width of the one-token path
-constexpr int kXPad = kMaxD + kGuWin * 128;  // token length padded to whole gate/up stages
-constexpr int kX8Lo = kXPad + 256 + 128;     // LDS offset of the residual part (other banks)
-constexpr int kXsLo = kXPad / 32;            // offset of the residual's scales
+constexpr int kXPad = kMaxD + kGuWin * 128;  // token length padded to whole gate/up items
 constexpr int kShRows = 2;              // shared down rows per unit
 constexpr int kShMaxBlockUnits = 512;   // shared down units of one block (outputs staged in LDS)
 constexpr int kShMaxChunks = 8;         // 16-byte chunks per lane of a shared down row (F <= 4096)
@@ -297,82 +295,6 @@ __device__ __forceinline__ int grab(uint32_t lds_addr)
     return __builtin_amdgcn_readfirstlane(v) >> 6;
 }
 
-typedef int i32x8_t __attribute__((ext_vector_type(8)));
-
-// fp32 -> OCP fp8 e4m3 code, rounded to nearest even (|v| < 448)
-__device__ __forceinline__ uint32_t e4m3_rne(float v)
-{
-    const uint32_t sgn = (__float_as_uint(v) >> 24) & 0x80u;
-    const float a = fabsf(v);
-    // below 2^-6: steps of 2^-9 (8 is the smallest normal, field 0x08)
-    const uint32_t fs = (uint32_t)__builtin_rintf(a * 512.0f);
-    const uint32_t ab = __float_as_uint(a);
-    const uint32_t m = ab & 0x7FFFFFu;
-    const uint32_t r = (m + 0x7FFFFu + ((m >> 20) & 1u)) >> 20;  // 3 mantissa bits (8: carry)
-    const uint32_t fn = (((ab >> 23) - 120u) << 3) + r;        // exponent field e - 127 + 7
-    return sgn | (a < 0.015625f ? fs : fn);
-}
-__device__ __forceinline__ float e4m3_val(uint32_t c)
-{
-    const uint32_t e = (c >> 3) & 15u, m = c & 7u;
-    const float v = e ? ldexpf((float)(8u + m), (int)e - 10) : ldexpf((float)m, -9);
-    return (c & 0x80u) ? -v : v;
-}
-// E8M0 exponent for a 32-block whose largest magnitude is mx: the values
-// divided by 2^s stay below 2^8 (e4m3 holds up to 448)
-__device__ __forceinline__ int block_exp(float mx)
-{
-    const int e = (int)((__float_as_uint(mx) >> 23) & 255u) - 127;
-    return mx > 0.0f ? max(e - 7, -127) : 0;
-}
-
-// The token as B operand of the fp4 x fp8 matrix-core products: each
-// 32-block of x split into a high part h = e4m3(x / 2^sh) and the residual
-// l = e4m3((x - h 2^sh) / 2^sl), x = h 2^sh + l 2^sl up to the residual's
-// rounding (x is bf16: the residual of its 8 significant bits keeps at most
-// 4, which e4m3 holds, unless it falls below the block's subnormal range).
-// Thread t converts elements [8t, 8t + 8) (v: 8 bf16); the four threads of
-// a block are one DPP quad.
-__device__ __forceinline__ void split_token8(uint4 v, int t, uint8_t *hi, uint8_t *lo, uint8_t *shi, uint8_t *slo)
-{
-    const uint32_t w[4] = {v.x, v.y, v.z, v.w};
-    float f[8];
-#pragma unroll
-    for (int i = 0; i < 4; i++) {
-        f[2 * i] = __uint_as_float(w[i] << 16);
-        f[2 * i + 1] = __uint_as_float(w[i] & 0xFFFF0000u);
-    }
-    float mx = 0.0f;
-#pragma unroll
-    for (int i = 0; i < 8; i++) mx = fmaxf(mx, fabsf(f[i]));
-    mx = fmaxf(mx, dppf<0xB1>(mx));  // quad_perm [1,0,3,2]
-    mx = fmaxf(mx, dppf<0x4E>(mx));  // quad_perm [2,3,0,1]
-    const int sh = block_exp(mx);
-    uint32_t ch[8];
-    float r[8], mr = 0.0f;
-#pragma unroll
-    for (int i = 0; i < 8; i++) {
-        ch[i] = e4m3_rne(ldexpf(f[i], -sh));
-        r[i] = f[i] - ldexpf(e4m3_val(ch[i]), sh);
-        mr = fmaxf(mr, fabsf(r[i]));
-    }
-    mr = fmaxf(mr, dppf<0xB1>(mr));
-    mr = fmaxf(mr, dppf<0x4E>(mr));
-    const int sl = block_exp(mr);
-    uint32_t ph[2] = {0, 0}, pl[2] = {0, 0};
-#pragma unroll
-    for (int i = 0; i < 8; i++) {
-        ph[i >> 2] |= ch[i] << (8 * (i & 3));
-        pl[i >> 2] |= e4m3_rne(ldexpf(r[i], -sl)) << (8 * (i & 3));
-    }
-    *reinterpret_cast<uint2 *>(hi + 8 * t) = make_uint2(ph[0], ph[1]);
-    *reinterpret_cast<uint2 *>(lo + 8 * t) = make_uint2(pl[0], pl[1]);
-    if ((t & 3) == 0) {
-        shi[t >> 2] = (uint8_t)(sh + 127);
-        slo[t >> 2] = (uint8_t)(sl + 127);
-    }
-}
-
 // One block of 8 waves per CU.  Waves 0-3 pick the experts (top-k) while
 // waves 4-7 stream the shared experts' down rows (a work queue of their
 // own); then every wave takes routed gate/up units from the block's queue.
@@ -392,11 +314,8 @@ __global__ __launch_bounds__(kGuWaves * 64) void k_dec1_gateup(Dec1Params p)
     // load in flight: stores and loads share one counter)
     // per unit and K slice: the 16 gate and 16 up partial sums
     __shared__ __attribute__((aligned(16))) float s_part[kGuMaxBlockUnits][kGuMaxStages][2 * kGuFeat];
-    // the token as two scaled fp8 (e4m3) parts, zero-padded to whole
-    // stages: high part at 0, residual at kX8Lo; their E8M0 scales per
-    // 32-block in s_xs (high, then residual at kXsLo)
-    __shared__ __attribute__((aligned(16))) uint8_t s_x8[kX8Lo + kXPad];
-    __shared__ uint8_t s_xs[2 * kXsLo];
+    // the token (bf16), zero-padded to whole work items
+    __shared__ __attribute__((aligned(16))) uint16_t s_xb[kXPad];
     __shared__ __attribute__((aligned(8))) float s_ysh[kShMaxBlockUnits][kShRows];
     // [0], [1]: work queues (routed, shared); [2]: keying waves whose
     // candidates are written; [3]: picks ready; [4]: keying waves whose
@@ -566,15 +485,15 @@ __global__ __launch_bounds__(kGuWaves * 64) void k_dec1_gateup(Dec1Params p)
         }
         __builtin_amdgcn_s_setprio(0);
     } else {
-        // ---- staging: the shared activations to LDS (unconditional: past
-        // S * F the loads returned 0), the token split into its two fp8
-        // parts; then all four staging waves are waited for
+        // ---- staging: the shared activations and the token to LDS
+        // (unconditional: past S * F and d the loads returned 0); then all
+        // four staging waves are waited for
 #pragma unroll
         for (int i = 0; i < kHsRounds; i++) reinterpret_cast<uint4 *>(s_hs)[st + i * kStThreads] = hsv[i];
 #pragma unroll
         for (int i = 0; i < kXRounds; i++) {
-            const int t = st + i * kStThreads;  // elements [8t, 8t + 8); quads share a 32-block
-            if (8 * t < kXPad) split_token8(xv[i], t, s_x8, s_x8 + kX8Lo, s_xs, s_xs + kXsLo);
+            const int t = st + i * kStThreads;  // elements [8t, 8t + 8)
+            if (8 * t < kXPad) *reinterpret_cast<uint4 *>(s_xb + 8 * t) = xv[i];
         }
         flag_add(&s_ctl[5]);
         spin_until(&s_ctl[5], kGuWaves - kTkWaves);
@@ -601,22 +520,19 @@ __global__ __launch_bounds__(kGuWaves * 64) void k_dec1_gateup(Dec1Params p)
     spin_until(&s_ctl[3], 1);
     spin_until(&s_ctl[5], kGuWaves - kTkWaves);
 
-    // ---- routed gate/up units on the matrix cores.  Unit u = j * F / 16 +
-    // fb covers features [16 fb, 16 fb + 16) of pick j.  Per 128-wide K
-    // window, one v_mfma_scale_f32_16x16x128_f8f6f4 per matrix multiplies
-    // the MXFP4 rows as they are stored (A: lane l holds row l % 16, MX block
-    // 4w + l / 16 -- one 16-byte load, the four lanes of a row reading 64
-    // contiguous bytes -- with its E8M0 scale) by the token split into two
-    // scaled fp8 parts (B: column 0 the high part, column 1 the residual; the
-    // other columns repeat column 0).  The matrix core applies both scales
-    // and sums exact products in fp32, so no weight is ever converted.  The
-    // work items are (unit, K slice of kGuWin windows), nloc * NS of them per
-    // block, taken from its queue (small items: a wave that the memory
-    // system serves late holds little when the queue runs dry); two items
-    // in flight per wave.  Rows end as D[row][0] + D[row][1]: lane 16 g'
-    // holds features [4 g', 4 g' + 4) in registers 0-3 and stores them as
-    // the item's partial sums; after the block's last item the slices are
-    // summed in order and the activations written to H[16 u, 16 u + 16).
+    // ---- routed gate/up units.  Unit u = j * F / 16 + fb covers features
+    // [16 fb, 16 fb + 16) of pick j: their W1 and W3 rows times x.  Lane l
+    // holds row l / 4 and, per 128-wide K window w, MX block 4w + l % 4 of it
+    // (one 16-byte load: the four lanes of a row read 64 contiguous bytes,
+    // 16 rows per load), decodes it to bf16 with its E8M0 scale folded in
+    // (v_cvt_scalef32_pk_bf16_fp4, exact) and dots it with the same 32 values
+    // of x read from LDS (v_dot2_f32_bf16, fp32 accumulate).  The work items
+    // are (unit, K slice of kGuWin windows), nloc * NS of them per block,
+    // taken from its queue (small items: a wave that the memory system
+    // serves late holds little when the queue runs dry); two items in flight
+    // per wave.  An item's row sums (the four lanes of a row added by DPP)
+    // are staged in LDS; after the block's last item the slices are summed
+    // in order and the activations written to H[16 u, 16 u + 16).
     const uint32_t qrow = (uint32_t)d / 2, srow = (uint32_t)d / 32;
     const int upr = F / kGuFeat;  // units per pick
     const int units = k * upr;
@@ -625,14 +541,11 @@ __global__ __launch_bounds__(kGuWaves * 64) void k_dec1_gateup(Dec1Params p)
     const int nloc = units > (int)blockIdx.x ? (units - 1 - (int)blockIdx.x) / (int)gridDim.x + 1 : 0;
     const int nblk_row = d / 32;                    // MX blocks per row
     const int nwin = (d + 127) / 128;               // 128-wide K windows
-    const int NS = (nwin + kGuWin - 1) / kGuWin;    // stages per unit
-    const int mrow = lane & 15, grp = lane >> 4;
+    const int NS = (nwin + kGuWin - 1) / kGuWin;    // K slices per unit
+    const int mrow = lane >> 2, grp = lane & 3;
     const uint32_t vo_w = (uint32_t)mrow * qrow + 16u * grp;  // + 64 w (window) + row offset
     const uint32_t vo_s = (uint32_t)mrow * srow + grp;        // + 4 w
     const uint32_t vo_s16 = (uint32_t)mrow * srow;            // the row's 16 bytes of the item
-    // B operand bytes of this lane: the residual for column 1, else the high part
-    const uint8_t *xb8 = s_x8 + (mrow == 1 ? kX8Lo : 0);
-    const uint8_t *xs8 = s_xs + (mrow == 1 ? kXsLo : 0);
     // lane j holds pick j; a unit's expert comes out through readlane (a
     // scalar), so the loads need no vector temporary and no LDS read
     const int my_e = lane < k ? s_eid[lane] : -1;
@@ -670,46 +583,39 @@ __global__ __launch_bounds__(kGuWaves * 64) void k_dec1_gateup(Dec1Params p)
         // (all of them issued before the arithmetic that follows)
         __builtin_amdgcn_sched_barrier(0);
     };
-    f32x4_t acc[2][2];  // [gate, up][even, odd window]
-    // multiply item `item` (valid) held in g, store its partial sums
+    // multiply item `item` (valid) held in g, store its row sums
     auto compute = [&](const GuStage<SA> &g, int item) __attribute__((always_inline)) {
         const int v = item / NS, st = item - v * NS;
-#pragma unroll
-        for (int m = 0; m < 2; m++)
-#pragma unroll
-            for (int h = 0; h < 2; h++) acc[m][h] = f32x4_t{0.0f, 0.0f, 0.0f, 0.0f};
+        float acc[2] = {0.0f, 0.0f};  // gate, up
 #pragma unroll
         for (int w = 0; w < kGuWin; w++) {
             const int wg = st * kGuWin + w;
-            // B: this lane's 32 codes (k = 128 wg + 16 grp + [0, 16) and
-            // 128 wg + 64 + 16 grp + [0, 16)) and the scale of block 4 wg + grp
-            const uint4 b0 = *reinterpret_cast<const uint4 *>(xb8 + wg * 128 + grp * 16);
-            const uint4 b1 = *reinterpret_cast<const uint4 *>(xb8 + wg * 128 + 64 + grp * 16);
-            const i32x8_t bv = {(int)b0.x, (int)b0.y, (int)b0.z, (int)b0.w, (int)b1.x, (int)b1.y, (int)b1.z, (int)b1.w};
-            const int bs = xs8[4 * wg + grp];
-            // A scales: a 255 byte (no value) or a block past the row counts as
-            // nothing (the smallest scale; the token is 0 past the row)
+            // x at k = 128 wg + 32 grp + [0, 32): 16 packed dwords
+            const uint4 *xp = reinterpret_cast<const uint4 *>(s_xb + wg * 128 + grp * 32);
+            uint32_t xw[16];
+#pragma unroll
+            for (int i = 0; i < 4; i++) {
+                const uint4 t = xp[i];
+                xw[4 * i + 0] = t.x; xw[4 * i + 1] = t.y; xw[4 * i + 2] = t.z; xw[4 * i + 3] = t.w;
+            }
+            // a 255 scale byte (no value) or a block past the row adds nothing
             const bool okb = 4 * wg + grp < nblk_row;
 #pragma unroll
             for (int m = 0; m < 2; m++) {
                 const uint32_t sb = g.scale(m, w, grp);
-                const int as = (okb && sb != 255u) ? (int)sb : 0;
-                const uint4 q = g.c[m][w];
-                const i32x8_t av = {(int)q.x, (int)q.y, (int)q.z, (int)q.w, 0, 0, 0, 0};
-                acc[m][w & 1] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(av, bv, acc[m][w & 1], 4, 0, 0, as, 0, bs);
+                const float sc = (okb && sb != 255u) ? e8m0_to_f32(sb) : 0.0f;
+                acc[m] = fmaf(fp4x32_dot_bf16(g.c[m][w], xw), sc, acc[m]);
             }
         }
-        f32x4_t y[2];
+        // the four lanes of a row
 #pragma unroll
         for (int m = 0; m < 2; m++) {
-            y[m] = acc[m][0] + acc[m][1];
-            // + column 1 (the residual part): lane 16 g' + 1 -> lane 16 g'
-#pragma unroll
-            for (int i = 0; i < 4; i++) y[m][i] += dppf<0xB1>(y[m][i]);  // quad_perm [1,0,3,2]
+            acc[m] += dppf<0xB1>(acc[m]);  // quad_perm [1,0,3,2]
+            acc[m] += dppf<0x4E>(acc[m]);  // quad_perm [2,3,0,1]
         }
-        if (mrow == 0) {
-            *reinterpret_cast<f32x4_t *>(&s_part[v][st][4 * grp]) = y[0];
-            *reinterpret_cast<f32x4_t *>(&s_part[v][st][kGuFeat + 4 * grp]) = y[1];
+        if (grp == 0) {
+            s_part[v][st][mrow] = acc[0];
+            s_part[v][st][kGuFeat + mrow] = acc[1];
         }
     };
 
