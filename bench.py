@@ -3,13 +3,14 @@
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload N]
 
-One step is one pass of the whole layer (router, dispatch, expert gate/up +
-activation, expert down, shared experts, combine) over one batch of tokens,
-with weights and tokens already resident in HBM.  Default workload: the
-Kimi-K3-shaped layer at decode T=1 (E=896 routed experts in MXFP4, top-16,
-2 bf16 shared experts, d=3584, F=3072).  Steps cycle through a pool of 32
-distinct token batches so consecutive steps pick different experts (no
-cache reuse of one fixed selection).
+One step is one pass of the whole layer (router, top-k, expert gate/up +
+activation, expert down, shared experts, weighted combine) over one batch of
+tokens, with weights and tokens already resident in HBM.  Default workload:
+the Kimi-K3-shaped layer at decode T=1 (E=896 routed experts in MXFP4,
+top-16, 2 bf16 shared experts, d=3584, F=3072).  Steps cycle through a pool
+of 32 distinct token batches so consecutive steps pick different experts (no
+cache reuse of one fixed selection).  Workload 4 stacks 12 such layers (own
+weights, own tokens, one Zipf selection bias) in one HIP graph per step.
 
 Prints one JSON line: throughput (tok/s), the roofline of the dominant kernel
 (algorithmic bytes / its average duration, timed live with the HIP events of
@@ -93,22 +94,28 @@ def flops(shape, T):
     return sum(phase_flops(shape, T).values())
 
 
-def cpu_baseline(shape, seed, layer, zipf, pool, budget_s):
+def cpu_baseline(shape, seed, zipf, pools, budget_s):
     """The oracle, as it is, on a bounded sample of the workload's tokens:
-    routing plus the expert mixture per token (expert generation untimed)."""
+    routing plus the expert mixture per token and layer (expert generation
+    untimed).  With L stacked layers the sample takes layer (n mod L) for its
+    n-th token, and the rate is tokens through all L layers per second."""
     import oracle
     import synth
-    rw = synth.router_weight(shape, seed, layer)
-    bias = synth.zipf_bias(shape, seed) if zipf else None
-    sh = synth.shared_weights(shape, seed, layer)
-    toks = pool.reshape(-1, shape.d_model)
+    L = len(pools)
+    per_layer = []
+    for l in range(L):
+        bias = synth.zipf_bias(shape, seed) if zipf else None
+        per_layer.append((synth.router_weight(shape, seed, l), bias, synth.shared_weights(shape, seed, l)))
+    toks = [p.reshape(-1, shape.d_model) for p in pools]
     done, spent = 0, 0.0
-    for t in range(toks.shape[0]):
-        x = toks[t:t + 1]
+    for n in range(toks[0].shape[0] * L):
+        l, t = n % L, n // L
+        rw, bias, sh = per_layer[l]
+        x = toks[l][t:t + 1]
         t0 = time.perf_counter()
         ids, w, _ = oracle.route(x, rw, bias, shape.top_k)
         spent += time.perf_counter() - t0
-        held = synth.host_layer(shape, seed, layer, zipf=zipf, experts=np.unique(ids))
+        held = synth.host_layer(shape, seed, l, zipf=zipf, experts=np.unique(ids))
         pos = {int(e): i for i, e in enumerate(held.experts)}
         slot = np.array([[pos[int(e)] for e in ids[0]]], dtype=np.int32)
         t0 = time.perf_counter()
@@ -117,8 +124,9 @@ def cpu_baseline(shape, seed, layer, zipf, pool, budget_s):
         done += 1
         if spent >= budget_s:
             break
-    return {"value": done / spent, "unit": "tok/s", "cores": oracle.threads(), "kind": "oracle",
-            "sample": f"{done} tokens of the workload, one at a time (router over all "
+    stack = f" over {L} stacked layers (token n on layer n mod {L})" if L > 1 else ""
+    return {"value": done / spent / L, "unit": "tok/s", "cores": oracle.threads(), "kind": "oracle",
+            "sample": f"{done} token-layer passes of the workload, one at a time{stack} (router over all "
                       f"{shape.n_experts} experts + {shape.top_k} routed + {shape.n_shared} "
                       f"shared expert FFNs each), {spent:.1f} s of oracle time"}
 
@@ -128,7 +136,9 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=200)
     ap.add_argument("--warmup", type=int, default=20)
-    ap.add_argument("--workload", type=int, default=1, help="index into synth.WORKLOADS (1..3)")
+    ap.add_argument("--workload", type=int, default=1,
+                    help="index into synth.WORKLOADS (1: decode T=1, 2: T=64, 3: prefill T=4096, "
+                         "4: 12 stacked layers with the Zipf selection bias, T=1)")
     ap.add_argument("--pool", type=int, default=32, help="distinct token batches cycled over")
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
@@ -157,48 +167,57 @@ def main():
     import quantized_expert_gemv_sigmoid_amd as moe
 
     wl = synth.WORKLOADS[args.workload]
-    if wl.layers != 1:
-        print("bench.py: the stacked workload is timed with --workload 1..3 per layer", file=sys.stderr)
-        sys.exit(2)
-    shape, T = wl.shape, wl.tokens
+    shape, T, L = wl.shape, wl.tokens, wl.layers
+    d = shape.d_model
     torch.cuda.set_device(0)
-    log(f"bench: {wl.name}: uploading {shape.n_experts} experts "
-        f"({shape.n_experts * shape.expert_bytes / 1e9:.2f} GB MXFP4)")
-    t = sdev.upload_layer(shape, wl.seed, 0, zipf=wl.zipf_bias)
-    desc = moe.make_desc(shape.n_experts, shape.top_k, shape.d_model, shape.d_ffn, shape.n_shared, t)
+    # L independent layers (own weights, own tokens), run one after another
+    # on one stream; the stacked workload shares one selection bias
+    tensors, descs = [], []
+    for l in range(L):
+        log(f"bench: {wl.name}: layer {l}: uploading {shape.n_experts} experts "
+            f"({shape.n_experts * shape.expert_bytes / 1e9:.2f} GB MXFP4)")
+        t = sdev.upload_layer(shape, wl.seed, l, zipf=wl.zipf_bias)
+        tensors.append(t)
+        descs.append(moe.make_desc(shape.n_experts, shape.top_k, d, shape.d_ffn, shape.n_shared, t))
     npool = max(1, min(args.pool, (1 << 16) // T))
-    pool = synth.x_tokens(shape, wl.seed, 0, npool * T).reshape(npool, T, shape.d_model)
-    xs = sdev.tokens_to_device(pool.reshape(npool * T, shape.d_model)).view(npool, T, shape.d_model)
-    ws = torch.empty(moe.workspace_bytes(desc, T), dtype=torch.uint8, device="cuda")
-    out = torch.empty((T, shape.d_model), dtype=torch.int16, device="cuda")
+    pools = [synth.x_tokens(shape, wl.seed, l, npool * T).reshape(npool, T, d) for l in range(L)]
+    xs = [sdev.tokens_to_device(pools[l].reshape(npool * T, d)).view(npool, T, d) for l in range(L)]
+    ws = torch.empty(moe.workspace_bytes(descs[0], T), dtype=torch.uint8, device="cuda")
+    outs = [torch.empty((T, d), dtype=torch.int16, device="cuda") for _ in range(L)]
     ids = torch.empty((T, shape.top_k), dtype=torch.int32, device="cuda")
     wts = torch.empty((T, shape.top_k), dtype=torch.float32, device="cuda")
     cnt = torch.empty(shape.n_experts, dtype=torch.int32, device="cuda")
-    counts = []
-    for i in range(npool):
-        moe.route(desc, xs[i], T, ids, wts, cnt, ws)
-        torch.cuda.synchronize()
-        counts.append(cnt.cpu().numpy().copy())
-    path = moe.path_for(desc, T)
+    counts = [[None] * npool for _ in range(L)]  # [layer][batch]
+    for l in range(L):
+        for i in range(npool):
+            moe.route(descs[l], xs[l][i], T, ids, wts, cnt, ws)
+            torch.cuda.synchronize()
+            counts[l][i] = cnt.cpu().numpy().copy()
+    path = moe.path_for(descs[0], T)
     # (the fused one-token kernels serve T = 1 on the GEMV path)
     kind = "decode1" if (path == 1 and T == 1) else {1: "gemv", 2: "mfma"}[path]
 
+    def step(i):
+        for l in range(L):
+            moe.layer(descs[l], xs[l][i % npool], T, outs[l], None, moe.OUT_BF16, ws)
+
     stream = torch.cuda.current_stream()
     for i in range(args.warmup):
-        moe.layer(desc, xs[i % npool], T, out, None, moe.OUT_BF16, ws)
+        step(i)
     torch.cuda.synchronize()
 
     K = args.steps
     start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     graph_ms = None
     if not args.no_graph:
-        # one HIP graph per token batch of the pool (the batch's address is
-        # baked into its graph, as a decode loop's fixed input buffer would be)
+        # one HIP graph per token batch of the pool, holding all L layers (the
+        # batch's addresses are baked into its graph, as a decode loop's fixed
+        # input buffers would be)
         graphs = []
         for i in range(npool):
             g = torch.cuda.CUDAGraph()
             with torch.cuda.graph(g):
-                moe.layer(desc, xs[i], T, out, None, moe.OUT_BF16, ws)
+                step(i)
             graphs.append(g)
         for i in range(args.warmup):
             graphs[i % npool].replay()
@@ -210,25 +229,31 @@ def main():
         torch.cuda.synchronize()
         graph_ms = start.elapsed_time(end) / K
 
-    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(moe.TIMED_EVENTS)] for _ in range(K)]
+    # per-phase durations: every layer of every step with its own events
+    evs = [[[torch.cuda.Event(enable_timing=True) for _ in range(moe.TIMED_EVENTS)] for _ in range(L)]
+           for _ in range(K)]
     for row in evs:  # torch creates an event's HIP handle at its first record
-        for e in row:
-            e.record(stream)
+        for lay in row:
+            for e in lay:
+                e.record(stream)
     torch.cuda.synchronize()
     start.record(stream)
     for i in range(K):
-        moe.layer_timed(desc, xs[i % npool], T, out, None, moe.OUT_BF16, ws, evs[i], stream=stream)
+        for l in range(L):
+            moe.layer_timed(descs[l], xs[l][i % npool], T, outs[l], None, moe.OUT_BF16, ws, evs[i][l],
+                            stream=stream)
     end.record(stream)
     torch.cuda.synchronize()
     eager_ms = start.elapsed_time(end) / K
     ms = graph_ms if graph_ms is not None else eager_ms
 
-    ph_ms = {p: float(np.mean([evs[i][j].elapsed_time(evs[i][j + 1]) for i in range(K)]))
+    ph_ms = {p: float(np.mean([evs[i][l][j].elapsed_time(evs[i][l][j + 1]) for i in range(K) for l in range(L)]))
              for j, p in enumerate(PHASES)}
-    ph_bytes = {p: float(np.mean([phase_bytes(shape, T, counts[i % npool], kind)[p] for i in range(K)]))
+    ph_bytes = {p: float(np.mean([phase_bytes(shape, T, counts[l][i % npool], kind)[p]
+                                  for i in range(K) for l in range(L)]))
                 for p in PHASES}
     ph_flops = phase_flops(shape, T)
-    step_bytes = sum(ph_bytes.values())
+    step_bytes = L * sum(ph_bytes.values())  # per step, all layers
     dom = max(("expert_gate_up", "expert_down"), key=lambda p: ph_ms[p])
     if kind == "mfma":
         # a dense contraction on the matrix cores (bf16 after the in-register
@@ -247,25 +272,27 @@ def main():
                     "avg_launch_us": round(ph_ms[dom] * 1e3, 2)}
     tok_s = T / (ms * 1e-3)
     layer_gbs = step_bytes / (ms * 1e-3) / 1e9
+    config = {"workload": wl.name, "n_experts": shape.n_experts, "top_k": shape.top_k,
+              "n_shared": shape.n_shared, "d_model": d, "d_ffn": shape.d_ffn,
+              "tokens": T, "layers": L, "selection_bias": "zipf" if wl.zipf_bias else "none",
+              "weights": "mxfp4 (e2m1 + e8m0/32) routed, bf16 shared",
+              "path": kind, "token_pool": npool,
+              "launch": "hip graph replay" if graph_ms is not None else "eager"}
     result = {
         "metric": METRIC, "value": round(tok_s, 2), "unit": "tok/s", "n_gpus": 1, "steps": K,
         "warmup": args.warmup, "ms_per_step": round(ms, 5), "higher_is_better": True,
         "scaling": "weak", "vs_baseline": None, "dtype": "fp32",
         "data": "synthetic",
-        "config": {"workload": wl.name, "n_experts": shape.n_experts, "top_k": shape.top_k,
-                   "n_shared": shape.n_shared, "d_model": shape.d_model, "d_ffn": shape.d_ffn,
-                   "tokens": T, "weights": "mxfp4 (e2m1 + e8m0/32) routed, bf16 shared",
-                   "path": kind, "token_pool": npool,
-                   "launch": "hip graph replay" if graph_ms is not None else "eager"},
+        "config": config,
         "ms_per_step_eager": round(eager_ms, 5),
-        "layer_hbm_gbs": round(layer_gbs, 1), "layer_hbm_frac": round(layer_gbs / PEAK_HBM_GBS, 4),
-        "layer_tflops": round(flops(shape, T) / (ms * 1e-3) / 1e12, 3),
+        "step_hbm_gbs": round(layer_gbs, 1), "step_hbm_frac": round(layer_gbs / PEAK_HBM_GBS, 4),
+        "step_tflops": round(L * flops(shape, T) / (ms * 1e-3) / 1e12, 3),
         "phase_us": {p: round(v * 1e3, 2) for p, v in ph_ms.items()},
         "roofline": roofline,
     }
     if not args.no_cpu_baseline:
         log("bench: timing the CPU oracle on a bounded sample")
-        result["cpu_baseline"] = cpu_baseline(shape, wl.seed, 0, wl.zipf_bias, pool,
+        result["cpu_baseline"] = cpu_baseline(shape, wl.seed, wl.zipf_bias, pools,
                                               args.cpu_seconds)
     print(json.dumps(result), flush=True)
 
