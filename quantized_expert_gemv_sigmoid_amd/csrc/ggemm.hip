@@ -457,34 +457,80 @@ __device__ __forceinline__ void gemm_pass(const GemmParams &p, const Blk &bk, co
     // ---- K loop, two A stages per trip (every K here is a multiple of
     // 2 * KCA).  A stage i sits in LDS stage i & 1 and was loaded into
     // registers two stages before it is stored (register sets ar0 / ar1), B
-    // stage j in LDS stage j & 1, loaded R stages ahead (fp4: one B stage per
-    // trip).  Loads past the end re-read the last stage (harmless) so every
-    // trip is identical.
+    // stage j in LDS stage j & 1.  Loads past the end re-read the last stage
+    // (harmless) so every trip is identical.
     uint4 ar0[NPASS], ar1[NPASS];
-    BRegs br;
-    load_a(ar0, 0);
-    load_b(br, 0);
-    store_a(ar0, 0);
-    store_b(br, 0);
-    load_a(ar1, min(1, nA - 1));
-    load_a(ar0, min(2, nA - 1));
-    load_b(br, min(1, nB - 1));
-    lds_barrier();
-    for (int i = 0; i < nA; i += 2) {
-        compute(0, (i / R) & 1, i % R);
-        store_a(ar1, 1);  // A stage i + 1
-        if constexpr (R == 1) store_b(br, 1);
-        lds_barrier();
-        load_a(ar1, min(i + 3, nA - 1));
-        if constexpr (R == 1) load_b(br, min(i + 2, nB - 1));
+    if constexpr (R == 2 && MT <= 3 && !SPLIT) {
+        if (nA % 4 == 0) {
+            // MXFP4 weights, an even number of trips: B stage t (one per
+            // trip) is loaded into one of two register sets two trips before
+            // it is stored, so about two trips' time covers its HBM latency
+            // (up to 96 rows: with 128 the registers would not hold it)
+            BRegs bra, brb;
+            load_a(ar0, 0);
+            load_b(bra, 0);
+            store_a(ar0, 0);
+            store_b(bra, 0);
+            load_a(ar1, min(1, nA - 1));
+            load_a(ar0, min(2, nA - 1));
+            load_b(bra, min(1, nB - 1));
+            load_b(brb, min(2, nB - 1));
+            lds_barrier();
+            for (int i = 0; i < nA; i += 4) {
+                const int t = i / 2;  // trips t (B stage t in LDS 0) and t + 1 (LDS 1)
+                compute(0, 0, 0);
+                store_a(ar1, 1);  // A stage i + 1
+                lds_barrier();
+                load_a(ar1, min(i + 3, nA - 1));
+                compute(1, 0, 1);
+                store_a(ar0, 0);  // A stage i + 2
+                store_b(bra, 1);  // B stage t + 1
+                lds_barrier();
+                load_a(ar0, min(i + 4, nA - 1));
+                load_b(bra, min(t + 3, nB - 1));
 
-        compute(1, ((i + 1) / R) & 1, (i + 1) % R);
-        store_a(ar0, 0);  // A stage i + 2
-        store_b(br, ((i + 1) / R + 1) & 1);
-        lds_barrier();
-        load_a(ar0, min(i + 4, nA - 1));
-        load_b(br, min((i + 1) / R + 2, nB - 1));
+                compute(0, 1, 0);
+                store_a(ar1, 1);  // A stage i + 3
+                lds_barrier();
+                load_a(ar1, min(i + 5, nA - 1));
+                compute(1, 1, 1);
+                store_a(ar0, 0);  // A stage i + 4
+                store_b(brb, 0);  // B stage t + 2
+                lds_barrier();
+                load_a(ar0, min(i + 6, nA - 1));
+                load_b(brb, min(t + 4, nB - 1));
+            }
+            goto epilogue;
+        }
     }
+    {
+        // B stage j loaded R stages ahead (fp4: one B stage per trip)
+        BRegs br;
+        load_a(ar0, 0);
+        load_b(br, 0);
+        store_a(ar0, 0);
+        store_b(br, 0);
+        load_a(ar1, min(1, nA - 1));
+        load_a(ar0, min(2, nA - 1));
+        load_b(br, min(1, nB - 1));
+        lds_barrier();
+        for (int i = 0; i < nA; i += 2) {
+            compute(0, (i / R) & 1, i % R);
+            store_a(ar1, 1);  // A stage i + 1
+            if constexpr (R == 1) store_b(br, 1);
+            lds_barrier();
+            load_a(ar1, min(i + 3, nA - 1));
+            if constexpr (R == 1) load_b(br, min(i + 2, nB - 1));
+
+            compute(1, ((i + 1) / R) & 1, (i + 1) % R);
+            store_a(ar0, 0);  // A stage i + 2
+            store_b(br, ((i + 1) / R + 1) & 1);
+            lds_barrier();
+            load_a(ar0, min(i + 4, nA - 1));
+            load_b(br, min((i + 1) / R + 2, nB - 1));
+        }
+    }
+epilogue:
 
     // ---- epilogue (D lane layout: register e of tile (mt, nb) holds row
     // mt * 32 + 8 (e / 4) + 4 kh + e % 4, column nb * 32 + col of the wave's 64)
