@@ -255,7 +255,11 @@ def main():
     ph_flops = phase_flops(shape, T)
     step_bytes = L * sum(ph_bytes.values())  # per step, all layers
     dom = max(("expert_gate_up", "expert_down"), key=lambda p: ph_ms[p])
-    if kind == "mfma":
+    # the bound of the dominant phase: its flops per algorithmic HBM byte
+    # against the machine balance (peak flops / peak bytes, 312 F/B); half of
+    # it or more counts as matrix-core bound
+    intensity = ph_flops[dom] / max(ph_bytes[dom], 1.0)
+    if kind == "mfma" and intensity >= 0.5 * PEAK_BF16_TFLOPS * 1e12 / (PEAK_HBM_GBS * 1e9):
         # a dense contraction on the matrix cores (bf16 after the in-register
         # MXFP4 decode): against the bf16 MFMA peak
         achieved = ph_flops[dom] / (ph_ms[dom] * 1e-3) / 1e12

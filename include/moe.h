@@ -51,8 +51,8 @@ typedef enum { MOE_ACT_SITU = 0, MOE_ACT_SWIGLU = 1 } moe_act;
 /* which outputs moe_expert_forward / moe_layer write */
 typedef enum { MOE_OUT_BF16 = 0, MOE_OUT_F32 = 1, MOE_OUT_BOTH = 2 } moe_out_mode;
 
-/* which expert kernels run: AUTO picks the dequant-fused GEMV for small token
- * counts and the grouped MFMA GEMM for large ones (moe_path_for reports it).
+/* which expert kernels run: AUTO picks the dequant-fused GEMV for up to 24
+ * tokens and the grouped MFMA GEMM above (moe_path_for reports it).
  * The MFMA path needs d and F to be multiples of 256 and every activation
  * operand below 2 GiB (T*k*F, T*d and T*S*F two-byte values); AUTO falls
  * back to GEMV outside that range, an explicit MOE_PATH_MFMA call returns

@@ -233,7 +233,7 @@ def test_graph_replay_matches_eager():
 MFMA_SHAPE = synth.LayerShape(n_experts=40, top_k=6, n_shared=2, d_model=512, d_ffn=768)
 
 
-@pytest.mark.parametrize("T", [1, 17, 130, 300, 700])
+@pytest.mark.parametrize("T", [1, 17, 130, 300, 700, 1100])
 def test_mfma_path_parity(T):
     import quantized_expert_gemv_sigmoid_amd as moe
     log(f"case: MFMA path E40 k6 S2 d512 F768 T={T}")
@@ -247,8 +247,8 @@ def test_mfma_auto_threshold_and_gemv_agree():
     h = synth.host_layer(MFMA_SHAPE, 62, 0)
     g_auto = make_gpu_layer(MFMA_SHAPE, 62, host=h)
     g_gemv = make_gpu_layer(MFMA_SHAPE, 62, host=h, path=moe.PATH_GEMV)
-    assert moe.path_for(g_auto.desc, 128) == moe.PATH_GEMV
-    assert moe.path_for(g_auto.desc, 129) == moe.PATH_MFMA
+    assert moe.path_for(g_auto.desc, 24) == moe.PATH_GEMV
+    assert moe.path_for(g_auto.desc, 25) == moe.PATH_MFMA
     T = 200
     x, rw, bias = tokens(g_auto, T)
     a = run_layer(g_auto, x)
