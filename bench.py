@@ -49,10 +49,10 @@ KERNELS = {
 
 # HBM bytes per dispatch measured by rocprofv3 (FETCH_SIZE and WRITE_SIZE,
 # each scaled by what the counter reads for a plain 256 MiB copy), for the
-# kernel as it stands; the summary and the commands are in
+# kernel as it stands, at decode T=1; the summary and the commands are in
 # profiles/moe_layer_kernels__k3-moe-decode-T1.md.  A kernel changed since
 # its counters were taken has no entry here (traffic: null).
-MEASURED_TRAFFIC = {}
+MEASURED_TRAFFIC = {"k_dec1_gateup": 232404177}
 
 
 def log(*a):
@@ -271,7 +271,7 @@ def main():
         achieved = ph_bytes[dom] / (ph_ms[dom] * 1e-3) / 1e9
         roofline = {"bound": "hbm", "achieved": round(achieved, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
                     "frac": round(achieved / PEAK_HBM_GBS, 4),
-                    "traffic": MEASURED_TRAFFIC.get(KERNELS[kind][dom]),
+                    "traffic": MEASURED_TRAFFIC.get(KERNELS[kind][dom]) if kind == "decode1" else None,
                     "kernel": KERNELS[kind][dom], "bytes_per_launch": int(ph_bytes[dom]),
                     "avg_launch_us": round(ph_ms[dom] * 1e3, 2)}
     tok_s = T / (ms * 1e-3)
