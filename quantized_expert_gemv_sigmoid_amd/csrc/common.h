@@ -39,6 +39,7 @@ struct Work {
     float *Y;          // [T*k][d] weighted expert outputs
     float *Ysh;        // [S][T][d] shared experts' outputs
     void *extra;       // MFMA path: router weights split into 3 bf16 parts [E][3d]
+    float *rpart;      // MFMA path: partial router logits of the K slices
 };
 
 struct Shape {
@@ -295,6 +296,8 @@ hipError_t launch_gemv_experts(const Shape &s, const uint16_t *x, const Weights 
 // the router weights, and the experts (shared + routed gate/up, then down)
 bool mfma_supported(const Shape &s);
 size_t mfma_extra_workspace(const Shape &s);
+size_t router_part_workspace(const Shape &s);
+constexpr int kRouterPartRows = 8192;  // rows of E partial logits (MFMA router K slices)
 hipError_t launch_mfma_router(const Shape &s, const uint16_t *x, const Weights &wt, const Work &w,
                               hipStream_t stream);
 hipError_t launch_mfma_experts(const Shape &s, const uint16_t *x, const Weights &wt,

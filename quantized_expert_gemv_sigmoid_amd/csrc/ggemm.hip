@@ -63,6 +63,8 @@ struct GemmParams {
     int groups;       // group count (upper bound for routed: max active experts)
     int n_tiles;      // column tiles per group
     int m_blocks;     // M passes spread over blocks (shared / router); 1 for routed
+    int ksplit;       // router: K slices over blocks (partial logits summed after)
+    float *rpart;     // router: partial logits [ksplit][T][E] (ksplit > 1)
 };
 
 // ---------------------------------------------------------------- helpers
@@ -155,8 +157,9 @@ __device__ __forceinline__ f32x16_t mfma32(f16x8_t a, f16x8_t b, f32x16_t c)
 // Per-block geometry: which group (expert / shared expert / router) and
 // which 256-column tile this block computes.
 struct Blk {
-    int group, tile, mb;
+    int group, tile, mb, ks;
     int M, base, e, K, nA, nB, ncols;
+    int kst0;  // first A stage of the block's K range
 };
 
 // Global sources of this thread's B staging copies: 16-byte piece (t % 8)
@@ -274,7 +277,7 @@ __device__ __forceinline__ void gemm_pass(const GemmParams &p, const Blk &bk, co
         arow[ps] = (e + qa * 8) * 2;
     }
     auto load_a = [&](uint4 (&ar)[NPASS], int i) __attribute__((always_inline)) {
-        const int k0 = i * KCA;
+        const int k0 = (i + bk.kst0) * KCA;
         const uint16_t *abase;
         int kk = k0;
         if constexpr (MODE == M_G13 || MODE == M_S13) {
@@ -307,7 +310,7 @@ __device__ __forceinline__ void gemm_pass(const GemmParams &p, const Blk &bk, co
         uint2 sc;
     };
     auto load_b = [&](BRegs &br, int j) __attribute__((always_inline)) {
-        const int k0 = j * C::KCB;
+        const int k0 = (j + bk.kst0 / R) * C::KCB;
         uint32_t koff;  // byte offset of the stage in a weight row
         if constexpr (C::kFp4) koff = k0 / 2;
         else if constexpr (MODE == M_S2) koff = (k0 % s.F) * 2;  // B repeats for the hi / lo halves
@@ -564,6 +567,7 @@ epilogue:
                     const float v = acc[mt][nb][e];
                     if constexpr (MODE == M_D2) p.w.Y[(size_t)(bk.base + m) * s.d + n] = v * wrow;
                     else if constexpr (MODE == M_S2) p.w.Ysh[((size_t)bk.group * s.T + m) * s.d + n] = v;
+                    else if (p.ksplit > 1) p.rpart[((size_t)bk.ks * s.T + m) * s.E + n] = v;
                     else p.w.logits[(size_t)m * s.E + n] = v;
                 }
             }
@@ -589,6 +593,11 @@ __global__ __launch_bounds__(GT) void k_ggemm(GemmParams p)
     int x = blockIdx.x;
     const int gt = p.groups * p.n_tiles;
     b.mb = 0;
+    b.ks = 0;
+    if constexpr (MODE == M_R) {
+        b.ks = x / (gt * p.m_blocks);
+        x = x % (gt * p.m_blocks);
+    }
     if (p.m_blocks > 1) {
         b.mb = x / gt;
         x = x % gt;
@@ -615,8 +624,10 @@ __global__ __launch_bounds__(GT) void k_ggemm(GemmParams p)
         b.M = s.T;
         b.K = MODE == M_S13 ? s.d : (MODE == M_S2 ? 2 * s.F : 3 * s.d);
     }
+    if constexpr (MODE == M_R) b.K /= p.ksplit;  // (a multiple of 2 * KCA, see the launch)
     b.nA = b.K / C::KCA;
     b.nB = b.K / C::KCB;
+    b.kst0 = b.ks * b.nA;
     b.ncols = C::kGated ? s.F : (MODE == M_R ? s.E : s.d);
     const BSrc<MODE> bsrc = make_bsrc<MODE>(p, b);
 
@@ -681,6 +692,17 @@ __global__ __launch_bounds__(256) void k_split_router(int E, int d, const float 
     row[2 * d + c] = lo;
 }
 
+// logits[t][e] = sum over the K slices, in slice order, of the partials
+__global__ __launch_bounds__(256) void k_router_reduce(int n, int ksplit, const float *__restrict__ rpart,
+                                                       float *__restrict__ logits)
+{
+    const int i = blockIdx.x * 256 + threadIdx.x;
+    if (i >= n) return;
+    float v = 0.0f;
+    for (int j = 0; j < ksplit; j++) v += rpart[(size_t)j * n + i];
+    logits[i] = v;
+}
+
 // ---------------------------------------------------------------- host
 
 bool mfma_supported(const Shape &s)
@@ -693,6 +715,30 @@ bool mfma_supported(const Shape &s)
            (size_t)s.T * s.d * 2 < lim && (size_t)s.T * s.S * s.F * 2 < lim;
 }
 
+// K slices of the router GEMM: its grid has only ceil(E / 256) * ceil(T /
+// 128) blocks, so small T splits K = 3d (in units of two 64-wide stages)
+// until about 256 blocks run, within kRouterPartRows rows of partials
+int router_ksplit(const Shape &s)
+{
+    if (s.d % 256 != 0 || s.F % 256 != 0) return 1;
+    const int nk = 3 * s.d / 128;
+    const int blocks = ((s.E + GN - 1) / GN) * ((s.T + GM - 1) / GM);
+    const int cap = min(min((256 + blocks - 1) / blocks, kRouterPartRows / max(s.T, 1)), nk);
+    int ks = 1;
+    for (int c = 1; c <= cap; c++)
+        if (nk % c == 0) ks = c;
+    return ks;
+}
+
+// partial router logits of the MFMA path: [ksplit][T][E], ksplit * T <=
+// min(T * 3d / 128, kRouterPartRows) (non-decreasing in T)
+size_t router_part_workspace(const Shape &s)
+{
+    if (s.d % 256 != 0 || s.F % 256 != 0) return 0;
+    const size_t rows = min((size_t)s.T * (3 * s.d / 128), (size_t)kRouterPartRows);
+    return rows * s.E * 4;
+}
+
 // extra workspace of the MFMA path: router weights split in 3 bf16 parts
 size_t mfma_extra_workspace(const Shape &s)
 {
@@ -701,14 +747,16 @@ size_t mfma_extra_workspace(const Shape &s)
 }
 
 template <int MODE>
-static void launch_mode(const GemmParams &p0, int groups, int n_tiles, int m_blocks, hipStream_t st)
+static void launch_mode(const GemmParams &p0, int groups, int n_tiles, int m_blocks, hipStream_t st,
+                        int ksplit = 1)
 {
     GemmParams p = p0;
     p.groups = groups;
     p.n_tiles = n_tiles;
     p.m_blocks = m_blocks;
+    p.ksplit = ksplit;
     const int padded = groups >= 8 ? (groups + 7) / 8 * 8 : groups;
-    const int nblk = padded * n_tiles * m_blocks;
+    const int nblk = padded * n_tiles * m_blocks * ksplit;
     if (nblk > 0) k_ggemm<MODE><<<nblk, GT, 0, st>>>(p);
 }
 
@@ -727,6 +775,8 @@ static GemmParams make_gemm_params(const Shape &s, const uint16_t *x, const Weig
     p.hs_hi_w = reinterpret_cast<uint16_t *>(w.Hs);
     p.hs_lo_w = p.hs_hi_w + (size_t)s.T * s.S * s.F;
     p.groups = p.n_tiles = p.m_blocks = 0;
+    p.ksplit = 1;
+    p.rpart = w.rpart;
     return p;
 }
 
@@ -737,7 +787,13 @@ hipError_t launch_mfma_router(const Shape &s, const uint16_t *x, const Weights &
     k_split_router<<<(unsigned)((n + 255) / 256), 256, 0, st>>>(s.E, s.d, wt.router_w,
                                                                reinterpret_cast<uint16_t *>(w.extra));
     GemmParams p = make_gemm_params(s, x, wt, w);
-    launch_mode<M_R>(p, 1, (s.E + GN - 1) / GN, (s.T + GM - 1) / GM, st);
+    const int nt = (s.E + GN - 1) / GN, mb = (s.T + GM - 1) / GM;
+    const int ks = router_ksplit(s);
+    launch_mode<M_R>(p, 1, nt, mb, st, ks);
+    if (ks > 1) {
+        const int n = s.T * s.E;
+        k_router_reduce<<<(n + 255) / 256, 256, 0, st>>>(n, ks, w.rpart, w.logits);
+    }
     return hipGetLastError();
 }
 

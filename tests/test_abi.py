@@ -130,7 +130,9 @@ def test_call_argument_checks(L):
 
 def test_workspace_monotone_and_paths(L):
     d = desc()
-    sizes = [L.moe_workspace_bytes(ctypes.byref(d), t) for t in (1, 2, 64, 65, 4096)]
+    # every T: one call sized for max_tokens serves any smaller T
+    ts = list(range(1, 300)) + [511, 512, 513, 1023, 1024, 1025, 2048, 4095, 4096, 4097, 8192]
+    sizes = [L.moe_workspace_bytes(ctypes.byref(d), t) for t in ts]
     assert all(a <= b for a, b in zip(sizes, sizes[1:]))
     assert sizes[0] % 256 == 0
     assert moe.path_for(d, 1) == moe.PATH_GEMV
