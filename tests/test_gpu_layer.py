@@ -159,6 +159,11 @@ def test_k3_decode_T1():
     w, gl = _k3(1)
     x, out_f, out_b, ids, wts, cnt = _full_check(gl, 1)
     assert cnt.sum() == 16 and (cnt <= 1).all()
+    # the one-token kernels take work from queues in whatever order the
+    # waves get to them; the result must not depend on it
+    for _ in range(3):
+        out_f2, out_b2, ids2, _, _ = run_layer(gl, x)
+        assert np.array_equal(out_f, out_f2) and np.array_equal(ids, ids2)
     del gl
 
 
@@ -167,6 +172,14 @@ def test_k3_decode_T1_zipf_bias():
     log(f"case: {w.name} layer 0 (one layer of the stack)")
     gl = make_gpu_layer(w.shape, w.seed, zipf=True)
     _full_check(gl, 4)
+    # the stack runs one token per call: the one-token path with the bias
+    x, rw, bias = tokens(gl, 4)
+    rids, rw_, gap, rout = oracle_outputs(gl, x, rw, bias, np.arange(4))
+    for t in range(4):
+        of, ob, it, wt, ct = run_layer(gl, x[t:t + 1])
+        check_routing(it, wt, ct, rids[t:t + 1], rw_[t:t + 1], w.shape.n_experts, f"token {t}")
+        assert_close(of, rout[t:t + 1], f"one-token call {t}")
+        assert np.array_equal(ob, bf16_rne(of))
     del gl
 
 
