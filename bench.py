@@ -37,8 +37,9 @@ PHASES = ("router_logits", "topk_dispatch", "expert_gate_up", "expert_down", "co
 # and combine folded into the expert kernels), the GEMV path (small T), the
 # MFMA path (grouped GEMM over expert-sorted tokens)
 KERNELS = {
-    "decode1": {"router_logits": "k_front (router + shared gate/up)", "topk_dispatch": "-",
-                "expert_gate_up": "k_dec1_gateup", "expert_down": "k_dec1_down", "combine": "-"},
+    "decode1": {"router_logits": "- (in k_dec1_gateup)", "topk_dispatch": "- (in k_dec1_gateup)",
+                "expert_gate_up": "k_dec1_gateup (router + top-k + shared and routed gate/up)",
+                "expert_down": "k_dec1_down (shared and routed down + combine)", "combine": "-"},
     "gemv": {"router_logits": "k_front", "topk_dispatch": "k_dispatch_small/k_topk+k_dispatch_*",
              "expert_gate_up": "k_gemv_gateup", "expert_down": "k_gemv_down", "combine": "k_combine"},
     "mfma": {"router_logits": "k_split_router + k_ggemm<M_R>", "topk_dispatch": "k_topk + k_dispatch_*",
@@ -52,7 +53,7 @@ KERNELS = {
 # kernel as it stands, at decode T=1; the summary and the commands are in
 # profiles/moe_layer_kernels__k3-moe-decode-T1.md.  A kernel changed since
 # its counters were taken has no entry here (traffic: null).
-MEASURED_TRAFFIC = {"k_dec1_gateup": 232404177}
+MEASURED_TRAFFIC = {}
 
 
 def log(*a):
@@ -62,17 +63,18 @@ def log(*a):
 def phase_bytes(shape, T, counts, kind):
     """Algorithmic HBM bytes of each phase for one step (every touched expert
     read once; shared, router, tokens and outputs once; workspace excluded).
-    On the fused one-token path the shared experts' gate/up runs in the front
-    kernel and their down in the gate/up kernel."""
+    On the fused one-token path the router and the shared experts' gate/up
+    run in the gate/up kernel and the shared experts' down in the down
+    kernel."""
     d, F, S, E, k = shape.d_model, shape.d_ffn, shape.n_shared, shape.n_experts, shape.top_k
     active = int((counts > 0).sum())
     w13 = 2 * (F * d // 2 + F * d // 32)
     w2 = d * F // 2 + d * F // 32
     sh13, sh2 = S * 2 * F * d * 2, S * d * F * 2
     if kind == "decode1":
-        return {"router_logits": E * d * 4 + sh13 + T * d * 2, "topk_dispatch": 0,
-                "expert_gate_up": active * w13 + sh2 + T * d * 2,
-                "expert_down": active * w2 + T * d * 2, "combine": 0}
+        return {"router_logits": 0, "topk_dispatch": 0,
+                "expert_gate_up": E * d * 4 + sh13 + active * w13 + T * d * 2,
+                "expert_down": active * w2 + sh2 + T * d * 2, "combine": 0}
     return {
         "router_logits": E * d * 4 + T * d * 2,
         "topk_dispatch": 0,
@@ -182,7 +184,7 @@ def main():
     npool = max(1, min(args.pool, (1 << 16) // T))
     pools = [synth.x_tokens(shape, wl.seed, l, npool * T).reshape(npool, T, d) for l in range(L)]
     xs = [sdev.tokens_to_device(pools[l].reshape(npool * T, d)).view(npool, T, d) for l in range(L)]
-    ws = torch.empty(moe.workspace_bytes(descs[0], T), dtype=torch.uint8, device="cuda")
+    ws = torch.zeros(moe.workspace_bytes(descs[0], T), dtype=torch.uint8, device="cuda")
     outs = [torch.empty((T, d), dtype=torch.int16, device="cuda") for _ in range(L)]
     ids = torch.empty((T, shape.top_k), dtype=torch.int32, device="cuda")
     wts = torch.empty((T, shape.top_k), dtype=torch.float32, device="cuda")
@@ -271,7 +273,7 @@ def main():
         achieved = ph_bytes[dom] / (ph_ms[dom] * 1e-3) / 1e9
         roofline = {"bound": "hbm", "achieved": round(achieved, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
                     "frac": round(achieved / PEAK_HBM_GBS, 4),
-                    "traffic": MEASURED_TRAFFIC.get(KERNELS[kind][dom]) if kind == "decode1" else None,
+                    "traffic": MEASURED_TRAFFIC.get(KERNELS[kind][dom].split()[0]) if kind == "decode1" else None,
                     "kernel": KERNELS[kind][dom], "bytes_per_launch": int(ph_bytes[dom]),
                     "avg_launch_us": round(ph_ms[dom] * 1e3, 2)}
     tok_s = T / (ms * 1e-3)

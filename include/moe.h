@@ -20,8 +20,8 @@
  *
  * Conventions (every call):
  *  - All pointers are DEVICE pointers owned by the caller; the library
- *    allocates nothing, keeps no state between calls and never synchronises
- *    the host.  Work is enqueued on `stream` (a hipStream_t; NULL = the null
+ *    allocates nothing, keeps no state of its own between calls and never
+ *    synchronises the host.  Work is enqueued on `stream` (a hipStream_t; NULL = the null
  *    stream) and may be captured into a HIP graph (no memset, no allocation).
  *  - Arguments are validated before anything is launched; on any error
  *    nothing is enqueued and a negative moe_status is returned.
@@ -91,8 +91,19 @@ typedef struct {
 
 /* Workspace bytes a call with up to max_tokens tokens needs (0 if the
  * descriptor is invalid or unsupported).  Pass a buffer of at least this
- * size, 256-byte aligned, to the calls below. */
+ * size, 256-byte aligned, to the calls below.
+ *
+ * The first MOE_WS_CONTROL_BYTES bytes of a workspace are a control block
+ * (the router logits that the blocks of the one-token path hand to each
+ * other, each with a ready tag) and must be ZERO before the first call that
+ * uses the workspace: a hipMemsetAsync of those bytes, or allocating the
+ * workspace zero-filled, does it.  Every call leaves them zero again, so
+ * zeroing once per workspace is enough.  A control block that was not
+ * zeroed is detected (a tag that no call writes); the call then writes NaN
+ * outputs, and so does every later call on that workspace until the block
+ * is zeroed again. */
 size_t moe_workspace_bytes(const moe_layer_desc *desc, int32_t max_tokens);
+#define MOE_WS_CONTROL_BYTES 9216
 
 /* The expert path (MOE_PATH_GEMV or MOE_PATH_MFMA) a call with T tokens
  * takes; a negative moe_status if desc is invalid. */

@@ -18,10 +18,12 @@ constexpr int kMaxExperts = 1024;  // router top-k keeps E/64 scores per lane
 constexpr int kMaxTopK = 64;
 constexpr int kMaxDim = 4096;      // d and F: GEMV lanes hold <= 2 MXFP4 blocks
 constexpr int kMaxShared = 8;
+constexpr size_t kWsControlBytes = 9 * 1024;  // workspace bytes [0, this): the control block
 constexpr int kDispatchTokens = 64;  // tokens per dispatch block (one 64-bit mask)
 
 // Device views of the workspace of one call (see carve_workspace).
 struct Work {
+    int32_t *ctl;      // control block of the one-token path (kWsControlBytes, zero between calls)
     float *logits;     // [T][E]  router logits
     int32_t *ids;      // [T][k]  routing (when the caller passed none)
     float *wts;        // [T][k]
@@ -34,7 +36,8 @@ struct Work {
     int32_t *pos_tok;  // [T*k]   token of the slot at each expert-grouped position
     float *pos_w;      // [T*k]   its routing weight
     int32_t *tok_pos;  // [T][k]  positions of a token's slots, ascending expert id
-    void *H;           // [T*k][F] gate/up activations (fp32 or fp16)
+    void *H;           // [T*k][F] gate/up activations (fp32 or fp16; one token: fp16, then the
+                       // shared activations [S*F] fp32)
     float *Hs;         // [T][S*F] shared activations (fp32)
     float *Y;          // [T*k][d] weighted expert outputs
     float *Ysh;        // [S][T][d] shared experts' outputs

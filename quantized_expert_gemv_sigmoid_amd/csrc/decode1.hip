@@ -1,20 +1,25 @@
-// Fused decode path for one token (T = 1), three launches in all:
+// Fused decode path for one token (T = 1), two launches in all:
 //
-//   k_front (gemv.hip)  router logits + shared experts' gate/up
-//   k_dec1_gateup       one block of 8 waves per CU: the top-k (kimi-k3-in-c
-//                       section 9, "Picking 16 experts of 896"), recomputed by
-//                       every block from the logits, while the loads of the
-//                       shared experts' down rows are in flight; those rows;
-//                       then the routed experts' gate/up + activation -> H
-//                       (fp16, picks in ascending id)
-//   k_dec1_down         per output row: the routed down of every pick times
-//                       its routing weight, summed over the picks, plus the
-//                       shared experts' outputs -> out (the weighted combine
-//                       of section 9)
+//   k_dec1_gateup  one block of 8 waves per CU.  Waves 0-3 compute the
+//                  router logits (four rows per block), wait until every row
+//                  is stored, and pick the top k (kimi-k3-in-c section 9,
+//                  "Picking 16 experts of 896"), recomputed by every block
+//                  from the logits; meanwhile waves 4-7 (and 0-3 while they
+//                  wait) stream the shared experts' gate/up rows.  Then all
+//                  waves take the routed experts' gate/up + activation -> H
+//                  (fp16, picks in ascending id)
+//   k_dec1_down    per output row: the shared experts' down rows, then the
+//                  routed down of every pick times its routing weight,
+//                  summed over the picks -> out (the weighted combine of
+//                  section 9, then the shared add)
 //
 // No dispatch kernel and no combine kernel: with one token the dispatch is
 // the ascending sort of 16 ids, and the combine is a sum over the picks that
 // the down kernel accumulates in registers.
+//
+// The logits pass between the blocks of the gate/up kernel through slots in
+// the workspace's control block (see slot_store); the down kernel returns
+// them to zero for the next call.
 //
 // Weight streaming (kimi-k3-in-c section 4: MXFP4 = E2M1 codes two per byte,
 // low nibble first, one E8M0 scale per 32 weights): a row is spread over the
@@ -31,15 +36,17 @@ namespace moe {
 struct Dec1Params {
     Shape s;
     const uint16_t *x;     // [d] bf16 token
+    const float *Wr;       // router weights [E][d] fp32
     const float *bias;     // router selection bias [E] or null
     const uint8_t *w1q, *w1s, *w3q, *w3s, *w2q, *w2s;
-    const uint16_t *sh2;   // shared experts' down [S][d][F] bf16
+    const uint16_t *sh1, *sh3;  // shared experts' gate / up [S][F][d] bf16
+    const uint16_t *sh2;        // shared experts' down [S][d][F] bf16
     Work w;
-    int do_topk;           // 1: pick from w.logits; 0: ids / wts given
+    int do_topk;           // 1: router + pick; 0: ids / wts given
     int32_t *ids;          // [k]: written (do_topk) or read
     float *wts;            // [k]
     int32_t *counts_out;   // [E] or null
-    int shared;            // shared experts included (their gate/up ran in k_front)
+    int shared;            // shared experts included
     uint16_t *out_bf16;
     float *out_f32;
 };
@@ -51,14 +58,20 @@ constexpr int kGuMaxBlockUnits = 32;    // gate/up units of one block (partial s
 constexpr int kGuMaxStages = 8;         // K slices per unit (d <= 4096)
 constexpr int kMaxD = 4096;             // token width of the one-token path
 constexpr int kXPad = kMaxD + kGuWin * 128;  // token length padded to whole gate/up items
-constexpr int kShRows = 2;              // shared down rows per unit
-constexpr int kShMaxBlockUnits = 512;   // shared down units of one block (outputs staged in LDS)
-constexpr int kShMaxChunks = 8;         // 16-byte chunks per lane of a shared down row (F <= 4096)
-constexpr int kShMaxHs = 8192;          // shared activations S * F (fp32) staged in LDS
+constexpr int kShMaxBlockUnits = 512;   // shared gate/up units of one block (activations staged in LDS)
+constexpr int kShMaxChunks = 8;         // 16-byte chunks per lane of a bf16 row (width <= 4096)
+constexpr int kRtChunks = kMaxD / 256;  // 16-byte chunks per lane of an fp32 router row
 constexpr int kDnWaves = 7;             // waves per down block
 constexpr int kDnRows = 2;              // output rows per down wave
 constexpr int kDnBlockRows = kDnWaves * kDnRows;
-constexpr int kDnMaxH = 150 * 1024;     // LDS bytes for the fp16 H of the picks
+constexpr int kDnMaxLds = 152 * 1024;   // LDS bytes for the fp16 H of the picks + the fp32 shared H
+constexpr int kGuDynLds = 32 * 1024;    // unused LDS that keeps a second gate/up block off a CU
+// control block of the workspace (zero between calls): one 8-byte slot per
+// router row, {logit bits (low word), kSlotTag (high word)} once the logit
+// is stored, then a sticky fault word on a line of its own
+constexpr uint32_t kSlotTag = 0x4C4F4749u;  // any other nonzero high word: the block was not zeroed
+constexpr int kCtlFault = 2 * kMaxExperts + 64;  // int32 index
+constexpr uint64_t kHelpTicks = 5000;   // 50 us of the 100 MHz counter; then a waiter computes missing rows
 
 __device__ __forceinline__ uint4 gl16(const void *p) { return *reinterpret_cast<const uint4 *>(p); }
 
@@ -295,10 +308,62 @@ __device__ __forceinline__ int grab(uint32_t lds_addr)
     return __builtin_amdgcn_readfirstlane(v) >> 6;
 }
 
-// One block of 8 waves per CU.  Waves 0-3 pick the experts (top-k) while
-// waves 4-7 stream the shared experts' down rows (a work queue of their
-// own); then every wave takes routed gate/up units from the block's queue.
-// SHC: 16-byte chunks per lane of a shared down row (ceil(F / 512)).
+// Router logits between the blocks of the gate/up kernel.  Block b's
+// keying waves compute router rows 4b .. 4b + 3 and publish each as one
+// 8-byte slot {logit, tag}, stored agent-coherent (written through to the
+// level all XCDs share); a waiter reads the slots of its experts with
+// agent-coherent loads, which is its poll and its logits load at once.  A
+// waiter that has waited past kHelpTicks computes the rows still missing
+// itself (the same sums, so the same bits), so no wait depends on another
+// block being resident.  No counter and no cache-wide fence is needed.
+__device__ __forceinline__ void ctl_set(int *ctl, int w, int v)
+{
+    __hip_atomic_store(ctl + w, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ void slot_store(int *ctl, int e, float v)
+{
+    __hip_atomic_store(reinterpret_cast<uint64_t *>(ctl) + e, ((uint64_t)kSlotTag << 32) | __float_as_uint(v),
+                       __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ uint64_t slot_load(const int *ctl, int e)
+{
+    return __hip_atomic_load(reinterpret_cast<const uint64_t *>(ctl) + e, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+// router row e (fp32 [d]) into registers: lane l holds 16-byte chunks
+// l + 64 c (zeros past d: reads past the resource return 0)
+__device__ __forceinline__ void router_load(uint4 (&wv)[kRtChunks], const float *Wr, int e, int d, bool ok)
+{
+    const int lane = threadIdx.x & 63;
+    const auto rr = brsrc(Wr + (size_t)e * d, ok ? (uint32_t)d * 4 : 0u);
+#pragma unroll
+    for (int q = 0; q < kRtChunks; q++) wv[q] = bld16(rr, (uint32_t)(lane + 64 * q) * 16u, 0);
+}
+
+// logit = row . x (bf16 token from LDS, zeros past d), fp32 sums in the
+// order of router_row (lane chunks ascending, then the lane butterfly): the
+// same logit bits on every path, so a route call plus an expert call with
+// its picks equals the whole layer bit for bit
+__device__ __forceinline__ float router_dot(const uint4 (&wv)[kRtChunks], const uint16_t *xb)
+{
+    const int lane = threadIdx.x & 63;
+    float acc = 0.0f;
+#pragma unroll
+    for (int q = 0; q < kRtChunks; q++) {
+        const uint2 xq = *reinterpret_cast<const uint2 *>(xb + (lane + 64 * q) * 4);
+        acc = fmaf(__uint_as_float(wv[q].x), bf16_lo(xq.x), acc);
+        acc = fmaf(__uint_as_float(wv[q].y), bf16_hi(xq.x), acc);
+        acc = fmaf(__uint_as_float(wv[q].z), bf16_lo(xq.y), acc);
+        acc = fmaf(__uint_as_float(wv[q].w), bf16_hi(xq.y), acc);
+    }
+    return wave_sum(acc);
+}
+
+// One block of 8 waves per CU.  Waves 0-3 compute their router rows, then
+// pick the experts (top-k) from the logits of the whole grid, while waves
+// 4-7 stream the shared experts' gate/up rows (a work queue of their own);
+// then every wave takes routed gate/up units from the block's queue.
+// SHC: 16-byte chunks per lane of a shared gate/up row (ceil(d / 512)).
 // SA: a row's scale bytes are 16-byte aligned (d % 512 == 0).
 template <int SHC, bool SA>
 __global__ __launch_bounds__(kGuWaves * 64) void k_dec1_gateup(Dec1Params p)
@@ -308,7 +373,6 @@ __global__ __launch_bounds__(kGuWaves * 64) void k_dec1_gateup(Dec1Params p)
     __shared__ int s_eid[kMaxTopK];      // picks in ascending id (-1: no pick)
     __shared__ float s_wt[kMaxTopK];
     __shared__ float s_score[kMaxExperts];  // unbiased scores; then block 0's counts
-    __shared__ __attribute__((aligned(16))) float s_hs[kShMaxHs];  // shared activations [S][F]
     // the block's results, written out after its last unit (a global store
     // inside a unit loop would make the next register reuse wait for every
     // load in flight: stores and loads share one counter)
@@ -316,113 +380,85 @@ __global__ __launch_bounds__(kGuWaves * 64) void k_dec1_gateup(Dec1Params p)
     __shared__ __attribute__((aligned(16))) float s_part[kGuMaxBlockUnits][kGuMaxStages][2 * kGuFeat];
     // the token (bf16), zero-padded to whole work items
     __shared__ __attribute__((aligned(16))) uint16_t s_xb[kXPad];
-    __shared__ __attribute__((aligned(8))) float s_ysh[kShMaxBlockUnits][kShRows];
+    __shared__ float s_hsh[kShMaxBlockUnits];  // shared activations of the block's units
     // [0], [1]: work queues (routed, shared); [2]: keying waves whose
     // candidates are written; [3]: picks ready; [4]: keying waves whose
-    // candidates are ranked; [5]: waves 4-7 whose part of the token and of
-    // the shared activations is staged
-    __shared__ int s_ctl[6];
+    // candidates are ranked; [5]: waves 4-7 whose part of the token is
+    // staged; [6]: keying waves whose router row has arrived (or that have
+    // none)
+    __shared__ int s_ctl[7];
     const Shape &s = p.s;
     const int lane = threadIdx.x & 63;
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int d = s.d, F = s.F, E = s.E, k = s.k;
     const int S = p.shared ? s.S : 0;
+    int *ctl = p.w.ctl;
 
-    // ---- loads, in the order they are waited for (reads past a resource's
-    // size return 0, so none of them is conditional)
-    // the router logits and biases of this thread's four experts (keying
-    // waves), or the given picks
-    const bool keyer = p.do_topk && wave < kTkWaves;
-    const int EQ = (E + kTkWaves - 1) / kTkWaves;
-    const auto rlg = brsrc(p.w.logits, keyer ? (uint32_t)E * 4 : 0u);
-    const auto rbs = brsrc(p.bias, keyer && p.bias ? (uint32_t)E * 4 : 0u);
+    // ---- the router row of a keying wave (4 blockIdx + wave), loaded first
+    const int rrow = (int)blockIdx.x * kTkWaves + wave;
+    const bool own_row = p.do_topk && wave < kTkWaves && rrow < E;
+    uint4 rw[kRtChunks];
+    router_load(rw, p.Wr, own_row ? rrow : 0, d, own_row);
+    // the given picks (wave 0 when there is no top-k; reads past a
+    // resource's size return 0, so none of the loads is conditional)
     const auto rid = brsrc(p.ids, p.do_topk || wave ? 0u : (uint32_t)k * 4);
     const auto rwt = brsrc(p.wts, p.do_topk || wave ? 0u : (uint32_t)k * 4);
-    float lg[4], bs[4];
-#pragma unroll
-    for (int i = 0; i < 4; i++) {
-        const uint32_t e = (uint32_t)(min(wave, kTkWaves - 1) * EQ + lane + 64 * i);
-        lg[i] = __uint_as_float(bld4(rlg, e * 4, 0));
-        bs[i] = __uint_as_float(bld4(rbs, e * 4, 0));
-    }
     const int gid = (int)bld4(rid, lane * 4u, 0);
     const float gwt = __uint_as_float(bld4(rwt, lane * 4u, 0));
     __builtin_amdgcn_sched_barrier(0);
-    // waves 4-7 (thread st of 256) stage the shared activations (S * F
-    // fp32) and the token (d bf16; zeros past d), 16 bytes per round
+    // waves 4-7 (thread st of 256) stage the token (d bf16; zeros past d),
+    // 16 bytes per round
     const bool stager = wave >= kTkWaves;
     const int st = (int)threadIdx.x - kTkWaves * 64;
     constexpr int kStThreads = (kGuWaves - kTkWaves) * 64;
-    constexpr int kHsRounds = kShMaxHs / 4 / kStThreads;
-    const auto rhs = brsrc(p.w.Hs, stager ? (uint32_t)(S * F * 4) : 0u);
-    uint4 hsv[kHsRounds];
-#pragma unroll
-    for (int i = 0; i < kHsRounds; i++) hsv[i] = bld16(rhs, (uint32_t)(st + i * kStThreads) * 16u, 0);
     constexpr int kXRounds = (kXPad / 8 + kStThreads - 1) / kStThreads;
     const auto rx = brsrc(p.x, stager ? (uint32_t)d * 2 : 0u);
     uint4 xv[kXRounds];
 #pragma unroll
     for (int i = 0; i < kXRounds; i++) xv[i] = bld16(rx, (uint32_t)(st + i * kStThreads) * 16u, 0);
-    // ---- shared experts' down rows [2 n', 2 n' + 2) of expert si: unit
-    // u = si * d / 2 + n' writes Ysh[2u, 2u + 2) (T = 1).  The block owns
-    // units [sbeg, sbeg + nsloc), streamed by waves 4-7 from their queue
-    // (the first four at once, before the top-k's inputs are even in).
-    const int per_sh = d / kShRows;
-    const int nsh = S * per_sh;
+    // ---- shared experts' gate/up: unit u = si * F + f is feature f of
+    // shared expert si (its W1 and W3 rows times x) and writes Hs[u].  The
+    // block owns units [sbeg, sbeg + nsloc), streamed by waves 4-7 from
+    // their queue (the first four at once, before the token is even in).
+    // Lane l holds 16-byte chunks l + 64 c of both rows; chunks past the
+    // row re-read its last chunk and meet zeros of the padded token.
+    const int nsh = S * F;
     const int sper = (nsh + gridDim.x - 1) / gridDim.x;
     const int sbeg = blockIdx.x * sper;
     const int nsloc = max(min(nsh - sbeg, sper), 0);
-    const int nch = F / 8;  // 16-byte chunks of a bf16 row
-    auto load_sh = [&](uint4 (&w)[kShRows][SHC], int v) __attribute__((always_inline)) {
+    const int nch = d / 8;  // 16-byte chunks of a bf16 row of width d
+    auto load_sh = [&](uint4 (&w)[2][SHC], int v) __attribute__((always_inline)) {
         const bool ok = v < nsloc;
         const int u = ok ? sbeg + v : 0;
-        const int si = u / per_sh, n0 = (u % per_sh) * kShRows;
-        const auto r = brsrc(p.sh2 + (size_t)si * d * F, ok ? (uint32_t)((size_t)d * F * 2) : 0u);
-#pragma unroll
-        for (int rr = 0; rr < kShRows; rr++)
-#pragma unroll
-            for (int c = 0; c < SHC; c++) {
-                const int ch = min(lane + 64 * c, nch - 1);
-                w[rr][c] = bld16(r, (uint32_t)ch * 16, (uint32_t)((n0 + rr) * F * 2));
-            }
-        __builtin_amdgcn_sched_barrier(0);
-    };
-    auto dot_sh = [&](const uint4 (&w)[kShRows][SHC], int v) __attribute__((always_inline)) {
-        const int si = (sbeg + v) / per_sh;
-        float acc[kShRows];
-#pragma unroll
-        for (int rr = 0; rr < kShRows; rr++) acc[rr] = 0.0f;
+        const int si = u / F, f = u - si * F;
+        const uint32_t bytes = ok ? (uint32_t)((size_t)F * d * 2) : 0u;
+        const auto r1 = brsrc(p.sh1 + (size_t)si * F * d, bytes);
+        const auto r3 = brsrc(p.sh3 + (size_t)si * F * d, bytes);
 #pragma unroll
         for (int c = 0; c < SHC; c++) {
-            const int ch = lane + 64 * c;
-            const bool ok = ch < nch;
-            const float4 *h4 = reinterpret_cast<const float4 *>(s_hs + (size_t)si * F + (size_t)min(ch, nch - 1) * 8);
-            const float4 a = h4[0], b = h4[1];
-            const float hv[8] = {a.x, a.y, a.z, a.w, b.x, b.y, b.z, b.w};
-#pragma unroll
-            for (int rr = 0; rr < kShRows; rr++) {
-                const float t = bf16x8_dot_f32(w[rr][c], hv, 0.0f);
-                acc[rr] += ok ? t : 0.0f;
-            }
+            const uint32_t ch = (uint32_t)min(lane + 64 * c, nch - 1);
+            w[0][c] = bld16(r1, ch * 16, (uint32_t)f * d * 2);
+            w[1][c] = bld16(r3, ch * 16, (uint32_t)f * d * 2);
         }
-        float o = 0.0f;
-#pragma unroll
-        for (int rr = 0; rr < kShRows; rr++) {
-            const float t = wave_total(acc[rr]);
-            o = lane == rr ? t : o;
-        }
-        if (lane < kShRows) s_ysh[v][lane] = o;
+        __builtin_amdgcn_sched_barrier(0);
     };
-
-    // waves 4-7: local shared units 0-3, loaded now (for waves 0-3 the
-    // resources are empty: nothing read, and the same program for all)
-    uint4 sa[kShRows][SHC];
-    load_sh(sa, wave >= kTkWaves ? wave - kTkWaves : nsloc);
+    auto dot_sh = [&](const uint4 (&w)[2][SHC], int v) __attribute__((always_inline)) {
+        float ga = 0.0f, ua = 0.0f;
+#pragma unroll
+        for (int c = 0; c < SHC; c++) {
+            const uint4 xq = *reinterpret_cast<const uint4 *>(s_xb + (lane + 64 * c) * 8);
+            const uint32_t xw[4] = {xq.x, xq.y, xq.z, xq.w};
+            ga = bf16x8_dot_bf16(w[0][c], xw, ga);
+            ua = bf16x8_dot_bf16(w[1][c], xw, ua);
+        }
+        const float g = wave_total(ga), u = wave_total(ua);
+        if (lane == 0) s_hsh[v] = gated_act(g, u, s.act, s.b1, s.b2);
+    };
 
     // the queues and flags cleared: the one workgroup barrier before the
     // last (the loads above stay in flight; the shared queue starts past
     // the four units already loaded)
-    if (threadIdx.x < 6) s_ctl[threadIdx.x] = threadIdx.x == 1 ? kTkWaves * 64 : 0;
+    if (threadIdx.x < 7) s_ctl[threadIdx.x] = threadIdx.x == 1 ? kTkWaves * 64 : 0;
     lds_barrier();
 
     const uint32_t q_addr = (uint32_t)(uintptr_t)(__attribute__((address_space(3))) int *)&s_ctl[0];
@@ -434,6 +470,61 @@ __global__ __launch_bounds__(kGuWaves * 64) void k_dec1_gateup(Dec1Params p)
         int id = -1;
         float wt = 0.0f;
         if (p.do_topk) {
+            // the wave's own router row, published as its slot
+            spin_until(&s_ctl[5], kGuWaves - kTkWaves);
+            if (own_row) {
+                const float v = router_dot(rw, s_xb);
+                flag_add(&s_ctl[6]);
+                if (lane == 0) slot_store(ctl, rrow, v);
+            } else {
+                flag_add(&s_ctl[6]);
+            }
+            // the slots of this thread's four experts (wave * EQ + lane + 64 i),
+            // read until all are stored
+            const int EQ = (E + kTkWaves - 1) / kTkWaves;
+            const auto rbs = brsrc(p.bias, p.bias ? (uint32_t)E * 4 : 0u);
+            float lg[4], bs[4];
+            const uint64_t t0 = __builtin_amdgcn_s_memrealtime();
+            for (;;) {
+                uint64_t sv[4];
+#pragma unroll
+                for (int i = 0; i < 4; i++) {
+                    const int e = wave * EQ + lane + 64 * i;
+                    sv[i] = e < E ? slot_load(ctl, e) : ((uint64_t)kSlotTag << 32);  // (padding: ready, unused)
+                }
+                bool miss = false, bad = false;
+#pragma unroll
+                for (int i = 0; i < 4; i++) {
+                    const uint32_t tag = (uint32_t)(sv[i] >> 32);
+                    miss = miss || tag == 0u;
+                    bad = bad || (tag != 0u && tag != kSlotTag);
+                    lg[i] = __uint_as_float((uint32_t)sv[i]);
+                }
+                if (__builtin_amdgcn_ballot_w64(bad)) {
+                    if (lane == 0) ctl_set(ctl, kCtlFault, 1);
+                    break;
+                }
+                if (!__builtin_amdgcn_ballot_w64(miss)) break;
+                if (__builtin_amdgcn_s_memrealtime() - t0 > kHelpTicks) {
+                    // waited long: compute this wave's missing rows here
+#pragma unroll 1
+                    for (int i = 0; i < 4; i++) {
+                        uint64_t m = __builtin_amdgcn_ballot_w64((uint32_t)(sv[i] >> 32) == 0u);
+                        while (m) {
+                            const int l = __builtin_ctzll(m);
+                            m &= m - 1;
+                            const int e = wave * EQ + l + 64 * i;
+                            uint4 hw[kRtChunks];
+                            router_load(hw, p.Wr, e, d, true);
+                            const float v = router_dot(hw, s_xb);
+                            if (lane == 0) slot_store(ctl, e, v);
+                        }
+                    }
+                }
+                __builtin_amdgcn_s_sleep(2);
+            }
+#pragma unroll
+            for (int i = 0; i < 4; i++) bs[i] = __uint_as_float(bld4(rbs, (uint32_t)(wave * EQ + lane + 64 * i) * 4, 0));
             topk_candidates(E, k, wave, lg, bs, s_cand, s_score);
             flag_add(&s_ctl[2]);
             spin_until(&s_ctl[2], kTkWaves);
@@ -444,6 +535,7 @@ __global__ __launch_bounds__(kGuWaves * 64) void k_dec1_gateup(Dec1Params p)
                 topk_weights(k, s.renorm, s.routed_scale, s_sel, s_score, id, wt);
             }
         } else {
+            flag_add(&s_ctl[6]);
             id = lane < k ? gid : -1;
             wt = lane < k ? gwt : 0.0f;
         }
@@ -485,11 +577,8 @@ __global__ __launch_bounds__(kGuWaves * 64) void k_dec1_gateup(Dec1Params p)
         }
         __builtin_amdgcn_s_setprio(0);
     } else {
-        // ---- staging: the shared activations and the token to LDS
-        // (unconditional: past S * F and d the loads returned 0); then all
-        // four staging waves are waited for
-#pragma unroll
-        for (int i = 0; i < kHsRounds; i++) reinterpret_cast<uint4 *>(s_hs)[st + i * kStThreads] = hsv[i];
+        // ---- staging: the token to LDS (unconditional: past d the loads
+        // returned 0); then all four staging waves are waited for
 #pragma unroll
         for (int i = 0; i < kXRounds; i++) {
             const int t = st + i * kStThreads;  // elements [8t, 8t + 8)
@@ -497,10 +586,16 @@ __global__ __launch_bounds__(kGuWaves * 64) void k_dec1_gateup(Dec1Params p)
         }
         flag_add(&s_ctl[5]);
         spin_until(&s_ctl[5], kGuWaves - kTkWaves);
-        // ---- the shared rows, two units in flight per wave (unit va is in sa)
+        // ---- the shared gate/up units, two in flight per wave, from local
+        // units 0-3 on (the queue starts past them).  They start once the
+        // block's router rows have arrived: those loads are on the way to
+        // the picks and should not queue behind a CU's worth of stream.
+        spin_until(&s_ctl[6], kTkWaves);
+        uint4 sa[2][SHC];
+        load_sh(sa, wave - kTkWaves);
         int va = wave - kTkWaves;
         if (va < nsloc) {
-            uint4 sb[kShRows][SHC];
+            uint4 sb[2][SHC];
             int vb = grab(s_addr);
             load_sh(sb, vb);
             // (one exit, at the bottom)
@@ -645,7 +740,7 @@ __global__ __launch_bounds__(kGuWaves * 64) void k_dec1_gateup(Dec1Params p)
 
     lds_barrier();
     // the block's results: routed activations to H (the K slices summed in
-    // order; skipped where no pick), shared outputs to Ysh
+    // order; skipped where no pick), shared activations to Hs
     _Float16 *H = reinterpret_cast<_Float16 *>(p.w.H);
     for (int i = threadIdx.x; i < nloc * kGuFeat; i += kGuWaves * 64) {
         const int v = i / kGuFeat, f = i - v * kGuFeat;
@@ -657,8 +752,10 @@ __global__ __launch_bounds__(kGuWaves * 64) void k_dec1_gateup(Dec1Params p)
         }
         if (s_eid[u / upr] >= 0) H[(size_t)u * kGuFeat + f] = (_Float16)gated_act(g, up, s.act, s.b1, s.b2);
     }
-    for (int i = threadIdx.x; i < nsloc; i += kGuWaves * 64)
-        *reinterpret_cast<float2 *>(p.w.Ysh + (size_t)(sbeg + i) * kShRows) = *reinterpret_cast<const float2 *>(s_ysh[i]);
+    // (the shared activations follow the fp16 H of the picks: the down
+    // kernel stages both in one copy)
+    float *hs1 = reinterpret_cast<float *>(H + (size_t)k * F);
+    for (int i = threadIdx.x; i < nsloc; i += kGuWaves * 64) hs1[sbeg + i] = s_hsh[i];
 }
 
 // ------------------------------------------------------------ routed down + combine
@@ -668,15 +765,19 @@ struct DnLoads {
     uint16_t sc[2][kDnRows];
 };
 
+// SHC: 16-byte chunks per lane of a shared down row (ceil(F / 512))
+template <int SHC>
 __global__ __launch_bounds__(kDnWaves * 64) void k_dec1_down(Dec1Params p)
 {
-    extern __shared__ __attribute__((aligned(16))) uint8_t s_h[];  // fp16 H [k][F]
+    // fp16 H of the picks [k][F], then the fp32 shared activations [S][F]
+    extern __shared__ __attribute__((aligned(16))) uint8_t s_h[];
     __shared__ int s_e[kMaxTopK];
     __shared__ float s_w[kMaxTopK];
     const Shape &s = p.s;
     const int lane = threadIdx.x & 63;
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int d = s.d, F = s.F, k = s.k;
+    const int S = p.shared ? s.S : 0;
     const int nbp = F / 64;
     const int lp = lane < nbp ? lane : nbp - 1;
     const float lmask = lane < nbp ? 1.0f : 0.0f;
@@ -687,13 +788,42 @@ __global__ __launch_bounds__(kDnWaves * 64) void k_dec1_down(Dec1Params p)
     int rows[kDnRows];
 #pragma unroll
     for (int r = 0; r < kDnRows; r++) rows[r] = min(n0 + r, d - 1);
+    const float *s_hs = reinterpret_cast<const float *>(s_h + (size_t)k * F * 2);
 
     // the picks (ascending id, -1: none) and their weights, once
     if (threadIdx.x < k) {
         s_e[threadIdx.x] = p.w.active[threadIdx.x];
         s_w[threadIdx.x] = p.w.pos_w[threadIdx.x];
     }
+    // a router wait that timed out (control block not zeroed) poisons the output
+    const bool fault = __hip_atomic_load(p.w.ctl + kCtlFault, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) != 0;
+    // the router slots back to zero for the next call (the gate/up kernel,
+    // their only reader, has ended)
+    if (blockIdx.x == 0)
+        for (int e = threadIdx.x; e < s.E; e += kDnWaves * 64) reinterpret_cast<uint64_t *>(p.w.ctl)[e] = 0;
     __syncthreads();
+
+    // shared experts' down: the wave's rows of W2s[si] (bf16), lane l
+    // holding 16-byte chunks l + 64 c; chunks past the row re-read its last
+    // chunk and are masked out
+    const int nchf = F / 8;
+    auto load_shd = [&](uint4 (&w)[kDnRows][SHC], int si) __attribute__((always_inline)) {
+        const auto r = brsrc(p.sh2 + (size_t)si * d * F, (uint32_t)((size_t)d * F * 2));
+#pragma unroll
+        for (int rr = 0; rr < kDnRows; rr++)
+#pragma unroll
+            for (int c = 0; c < SHC; c++) {
+                const uint32_t ch = (uint32_t)min(lane + 64 * c, nchf - 1);
+                w[rr][c] = bld16(r, ch * 16, (uint32_t)rows[rr] * F * 2);
+            }
+    };
+    // the first two shared experts' rows are loaded now (one if the rows are
+    // so wide that two would not fit the registers), a later one into the
+    // registers of the one just multiplied
+    constexpr int NSH = SHC <= 6 ? 2 : 1;
+    uint4 shw[NSH][kDnRows][SHC];
+    if (S > 0) load_shd(shw[0], 0);
+    if (NSH > 1 && S > 1) load_shd(shw[NSH - 1], 1);
 
     const int npair = (k + 1) / 2;
     // loads of pick pair q; past the end (or no pick) they re-read valid rows
@@ -716,28 +846,58 @@ __global__ __launch_bounds__(kDnWaves * 64) void k_dec1_down(Dec1Params p)
 
     DnLoads ga, gb;
     load(ga, 0);
-    // stage the fp16 H of all picks (k * F * 2 bytes) into LDS: every load of
-    // a round is issued before its stores
+    // stage the fp16 H of all picks (k * F * 2 bytes) and the shared
+    // activations after it (S * F * 4 bytes), one contiguous region, into
+    // LDS: every load of a round is issued before its stores
     {
         constexpr int NB = 16;
-        const int n16 = k * F / 8;
+        const int n16 = (k * F * 2 + S * F * 4) / 16;
         const uint4 *src = reinterpret_cast<const uint4 *>(p.w.H);
         for (int i0 = 0; i0 < n16; i0 += NB * kDnWaves * 64) {
             uint4 v[NB];
 #pragma unroll
-            for (int b = 0; b < NB; b++) {
-                const int i = i0 + b * kDnWaves * 64 + threadIdx.x;
-                v[b] = src[min(i, n16 - 1)];
-            }
-            // (indexes past the end store the last chunk again, same value)
+            for (int b = 0; b < NB; b++) v[b] = src[min(i0 + b * kDnWaves * 64 + (int)threadIdx.x, n16 - 1)];
+            // (indexes past the end store the last piece again, same value)
 #pragma unroll
-            for (int b = 0; b < NB; b++) {
-                const int i = min(i0 + b * kDnWaves * 64 + (int)threadIdx.x, n16 - 1);
-                *reinterpret_cast<uint4 *>(s_h + (size_t)i * 16) = v[b];
-            }
+            for (int b = 0; b < NB; b++)
+                *reinterpret_cast<uint4 *>(s_h + (size_t)min(i0 + b * kDnWaves * 64 + (int)threadIdx.x, n16 - 1) * 16) = v[b];
         }
     }
     __syncthreads();
+
+    // the shared rows
+    float ysh[kDnRows];
+#pragma unroll
+    for (int r = 0; r < kDnRows; r++) ysh[r] = 0.0f;
+    auto dot_shd = [&](const uint4 (&w)[kDnRows][SHC], int si) __attribute__((always_inline)) {
+        float a[kDnRows];
+#pragma unroll
+        for (int r = 0; r < kDnRows; r++) a[r] = 0.0f;
+#pragma unroll
+        for (int c = 0; c < SHC; c++) {
+            const int ch = lane + 64 * c;
+            const bool ok = ch < nchf;
+            const float4 *h4 = reinterpret_cast<const float4 *>(s_hs + (size_t)si * F + (size_t)min(ch, nchf - 1) * 8);
+            const float4 h0 = h4[0], h1 = h4[1];
+            const float hv[8] = {h0.x, h0.y, h0.z, h0.w, h1.x, h1.y, h1.z, h1.w};
+#pragma unroll
+            for (int r = 0; r < kDnRows; r++) {
+                const float t = bf16x8_dot_f32(w[r][c], hv, 0.0f);
+                a[r] += ok ? t : 0.0f;
+            }
+        }
+#pragma unroll
+        for (int r = 0; r < kDnRows; r++) ysh[r] += wave_total(a[r]);
+    };
+    for (int si = 0; si < S; si++) {
+        if (NSH > 1 && (si & 1)) {
+            dot_shd(shw[NSH - 1], si);
+            if (si + 2 < S) load_shd(shw[NSH - 1], si + 2);
+        } else {
+            dot_shd(shw[0], si);
+            if (si + NSH < S) load_shd(shw[0], si + NSH);
+        }
+    }
 
     float acc[kDnRows];
 #pragma unroll
@@ -779,11 +939,11 @@ __global__ __launch_bounds__(kDnWaves * 64) void k_dec1_down(Dec1Params p)
 
 #pragma unroll
     for (int r = 0; r < kDnRows; r++) {
-        float v = wave_total(acc[r] * lmask);
+        // the weighted sum over the picks, then the shared experts' outputs
+        float v = wave_total(acc[r] * lmask) + ysh[r];
+        if (fault) v = __builtin_nanf("");
         const int n = n0 + r;
         if (lane == 0 && n < d) {
-            if (p.shared)
-                for (int si = 0; si < s.S; si++) v += p.w.Ysh[(size_t)si * d + n];
             if (p.out_f32) p.out_f32[n] = v;
             if (p.out_bf16) p.out_bf16[n] = f32_to_bf16_rne(v);
         }
@@ -794,9 +954,9 @@ __global__ __launch_bounds__(kDnWaves * 64) void k_dec1_down(Dec1Params p)
 
 bool decode1_supported(const Shape &s)
 {
-    return s.T == 1 && s.d % 64 == 0 && s.d <= 4096 && s.F % 64 == 0 && s.F <= 512 * kShMaxChunks &&
-           s.E <= kMaxExperts && s.k <= kMaxTopK && (size_t)s.k * s.F * 2 <= kDnMaxH &&
-           (size_t)s.S * s.F <= kShMaxHs;
+    return s.T == 1 && s.d % 64 == 0 && s.d <= kMaxD && s.F % 64 == 0 && s.F <= 512 * kShMaxChunks &&
+           s.E <= kMaxExperts && s.k <= kMaxTopK &&
+           (size_t)s.k * s.F * 2 + (size_t)s.S * s.F * 4 <= (size_t)kDnMaxLds;
 }
 
 static int cu_count()
@@ -817,6 +977,9 @@ hipError_t launch_decode1(const Shape &s, const uint16_t *x, const Weights &wt, 
     p.x = x;
     p.bias = bias;
     p.w1q = wt.w1q; p.w1s = wt.w1s; p.w3q = wt.w3q; p.w3s = wt.w3s; p.w2q = wt.w2q; p.w2s = wt.w2s;
+    p.Wr = wt.router_w;
+    p.sh1 = wt.sh1;
+    p.sh3 = wt.sh3;
     p.sh2 = wt.sh2;
     p.w = w;
     p.do_topk = do_topk;
@@ -826,26 +989,33 @@ hipError_t launch_decode1(const Shape &s, const uint16_t *x, const Weights &wt, 
     p.shared = shared && s.S > 0;
     p.out_bf16 = out_bf16;
     p.out_f32 = out_f32;
-    // one block per CU, more if a block's ranges would not fit its LDS records
+    // one block per CU (its LDS keeps a second one off), more if a block's
+    // ranges would not fit its LDS records
     const int units = s.k * (s.F / kGuFeat);
-    const int sh_units = p.shared ? s.S * (s.d / kShRows) : 0;
+    const int sh_units = p.shared ? s.S * s.F : 0;
     const int nblk = max(cu_count(), max((units + kGuMaxBlockUnits - 1) / kGuMaxBlockUnits,
                                          (sh_units + kShMaxBlockUnits - 1) / kShMaxBlockUnits));
-    const int shc = (s.F / 8 + 63) / 64;  // 16-byte chunks per lane of a shared down row
+    const int shc = (s.d / 8 + 63) / 64;  // 16-byte chunks per lane of a shared gate/up row
     const bool sa = s.d % 512 == 0;
-#define MOE_DEC1_GU(C)                                                                   \
-    do {                                                                                 \
-        if (sa) k_dec1_gateup<C, true><<<nblk, kGuWaves * 64, 0, stream>>>(p);           \
-        else k_dec1_gateup<C, false><<<nblk, kGuWaves * 64, 0, stream>>>(p);            \
+#define MOE_DEC1_GU(C)                                                                          \
+    do {                                                                                        \
+        if (sa) k_dec1_gateup<C, true><<<nblk, kGuWaves * 64, kGuDynLds, stream>>>(p);          \
+        else k_dec1_gateup<C, false><<<nblk, kGuWaves * 64, kGuDynLds, stream>>>(p);           \
     } while (0)
     if (shc <= 2) MOE_DEC1_GU(2);
     else if (shc <= 4) MOE_DEC1_GU(4);
     else if (shc <= 6) MOE_DEC1_GU(6);
+    else if (shc <= 7) MOE_DEC1_GU(7);
     else MOE_DEC1_GU(8);
 #undef MOE_DEC1_GU
     if (ev2) (void)hipEventRecord(ev2[0], stream);
     const int nd = (s.d + kDnBlockRows - 1) / kDnBlockRows;
-    k_dec1_down<<<nd, kDnWaves * 64, (size_t)s.k * s.F * 2, stream>>>(p);
+    const size_t lds = (size_t)s.k * s.F * 2 + (size_t)(p.shared ? s.S : 0) * s.F * 4;
+    const int shd = (s.F / 8 + 63) / 64;  // 16-byte chunks per lane of a shared down row
+    if (shd <= 2) k_dec1_down<2><<<nd, kDnWaves * 64, lds, stream>>>(p);
+    else if (shd <= 4) k_dec1_down<4><<<nd, kDnWaves * 64, lds, stream>>>(p);
+    else if (shd <= 6) k_dec1_down<6><<<nd, kDnWaves * 64, lds, stream>>>(p);
+    else k_dec1_down<8><<<nd, kDnWaves * 64, lds, stream>>>(p);
     if (ev2) (void)hipEventRecord(ev2[1], stream);
     return hipGetLastError();
 }

@@ -1,6 +1,8 @@
 // C ABI of the MoE layer: argument validation, workspace carving and the
 // launch sequence of each entry point (see include/moe.h).
 #include <math.h>
+
+#include <algorithm>
 #include <string.h>
 
 #include "../../include/moe.h"
@@ -85,6 +87,7 @@ size_t carve(const Shape &s, char *base, Work *w)
     const size_t T = (size_t)s.T, E = (size_t)s.E, k = (size_t)s.k;
     const size_t nblk = (T + moe::kDispatchTokens - 1) / moe::kDispatchTokens;
     Work v;
+    v.ctl = (int32_t *)take(moe::kWsControlBytes);  // first: at offset 0 for every T
     v.logits = (float *)take(T * E * 4);
     v.ids = (int32_t *)take(T * k * 4);
     v.wts = (float *)take(T * k * 4);
@@ -97,7 +100,8 @@ size_t carve(const Shape &s, char *base, Work *w)
     v.pos_tok = (int32_t *)take(T * k * 4);
     v.pos_w = (float *)take(T * k * 4);
     v.tok_pos = (int32_t *)take(T * k * 4);
-    v.H = (void *)take(T * k * (size_t)s.F * 4);
+    // (one token: the fp16 H of the picks, then the fp32 shared activations)
+    v.H = (void *)take(std::max(T * k * (size_t)s.F * 4, k * (size_t)s.F * 2 + (size_t)s.S * s.F * 4));
     v.Hs = (float *)take(T * (size_t)s.S * s.F * 4);
     v.Y = (float *)take(T * k * (size_t)s.d * 4);
     v.Ysh = (float *)take((size_t)s.S * T * s.d * 4);
@@ -176,15 +180,10 @@ moe_status run_layer(const moe_layer_desc *d, const Shape &s, const uint16_t *x,
     const moe::Weights wt = weights_of(d);
     const int shared = include_shared && s.S > 0;
     MOE_TRY(mark(ev, 0, st));
-    const int front_shared = experts && shared && path == MOE_PATH_GEMV;
-    if (do_router && path == MOE_PATH_MFMA) {
-        MOE_TRY(moe::launch_mfma_router(s, x, wt, w, st));
-    } else if (do_router || front_shared) {
-        MOE_TRY(moe::launch_front(s, x, wt, do_router, front_shared, w, st));
-    }
-    MOE_TRY(mark(ev, 1, st));
     if (experts && path == MOE_PATH_GEMV && moe::decode1_supported(s)) {
-        // one token: top-k, dispatch and combine fused into the expert kernels
+        // one token: router, top-k, dispatch and combine fused into the two
+        // expert kernels (the first phases are empty)
+        MOE_TRY(mark(ev, 1, st));
         MOE_TRY(mark(ev, 2, st));
         MOE_TRY(moe::launch_decode1(s, x, wt, d->router_bias, do_router, ids, wts, counts_out, shared,
                                     w, out_mode != MOE_OUT_F32 ? out_bf16 : nullptr,
@@ -193,6 +192,13 @@ moe_status run_layer(const moe_layer_desc *d, const Shape &s, const uint16_t *x,
         MOE_TRY(mark(ev, 5, st));
         return MOE_OK;
     }
+    const int front_shared = experts && shared && path == MOE_PATH_GEMV;
+    if (do_router && path == MOE_PATH_MFMA) {
+        MOE_TRY(moe::launch_mfma_router(s, x, wt, w, st));
+    } else if (do_router || front_shared) {
+        MOE_TRY(moe::launch_front(s, x, wt, do_router, front_shared, w, st));
+    }
+    MOE_TRY(mark(ev, 1, st));
     MOE_TRY(moe::launch_dispatch(s, do_router, w.logits, d->router_bias, ids, wts, counts_out, w,
                                  st));
     MOE_TRY(mark(ev, 2, st));

@@ -104,7 +104,7 @@ def run_layer(gl: GpuLayer, x_bits: np.ndarray, out_mode: int = 2):
     ids = torch.empty((T, k), dtype=torch.int32, device="cuda")
     w = torch.empty((T, k), dtype=torch.float32, device="cuda")
     cnt = torch.empty(E, dtype=torch.int32, device="cuda")
-    ws = torch.empty(moe.workspace_bytes(gl.desc, T), dtype=torch.uint8, device="cuda")
+    ws = torch.zeros(moe.workspace_bytes(gl.desc, T), dtype=torch.uint8, device="cuda")
     moe.layer(gl.desc, x, T, out_b if out_mode != 1 else None, out_f if out_mode != 0 else None,
               out_mode, ws, ids=ids, weights=w, counts=cnt)
     torch.cuda.synchronize()

@@ -67,7 +67,7 @@ def test_route_then_forward_equals_layer():
         ids2 = torch.empty((T, 6), dtype=torch.int32, device="cuda")
         w2 = torch.empty((T, 6), dtype=torch.float32, device="cuda")
         c2 = torch.empty(40, dtype=torch.int32, device="cuda")
-        ws = torch.empty(moe.workspace_bytes(gl.desc, T), dtype=torch.uint8, device="cuda")
+        ws = torch.zeros(moe.workspace_bytes(gl.desc, T), dtype=torch.uint8, device="cuda")
         moe.route(gl.desc, xd, T, ids2, w2, c2, ws)
         of = torch.empty((T, 320), dtype=torch.float32, device="cuda")
         ob = torch.empty((T, 320), dtype=torch.int16, device="cuda")
@@ -140,7 +140,7 @@ def test_zero_tokens_is_noop():
     w = synth.WORKLOADS[0]
     gl = make_gpu_layer(w.shape, w.seed)
     out = torch.full((2, w.shape.d_model), 7.0, device="cuda")
-    ws = torch.empty(moe.workspace_bytes(gl.desc, 1), dtype=torch.uint8, device="cuda")
+    ws = torch.zeros(moe.workspace_bytes(gl.desc, 1), dtype=torch.uint8, device="cuda")
     x = torch.zeros((1, w.shape.d_model), dtype=torch.int16, device="cuda")
     moe.layer(gl.desc, x, 0, None, out, moe.OUT_F32, ws)
     torch.cuda.synchronize()
@@ -223,7 +223,7 @@ def test_graph_replay_matches_eager():
     ref_b, _, _, _, _ = run_layer(gl, xb)
     xd = sdev.tokens_to_device(xa)
     xo = sdev.tokens_to_device(xb)
-    ws = torch.empty(moe.workspace_bytes(gl.desc, T), dtype=torch.uint8, device="cuda")
+    ws = torch.zeros(moe.workspace_bytes(gl.desc, T), dtype=torch.uint8, device="cuda")
     out = torch.empty((T, shape.d_model), dtype=torch.float32, device="cuda")
     out_o = torch.empty_like(out)
     moe.layer(gl.desc, xd, T, None, out, moe.OUT_F32, ws)

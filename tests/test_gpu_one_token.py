@@ -103,7 +103,7 @@ def test_one_token_expert_forward_with_given_picks():
         ids2 = torch.empty((1, 6), dtype=torch.int32, device="cuda")
         w2 = torch.empty((1, 6), dtype=torch.float32, device="cuda")
         c2 = torch.empty(40, dtype=torch.int32, device="cuda")
-        ws = torch.empty(moe.workspace_bytes(gl.desc, 1), dtype=torch.uint8, device="cuda")
+        ws = torch.zeros(moe.workspace_bytes(gl.desc, 1), dtype=torch.uint8, device="cuda")
         moe.route(gl.desc, xd, 1, ids2, w2, c2, ws)
         of = torch.empty((1, 512), dtype=torch.float32, device="cuda")
         ob = torch.empty((1, 512), dtype=torch.int16, device="cuda")
@@ -138,7 +138,7 @@ def test_graph_replay_one_token_and_mfma_paths(T):
     ref_b = run_layer(gl, xb)[0]
     xd = sdev.tokens_to_device(xa)
     xo = sdev.tokens_to_device(xb)
-    ws = torch.empty(moe.workspace_bytes(gl.desc, T), dtype=torch.uint8, device="cuda")
+    ws = torch.zeros(moe.workspace_bytes(gl.desc, T), dtype=torch.uint8, device="cuda")
     out = torch.empty((T, shape.d_model), dtype=torch.float32, device="cuda")
     out_o = torch.empty_like(out)
     moe.layer(gl.desc, xd, T, None, out, moe.OUT_F32, ws)
