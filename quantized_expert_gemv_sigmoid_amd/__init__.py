@@ -25,6 +25,9 @@ PATH_AUTO, PATH_GEMV, PATH_MFMA = 0, 1, 2
 EXPORTS = ("moe_workspace_bytes", "moe_path_for", "moe_route", "moe_expert_forward",
            "moe_layer", "moe_layer_timed", "moe_status_str")
 TIMED_EVENTS = 6
+# leading workspace bytes that must be zero before a workspace's first call
+# (MOE_WS_CONTROL_BYTES in include/moe.h); every call leaves them zero
+WS_CONTROL_BYTES = 9216
 
 
 class MoeError(RuntimeError):

@@ -28,6 +28,8 @@
 // (the next unit is issued before the current one is multiplied); the lane's
 // 64 inputs stay in registers (gate/up) or are read from LDS (down: the fp16
 // H of all picks, staged once per block).
+#include <stdlib.h>
+
 #include "common.h"
 #include "router_dev.h"
 
@@ -49,6 +51,7 @@ struct Dec1Params {
     int shared;            // shared experts included
     uint16_t *out_bf16;
     float *out_f32;
+    uint64_t help_ticks;   // real-time ticks (100 MHz) a router waiter waits before it computes missing rows
 };
 
 constexpr int kGuWaves = 8;             // waves per gate/up block (one block per CU)
@@ -72,6 +75,7 @@ constexpr int kGuDynLds = 32 * 1024;    // unused LDS that keeps a second gate/u
 constexpr uint32_t kSlotTag = 0x4C4F4749u;  // any other nonzero high word: the block was not zeroed
 constexpr int kCtlFault = 2 * kMaxExperts + 64;  // int32 index
 constexpr uint64_t kHelpTicks = 5000;   // 50 us of the 100 MHz counter; then a waiter computes missing rows
+                                        // (MOE_ONE_TOKEN_HELP_US in the environment overrides it)
 
 __device__ __forceinline__ uint4 gl16(const void *p) { return *reinterpret_cast<const uint4 *>(p); }
 
@@ -505,7 +509,7 @@ __global__ __launch_bounds__(kGuWaves * 64) void k_dec1_gateup(Dec1Params p)
                     break;
                 }
                 if (!__builtin_amdgcn_ballot_w64(miss)) break;
-                if (__builtin_amdgcn_s_memrealtime() - t0 > kHelpTicks) {
+                if (__builtin_amdgcn_s_memrealtime() - t0 >= p.help_ticks) {
                     // waited long: compute this wave's missing rows here
 #pragma unroll 1
                     for (int i = 0; i < 4; i++) {
@@ -989,6 +993,8 @@ hipError_t launch_decode1(const Shape &s, const uint16_t *x, const Weights &wt, 
     p.shared = shared && s.S > 0;
     p.out_bf16 = out_bf16;
     p.out_f32 = out_f32;
+    p.help_ticks = kHelpTicks;
+    if (const char *h = getenv("MOE_ONE_TOKEN_HELP_US")) p.help_ticks = (uint64_t)strtoull(h, nullptr, 10) * 100;
     // one block per CU (its LDS keeps a second one off), more if a block's
     // ranges would not fit its LDS records
     const int units = s.k * (s.F / kGuFeat);

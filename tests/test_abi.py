@@ -144,3 +144,13 @@ def test_status_strings(L):
     for s in (moe.OK, moe.EINVAL, moe.EUNSUPPORTED, moe.EWORKSPACE, moe.EHIP):
         assert moe.status_str(s) not in ("", "unknown status")
     assert moe.status_str(12345) == "unknown status"
+
+
+def test_control_block_size_matches_header(L):
+    """The binding's WS_CONTROL_BYTES is the header's MOE_WS_CONTROL_BYTES, and
+    every workspace holds at least the control block."""
+    m = re.search(r"#define\s+MOE_WS_CONTROL_BYTES\s+(\d+)", open(HEADER).read())
+    assert m and int(m.group(1)) == moe.WS_CONTROL_BYTES
+    d = desc()
+    for t in (0, 1, 2, 64):
+        assert L.moe_workspace_bytes(ctypes.byref(d), t) >= moe.WS_CONTROL_BYTES

@@ -9,7 +9,9 @@ The shapes here exercise that path's branches:
 - top-k = E, a single expert, no shared experts;
 - a selection bias, SwiGLU;
 - picks given to moe_expert_forward;
-- HIP graph replays.
+- HIP graph replays;
+- the router hand-off between blocks: its fallback (a waiter that computes
+  missing logits itself) and a control block that was not zeroed.
 
 The bar is the one the other GPU tests use:
 - ids (per-token sets) and counts bit-exact;
@@ -154,3 +156,47 @@ def test_graph_replay_one_token_and_mfma_paths(T):
         moe.layer(gl.desc, xo, T, None, out_o, moe.OUT_F32, ws)
         torch.cuda.synchronize()
         assert np.array_equal(out_o.cpu().numpy(), ref_b)
+
+
+def test_one_token_router_fallback_is_bit_identical(monkeypatch):
+    """With no wait allowed, every waiter of the gate/up kernel computes the
+    router rows it has not yet seen itself: the same sums, so the same bits."""
+    shape = S(300, 16, 2, 2048, 1536)
+    gl = make_gpu_layer(shape, 76)
+    x, rw, bias = tokens(gl, 3)
+    rids, rw_, _, rout = oracle_outputs(gl, x, rw, bias, np.arange(3))
+    for t in range(3):
+        log(f"case: one-token router fallback, token {t}")
+        ref = run_layer(gl, x[t:t + 1])
+        monkeypatch.setenv("MOE_ONE_TOKEN_HELP_US", "0")
+        got = run_layer(gl, x[t:t + 1])
+        monkeypatch.delenv("MOE_ONE_TOKEN_HELP_US")
+        for a, b in zip(ref, got):
+            assert np.array_equal(a, b), "fallback output differs"
+        check_routing(got[2], got[3], got[4], rids[t:t + 1], rw_[t:t + 1], shape.n_experts, f"token {t}")
+        assert_close(got[0], rout[t:t + 1], f"token {t}")
+
+
+def test_one_token_control_block_not_zeroed():
+    """A workspace whose control block holds something else gives NaN outputs
+    (and keeps giving them) instead of waiting or reading stale logits; once
+    the block is zeroed the call is exact again."""
+    import quantized_expert_gemv_sigmoid_amd as moe
+    import synth.device as sdev
+    shape = S(40, 6, 2, 512, 768)
+    gl = make_gpu_layer(shape, 77)
+    x, _, _ = tokens(gl, 1)
+    log("case: one-token control block not zeroed")
+    ref_f = run_layer(gl, x)[0]
+    xd = sdev.tokens_to_device(x)
+    ws = torch.zeros(moe.workspace_bytes(gl.desc, 1), dtype=torch.uint8, device="cuda")
+    ws[:moe.WS_CONTROL_BYTES] = 0xA5
+    of = torch.empty((1, shape.d_model), dtype=torch.float32, device="cuda")
+    for _ in range(2):
+        moe.layer(gl.desc, xd, 1, None, of, moe.OUT_F32, ws)
+        torch.cuda.synchronize()
+        assert np.isnan(of.cpu().numpy()).all(), "a garbage control block must poison the output"
+    ws[:moe.WS_CONTROL_BYTES] = 0
+    moe.layer(gl.desc, xd, 1, None, of, moe.OUT_F32, ws)
+    torch.cuda.synchronize()
+    assert np.array_equal(of.cpu().numpy(), ref_f), "zeroed again, the call must match"
