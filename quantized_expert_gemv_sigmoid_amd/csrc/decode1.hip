@@ -403,6 +403,16 @@ __global__ __launch_bounds__(kGuWaves * 64) void k_dec1_gateup(Dec1Params p)
     const bool own_row = p.do_topk && wave < kTkWaves && rrow < E;
     uint4 rw[kRtChunks];
     router_load(rw, p.Wr, own_row ? rrow : 0, d, own_row);
+    // the selection biases of this thread's four experts (wave * EQ + lane +
+    // 64 i): issued now, since a load issued later waits behind the
+    // streaming waves' loads in the CU's queue
+    const int EQ = (E + kTkWaves - 1) / kTkWaves;
+    float bs[4];
+    {
+        const auto rbs = brsrc(p.bias, p.bias && p.do_topk && wave < kTkWaves ? (uint32_t)E * 4 : 0u);
+#pragma unroll
+        for (int i = 0; i < 4; i++) bs[i] = __uint_as_float(bld4(rbs, (uint32_t)(wave * EQ + lane + 64 * i) * 4, 0));
+    }
     // the given picks (wave 0 when there is no top-k; reads past a
     // resource's size return 0, so none of the loads is conditional)
     const auto rid = brsrc(p.ids, p.do_topk || wave ? 0u : (uint32_t)k * 4);
@@ -485,9 +495,7 @@ __global__ __launch_bounds__(kGuWaves * 64) void k_dec1_gateup(Dec1Params p)
             }
             // the slots of this thread's four experts (wave * EQ + lane + 64 i),
             // read until all are stored
-            const int EQ = (E + kTkWaves - 1) / kTkWaves;
-            const auto rbs = brsrc(p.bias, p.bias ? (uint32_t)E * 4 : 0u);
-            float lg[4], bs[4];
+            float lg[4];
             const uint64_t t0 = __builtin_amdgcn_s_memrealtime();
             for (;;) {
                 uint64_t sv[4];
@@ -527,8 +535,6 @@ __global__ __launch_bounds__(kGuWaves * 64) void k_dec1_gateup(Dec1Params p)
                 }
                 __builtin_amdgcn_s_sleep(2);
             }
-#pragma unroll
-            for (int i = 0; i < 4; i++) bs[i] = __uint_as_float(bld4(rbs, (uint32_t)(wave * EQ + lane + 64 * i) * 4, 0));
             topk_candidates(E, k, wave, lg, bs, s_cand, s_score);
             flag_add(&s_ctl[2]);
             spin_until(&s_ctl[2], kTkWaves);
