@@ -771,8 +771,8 @@ __global__ __launch_bounds__(kGuWaves * 64) void k_dec1_gateup(Dec1Params p)
 // ------------------------------------------------------------ routed down + combine
 
 struct DnLoads {
-    uint4 c[2][kDnRows][2];   // [pick of the pair][row][block 2l, 2l + 1]
-    uint16_t sc[2][kDnRows];
+    uint4 c[2][kDnRows][2];   // [pick of the pair][row][block l, 64 + l]
+    uint32_t sc[2][kDnRows][2];
 };
 
 // SHC: 16-byte chunks per lane of a shared down row (ceil(F / 512))
@@ -788,11 +788,16 @@ __global__ __launch_bounds__(kDnWaves * 64) void k_dec1_down(Dec1Params p)
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int d = s.d, F = s.F, k = s.k;
     const int S = p.shared ? s.S : 0;
-    const int nbp = F / 64;
-    const int lp = lane < nbp ? lane : nbp - 1;
-    const float lmask = lane < nbp ? 1.0f : 0.0f;
+    // lane l holds MX blocks l and 64 + l of a W2 row (so that a row's code
+    // bytes come in two fully contiguous loads); a block past the row
+    // (F < 4096) is read past the resource, which returns zeros and reads
+    // nothing, and its H read is clamped to a real block
+    const int nb = F / 32;
+    constexpr uint32_t kPast = 0xF0000000u;  // a buffer offset past every resource
     const size_t qrow = (size_t)F / 2, srow = (size_t)F / 32;
-    const uint32_t voq = (uint32_t)lp * 32, vos = (uint32_t)lp * 2;
+    const uint32_t voq0 = lane < nb ? (uint32_t)lane * 16 : kPast, voq1 = lane + 64 < nb ? (uint32_t)(lane + 64) * 16 : kPast;
+    const uint32_t vos0 = lane < nb ? (uint32_t)lane : kPast, vos1 = lane + 64 < nb ? (uint32_t)(lane + 64) : kPast;
+    const int hb0 = min(lane, nb - 1), hb1 = min(lane + 64, nb - 1);
     const int n0 = blockIdx.x * kDnBlockRows + wave * kDnRows;
     // rows past d (last block) re-read row d - 1 and are not stored
     int rows[kDnRows];
@@ -847,9 +852,10 @@ __global__ __launch_bounds__(kDnWaves * 64) void k_dec1_down(Dec1Params p)
 #pragma unroll
             for (int r = 0; r < kDnRows; r++) {
                 const uint32_t so = (uint32_t)(rows[r] * qrow), ss = (uint32_t)(rows[r] * srow);
-                g.c[h][r][0] = bld16(rq, voq, so);
-                g.c[h][r][1] = bld16(rq, voq + 16, so);
-                g.sc[h][r] = bld2(rs, vos, ss);
+                g.c[h][r][0] = bld16(rq, voq0, so);
+                g.c[h][r][1] = bld16(rq, voq1, so);
+                g.sc[h][r][0] = bld1(rs, vos0, ss);
+                g.sc[h][r][1] = bld1(rs, vos1, ss);
             }
         }
     };
@@ -920,17 +926,19 @@ __global__ __launch_bounds__(kDnWaves * 64) void k_dec1_down(Dec1Params p)
             const bool use = j < k && s_e[jc] >= 0;
             const float wj = s_w[jc];
             uint32_t hr[32];
-            const uint4 *hs = reinterpret_cast<const uint4 *>(s_h + ((size_t)jc * F + (size_t)lp * 64) * 2);
+            const uint4 *hs0 = reinterpret_cast<const uint4 *>(s_h + ((size_t)jc * F + (size_t)hb0 * 32) * 2);
+            const uint4 *hs1 = reinterpret_cast<const uint4 *>(s_h + ((size_t)jc * F + (size_t)hb1 * 32) * 2);
 #pragma unroll
-            for (int i = 0; i < 8; i++) {
-                const uint4 v = hs[i];
+            for (int i = 0; i < 4; i++) {
+                const uint4 v = hs0[i], w = hs1[i];
                 hr[4 * i + 0] = v.x; hr[4 * i + 1] = v.y; hr[4 * i + 2] = v.z; hr[4 * i + 3] = v.w;
+                hr[16 + 4 * i + 0] = w.x; hr[16 + 4 * i + 1] = w.y; hr[16 + 4 * i + 2] = w.z; hr[16 + 4 * i + 3] = w.w;
             }
 #pragma unroll
             for (int r = 0; r < kDnRows; r++) {
                 const float a0 = fp4x32_dot_f16(g.c[h][r][0], hr);
                 const float a1 = fp4x32_dot_f16(g.c[h][r][1], hr + 16);
-                const float v = scaled2(a0, a1, g.sc[h][r]);
+                const float v = scaled2(a0, a1, (g.sc[h][r][0] & 0xFFu) | ((g.sc[h][r][1] & 0xFFu) << 8));
                 acc[r] = use ? fmaf(wj, v, acc[r]) : acc[r];
             }
         }
@@ -950,7 +958,7 @@ __global__ __launch_bounds__(kDnWaves * 64) void k_dec1_down(Dec1Params p)
 #pragma unroll
     for (int r = 0; r < kDnRows; r++) {
         // the weighted sum over the picks, then the shared experts' outputs
-        float v = wave_total(acc[r] * lmask) + ysh[r];
+        float v = wave_total(acc[r]) + ysh[r];
         if (fault) v = __builtin_nanf("");
         const int n = n0 + r;
         if (lane == 0 && n < d) {
