@@ -200,3 +200,18 @@ def test_one_token_control_block_not_zeroed():
     moe.layer(gl.desc, xd, 1, None, of, moe.OUT_F32, ws)
     torch.cuda.synchronize()
     assert np.array_equal(of.cpu().numpy(), ref_f), "zeroed again, the call must match"
+
+
+@pytest.mark.parametrize("name,shape,seed", [
+    # the widest rows the one-token path takes (d = F = 4096: the largest
+    # chunk counts per lane in both kernels, one shared row set in flight)
+    ("d4096 F4096 E64 k8 S2", S(64, 8, 2, 4096, 4096), 78),
+    # the most experts (every keying lane holds four) and the most picks
+    ("E1024 k16 S1 d128 F128", S(1024, 16, 1, 128, 128), 79),
+    ("E128 k64 S1 d256 F512", S(128, 64, 1, 256, 512), 80),
+])
+def test_one_token_limits(name, shape, seed):
+    log(f"case: one-token limits {name}")
+    gl = make_gpu_layer(shape, seed)
+    assert _is_one_token_path(gl)
+    _check_tokens_one_by_one(gl, 3)
