@@ -537,29 +537,63 @@ epilogue:
 
     // ---- epilogue (D lane layout: register e of tile (mt, nb) holds row
     // mt * 32 + 8 (e / 4) + 4 kh + e % 4, column nb * 32 + col of the wave's 64)
+    if constexpr (C::kGated) {
+        // the activations first, all of them and without a branch (one copy
+        // per activation, chosen once), so that the exp / rcp chains of
+        // different values interleave; then the stores of the rows in range
+        float hv[MT][16];
+        if (s.act == MOE_ACT_SWIGLU) {
+#pragma unroll
+            for (int mt = 0; mt < MT; mt++)
+#pragma unroll
+                for (int e = 0; e < 16; e++) hv[mt][e] = gated_act(acc[mt][0][e], acc[mt][1][e], MOE_ACT_SWIGLU, s.b1, s.b2);
+        } else {
+#pragma unroll
+            for (int mt = 0; mt < MT; mt++)
+#pragma unroll
+                for (int e = 0; e < 16; e++) hv[mt][e] = gated_act(acc[mt][0][e], acc[mt][1][e], MOE_ACT_SITU, s.b1, s.b2);
+        }
+        const int f = bk.tile * 128 + wave * 32 + col;
+#pragma unroll
+        for (int mt = 0; mt < MT; mt++) {
+#pragma unroll
+            for (int e = 0; e < 16; e++) {
+                const int r = mt * 32 + 8 * (e >> 2) + 4 * kh + (e & 3);
+                if (r >= mrows) continue;
+                const int m = m0 + r;
+                if constexpr (MODE == M_G13) {
+                    // (32-bit offsets: the host keeps T k F below 2^31)
+                    _Float16 *H = reinterpret_cast<_Float16 *>(p.w.H);
+                    H[(uint32_t)(bk.base + m) * (uint32_t)s.F + (uint32_t)f] = (_Float16)hv[mt][e];
+                } else {
+                    const uint16_t hi = f32_to_bf16_rne(hv[mt][e]);
+                    const uint16_t lo = f32_to_bf16_rne(hv[mt][e] - __uint_as_float((uint32_t)hi << 16));
+                    const size_t o = (size_t)m * s.S * s.F + (size_t)bk.group * s.F + f;
+                    p.hs_hi_w[o] = hi;
+                    p.hs_lo_w[o] = lo;
+                }
+            }
+        }
+        return;
+    }
+    // (down projection: lane i holds the routing weights of the pass's rows
+    // i and 64 + i, loaded once; a row's weight comes by a lane shuffle.
+    // Rows past the group read its last row's.)
+    float w_lo = 1.0f, w_hi = 1.0f;
+    if constexpr (MODE == M_D2) {
+        w_lo = p.w.pos_w[bk.base + m0 + min(lane, mrows - 1)];
+        if constexpr (MT > 2) w_hi = p.w.pos_w[bk.base + m0 + min(64 + lane, mrows - 1)];
+    }
 #pragma unroll
     for (int mt = 0; mt < MT; mt++) {
 #pragma unroll
         for (int e = 0; e < 16; e++) {
             const int r = mt * 32 + 8 * (e >> 2) + 4 * kh + (e & 3);
+            float wrow = 1.0f;
+            if constexpr (MODE == M_D2) wrow = mt < 2 ? __shfl(w_lo, r, 64) : __shfl(w_hi, r - 64, 64);
             if (r >= mrows) continue;
             const int m = m0 + r;
-            if constexpr (C::kGated) {
-                const int f = bk.tile * 128 + wave * 32 + col;
-                const float hv = gated_act(acc[mt][0][e], acc[mt][1][e], s.act, s.b1, s.b2);
-                if constexpr (MODE == M_G13) {
-                    _Float16 *H = reinterpret_cast<_Float16 *>(p.w.H);
-                    H[(size_t)(bk.base + m) * s.F + f] = (_Float16)hv;
-                } else {
-                    const uint16_t hi = f32_to_bf16_rne(hv);
-                    const uint16_t lo = f32_to_bf16_rne(hv - __uint_as_float((uint32_t)hi << 16));
-                    const size_t o = (size_t)m * s.S * s.F + (size_t)bk.group * s.F + f;
-                    p.hs_hi_w[o] = hi;
-                    p.hs_lo_w[o] = lo;
-                }
-            } else {
-                float wrow = 1.0f;
-                if constexpr (MODE == M_D2) wrow = p.w.pos_w[bk.base + m];
+            {
 #pragma unroll
                 for (int nb = 0; nb < 2; nb++) {
                     const int n = bk.tile * GN + wave * 64 + nb * 32 + col;
