@@ -184,7 +184,7 @@ def main():
     npool = max(1, min(args.pool, (1 << 16) // T))
     pools = [synth.x_tokens(shape, wl.seed, l, npool * T).reshape(npool, T, d) for l in range(L)]
     xs = [sdev.tokens_to_device(pools[l].reshape(npool * T, d)).view(npool, T, d) for l in range(L)]
-    ws = torch.zeros(moe.workspace_bytes(descs[0], T), dtype=torch.uint8, device="cuda")
+    ws = moe.workspace(descs[0], T)  # zero-filled (the control block must start at zero)
     outs = [torch.empty((T, d), dtype=torch.int16, device="cuda") for _ in range(L)]
     ids = torch.empty((T, shape.top_k), dtype=torch.int32, device="cuda")
     wts = torch.empty((T, shape.top_k), dtype=torch.float32, device="cuda")

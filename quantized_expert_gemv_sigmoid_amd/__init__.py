@@ -119,7 +119,19 @@ def status_str(status: int) -> str:
 
 
 def workspace_bytes(desc: LayerDesc, max_tokens: int) -> int:
+    """Bytes of workspace a call with up to max_tokens tokens needs.  Its first
+    WS_CONTROL_BYTES bytes must be zero before the workspace's first call
+    (every call leaves them zero): allocate it with workspace()."""
     return int(lib().moe_workspace_bytes(ctypes.byref(desc), max_tokens))
+
+
+def workspace(desc: LayerDesc, max_tokens: int, device="cuda"):
+    """A zero-filled workspace (uint8 tensor) for calls of up to max_tokens tokens."""
+    import torch
+    n = workspace_bytes(desc, max_tokens)
+    if n == 0:
+        raise MoeError(EINVAL, "moe_workspace_bytes: invalid or unsupported descriptor")
+    return torch.zeros(n, dtype=torch.uint8, device=device)
 
 
 def path_for(desc: LayerDesc, T: int) -> int:
