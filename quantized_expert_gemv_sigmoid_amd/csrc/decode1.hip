@@ -431,9 +431,11 @@ __global__ __launch_bounds__(kGuWaves * 64) void k_dec1_gateup(Dec1Params p)
 #pragma unroll
     for (int i = 0; i < kXRounds; i++) xv[i] = bld16(rx, (uint32_t)(st + i * kStThreads) * 16u, 0);
     // ---- shared experts' gate/up: unit u = si * F + f is feature f of
-    // shared expert si (its W1 and W3 rows times x) and writes Hs[u].  The
+    // shared expert si (its W1 and W3 rows times x); its activation goes to
+    // entry u of the shared activations (after the picks' fp16 H).  The
     // block owns units [sbeg, sbeg + nsloc), streamed by waves 4-7 from
-    // their queue (the first four at once, before the token is even in).
+    // their queue (the first four at once, once the block's router rows are
+    // in).
     // Lane l holds 16-byte chunks l + 64 c of both rows; chunks past the
     // row re-read its last chunk and meet zeros of the padded token.
     const int nsh = S * F;
@@ -471,7 +473,7 @@ __global__ __launch_bounds__(kGuWaves * 64) void k_dec1_gateup(Dec1Params p)
 
     // the queues and flags cleared: the one workgroup barrier before the
     // last (the loads above stay in flight; the shared queue starts past
-    // the four units already loaded)
+    // the four units that waves 4-7 take first)
     if (threadIdx.x < 7) s_ctl[threadIdx.x] = threadIdx.x == 1 ? kTkWaves * 64 : 0;
     lds_barrier();
 
