@@ -215,3 +215,33 @@ def test_one_token_limits(name, shape, seed):
     gl = make_gpu_layer(shape, seed)
     assert _is_one_token_path(gl)
     _check_tokens_one_by_one(gl, 3)
+
+
+def test_workspace_shared_across_paths():
+    """One workspace, sized for the largest call, serves one-token, GEMV and
+    MFMA calls in any order: the one-token path's control block stays zero
+    between calls, and every output equals that of a call with a fresh
+    workspace, bit for bit."""
+    import quantized_expert_gemv_sigmoid_amd as moe
+    import synth.device as sdev
+    shape = S(40, 6, 2, 512, 768)
+    gl = make_gpu_layer(shape, 81)
+    sizes = (1, 300, 1, 5, 1)
+    x, _, _ = tokens(gl, max(sizes), screened=False)
+    ws = moe.workspace(gl.desc, max(sizes))
+    for n, T in enumerate(sizes):
+        log(f"case: shared workspace, call {n}: T={T} path={moe.path_for(gl.desc, T)}")
+        xt = x[:T]
+        ref_f, ref_b, ref_ids, ref_w, ref_c = run_layer(gl, xt)
+        xd = sdev.tokens_to_device(xt)
+        of = torch.empty((T, shape.d_model), dtype=torch.float32, device="cuda")
+        ob = torch.empty((T, shape.d_model), dtype=torch.int16, device="cuda")
+        ids = torch.empty((T, shape.top_k), dtype=torch.int32, device="cuda")
+        w = torch.empty((T, shape.top_k), dtype=torch.float32, device="cuda")
+        c = torch.empty(shape.n_experts, dtype=torch.int32, device="cuda")
+        moe.layer(gl.desc, xd, T, ob, of, moe.OUT_BOTH, ws, ids=ids, weights=w, counts=c)
+        torch.cuda.synchronize()
+        assert np.array_equal(of.cpu().numpy(), ref_f), f"call {n} (T={T}): output differs"
+        assert np.array_equal(ob.cpu().numpy().view(np.uint16), ref_b)
+        assert np.array_equal(ids.cpu().numpy(), ref_ids) and np.array_equal(c.cpu().numpy(), ref_c)
+        assert not ws[:moe.WS_CONTROL_BYTES].any().item(), f"call {n}: control block left nonzero"
