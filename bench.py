@@ -293,7 +293,10 @@ def main():
         "ms_per_step_eager": round(eager_ms, 5),
         "step_hbm_gbs": round(layer_gbs, 1), "step_hbm_frac": round(layer_gbs / PEAK_HBM_GBS, 4),
         "step_tflops": round(L * flops(shape, T) / (ms * 1e-3) / 1e12, 3),
-        "phase_us": {p: round(v * 1e3, 2) for p, v in ph_ms.items()},
+        # (phases with no kernel of their own on this path, such as the router,
+        # top-k and combine of the fused one-token path, are null: the events
+        # around them measure only their own overhead)
+        "phase_us": {p: (round(v * 1e3, 2) if KERNELS[kind][p][0] != "-" else None) for p, v in ph_ms.items()},
         "roofline": roofline,
     }
     if not args.no_cpu_baseline:
