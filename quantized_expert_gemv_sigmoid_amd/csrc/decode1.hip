@@ -68,7 +68,10 @@ constexpr int kDnWaves = 7;             // waves per down block
 constexpr int kDnRows = 2;              // output rows per down wave
 constexpr int kDnBlockRows = kDnWaves * kDnRows;
 constexpr int kDnMaxLds = 152 * 1024;   // LDS bytes for the fp16 H of the picks + the fp32 shared H
-constexpr int kGuDynLds = 32 * 1024;    // unused LDS that keeps a second gate/up block off a CU
+constexpr int kGuPartBytes = kGuMaxBlockUnits * kGuMaxStages * 2 * kGuFeat * 4;  // gate/up partial sums
+// dynamic LDS of a gate/up block: the partial sums and the token, then
+// unused bytes that keep a second gate/up block off a CU
+constexpr int kGuDynLds = kGuPartBytes + kXPad * 2 + 32 * 1024;
 // control block of the workspace (zero between calls): one 8-byte slot per
 // router row, {logit bits (low word), kSlotTag (high word)} once the logit
 // is stored, then a sticky fault word on a line of its own
@@ -380,10 +383,11 @@ __global__ __launch_bounds__(kGuWaves * 64) void k_dec1_gateup(Dec1Params p)
     // the block's results, written out after its last unit (a global store
     // inside a unit loop would make the next register reuse wait for every
     // load in flight: stores and loads share one counter)
-    // per unit and K slice: the 16 gate and 16 up partial sums
-    __shared__ __attribute__((aligned(16))) float s_part[kGuMaxBlockUnits][kGuMaxStages][2 * kGuFeat];
-    // the token (bf16), zero-padded to whole work items
-    __shared__ __attribute__((aligned(16))) uint16_t s_xb[kXPad];
+    // per unit and K slice: the 16 gate and 16 up partial sums, then the
+    // token (bf16, zero-padded to whole work items), in the dynamic segment
+    extern __shared__ __attribute__((aligned(16))) uint8_t s_dyn[];
+    auto s_part = reinterpret_cast<float (*)[kGuMaxStages][2 * kGuFeat]>(s_dyn);
+    uint16_t *s_xb = reinterpret_cast<uint16_t *>(s_dyn + kGuPartBytes);
     __shared__ float s_hsh[kShMaxBlockUnits];  // shared activations of the block's units
     // [0], [1]: work queues (routed, shared); [2]: keying waves whose
     // candidates are written; [3]: picks ready; [4]: keying waves whose
@@ -777,14 +781,18 @@ struct DnLoads {
     uint32_t sc[2][kDnRows][2];
 };
 
-// SHC: 16-byte chunks per lane of a shared down row (ceil(F / 512))
-template <int SHC>
-__global__ __launch_bounds__(kDnWaves * 64) void k_dec1_down(Dec1Params p)
+// Rows [14 rblk, 14 rblk + 14) of the output: waves 0-6 own two rows each
+// (other waves of the block only stage and wait at the barrier).  s_h: LDS
+// for the fp16 H of the picks [k][F] and the fp32 shared activations [S][F];
+// s_e / s_w: the picks in ascending id (-1: none) and their weights.  The
+// rows' weight loads go out first; wait_h() then returns once H is written
+// (the gate/up kernel has ended, or every block of the fused kernel has
+// raised its flag); H is staged with agent-coherent loads when COHERENT.
+// SHC: 16-byte chunks per lane of a shared down row (ceil(F / 512)).
+template <int SHC, bool COHERENT, typename WaitH>
+__device__ __forceinline__ void dec1_down_rows(const Dec1Params &p, int rblk, uint8_t *s_h, const int *s_e,
+                                               const float *s_w, bool fault, WaitH &&wait_h)
 {
-    // fp16 H of the picks [k][F], then the fp32 shared activations [S][F]
-    extern __shared__ __attribute__((aligned(16))) uint8_t s_h[];
-    __shared__ int s_e[kMaxTopK];
-    __shared__ float s_w[kMaxTopK];
     const Shape &s = p.s;
     const int lane = threadIdx.x & 63;
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -800,25 +808,14 @@ __global__ __launch_bounds__(kDnWaves * 64) void k_dec1_down(Dec1Params p)
     const uint32_t voq0 = lane < nb ? (uint32_t)lane * 16 : kPast, voq1 = lane + 64 < nb ? (uint32_t)(lane + 64) * 16 : kPast;
     const uint32_t vos0 = lane < nb ? (uint32_t)lane : kPast, vos1 = lane + 64 < nb ? (uint32_t)(lane + 64) : kPast;
     const int hb0 = min(lane, nb - 1), hb1 = min(lane + 64, nb - 1);
-    const int n0 = blockIdx.x * kDnBlockRows + wave * kDnRows;
+    const bool row_wave = wave < kDnWaves;
+    const int n0 = rblk * kDnBlockRows + wave * kDnRows;
     // rows past d (last block) re-read row d - 1 and are not stored
     int rows[kDnRows];
 #pragma unroll
     for (int r = 0; r < kDnRows; r++) rows[r] = min(n0 + r, d - 1);
     const float *s_hs = reinterpret_cast<const float *>(s_h + (size_t)k * F * 2);
 
-    // the picks (ascending id, -1: none) and their weights, once
-    if (threadIdx.x < k) {
-        s_e[threadIdx.x] = p.w.active[threadIdx.x];
-        s_w[threadIdx.x] = p.w.pos_w[threadIdx.x];
-    }
-    // a router wait that timed out (control block not zeroed) poisons the output
-    const bool fault = __hip_atomic_load(p.w.ctl + kCtlFault, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) != 0;
-    // the router slots back to zero for the next call (the gate/up kernel,
-    // their only reader, has ended)
-    if (blockIdx.x == 0)
-        for (int e = threadIdx.x; e < s.E; e += kDnWaves * 64) reinterpret_cast<uint64_t *>(p.w.ctl)[e] = 0;
-    __syncthreads();
 
     // shared experts' down: the wave's rows of W2s[si] (bf16), lane l
     // holding 16-byte chunks l + 64 c; chunks past the row re-read its last
@@ -839,8 +836,8 @@ __global__ __launch_bounds__(kDnWaves * 64) void k_dec1_down(Dec1Params p)
     // registers of the one just multiplied
     constexpr int NSH = SHC <= 6 ? 2 : 1;
     uint4 shw[NSH][kDnRows][SHC];
-    if (S > 0) load_shd(shw[0], 0);
-    if (NSH > 1 && S > 1) load_shd(shw[NSH - 1], 1);
+    if (row_wave && S > 0) load_shd(shw[0], 0);
+    if (row_wave && NSH > 1 && S > 1) load_shd(shw[NSH - 1], 1);
 
     const int npair = (k + 1) / 2;
     // loads of pick pair q; past the end (or no pick) they re-read valid rows
@@ -863,25 +860,32 @@ __global__ __launch_bounds__(kDnWaves * 64) void k_dec1_down(Dec1Params p)
     };
 
     DnLoads ga, gb;
-    load(ga, 0);
+    if (row_wave) load(ga, 0);
+    wait_h();
     // stage the fp16 H of all picks (k * F * 2 bytes) and the shared
     // activations after it (S * F * 4 bytes), one contiguous region, into
     // LDS: every load of a round is issued before its stores
     {
         constexpr int NB = 16;
+        const int nt = (int)blockDim.x;
         const int n16 = (k * F * 2 + S * F * 4) / 16;
-        const uint4 *src = reinterpret_cast<const uint4 *>(p.w.H);
-        for (int i0 = 0; i0 < n16; i0 += NB * kDnWaves * 64) {
+        const auto rh = brsrc(p.w.H, (uint32_t)n16 * 16);
+        for (int i0 = 0; i0 < n16; i0 += NB * nt) {
             uint4 v[NB];
 #pragma unroll
-            for (int b = 0; b < NB; b++) v[b] = src[min(i0 + b * kDnWaves * 64 + (int)threadIdx.x, n16 - 1)];
+            for (int b = 0; b < NB; b++) {
+                const uint32_t i = (uint32_t)min(i0 + b * nt + (int)threadIdx.x, n16 - 1);
+                // (sc1: agent-coherent, for H written by other blocks of this kernel)
+                v[b] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(rh, (int)(i * 16), 0, COHERENT ? 16 : 0));
+            }
             // (indexes past the end store the last piece again, same value)
 #pragma unroll
             for (int b = 0; b < NB; b++)
-                *reinterpret_cast<uint4 *>(s_h + (size_t)min(i0 + b * kDnWaves * 64 + (int)threadIdx.x, n16 - 1) * 16) = v[b];
+                *reinterpret_cast<uint4 *>(s_h + (size_t)min(i0 + b * nt + (int)threadIdx.x, n16 - 1) * 16) = v[b];
         }
     }
     __syncthreads();
+    if (!row_wave) return;
 
     // the shared rows
     float ysh[kDnRows];
@@ -968,6 +972,30 @@ __global__ __launch_bounds__(kDnWaves * 64) void k_dec1_down(Dec1Params p)
             if (p.out_bf16) p.out_bf16[n] = f32_to_bf16_rne(v);
         }
     }
+}
+
+// SHC: 16-byte chunks per lane of a shared down row (ceil(F / 512))
+template <int SHC>
+__global__ __launch_bounds__(kDnWaves * 64) void k_dec1_down(Dec1Params p)
+{
+    // fp16 H of the picks [k][F], then the fp32 shared activations [S][F]
+    extern __shared__ __attribute__((aligned(16))) uint8_t s_h[];
+    __shared__ int s_e[kMaxTopK];
+    __shared__ float s_w[kMaxTopK];
+    // the picks (ascending id, -1: none) and their weights, once
+    if (threadIdx.x < p.s.k) {
+        s_e[threadIdx.x] = p.w.active[threadIdx.x];
+        s_w[threadIdx.x] = p.w.pos_w[threadIdx.x];
+    }
+    // a router wait that timed out (control block not zeroed) poisons the output
+    const bool fault = __hip_atomic_load(p.w.ctl + kCtlFault, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) != 0;
+    // the router slots back to zero for the next call (the gate/up kernel,
+    // their only reader, has ended)
+    if (blockIdx.x == 0)
+        for (int e = threadIdx.x; e < p.s.E; e += kDnWaves * 64) reinterpret_cast<uint64_t *>(p.w.ctl)[e] = 0;
+    __syncthreads();
+    // (H was written by the gate/up kernel, which has ended: nothing to wait for)
+    dec1_down_rows<SHC, false>(p, (int)blockIdx.x, s_h, s_e, s_w, fault, [] {});
 }
 
 // ---------------------------------------------------------------- host
