@@ -87,6 +87,35 @@ def test_route_then_forward_equals_layer():
         assert_close(of.cpu().numpy(), ref, f"no-shared T={T}")
 
 
+@pytest.mark.parametrize("T", [1, 3, 300])
+def test_route_then_forward_equals_layer_every_path(T):
+    """moe_route, then moe_expert_forward with its picks and the shared
+    experts, equals moe_layer bit for bit on each path: the one-token kernels
+    (T = 1), the GEMV path (T = 3) and the grouped MFMA GEMM (T = 300; d and F
+    multiples of 256)."""
+    import quantized_expert_gemv_sigmoid_amd as moe
+    import synth.device as sdev
+    shape = synth.LayerShape(n_experts=40, top_k=6, n_shared=2, d_model=512, d_ffn=768)
+    gl = make_gpu_layer(shape, 8)
+    log(f"case: route+forward vs layer T={T} path={moe.path_for(gl.desc, T)}")
+    x, _, _ = tokens(gl, T, screened=False)
+    out_f, out_b, ids, w, cnt = run_layer(gl, x)
+    xd = sdev.tokens_to_device(x)
+    ids2 = torch.empty((T, 6), dtype=torch.int32, device="cuda")
+    w2 = torch.empty((T, 6), dtype=torch.float32, device="cuda")
+    c2 = torch.empty(40, dtype=torch.int32, device="cuda")
+    ws = moe.workspace(gl.desc, T)
+    moe.route(gl.desc, xd, T, ids2, w2, c2, ws)
+    of = torch.empty((T, 512), dtype=torch.float32, device="cuda")
+    ob = torch.empty((T, 512), dtype=torch.int16, device="cuda")
+    moe.expert_forward(gl.desc, xd, T, ids2, w2, 1, ob, of, moe.OUT_BOTH, ws)
+    torch.cuda.synchronize()
+    assert np.array_equal(ids2.cpu().numpy(), ids) and np.array_equal(w2.cpu().numpy(), w)
+    assert np.array_equal(c2.cpu().numpy(), cnt)
+    assert np.array_equal(of.cpu().numpy(), out_f), "route + expert_forward differs from layer"
+    assert np.array_equal(ob.cpu().numpy().view(np.uint16), out_b)
+
+
 @pytest.mark.parametrize("T", [1, 5, 37, 64, 65, 130])
 def test_ragged_shapes(T):
     # d = 320 -> 10 MX blocks per row (lanes partly idle); F = 416 -> 13 blocks;
