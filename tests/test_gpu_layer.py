@@ -350,3 +350,43 @@ def test_mfma_down_projection_mixed_blocks():
     other[400] = False
     assert_close(out_f[:, other], rout[:, other], "columns other than 400")
     assert_close(out_f[:, 400:401], rout[:, 400:401], "column 400 (scale byte 141)")
+
+
+def test_stacked_layers_in_one_graph():
+    """The 12-layer workload's mechanics at a smaller shape: independent
+    layers (own weights, own tokens, one Zipf selection bias) run one after
+    another on one stream with one workspace, captured in one HIP graph per
+    token set; every replay of every set gives, for every layer, the eager
+    result, which matches the oracle."""
+    import quantized_expert_gemv_sigmoid_amd as moe
+    import synth.device as sdev
+    shape = synth.LayerShape(n_experts=64, top_k=8, n_shared=2, d_model=1024, d_ffn=1024)
+    L, NSET, seed = 3, 4, 91
+    layers = [make_gpu_layer(shape, seed, layer=l, zipf=True) for l in range(L)]
+    xs, refs = [], []
+    for l, gl in enumerate(layers):
+        x, rw, bias = tokens(gl, NSET)  # token set i of layer l is x[i]
+        ref_f, _, _, _, _ = zip(*[run_layer(gl, x[i:i + 1]) for i in range(NSET)])
+        rids, rw_, _, rout = oracle_outputs(gl, x, rw, bias, np.arange(NSET))
+        for i in range(NSET):
+            assert_close(ref_f[i], rout[i:i + 1], f"layer {l} set {i}")
+        xs.append([sdev.tokens_to_device(x[i:i + 1]) for i in range(NSET)])
+        refs.append(ref_f)
+    ws = moe.workspace(layers[0].desc, 1)
+    outs = [torch.empty((1, shape.d_model), dtype=torch.float32, device="cuda") for _ in range(L)]
+    graphs = []
+    for i in range(NSET):
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            for l in range(L):
+                moe.layer(layers[l].desc, xs[l][i], 1, None, outs[l], moe.OUT_F32, ws)
+        graphs.append(g)
+    torch.cuda.synchronize()
+    for rep in range(2 * NSET):
+        i = rep % NSET
+        log(f"case: stacked graph replay {rep} (set {i})")
+        graphs[i].replay()
+        torch.cuda.synchronize()
+        for l in range(L):
+            assert np.array_equal(outs[l].cpu().numpy(), refs[l][i]), f"replay {rep}: layer {l} differs"
+    assert not ws[:moe.WS_CONTROL_BYTES].any().item(), "control block left nonzero"
