@@ -86,12 +86,16 @@ __device__ __forceinline__ void lds_st16(LDS uint8_t *p, uint4 v)
 __device__ __forceinline__ void lds_st4(LDS uint8_t *p, uint32_t v) { *reinterpret_cast<LDS uint32_t *>(p) = v; }
 
 
-// element offset of 16-byte piece q of row r in an LDS stage of KC columns
+// element offset of 16-byte piece q of row r in an LDS stage of KC columns.
+// A fragment read takes one piece of 16 consecutive rows per 16 lanes, and
+// the LDS serves 256 bytes (16 pieces' worth of banks) at a time: 256-byte
+// rows XOR the piece with r & 15; 128-byte rows (two per 256 bytes) with
+// (r >> 1) & 7, so that rows r and r + 8 do not share banks.
 template <int KC>
 __device__ __forceinline__ int lds_off(int r, int q)
 {
     if constexpr (KC == 128) return r * KC + ((q ^ (r & 15)) << 3);
-    else return r * KC + ((q ^ (r & 7)) << 3);
+    else return r * KC + ((q ^ ((r >> 1) & 7)) << 3);
 }
 
 __device__ __forceinline__ float e8m0f(uint32_t b)
@@ -140,9 +144,9 @@ struct Cfg {
 // elements) is kh * STEPS + st.
 
 // byte offset of 16-byte piece p of column c inside a B stage (8 pieces per
-// column, XOR-swizzled so the fragment reads of 8 consecutive columns hit
-// distinct banks)
-__device__ __forceinline__ int b_off(int c, int p) { return c * 128 + ((p ^ (c & 7)) << 4); }
+// column, XOR-swizzled with (c >> 1) & 7 so that the fragment reads of 16
+// consecutive columns, two per 256 bytes, hit distinct banks)
+__device__ __forceinline__ int b_off(int c, int p) { return c * 128 + ((p ^ ((c >> 1) & 7)) << 4); }
 
 
 __device__ __forceinline__ f32x16_t mfma32(bf16x8_t a, bf16x8_t b, f32x16_t c)
