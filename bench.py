@@ -133,6 +133,24 @@ def cpu_baseline(shape, seed, zipf, pools, budget_s):
                       f"shared expert FFNs each), {spent:.1f} s of oracle time"}
 
 
+def copy_gbs(torch, nbytes: int, reps: int) -> float:
+    """Bytes read plus bytes written per second of a plain device copy."""
+    src = torch.ones(nbytes, dtype=torch.uint8, device="cuda")
+    dst = torch.empty_like(src)
+    dst.copy_(src)  # (first touch)
+    torch.cuda.synchronize()
+    t0, t1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    t0.record()
+    for _ in range(reps):
+        dst.copy_(src)
+    t1.record()
+    t1.synchronize()
+    ms = t0.elapsed_time(t1) / reps
+    del src, dst
+    torch.cuda.empty_cache()
+    return 2 * nbytes / (ms * 1e-3) / 1e9
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -156,14 +174,14 @@ def main():
 
     import torch
     if args.copy_mib:
-        n = args.copy_mib << 20
-        src = torch.ones(n, dtype=torch.uint8, device="cuda")
-        dst = torch.empty_like(src)
-        for _ in range(args.steps):
-            dst.copy_(src)
-        torch.cuda.synchronize()
-        print(json.dumps({"copy_bytes": n, "steps": args.steps}), flush=True)
+        gbs = copy_gbs(torch, args.copy_mib << 20, args.steps)
+        print(json.dumps({"copy_bytes": args.copy_mib << 20, "steps": args.steps, "copy_gbs": round(gbs, 1)}),
+              flush=True)
         return
+    # a plain device copy of 1 GiB (four times the last-level cache), read and
+    # written bytes over its time: the HBM rate an ordinary kernel reaches on
+    # this GPU, reported beside the published peak
+    hbm_copy_gbs = copy_gbs(torch, 1 << 30, 20)
     import synth
     import synth.device as sdev
     import quantized_expert_gemv_sigmoid_amd as moe
@@ -275,7 +293,8 @@ def main():
                     "frac": round(achieved / PEAK_HBM_GBS, 4),
                     "traffic": MEASURED_TRAFFIC.get(KERNELS[kind][dom].split()[0]) if kind == "decode1" else None,
                     "kernel": KERNELS[kind][dom], "bytes_per_launch": int(ph_bytes[dom]),
-                    "avg_launch_us": round(ph_ms[dom] * 1e3, 2)}
+                    "avg_launch_us": round(ph_ms[dom] * 1e3, 2),
+                    "frac_of_copy": round(achieved / hbm_copy_gbs, 4)}
     tok_s = T / (ms * 1e-3)
     layer_gbs = step_bytes / (ms * 1e-3) / 1e9
     config = {"workload": wl.name, "n_experts": shape.n_experts, "top_k": shape.top_k,
@@ -292,6 +311,7 @@ def main():
         "config": config,
         "ms_per_step_eager": round(eager_ms, 5),
         "step_hbm_gbs": round(layer_gbs, 1), "step_hbm_frac": round(layer_gbs / PEAK_HBM_GBS, 4),
+        "hbm_copy_gbs": round(hbm_copy_gbs, 1), "step_frac_of_copy": round(layer_gbs / hbm_copy_gbs, 4),
         "step_tflops": round(L * flops(shape, T) / (ms * 1e-3) / 1e12, 3),
         # (phases with no kernel of their own on this path, such as the router,
         # top-k and combine of the fused one-token path, are null: the events
