@@ -166,6 +166,9 @@ def main():
     ap.add_argument("--copy-mib", type=int, default=0,
                     help="only run a plain device copy of this many MiB, --steps times (the known-size "
                          "kernel that scales the FETCH_SIZE / WRITE_SIZE counters)")
+    ap.add_argument("--mv-mib", type=int, default=0,
+                    help="only time the library's bf16 matrix-vector product (torch.mv) over a matrix of this "
+                         "many MiB, --steps times: a read-only weight stream for reference")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py measures one GPU: this layer's path is built and measured on a single "
@@ -177,6 +180,23 @@ def main():
         gbs = copy_gbs(torch, args.copy_mib << 20, args.steps)
         print(json.dumps({"copy_bytes": args.copy_mib << 20, "steps": args.steps, "copy_gbs": round(gbs, 1)}),
               flush=True)
+        return
+    if args.mv_mib:
+        cols = 16384
+        rows = (args.mv_mib << 20) // (2 * cols)
+        A = torch.randn(rows, cols, dtype=torch.bfloat16, device="cuda")
+        v = torch.randn(cols, dtype=torch.bfloat16, device="cuda")
+        torch.mv(A, v)
+        torch.cuda.synchronize()
+        t0, t1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        t0.record()
+        for _ in range(args.steps):
+            torch.mv(A, v)
+        t1.record()
+        t1.synchronize()
+        ms = t0.elapsed_time(t1) / args.steps
+        print(json.dumps({"mv_matrix_bytes": rows * cols * 2, "steps": args.steps,
+                          "mv_read_gbs": round(rows * cols * 2 / (ms * 1e-3) / 1e9, 1)}), flush=True)
         return
     # a plain device copy of 1 GiB (four times the last-level cache), read and
     # written bytes over its time: the HBM rate an ordinary kernel reaches on
