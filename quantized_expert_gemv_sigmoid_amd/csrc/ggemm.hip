@@ -103,6 +103,28 @@ __device__ __forceinline__ float e8m0f(uint32_t b)
     return __uint_as_float(b == 0 ? 0x00400000u : (b << 23));
 }
 
+// SiTU-GLU of one (gate, up) pair for the GEMM epilogues (kimi-k3-in-c
+// section 9, k3_situ_glu; betas b1, b2).  With e1 = exp(-2|g|/b1),
+// e2 = exp(-g) and e3 = exp(-2|u|/b2):
+//   b1 tanh(g/b1) sigmoid(g) b2 tanh(u/b2)
+//     = sign(g u) b1 b2 (1 - e1)(1 - e3) / ((1 + e1)(1 + e2)(1 + e3)),
+// one reciprocal for the whole product.  k1 = -2 log2(e) / b1,
+// k3 = -2 log2(e) / b2, b12 = b1 b2.  For small |g| / b1 or |u| / b2 the
+// 1 - e terms cancel: the absolute error that leaves in h is a few 2^-24
+// times b1 b2 / 4, below half an ulp of the fp16 H it is stored in for any
+// |h| above 1e-2, and negligible against the output.  For g << 0, 1 + e2 is
+// inf and h is 0, as sigmoid(g) is.
+__device__ __forceinline__ float situ_gemm(float g, float u, float k1, float k3, float b12)
+{
+    const float e1 = __builtin_amdgcn_exp2f(k1 * fabsf(g));
+    const float e2 = __builtin_amdgcn_exp2f(-1.44269504088896341f * g);
+    const float e3 = __builtin_amdgcn_exp2f(k3 * fabsf(u));
+    const float num = (b12 * (1.0f - e1)) * (1.0f - e3);
+    const float den = ((1.0f + e1) * (1.0f + e2)) * (1.0f + e3);
+    const float m = num * __builtin_amdgcn_rcpf(den);
+    return __uint_as_float(__float_as_uint(m) ^ ((__float_as_uint(g) ^ __float_as_uint(u)) & 0x80000000u));
+}
+
 // fp16 x8 -> (hi, lo) bf16 x8 with hi + lo == value exactly
 __device__ __forceinline__ void split_f16(const f16x8_t a, bf16x8_t &hi, bf16x8_t &lo)
 {
@@ -552,10 +574,12 @@ epilogue:
 #pragma unroll
                 for (int e = 0; e < 16; e++) hv[mt][e] = gated_act(acc[mt][0][e], acc[mt][1][e], MOE_ACT_SWIGLU, s.b1, s.b2);
         } else {
+            const float k1 = -2.0f * 1.44269504088896341f / s.b1, k3 = -2.0f * 1.44269504088896341f / s.b2;
+            const float b12 = s.b1 * s.b2;
 #pragma unroll
             for (int mt = 0; mt < MT; mt++)
 #pragma unroll
-                for (int e = 0; e < 16; e++) hv[mt][e] = gated_act(acc[mt][0][e], acc[mt][1][e], MOE_ACT_SITU, s.b1, s.b2);
+                for (int e = 0; e < 16; e++) hv[mt][e] = situ_gemm(acc[mt][0][e], acc[mt][1][e], k1, k3, b12);
         }
         const int f = bk.tile * 128 + wave * 32 + col;
 #pragma unroll
