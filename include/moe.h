@@ -20,7 +20,8 @@
  *
  * Conventions (every call):
  *  - All pointers are DEVICE pointers owned by the caller; the library
- *    allocates nothing, keeps no state of its own between calls and never
+ *    allocates nothing, keeps no state of its own between calls (apart from
+ *    the one setting of moe_set_one_token_router_wait) and never
  *    synchronises the host.  Work is enqueued on `stream` (a hipStream_t; NULL = the null
  *    stream) and may be captured into a HIP graph (no memset, no allocation).
  *  - Arguments are validated before anything is launched; on any error
@@ -52,11 +53,22 @@ typedef enum { MOE_ACT_SITU = 0, MOE_ACT_SWIGLU = 1 } moe_act;
 typedef enum { MOE_OUT_BF16 = 0, MOE_OUT_F32 = 1, MOE_OUT_BOTH = 2 } moe_out_mode;
 
 /* which expert kernels run: AUTO picks the dequant-fused GEMV for up to 24
- * tokens and the grouped MFMA GEMM above (moe_path_for reports it).
- * The MFMA path needs d and F to be multiples of 256 and every activation
- * operand below 2 GiB (T*k*F, T*d and T*S*F two-byte values); AUTO falls
- * back to GEMV outside that range, an explicit MOE_PATH_MFMA call returns
- * MOE_EUNSUPPORTED. */
+ * tokens and the grouped MFMA GEMM above (moe_path_for reports it); one
+ * token on the GEMV path takes fused one-token kernels where their limits
+ * allow (SiTU with b1*b2 <= 65504 among them).
+ * The MFMA path needs d and F to be multiples of 256, every activation
+ * operand below 2 GiB (T*k*F, T*d and T*S*F two-byte values) and, under
+ * SiTU, b1*b2 <= 65504; AUTO falls back to GEMV outside that range, and an
+ * explicit MOE_PATH_MFMA call returns MOE_EUNSUPPORTED.
+ *
+ * Precision of the activation H = act(g, u) between the gate/up and the down
+ * products: the GEMV path keeps it in fp32; the one-token kernels and the
+ * MFMA path store it in fp16 (relative rounding 2^-11).  SiTU bounds |h| by
+ * b1*b2, which is why those two paths need b1*b2 <= 65504 (the largest
+ * fp16).  SwiGLU is unbounded: the one-token kernels never take it, and on
+ * the MFMA path an |h| above 65504 becomes inf in H, so that token's outputs
+ * come out inf or NaN (never a finite wrong value); MOE_PATH_GEMV keeps such
+ * layers finite at any T. */
 typedef enum { MOE_PATH_AUTO = 0, MOE_PATH_GEMV = 1, MOE_PATH_MFMA = 2 } moe_path;
 
 /*
@@ -91,19 +103,15 @@ typedef struct {
 
 /* Workspace bytes a call with up to max_tokens tokens needs (0 if the
  * descriptor is invalid or unsupported).  Pass a buffer of at least this
- * size, 256-byte aligned, to the calls below.
- *
- * The first MOE_WS_CONTROL_BYTES bytes of a workspace are a control block
- * (the router logits that the blocks of the one-token path hand to each
- * other, each with a ready tag) and must be ZERO before the first call that
- * uses the workspace: a hipMemsetAsync of those bytes, or allocating the
- * workspace zero-filled, does it.  Every call leaves them zero again, so
- * zeroing once per workspace is enough.  A control block that was not
- * zeroed is detected (a tag that no call writes); the call then writes NaN
- * outputs, and so does every later call on that workspace until the block
- * is zeroed again. */
+ * size, 256-byte aligned, to the calls below.  Its contents need no
+ * initialisation and carry nothing a caller reads.  (The one-token kernels
+ * hand the router logits between their blocks through slots at the start of
+ * the workspace, each tagged with the call's epoch, a counter kept there
+ * that every call advances; a slot counts only with the running call's tag.
+ * Slots earlier calls left never carry it, and other contents carry it only
+ * by a coincidence of 1 in 2^32 per slot, so the workspace may start with
+ * any bytes.) */
 size_t moe_workspace_bytes(const moe_layer_desc *desc, int32_t max_tokens);
-#define MOE_WS_CONTROL_BYTES 9216
 
 /* The expert path (MOE_PATH_GEMV or MOE_PATH_MFMA) a call with T tokens
  * takes; a negative moe_status if desc is invalid. */
@@ -122,7 +130,10 @@ moe_status moe_route(const moe_layer_desc *desc, const uint16_t *x, int32_t T,
 
 /*
  * Experts for a given routing (ids/weights as moe_route writes them).
- * Ids must be distinct within a token; an id outside [0, E) drops that term.
+ * An id outside [0, E) drops that term.  An id given more than once in a
+ * token's row (moe_route never does that) adds each of its terms: the layer
+ * runs that expert once for the token, with the weights of its slots summed
+ * in slot order, since w1*FFN_e(x) + w2*FFN_e(x) = (w1 + w2)*FFN_e(x).
  * include_shared: 1 adds the shared experts, 0 leaves them out.
  * out_mode picks the outputs: out_bf16 [T][d] bf16 bits (round to nearest
  * even of the fp32 result) and/or out_f32 [T][d] fp32; the one not asked
@@ -157,6 +168,14 @@ moe_status moe_layer(const moe_layer_desc *desc, const uint16_t *x, int32_t T,
 moe_status moe_layer_timed(const moe_layer_desc *desc, const uint16_t *x, int32_t T,
                            uint16_t *out_bf16, float *out_f32, int32_t out_mode,
                            void *ws, size_t ws_bytes, void *stream, void *const *events);
+
+/* The one-token kernels' router hand-off: a block that has waited this many
+ * microseconds for router logits other blocks compute (default 50) computes
+ * the missing ones itself, the same sums, so the same bits; no wait depends
+ * on another block being resident.  Process-wide; it applies to calls
+ * enqueued after it returns (a captured graph keeps the value it was
+ * captured with).  MOE_EINVAL for a negative value. */
+moe_status moe_set_one_token_router_wait(int32_t microseconds);
 
 /* Static text for a status code. */
 const char *moe_status_str(int32_t status);

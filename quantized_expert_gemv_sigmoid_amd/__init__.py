@@ -23,11 +23,8 @@ OUT_BF16, OUT_F32, OUT_BOTH = 0, 1, 2
 PATH_AUTO, PATH_GEMV, PATH_MFMA = 0, 1, 2
 
 EXPORTS = ("moe_workspace_bytes", "moe_path_for", "moe_route", "moe_expert_forward",
-           "moe_layer", "moe_layer_timed", "moe_status_str")
+           "moe_layer", "moe_layer_timed", "moe_set_one_token_router_wait", "moe_status_str")
 TIMED_EVENTS = 6
-# leading workspace bytes that must be zero before a workspace's first call
-# (MOE_WS_CONTROL_BYTES in include/moe.h); every call leaves them zero
-WS_CONTROL_BYTES = 9216
 
 
 class MoeError(RuntimeError):
@@ -77,6 +74,8 @@ def lib() -> ctypes.CDLL:
         L.moe_layer.argtypes = [P, vp, i32, vp, vp, i32, vp, vp, vp, vp, sz, vp]
         L.moe_layer_timed.restype = i32
         L.moe_layer_timed.argtypes = [P, vp, i32, vp, vp, i32, vp, sz, vp, ctypes.POINTER(vp)]
+        L.moe_set_one_token_router_wait.restype = i32
+        L.moe_set_one_token_router_wait.argtypes = [i32]
         L.moe_status_str.restype = ctypes.c_char_p
         L.moe_status_str.argtypes = [i32]
         _lib = L
@@ -119,19 +118,22 @@ def status_str(status: int) -> str:
 
 
 def workspace_bytes(desc: LayerDesc, max_tokens: int) -> int:
-    """Bytes of workspace a call with up to max_tokens tokens needs.  Its first
-    WS_CONTROL_BYTES bytes must be zero before the workspace's first call
-    (every call leaves them zero): allocate it with workspace()."""
+    """Bytes of workspace a call with up to max_tokens tokens needs (its
+    contents need no initialisation)."""
     return int(lib().moe_workspace_bytes(ctypes.byref(desc), max_tokens))
 
 
 def workspace(desc: LayerDesc, max_tokens: int, device="cuda"):
-    """A zero-filled workspace (uint8 tensor) for calls of up to max_tokens tokens."""
+    """An uninitialised workspace (uint8 tensor) for calls of up to max_tokens tokens."""
     import torch
     n = workspace_bytes(desc, max_tokens)
     if n == 0:
         raise MoeError(EINVAL, "moe_workspace_bytes: invalid or unsupported descriptor")
-    return torch.zeros(n, dtype=torch.uint8, device=device)
+    return torch.empty(n, dtype=torch.uint8, device=device)
+
+
+def set_one_token_router_wait(microseconds: int) -> None:
+    _check(lib().moe_set_one_token_router_wait(int(microseconds)), "moe_set_one_token_router_wait")
 
 
 def path_for(desc: LayerDesc, T: int) -> int:

@@ -18,12 +18,12 @@ constexpr int kMaxExperts = 1024;  // router top-k keeps E/64 scores per lane
 constexpr int kMaxTopK = 64;
 constexpr int kMaxDim = 4096;      // d and F: GEMV lanes hold <= 2 MXFP4 blocks
 constexpr int kMaxShared = 8;
-constexpr size_t kWsControlBytes = 9 * 1024;  // workspace bytes [0, this): the control block
+constexpr size_t kWsControlBytes = 9 * 1024;  // workspace bytes [0, this): the one-token control block
 constexpr int kDispatchTokens = 64;  // tokens per dispatch block (one 64-bit mask)
 
 // Device views of the workspace of one call (see carve_workspace).
 struct Work {
-    int32_t *ctl;      // control block of the one-token path (kWsControlBytes, zero between calls)
+    int32_t *ctl;      // control block of the one-token path (kWsControlBytes: router slots, epoch)
     float *logits;     // [T][E]  router logits
     int32_t *ids;      // [T][k]  routing (when the caller passed none)
     float *wts;        // [T][k]
@@ -52,6 +52,16 @@ struct Shape {
     int renorm;
     float routed_scale;
 };
+
+// The one-token and MFMA paths store the activation H in fp16.  SiTU bounds
+// |h| by b1 * b2, so with b1 * b2 <= 65504 (the largest fp16) every H is in
+// range; larger betas take the fp32-H GEMV kernels.  SwiGLU is unbounded:
+// the one-token path does not take it, the MFMA path does (the limit is
+// stated in moe.h).
+inline bool situ_h_fits_f16(const Shape &s)
+{
+    return s.act != 0 || (double)s.b1 * (double)s.b2 <= 65504.0;
+}
 
 // ------------------------------------------------------------------ helpers
 
@@ -311,6 +321,10 @@ hipError_t launch_mfma_experts(const Shape &s, const uint16_t *x, const Weights 
 //                 + sum over shared experts of Ysh[s][t]
 hipError_t launch_combine(const Shape &s, int include_shared, const Work &w, uint16_t *out_bf16,
                           float *out_f32, hipStream_t stream);
+
+// wait (us) of the one-token path's router waiters before they compute
+// missing router rows themselves (process-wide)
+void set_router_wait_us(uint32_t us);
 
 // fused one-token decode after launch_front: top-k (do_topk) or the given
 // ids / weights, routed gate/up (+ shared down), routed down + combine into

@@ -18,8 +18,9 @@
 // the down kernel accumulates in registers.
 //
 // The logits pass between the blocks of the gate/up kernel through slots in
-// the workspace's control block (see slot_store); the down kernel returns
-// them to zero for the next call.
+// the workspace's control block, tagged with the call's epoch (see
+// slot_store); the down kernel advances the epoch for the next call, so the
+// block needs no initialisation and nothing has to be cleared.
 //
 // Weight streaming (kimi-k3-in-c section 4: MXFP4 = E2M1 codes two per byte,
 // low nibble first, one E8M0 scale per 32 weights): a row is spread over the
@@ -28,7 +29,7 @@
 // (the next unit is issued before the current one is multiplied); the lane's
 // 64 inputs stay in registers (gate/up) or are read from LDS (down: the fp16
 // H of all picks, staged once per block).
-#include <stdlib.h>
+#include <atomic>
 
 #include "common.h"
 #include "router_dev.h"
@@ -72,13 +73,15 @@ constexpr int kGuPartBytes = kGuMaxBlockUnits * kGuMaxStages * 2 * kGuFeat * 4; 
 // dynamic LDS of a gate/up block: the partial sums and the token, then
 // unused bytes that keep a second gate/up block off a CU
 constexpr int kGuDynLds = kGuPartBytes + kXPad * 2 + 32 * 1024;
-// control block of the workspace (zero between calls): one 8-byte slot per
-// router row, {logit bits (low word), kSlotTag (high word)} once the logit
-// is stored, then a sticky fault word on a line of its own
-constexpr uint32_t kSlotTag = 0x4C4F4749u;  // any other nonzero high word: the block was not zeroed
-constexpr int kCtlFault = 2 * kMaxExperts + 64;  // int32 index
-constexpr uint64_t kHelpTicks = 5000;   // 50 us of the 100 MHz counter; then a waiter computes missing rows
-                                        // (MOE_ONE_TOKEN_HELP_US in the environment overrides it)
+// control block of the workspace: one 8-byte slot per router row, {logit
+// bits (low word), tag (high word)}, then the epoch word on a line of its
+// own.  A call reads the epoch n and stores every logit with the tag of
+// epoch n + 1 (slot_tag); its down kernel then writes n + 1.  A slot counts
+// as stored once it holds the tag of the running call: left-over tags of
+// earlier calls never match it, and whatever the block held before its
+// first call (it is never cleared) matches only by a 32-bit coincidence.
+constexpr int kCtlEpoch = 2 * kMaxExperts + 64;  // int32 index
+constexpr uint32_t kHelpUsDefault = 50;  // wait (us) before a waiter computes missing router rows itself
 
 __device__ __forceinline__ uint4 gl16(const void *p) { return *reinterpret_cast<const uint4 *>(p); }
 
@@ -317,20 +320,24 @@ __device__ __forceinline__ int grab(uint32_t lds_addr)
 
 // Router logits between the blocks of the gate/up kernel.  Block b's
 // keying waves compute router rows 4b .. 4b + 3 and publish each as one
-// 8-byte slot {logit, tag}, stored agent-coherent (written through to the
-// level all XCDs share); a waiter reads the slots of its experts with
-// agent-coherent loads, which is its poll and its logits load at once.  A
-// waiter that has waited past kHelpTicks computes the rows still missing
-// itself (the same sums, so the same bits), so no wait depends on another
-// block being resident.  No counter and no cache-wide fence is needed.
-__device__ __forceinline__ void ctl_set(int *ctl, int w, int v)
+// 8-byte slot {logit, tag of this call's epoch}, stored agent-coherent
+// (written through to the level all XCDs share); a waiter reads the slots of
+// its experts with agent-coherent loads, which is its poll and its logits
+// load at once.  A waiter that has waited past help_ticks computes the rows
+// still missing itself (the same sums, so the same bits), so no wait depends
+// on another block being resident.  No counter and no cache-wide fence is
+// needed.
+// the tag of router row e in epoch ep: distinct epochs give distinct tags
+// for every row (a multiplication by an odd constant is a bijection)
+__device__ __forceinline__ uint32_t slot_tag(uint32_t ep, int e)
 {
-    __hip_atomic_store(ctl + w, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    return (ep * 0x9E3779B1u) ^ (uint32_t)e;
 }
-__device__ __forceinline__ void slot_store(int *ctl, int e, float v)
+__device__ __forceinline__ void slot_store(int *ctl, int e, float v, uint32_t ep)
 {
-    __hip_atomic_store(reinterpret_cast<uint64_t *>(ctl) + e, ((uint64_t)kSlotTag << 32) | __float_as_uint(v),
-                       __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    __hip_atomic_store(reinterpret_cast<uint64_t *>(ctl) + e,
+                       ((uint64_t)slot_tag(ep, e) << 32) | __float_as_uint(v), __ATOMIC_RELAXED,
+                       __HIP_MEMORY_SCOPE_AGENT);
 }
 __device__ __forceinline__ uint64_t slot_load(const int *ctl, int e)
 {
@@ -401,6 +408,8 @@ __global__ __launch_bounds__(kGuWaves * 64) void k_dec1_gateup(Dec1Params p)
     const int d = s.d, F = s.F, E = s.E, k = s.k;
     const int S = p.shared ? s.S : 0;
     int *ctl = p.w.ctl;
+    // this call's epoch (the previous call's down kernel wrote the one before)
+    const uint32_t ep = (uint32_t)__hip_atomic_load(ctl + kCtlEpoch, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) + 1u;
 
     // ---- the router row of a keying wave (4 blockIdx + wave), loaded first
     const int rrow = (int)blockIdx.x * kTkWaves + wave;
@@ -495,7 +504,7 @@ __global__ __launch_bounds__(kGuWaves * 64) void k_dec1_gateup(Dec1Params p)
             if (own_row) {
                 const float v = router_dot(rw, s_xb);
                 flag_add(&s_ctl[6]);
-                if (lane == 0) slot_store(ctl, rrow, v);
+                if (lane == 0) slot_store(ctl, rrow, v, ep);
             } else {
                 flag_add(&s_ctl[6]);
             }
@@ -505,29 +514,27 @@ __global__ __launch_bounds__(kGuWaves * 64) void k_dec1_gateup(Dec1Params p)
             const uint64_t t0 = __builtin_amdgcn_s_memrealtime();
             for (;;) {
                 uint64_t sv[4];
+                bool miss[4];
 #pragma unroll
                 for (int i = 0; i < 4; i++) {
                     const int e = wave * EQ + lane + 64 * i;
-                    sv[i] = e < E ? slot_load(ctl, e) : ((uint64_t)kSlotTag << 32);  // (padding: ready, unused)
+                    // (padding: ready, unused)
+                    sv[i] = e < E ? slot_load(ctl, e) : ((uint64_t)slot_tag(ep, e) << 32);
                 }
-                bool miss = false, bad = false;
+                bool any = false;
 #pragma unroll
                 for (int i = 0; i < 4; i++) {
-                    const uint32_t tag = (uint32_t)(sv[i] >> 32);
-                    miss = miss || tag == 0u;
-                    bad = bad || (tag != 0u && tag != kSlotTag);
+                    const int e = wave * EQ + lane + 64 * i;
+                    miss[i] = (uint32_t)(sv[i] >> 32) != slot_tag(ep, e);
+                    any = any || miss[i];
                     lg[i] = __uint_as_float((uint32_t)sv[i]);
                 }
-                if (__builtin_amdgcn_ballot_w64(bad)) {
-                    if (lane == 0) ctl_set(ctl, kCtlFault, 1);
-                    break;
-                }
-                if (!__builtin_amdgcn_ballot_w64(miss)) break;
+                if (!__builtin_amdgcn_ballot_w64(any)) break;
                 if (__builtin_amdgcn_s_memrealtime() - t0 >= p.help_ticks) {
                     // waited long: compute this wave's missing rows here
 #pragma unroll 1
                     for (int i = 0; i < 4; i++) {
-                        uint64_t m = __builtin_amdgcn_ballot_w64((uint32_t)(sv[i] >> 32) == 0u);
+                        uint64_t m = __builtin_amdgcn_ballot_w64(miss[i]);
                         while (m) {
                             const int l = __builtin_ctzll(m);
                             m &= m - 1;
@@ -535,7 +542,7 @@ __global__ __launch_bounds__(kGuWaves * 64) void k_dec1_gateup(Dec1Params p)
                             uint4 hw[kRtChunks];
                             router_load(hw, p.Wr, e, d, true);
                             const float v = router_dot(hw, s_xb);
-                            if (lane == 0) slot_store(ctl, e, v);
+                            if (lane == 0) slot_store(ctl, e, v, ep);
                         }
                     }
                 }
@@ -556,21 +563,33 @@ __global__ __launch_bounds__(kGuWaves * 64) void k_dec1_gateup(Dec1Params p)
             wt = lane < k ? gwt : 0.0f;
         }
         if (wave == 0) {
-            // rank among the valid ids (an id outside [0, E) drops its term)
+            // the picks in ascending id.  An id outside [0, E) drops its term;
+            // an id given more than once (the router never picks one twice)
+            // is one pick, led by its first slot, with the weights of all its
+            // slots summed in slot order: no contribution is lost
             const bool valid = lane < k && id >= 0 && id < E;
+            bool lead = valid;
+            float wsum = 0.0f;
+            for (int j = 0; j < k; j++) {
+                const int o = __builtin_amdgcn_readlane(id, j);
+                const float ow = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(wt), j));
+                lead = lead && !(o == id && j < lane);
+                wsum += o == id ? ow : 0.0f;
+            }
+            const uint64_t leaders = __builtin_amdgcn_ballot_w64(lead);
             int rank = 0;
             for (int j = 0; j < k; j++) {
                 const int o = __builtin_amdgcn_readlane(id, j);
-                rank += (o >= 0 && o < E && o < id) ? 1 : 0;
+                rank += ((leaders >> j) & 1ull) && o < id ? 1 : 0;
             }
             if (lane < k) {
                 s_eid[lane] = -1;
                 s_wt[lane] = 0.0f;
             }
             // (one wave: its LDS accesses are performed in order)
-            if (valid) {
+            if (lead) {
                 s_eid[rank] = id;
-                s_wt[rank] = wt;
+                s_wt[rank] = wsum;
             }
             if (blockIdx.x == 0) {
                 if (p.do_topk && lane < k) {
@@ -585,7 +604,7 @@ __global__ __launch_bounds__(kGuWaves * 64) void k_dec1_gateup(Dec1Params p)
                     // (the scores are no longer read: the merge is done)
                     int *cnt = reinterpret_cast<int *>(s_score);
                     for (int e = lane; e < E; e += 64) cnt[e] = 0;
-                    if (valid) cnt[id] = 1;
+                    if (lead) cnt[id] = 1;
                     for (int e = lane; e < E; e += 64) p.counts_out[e] = cnt[e];
                 }
             }
@@ -791,7 +810,7 @@ struct DnLoads {
 // SHC: 16-byte chunks per lane of a shared down row (ceil(F / 512)).
 template <int SHC, bool COHERENT, typename WaitH>
 __device__ __forceinline__ void dec1_down_rows(const Dec1Params &p, int rblk, uint8_t *s_h, const int *s_e,
-                                               const float *s_w, bool fault, WaitH &&wait_h)
+                                               const float *s_w, WaitH &&wait_h)
 {
     const Shape &s = p.s;
     const int lane = threadIdx.x & 63;
@@ -964,8 +983,7 @@ __device__ __forceinline__ void dec1_down_rows(const Dec1Params &p, int rblk, ui
 #pragma unroll
     for (int r = 0; r < kDnRows; r++) {
         // the weighted sum over the picks, then the shared experts' outputs
-        float v = wave_total(acc[r]) + ysh[r];
-        if (fault) v = __builtin_nanf("");
+        const float v = wave_total(acc[r]) + ysh[r];
         const int n = n0 + r;
         if (lane == 0 && n < d) {
             if (p.out_f32) p.out_f32[n] = v;
@@ -987,31 +1005,47 @@ __global__ __launch_bounds__(kDnWaves * 64) void k_dec1_down(Dec1Params p)
         s_e[threadIdx.x] = p.w.active[threadIdx.x];
         s_w[threadIdx.x] = p.w.pos_w[threadIdx.x];
     }
-    // a router wait that timed out (control block not zeroed) poisons the output
-    const bool fault = __hip_atomic_load(p.w.ctl + kCtlFault, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) != 0;
-    // the router slots back to zero for the next call (the gate/up kernel,
-    // their only reader, has ended)
-    if (blockIdx.x == 0)
-        for (int e = threadIdx.x; e < p.s.E; e += kDnWaves * 64) reinterpret_cast<uint64_t *>(p.w.ctl)[e] = 0;
+    // the next call's epoch (the gate/up kernel, the only reader of the
+    // router slots and of the epoch, has ended)
+    if (blockIdx.x == 0 && threadIdx.x == 0) {
+        const int ep = __hip_atomic_load(p.w.ctl + kCtlEpoch, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        __hip_atomic_store(p.w.ctl + kCtlEpoch, ep + 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    }
     __syncthreads();
     // (H was written by the gate/up kernel, which has ended: nothing to wait for)
-    dec1_down_rows<SHC, false>(p, (int)blockIdx.x, s_h, s_e, s_w, fault, [] {});
+    dec1_down_rows<SHC, false>(p, (int)blockIdx.x, s_h, s_e, s_w, [] {});
 }
 
 // ---------------------------------------------------------------- host
 
 bool decode1_supported(const Shape &s)
 {
-    return s.T == 1 && s.d % 64 == 0 && s.d <= kMaxD && s.F % 64 == 0 && s.F <= 512 * kShMaxChunks &&
+    // (fp16 H: SiTU with b1 b2 <= 65504 only; SwiGLU takes the fp32-H GEMV kernels)
+    return s.T == 1 && s.act == 0 && situ_h_fits_f16(s) && s.d % 64 == 0 && s.d <= kMaxD && s.F % 64 == 0 && s.F <= 512 * kShMaxChunks &&
            s.E <= kMaxExperts && s.k <= kMaxTopK &&
            (size_t)s.k * s.F * 2 + (size_t)s.S * s.F * 4 <= (size_t)kDnMaxLds;
 }
 
+// the wait before a router waiter computes missing rows itself, in us
+// (moe_set_one_token_router_wait); read at every launch, set rarely
+static std::atomic<uint32_t> g_help_us{kHelpUsDefault};
+
+void set_router_wait_us(uint32_t us) { g_help_us.store(us, std::memory_order_relaxed); }
+
+// compute units of the current device, queried once per device
 static int cu_count()
 {
-    int dev = 0, n = 0;
+    constexpr int kDevs = 64;
+    static std::atomic<int> cache[kDevs];
+    int dev = 0;
     if (hipGetDevice(&dev) != hipSuccess) return 256;
-    if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0) return 256;
+    if (dev >= 0 && dev < kDevs) {
+        const int c = cache[dev].load(std::memory_order_relaxed);
+        if (c > 0) return c;
+    }
+    int n = 0;
+    if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0) n = 256;
+    if (dev >= 0 && dev < kDevs) cache[dev].store(n, std::memory_order_relaxed);
     return n;
 }
 
@@ -1037,8 +1071,8 @@ hipError_t launch_decode1(const Shape &s, const uint16_t *x, const Weights &wt, 
     p.shared = shared && s.S > 0;
     p.out_bf16 = out_bf16;
     p.out_f32 = out_f32;
-    p.help_ticks = kHelpTicks;
-    if (const char *h = getenv("MOE_ONE_TOKEN_HELP_US")) p.help_ticks = (uint64_t)strtoull(h, nullptr, 10) * 100;
+    // (s_memrealtime counts at 100 MHz)
+    p.help_ticks = (uint64_t)g_help_us.load(std::memory_order_relaxed) * 100u;
     // one block per CU (its LDS keeps a second one off), more if a block's
     // ranges would not fit its LDS records
     const int units = s.k * (s.F / kGuFeat);

@@ -773,7 +773,7 @@ bool mfma_supported(const Shape &s)
     // a column per stage are read as one 8-byte-aligned load) and every
     // column tile full; activation operands addressed with 32-bit offsets
     const size_t lim = (size_t)1 << 31;
-    return s.d % 256 == 0 && s.F % 256 == 0 && (size_t)s.T * s.k * s.F * 2 < lim &&
+    return situ_h_fits_f16(s) && s.d % 256 == 0 && s.F % 256 == 0 && (size_t)s.T * s.k * s.F * 2 < lim &&
            (size_t)s.T * s.d * 2 < lim && (size_t)s.T * s.S * s.F * 2 < lim;
 }
 

@@ -118,7 +118,7 @@ size_t ws_needed(const moe_layer_desc *d, int32_t T)
 }
 
 moe_status check_call(const moe_layer_desc *d, const uint16_t *x, int32_t T, void *ws,
-                      size_t ws_bytes, bool experts)
+                      size_t ws_bytes)
 {
     const moe_status st = check_desc(d);
     if (st != MOE_OK) return st;
@@ -127,7 +127,8 @@ moe_status check_call(const moe_layer_desc *d, const uint16_t *x, int32_t T, voi
     if (T == 0) return MOE_OK;
     if (!x || !aligned(x, 16)) return MOE_EINVAL;
     if (!ws || !aligned(ws, 256)) return MOE_EINVAL;
-    if (experts && path_of(d, T) == MOE_PATH_MFMA && !moe::mfma_supported(shape_of(d, T)))
+    // (every entry point: moe_route runs the MFMA path's router too)
+    if (path_of(d, T) == MOE_PATH_MFMA && !moe::mfma_supported(shape_of(d, T)))
         return MOE_EUNSUPPORTED;
     if (ws_bytes < ws_needed(d, T)) return MOE_EWORKSPACE;
     return MOE_OK;
@@ -234,7 +235,7 @@ int32_t moe_path_for(const moe_layer_desc *desc, int32_t T)
 moe_status moe_route(const moe_layer_desc *desc, const uint16_t *x, int32_t T, int32_t *ids,
                      float *weights, int32_t *counts, void *ws, size_t ws_bytes, void *stream)
 {
-    moe_status st = check_call(desc, x, T, ws, ws_bytes, false);
+    moe_status st = check_call(desc, x, T, ws, ws_bytes);
     if (st != MOE_OK || T == 0) return st;
     if (!ids || !weights) return MOE_EINVAL;
     (void)hipGetLastError();
@@ -250,7 +251,7 @@ moe_status moe_expert_forward(const moe_layer_desc *desc, const uint16_t *x, int
                               uint16_t *out_bf16, float *out_f32, int32_t out_mode, void *ws,
                               size_t ws_bytes, void *stream)
 {
-    moe_status st = check_call(desc, x, T, ws, ws_bytes, true);
+    moe_status st = check_call(desc, x, T, ws, ws_bytes);
     if (st != MOE_OK) return st;
     if (include_shared != 0 && include_shared != 1) return MOE_EINVAL;
     st = check_out(out_mode, out_bf16, out_f32);
@@ -269,7 +270,7 @@ moe_status moe_layer(const moe_layer_desc *desc, const uint16_t *x, int32_t T, u
                      float *out_f32, int32_t out_mode, int32_t *ids_opt, float *weights_opt,
                      int32_t *counts_opt, void *ws, size_t ws_bytes, void *stream)
 {
-    moe_status st = check_call(desc, x, T, ws, ws_bytes, true);
+    moe_status st = check_call(desc, x, T, ws, ws_bytes);
     if (st != MOE_OK) return st;
     st = check_out(out_mode, out_bf16, out_f32);
     if (st != MOE_OK || T == 0) return st;
@@ -285,7 +286,7 @@ moe_status moe_layer_timed(const moe_layer_desc *desc, const uint16_t *x, int32_
                            uint16_t *out_bf16, float *out_f32, int32_t out_mode, void *ws,
                            size_t ws_bytes, void *stream, void *const *events)
 {
-    moe_status st = check_call(desc, x, T, ws, ws_bytes, true);
+    moe_status st = check_call(desc, x, T, ws, ws_bytes);
     if (st != MOE_OK) return st;
     st = check_out(out_mode, out_bf16, out_f32);
     if (st != MOE_OK || T == 0) return st;
@@ -298,6 +299,13 @@ moe_status moe_layer_timed(const moe_layer_desc *desc, const uint16_t *x, int32_
     carve(s, (char *)ws, &w);
     return run_layer(desc, s, x, 1, 1, w.ids, w.wts, nullptr, w, out_mode, out_bf16, out_f32,
                      (hipStream_t)stream, reinterpret_cast<hipEvent_t const *>(events), true);
+}
+
+moe_status moe_set_one_token_router_wait(int32_t microseconds)
+{
+    if (microseconds < 0) return MOE_EINVAL;
+    moe::set_router_wait_us((uint32_t)microseconds);
+    return MOE_OK;
 }
 
 const char *moe_status_str(int32_t status)

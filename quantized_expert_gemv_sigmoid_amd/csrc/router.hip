@@ -8,10 +8,14 @@
 // a wave-wide 64-bit max (DPP inside each row of 16 lanes, then readlane
 // across the four rows) pick the experts in descending order.
 //
-// Dispatch: positions group the T*k slots by expert (ascending id) and, inside
-// an expert, by token.  A token picks an expert at most once, so the slots of
-// expert e inside a 64-token block form a 64-bit token bitmap; the rank of
-// token t among them is popcount(mask & (bit(t) - 1)).
+// Dispatch: positions group the (token, expert) pairs by expert (ascending
+// id) and, inside an expert, by token.  The pairs of expert e inside a
+// 64-token block form a 64-bit token bitmap; the rank of token t among them
+// is popcount(mask & (bit(t) - 1)).  The router never picks an expert twice
+// for one token, but ids given to moe_expert_forward may repeat one: the
+// repeats of an id in a token's row share one position (one bit of the
+// bitmap), whose weight is the sum of their weights in slot order, so that
+// w1 FFN_e(x) + w2 FFN_e(x) = (w1 + w2) FFN_e(x) loses no contribution.
 #include "common.h"
 #include "router_dev.h"
 
@@ -99,20 +103,44 @@ __device__ __forceinline__ int write_offsets(int e, int E, int c, int *tmp16, in
     return off;
 }
 
-// positions of token t's slots in ascending expert id (invalid ids last, -1)
+// the first slot of a token's row holding a valid id leads that id: it owns
+// the (token, expert) position; later slots with the same id follow it
+__device__ __forceinline__ bool leads(const int32_t *__restrict__ row, int j, int E)
+{
+    const int o = row[j];
+    if (!valid_id(o, E)) return false;
+    for (int i = 0; i < j; i++)
+        if (row[i] == o) return false;
+    return true;
+}
+
+// the routing weight of a leading slot: the weights of every slot of the row
+// with its id, summed in slot order (just its own weight when it has no repeat)
+__device__ __forceinline__ float merged_weight(const int32_t *__restrict__ row,
+                                               const float *__restrict__ wrow, int j, int k)
+{
+    const int o = row[j];
+    float w = 0.0f;
+    for (int i = 0; i < k; i++)
+        if (row[i] == o) w += wrow[i];
+    return w;
+}
+
+// positions of token t's (token, expert) pairs in ascending expert id, one
+// entry per slot: leading slots first, then -1 for the rest (invalid ids and
+// repeats)
 __device__ __forceinline__ void write_tok_pos(int t, int slot_j, int E, int k,
                                               const int32_t *__restrict__ row, int pos,
                                               int32_t *__restrict__ tok_pos)
 {
-    const int me = row[slot_j];
-    const int mk = valid_id(me, E) ? me : 0x7fffffff;
+    const bool me_leads = leads(row, slot_j, E);
+    const int mk = me_leads ? row[slot_j] : 0x7fffffff;
     int r = 0;
     for (int j = 0; j < k; j++) {
-        const int o = row[j];
-        const int ok = valid_id(o, E) ? o : 0x7fffffff;
+        const int ok = leads(row, j, E) ? row[j] : 0x7fffffff;
         r += (ok < mk) || (ok == mk && j < slot_j);
     }
-    tok_pos[(size_t)t * k + r] = valid_id(me, E) ? pos : -1;
+    tok_pos[(size_t)t * k + r] = me_leads ? pos : -1;
 }
 
 // T <= 64 and T*k < 65536: one block of 1024 threads does top-k (optional),
@@ -145,14 +173,15 @@ __global__ __launch_bounds__(1024) void k_dispatch_small(
     __syncthreads();
     for (int sl = threadIdx.x; sl < T * k; sl += 1024) {
         const int t = sl / k, j = sl % k;
-        const int ee = ids[sl];
+        const int32_t *row = ids + (size_t)t * k;
+        const int ee = row[j];
         int p = -1;
-        if (valid_id(ee, E)) {
+        if (leads(row, j, E)) {
             p = offs[ee] + __popcll(masks[ee] & ((1ull << t) - 1ull));
             w.pos_tok[p] = t;
-            w.pos_w[p] = wts[sl];
+            w.pos_w[p] = merged_weight(row, wts + (size_t)t * k, j, k);
         }
-        write_tok_pos(t, j, E, k, ids + (size_t)t * k, p, w.tok_pos);
+        write_tok_pos(t, j, E, k, row, p, w.tok_pos);
     }
 }
 
@@ -210,16 +239,17 @@ __global__ __launch_bounds__(256) void k_dispatch_scatter(Shape s, const int32_t
     const int sl = blockIdx.x * blockDim.x + threadIdx.x;
     if (sl >= s.T * s.k) return;
     const int t = sl / s.k, j = sl % s.k;
-    const int e = ids[sl];
+    const int32_t *row = ids + (size_t)t * s.k;
+    const int e = row[j];
     int p = -1;
-    if (valid_id(e, s.E)) {
+    if (leads(row, j, s.E)) {
         const int b = t / kDispatchTokens, tl = t % kDispatchTokens;
         const unsigned long long m = w.masks[(size_t)b * s.E + e];
         p = w.offsets[e] + w.blk_base[(size_t)b * s.E + e] + __popcll(m & ((1ull << tl) - 1ull));
         w.pos_tok[p] = t;
-        w.pos_w[p] = wts[sl];
+        w.pos_w[p] = merged_weight(row, wts + (size_t)t * s.k, j, s.k);
     }
-    write_tok_pos(t, j, s.E, s.k, ids + (size_t)t * s.k, p, w.tok_pos);
+    write_tok_pos(t, j, s.E, s.k, row, p, w.tok_pos);
 }
 
 template <int EPL>

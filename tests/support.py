@@ -41,9 +41,14 @@ def assert_close(gpu: np.ndarray, ref: np.ndarray, what: str = ""):
 
 
 def bf16_rne(a: np.ndarray) -> np.ndarray:
-    """fp32 -> bf16 bits, round to nearest even (the output rule of the ABI)."""
+    """fp32 -> bf16 bits, round to nearest even (the output rule of the ABI):
+    add 0x7FFF plus the kept low bit and drop 16 bits; a NaN keeps its top
+    bits with the quiet bit set (adding to its pattern could carry it into an
+    infinity or a zero)."""
     u = np.ascontiguousarray(a, dtype=np.float32).view(np.uint32).astype(np.uint64)
-    r = (u + 0x7FFF + ((u >> 16) & 1)) >> 16
+    r = ((u + 0x7FFF + ((u >> 16) & 1)) >> 16) & 0xFFFF
+    nan = ((u & 0x7F800000) == 0x7F800000) & ((u & 0x007FFFFF) != 0)
+    r = np.where(nan, (u >> 16) | 0x40, r)
     return r.astype(np.uint16)
 
 
@@ -104,7 +109,7 @@ def run_layer(gl: GpuLayer, x_bits: np.ndarray, out_mode: int = 2):
     ids = torch.empty((T, k), dtype=torch.int32, device="cuda")
     w = torch.empty((T, k), dtype=torch.float32, device="cuda")
     cnt = torch.empty(E, dtype=torch.int32, device="cuda")
-    ws = torch.zeros(moe.workspace_bytes(gl.desc, T), dtype=torch.uint8, device="cuda")
+    ws = moe.workspace(gl.desc, T)  # uninitialised: the library needs no particular contents
     moe.layer(gl.desc, x, T, out_b if out_mode != 1 else None, out_f if out_mode != 0 else None,
               out_mode, ws, ids=ids, weights=w, counts=cnt)
     torch.cuda.synchronize()

@@ -146,11 +146,33 @@ def test_status_strings(L):
     assert moe.status_str(12345) == "unknown status"
 
 
-def test_control_block_size_matches_header(L):
-    """The binding's WS_CONTROL_BYTES is the header's MOE_WS_CONTROL_BYTES, and
-    every workspace holds at least the control block."""
-    m = re.search(r"#define\s+MOE_WS_CONTROL_BYTES\s+(\d+)", open(HEADER).read())
-    assert m and int(m.group(1)) == moe.WS_CONTROL_BYTES
-    d = desc()
-    for t in (0, 1, 2, 64):
-        assert L.moe_workspace_bytes(ctypes.byref(d), t) >= moe.WS_CONTROL_BYTES
+def test_router_wait_setting(L):
+    assert L.moe_set_one_token_router_wait(-1) == moe.EINVAL
+    assert L.moe_set_one_token_router_wait(0) == moe.OK
+    assert L.moe_set_one_token_router_wait(50) == moe.OK
+
+
+def test_mfma_route_outside_its_range_refused(L):
+    """moe_route with an explicit MFMA path checks the path's range before any
+    launch, as the expert entry points do: d = 3200 is not a multiple of 256."""
+    d = desc(d_model=3200, path=moe.PATH_MFMA)
+    need = L.moe_workspace_bytes(ctypes.byref(d), 4)
+    assert need > 0
+    assert L.moe_route(ctypes.byref(d), FAKE, 4, FAKE, FAKE, None, FAKE * 16, need, None) == moe.EUNSUPPORTED
+    assert call_layer(L, d, T=4, ws=(FAKE * 16, need)) == moe.EUNSUPPORTED
+    assert L.moe_expert_forward(ctypes.byref(d), FAKE, 4, FAKE, FAKE, 1, None, FAKE, moe.OUT_F32,
+                                FAKE * 16, need, None) == moe.EUNSUPPORTED
+    # AUTO stays on the GEMV path there
+    assert moe.path_for(desc(d_model=3200), 4096) == moe.PATH_GEMV
+
+
+def test_fp16_h_paths_need_situ_within_fp16(L):
+    """SiTU bounds |h| by b1*b2: above 65504 (the largest fp16) the fp16-H MFMA
+    path is refused when asked for and AUTO keeps the fp32-H GEMV kernels."""
+    big = desc(situ_b1=4.0, situ_b2=20000.0, path=moe.PATH_MFMA)
+    need = L.moe_workspace_bytes(ctypes.byref(big), 4096)
+    assert need > 0
+    assert call_layer(L, big, T=4096, ws=(FAKE * 16, need)) == moe.EUNSUPPORTED
+    assert moe.path_for(desc(situ_b1=4.0, situ_b2=20000.0), 4096) == moe.PATH_GEMV
+    assert moe.path_for(desc(situ_b1=4.0, situ_b2=16376.0), 4096) == moe.PATH_MFMA  # 65504 exactly
+    assert moe.path_for(desc(act=moe.ACT_SWIGLU), 4096) == moe.PATH_MFMA

@@ -389,4 +389,112 @@ def test_stacked_layers_in_one_graph():
         torch.cuda.synchronize()
         for l in range(L):
             assert np.array_equal(outs[l].cpu().numpy(), refs[l][i]), f"replay {rep}: layer {l} differs"
-    assert not ws[:moe.WS_CONTROL_BYTES].any().item(), "control block left nonzero"
+
+
+# ------------------------------------------------------------- given routings
+
+@pytest.mark.parametrize("T,path", [(1, 1), (3, 1), (300, 2)])
+def test_repeated_ids_add_every_term(T, path):
+    """moe_expert_forward with an id repeated in a token's row (the router
+    never does that, a caller may): each slot's term is added, as the oracle's
+    plain sum over the slots does, on the one-token kernels (T = 1), the GEMV
+    path (T = 3) and the grouped MFMA GEMM (T = 300)."""
+    import quantized_expert_gemv_sigmoid_amd as moe
+    import synth.device as sdev
+    log(f"case: repeated ids T={T} path={path}")
+    gl = make_gpu_layer(MFMA_SHAPE, 66, path=path)
+    k, E, d = MFMA_SHAPE.top_k, MFMA_SHAPE.n_experts, MFMA_SHAPE.d_model
+    x, rw, bias = tokens(gl, T, screened=False)
+    ids, w, _ = oracle.route(x, rw, bias, k)
+    rng = np.random.default_rng(T)
+    for t in range(T):
+        # slot 1 repeats slot 0; every third token also repeats slot 2 in
+        # slots 3 and 5 (an id three times); every fifth gets an invalid id
+        ids[t, 1] = ids[t, 0]
+        if t % 3 == 0:
+            ids[t, 3] = ids[t, 5] = ids[t, 2]
+        if t % 5 == 0:
+            ids[t, 4] = -1
+        rng.shuffle(ids[t])
+    w = rng.uniform(0.05, 0.5, size=w.shape).astype(np.float32)
+    xd = sdev.tokens_to_device(x)
+    idd = torch.from_numpy(ids).cuda()
+    wd = torch.from_numpy(w).cuda()
+    of = torch.empty((T, d), dtype=torch.float32, device="cuda")
+    ob = torch.empty((T, d), dtype=torch.int16, device="cuda")
+    ws = moe.workspace(gl.desc, T)
+    moe.expert_forward(gl.desc, xd, T, idd, wd, 1, ob, of, moe.OUT_BOTH, ws)
+    torch.cuda.synchronize()
+    slot = np.where(ids >= 0, ids, -1).astype(np.int32)
+    ref = oracle.forward(x, slot, w, oracle.held_arrays(gl.host), oracle.shared_arrays(gl.host))
+    assert_close(of.cpu().numpy(), ref, f"repeated ids T={T}")
+    assert np.array_equal(ob.cpu().numpy().view(np.uint16), bf16_rne(of.cpu().numpy()))
+
+
+def test_situ_betas_beyond_fp16_take_fp32_h():
+    """SiTU with b1 * b2 above 65504 can give |h| past the fp16 range: AUTO
+    keeps such a layer on the fp32-H GEMV kernels at every T (also T = 1,
+    where the fused one-token kernels are not taken), and the results match
+    the oracle with h well beyond 65504."""
+    import quantized_expert_gemv_sigmoid_amd as moe
+    shape = synth.LayerShape(n_experts=24, top_k=4, n_shared=1, d_model=512, d_ffn=512)
+    h = synth.host_layer(shape, 67, 0)
+    # gate and up scales 2^5..2^6 times the workload's: |g|, |u| in the
+    # thousands, so |h| = |b1 tanh(g/b1) sigmoid(g) b2 tanh(u/b2)| reaches
+    # about b1 * b2 = 4 * 2e5 = 8e5
+    for s in (h.w1s, h.w3s):
+        s[...] = s + 11
+    gl = make_gpu_layer(shape, 67, host=h)
+    gl.desc.situ_b2 = 2.0e5
+    for T in (1, 40):
+        assert moe.path_for(gl.desc, T) == moe.PATH_GEMV
+        log(f"case: SiTU b2=2e5 T={T}")
+        x, rw, bias = tokens(gl, T)
+        out_f, out_b, ids, wts, cnt = run_layer(gl, x)
+        rids, rw_, _ = oracle.route(x, rw, bias, shape.top_k)
+        ref = oracle.forward(x, rids, rw_, oracle.held_arrays(h), oracle.shared_arrays(h), True,
+                             oracle.ACT_SITU, 4.0, 2.0e5)
+        check_routing(ids, wts, cnt, rids, rw_, shape.n_experts, "routing")
+        assert_close(out_f, ref, f"SiTU b2=2e5 T={T}")
+
+
+def test_swiglu_beyond_fp16_range():
+    """Under SwiGLU |h| is unbounded.  The GEMV path (fp32 H, and the only one
+    SwiGLU takes at T = 1) matches the oracle with |h| far above 65504; the
+    MFMA path stores H in fp16, where such a token's outputs come out
+    non-finite, never as finite wrong values."""
+    import quantized_expert_gemv_sigmoid_amd as moe
+    shape = synth.LayerShape(n_experts=24, top_k=4, n_shared=1, d_model=512, d_ffn=512)
+    h = synth.host_layer(shape, 68, 0)
+    for s in (h.w1s, h.w3s):
+        s[...] = s + 11  # |g|, |u| in the thousands: |h| ~ 1e6 and more
+    g_gemv = make_gpu_layer(shape, 68, host=h, act=oracle.ACT_SWIGLU, path=moe.PATH_GEMV)
+    g_auto = make_gpu_layer(shape, 68, host=h, act=oracle.ACT_SWIGLU)
+    g_mfma = make_gpu_layer(shape, 68, host=h, act=oracle.ACT_SWIGLU, path=moe.PATH_MFMA)
+    assert moe.path_for(g_auto.desc, 1) == moe.PATH_GEMV
+    for gl, T in ((g_gemv, 1), (g_auto, 1), (g_gemv, 40)):
+        log(f"case: SwiGLU |h| >> 65504, GEMV path, T={T}")
+        x, rw, bias = tokens(gl, T)
+        out_f, out_b, ids, wts, cnt = run_layer(gl, x)
+        rids, rw_, gap, rout = oracle_outputs(gl, x, rw, bias, np.arange(T), act=oracle.ACT_SWIGLU)
+        check_routing(ids, wts, cnt, rids, rw_, shape.n_experts, "routing")
+        assert_close(out_f, rout, f"SwiGLU GEMV T={T}")
+    log("case: SwiGLU |h| >> 65504, MFMA path (fp16 H), T=40")
+    x, rw, bias = tokens(g_mfma, 40)
+    out_f, out_b, ids, wts, cnt = run_layer(g_mfma, x)
+    # the oracle's H: which tokens have an |h| past the fp16 range
+    big = []
+    for t in range(40):
+        hh = []
+        xf = oracle.bf16_to_f32(x[t])
+        for e in ids[t]:
+            g = oracle.mxfp4_matvec(xf, h.w1q[e], h.w1s[e])
+            u = oracle.mxfp4_matvec(xf, h.w3q[e], h.w3s[e])
+            hh.append(np.abs(oracle.act(g, u, oracle.ACT_SWIGLU)).max())
+        big.append(max(hh) > 65520.0)
+    big = np.array(big)
+    assert big.any(), "the fixture should push some |h| past the fp16 range"
+    for t in range(40):
+        if big[t]:
+            assert not np.isfinite(out_f[t]).any(), f"token {t}: finite output from an overflowed H"
+    assert np.array_equal(out_b, bf16_rne(out_f))

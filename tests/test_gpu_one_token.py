@@ -11,7 +11,7 @@ The shapes here exercise that path's branches:
 - picks given to moe_expert_forward;
 - HIP graph replays;
 - the router hand-off between blocks: its fallback (a waiter that computes
-  missing logits itself) and a control block that was not zeroed.
+  missing logits itself) and a workspace that was never initialised.
 
 The bar is the one the other GPU tests use:
 - ids (per-token sets) and counts bit-exact;
@@ -78,6 +78,8 @@ def test_one_token_calls(name, shape, zipf):
 
 
 def test_one_token_swiglu():
+    """SwiGLU at T = 1 (unbounded h: the fp32-H GEMV kernels, not the fused
+    one-token kernels, whose H is fp16)."""
     log("case: one-token SwiGLU E40 k6 S2 d512 F768")
     gl = make_gpu_layer(S(40, 6, 2, 512, 768), 72, act=oracle.ACT_SWIGLU)
     _check_tokens_one_by_one(gl, 4, act=oracle.ACT_SWIGLU)
@@ -158,9 +160,10 @@ def test_graph_replay_one_token_and_mfma_paths(T):
         assert np.array_equal(out_o.cpu().numpy(), ref_b)
 
 
-def test_one_token_router_fallback_is_bit_identical(monkeypatch):
+def test_one_token_router_fallback_is_bit_identical():
     """With no wait allowed, every waiter of the gate/up kernel computes the
     router rows it has not yet seen itself: the same sums, so the same bits."""
+    import quantized_expert_gemv_sigmoid_amd as moe
     shape = S(300, 16, 2, 2048, 1536)
     gl = make_gpu_layer(shape, 76)
     x, rw, bias = tokens(gl, 3)
@@ -168,38 +171,57 @@ def test_one_token_router_fallback_is_bit_identical(monkeypatch):
     for t in range(3):
         log(f"case: one-token router fallback, token {t}")
         ref = run_layer(gl, x[t:t + 1])
-        monkeypatch.setenv("MOE_ONE_TOKEN_HELP_US", "0")
-        got = run_layer(gl, x[t:t + 1])
-        monkeypatch.delenv("MOE_ONE_TOKEN_HELP_US")
+        moe.set_one_token_router_wait(0)
+        try:
+            got = run_layer(gl, x[t:t + 1])
+        finally:
+            moe.set_one_token_router_wait(50)
         for a, b in zip(ref, got):
             assert np.array_equal(a, b), "fallback output differs"
         check_routing(got[2], got[3], got[4], rids[t:t + 1], rw_[t:t + 1], shape.n_experts, f"token {t}")
         assert_close(got[0], rout[t:t + 1], f"token {t}")
 
 
-def test_one_token_control_block_not_zeroed():
-    """A workspace whose control block holds something else gives NaN outputs
-    (and keeps giving them) instead of waiting or reading stale logits; once
-    the block is zeroed the call is exact again."""
+def test_one_token_workspace_needs_no_initialisation():
+    """The one-token kernels take whatever the workspace holds: zeros, a
+    constant byte, random bytes, or the slots and epoch an earlier call left
+    (copied back so that the same epoch repeats) give the exact result of a
+    fresh call, on every call in a row."""
     import quantized_expert_gemv_sigmoid_amd as moe
     import synth.device as sdev
     shape = S(40, 6, 2, 512, 768)
     gl = make_gpu_layer(shape, 77)
-    x, _, _ = tokens(gl, 1)
-    log("case: one-token control block not zeroed")
-    ref_f = run_layer(gl, x)[0]
-    xd = sdev.tokens_to_device(x)
-    ws = torch.zeros(moe.workspace_bytes(gl.desc, 1), dtype=torch.uint8, device="cuda")
-    ws[:moe.WS_CONTROL_BYTES] = 0xA5
+    x, _, _ = tokens(gl, 2)
+    refs = [run_layer(gl, x[t:t + 1])[0] for t in range(2)]
+    xds = [sdev.tokens_to_device(x[t:t + 1]) for t in range(2)]
+    n = moe.workspace_bytes(gl.desc, 1)
     of = torch.empty((1, shape.d_model), dtype=torch.float32, device="cuda")
-    for _ in range(2):
-        moe.layer(gl.desc, xd, 1, None, of, moe.OUT_F32, ws)
-        torch.cuda.synchronize()
-        assert np.isnan(of.cpu().numpy()).all(), "a garbage control block must poison the output"
-    ws[:moe.WS_CONTROL_BYTES] = 0
-    moe.layer(gl.desc, xd, 1, None, of, moe.OUT_F32, ws)
+    gen = torch.Generator(device="cpu").manual_seed(5)
+    fills = {"zeros": torch.zeros(n, dtype=torch.uint8), "0xA5": torch.full((n,), 0xA5, dtype=torch.uint8),
+             "0xFF": torch.full((n,), 0xFF, dtype=torch.uint8),
+             "random": torch.randint(0, 256, (n,), dtype=torch.uint8, generator=gen)}
+    for name, fill in fills.items():
+        log(f"case: one-token workspace filled with {name}")
+        ws = fill.to("cuda")
+        for rep in range(3):
+            t = rep % 2
+            moe.layer(gl.desc, xds[t], 1, None, of, moe.OUT_F32, ws)
+            torch.cuda.synchronize()
+            assert np.array_equal(of.cpu().numpy(), refs[t]), f"{name}: call {rep} differs"
+    # the control block as token 0's call left it, put back after token 1's
+    # call: the next call (token 1) runs one epoch past the slots it finds,
+    # and must not route token 1 with token 0's logits
+    log("case: one-token workspace with an earlier call's control block restored")
+    ws = moe.workspace(gl.desc, 1)
+    moe.layer(gl.desc, xds[0], 1, None, of, moe.OUT_F32, ws)
     torch.cuda.synchronize()
-    assert np.array_equal(of.cpu().numpy(), ref_f), "zeroed again, the call must match"
+    snap = ws.clone()
+    moe.layer(gl.desc, xds[1], 1, None, of, moe.OUT_F32, ws)
+    torch.cuda.synchronize()
+    ws.copy_(snap)
+    moe.layer(gl.desc, xds[1], 1, None, of, moe.OUT_F32, ws)
+    torch.cuda.synchronize()
+    assert np.array_equal(of.cpu().numpy(), refs[1])
 
 
 @pytest.mark.parametrize("name,shape,seed", [
@@ -219,9 +241,8 @@ def test_one_token_limits(name, shape, seed):
 
 def test_workspace_shared_across_paths():
     """One workspace, sized for the largest call, serves one-token, GEMV and
-    MFMA calls in any order: the one-token path's control block stays zero
-    between calls, and every output equals that of a call with a fresh
-    workspace, bit for bit."""
+    MFMA calls in any order, and every output equals that of a call with a
+    fresh workspace, bit for bit."""
     import quantized_expert_gemv_sigmoid_amd as moe
     import synth.device as sdev
     shape = S(40, 6, 2, 512, 768)
@@ -244,4 +265,3 @@ def test_workspace_shared_across_paths():
         assert np.array_equal(of.cpu().numpy(), ref_f), f"call {n} (T={T}): output differs"
         assert np.array_equal(ob.cpu().numpy().view(np.uint16), ref_b)
         assert np.array_equal(ids.cpu().numpy(), ref_ids) and np.array_equal(c.cpu().numpy(), ref_c)
-        assert not ws[:moe.WS_CONTROL_BYTES].any().item(), f"call {n}: control block left nonzero"
