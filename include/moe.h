@@ -155,6 +155,27 @@ moe_status moe_layer(const moe_layer_desc *desc, const uint16_t *x, int32_t T,
                      void *ws, size_t ws_bytes, void *stream);
 
 /*
+ * moe_layer without a caller workspace, for callers that cannot allocate or
+ * hold one (code under HIP graph capture, tight serving loops, harnesses that
+ * forbid hipMalloc).  Arguments and results are those of moe_layer, bit for
+ * bit; the call allocates nothing (no hipMalloc, no allocating library
+ * routine).  Its workspace is a static device array of MOE_NOALLOC_WS_BYTES
+ * inside the library, one per GPU, held until the process ends and shared
+ * by every moe_layer_noalloc call on that GPU: calls that overlap in time
+ * on one GPU (two streams, two threads) race on it and must not be issued.
+ * A call that would need more (moe_workspace_bytes(desc, T) above
+ * MOE_NOALLOC_WS_BYTES; at the Kimi-K3 shape about 170 tokens) returns
+ * MOE_EWORKSPACE before anything is launched.  The array needs no
+ * initialisation and keeps the last call's contents, which carry nothing a
+ * caller reads.
+ */
+#define MOE_NOALLOC_WS_BYTES ((size_t)128 << 20)
+moe_status moe_layer_noalloc(const moe_layer_desc *desc, const uint16_t *x, int32_t T,
+                             uint16_t *out_bf16, float *out_f32, int32_t out_mode,
+                             int32_t *ids_opt, float *weights_opt, int32_t *counts_opt,
+                             void *stream);
+
+/*
  * moe_layer with phase timing: records the caller's HIP events (hipEvent_t
  * handles, exactly MOE_TIMED_EVENTS of them) on `stream` at the phase
  * boundaries: events[0] before the router, [1] after the router logits (and,

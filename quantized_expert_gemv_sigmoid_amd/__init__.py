@@ -23,8 +23,10 @@ OUT_BF16, OUT_F32, OUT_BOTH = 0, 1, 2
 PATH_AUTO, PATH_GEMV, PATH_MFMA = 0, 1, 2
 
 EXPORTS = ("moe_workspace_bytes", "moe_path_for", "moe_route", "moe_expert_forward",
-           "moe_layer", "moe_layer_timed", "moe_set_one_token_router_wait", "moe_status_str")
+           "moe_layer", "moe_layer_noalloc", "moe_layer_timed", "moe_set_one_token_router_wait",
+           "moe_status_str")
 TIMED_EVENTS = 6
+NOALLOC_WS_BYTES = 128 << 20  # MOE_NOALLOC_WS_BYTES: the static workspace of moe_layer_noalloc
 
 
 class MoeError(RuntimeError):
@@ -72,6 +74,8 @@ def lib() -> ctypes.CDLL:
         L.moe_expert_forward.argtypes = [P, vp, i32, vp, vp, i32, vp, vp, i32, vp, sz, vp]
         L.moe_layer.restype = i32
         L.moe_layer.argtypes = [P, vp, i32, vp, vp, i32, vp, vp, vp, vp, sz, vp]
+        L.moe_layer_noalloc.restype = i32
+        L.moe_layer_noalloc.argtypes = [P, vp, i32, vp, vp, i32, vp, vp, vp, vp]
         L.moe_layer_timed.restype = i32
         L.moe_layer_timed.argtypes = [P, vp, i32, vp, vp, i32, vp, sz, vp, ctypes.POINTER(vp)]
         L.moe_set_one_token_router_wait.restype = i32
@@ -163,6 +167,14 @@ def layer(desc: LayerDesc, x, T: int, out_bf16, out_f32, out_mode: int, ws, ids=
     _check(lib().moe_layer(ctypes.byref(desc), _ptr(x), T, _ptr(out_bf16), _ptr(out_f32),
                            out_mode, _ptr(ids), _ptr(weights), _ptr(counts), wp, wn,
                            _stream(stream)), "moe_layer")
+
+
+def layer_noalloc(desc: LayerDesc, x, T: int, out_bf16, out_f32, out_mode: int, ids=None,
+                  weights=None, counts=None, stream=None) -> None:
+    """moe_layer on the library's static per-GPU workspace (no allocation)."""
+    _check(lib().moe_layer_noalloc(ctypes.byref(desc), _ptr(x), T, _ptr(out_bf16), _ptr(out_f32),
+                                   out_mode, _ptr(ids), _ptr(weights), _ptr(counts), _stream(stream)),
+           "moe_layer_noalloc")
 
 
 def layer_timed(desc: LayerDesc, x, T: int, out_bf16, out_f32, out_mode: int, ws, events,

@@ -3,10 +3,18 @@
 #include <math.h>
 
 #include <algorithm>
+#include <atomic>
 #include <string.h>
 
 #include "../../include/moe.h"
 #include "common.h"
+
+// The workspace of moe_layer_noalloc: one static array per device (each GPU
+// the library runs on holds its own copy until the process ends).  In host
+// code `scratch` names a host-side stand-in, not device memory: host code
+// uses only the device address hipGetSymbolAddress returns for it, taken
+// once per device with that device current (scratch_device_ptr below).
+static __device__ __align__(256) uint8_t scratch[MOE_NOALLOC_WS_BYTES];
 
 namespace {
 
@@ -215,6 +223,21 @@ moe_status run_layer(const moe_layer_desc *d, const Shape &s, const uint16_t *x,
     return MOE_OK;
 }
 
+constexpr int kMaxDevices = 64;
+std::atomic<void *> g_scratch_dev[kMaxDevices];
+
+// the current device's address of `scratch` (nullptr on a HIP error)
+void *scratch_device_ptr()
+{
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return nullptr;
+    void *ptr = g_scratch_dev[dev].load(std::memory_order_acquire);
+    if (ptr) return ptr;
+    if (hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch)) != hipSuccess || !ptr) return nullptr;
+    g_scratch_dev[dev].store(ptr, std::memory_order_release);
+    return ptr;
+}
+
 }  // namespace
 
 extern "C" {
@@ -275,6 +298,27 @@ moe_status moe_layer(const moe_layer_desc *desc, const uint16_t *x, int32_t T, u
     st = check_out(out_mode, out_bf16, out_f32);
     if (st != MOE_OK || T == 0) return st;
     (void)hipGetLastError();
+    const Shape s = shape_of(desc, T);
+    Work w;
+    carve(s, (char *)ws, &w);
+    return run_layer(desc, s, x, 1, 1, ids_opt ? ids_opt : w.ids, weights_opt ? weights_opt : w.wts,
+                     counts_opt, w, out_mode, out_bf16, out_f32, (hipStream_t)stream, nullptr, true);
+}
+
+moe_status moe_layer_noalloc(const moe_layer_desc *desc, const uint16_t *x, int32_t T,
+                             uint16_t *out_bf16, float *out_f32, int32_t out_mode, int32_t *ids_opt,
+                             float *weights_opt, int32_t *counts_opt, void *stream)
+{
+    // validated as moe_layer validates a call with a workspace of
+    // MOE_NOALLOC_WS_BYTES (256 stands in for its address, which check_call
+    // only tests for null and alignment), before anything is launched
+    moe_status st = check_call(desc, x, T, reinterpret_cast<void *>(256), MOE_NOALLOC_WS_BYTES);
+    if (st != MOE_OK) return st;
+    st = check_out(out_mode, out_bf16, out_f32);
+    if (st != MOE_OK || T == 0) return st;
+    (void)hipGetLastError();
+    void *ws = scratch_device_ptr();
+    if (!ws) return MOE_EHIP;
     const Shape s = shape_of(desc, T);
     Work w;
     carve(s, (char *)ws, &w);
