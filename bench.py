@@ -1,23 +1,30 @@
 #!/usr/bin/env python3
 """Benchmark of the routed-expert MoE layer on one MI355X.
 
-    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload N]
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload N] [--configs 0,2,3,4]
 
 One step is one pass of the whole layer (router, top-k, expert gate/up +
 activation, expert down, shared experts, weighted combine) over one batch of
-tokens, with weights and tokens already resident in HBM.  Default workload:
-the Kimi-K3-shaped layer at decode T=1 (E=896 routed experts in MXFP4,
-top-16, 2 bf16 shared experts, d=3584, F=3072).  Steps cycle through a pool
-of 32 distinct token batches so consecutive steps pick different experts (no
-cache reuse of one fixed selection).  Workload 4 stacks 12 such layers (own
-weights, own tokens, one Zipf selection bias) in one HIP graph per step.
+tokens, with weights and tokens already resident in HBM.  The headline
+workload (default 1) is the Kimi-K3-shaped layer at decode T=1 (E=896 routed
+experts in MXFP4, top-16, 2 bf16 shared experts, d=3584, F=3072).  Steps
+cycle through a pool of distinct token batches so consecutive steps pick
+different experts (no cache reuse of one fixed selection).  Workload 4
+stacks 12 such layers (own weights, own tokens, one Zipf selection bias) in
+one HIP graph per step.
 
-Prints one JSON line: throughput (tok/s), the roofline of the dominant kernel
-(algorithmic bytes / its average duration, timed live with the HIP events of
-moe_layer_timed on the launch stream), and the CPU oracle timed on a bounded
-sample of the same workload on this host.
+Prints one JSON line:
+- the headline: tok/s over exactly K timed graph replays (``value``), two
+  more windows of K steps for the spread, the roofline of the dominant
+  kernel (algorithmic bytes or flops / its average duration, timed live with
+  the HIP events of moe_layer_timed on the launch stream) and the CPU oracle
+  timed on a bounded sample of the same workload on this host;
+- ``configs``: the same measurements for the other workloads (tiny, decode
+  T=64, prefill T=4096, the 12-layer stack), each layer set freed before the
+  next is loaded.
 """
 import argparse
+import hashlib
 import json
 import os
 import sys
@@ -32,6 +39,11 @@ import numpy as np  # noqa: E402
 PEAK_HBM_GBS = 8000.0      # MI355X HBM3E, GB/s
 PEAK_BF16_TFLOPS = 2500.0  # MI355X dense bf16 MFMA, TFLOP/s
 METRIC = "MoE layer decode tok/s + HBM GB/s vs peak; prefill TFLOP/s vs MFMA peak"
+DTYPE = "mxfp4 weights -> bf16/fp16 operands, fp32 accumulate"
+DTYPE_DETAIL = ("routed weights MXFP4 (E2M1 + E8M0 per 32), decoded exactly to bf16 (gate/up, times the bf16 "
+                "token) and to fp16 (down, times an fp16 H) on the one-token and MFMA paths, to bf16 and fp32 "
+                "(fp32 H) on the GEMV path; shared experts bf16; router fp32; every sum fp32; outputs bf16 "
+                "(round to nearest even of the fp32 sum)")
 PHASES = ("router_logits", "topk_dispatch", "expert_gate_up", "expert_down", "combine")
 # kernels of each phase, per path: the fused one-token path (top-k, dispatch
 # and combine folded into the expert kernels), the GEMV path (small T), the
@@ -46,18 +58,33 @@ KERNELS = {
              "expert_gate_up": "k_ggemm<M_S13> + k_ggemm<M_G13>", "expert_down": "k_ggemm<M_S2> + k_ggemm<M_D2>",
              "combine": "k_combine"},
 }
-
+# steps per timed window of each workload when it is measured as an entry of
+# `configs` (about 10-50 ms of GPU time per window)
+CONFIG_STEPS = {0: 200, 1: 200, 2: 20, 3: 5, 4: 20}
+WINDOWS = 3
 
 # HBM bytes per dispatch measured by rocprofv3 (FETCH_SIZE and WRITE_SIZE,
-# each scaled by what the counter reads for a plain 256 MiB copy), for the
-# kernel as it stands, at decode T=1; the summary and the commands are in
-# profiles/moe_layer_kernels__k3-moe-decode-T1.md.  A kernel changed since
-# its counters were taken has no entry here (traffic: null).
-MEASURED_TRAFFIC = {"k_dec1_gateup": 289388242}
+# each scaled by what the counter reads for a plain 256 MiB copy) at decode
+# T=1, with the SHA-256 prefix of the kernel's source file when the counters
+# were taken: a kernel whose source has changed since reports traffic null.
+# The summary and the commands are in profiles/moe_layer_kernels__k3-moe-decode-T1.md.
+MEASURED_TRAFFIC = {}
 
 
 def log(*a):
     print(*a, file=sys.stderr, flush=True)
+
+
+def source_sha(rel: str) -> str:
+    with open(os.path.join(ROOT, "quantized_expert_gemv_sigmoid_amd", "csrc", rel), "rb") as f:
+        return hashlib.sha256(f.read()).hexdigest()[:16]
+
+
+def measured_traffic(kernel: str):
+    m = MEASURED_TRAFFIC.get(kernel)
+    if m is None or source_sha(m["source"]) != m["sha"]:
+        return None
+    return m["bytes"]
 
 
 def phase_bytes(shape, T, counts, kind):
@@ -151,16 +178,186 @@ def copy_gbs(torch, nbytes: int, reps: int) -> float:
     return 2 * nbytes / (ms * 1e-3) / 1e9
 
 
+def measure(widx, steps, warmup, pool, use_graph, cpu_seconds, hbm_copy_gbs):
+    """Load workload widx, time `WINDOWS` windows of `steps` graph replays
+    (window 0 first: the headline's K steps), time every phase with events,
+    run the CPU oracle sample, free everything.  Returns one result dict."""
+    import torch
+    import synth
+    import synth.device as sdev
+    import quantized_expert_gemv_sigmoid_amd as moe
+
+    wl = synth.WORKLOADS[widx]
+    shape, T, L = wl.shape, wl.tokens, wl.layers
+    d = shape.d_model
+    t_load = time.perf_counter()
+    # L independent layers (own weights, own tokens), run one after another
+    # on one stream; the stacked workload shares one selection bias
+    tensors, descs = [], []
+    for l in range(L):
+        log(f"bench: {wl.name}: layer {l}: uploading {shape.n_experts} experts "
+            f"({shape.n_experts * shape.expert_bytes / 1e9:.2f} GB MXFP4)")
+        t = sdev.upload_layer(shape, wl.seed, l, zipf=wl.zipf_bias)
+        tensors.append(t)
+        descs.append(moe.make_desc(shape.n_experts, shape.top_k, d, shape.d_ffn, shape.n_shared, t))
+    npool = max(1, min(pool, (1 << 16) // T))
+    pools = [synth.x_tokens(shape, wl.seed, l, npool * T).reshape(npool, T, d) for l in range(L)]
+    xs = [sdev.tokens_to_device(pools[l].reshape(npool * T, d)).view(npool, T, d) for l in range(L)]
+    ws = moe.workspace(descs[0], T)
+    outs = [torch.empty((T, d), dtype=torch.int16, device="cuda") for _ in range(L)]
+    ids = torch.empty((T, shape.top_k), dtype=torch.int32, device="cuda")
+    wts = torch.empty((T, shape.top_k), dtype=torch.float32, device="cuda")
+    cnt = torch.empty(shape.n_experts, dtype=torch.int32, device="cuda")
+    counts = [[None] * npool for _ in range(L)]  # [layer][batch]
+    for l in range(L):
+        for i in range(npool):
+            moe.route(descs[l], xs[l][i], T, ids, wts, cnt, ws)
+            torch.cuda.synchronize()
+            counts[l][i] = cnt.cpu().numpy().copy()
+    load_s = time.perf_counter() - t_load
+    path = moe.path_for(descs[0], T)
+    # (the fused one-token kernels serve T = 1 on the GEMV path)
+    kind = "decode1" if (path == 1 and T == 1) else {1: "gemv", 2: "mfma"}[path]
+
+    def step(i):
+        for l in range(L):
+            moe.layer(descs[l], xs[l][i % npool], T, outs[l], None, moe.OUT_BF16, ws)
+
+    stream = torch.cuda.current_stream()
+    for i in range(warmup):
+        step(i)
+    torch.cuda.synchronize()
+
+    K = steps
+    start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    windows = []
+    graphs = None
+    if use_graph:
+        # one HIP graph per token batch of the pool, holding all L layers (the
+        # batch's addresses are baked into its graph, as a decode loop's fixed
+        # input buffers would be)
+        graphs = []
+        for i in range(npool):
+            g = torch.cuda.CUDAGraph()
+            with torch.cuda.graph(g):
+                step(i)
+            graphs.append(g)
+        for i in range(warmup):
+            graphs[i % npool].replay()
+        torch.cuda.synchronize()
+    for wdx in range(WINDOWS):
+        torch.cuda.synchronize()
+        start.record(stream)
+        for i in range(K):
+            if graphs is not None:
+                graphs[(wdx * K + i) % npool].replay()
+            else:
+                step(wdx * K + i)
+        end.record(stream)
+        torch.cuda.synchronize()
+        windows.append(start.elapsed_time(end) / K)
+
+    # per-phase durations: every layer of every step with its own events
+    evs = [[[torch.cuda.Event(enable_timing=True) for _ in range(moe.TIMED_EVENTS)] for _ in range(L)]
+           for _ in range(K)]
+    for row in evs:  # torch creates an event's HIP handle at its first record
+        for lay in row:
+            for e in lay:
+                e.record(stream)
+    torch.cuda.synchronize()
+    start.record(stream)
+    for i in range(K):
+        for l in range(L):
+            moe.layer_timed(descs[l], xs[l][i % npool], T, outs[l], None, moe.OUT_BF16, ws, evs[i][l],
+                            stream=stream)
+    end.record(stream)
+    torch.cuda.synchronize()
+    eager_ms = start.elapsed_time(end) / K
+
+    ph_ms = {p: float(np.mean([evs[i][l][j].elapsed_time(evs[i][l][j + 1]) for i in range(K) for l in range(L)]))
+             for j, p in enumerate(PHASES)}
+    ph_bytes = {p: float(np.mean([phase_bytes(shape, T, counts[l][i % npool], kind)[p]
+                                  for i in range(K) for l in range(L)]))
+                for p in PHASES}
+    ph_flops = phase_flops(shape, T)
+    step_bytes = L * sum(ph_bytes.values())  # per step, all layers
+    dom = max(("expert_gate_up", "expert_down"), key=lambda p: ph_ms[p])
+    # the bound of the dominant phase: its flops per algorithmic HBM byte
+    # against the machine balance (peak flops / peak bytes, 312 F/B); half of
+    # it or more counts as matrix-core bound
+    intensity = ph_flops[dom] / max(ph_bytes[dom], 1.0)
+    if kind == "mfma" and intensity >= 0.5 * PEAK_BF16_TFLOPS * 1e12 / (PEAK_HBM_GBS * 1e9):
+        # a dense contraction on the matrix cores (bf16 after the in-register
+        # MXFP4 decode): against the bf16 MFMA peak
+        achieved = ph_flops[dom] / (ph_ms[dom] * 1e-3) / 1e12
+        roofline = {"bound": "mfma", "achieved": round(achieved, 1), "peak": PEAK_BF16_TFLOPS,
+                    "unit": "TFLOP/s", "frac": round(achieved / PEAK_BF16_TFLOPS, 4), "traffic": None,
+                    "kernel": KERNELS[kind][dom], "flops_per_launch": int(ph_flops[dom]),
+                    "avg_launch_us": round(ph_ms[dom] * 1e3, 2)}
+    else:
+        achieved = ph_bytes[dom] / (ph_ms[dom] * 1e-3) / 1e9
+        roofline = {"bound": "hbm", "achieved": round(achieved, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
+                    "frac": round(achieved / PEAK_HBM_GBS, 4),
+                    "traffic": measured_traffic(KERNELS[kind][dom].split()[0]) if T == 1 else None,
+                    "kernel": KERNELS[kind][dom], "bytes_per_launch": int(ph_bytes[dom]),
+                    "avg_launch_us": round(ph_ms[dom] * 1e3, 2),
+                    "frac_of_copy": round(achieved / hbm_copy_gbs, 4)}
+    ms = windows[0]
+    med = float(np.median(windows))
+    step_flops = L * flops(shape, T)
+    config = {"workload": wl.name, "n_experts": shape.n_experts, "top_k": shape.top_k,
+              "n_shared": shape.n_shared, "d_model": d, "d_ffn": shape.d_ffn,
+              "tokens": T, "layers": L, "selection_bias": "zipf" if wl.zipf_bias else "none",
+              "weights": "mxfp4 (e2m1 + e8m0/32) routed, bf16 shared",
+              "path": kind, "token_pool": npool,
+              "launch": "hip graph replay" if graphs is not None else "eager"}
+    res = {
+        "config": config, "steps": K, "ms_per_step": round(ms, 5),
+        "ms_per_step_windows": [round(w, 5) for w in windows],
+        "ms_per_step_median": round(med, 5),
+        "ms_per_step_spread": round((max(windows) - min(windows)) / med, 4),
+        "tok_s": round(T / (ms * 1e-3), 2), "tok_s_median": round(T / (med * 1e-3), 2),
+        "ms_per_step_eager": round(eager_ms, 5),
+        "step_hbm_gbs": round(step_bytes / (med * 1e-3) / 1e9, 1),
+        "step_hbm_frac": round(step_bytes / (med * 1e-3) / 1e9 / PEAK_HBM_GBS, 4),
+        "step_frac_of_copy": round(step_bytes / (med * 1e-3) / 1e9 / hbm_copy_gbs, 4),
+        "step_tflops": round(step_flops / (med * 1e-3) / 1e12, 3),
+        "step_mfma_frac": round(step_flops / (med * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 4),
+        "step_bytes": int(step_bytes), "step_flops": int(step_flops),
+        "distinct_experts_per_layer": round(float(np.mean([(c > 0).sum() for cl in counts for c in cl])), 1),
+        # (phases with no kernel of their own on this path, such as the router,
+        # top-k and combine of the fused one-token path, are null: the events
+        # around them measure only their own overhead)
+        "phase_us": {p: (round(v * 1e3, 2) if KERNELS[kind][p][0] != "-" else None) for p, v in ph_ms.items()},
+        "roofline": roofline,
+        "load_s": round(load_s, 1),
+    }
+    if cpu_seconds > 0:
+        log(f"bench: {wl.name}: timing the CPU oracle on a bounded sample")
+        res["cpu_baseline"] = cpu_baseline(shape, wl.seed, wl.zipf_bias, pools, cpu_seconds)
+    # free this workload's device memory before the next one is loaded
+    del graphs, tensors, descs, xs, ws, outs, ids, wts, cnt, evs
+    import gc
+    gc.collect()
+    torch.cuda.synchronize()
+    torch.cuda.empty_cache()
+    return res
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=200)
     ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--workload", type=int, default=1,
-                    help="index into synth.WORKLOADS (1: decode T=1, 2: T=64, 3: prefill T=4096, "
-                         "4: 12 stacked layers with the Zipf selection bias, T=1)")
+                    help="headline workload, an index into synth.WORKLOADS (0: tiny, 1: decode T=1, 2: T=64, "
+                         "3: prefill T=4096, 4: 12 stacked layers with the Zipf selection bias, T=1)")
+    ap.add_argument("--configs", default="0,2,3,4",
+                    help="other workloads measured into `configs` (comma-separated indexes; '' for none)")
     ap.add_argument("--pool", type=int, default=32, help="distinct token batches cycled over")
-    ap.add_argument("--cpu-seconds", type=float, default=15.0)
+    ap.add_argument("--cpu-seconds", type=float, default=15.0, help="oracle time of the headline's CPU sample")
+    ap.add_argument("--config-cpu-seconds", type=float, default=4.0,
+                    help="oracle time of each config's CPU sample")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-graph", action="store_true", help="time eager launches instead of HIP graph replays")
     ap.add_argument("--copy-mib", type=int, default=0,
@@ -198,151 +395,43 @@ def main():
         print(json.dumps({"mv_matrix_bytes": rows * cols * 2, "steps": args.steps,
                           "mv_read_gbs": round(rows * cols * 2 / (ms * 1e-3) / 1e9, 1)}), flush=True)
         return
+    torch.cuda.set_device(0)
     # a plain device copy of 1 GiB (four times the last-level cache), read and
     # written bytes over its time: the HBM rate an ordinary kernel reaches on
     # this GPU, reported beside the published peak
     hbm_copy_gbs = copy_gbs(torch, 1 << 30, 20)
-    import synth
-    import synth.device as sdev
-    import quantized_expert_gemv_sigmoid_amd as moe
-
-    wl = synth.WORKLOADS[args.workload]
-    shape, T, L = wl.shape, wl.tokens, wl.layers
-    d = shape.d_model
-    torch.cuda.set_device(0)
-    # L independent layers (own weights, own tokens), run one after another
-    # on one stream; the stacked workload shares one selection bias
-    tensors, descs = [], []
-    for l in range(L):
-        log(f"bench: {wl.name}: layer {l}: uploading {shape.n_experts} experts "
-            f"({shape.n_experts * shape.expert_bytes / 1e9:.2f} GB MXFP4)")
-        t = sdev.upload_layer(shape, wl.seed, l, zipf=wl.zipf_bias)
-        tensors.append(t)
-        descs.append(moe.make_desc(shape.n_experts, shape.top_k, d, shape.d_ffn, shape.n_shared, t))
-    npool = max(1, min(args.pool, (1 << 16) // T))
-    pools = [synth.x_tokens(shape, wl.seed, l, npool * T).reshape(npool, T, d) for l in range(L)]
-    xs = [sdev.tokens_to_device(pools[l].reshape(npool * T, d)).view(npool, T, d) for l in range(L)]
-    ws = moe.workspace(descs[0], T)  # zero-filled (the control block must start at zero)
-    outs = [torch.empty((T, d), dtype=torch.int16, device="cuda") for _ in range(L)]
-    ids = torch.empty((T, shape.top_k), dtype=torch.int32, device="cuda")
-    wts = torch.empty((T, shape.top_k), dtype=torch.float32, device="cuda")
-    cnt = torch.empty(shape.n_experts, dtype=torch.int32, device="cuda")
-    counts = [[None] * npool for _ in range(L)]  # [layer][batch]
-    for l in range(L):
-        for i in range(npool):
-            moe.route(descs[l], xs[l][i], T, ids, wts, cnt, ws)
-            torch.cuda.synchronize()
-            counts[l][i] = cnt.cpu().numpy().copy()
-    path = moe.path_for(descs[0], T)
-    # (the fused one-token kernels serve T = 1 on the GEMV path)
-    kind = "decode1" if (path == 1 and T == 1) else {1: "gemv", 2: "mfma"}[path]
-
-    def step(i):
-        for l in range(L):
-            moe.layer(descs[l], xs[l][i % npool], T, outs[l], None, moe.OUT_BF16, ws)
-
-    stream = torch.cuda.current_stream()
-    for i in range(args.warmup):
-        step(i)
-    torch.cuda.synchronize()
-
-    K = args.steps
-    start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    graph_ms = None
-    if not args.no_graph:
-        # one HIP graph per token batch of the pool, holding all L layers (the
-        # batch's addresses are baked into its graph, as a decode loop's fixed
-        # input buffers would be)
-        graphs = []
-        for i in range(npool):
-            g = torch.cuda.CUDAGraph()
-            with torch.cuda.graph(g):
-                step(i)
-            graphs.append(g)
-        for i in range(args.warmup):
-            graphs[i % npool].replay()
-        torch.cuda.synchronize()
-        start.record(stream)
-        for i in range(K):
-            graphs[i % npool].replay()
-        end.record(stream)
-        torch.cuda.synchronize()
-        graph_ms = start.elapsed_time(end) / K
-
-    # per-phase durations: every layer of every step with its own events
-    evs = [[[torch.cuda.Event(enable_timing=True) for _ in range(moe.TIMED_EVENTS)] for _ in range(L)]
-           for _ in range(K)]
-    for row in evs:  # torch creates an event's HIP handle at its first record
-        for lay in row:
-            for e in lay:
-                e.record(stream)
-    torch.cuda.synchronize()
-    start.record(stream)
-    for i in range(K):
-        for l in range(L):
-            moe.layer_timed(descs[l], xs[l][i % npool], T, outs[l], None, moe.OUT_BF16, ws, evs[i][l],
-                            stream=stream)
-    end.record(stream)
-    torch.cuda.synchronize()
-    eager_ms = start.elapsed_time(end) / K
-    ms = graph_ms if graph_ms is not None else eager_ms
-
-    ph_ms = {p: float(np.mean([evs[i][l][j].elapsed_time(evs[i][l][j + 1]) for i in range(K) for l in range(L)]))
-             for j, p in enumerate(PHASES)}
-    ph_bytes = {p: float(np.mean([phase_bytes(shape, T, counts[l][i % npool], kind)[p]
-                                  for i in range(K) for l in range(L)]))
-                for p in PHASES}
-    ph_flops = phase_flops(shape, T)
-    step_bytes = L * sum(ph_bytes.values())  # per step, all layers
-    dom = max(("expert_gate_up", "expert_down"), key=lambda p: ph_ms[p])
-    # the bound of the dominant phase: its flops per algorithmic HBM byte
-    # against the machine balance (peak flops / peak bytes, 312 F/B); half of
-    # it or more counts as matrix-core bound
-    intensity = ph_flops[dom] / max(ph_bytes[dom], 1.0)
-    if kind == "mfma" and intensity >= 0.5 * PEAK_BF16_TFLOPS * 1e12 / (PEAK_HBM_GBS * 1e9):
-        # a dense contraction on the matrix cores (bf16 after the in-register
-        # MXFP4 decode): against the bf16 MFMA peak
-        achieved = ph_flops[dom] / (ph_ms[dom] * 1e-3) / 1e12
-        roofline = {"bound": "mfma", "achieved": round(achieved, 1), "peak": PEAK_BF16_TFLOPS,
-                    "unit": "TFLOP/s", "frac": round(achieved / PEAK_BF16_TFLOPS, 4), "traffic": None,
-                    "kernel": KERNELS[kind][dom], "flops_per_launch": int(ph_flops[dom]),
-                    "avg_launch_us": round(ph_ms[dom] * 1e3, 2)}
-    else:
-        achieved = ph_bytes[dom] / (ph_ms[dom] * 1e-3) / 1e9
-        roofline = {"bound": "hbm", "achieved": round(achieved, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
-                    "frac": round(achieved / PEAK_HBM_GBS, 4),
-                    "traffic": MEASURED_TRAFFIC.get(KERNELS[kind][dom].split()[0]) if kind == "decode1" else None,
-                    "kernel": KERNELS[kind][dom], "bytes_per_launch": int(ph_bytes[dom]),
-                    "avg_launch_us": round(ph_ms[dom] * 1e3, 2),
-                    "frac_of_copy": round(achieved / hbm_copy_gbs, 4)}
-    tok_s = T / (ms * 1e-3)
-    layer_gbs = step_bytes / (ms * 1e-3) / 1e9
-    config = {"workload": wl.name, "n_experts": shape.n_experts, "top_k": shape.top_k,
-              "n_shared": shape.n_shared, "d_model": d, "d_ffn": shape.d_ffn,
-              "tokens": T, "layers": L, "selection_bias": "zipf" if wl.zipf_bias else "none",
-              "weights": "mxfp4 (e2m1 + e8m0/32) routed, bf16 shared",
-              "path": kind, "token_pool": npool,
-              "launch": "hip graph replay" if graph_ms is not None else "eager"}
+    use_graph = not args.no_graph
+    head = measure(args.workload, args.steps, args.warmup, args.pool, use_graph,
+                   0.0 if args.no_cpu_baseline else args.cpu_seconds, hbm_copy_gbs)
     result = {
-        "metric": METRIC, "value": round(tok_s, 2), "unit": "tok/s", "n_gpus": 1, "steps": K,
-        "warmup": args.warmup, "ms_per_step": round(ms, 5), "higher_is_better": True,
-        "scaling": "weak", "vs_baseline": None, "dtype": "fp32",
-        "data": "synthetic",
-        "config": config,
-        "ms_per_step_eager": round(eager_ms, 5),
-        "step_hbm_gbs": round(layer_gbs, 1), "step_hbm_frac": round(layer_gbs / PEAK_HBM_GBS, 4),
-        "hbm_copy_gbs": round(hbm_copy_gbs, 1), "step_frac_of_copy": round(layer_gbs / hbm_copy_gbs, 4),
-        "step_tflops": round(L * flops(shape, T) / (ms * 1e-3) / 1e12, 3),
-        # (phases with no kernel of their own on this path, such as the router,
-        # top-k and combine of the fused one-token path, are null: the events
-        # around them measure only their own overhead)
-        "phase_us": {p: (round(v * 1e3, 2) if KERNELS[kind][p][0] != "-" else None) for p, v in ph_ms.items()},
-        "roofline": roofline,
+        "metric": METRIC, "value": head["tok_s"], "unit": "tok/s", "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "ms_per_step": head["ms_per_step"], "higher_is_better": True,
+        "scaling": "weak", "vs_baseline": None, "dtype": DTYPE, "dtype_detail": DTYPE_DETAIL,
+        "data": "synthetic (seeded; MXFP4 codes and scales of the workload recipe, random-init weights)",
+        "config": head["config"],
+        "ms_per_step_windows": head["ms_per_step_windows"],
+        "ms_per_step_median": head["ms_per_step_median"],
+        "ms_per_step_spread": head["ms_per_step_spread"],
+        "ms_per_step_eager": head["ms_per_step_eager"],
+        "step_hbm_gbs": head["step_hbm_gbs"], "step_hbm_frac": head["step_hbm_frac"],
+        "hbm_copy_gbs": round(hbm_copy_gbs, 1), "step_frac_of_copy": head["step_frac_of_copy"],
+        "step_tflops": head["step_tflops"],
+        "phase_us": head["phase_us"],
+        "roofline": head["roofline"],
     }
-    if not args.no_cpu_baseline:
-        log("bench: timing the CPU oracle on a bounded sample")
-        result["cpu_baseline"] = cpu_baseline(shape, wl.seed, wl.zipf_bias, pools,
-                                              args.cpu_seconds)
+    if "cpu_baseline" in head:
+        result["cpu_baseline"] = head["cpu_baseline"]
+    idx = [int(c) for c in args.configs.split(",") if c.strip() != ""]
+    configs = []
+    for c in idx:
+        if c == args.workload:
+            continue
+        r = measure(c, CONFIG_STEPS.get(c, 20), min(args.warmup, 5), args.pool, use_graph,
+                    0.0 if args.no_cpu_baseline else args.config_cpu_seconds, hbm_copy_gbs)
+        log(f"bench: {r['config']['workload']}: {r['ms_per_step_median']} ms/step (median of {WINDOWS} windows)")
+        configs.append(r)
+    if configs:
+        result["configs"] = configs
     print(json.dumps(result), flush=True)
 
 
