@@ -12,21 +12,24 @@
 // experts (bf16) and the router (fp32) run through the same kernel as extra
 // groups.
 //
-// Block = 4 waves (one per SIMD), 256 output columns: wave w owns 64 of them
-// as two 32-column tiles of v_mfma_f32_32x32x16_{bf16,f16} (the 32x32 shape
-// sustains about twice the rate of 16x16x32 from one wave), and all M rows
-// of the group in passes of up to 128 (four 32-row tiles, the tile count a
-// compile-time parameter).  K runs in stages:
-//  - A (token rows, bf16 or fp16) is staged through LDS, double buffered, in
-//    16-byte pieces XOR-swizzled by row so the fragment reads are bank
-//    conflict free;
-//  - B (weights) is staged through LDS too, copied as 128-byte runs of each
-//    column; a lane reads its fragment for a whole A stage at once (two MX
-//    blocks), decodes it in registers with v_cvt_scalef32_pk_{bf16,f16}_fp4
-//    and its E8M0 scales (exact), and feeds the MFMAs;
-//  - global loads for stages ahead are in flight while a stage is multiplied,
-//    and the fragment reads / decodes of the next MFMA step overlap the
-//    current step's MFMAs.
+// Block = 8 waves, two per SIMD, one block per CU, and 256 output columns:
+// the two waves w and w + 4 of a SIMD own columns 64 (w % 4) .. + 63 as two
+// 32-column tiles of v_mfma_f32_32x32x16_{bf16,f16}, and split the pass's
+// 32-row tiles between them (up to four tiles, 128 rows, per pass), so
+// neither operand is read twice and no partial sums are merged, while one
+// wave's waits overlap the other's MFMAs.  K runs in stages (128 for MXFP4
+// weights, 64 for bf16) that hold, in LDS, the pass's A rows (token rows,
+// bf16 or fp16), the block's 256 B columns (weights) and, for MXFP4, their
+// scale bytes.  A ring of three to six stages (as many as 150 KB holds) is
+// filled by direct 16-byte global -> LDS loads (no registers) issued by all
+// waves, as many stages ahead as the ring allows; one barrier per stage.
+//  - A load writes lane i's 16 bytes at 16 i of its 1 KB LDS segment, so
+//    the XOR swizzles that keep the fragment reads bank-conflict free are
+//    applied on the global side (which piece a lane fetches).
+//  - B columns are fetched as runs of 64 (MXFP4) or 128 (bf16) contiguous
+//    bytes per column, four or eight lanes per column and load.
+//  - A lane decodes its MX blocks in registers with
+//    v_cvt_scalef32_pk_{bf16,f16}_fp4 and their E8M0 scales (exact).
 // The K order inside a stage is permuted identically for A and B (lane half
 // h of a column holds the stage's h-th half of K), which is what lets one
 // lane own whole MX blocks.
@@ -44,10 +47,14 @@ namespace moe {
 
 typedef float f32x16_t __attribute__((ext_vector_type(16)));
 
-constexpr int GT = 256;          // threads per block: 4 waves, one per SIMD
-constexpr int GN = 256;          // output columns per block (64 per wave: two 32-column tiles)
-constexpr int GMT = 4;           // 32-row MFMA tiles per M pass
-constexpr int GM = GMT * 32;     // 128 rows per M pass
+constexpr int GT = 512;              // threads per block: 8 waves, two per SIMD
+constexpr int GN = 256;              // output columns per block (64 per SIMD: two 32-column tiles)
+constexpr int GMT = 4;               // 32-row MFMA tiles per M pass, bf16 weights
+constexpr int GMT4 = 3;              // 32-row MFMA tiles per M pass (at most), MXFP4 weights
+constexpr int GM = GMT * 32;         // rows per M pass
+constexpr int kLdsBytes = 152 * 1024;   // LDS of a block (one block per CU)
+constexpr int kScaleBytes = 32 * 1024;  // MXFP4: the block's scale rows (256 of at most 128 bytes)
+constexpr uint32_t kPast = 0xF0000000u;  // a buffer offset past every resource: loads return 0, read nothing
 
 enum Mode { M_G13 = 0, M_D2 = 1, M_S13 = 2, M_S2 = 3, M_R = 4 };
 
@@ -69,8 +76,6 @@ struct GemmParams {
 
 // ---------------------------------------------------------------- helpers
 
-__device__ __forceinline__ uint4 gld16(const void *p) { return *reinterpret_cast<const uint4 *>(p); }
-
 // LDS pointers keep their address space through every helper (generic
 // pointers would let the compiler fall back to flat instructions)
 #define LDS __attribute__((address_space(3)))
@@ -79,23 +84,55 @@ __device__ __forceinline__ uint4 lds_ld16(const LDS uint8_t *p)
 {
     return __builtin_bit_cast(uint4, *reinterpret_cast<const LDS u32x4_t *>(p));
 }
-__device__ __forceinline__ void lds_st16(LDS uint8_t *p, uint4 v)
+
+// a buffer resource over [base, base + bytes) (wave-uniform: the copies
+// below take it in scalar registers)
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t grsrc(const void *base, uint32_t bytes)
 {
-    *reinterpret_cast<LDS u32x4_t *>(p) = __builtin_bit_cast(u32x4_t, v);
+    const uint64_t a = (uint64_t)(uintptr_t)base;
+    const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)a);
+    const uint32_t hi = __builtin_amdgcn_readfirstlane((uint32_t)(a >> 32));
+    void *ub = (void *)(uintptr_t)(((uint64_t)hi << 32) | lo);
+    return __builtin_amdgcn_make_buffer_rsrc(ub, (short)0, (int)__builtin_amdgcn_readfirstlane(bytes), 0x00020000);
 }
-__device__ __forceinline__ void lds_st4(LDS uint8_t *p, uint32_t v) { *reinterpret_cast<LDS uint32_t *>(p) = v; }
-
-
-// element offset of 16-byte piece q of row r in an LDS stage of KC columns.
-// A fragment read takes one piece of 16 consecutive rows per 16 lanes, and
-// the LDS serves 256 bytes (16 pieces' worth of banks) at a time: 256-byte
-// rows XOR the piece with r & 15; 128-byte rows (two per 256 bytes) with
-// (r >> 1) & 7, so that rows r and r + 8 do not share banks.
-template <int KC>
-__device__ __forceinline__ int lds_off(int r, int q)
+__device__ __forceinline__ uint4 gbld16(__amdgpu_buffer_rsrc_t r, uint32_t voff)
 {
-    if constexpr (KC == 128) return r * KC + ((q ^ (r & 15)) << 3);
-    else return r * KC + ((q ^ ((r >> 1) & 7)) << 3);
+    return __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(r, (int)voff, 0, 0));
+}
+__device__ __forceinline__ uint32_t gbld1(__amdgpu_buffer_rsrc_t r, uint32_t voff)
+{
+    return __builtin_amdgcn_raw_buffer_load_b8(r, (int)voff, 0, 0);
+}
+// Direct global -> LDS loads: lane i's bytes at voff of r go to LDS at
+// dst + size * i (dst wave-uniform, in M0).  Written out: the compiler,
+// which cannot tell such a copy from the LDS reads of another ring slot,
+// would otherwise wait for every copy in flight before each LDS read.  The
+// caller orders the copies with explicit waits (wait_vm) and barriers; M0 is
+// restored for the compiler's own uses.
+__device__ __forceinline__ void gbld16_lds(__amdgpu_buffer_rsrc_t r, LDS uint8_t *dst, uint32_t voff)
+{
+    const uint32_t m0v = (uint32_t)(uintptr_t)dst;
+    uint32_t save;
+    asm volatile("s_mov_b32 %0, m0\n\ts_mov_b32 m0, %1\n\tbuffer_load_dwordx4 %2, %3, 0 offen lds\n\ts_mov_b32 m0, %0"
+                 : "=&s"(save)
+                 : "s"(m0v), "v"(voff), "s"(r)
+                 : "memory");
+}
+// workgroup barrier that no memory access is moved across
+__device__ __forceinline__ void block_barrier()
+{
+    asm volatile("" ::: "memory");
+    __builtin_amdgcn_s_barrier();
+    asm volatile("" ::: "memory");
+}
+
+// s_waitcnt vmcnt(N) lgkmcnt(0): at most N of this wave's memory loads (and
+// direct-to-LDS copies) still in flight, and all of its LDS accesses done
+template <int N>
+__device__ __forceinline__ void wait_vm()
+{
+    static_assert(N >= 0 && N < 64, "vmcnt field");
+    __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (0 << 8));
 }
 
 __device__ __forceinline__ float e8m0f(uint32_t b)
@@ -139,38 +176,6 @@ __device__ __forceinline__ void split_f16(const f16x8_t a, bf16x8_t &hi, bf16x8_
     }
 }
 
-// ----------------------------------------------------- per-mode geometry
-
-template <int MODE>
-struct Cfg {
-    static constexpr bool kFp4 = (MODE == M_G13 || MODE == M_D2);
-    static constexpr bool kGated = (MODE == M_G13 || MODE == M_S13);
-    // K per A stage and per B stage.  A B stage holds 128 bytes of every
-    // column (256 fp4 codes = 8 MX blocks, or 64 bf16 values), loaded as
-    // 128-byte runs.
-    static constexpr int KCA = kFp4 ? 128 : 64;
-    static constexpr int KCB = kFp4 ? 256 : 64;
-    static constexpr int R = KCB / KCA;                 // A stages per B stage
-    static constexpr int STEPS = KCA / 16;              // MFMA K steps per A stage
-    static constexpr int QPR = KCA / 8;                 // 16-byte A pieces per row of a stage
-    static constexpr int RPP = GT / QPR;                // A rows staged per pass
-    static constexpr int BSC = kFp4 ? KCB / 32 : 0;     // scale bytes per column per B stage
-    static constexpr int BPASS = GN * 8 / GT;           // B staging passes (32 columns each)
-};
-
-// K order inside an A stage: MFMA step st, lane half kh (lane / 32) and
-// element i (0..7) of a fragment multiply K index kh * (KCA / 2) + st * 8 + i
-// of the stage, for A and B alike.  A lane's fragments over the stage are
-// then one contiguous run of K: for MXFP4 two whole MX blocks (64 codes, two
-// scales), read from LDS as two 16-byte pieces.  A-stage piece q (8
-// elements) is kh * STEPS + st.
-
-// byte offset of 16-byte piece p of column c inside a B stage (8 pieces per
-// column, XOR-swizzled with (c >> 1) & 7 so that the fragment reads of 16
-// consecutive columns, two per 256 bytes, hit distinct banks)
-__device__ __forceinline__ int b_off(int c, int p) { return c * 128 + ((p ^ ((c >> 1) & 7)) << 4); }
-
-
 __device__ __forceinline__ f32x16_t mfma32(bf16x8_t a, bf16x8_t b, f32x16_t c)
 {
     return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
@@ -180,478 +185,482 @@ __device__ __forceinline__ f32x16_t mfma32(f16x8_t a, f16x8_t b, f32x16_t c)
     return __builtin_amdgcn_mfma_f32_32x32x16_f16(a, b, c, 0, 0, 0);
 }
 
+// ----------------------------------------------------- per-mode geometry
+
+template <int MODE>
+struct Cfg {
+    static constexpr bool kFp4 = (MODE == M_G13 || MODE == M_D2);
+    static constexpr bool kGated = (MODE == M_G13 || MODE == M_S13);
+    static constexpr int KS = kFp4 ? 128 : 64;     // K per stage
+    static constexpr int STEPS = KS / 16;          // MFMA K steps per stage
+    static constexpr int AROW = KS * 2;            // bytes of one A row of a stage
+    static constexpr int ASLOTS = AROW / 16;       // 16-byte pieces of an A row
+    static constexpr int BCOL = kFp4 ? KS / 2 : KS * 2;  // bytes of one B column of a stage
+    static constexpr int BP = BCOL / 16;           // 16-byte pieces of a B column
+};
+
+// The stage ring of an MT-tile pass: A rows and B columns.  With MXFP4
+// weights it follows the block's scale rows in LDS.
+template <int MODE, int MT>
+struct Ring {
+    using C = Cfg<MODE>;
+    static constexpr int BASE = C::kFp4 ? kScaleBytes : 0;
+    static constexpr int ABYTES = MT * 32 * C::AROW;
+    static constexpr int BBYTES = GN * C::BCOL;
+    static constexpr int STAGE = ABYTES + BBYTES;
+    static constexpr int NMAX = (kLdsBytes - BASE) / STAGE;
+    static constexpr int NST = NMAX < 6 ? NMAX : 6;
+    // copies per wave per stage (1 KB per 16-byte copy instruction, 8 waves)
+    static constexpr int NA = ABYTES / 1024 / 8;
+    static constexpr int NB = BBYTES / 1024 / 8;
+    static_assert(ABYTES % 8192 == 0 && BBYTES % 8192 == 0, "copies");
+    static_assert(NST >= 3, "ring depth");
+};
+
+// K order inside a stage: MFMA step st, lane half kh (lane / 32) and element
+// i (0..7) of a fragment multiply K index kh * KS / 2 + st * 8 + i of the
+// stage, for A and B alike.  A lane's A fragments of a row are then the
+// 16-byte pieces q = kh * STEPS + st of that row, and its B fragments of a
+// column one run of K: whole MX blocks for MXFP4.
+//
+// Layout of a stage in LDS, each part XOR-swizzled so that the fragment
+// reads (one 16-byte piece of 16 consecutive rows or columns per 16 lanes;
+// the LDS serves 256 bytes, 16 pieces' worth of banks, at a time) hit
+// distinct banks:
+//  - A row r at r * AROW, its piece q at slot q ^ swz_a(r): r & 15 for
+//    256-byte rows, (r >> 1) & 7 for 128-byte rows (rows r, r + 1 on the two
+//    bank halves);
+//  - B column c at c * BCOL, its piece p at slot p ^ swz_b(c): (c >> 2) & 3
+//    for 64-byte columns, (c >> 1) & 7 for 128-byte ones;
+//  - MXFP4 scales, loaded once per block ahead of the ring: a 128-byte row
+//    (the K / 32 <= 128 scale bytes of a weight row) per column, ordered by
+//    matrix and feature (gate / up feature f of a gated tile is row
+//    up * 128 + f - 128 tile, column c of a down tile row c), piece q of
+//    row R at slot q ^ (R & 7).
+template <int MODE>
+__device__ __forceinline__ int swz_a(int r)
+{
+    return Cfg<MODE>::ASLOTS == 16 ? (r & 15) : ((r >> 1) & 7);
+}
+template <int MODE>
+__device__ __forceinline__ int swz_b(int c)
+{
+    return Cfg<MODE>::BP == 4 ? ((c >> 2) & 3) : ((c >> 1) & 7);
+}
+
 // Per-block geometry: which group (expert / shared expert / router) and
 // which 256-column tile this block computes.
 struct Blk {
     int group, tile, mb, ks;
-    int M, base, e, K, nA, nB, ncols;
-    int kst0;  // first A stage of the block's K range
+    int M, base, e, K, nS, ncols;
+    int kst0;  // first stage of the block's K range
 };
 
-// Global sources of this thread's B staging copies: 16-byte piece (t % 8)
-// of block columns ps * 32 + t / 8 (ps < BPASS), and (MXFP4) the 8 scale
-// bytes per stage of column t.  Offsets are 32-bit bytes from a 64-bit base.
-// Every column of an expert's tile is in range (the path requires d and F
-// to be multiples of 256); the router's columns past E re-read row E - 1
-// and are never stored.
-template <int MODE>
-struct BSrc {
-    const uint8_t *base0, *base1;  // gated: gate / up weights (even / odd passes)
-    uint32_t off;                  // this thread's pass-0 column row + piece
-    uint32_t pstride;              // bytes between the rows of consecutive passes (gated: pass pairs)
-    uint32_t roff[MODE == M_R ? Cfg<MODE>::BPASS : 1];  // router: clamped per-pass rows
-    const uint8_t *sbase;          // MXFP4 scales of column t: sbase + soff + stage offset
-    uint32_t soff;
-};
-
-// block column c (0..255) of a gated tile -> feature and gate / up: wave
-// w = c / 64 holds features tile * 128 + w * 32 + 0..31, the gate ones in
-// its first 32 columns and the up ones in the next 32
+// block column c (0..255) of a gated tile -> feature: the SIMD's columns
+// 64 g .. 64 g + 63 hold features tile * 128 + g * 32 + 0..31, the gate ones
+// in its first 32 columns and the up ones in the next 32
 __device__ __forceinline__ int gated_feature(int tile, int c) { return tile * 128 + (c >> 6) * 32 + (c & 31); }
-__device__ __forceinline__ bool gated_up(int c) { return (c >> 5) & 1; }
 
+// B sources of block column c (gated tiles: which matrix and feature), as
+// byte offsets of the column's row in its matrix; a gated column's matrix is
+// the gate one (0) or the up one (1)
 template <int MODE>
-__device__ __forceinline__ BSrc<MODE> make_bsrc(const GemmParams &p, const Blk &b)
+__device__ __forceinline__ uint32_t b_row(const GemmParams &p, const Blk &b, int c)
 {
-    using C = Cfg<MODE>;
     const Shape &s = p.s;
-    const int t = threadIdx.x;
-    const uint32_t piece = (t & 7) * 16;
-    const int c0 = t >> 3;  // block column of pass 0 (pass ps adds 32 ps)
-    BSrc<MODE> r;
-    r.base1 = nullptr;
-    r.sbase = nullptr;
-    r.soff = 0;
-    r.roff[0] = 0;
-    if constexpr (C::kGated) {
-        // pass ps copies column ps * 32 + c0: wave part ps / 2, up if ps is
-        // odd, feature gated_feature(tile, c0) + (ps / 2) * 32
-        const uint32_t f0 = gated_feature(b.tile, c0);
-        if constexpr (MODE == M_G13) {
-            const size_t eo = (size_t)b.e * s.F * (s.d / 2);
-            r.base0 = p.w1q + eo;
-            r.base1 = p.w3q + eo;
-            r.off = f0 * (s.d / 2) + piece;
-            r.pstride = 32 * (s.d / 2);
-            r.sbase = (gated_up(t) ? p.w3s : p.w1s) + (size_t)b.e * s.F * (s.d / 32);
-            r.soff = gated_feature(b.tile, t) * (s.d / 32);
-        } else {
-            const size_t go = (size_t)b.group * s.F * s.d * 2;
-            r.base0 = reinterpret_cast<const uint8_t *>(p.sh1) + go;
-            r.base1 = reinterpret_cast<const uint8_t *>(p.sh3) + go;
-            r.off = f0 * (s.d * 2) + piece;
-            r.pstride = 32 * (s.d * 2);
-        }
-    } else if constexpr (MODE == M_D2) {
-        r.base0 = p.w2q + (size_t)b.e * s.d * (s.F / 2);
-        r.off = (b.tile * GN + c0) * (s.F / 2) + piece;
-        r.pstride = 32 * (s.F / 2);
-        r.sbase = p.w2s + (size_t)b.e * s.d * (s.F / 32);
-        r.soff = (b.tile * GN + t) * (s.F / 32);
-    } else if constexpr (MODE == M_S2) {
-        r.base0 = reinterpret_cast<const uint8_t *>(p.sh2) + (size_t)b.group * s.d * s.F * 2;
-        r.off = (b.tile * GN + c0) * (s.F * 2) + piece;
-        r.pstride = 32 * (s.F * 2);
-    } else {
-        r.base0 = reinterpret_cast<const uint8_t *>(p.wr3);
-        r.off = piece;
-        r.pstride = 0;
-#pragma unroll
-        for (int ps = 0; ps < C::BPASS; ps++) {
-            const int n = min(b.tile * GN + ps * 32 + c0, s.E - 1);
-            r.roff[ps] = (uint32_t)n * (3 * s.d * 2);
-        }
-    }
-    return r;
+    if constexpr (MODE == M_G13) return (uint32_t)gated_feature(b.tile, c) * (s.d / 2);
+    else if constexpr (MODE == M_D2) return (uint32_t)(b.tile * GN + c) * (s.F / 2);
+    else if constexpr (MODE == M_S13) return (uint32_t)gated_feature(b.tile, c) * (s.d * 2);
+    else if constexpr (MODE == M_S2) return (uint32_t)(b.tile * GN + c) * (s.F * 2);
+    else return (uint32_t)min(b.tile * GN + c, s.E - 1) * (3 * s.d * 2);  // router: past E re-read row E - 1
+}
+// scale row of block column c (see the layout above)
+template <int MODE>
+__device__ __forceinline__ int s_row_of(int c)
+{
+    return MODE == M_G13 ? ((c >> 5) & 1) * 128 + (c >> 6) * 32 + (c & 31) : c;
 }
 
-// One M pass of MT 32-row tiles (rows m0 .. m0 + mrows - 1 of the group)
-// over the whole K, then its epilogue.  la / lb / lbs: the LDS stages.  Wave
-// w computes block columns 64 w .. 64 w + 63 as two 32-column MFMA tiles.
-template <int MODE, int MT, bool SPLIT = false>
-__device__ __forceinline__ void gemm_pass(const GemmParams &p, const Blk &bk, const BSrc<MODE> &bsrc,
-                                          int m0, int mrows, LDS uint16_t *la, LDS uint8_t *lb,
-                                          LDS uint8_t *lbs)
+// The block's scale rows into LDS at sc: copy j of wave w fills rows
+// 8 n .. 8 n + 7, n = 8 j + w; lane i writes slot i % 8 of row 8 n + i / 8,
+// fetching piece slot ^ (row & 7) of the weight row's scale bytes (pieces
+// past the row's K / 32 bytes hold the next row's bytes or zeros past the
+// matrix: never read).
+template <int MODE>
+__device__ __forceinline__ void load_scales(const GemmParams &p, const Blk &b, LDS uint8_t *sc)
+{
+    const Shape &s = p.s;
+    const int lane = threadIdx.x & 63, wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+#pragma unroll
+    for (int j = 0; j < 4; j++) {
+        const int n = 8 * j + wave;
+        const int R = 8 * n + lane / 8;
+        const int q = (lane & 7) ^ (R & 7);
+        uint32_t off;
+        __amdgpu_buffer_rsrc_t r;
+        if constexpr (MODE == M_G13) {
+            const uint32_t sb = (uint32_t)s.F * (s.d / 32);
+            r = grsrc((n >= 16 ? p.w3s : p.w1s) + (size_t)b.e * sb, sb);  // (rows 128.. : up)
+            off = (uint32_t)(b.tile * 128 + (R & 127)) * (s.d / 32) + q * 16;
+        } else {
+            const uint32_t sb = (uint32_t)s.d * (s.F / 32);
+            r = grsrc(p.w2s + (size_t)b.e * sb, sb);
+            off = (uint32_t)(b.tile * GN + R) * (s.F / 32) + q * 16;
+        }
+        gbld16_lds(r, sc + n * 1024, off);
+    }
+}
+
+// The pass of one wave over its NTW tiles (tiles T0 .. T0 + NTW - 1 of the
+// pass's MT), all stages of K, then its epilogue.  Every wave of the block
+// issues its share of every stage's copies and meets every barrier, whatever
+// its NTW (0 included).
+template <int MODE, int MT, int NTW, int T0, bool SPLIT>
+__device__ __forceinline__ void wave_pass(const GemmParams &p, const Blk &bk, int m0, int mrows, LDS uint8_t *lds)
 {
     using C = Cfg<MODE>;
-    constexpr int KCA = C::KCA, R = C::R, STEPS = C::STEPS, QPR = C::QPR, RPP = C::RPP;
-    constexpr int NPASS = (MT * 32 + RPP - 1) / RPP;  // A staging passes for MT tiles
-    constexpr int ASTAGE = GM * KCA;                  // elements per A stage
-    constexpr int BSTAGE = GN * 128;                  // bytes per B stage
-    constexpr int SSTAGE = GN * (C::kFp4 ? C::BSC : 1);
+    using RG = Ring<MODE, MT>;
+    constexpr int NST = RG::NST, STEPS = C::STEPS, AROW = C::AROW;
     const Shape &s = p.s;
-    const int t = threadIdx.x;
-    const int lane = t & 63, wave = t >> 6;
+    const int lane = threadIdx.x & 63, wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int col = lane & 31, kh = lane >> 5;
-    const int nA = bk.nA, nB = bk.nB;
+    const int cg = wave & 3;  // the SIMD's column group
+    const int nS = bk.nS;
+    LDS uint8_t *ring = lds + RG::BASE;
+    const LDS uint8_t *scl = lds;  // (MXFP4) the block's scale rows
 
-    // ---- A staging: this thread copies piece qa of rows ps * RPP + t / QPR
-    // (rows past the group's end re-read its last row; their results are
+    // ---- A copies: copy j of wave w fills rows RPI n .. RPI n + RPI - 1 of
+    // the stage, n = 8 j + w (RPI = 1024 / AROW rows per copy); lane i writes
+    // slot i % ASLOTS of row RPI n + i / ASLOTS, which holds piece
+    // slot ^ swz_a(row).  Rows past the group's end read nothing (zeros,
     // never stored).  Byte offsets are 32-bit: the host checks that every A
     // operand is below 2 GiB.
-    const int qa = t % QPR;
-    uint32_t arow[NPASS];
-#pragma unroll
-    for (int ps = 0; ps < NPASS; ps++) {
-        const int r = min(ps * RPP + t / QPR, mrows - 1);
-        const int m = m0 + r;
-        uint32_t e;
-        if constexpr (MODE == M_G13) e = (uint32_t)p.w.pos_tok[bk.base + m] * s.d;
-        else if constexpr (MODE == M_D2) e = (uint32_t)(bk.base + m) * s.F;
-        else if constexpr (MODE == M_S2) e = (uint32_t)m * s.S * s.F + (uint32_t)bk.group * s.F;
-        else e = (uint32_t)m * s.d;
-        arow[ps] = (e + qa * 8) * 2;
-    }
-    auto load_a = [&](uint4 (&ar)[NPASS], int i) __attribute__((always_inline)) {
-        const int k0 = (i + bk.kst0) * KCA;
-        const uint16_t *abase;
-        int kk = k0;
-        if constexpr (MODE == M_G13 || MODE == M_S13) {
-            abase = p.x;
-        } else if constexpr (MODE == M_D2) {
-            abase = reinterpret_cast<const uint16_t *>(p.w.H);
+    __amdgpu_buffer_rsrc_t ra0, ra1;  // (ra1: the shared down's lo half of K)
+    uint32_t aoff[RG::NA];
+    {
+        uint32_t abytes;
+        const uint8_t *abase;
+        if constexpr (MODE == M_D2) {
+            abase = reinterpret_cast<const uint8_t *>(p.w.H);
+            abytes = (uint32_t)s.T * s.k * s.F * 2;
         } else if constexpr (MODE == M_S2) {
-            abase = k0 < s.F ? p.hs_hi : p.hs_lo;  // K runs over [hi parts | lo parts]
-            kk = k0 % s.F;
+            abase = reinterpret_cast<const uint8_t *>(p.hs_hi);
+            abytes = (uint32_t)s.T * s.S * s.F * 2;
         } else {
-            abase = p.x;  // router: K runs over [x | x | x]
-            kk = k0 % s.d;
+            abase = reinterpret_cast<const uint8_t *>(p.x);
+            abytes = (uint32_t)s.T * s.d * 2;
         }
-        const uint8_t *ab = reinterpret_cast<const uint8_t *>(abase);
+        ra0 = grsrc(abase, abytes);
+        ra1 = MODE == M_S2 ? grsrc(p.hs_lo, abytes) : ra0;
+        constexpr int RPI = 1024 / AROW;
 #pragma unroll
-        for (int ps = 0; ps < NPASS; ps++) ar[ps] = gld16(ab + (arow[ps] + (uint32_t)kk * 2));
-    };
-    auto store_a = [&](const uint4 (&ar)[NPASS], int stage) __attribute__((always_inline)) {
-#pragma unroll
-        for (int ps = 0; ps < NPASS; ps++) {
-            const int r = ps * RPP + t / QPR;
-            lds_st16(reinterpret_cast<LDS uint8_t *>(la + stage * ASTAGE + lds_off<KCA>(r, qa)), ar[ps]);
+        for (int j = 0; j < RG::NA; j++) {
+            const int r = RPI * (8 * j + wave) + lane / C::ASLOTS;
+            const int q = (lane % C::ASLOTS) ^ swz_a<MODE>(r);
+            const int m = m0 + min(r, mrows - 1);
+            uint32_t e;  // element offset of the row
+            if constexpr (MODE == M_G13) e = (uint32_t)p.w.pos_tok[bk.base + m] * s.d;
+            else if constexpr (MODE == M_D2) e = (uint32_t)(bk.base + m) * s.F;
+            else if constexpr (MODE == M_S2) e = (uint32_t)m * s.S * s.F + (uint32_t)bk.group * s.F;
+            else e = (uint32_t)m * s.d;
+            aoff[j] = r < mrows ? e * 2 + q * 16 : kPast;
         }
+    }
+    // ---- B copies: copy j of wave w fills the stage's B pieces 64 n .. 64 n
+    // + 63, n = 8 j + w: piece t is slot t % BP of column t / BP, holding piece
+    // slot ^ swz_b(column) of the column's run of the stage; the BP lanes of
+    // a column read one contiguous run.  The copy's columns share a matrix.
+    __amdgpu_buffer_rsrc_t rb[RG::NB];
+    uint32_t boff[RG::NB];
+#pragma unroll
+    for (int j = 0; j < RG::NB; j++) {
+        const int t = 64 * (8 * j + wave) + lane;
+        const int c = t / C::BP;
+        const int pc = (t % C::BP) ^ swz_b<MODE>(c);
+        const int c0 = 64 * (8 * j + wave) / C::BP;  // the copy's first column (uniform)
+        const bool up = (c0 >> 5) & 1;               // gated: the up matrix
+        if constexpr (MODE == M_G13) {
+            const uint32_t qb = (uint32_t)s.F * (s.d / 2);
+            rb[j] = grsrc((up ? p.w3q : p.w1q) + (size_t)bk.e * qb, qb);
+        } else if constexpr (MODE == M_D2) {
+            const uint32_t qb = (uint32_t)s.d * (s.F / 2);
+            rb[j] = grsrc(p.w2q + (size_t)bk.e * qb, qb);
+        } else if constexpr (MODE == M_S13) {
+            const uint32_t qb = (uint32_t)s.F * s.d * 2;
+            rb[j] = grsrc(reinterpret_cast<const uint8_t *>(up ? p.sh3 : p.sh1) + (size_t)bk.group * qb, qb);
+        } else if constexpr (MODE == M_S2) {
+            const uint32_t qb = (uint32_t)s.d * s.F * 2;
+            rb[j] = grsrc(reinterpret_cast<const uint8_t *>(p.sh2) + (size_t)bk.group * qb, qb);
+        } else {
+            rb[j] = grsrc(p.wr3, (uint32_t)s.E * 3 * s.d * 2);
+        }
+        boff[j] = b_row<MODE>(p, bk, c) + pc * 16;
+    }
+
+    // stage i (of the block's range) into ring slot sl; past the end the
+    // copies read nothing and fill a slot no stage reads
+    auto issue = [&](int i, int sl) __attribute__((always_inline)) {
+        const int sa = i + bk.kst0;
+        const bool ok = i < nS;
+        LDS uint8_t *st = ring + sl * RG::STAGE;
+        // A
+        int kk = sa * C::KS;
+        bool hi = true;
+        if constexpr (MODE == M_S2) {
+            hi = kk < s.F;  // K runs over [hi parts | lo parts]
+            kk = hi ? kk : kk - s.F;
+        } else if constexpr (MODE == M_R) {
+            kk = kk % s.d;  // K runs over [x | x | x]
+        }
+#pragma unroll
+        for (int j = 0; j < RG::NA; j++)
+            gbld16_lds(hi ? ra0 : ra1, st + (8 * j + wave) * 1024, ok ? aoff[j] + (uint32_t)kk * 2 : kPast);
+        // B
+        uint32_t kb = (uint32_t)sa * C::BCOL;  // byte offset of the stage in a B row
+        if constexpr (MODE == M_S2) kb = (uint32_t)((sa * C::KS) % s.F) * 2;  // repeats for hi / lo
+#pragma unroll
+        for (int j = 0; j < RG::NB; j++)
+            gbld16_lds(rb[j], st + RG::ABYTES + (8 * j + wave) * 1024, ok ? boff[j] + kb : kPast);
     };
 
-    // ---- B staging
-    const int bpiece = t & 7;  // 16-byte piece of a column this thread copies
-    struct BRegs {
-        uint4 v[C::BPASS];
-        uint2 sc;
-    };
-    auto load_b = [&](BRegs &br, int j) __attribute__((always_inline)) {
-        const int k0 = (j + bk.kst0 / R) * C::KCB;
-        uint32_t koff;  // byte offset of the stage in a weight row
-        if constexpr (C::kFp4) koff = k0 / 2;
-        else if constexpr (MODE == M_S2) koff = (k0 % s.F) * 2;  // B repeats for the hi / lo halves
-        else koff = k0 * 2;                                       // router row = [hi | mid | lo]
+    f32x16_t acc[NTW > 0 ? NTW : 1][2];
 #pragma unroll
-        for (int ps = 0; ps < C::BPASS; ps++) {
-            if constexpr (C::kGated)
-                br.v[ps] = gld16(((ps & 1) ? bsrc.base1 : bsrc.base0) + (bsrc.off + (ps >> 1) * bsrc.pstride + koff));
-            else if constexpr (MODE == M_R)
-                br.v[ps] = gld16(bsrc.base0 + (bsrc.roff[ps] + bsrc.off + koff));
-            else
-                br.v[ps] = gld16(bsrc.base0 + (bsrc.off + ps * bsrc.pstride + koff));
-        }
-        if constexpr (C::kFp4) br.sc = *reinterpret_cast<const uint2 *>(bsrc.sbase + (bsrc.soff + k0 / 32));
-    };
-    auto store_b = [&](const BRegs &br, int stage) __attribute__((always_inline)) {
-#pragma unroll
-        for (int ps = 0; ps < C::BPASS; ps++) {
-            const int cc = ps * 32 + (t >> 3);
-            lds_st16(lb + stage * BSTAGE + b_off(cc, bpiece), br.v[ps]);
-        }
-        if constexpr (C::kFp4) {
-            lds_st4(lbs + stage * SSTAGE + t * C::BSC, br.sc.x);
-            lds_st4(lbs + stage * SSTAGE + t * C::BSC + 4, br.sc.y);
-        }
-    };
-
-    f32x16_t acc[MT][2];
-#pragma unroll
-    for (int i = 0; i < MT; i++) {
+    for (int i = 0; i < (NTW > 0 ? NTW : 1); i++) {
         acc[i][0] = (f32x16_t)0.0f;
         acc[i][1] = (f32x16_t)0.0f;
     }
 
-    // A fragment of tile mt, step st: row mt * 32 + col, 8 values of piece kh * STEPS + st
-    auto a_frag = [&](const LDS uint16_t *A, int mt, int st) __attribute__((always_inline)) -> uint4 {
-        return lds_ld16(reinterpret_cast<const LDS uint8_t *>(A + lds_off<KCA>(mt * 32 + col, kh * STEPS + st)));
+    const int sa_ = swz_a<MODE>(col), sb_ = swz_b<MODE>(col);
+    // A fragment of pass tile T0 + mt, step st: row (T0 + mt) * 32 + col, piece kh * STEPS + st
+    auto a_frag = [&](const LDS uint8_t *A, int mt, int st) __attribute__((always_inline)) -> uint4 {
+        return lds_ld16(A + ((T0 + mt) * 32 + col) * AROW + (((kh * STEPS + st) ^ sa_) << 4));
+    };
+    // B column of this lane for nb (0, 1): block column 64 cg + 32 nb + col
+    auto b_piece = [&](const LDS uint8_t *B, int nb, int pc) __attribute__((always_inline)) -> uint4 {
+        return lds_ld16(B + (cg * 64 + nb * 32 + col) * C::BCOL + ((pc ^ sb_) << 4));
     };
 
-    // One A stage (STEPS MFMA K steps) against sub-stage `sub` of a B stage.
-    // Software pipelined: the A fragments and decoded B fragments of step
-    // st + 1 are read / decoded while the MFMAs of step st run.
-    auto compute = [&](int sa, int sb, int sub) __attribute__((always_inline)) {
-        const LDS uint16_t *A = la + sa * ASTAGE;
-        const LDS uint8_t *B = lb + sb * BSTAGE;
-        uint4 af[2][MT];
-        if constexpr (C::kFp4) {
-            using BT = typename std::conditional<MODE == M_D2, f16x8_t, bf16x8_t>::type;
-            // this lane's two MX blocks (sub * 4 + kh * 2 + {0, 1}) of each of
-            // its 2 columns: 32 bytes + 2 scales
-            uint4 q[2][2];
-            float scf[2][2];
+    // multiply stage i, in ring slot sl
+    auto compute = [&](int i, int sl) __attribute__((always_inline)) {
+        if constexpr (NTW > 0) {
+            const LDS uint8_t *A = ring + sl * RG::STAGE;
+            const LDS uint8_t *B = A + RG::ABYTES;
+            uint4 af[2][NTW];
+            if constexpr (C::kFp4) {
+                using BT = typename std::conditional<MODE == M_D2 && !SPLIT, f16x8_t, bf16x8_t>::type;
+                // this lane's two MX blocks (pieces 2 kh, 2 kh + 1) of each of its
+                // two columns, and their scale bytes (bytes 4 sa + 2 kh, + 1 of
+                // the column's scale row)
+                const int sa = i + bk.kst0;
+                uint4 q[2][2];
+                float scf[2][2];
 #pragma unroll
-            for (int nb = 0; nb < 2; nb++) {
-                const int cc = wave * 64 + nb * 32 + col;
-                const int blk = sub * 4 + kh * 2;
-                q[nb][0] = lds_ld16(B + b_off(cc, blk));
-                q[nb][1] = lds_ld16(B + b_off(cc, blk + 1));
-                const uint32_t s2 = *reinterpret_cast<const LDS uint16_t *>(lbs + sb * SSTAGE + cc * C::BSC + blk);
+                for (int nb = 0; nb < 2; nb++) {
+                    q[nb][0] = b_piece(B, nb, 2 * kh);
+                    q[nb][1] = b_piece(B, nb, 2 * kh + 1);
+                    const int R = s_row_of<MODE>(cg * 64 + nb * 32 + col);
+                    const uint32_t s2 = *reinterpret_cast<const LDS uint16_t *>(
+                        scl + R * 128 + (((sa >> 2) ^ (R & 7)) << 4) + 4 * (sa & 3) + 2 * kh);
 #pragma unroll
-                for (int h = 0; h < 2; h++) {
-                    // NaN scale (255): the block contributes 0
-                    const uint32_t sc = (s2 >> (8 * h)) & 0xffu;
-                    const uint32_t keep = sc == 255u ? 0u : ~0u;
-                    q[nb][h].x &= keep; q[nb][h].y &= keep; q[nb][h].z &= keep; q[nb][h].w &= keep;
-                    scf[nb][h] = e8m0f(sc == 255u ? 127u : sc);
+                    for (int h = 0; h < 2; h++) {
+                        // NaN scale (255): the block contributes 0
+                        const uint32_t sc = (s2 >> (8 * h)) & 0xffu;
+                        const uint32_t keep = sc == 255u ? 0u : ~0u;
+                        q[nb][h].x &= keep; q[nb][h].y &= keep; q[nb][h].z &= keep; q[nb][h].w &= keep;
+                        scf[nb][h] = e8m0f(sc == 255u ? 127u : sc);
+                    }
                 }
-            }
-            if constexpr (!SPLIT) {
-#pragma unroll
-                for (int mt = 0; mt < MT; mt++) af[0][mt] = a_frag(A, mt, 0);
-                BT b[2][2];
                 auto decode = [&](BT (&bb)[2], int st) __attribute__((always_inline)) {
 #pragma unroll
                     for (int nb = 0; nb < 2; nb++) {
                         const uint32_t w = u4at(q[nb][st >> 2], st & 3);
-                        if constexpr (MODE == M_D2) bb[nb] = cvt8_f16(w, scf[nb][st >> 2]);
+                        if constexpr (std::is_same<BT, f16x8_t>::value) bb[nb] = cvt8_f16(w, scf[nb][st >> 2]);
                         else bb[nb] = cvt8_bf16(w, scf[nb][st >> 2]);
                     }
                 };
-                decode(b[0], 0);
+                if constexpr (!SPLIT) {
+                    BT b[2][2];
+#pragma unroll
+                    for (int mt = 0; mt < NTW; mt++) af[0][mt] = a_frag(A, mt, 0);
+                    decode(b[0], 0);
+#pragma unroll
+                    for (int st = 0; st < STEPS; st++) {
+                        const int cur = st & 1, nxt = cur ^ 1;
+                        if (st + 1 < STEPS) {
+#pragma unroll
+                            for (int mt = 0; mt < NTW; mt++) af[nxt][mt] = a_frag(A, mt, st + 1);
+                            decode(b[nxt], st + 1);
+                        }
+#pragma unroll
+                        for (int mt = 0; mt < NTW; mt++)
+#pragma unroll
+                            for (int nb = 0; nb < 2; nb++)
+                                acc[mt][nb] = mfma32(__builtin_bit_cast(BT, af[cur][mt]), b[cur][nb], acc[mt][nb]);
+                    }
+                } else {
+                    // exact fallback: bf16 weights, fp16 inputs split in two bf16 parts
+#pragma unroll
+                    for (int st = 0; st < STEPS; st++) {
+                        bf16x8_t b[2];
+                        decode(b, st);
+#pragma unroll
+                        for (int mt = 0; mt < NTW; mt++) {
+                            bf16x8_t ah, al;
+                            split_f16(__builtin_bit_cast(f16x8_t, a_frag(A, mt, st)), ah, al);
+#pragma unroll
+                            for (int nb = 0; nb < 2; nb++) {
+                                acc[mt][nb] = mfma32(ah, b[nb], acc[mt][nb]);
+                                acc[mt][nb] = mfma32(al, b[nb], acc[mt][nb]);
+                            }
+                        }
+                    }
+                }
+            } else {
+                uint4 bf[2][2];
+#pragma unroll
+                for (int mt = 0; mt < NTW; mt++) af[0][mt] = a_frag(A, mt, 0);
+#pragma unroll
+                for (int nb = 0; nb < 2; nb++) bf[0][nb] = b_piece(B, nb, kh * STEPS);
 #pragma unroll
                 for (int st = 0; st < STEPS; st++) {
                     const int cur = st & 1, nxt = cur ^ 1;
                     if (st + 1 < STEPS) {
 #pragma unroll
-                        for (int mt = 0; mt < MT; mt++) af[nxt][mt] = a_frag(A, mt, st + 1);
-                        decode(b[nxt], st + 1);
+                        for (int mt = 0; mt < NTW; mt++) af[nxt][mt] = a_frag(A, mt, st + 1);
+#pragma unroll
+                        for (int nb = 0; nb < 2; nb++) bf[nxt][nb] = b_piece(B, nb, kh * STEPS + st + 1);
                     }
 #pragma unroll
-                    for (int mt = 0; mt < MT; mt++) {
+                    for (int mt = 0; mt < NTW; mt++)
 #pragma unroll
-                        for (int nb = 0; nb < 2; nb++) acc[mt][nb] = mfma32(__builtin_bit_cast(BT, af[cur][mt]), b[cur][nb], acc[mt][nb]);
-                    }
-                    __builtin_amdgcn_sched_barrier(0);
+                        for (int nb = 0; nb < 2; nb++)
+                            acc[mt][nb] = mfma32(__builtin_bit_cast(bf16x8_t, af[cur][mt]),
+                                                 __builtin_bit_cast(bf16x8_t, bf[cur][nb]), acc[mt][nb]);
                 }
-            } else {
-                // exact fallback: bf16 weights, fp16 inputs split in two bf16 parts
-#pragma unroll
-                for (int st = 0; st < STEPS; st++) {
-                    bf16x8_t b[2];
-#pragma unroll
-                    for (int nb = 0; nb < 2; nb++) b[nb] = cvt8_bf16(u4at(q[nb][st >> 2], st & 3), scf[nb][st >> 2]);
-#pragma unroll
-                    for (int mt = 0; mt < MT; mt++) {
-                        // one fragment at a time (a rare path; keeps its registers few)
-                        bf16x8_t ah, al;
-                        split_f16(__builtin_bit_cast(f16x8_t, a_frag(A, mt, st)), ah, al);
-#pragma unroll
-                        for (int nb = 0; nb < 2; nb++) {
-                            acc[mt][nb] = mfma32(ah, b[nb], acc[mt][nb]);
-                            acc[mt][nb] = mfma32(al, b[nb], acc[mt][nb]);
-                        }
-                        __builtin_amdgcn_sched_barrier(0);
-                    }
-                    __builtin_amdgcn_sched_barrier(0);
-                }
-            }
-        } else {
-            uint4 b[2][2];
-            auto read_b = [&](uint4 (&bb)[2], int st) __attribute__((always_inline)) {
-#pragma unroll
-                for (int nb = 0; nb < 2; nb++) bb[nb] = lds_ld16(B + b_off(wave * 64 + nb * 32 + col, kh * STEPS + st));
-            };
-            read_b(b[0], 0);
-#pragma unroll
-            for (int mt = 0; mt < MT; mt++) af[0][mt] = a_frag(A, mt, 0);
-#pragma unroll
-            for (int st = 0; st < STEPS; st++) {
-                const int cur = st & 1, nxt = cur ^ 1;
-                if (st + 1 < STEPS) {
-                    read_b(b[nxt], st + 1);
-#pragma unroll
-                    for (int mt = 0; mt < MT; mt++) af[nxt][mt] = a_frag(A, mt, st + 1);
-                }
-#pragma unroll
-                for (int mt = 0; mt < MT; mt++)
-#pragma unroll
-                    for (int nb = 0; nb < 2; nb++)
-                        acc[mt][nb] = mfma32(__builtin_bit_cast(bf16x8_t, af[cur][mt]),
-                                             __builtin_bit_cast(bf16x8_t, b[cur][nb]), acc[mt][nb]);
-                __builtin_amdgcn_sched_barrier(0);
             }
         }
     };
 
-    // ---- K loop, two A stages per trip (every K here is a multiple of
-    // 2 * KCA).  A stage i sits in LDS stage i & 1 and was loaded into
-    // registers two stages before it is stored (register sets ar0 / ar1), B
-    // stage j in LDS stage j & 1.  Loads past the end re-read the last stage
-    // (harmless) so every trip is identical.
-    uint4 ar0[NPASS], ar1[NPASS];
-    if constexpr (R == 2 && MT <= 3 && !SPLIT) {
-        if (nA % 4 == 0) {
-            // MXFP4 weights, an even number of trips: B stage t (one per
-            // trip) is loaded into one of two register sets two trips before
-            // it is stored, so about two trips' time covers its HBM latency
-            // (up to 96 rows: with 128 the registers would not hold it)
-            BRegs bra, brb;
-            load_a(ar0, 0);
-            load_b(bra, 0);
-            store_a(ar0, 0);
-            store_b(bra, 0);
-            load_a(ar1, min(1, nA - 1));
-            load_a(ar0, min(2, nA - 1));
-            load_b(bra, min(1, nB - 1));
-            load_b(brb, min(2, nB - 1));
-            lds_barrier();
-            for (int i = 0; i < nA; i += 4) {
-                const int t = i / 2;  // trips t (B stage t in LDS 0) and t + 1 (LDS 1)
-                compute(0, 0, 0);
-                store_a(ar1, 1);  // A stage i + 1
-                lds_barrier();
-                load_a(ar1, min(i + 3, nA - 1));
-                compute(1, 0, 1);
-                store_a(ar0, 0);  // A stage i + 2
-                store_b(bra, 1);  // B stage t + 1
-                lds_barrier();
-                load_a(ar0, min(i + 4, nA - 1));
-                load_b(bra, min(t + 3, nB - 1));
+    // ---- K loop: stage i's copies are issued at the top of iteration
+    // i - (NST - 1) (the prologue issues stages 0 .. NST - 2), so before
+    // stage i is multiplied the copies of the NST - 2 stages after it may
+    // still be in flight
+    constexpr int IN_FLIGHT = (NST - 2) * (RG::NA + RG::NB);
+#pragma unroll
+    for (int i = 0; i < NST - 1; i++) issue(i, i);
+    int sl = 0;  // ring slot of stage i
+    for (int i = 0; i < nS; i++) {
+        // this wave's copies of stage i have landed and its reads of stage
+        // i - 1 are done; after the barrier every wave's are, so the next
+        // copies may fill stage i - 1's slot
+        wait_vm<IN_FLIGHT>();
+        block_barrier();
+        issue(i + NST - 1, sl == 0 ? NST - 1 : sl - 1);
+        compute(i, sl);
+        sl = sl == NST - 1 ? 0 : sl + 1;
+    }
+    // the ring is reused by the next pass: every copy (past-the-end ones
+    // included) must have landed, and every wave be done reading
+    wait_vm<0>();
+    block_barrier();
 
-                compute(0, 1, 0);
-                store_a(ar1, 1);  // A stage i + 3
-                lds_barrier();
-                load_a(ar1, min(i + 5, nA - 1));
-                compute(1, 1, 1);
-                store_a(ar0, 0);  // A stage i + 4
-                store_b(brb, 0);  // B stage t + 2
-                lds_barrier();
-                load_a(ar0, min(i + 6, nA - 1));
-                load_b(brb, min(t + 4, nB - 1));
+    if constexpr (NTW > 0) {
+        // ---- epilogue (D lane layout: register e of tile (mt, nb) holds row
+        // 8 (e / 4) + 4 kh + e % 4 of the tile, column nb * 32 + col of the
+        // SIMD's 64)
+        if constexpr (C::kGated) {
+            // the activations first, all of them and without a branch (one
+            // copy per activation, chosen once), so that the exp / rcp chains
+            // of different values interleave; then the stores of the rows in
+            // range
+            float hv[NTW][16];
+            if (s.act == MOE_ACT_SWIGLU) {
+#pragma unroll
+                for (int mt = 0; mt < NTW; mt++)
+#pragma unroll
+                    for (int e = 0; e < 16; e++) hv[mt][e] = gated_act(acc[mt][0][e], acc[mt][1][e], MOE_ACT_SWIGLU, s.b1, s.b2);
+            } else {
+                const float k1 = -2.0f * 1.44269504088896341f / s.b1, k3 = -2.0f * 1.44269504088896341f / s.b2;
+                const float b12 = s.b1 * s.b2;
+#pragma unroll
+                for (int mt = 0; mt < NTW; mt++)
+#pragma unroll
+                    for (int e = 0; e < 16; e++) hv[mt][e] = situ_gemm(acc[mt][0][e], acc[mt][1][e], k1, k3, b12);
             }
-            goto epilogue;
-        }
-    }
-    {
-        // B stage j loaded R stages ahead (fp4: one B stage per trip)
-        BRegs br;
-        load_a(ar0, 0);
-        load_b(br, 0);
-        store_a(ar0, 0);
-        store_b(br, 0);
-        load_a(ar1, min(1, nA - 1));
-        load_a(ar0, min(2, nA - 1));
-        load_b(br, min(1, nB - 1));
-        lds_barrier();
-        for (int i = 0; i < nA; i += 2) {
-            compute(0, (i / R) & 1, i % R);
-            store_a(ar1, 1);  // A stage i + 1
-            if constexpr (R == 1) store_b(br, 1);
-            lds_barrier();
-            load_a(ar1, min(i + 3, nA - 1));
-            if constexpr (R == 1) load_b(br, min(i + 2, nB - 1));
-
-            compute(1, ((i + 1) / R) & 1, (i + 1) % R);
-            store_a(ar0, 0);  // A stage i + 2
-            store_b(br, ((i + 1) / R + 1) & 1);
-            lds_barrier();
-            load_a(ar0, min(i + 4, nA - 1));
-            load_b(br, min((i + 1) / R + 2, nB - 1));
-        }
-    }
-epilogue:
-
-    // ---- epilogue (D lane layout: register e of tile (mt, nb) holds row
-    // mt * 32 + 8 (e / 4) + 4 kh + e % 4, column nb * 32 + col of the wave's 64)
-    if constexpr (C::kGated) {
-        // the activations first, all of them and without a branch (one copy
-        // per activation, chosen once), so that the exp / rcp chains of
-        // different values interleave; then the stores of the rows in range
-        float hv[MT][16];
-        if (s.act == MOE_ACT_SWIGLU) {
+            const int f = bk.tile * 128 + cg * 32 + col;
 #pragma unroll
-            for (int mt = 0; mt < MT; mt++)
+            for (int mt = 0; mt < NTW; mt++) {
 #pragma unroll
-                for (int e = 0; e < 16; e++) hv[mt][e] = gated_act(acc[mt][0][e], acc[mt][1][e], MOE_ACT_SWIGLU, s.b1, s.b2);
+                for (int e = 0; e < 16; e++) {
+                    const int r = (T0 + mt) * 32 + 8 * (e >> 2) + 4 * kh + (e & 3);
+                    if (r >= mrows) continue;
+                    const int m = m0 + r;
+                    if constexpr (MODE == M_G13) {
+                        // (32-bit offsets: the host keeps T k F below 2^31)
+                        _Float16 *H = reinterpret_cast<_Float16 *>(p.w.H);
+                        H[(uint32_t)(bk.base + m) * (uint32_t)s.F + (uint32_t)f] = (_Float16)hv[mt][e];
+                    } else {
+                        const uint16_t hi = f32_to_bf16_rne(hv[mt][e]);
+                        const uint16_t lo = f32_to_bf16_rne(hv[mt][e] - __uint_as_float((uint32_t)hi << 16));
+                        const size_t o = (size_t)m * s.S * s.F + (size_t)bk.group * s.F + f;
+                        p.hs_hi_w[o] = hi;
+                        p.hs_lo_w[o] = lo;
+                    }
+                }
+            }
         } else {
-            const float k1 = -2.0f * 1.44269504088896341f / s.b1, k3 = -2.0f * 1.44269504088896341f / s.b2;
-            const float b12 = s.b1 * s.b2;
+            // (down projection: lane i holds the routing weight of the wave's
+            // row 32 T0 + i, loaded once; a row's weight comes by a lane
+            // shuffle.  Rows past the group read its last row's.)
+            float wl = 1.0f;
+            if constexpr (MODE == M_D2) wl = p.w.pos_w[bk.base + m0 + min(T0 * 32 + lane, mrows - 1)];
 #pragma unroll
-            for (int mt = 0; mt < MT; mt++)
+            for (int mt = 0; mt < NTW; mt++) {
 #pragma unroll
-                for (int e = 0; e < 16; e++) hv[mt][e] = situ_gemm(acc[mt][0][e], acc[mt][1][e], k1, k3, b12);
-        }
-        const int f = bk.tile * 128 + wave * 32 + col;
+                for (int e = 0; e < 16; e++) {
+                    const int rl = mt * 32 + 8 * (e >> 2) + 4 * kh + (e & 3);  // row of the wave's tiles
+                    const int r = T0 * 32 + rl;
+                    float wrow = 1.0f;
+                    if constexpr (MODE == M_D2) wrow = __shfl(wl, rl, 64);
+                    if (r >= mrows) continue;
+                    const int m = m0 + r;
 #pragma unroll
-        for (int mt = 0; mt < MT; mt++) {
-#pragma unroll
-            for (int e = 0; e < 16; e++) {
-                const int r = mt * 32 + 8 * (e >> 2) + 4 * kh + (e & 3);
-                if (r >= mrows) continue;
-                const int m = m0 + r;
-                if constexpr (MODE == M_G13) {
-                    // (32-bit offsets: the host keeps T k F below 2^31)
-                    _Float16 *H = reinterpret_cast<_Float16 *>(p.w.H);
-                    H[(uint32_t)(bk.base + m) * (uint32_t)s.F + (uint32_t)f] = (_Float16)hv[mt][e];
-                } else {
-                    const uint16_t hi = f32_to_bf16_rne(hv[mt][e]);
-                    const uint16_t lo = f32_to_bf16_rne(hv[mt][e] - __uint_as_float((uint32_t)hi << 16));
-                    const size_t o = (size_t)m * s.S * s.F + (size_t)bk.group * s.F + f;
-                    p.hs_hi_w[o] = hi;
-                    p.hs_lo_w[o] = lo;
-                }
-            }
-        }
-        return;
-    }
-    // (down projection: lane i holds the routing weights of the pass's rows
-    // i and 64 + i, loaded once; a row's weight comes by a lane shuffle.
-    // Rows past the group read its last row's.)
-    float w_lo = 1.0f, w_hi = 1.0f;
-    if constexpr (MODE == M_D2) {
-        w_lo = p.w.pos_w[bk.base + m0 + min(lane, mrows - 1)];
-        if constexpr (MT > 2) w_hi = p.w.pos_w[bk.base + m0 + min(64 + lane, mrows - 1)];
-    }
-#pragma unroll
-    for (int mt = 0; mt < MT; mt++) {
-#pragma unroll
-        for (int e = 0; e < 16; e++) {
-            const int r = mt * 32 + 8 * (e >> 2) + 4 * kh + (e & 3);
-            float wrow = 1.0f;
-            if constexpr (MODE == M_D2) wrow = mt < 2 ? __shfl(w_lo, r, 64) : __shfl(w_hi, r - 64, 64);
-            if (r >= mrows) continue;
-            const int m = m0 + r;
-            {
-#pragma unroll
-                for (int nb = 0; nb < 2; nb++) {
-                    const int n = bk.tile * GN + wave * 64 + nb * 32 + col;
-                    if (n >= bk.ncols) continue;
-                    const float v = acc[mt][nb][e];
-                    if constexpr (MODE == M_D2) p.w.Y[(size_t)(bk.base + m) * s.d + n] = v * wrow;
-                    else if constexpr (MODE == M_S2) p.w.Ysh[((size_t)bk.group * s.T + m) * s.d + n] = v;
-                    else if (p.ksplit > 1) p.rpart[((size_t)bk.ks * s.T + m) * s.E + n] = v;
-                    else p.w.logits[(size_t)m * s.E + n] = v;
+                    for (int nb = 0; nb < 2; nb++) {
+                        const int n = bk.tile * GN + cg * 64 + nb * 32 + col;
+                        if (n >= bk.ncols) continue;
+                        const float v = acc[mt][nb][e];
+                        if constexpr (MODE == M_D2) p.w.Y[(size_t)(bk.base + m) * s.d + n] = v * wrow;
+                        else if constexpr (MODE == M_S2) p.w.Ysh[((size_t)bk.group * s.T + m) * s.d + n] = v;
+                        else if (p.ksplit > 1) p.rpart[((size_t)bk.ks * s.T + m) * s.E + n] = v;
+                        else p.w.logits[(size_t)m * s.E + n] = v;
+                    }
                 }
             }
         }
     }
+}
+
+// One M pass of MT 32-row tiles (rows m0 .. m0 + mrows - 1 of the group):
+// the two waves of a SIMD take the first (MT + 1) / 2 tiles and the rest.
+template <int MODE, int MT, bool SPLIT = false>
+__device__ __forceinline__ void gemm_pass(const GemmParams &p, const Blk &bk, int m0, int mrows, LDS uint8_t *lds)
+{
+    constexpr int N0 = (MT + 1) / 2, N1 = MT / 2;
+    if (__builtin_amdgcn_readfirstlane(threadIdx.x >> 6) < 4) wave_pass<MODE, MT, N0, 0, SPLIT>(p, bk, m0, mrows, lds);
+    else wave_pass<MODE, MT, N1, N0, SPLIT>(p, bk, m0, mrows, lds);
 }
 
 template <int MODE>
 __global__ __launch_bounds__(GT) void k_ggemm(GemmParams p)
 {
     using C = Cfg<MODE>;
-    __shared__ __attribute__((aligned(16))) uint16_t lds_a[2 * GM * C::KCA];
-    __shared__ __attribute__((aligned(16))) uint8_t lds_b[2 * GN * 128];
-    __shared__ __attribute__((aligned(16))) uint8_t lds_bs[2 * GN * (C::kFp4 ? C::BSC : 1)];
-
-    LDS uint16_t *la = (LDS uint16_t *)lds_a;
-    LDS uint8_t *lb = (LDS uint8_t *)lds_b;
-    LDS uint8_t *lbs = (LDS uint8_t *)lds_bs;
+    __shared__ __attribute__((aligned(1024))) uint8_t lds_blk[kLdsBytes];
+    LDS uint8_t *ring = (LDS uint8_t *)lds_blk;  // (MXFP4: the scale rows, then the ring)
     const Shape &s = p.s;
     Blk b;
     // ---- block -> (m block, group, column tile); consecutive groups of
-    // tiles go to one XCD (blocks are dealt to the 8 XCDs round robin)
+    // tiles go to one XCD (blocks are dealt to the 8 XCDs round robin), so
+    // the blocks of one group share its A rows in that XCD's L2
     int x = blockIdx.x;
     const int gt = p.groups * p.n_tiles;
     b.mb = 0;
@@ -686,50 +695,53 @@ __global__ __launch_bounds__(GT) void k_ggemm(GemmParams p)
         b.M = s.T;
         b.K = MODE == M_S13 ? s.d : (MODE == M_S2 ? 2 * s.F : 3 * s.d);
     }
-    if constexpr (MODE == M_R) b.K /= p.ksplit;  // (a multiple of 2 * KCA, see the launch)
-    b.nA = b.K / C::KCA;
-    b.nB = b.K / C::KCB;
-    b.kst0 = b.ks * b.nA;
+    if constexpr (MODE == M_R) b.K /= p.ksplit;  // (a multiple of the stage, see the launch)
+    b.nS = b.K / C::KS;
+    b.kst0 = b.ks * b.nS;
     b.ncols = C::kGated ? s.F : (MODE == M_R ? s.E : s.d);
-    const BSrc<MODE> bsrc = make_bsrc<MODE>(p, b);
+
+    // the block's scale rows, ahead of every pass (the first stage's wait and
+    // barrier cover them: the copies land in order)
+    if constexpr (C::kFp4) load_scales<MODE>(p, b, ring);
 
     if constexpr (MODE == M_D2) {
         // The down projection multiplies fp16 H by W2 decoded to fp16, which
         // is exact for scale bytes 104..140 (and 255, which decodes to 0).
         // A block whose W2 scales leave that range takes the exact split
         // path (bf16 weights, H split into two bf16 parts) for all its rows.
-        const uint8_t *sc = p.w2s + ((size_t)b.e * s.d + b.tile * GN + threadIdx.x) * (s.F / 32);
         bool ok = true;
-        for (int i = 0; i < s.F / 32; i += 4) {
-            const uint32_t v = *reinterpret_cast<const uint32_t *>(sc + i);
+        if (threadIdx.x < GN) {
+            const uint8_t *sc = p.w2s + ((size_t)b.e * s.d + b.tile * GN + threadIdx.x) * (s.F / 32);
+            for (int i = 0; i < s.F / 32; i += 4) {
+                const uint32_t v = *reinterpret_cast<const uint32_t *>(sc + i);
 #pragma unroll
-            for (int k = 0; k < 4; k++) {
-                const uint32_t by = (v >> (8 * k)) & 0xffu;
-                ok = ok && (by == 255u || (by - 104u) <= 36u);
+                for (int k = 0; k < 4; k++) {
+                    const uint32_t by = (v >> (8 * k)) & 0xffu;
+                    ok = ok && (by == 255u || (by - 104u) <= 36u);
+                }
             }
         }
         if (!__syncthreads_and(ok)) {
-            for (int m0 = 0; m0 < b.M; m0 += GM)
-                gemm_pass<MODE, GMT, true>(p, b, bsrc, m0, min(GM, b.M - m0), la, lb, lbs);
+            // (64-row passes: this rare path then needs few registers)
+            for (int m0 = 0; m0 < b.M; m0 += 64) gemm_pass<MODE, 2, true>(p, b, m0, min(64, b.M - m0), ring);
             return;
         }
     }
     if constexpr (C::kFp4) {
-        // routed experts: all of the group's rows, in passes of up to 128
-        for (int m0 = 0; m0 < b.M; m0 += GM) {
-            const int mrows = min(GM, b.M - m0);
+        // routed experts: all of the group's rows, in passes of up to 32 GMT4
+        for (int m0 = 0; m0 < b.M; m0 += 32 * GMT4) {
+            const int mrows = min(32 * GMT4, b.M - m0);
             switch ((mrows + 31) >> 5) {
-            case 1: gemm_pass<MODE, 1>(p, b, bsrc, m0, mrows, la, lb, lbs); break;
-            case 2: gemm_pass<MODE, 2>(p, b, bsrc, m0, mrows, la, lb, lbs); break;
-            case 3: gemm_pass<MODE, 3>(p, b, bsrc, m0, mrows, la, lb, lbs); break;
-            default: gemm_pass<MODE, 4>(p, b, bsrc, m0, mrows, la, lb, lbs); break;
+            case 1: gemm_pass<MODE, 1>(p, b, m0, mrows, ring); break;
+            case 2: gemm_pass<MODE, 2>(p, b, m0, mrows, ring); break;
+            default: gemm_pass<MODE, 3>(p, b, m0, mrows, ring); break;
             }
         }
     } else {
-        // shared experts / router: one 128-row pass per block (a short last
-        // pass computes clamped copies of its last row, never stored)
+        // shared experts / router: one pass of GM rows per block (rows past
+        // the end read nothing and are never stored)
         const int m0 = b.mb * GM;
-        if (m0 < b.M) gemm_pass<MODE, GMT>(p, b, bsrc, m0, min(GM, b.M - m0), la, lb, lbs);
+        if (m0 < b.M) gemm_pass<MODE, GMT>(p, b, m0, min(GM, b.M - m0), ring);
     }
 }
 
