@@ -42,6 +42,7 @@ struct Work {
     float *Y;          // [T*k][d] weighted expert outputs
     float *Ysh;        // [S][T][d] shared experts' outputs
     void *extra;       // MFMA path: router weights split into 3 bf16 parts [E][3d]
+    uint8_t *xq;       // MFMA path: tokens as two fp8 terms [T][2d], then their scales [T]
     float *rpart;      // MFMA path: partial router logits of the K slices
 };
 
@@ -309,6 +310,7 @@ hipError_t launch_gemv_experts(const Shape &s, const uint16_t *x, const Weights 
 // the router weights, and the experts (shared + routed gate/up, then down)
 bool mfma_supported(const Shape &s);
 size_t mfma_extra_workspace(const Shape &s);
+size_t mfma_token_workspace(const Shape &s);
 size_t router_part_workspace(const Shape &s);
 constexpr int kRouterPartRows = 8192;  // rows of E partial logits (MFMA router K slices)
 hipError_t launch_mfma_router(const Shape &s, const uint16_t *x, const Weights &wt, const Work &w,

@@ -64,6 +64,8 @@ struct GemmParams {
     const uint8_t *w1q, *w1s, *w3q, *w3s, *w2q, *w2s;
     const uint16_t *sh1, *sh3, *sh2;      // shared experts (bf16)
     const uint16_t *wr3;                  // router weights split in 3 bf16 parts [E][3d]
+    const uint8_t *xq;                    // tokens as two fp8 terms [T][hi (d) | lo (d)]
+    const uint32_t *xs;                   // their E8M0 scales [T]: hi byte, lo byte
     Work w;
     const uint16_t *hs_hi, *hs_lo;        // shared H as bf16 hi / lo parts [T][S*F]
     uint16_t *hs_hi_w, *hs_lo_w;
@@ -193,7 +195,7 @@ struct Cfg {
     static constexpr bool kGated = (MODE == M_G13 || MODE == M_S13);
     static constexpr int KS = kFp4 ? 128 : 64;     // K per stage
     static constexpr int STEPS = KS / 16;          // MFMA K steps per stage
-    static constexpr int AROW = KS * 2;            // bytes of one A row of a stage
+    static constexpr int AROW = KS * 2;            // bytes of one A row of a stage (G13: fp8 hi | lo)
     static constexpr int ASLOTS = AROW / 16;       // 16-byte pieces of an A row
     static constexpr int BCOL = kFp4 ? KS / 2 : KS * 2;  // bytes of one B column of a stage
     static constexpr int BP = BCOL / 16;           // 16-byte pieces of a B column
@@ -340,7 +342,10 @@ __device__ __forceinline__ void wave_pass(const GemmParams &p, const Blk &bk, in
     {
         uint32_t abytes;
         const uint8_t *abase;
-        if constexpr (MODE == M_D2) {
+        if constexpr (MODE == M_G13) {
+            abase = p.xq;
+            abytes = (uint32_t)s.T * s.d * 2;
+        } else if constexpr (MODE == M_D2) {
             abase = reinterpret_cast<const uint8_t *>(p.w.H);
             abytes = (uint32_t)s.T * s.k * s.F * 2;
         } else if constexpr (MODE == M_S2) {
@@ -358,12 +363,18 @@ __device__ __forceinline__ void wave_pass(const GemmParams &p, const Blk &bk, in
             const int r = RPI * (8 * j + wave) + lane / C::ASLOTS;
             const int q = (lane % C::ASLOTS) ^ swz_a<MODE>(r);
             const int m = m0 + min(r, mrows - 1);
-            uint32_t e;  // element offset of the row
-            if constexpr (MODE == M_G13) e = (uint32_t)p.w.pos_tok[bk.base + m] * s.d;
-            else if constexpr (MODE == M_D2) e = (uint32_t)(bk.base + m) * s.F;
-            else if constexpr (MODE == M_S2) e = (uint32_t)m * s.S * s.F + (uint32_t)bk.group * s.F;
-            else e = (uint32_t)m * s.d;
-            aoff[j] = r < mrows ? e * 2 + q * 16 : kPast;
+            uint32_t e;  // byte offset of the row, and of piece q in it
+            if constexpr (MODE == M_G13) {
+                // pieces 0-7: the hi fp8 bytes of the stage, 8-15: the lo ones
+                e = (uint32_t)p.w.pos_tok[bk.base + m] * (2 * s.d) + (q >= 8 ? s.d : 0) + (q & 7) * 16;
+            } else {
+                uint32_t el;  // element offset
+                if constexpr (MODE == M_D2) el = (uint32_t)(bk.base + m) * s.F;
+                else if constexpr (MODE == M_S2) el = (uint32_t)m * s.S * s.F + (uint32_t)bk.group * s.F;
+                else el = (uint32_t)m * s.d;
+                e = el * 2 + q * 16;
+            }
+            aoff[j] = r < mrows ? e : kPast;
         }
     }
     // ---- B copies: copy j of wave w fills the stage's B pieces 64 n .. 64 n
@@ -412,9 +423,11 @@ __device__ __forceinline__ void wave_pass(const GemmParams &p, const Blk &bk, in
         } else if constexpr (MODE == M_R) {
             kk = kk % s.d;  // K runs over [x | x | x]
         }
+        // (bytes per A element of a stage row: 1 for each fp8 term, else 2)
+        constexpr uint32_t EB = MODE == M_G13 ? 1 : 2;
 #pragma unroll
         for (int j = 0; j < RG::NA; j++)
-            gbld16_lds(hi ? ra0 : ra1, st + (8 * j + wave) * 1024, ok ? aoff[j] + (uint32_t)kk * 2 : kPast);
+            gbld16_lds(hi ? ra0 : ra1, st + (8 * j + wave) * 1024, ok ? aoff[j] + (uint32_t)kk * EB : kPast);
         // B
         uint32_t kb = (uint32_t)sa * C::BCOL;  // byte offset of the stage in a B row
         if constexpr (MODE == M_S2) kb = (uint32_t)((sa * C::KS) % s.F) * 2;  // repeats for hi / lo
@@ -422,6 +435,19 @@ __device__ __forceinline__ void wave_pass(const GemmParams &p, const Blk &bk, in
         for (int j = 0; j < RG::NB; j++)
             gbld16_lds(rb[j], st + RG::ABYTES + (8 * j + wave) * 1024, ok ? boff[j] + kb : kPast);
     };
+
+    // (G13) the E8M0 scales of this lane's token row in each of its tiles:
+    // hi term in byte 0, lo term in byte 1; loaded here, before the copies,
+    // and waited for at once
+    uint32_t sca[NTW > 0 ? NTW : 1];
+    if constexpr (MODE == M_G13) {
+#pragma unroll
+        for (int mt = 0; mt < NTW; mt++) {
+            const int m = m0 + min((T0 + mt) * 32 + col, mrows - 1);
+            sca[mt] = p.xs[p.w.pos_tok[bk.base + m]];
+            asm volatile("" : "+v"(sca[mt]));
+        }
+    }
 
     f32x16_t acc[NTW > 0 ? NTW : 1][2];
 #pragma unroll
@@ -442,7 +468,74 @@ __device__ __forceinline__ void wave_pass(const GemmParams &p, const Blk &bk, in
 
     // multiply stage i, in ring slot sl
     auto compute = [&](int i, int sl) __attribute__((always_inline)) {
-        if constexpr (NTW > 0) {
+        if constexpr (NTW > 0 && MODE == M_G13) {
+            // Scaled MX MFMA (32x32x64, A fp8 e4m3, B fp4 e2m1).  In step stp
+            // (0, 1) of the stage, lane (col, kh) holds for each of its two
+            // columns MX block 2 stp + kh (K 64 stp + 32 kh .. + 31; B piece
+            // 2 stp + kh) with its E8M0 scale, and of its token row the 16-byte
+            // runs K 64 stp + 16 kh .. + 15 and 64 stp + 32 + 16 kh .. + 15
+            // (A pieces 4 stp + kh and 4 stp + 2 + kh; the lo term's 8 later):
+            // the A lanes' 32 elements interleave in 16s against a B lane's
+            // contiguous block (measured on gfx950).  The token rows have one
+            // E8M0 scale per term.  The hi and lo terms are two MFMAs into one
+            // sum.
+            const LDS uint8_t *A = ring + sl * RG::STAGE;
+            const LDS uint8_t *B = A + RG::ABYTES;
+            const int sa = i + bk.kst0;
+            typedef int i32x8_t __attribute__((ext_vector_type(8)));
+            uint4 q[2][2];
+            int scb[2][2];
+#pragma unroll
+            for (int nb = 0; nb < 2; nb++) {
+                // the stage's 4 scale bytes of the column (blocks 0..3)
+                const int R = s_row_of<MODE>(cg * 64 + nb * 32 + col);
+                const uint32_t s4 = *reinterpret_cast<const LDS uint32_t *>(
+                    scl + R * 128 + (((sa >> 2) ^ (R & 7)) << 4) + 4 * (sa & 3));
+#pragma unroll
+                for (int stp = 0; stp < 2; stp++) {
+                    q[nb][stp] = b_piece(B, nb, 2 * stp + kh);
+                    // NaN scale (255): the block contributes 0
+                    const uint32_t sc = (s4 >> (8 * (2 * stp + kh))) & 0xffu;
+                    const uint32_t keep = sc == 255u ? 0u : ~0u;
+                    q[nb][stp].x &= keep; q[nb][stp].y &= keep; q[nb][stp].z &= keep; q[nb][stp].w &= keep;
+                    scb[nb][stp] = (int)(sc == 255u ? 127u : sc);
+                }
+            }
+            // (the MFMAs of a step run through all accumulators once per term,
+            // so that consecutive ones never depend on each other)
+#pragma unroll
+            for (int stp = 0; stp < 2; stp++) {
+                i32x8_t at[2][NTW];  // [term][tile]
+#pragma unroll
+                for (int mt = 0; mt < NTW; mt++) {
+                    const LDS uint8_t *arow = A + ((T0 + mt) * 32 + col) * AROW;
+                    const int q0 = 4 * stp + kh, q1 = q0 + 2;
+#pragma unroll
+                    for (int tm = 0; tm < 2; tm++) {
+                        const uint4 u0 = lds_ld16(arow + (((q0 + 8 * tm) ^ sa_) << 4));
+                        const uint4 u1 = lds_ld16(arow + (((q1 + 8 * tm) ^ sa_) << 4));
+                        at[tm][mt] = (i32x8_t){(int)u0.x, (int)u0.y, (int)u0.z, (int)u0.w,
+                                               (int)u1.x, (int)u1.y, (int)u1.z, (int)u1.w};
+                    }
+                }
+#pragma unroll
+                for (int tm = 0; tm < 2; tm++)
+#pragma unroll
+                    for (int mt = 0; mt < NTW; mt++)
+#pragma unroll
+                        for (int nb = 0; nb < 2; nb++) {
+                            const uint4 bq = q[nb][stp];
+                            const i32x8_t bv = {(int)bq.x, (int)bq.y, (int)bq.z, (int)bq.w, 0, 0, 0, 0};
+                            // (the token row's scale register: hi term byte 0, lo term byte 1)
+                            if (tm == 0)
+                                acc[mt][nb] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(
+                                    at[0][mt], bv, acc[mt][nb], 0, 4, 0, (int)sca[mt], 0, scb[nb][stp]);
+                            else
+                                acc[mt][nb] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(
+                                    at[1][mt], bv, acc[mt][nb], 0, 4, 1, (int)sca[mt], 0, scb[nb][stp]);
+                        }
+            }
+        } else if constexpr (NTW > 0) {
             const LDS uint8_t *A = ring + sl * RG::STAGE;
             const LDS uint8_t *B = A + RG::ABYTES;
             uint4 af[2][NTW];
@@ -766,6 +859,68 @@ __global__ __launch_bounds__(256) void k_split_router(int E, int d, const float 
     row[2 * d + c] = lo;
 }
 
+// The tokens as two fp8 (E4M3) terms for the scaled MFMA of the routed
+// gate/up: per token row, the E8M0 scale 2^shi puts the row's largest |x| in
+// [128, 256), hi = rne_fp8(x / 2^shi), and the remainder x - hi 2^shi (exact
+// in fp32) goes to lo = rne_fp8(remainder / 2^(shi - 4)).  A bf16 x has 8
+// significant bits and hi holds 4 of them, so hi 2^shi + lo 2^(shi - 4) is x
+// exactly unless x is below about 2^-13 of its row's largest (there a few
+// low bits are lost, far below the fp32 sums' rounding).  One wave per row.
+__global__ __launch_bounds__(256) void k_quant_x(int T, int d, const uint16_t *__restrict__ x,
+                                                 uint8_t *__restrict__ xq, uint32_t *__restrict__ xs)
+{
+    const int t = blockIdx.x * 4 + (threadIdx.x >> 6);
+    if (t >= T) return;
+    const int lane = threadIdx.x & 63;
+    const int nch = d / 8;  // 16-byte chunks of the row (at most 512: 8 per lane)
+    const uint4 *row = reinterpret_cast<const uint4 *>(x + (size_t)t * d);
+    uint4 v[8];
+    float amax = 0.0f;
+#pragma unroll
+    for (int c = 0; c < 8; c++) {
+        const int ch = lane + 64 * c;
+        v[c] = ch < nch ? row[ch] : make_uint4(0, 0, 0, 0);
+#pragma unroll
+        for (int k = 0; k < 4; k++) {
+            const uint32_t w = u4at(v[c], k);
+            amax = fmaxf(amax, fmaxf(fabsf(bf16_lo(w)), fabsf(bf16_hi(w))));
+        }
+    }
+#pragma unroll
+    for (int m = 32; m >= 1; m >>= 1) amax = fmaxf(amax, __shfl_xor(amax, m, 64));
+    // floor(log2(amax)) from the exponent bits (a zero row: any scale)
+    const int ea = amax > 0.0f ? (int)((__float_as_uint(amax) >> 23) & 0xff) - 127 : 0;
+    const int shi = min(max(ea - 7, -123), 127), slo = shi - 4;
+    const float inv_hi = ldexpf(1.0f, -shi), one_hi = ldexpf(1.0f, shi), inv_lo = ldexpf(1.0f, -slo);
+    uint8_t *qh = xq + (size_t)t * 2 * d, *ql = qh + d;
+#pragma unroll
+    for (int c = 0; c < 8; c++) {
+        const int ch = lane + 64 * c;
+        if (ch >= nch) break;
+        uint32_t hw[2], lw[2];
+#pragma unroll
+        for (int h = 0; h < 2; h++) {
+            float f[4];
+            f[0] = bf16_lo(u4at(v[c], 2 * h)); f[1] = bf16_hi(u4at(v[c], 2 * h));
+            f[2] = bf16_lo(u4at(v[c], 2 * h + 1)); f[3] = bf16_hi(u4at(v[c], 2 * h + 1));
+            int hp = __builtin_amdgcn_cvt_pk_fp8_f32(f[0] * inv_hi, f[1] * inv_hi, 0, false);
+            hp = __builtin_amdgcn_cvt_pk_fp8_f32(f[2] * inv_hi, f[3] * inv_hi, hp, true);
+            float r[4];
+            r[0] = f[0] - __builtin_amdgcn_cvt_f32_fp8(hp, 0) * one_hi;
+            r[1] = f[1] - __builtin_amdgcn_cvt_f32_fp8(hp, 1) * one_hi;
+            r[2] = f[2] - __builtin_amdgcn_cvt_f32_fp8(hp, 2) * one_hi;
+            r[3] = f[3] - __builtin_amdgcn_cvt_f32_fp8(hp, 3) * one_hi;
+            int lp = __builtin_amdgcn_cvt_pk_fp8_f32(r[0] * inv_lo, r[1] * inv_lo, 0, false);
+            lp = __builtin_amdgcn_cvt_pk_fp8_f32(r[2] * inv_lo, r[3] * inv_lo, lp, true);
+            hw[h] = (uint32_t)hp;
+            lw[h] = (uint32_t)lp;
+        }
+        *reinterpret_cast<uint2 *>(qh + ch * 8) = make_uint2(hw[0], hw[1]);
+        *reinterpret_cast<uint2 *>(ql + ch * 8) = make_uint2(lw[0], lw[1]);
+    }
+    if (lane == 0) xs[t] = (uint32_t)(shi + 127) | ((uint32_t)(slo + 127) << 8);
+}
+
 // logits[t][e] = sum over the K slices, in slice order, of the partials
 __global__ __launch_bounds__(256) void k_router_reduce(int n, int ksplit, const float *__restrict__ rpart,
                                                        float *__restrict__ logits)
@@ -813,6 +968,14 @@ size_t router_part_workspace(const Shape &s)
     return rows * s.E * 4;
 }
 
+// token workspace of the MFMA path: the tokens as two fp8 terms [T][2d],
+// then their scales [T] (4 bytes each)
+size_t mfma_token_workspace(const Shape &s)
+{
+    if (s.d % 256 != 0 || s.F % 256 != 0) return 0;
+    return ((((size_t)s.T * 2 * s.d) + 255) & ~(size_t)255) + ((((size_t)s.T * 4) + 255) & ~(size_t)255);
+}
+
 // extra workspace of the MFMA path: router weights split in 3 bf16 parts
 size_t mfma_extra_workspace(const Shape &s)
 {
@@ -843,6 +1006,8 @@ static GemmParams make_gemm_params(const Shape &s, const uint16_t *x, const Weig
     p.sh1 = wt.sh1; p.sh3 = wt.sh3; p.sh2 = wt.sh2;
     p.w = w;
     p.wr3 = reinterpret_cast<const uint16_t *>(w.extra);
+    p.xq = w.xq;
+    p.xs = reinterpret_cast<const uint32_t *>(w.xq + ((((size_t)s.T * 2 * s.d) + 255) & ~(size_t)255));
     // the shared H (bf16 hi and lo parts) lives in the fp32 shared-H region
     p.hs_hi = reinterpret_cast<const uint16_t *>(w.Hs);
     p.hs_lo = p.hs_hi + (size_t)s.T * s.S * s.F;
@@ -878,6 +1043,8 @@ hipError_t launch_mfma_experts(const Shape &s, const uint16_t *x, const Weights 
     GemmParams p = make_gemm_params(s, x, wt, w);
     const int max_active = min(s.E, s.T * s.k);
     const int mb = (s.T + GM - 1) / GM;
+    // the tokens as two fp8 terms (the routed gate/up's A operand)
+    k_quant_x<<<(s.T + 3) / 4, 256, 0, st>>>(s.T, s.d, x, w.xq, const_cast<uint32_t *>(p.xs));
     if (include_shared && s.S > 0) launch_mode<M_S13>(p, s.S, (s.F + 127) / 128, mb, st);
     launch_mode<M_G13>(p, max_active, (s.F + 127) / 128, 1, st);
     if (ev2) (void)hipEventRecord(ev2[0], st);

@@ -114,6 +114,7 @@ size_t carve(const Shape &s, char *base, Work *w)
     v.Y = (float *)take(T * k * (size_t)s.d * 4);
     v.Ysh = (float *)take((size_t)s.S * T * s.d * 4);
     v.extra = (void *)take(moe::mfma_extra_workspace(s));
+    v.xq = (uint8_t *)take(moe::mfma_token_workspace(s));
     v.rpart = (float *)take(moe::router_part_workspace(s));
     if (w) *w = v;
     return off;
