@@ -19,6 +19,12 @@ and 9; "Part 4 - Lecture 01", section 1 model table):
   weights (section 9; "Three invariants").
 * ``forward`` / ``layer`` -- weighted expert mixture plus unweighted shared
   experts on the same input (section 9, the per-token MoE).
+* ``rmsnorm`` -- k3_rmsnorm (section 5): double sum of squares, eps inside
+  the square root.
+* ``latent_forward`` / ``latent_layer`` -- Kimi-K3's Stable LatentMoE
+  (section 9, k3_moe): routing on the full width, down-projection into the
+  latent, experts there, RMSNorm of the weighted aggregate, up-projection,
+  full-width shared experts added unweighted.
 """
 from __future__ import annotations
 
@@ -73,6 +79,9 @@ def lib():
         L.orc_forward.argtypes = [vp, vp, i, i, i, i, vp, vp, vp, vp, vp, vp, vp, vp,
                                   i, vp, vp, vp, i, i, f, f]
         L.orc_counts.argtypes = [vp, vp, i, i, i]
+        L.orc_rmsnorm.argtypes = [vp, vp, vp, i, f]
+        L.orc_latent_forward.argtypes = [vp, vp, i, i, i, i, i, vp, vp, vp, vp, vp, vp, vp, vp,
+                                         vp, i, vp, f, vp, i, vp, vp, vp, i, f, f]
         L.orc_threads.restype = i
         L.orc_threads.argtypes = []
         _lib = L
@@ -256,3 +265,66 @@ def screened_tokens(shape, seed: int, layer_idx: int, T: int, router_w: np.ndarr
                                   first_token=first_token + int(t))[0]
         todo = bad
     raise RuntimeError("screened_tokens: no acceptable draw within max_attempts")
+
+
+# ------------------------------------------------------------------ latent layer
+
+RMS_EPS = 1e-5
+
+
+def rmsnorm(x: np.ndarray, w: Optional[np.ndarray], eps: float = RMS_EPS) -> np.ndarray:
+    x = _c(x, np.float32)
+    assert x.ndim == 1
+    wv = None if w is None else _c(w, np.float32)
+    assert wv is None or wv.shape == x.shape
+    out = np.empty_like(x)
+    lib().orc_rmsnorm(_p(out), _p(x), _p(wv), x.size, eps)
+    return out
+
+
+def latent_forward(x_bf16: np.ndarray, slot: np.ndarray, weights: np.ndarray, held, down, up,
+                   norm_w: Optional[np.ndarray], shared, latent_norm: int = 1,
+                   eps: float = RMS_EPS, mode: int = ACT_SITU, b1: float = SITU_B1,
+                   b2: float = SITU_B2) -> np.ndarray:
+    """out[T][hidden] fp32 of the latent layer given the routing: ``held`` =
+    (w1q, w1s, w3q, w3s, w2q, w2s) of the experts (latent width) that
+    ``slot[T][k]`` indexes (negative = skip); ``down`` [latent][hidden] and
+    ``up`` [hidden][latent] bf16 bits; ``shared`` = (sh1, sh3, sh2) at the
+    hidden width."""
+    x = _c(x_bf16, np.uint16)
+    T, H = x.shape
+    slot = _c(slot, np.int32)
+    k = slot.shape[1] if slot.ndim == 2 else 0
+    w = _c(weights, np.float32)
+    w1q, w1s, w3q, w3s, w2q, w2s = [_c(a, np.uint8) for a in held]
+    F, Ld = w1q.shape[1], w1q.shape[2] * 2
+    assert w2q.shape[1] == Ld and w2q.shape[2] * 2 == F
+    assert slot.size == 0 or int(slot.max()) < w1q.shape[0]
+    down = _c(down, np.uint16)
+    up = _c(up, np.uint16)
+    assert down.shape == (Ld, H) and up.shape == (H, Ld)
+    nw = None if norm_w is None else _c(norm_w, np.float32)
+    assert nw is None or nw.shape == (Ld,)
+    sh1, sh3, sh2 = [_c(a, np.uint16) for a in shared]
+    S = sh1.shape[0]
+    assert S == 0 or (sh1.shape == (S, F, H) and sh2.shape == (S, H, F))
+    out = np.empty((T, H), dtype=np.float32)
+    lib().orc_latent_forward(_p(out), _p(x), T, H, Ld, F, k, _p(slot), _p(w), _p(down), _p(w1q),
+                             _p(w1s), _p(w3q), _p(w3s), _p(w2q), _p(w2s), int(latent_norm), _p(nw),
+                             eps, _p(up), S, _p(sh1), _p(sh3), _p(sh2), mode, b1, b2)
+    return out
+
+
+def latent_layer(h, x_bf16: np.ndarray, k: int, latent_norm: int = 1, eps: float = RMS_EPS,
+                 mode: int = ACT_SITU, b1: float = SITU_B1, b2: float = SITU_B2,
+                 renorm: int = 1, routed_scale: float = 1.0):
+    """Whole latent layer (``h``: a synth.HostLatentLayer holding every
+    expert the router picks): returns (ids, weights, out)."""
+    c = h.core
+    ids, w, _ = route(x_bf16, c.router_w, c.router_bias, k, renorm, routed_scale)
+    pos = {int(e): i for i, e in enumerate(c.experts)}
+    slot = np.vectorize(lambda e: pos.get(int(e), -1), otypes=[np.int32])(ids)
+    assert (slot >= 0).all(), "latent_layer(): an expert the router picked is not held"
+    out = latent_forward(x_bf16, slot, w, held_arrays(c), h.down, h.up, h.norm_w,
+                         shared_arrays(c), latent_norm, eps, mode, b1, b2)
+    return ids, w, out

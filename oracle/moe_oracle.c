@@ -1,7 +1,10 @@
 /*
  * moe_oracle.c -- plain, slow, obviously correct CPU reference of the
  * routed-expert MoE layer (sigmoid top-k router, MXFP4 expert FFNs with a
- * gated activation, weighted combine, unweighted bf16 shared experts).
+ * gated activation, weighted combine, unweighted bf16 shared experts), and
+ * of Kimi-K3's Stable LatentMoE around it (router and shared experts on the
+ * full-width input, bf16 projections into and out of the experts' latent,
+ * RMSNorm of the weighted aggregate).
  *
  * TEST INFRASTRUCTURE ONLY.  Nothing on the product path may link, load or
  * call this file: only the tests, the smoke check and the benchmark's CPU
@@ -282,6 +285,86 @@ void orc_forward(float *out, const uint16_t *x, int T, int d, int F, int k,
         for (int i = 0; i < d; i++) out[(size_t)t * d + i] = (float)acc[i];
     }
     free(xf); free(y); free(g); free(u); free(h); free(acc);
+}
+
+/* ---------------------------------------------------------- latent layer */
+
+/*
+ * RMSNorm of one vector (kimi-k3-in-c section 5, k3_rmsnorm): the sum of
+ * squares in double, eps inside the square root, the inverse rounded to
+ * fp32 once, then out[i] = x[i] * inv * w[i] as two fp32 products (w == NULL
+ * stands for a weight of 1).  out may alias x.
+ */
+void orc_rmsnorm(float *out, const float *x, const float *w, int n, float eps)
+{
+    double ss = 0.0;
+    for (int i = 0; i < n; i++) ss += (double)x[i] * (double)x[i];
+    const float inv = (float)(1.0 / sqrt(ss / (double)n + (double)eps));
+    for (int i = 0; i < n; i++) out[i] = x[i] * inv * (w ? w[i] : 1.0f);
+}
+
+/*
+ * Kimi-K3's Stable LatentMoE for T tokens, given the routing (kimi-k3-in-c
+ * section 9, k3_moe and its six steps; the routing itself, step 1, is
+ * orc_route on the full-width input):
+ *   2. z = Wdown x                       (bf16 [latent][hidden], fp32 z)
+ *   3. acc = sum_j w_j FFN_{slot_j}(z)   (experts in the latent; double sum
+ *                                         in j order, stored fp32)
+ *   4. n = RMSNorm(acc) * norm_w         (the AGGREGATE, if latent_norm)
+ *   5. out = Wup n                       (bf16 [hidden][latent])
+ *   6. out += sum_s FFN_shared_s(x)      (full width, on the ORIGINAL x,
+ *                                         unweighted; double sum, then fp32)
+ * Routed expert slot[t][j] indexes the held experts ([F][latent/2] codes +
+ * [F][latent/32] scales for W1, W3; [latent][F/2] + [latent][F/32] for W2);
+ * a negative slot skips the term.  Shared experts are [S][F][hidden] (W1s,
+ * W3s) and [S][hidden][F] (W2s) bf16.
+ */
+void orc_latent_forward(float *out, const uint16_t *x, int T, int hidden, int latent, int F, int k,
+                        const int32_t *slot, const float *w, const uint16_t *down,
+                        const uint8_t *w1q, const uint8_t *w1s, const uint8_t *w3q,
+                        const uint8_t *w3s, const uint8_t *w2q, const uint8_t *w2s,
+                        int latent_norm, const float *norm_w, float eps, const uint16_t *up,
+                        int n_shared, const uint16_t *sh1, const uint16_t *sh3,
+                        const uint16_t *sh2, int act, float b1, float b2)
+{
+    const size_t q13 = (size_t)F * (latent / 2), s13 = (size_t)F * (latent / 32);
+    const size_t q2b = (size_t)latent * (F / 2), s2b = (size_t)latent * (F / 32);
+    float *xf = (float *)malloc((size_t)hidden * sizeof(float));
+    float *z = (float *)malloc((size_t)latent * sizeof(float));
+    float *y = (float *)malloc((size_t)latent * sizeof(float));
+    float *nv = (float *)malloc((size_t)latent * sizeof(float));
+    float *o = (float *)malloc((size_t)hidden * sizeof(float));
+    float *ys = (float *)malloc((size_t)hidden * sizeof(float));
+    float *g = (float *)malloc((size_t)F * sizeof(float));
+    float *u = (float *)malloc((size_t)F * sizeof(float));
+    float *h = (float *)malloc((size_t)F * sizeof(float));
+    double *acc = (double *)malloc((size_t)(hidden > latent ? hidden : latent) * sizeof(double));
+    for (int t = 0; t < T; t++) {
+        orc_bf16_to_f32(xf, x + (size_t)t * hidden, (size_t)hidden);
+        orc_bf16_matvec(z, xf, down, hidden, latent);
+        for (int i = 0; i < latent; i++) acc[i] = 0.0;
+        for (int j = 0; j < k; j++) {
+            const int e = slot[(size_t)t * k + j];
+            if (e < 0) continue;
+            ffn(y, z, latent, F, act, b1, b2,
+                w1q + e * q13, w1s + e * s13, w3q + e * q13, w3s + e * s13,
+                w2q + e * q2b, w2s + e * s2b, NULL, NULL, NULL, g, u, h);
+            const double wj = (double)w[(size_t)t * k + j];
+            for (int i = 0; i < latent; i++) acc[i] += wj * (double)y[i];
+        }
+        for (int i = 0; i < latent; i++) nv[i] = (float)acc[i];
+        if (latent_norm) orc_rmsnorm(nv, nv, norm_w, latent, eps);
+        orc_bf16_matvec(o, nv, up, latent, hidden);
+        for (int i = 0; i < hidden; i++) acc[i] = (double)o[i];
+        for (int s = 0; s < n_shared; s++) {
+            ffn(ys, xf, hidden, F, act, b1, b2, NULL, NULL, NULL, NULL, NULL, NULL,
+                sh1 + (size_t)s * F * hidden, sh3 + (size_t)s * F * hidden,
+                sh2 + (size_t)s * hidden * F, g, u, h);
+            for (int i = 0; i < hidden; i++) acc[i] += (double)ys[i];
+        }
+        for (int i = 0; i < hidden; i++) out[(size_t)t * hidden + i] = (float)acc[i];
+    }
+    free(xf); free(z); free(y); free(nv); free(o); free(ys); free(g); free(u); free(h); free(acc);
 }
 
 /* expert counts: counts[e] = number of (t, j) with ids[t][j] == e */

@@ -14,7 +14,13 @@ Workload recipe (every shape and distribution of the five workloads):
 * shared expert weights bf16 ~ N(0, std = 1/sqrt(d)); router weights fp32
   ~ N(0, std = 1/sqrt(d)); tokens x bf16 ~ N(0, 1);
 * the 12-layer workload adds a Zipf(s = 1.1) selection bias over a seeded
-  permutation of the expert ids (one permutation for all layers).
+  permutation of the expert ids (one permutation for all layers);
+* the latent layer (Kimi-K3's Stable LatentMoE, kimi-k3-in-c section 9):
+  tokens, router and shared experts at the hidden width, routed experts at
+  the latent width with the distributions above; the bf16 projections down
+  [latent][hidden] ~ N(0, 1/sqrt(hidden)) and up [hidden][latent]
+  ~ N(0, 1/sqrt(latent)) (std = 1/sqrt(fan-in)); the fp32 RMSNorm weight
+  [latent] ~ N(1, 0.1).
 
 Token redraws (the rule that rejects tokens whose k-th / (k+1)-th selection
 score gap is under 1e-4) need router scores, which are the method's
@@ -37,6 +43,7 @@ _LIB = os.path.join(_HERE, "libsynth.so")
 
 # stream ids of the tensors of one layer
 T_X, T_ROUTER, T_W1Q, T_W1S, T_W3Q, T_W3S, T_W2Q, T_W2S, T_SH1, T_SH3, T_SH2, T_PERM = range(1, 13)
+T_DOWN, T_UP, T_NORM = range(13, 16)  # latent layer: projections and the aggregate's norm weight
 SCALE_LO, SCALE_COUNT = 119, 4
 ZIPF_S = 1.1
 
@@ -229,9 +236,13 @@ class HostLayer:
 
 
 def host_layer(shape: LayerShape, seed: int, layer: int, zipf: bool = False,
-               experts: Optional[Sequence[int]] = None) -> HostLayer:
+               experts: Optional[Sequence[int]] = None,
+               outer: Optional[LayerShape] = None) -> HostLayer:
     """Generate a layer on the host.  ``experts`` (default: all) picks which
-    routed experts to materialise; the bytes of an expert do not depend on it."""
+    routed experts to materialise; the bytes of an expert do not depend on it.
+    ``outer`` (default: ``shape``) is the shape of the router and the shared
+    experts, whose width differs from the experts' in the latent layer."""
+    outer = shape if outer is None else outer
     ids = np.arange(shape.n_experts, dtype=np.int32) if experts is None \
         else np.asarray(experts, dtype=np.int32)
     mats = {}
@@ -248,9 +259,79 @@ def host_layer(shape: LayerShape, seed: int, layer: int, zipf: bool = False,
             expert_mxfp4(shape, seed, layer, which, int(ids[i]), j - i + 1, q[i:j + 1], s[i:j + 1])
             i = j + 1
         mats[which] = (q, s)
-    sh1, sh3, sh2 = shared_weights(shape, seed, layer)
-    return HostLayer(shape=shape, router_w=router_weight(shape, seed, layer),
+    sh1, sh3, sh2 = shared_weights(outer, seed, layer)
+    return HostLayer(shape=shape, router_w=router_weight(outer, seed, layer),
                      router_bias=zipf_bias(shape, seed) if zipf else None, experts=ids,
                      w1q=mats["w1"][0], w1s=mats["w1"][1], w3q=mats["w3"][0], w3s=mats["w3"][1],
                      w2q=mats["w2"][0], w2s=mats["w2"][1], sh_w1=sh1, sh_w3=sh3, sh_w2=sh2,
                      meta=dict(seed=seed, layer=layer, zipf=zipf))
+
+
+# ------------------------------------------------------------------ latent layer
+
+@dataclass(frozen=True)
+class LatentShape:
+    """Kimi-K3's Stable LatentMoE: router and S shared experts on the hidden
+    width, E routed experts (top-k, FFN width F) in the latent width."""
+    n_experts: int
+    top_k: int
+    n_shared: int
+    hidden: int
+    latent: int
+    d_ffn: int
+
+    @property
+    def outer(self) -> LayerShape:
+        """The full-width tensors' shape (tokens, router, shared experts)."""
+        return LayerShape(self.n_experts, self.top_k, self.n_shared, self.hidden, self.d_ffn)
+
+    @property
+    def inner(self) -> LayerShape:
+        """The routed experts' shape (d_model = latent)."""
+        return LayerShape(self.n_experts, self.top_k, self.n_shared, self.latent, self.d_ffn)
+
+    @property
+    def projection_bytes(self) -> int:
+        return 2 * self.hidden * self.latent * 2 + self.latent * 4
+
+
+K3_LATENT = LatentShape(n_experts=896, top_k=16, n_shared=2, hidden=7168, latent=3584, d_ffn=3072)
+TINY_LATENT = LatentShape(n_experts=8, top_k=2, n_shared=1, hidden=512, latent=256, d_ffn=512)
+
+LATENT_WORKLOADS = [
+    Workload("tiny-latent-E8k2S1-h512l256F512-T4", TINY_LATENT.inner, tokens=4, seed=1100),
+    Workload("k3-latent-moe-decode-T1", K3_LATENT.inner, tokens=1, seed=1101),
+    Workload("k3-latent-moe-prefill-T4096", K3_LATENT.inner, tokens=4096, seed=1103),
+]
+
+
+def latent_projections(shape: LatentShape, seed: int, layer: int):
+    """down [latent][hidden] and up [hidden][latent] (bf16 bits), norm weight [latent] fp32."""
+    L = lib()
+    H, Ld = shape.hidden, shape.latent
+    down = np.empty((Ld, H), dtype=np.uint16)
+    up = np.empty((H, Ld), dtype=np.uint16)
+    nw = np.empty(Ld, dtype=np.float32)
+    L.synth_normal_bf16(_p(down), down.size, L.synth_key(seed, layer, T_DOWN, 0, 0), 1.0 / np.sqrt(H))
+    L.synth_normal_bf16(_p(up), up.size, L.synth_key(seed, layer, T_UP, 0, 0), 1.0 / np.sqrt(Ld))
+    L.synth_normal_f32(_p(nw), nw.size, L.synth_key(seed, layer, T_NORM, 0, 0), 0.1)
+    nw += np.float32(1.0)
+    return down, up, nw
+
+
+@dataclass
+class HostLatentLayer:
+    """A latent layer in host memory: ``core`` holds the router [E][hidden],
+    the routed experts (latent width) and the shared experts (hidden width)."""
+    shape: LatentShape
+    core: HostLayer
+    down: np.ndarray
+    up: np.ndarray
+    norm_w: np.ndarray
+
+
+def host_latent_layer(shape: LatentShape, seed: int, layer: int, zipf: bool = False,
+                      experts: Optional[Sequence[int]] = None) -> HostLatentLayer:
+    inner = host_layer(shape.inner, seed, layer, zipf=zipf, experts=experts, outer=shape.outer)
+    down, up, nw = latent_projections(shape, seed, layer)
+    return HostLatentLayer(shape=shape, core=inner, down=down, up=up, norm_w=nw)
