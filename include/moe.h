@@ -198,6 +198,92 @@ moe_status moe_layer_timed(const moe_layer_desc *desc, const uint16_t *x, int32_
  * captured with).  MOE_EINVAL for a negative value. */
 moe_status moe_set_one_token_router_wait(int32_t microseconds);
 
+/*
+ * Kimi-K3's Stable LatentMoE around the routed experts ("kimi-k3-in-c",
+ * section 9, k3_moe, its six steps; section 5, k3_rmsnorm; section 2, the
+ * K3Cfg fields latent, latent_norm and rms_eps):
+ *
+ *   1. route on the FULL-width x[t] (hidden wide), as moe_route does;
+ *   2. z = W_down x[t]                    (W_down [latent][hidden] bf16);
+ *   3. a = sum_j weight_j * FFN_{id_j}(z) (the routed experts, in the latent);
+ *   4. n = RMSNorm(a) * norm_w            (of the AGGREGATE, not per expert:
+ *                                          n_i = a_i * inv * w_i with
+ *                                          inv = 1 / sqrt(sum a^2 / latent
+ *                                          + rms_eps), if latent_norm);
+ *   5. out = W_up n                       (W_up [hidden][latent] bf16);
+ *   6. out += sum_s FFN_shared_s(x[t])    (full width, on the ORIGINAL x,
+ *                                          added unweighted).
+ *
+ * Shapes: E, k, F, S as for moe_layer_desc; H = hidden, L = latent.
+ * Supported: H a multiple of 32 in [32, 8192], L one in [32, 4096],
+ * L + S*F <= 16384 and the moe_layer_desc limits on E, k, F and S;
+ * otherwise MOE_EUNSUPPORTED.  The MFMA path (AUTO above 24 tokens) also needs H and
+ * L multiples of 256 and the moe_layer_desc MFMA limits; AUTO falls back to
+ * GEMV outside them.
+ *
+ * Precision: the latent z reaches the MXFP4 experts as fp16 with one
+ * power-of-two scale per token (11 significant bits); the normed aggregate
+ * reaches W_up in fp32 (GEMV) or as two bf16 parts (16 bits, MFMA); every
+ * product accumulates in fp32, sums of squares in double.
+ *
+ * The expert tensors are those of moe_layer_desc with d = latent (W1, W3
+ * [E][F][L/2] + [E][F][L/32]; W2 [E][L][F/2] + [E][L][F/32]); router and
+ * shared experts take the hidden width.  Alignment: code arrays, router_w,
+ * down, up and the shared weights 16 bytes.
+ */
+typedef struct {
+    int32_t n_experts, top_k, hidden, latent, d_ffn, n_shared;
+    int32_t renorm;          /* as in moe_layer_desc (K3: 1)                     */
+    float routed_scale;      /* (K3: 1.0)                                        */
+    int32_t act;             /* moe_act                                         */
+    float situ_b1, situ_b2;  /* (K3: 4.0, 25.0)                                  */
+    int32_t latent_norm;     /* 1: RMSNorm of the aggregate (K3: 1); 0: none     */
+    float rms_eps;           /* inside the square root (K3: 1e-5), >= 0           */
+    int32_t path;            /* moe_path                                        */
+    const float *router_w;   /* [E][H] fp32                                      */
+    const float *router_bias;/* [E] fp32 selection bias, or NULL                 */
+    const uint16_t *down;    /* [L][H] bf16 bits                                 */
+    const uint8_t *w1_q, *w1_s;  /* gate: [E][F][L/2], [E][F][L/32]             */
+    const uint8_t *w3_q, *w3_s;  /* up:   [E][F][L/2], [E][F][L/32]             */
+    const uint8_t *w2_q, *w2_s;  /* down: [E][L][F/2], [E][L][F/32]             */
+    const float *norm_w;     /* [L] fp32 RMSNorm weight, or NULL for weight 1     */
+    const uint16_t *up;      /* [H][L] bf16 bits                                 */
+    const uint16_t *sh_w1;   /* shared gate [S][F][H] bf16                        */
+    const uint16_t *sh_w3;   /* shared up   [S][F][H] bf16                        */
+    const uint16_t *sh_w2;   /* shared down [S][H][F] bf16                        */
+} moe_latent_desc;
+
+/* Workspace bytes of moe_latent_layer for up to max_tokens tokens (0 if the
+ * descriptor is invalid or unsupported); 256-byte aligned, no
+ * initialisation needed, nothing in it a caller reads. */
+size_t moe_latent_workspace_bytes(const moe_latent_desc *desc, int32_t max_tokens);
+
+/* The expert path a moe_latent_layer call with T tokens takes. */
+int32_t moe_latent_path_for(const moe_latent_desc *desc, int32_t T);
+
+/*
+ * The latent layer.  x: [T][H] bf16 bits (16-byte aligned); out_bf16 / out_f32
+ * [T][H] as out_mode asks (bf16 = round to nearest even of the fp32 result);
+ * ids_opt / weights_opt ([T][k], the routing as moe_route orders it) and
+ * counts_opt ([E]) receive the routing when non-NULL.
+ */
+moe_status moe_latent_layer(const moe_latent_desc *desc, const uint16_t *x, int32_t T,
+                            uint16_t *out_bf16, float *out_f32, int32_t out_mode,
+                            int32_t *ids_opt, float *weights_opt, int32_t *counts_opt,
+                            void *ws, size_t ws_bytes, void *stream);
+
+/*
+ * moe_latent_layer with phase timing (results equal bit for bit): events[0]
+ * before the first launch, [1] after the full-width front (router logits,
+ * z, the shared experts' gate/up), [2] after top-k, dispatch and the fp16 z,
+ * [3] after the routed gate/up, [4] after the routed down, [5] after the
+ * aggregate, its norm, the up projection, the shared experts' down and the
+ * output.
+ */
+moe_status moe_latent_layer_timed(const moe_latent_desc *desc, const uint16_t *x, int32_t T,
+                                  uint16_t *out_bf16, float *out_f32, int32_t out_mode,
+                                  void *ws, size_t ws_bytes, void *stream, void *const *events);
+
 /* Static text for a status code. */
 const char *moe_status_str(int32_t status);
 

@@ -227,6 +227,28 @@ __device__ __forceinline__ float fp4x32_dot_bf16(const uint4 q, const uint32_t *
     return p0 + p1;
 }
 
+// One MXFP4 block dotted with 32 fp16 inputs packed two per dword in column
+// order; unscaled partial sum (the codes decode exactly to fp16, the
+// products are exact in fp32)
+__device__ __forceinline__ float fp4x32_dot_f16(const uint4 q, const uint32_t *xp)
+{
+    uint32_t w[4];
+    opaque4(w, q);
+    float p0 = 0.0f, p1 = 0.0f;
+#pragma unroll
+    for (int i = 0; i < 4; i++) {
+        const f16x2v_t a0 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w[i], 1.0f, 0);
+        const f16x2v_t a1 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w[i], 1.0f, 1);
+        const f16x2v_t a2 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w[i], 1.0f, 2);
+        const f16x2v_t a3 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w[i], 1.0f, 3);
+        p0 = __builtin_amdgcn_fdot2(a0, __builtin_bit_cast(f16x2v_t, xp[4 * i + 0]), p0, false);
+        p1 = __builtin_amdgcn_fdot2(a1, __builtin_bit_cast(f16x2v_t, xp[4 * i + 1]), p1, false);
+        p0 = __builtin_amdgcn_fdot2(a2, __builtin_bit_cast(f16x2v_t, xp[4 * i + 2]), p0, false);
+        p1 = __builtin_amdgcn_fdot2(a3, __builtin_bit_cast(f16x2v_t, xp[4 * i + 3]), p1, false);
+    }
+    return p0 + p1;
+}
+
 // One MXFP4 block dotted with 32 fp32 inputs; unscaled partial sum.
 __device__ __forceinline__ float fp4x32_dot_f32(const uint4 q, const float *h)
 {
@@ -302,22 +324,76 @@ hipError_t launch_dispatch(const Shape &s, int do_topk, const float *logits, con
 
 // dequant-fused GEMV experts: shared down + routed gate/up + activation, then
 // routed down + weight.  ev2 (optional): events recorded after each launch.
+// zh / zsc (optional, the latent layer): the routed experts' input is the
+// fp16 rows zh[T][d] times their scales zsc[T] instead of x.
 hipError_t launch_gemv_experts(const Shape &s, const uint16_t *x, const Weights &wt,
                                int include_shared, const Work &w, hipStream_t stream,
-                               hipEvent_t const *ev2);
+                               hipEvent_t const *ev2, const uint16_t *zh = nullptr,
+                               const float *zsc = nullptr);
 
 // grouped MFMA GEMM path (prefill): router logits via 3-part bf16 split of
 // the router weights, and the experts (shared + routed gate/up, then down)
 bool mfma_supported(const Shape &s);
 size_t mfma_extra_workspace(const Shape &s);
 size_t mfma_token_workspace(const Shape &s);
-size_t router_part_workspace(const Shape &s);
+size_t router_part_workspace(const Shape &s, int parts = 3);
 constexpr int kRouterPartRows = 8192;  // rows of E partial logits (MFMA router K slices)
 hipError_t launch_mfma_router(const Shape &s, const uint16_t *x, const Weights &wt, const Work &w,
                               hipStream_t stream);
 hipError_t launch_mfma_experts(const Shape &s, const uint16_t *x, const Weights &wt,
                                int include_shared, const Work &w, hipStream_t stream,
                                hipEvent_t const *ev2);
+
+// ---- latent layer (Kimi-K3's Stable LatentMoE around the routed experts)
+
+// MFMA path pieces: out[T][N] = x W^T (bf16, s.d = K, s.E = N; partials in
+// w.rpart); the routed experts on the fp16 rows zh times zsc; the shared
+// experts' gate/up at the full width; the up projection of n (bf16 hi / lo
+// parts) into ysh slot 0 and the shared experts' down into slots 1 .. S
+hipError_t launch_mfma_linear(const Shape &s, const uint16_t *x, const uint16_t *W, float *out,
+                              const Work &w, hipStream_t st);
+hipError_t launch_mfma_latent_experts(const Shape &s, const Weights &wt, const uint16_t *zh,
+                                      const float *zsc, const Work &w, hipStream_t st,
+                                      hipEvent_t const *ev2);
+hipError_t launch_mfma_shared_gateup(const Shape &s, const uint16_t *x, const Weights &wt,
+                                     const Work &w, hipStream_t st);
+hipError_t launch_mfma_up_shared(const Shape &s, int L, const uint16_t *up, const uint16_t *nhi,
+                                 const uint16_t *nlo, const Weights &wt, const Work &w, float *ysh,
+                                 hipStream_t st);
+
+// the latent layer's own buffers (besides the routed part's Work)
+struct LatentBufs {
+    float *zf;        // [T][L] latent input z (fp32)
+    uint16_t *zh;     // [T][L] z / 2^s as fp16
+    float *zsc;       // [T]    2^s per token
+    float *accL;      // [T][L] weighted aggregate of the routed experts
+    double *ssp;      // [T][nch] its partial sums of squares
+    uint16_t *nhi, *nlo;  // [T][L] normed aggregate as bf16 hi + lo (MFMA path)
+    float *ysh;       // [S + 1][T][H] up projection, shared experts' downs (MFMA path)
+};
+constexpr int kLatentChunk = 1024;  // aggregate elements per block (one float4 per thread)
+inline int latent_chunks(int L) { return (L + kLatentChunk - 1) / kLatentChunk; }
+
+// GEMV front: router logits (width H), z = W_down x, shared gate/up +
+// activation (width H) -> w.logits, b.zf, w.Hs
+hipError_t launch_latent_front(const Shape &so, int L, const uint16_t *x, const Weights &wt,
+                               const uint16_t *down, const Work &w, const LatentBufs &b,
+                               hipStream_t st);
+// z -> fp16 rows with a power-of-two scale per token
+hipError_t launch_quant_z(int T, int L, const LatentBufs &b, hipStream_t st);
+// aggregate of each token's slot rows (ascending expert id) + partial sums of squares
+hipError_t launch_latent_accum(int T, int k, int L, const Work &w, const LatentBufs &b,
+                               hipStream_t st);
+// MFMA path: n = RMSNorm(aggregate) * norm_w (or the aggregate) as bf16 hi / lo
+hipError_t launch_latent_split(int T, int L, int do_norm, float eps, const float *norm_w,
+                               const LatentBufs &b, hipStream_t st);
+// GEMV path output: out = W_up n + sum_s W2s h_s (fp32 and / or bf16)
+hipError_t launch_latent_out(const Shape &so, int L, int do_norm, float eps, const float *norm_w,
+                             const uint16_t *up, const Weights &wt, const Work &w,
+                             const LatentBufs &b, uint16_t *out_bf16, float *out_f32,
+                             hipStream_t st);
+
+bool latent_out_fits(int L, int S, int F);
 
 // combine: out[t] = sum of the token's slot rows (ascending expert id)
 //                 + sum over shared experts of Ysh[s][t]

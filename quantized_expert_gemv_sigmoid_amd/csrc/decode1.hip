@@ -123,29 +123,6 @@ __device__ __forceinline__ float wave_total(float v)
     return (r0 + r1) + (r2 + r3);
 }
 
-typedef _Float16 f16x2d_t __attribute__((ext_vector_type(2)));
-
-// One MX block (16 bytes, 32 codes) times 32 fp16 inputs (16 packed dwords):
-// unscaled partial sum, products exact in fp32 (v_dot2_f32_f16)
-__device__ __forceinline__ float fp4x32_dot_f16(const uint4 q, const uint32_t *hp)
-{
-    uint32_t w[4];
-    opaque4(w, q);
-    float p0 = 0.0f, p1 = 0.0f;
-#pragma unroll
-    for (int i = 0; i < 4; i++) {
-        const f16x2d_t a0 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w[i], 1.0f, 0);
-        const f16x2d_t a1 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w[i], 1.0f, 1);
-        const f16x2d_t a2 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w[i], 1.0f, 2);
-        const f16x2d_t a3 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w[i], 1.0f, 3);
-        p0 = __builtin_amdgcn_fdot2(a0, __builtin_bit_cast(f16x2d_t, hp[4 * i + 0]), p0, false);
-        p1 = __builtin_amdgcn_fdot2(a1, __builtin_bit_cast(f16x2d_t, hp[4 * i + 1]), p1, false);
-        p0 = __builtin_amdgcn_fdot2(a2, __builtin_bit_cast(f16x2d_t, hp[4 * i + 2]), p0, false);
-        p1 = __builtin_amdgcn_fdot2(a3, __builtin_bit_cast(f16x2d_t, hp[4 * i + 3]), p1, false);
-    }
-    return p0 + p1;
-}
-
 // partial sums of two MX blocks scaled by their E8M0 bytes (low byte: first
 // block); a 255 byte drops its block
 __device__ __forceinline__ float scaled2(float a0, float a1, uint32_t s2)

@@ -27,6 +27,8 @@ struct GemvParams {
     const uint8_t *w1q, *w1s, *w3q, *w3s, *w2q, *w2s;
     const uint16_t *sh1, *sh3, *sh2;
     Work w;
+    const uint16_t *zh;  // latent layer: the experts' input as fp16 [T][d] ...
+    const float *zsc;    // ... times the token's power-of-two scale [T] (else null)
     int n_sh13;   // shared gate/up blocks (front kernel)
     int n_router; // router blocks (front kernel)
     int n_sh2;    // shared down blocks (gate/up kernel)
@@ -163,7 +165,9 @@ __device__ __forceinline__ void shared_down_tile(const GemvParams &p, int blk)
 // Gate/up of one routed expert for a tile of rows.  L lanes per row, so a
 // wave covers 64/L rows per load instruction; G such row groups are loaded
 // at once, before the token loop.  Lane g of a row holds MX blocks g + L*i.
-template <int NT, int L, int BPL, int G>
+// XH: the input is the fp16 rows zh, each times its scale zsc[t] (the
+// latent layer's experts), instead of the bf16 tokens x.
+template <int NT, int L, int BPL, int G, bool XH = false>
 __device__ __forceinline__ void routed_gateup_tile(const GemvParams &p, int blk)
 {
     constexpr int RPI = 64 / L;        // rows per load instruction
@@ -199,10 +203,13 @@ __device__ __forceinline__ void routed_gateup_tile(const GemvParams &p, int blk)
     }
     for (int c0 = 0; c0 < n; c0 += NT) {
         uint32_t xr[NT][BPL][16];
+        float xsc[NT];
 #pragma unroll
         for (int tt = 0; tt < NT; tt++) {
             const int i0 = c0 + tt;
-            const uint16_t *src = i0 < n ? p.x + (size_t)p.w.pos_tok[base + i0] * d : nullptr;
+            const int tok = i0 < n ? p.w.pos_tok[base + i0] : 0;
+            xsc[tt] = XH ? p.zsc[tok] : 1.0f;
+            const uint16_t *src = i0 < n ? (XH ? p.zh : p.x) + (size_t)tok * d : nullptr;
 #pragma unroll
             for (int i = 0; i < BPL; i++) {
                 const int bc = g + L * i;
@@ -229,8 +236,8 @@ __device__ __forceinline__ void routed_gateup_tile(const GemvParams &p, int blk)
                 float ga = 0.0f, ua = 0.0f;
 #pragma unroll
                 for (int i = 0; i < BPL; i++) {
-                    const float pg = fp4x32_dot_bf16(qa[gi][i], xr[tt][i]);
-                    const float pu = fp4x32_dot_bf16(qb[gi][i], xr[tt][i]);
+                    const float pg = XH ? fp4x32_dot_f16(qa[gi][i], xr[tt][i]) : fp4x32_dot_bf16(qa[gi][i], xr[tt][i]);
+                    const float pu = XH ? fp4x32_dot_f16(qb[gi][i], xr[tt][i]) : fp4x32_dot_bf16(qb[gi][i], xr[tt][i]);
                     ga = sa[gi][i] == 255u ? ga : fmaf(pg, e8m0_to_f32(sa[gi][i]), ga);
                     ua = sb[gi][i] == 255u ? ua : fmaf(pu, e8m0_to_f32(sb[gi][i]), ua);
                     // keep each block's decode next to its use (register pressure)
@@ -239,8 +246,8 @@ __device__ __forceinline__ void routed_gateup_tile(const GemvParams &p, int blk)
                 ga = group_sum<L>(ga);
                 ua = group_sum<L>(ua);
                 if (g == tt) {
-                    gv = ga;
-                    uv = ua;
+                    gv = XH ? ga * xsc[tt] : ga;
+                    uv = XH ? ua * xsc[tt] : ua;
                 }
             }
             if (g < NT && row < F && c0 + g < n)
@@ -340,12 +347,12 @@ __global__ __launch_bounds__(256) void k_front(GemvParams p)
     }
 }
 
-template <int NT, int L, int BPL, int G>
+template <int NT, int L, int BPL, int G, bool XH>
 __global__ __launch_bounds__(256) void k_gemv_gateup(GemvParams p)
 {
     const int blk = blockIdx.x;
     if (blk < p.n_sh2) shared_down_tile<NT>(p, blk);
-    else routed_gateup_tile<NT, L, BPL, G>(p, blk - p.n_sh2);
+    else routed_gateup_tile<NT, L, BPL, G, XH>(p, blk - p.n_sh2);
 }
 
 template <int NT, int L, int BPL, int G>
@@ -365,6 +372,8 @@ static GemvParams make_params(const Shape &s, const uint16_t *x, const Weights &
     p.w1q = wt.w1q; p.w1s = wt.w1s; p.w3q = wt.w3q; p.w3s = wt.w3s; p.w2q = wt.w2q; p.w2s = wt.w2s;
     p.sh1 = wt.sh1; p.sh3 = wt.sh3; p.sh2 = wt.sh2;
     p.w = w;
+    p.zh = nullptr;
+    p.zsc = nullptr;
     p.n_sh13 = p.n_router = p.n_sh2 = 0;
     p.tiles13 = p.tiles2 = 0;
     return p;
@@ -389,7 +398,9 @@ static void gateup_launch(GemvParams p, int max_active, hipStream_t stream)
     constexpr int RPB = (64 / L) * G * kWaves;
     p.tiles13 = (p.s.F + RPB - 1) / RPB;
     const int nblk = p.n_sh2 + max_active * p.tiles13;
-    if (nblk > 0) k_gemv_gateup<NT, L, BPL, G><<<nblk, 256, 0, stream>>>(p);
+    if (nblk <= 0) return;
+    if (p.zh) k_gemv_gateup<NT, L, BPL, G, true><<<nblk, 256, 0, stream>>>(p);
+    else k_gemv_gateup<NT, L, BPL, G, false><<<nblk, 256, 0, stream>>>(p);
 }
 
 template <int NT, int L, int BPL, int G>
@@ -403,9 +414,11 @@ static void down_launch(GemvParams p, int max_active, hipStream_t stream)
 
 hipError_t launch_gemv_experts(const Shape &s, const uint16_t *x, const Weights &wt,
                                int include_shared, const Work &w, hipStream_t stream,
-                               hipEvent_t const *ev2)
+                               hipEvent_t const *ev2, const uint16_t *zh, const float *zsc)
 {
     GemvParams p = make_params(s, x, wt, w);
+    p.zh = zh;
+    p.zsc = zsc;
     const int max_active = min(s.E, s.T * s.k);
     p.n_sh2 = (include_shared && s.S > 0) ? s.S * ((s.d + 7) / 8) : 0;
     const int nb13 = s.d / 32, nb2 = s.F / 32;

@@ -56,7 +56,11 @@ constexpr int kLdsBytes = 152 * 1024;   // LDS of a block (one block per CU)
 constexpr int kScaleBytes = 32 * 1024;  // MXFP4: the block's scale rows (256 of at most 128 bytes)
 constexpr uint32_t kPast = 0xF0000000u;  // a buffer offset past every resource: loads return 0, read nothing
 
-enum Mode { M_G13 = 0, M_D2 = 1, M_S13 = 2, M_S2 = 3, M_R = 4 };
+// G13 routed gate/up (tokens as fp8 terms, scaled MX MFMA); D2 routed down;
+// S13 / S2 shared gate/up and down (bf16); R router / plain linear (bf16
+// parts of the weights, fp32 out); G13H routed gate/up on fp16 input rows
+// with a power-of-two scale per row (the latent layer's experts)
+enum Mode { M_G13 = 0, M_D2 = 1, M_S13 = 2, M_S2 = 3, M_R = 4, M_G13H = 5 };
 
 struct GemmParams {
     Shape s;
@@ -74,6 +78,9 @@ struct GemmParams {
     int m_blocks;     // M passes spread over blocks (shared / router); 1 for routed
     int ksplit;       // router: K slices over blocks (partial logits summed after)
     float *rpart;     // router: partial logits [ksplit][T][E] (ksplit > 1)
+    int rparts;       // router: bf16 parts per weight row (3: fp32 weights; 1: bf16 weights)
+    const uint16_t *zh;  // G13H: input rows [T][d] fp16 ...
+    const float *zsc;    // ... times their scales [T]
 };
 
 // ---------------------------------------------------------------- helpers
@@ -191,8 +198,8 @@ __device__ __forceinline__ f32x16_t mfma32(f16x8_t a, f16x8_t b, f32x16_t c)
 
 template <int MODE>
 struct Cfg {
-    static constexpr bool kFp4 = (MODE == M_G13 || MODE == M_D2);
-    static constexpr bool kGated = (MODE == M_G13 || MODE == M_S13);
+    static constexpr bool kFp4 = (MODE == M_G13 || MODE == M_D2 || MODE == M_G13H);
+    static constexpr bool kGated = (MODE == M_G13 || MODE == M_S13 || MODE == M_G13H);
     static constexpr int KS = kFp4 ? 128 : 64;     // K per stage
     static constexpr int STEPS = KS / 16;          // MFMA K steps per stage
     static constexpr int AROW = KS * 2;            // bytes of one A row of a stage (G13: fp8 hi | lo)
@@ -270,17 +277,17 @@ template <int MODE>
 __device__ __forceinline__ uint32_t b_row(const GemmParams &p, const Blk &b, int c)
 {
     const Shape &s = p.s;
-    if constexpr (MODE == M_G13) return (uint32_t)gated_feature(b.tile, c) * (s.d / 2);
+    if constexpr (MODE == M_G13 || MODE == M_G13H) return (uint32_t)gated_feature(b.tile, c) * (s.d / 2);
     else if constexpr (MODE == M_D2) return (uint32_t)(b.tile * GN + c) * (s.F / 2);
     else if constexpr (MODE == M_S13) return (uint32_t)gated_feature(b.tile, c) * (s.d * 2);
     else if constexpr (MODE == M_S2) return (uint32_t)(b.tile * GN + c) * (s.F * 2);
-    else return (uint32_t)min(b.tile * GN + c, s.E - 1) * (3 * s.d * 2);  // router: past E re-read row E - 1
+    else return (uint32_t)min(b.tile * GN + c, s.E - 1) * (p.rparts * s.d * 2);  // router: past E re-read row E - 1
 }
 // scale row of block column c (see the layout above)
 template <int MODE>
 __device__ __forceinline__ int s_row_of(int c)
 {
-    return MODE == M_G13 ? ((c >> 5) & 1) * 128 + (c >> 6) * 32 + (c & 31) : c;
+    return (MODE == M_G13 || MODE == M_G13H) ? ((c >> 5) & 1) * 128 + (c >> 6) * 32 + (c & 31) : c;
 }
 
 // The block's scale rows into LDS at sc: copy j of wave w fills rows
@@ -300,7 +307,7 @@ __device__ __forceinline__ void load_scales(const GemmParams &p, const Blk &b, L
         const int q = (lane & 7) ^ (R & 7);
         uint32_t off;
         __amdgpu_buffer_rsrc_t r;
-        if constexpr (MODE == M_G13) {
+        if constexpr (MODE == M_G13 || MODE == M_G13H) {
             const uint32_t sb = (uint32_t)s.F * (s.d / 32);
             r = grsrc((n >= 16 ? p.w3s : p.w1s) + (size_t)b.e * sb, sb);  // (rows 128.. : up)
             off = (uint32_t)(b.tile * 128 + (R & 127)) * (s.d / 32) + q * 16;
@@ -351,6 +358,9 @@ __device__ __forceinline__ void wave_pass(const GemmParams &p, const Blk &bk, in
         } else if constexpr (MODE == M_S2) {
             abase = reinterpret_cast<const uint8_t *>(p.hs_hi);
             abytes = (uint32_t)s.T * s.S * s.F * 2;
+        } else if constexpr (MODE == M_G13H) {
+            abase = reinterpret_cast<const uint8_t *>(p.zh);
+            abytes = (uint32_t)s.T * s.d * 2;
         } else {
             abase = reinterpret_cast<const uint8_t *>(p.x);
             abytes = (uint32_t)s.T * s.d * 2;
@@ -371,6 +381,7 @@ __device__ __forceinline__ void wave_pass(const GemmParams &p, const Blk &bk, in
                 uint32_t el;  // element offset
                 if constexpr (MODE == M_D2) el = (uint32_t)(bk.base + m) * s.F;
                 else if constexpr (MODE == M_S2) el = (uint32_t)m * s.S * s.F + (uint32_t)bk.group * s.F;
+                else if constexpr (MODE == M_G13H) el = (uint32_t)p.w.pos_tok[bk.base + m] * s.d;
                 else el = (uint32_t)m * s.d;
                 e = el * 2 + q * 16;
             }
@@ -390,7 +401,7 @@ __device__ __forceinline__ void wave_pass(const GemmParams &p, const Blk &bk, in
         const int pc = (t % C::BP) ^ swz_b<MODE>(c);
         const int c0 = 64 * (8 * j + wave) / C::BP;  // the copy's first column (uniform)
         const bool up = (c0 >> 5) & 1;               // gated: the up matrix
-        if constexpr (MODE == M_G13) {
+        if constexpr (MODE == M_G13 || MODE == M_G13H) {
             const uint32_t qb = (uint32_t)s.F * (s.d / 2);
             rb[j] = grsrc((up ? p.w3q : p.w1q) + (size_t)bk.e * qb, qb);
         } else if constexpr (MODE == M_D2) {
@@ -403,7 +414,7 @@ __device__ __forceinline__ void wave_pass(const GemmParams &p, const Blk &bk, in
             const uint32_t qb = (uint32_t)s.d * s.F * 2;
             rb[j] = grsrc(reinterpret_cast<const uint8_t *>(p.sh2) + (size_t)bk.group * qb, qb);
         } else {
-            rb[j] = grsrc(p.wr3, (uint32_t)s.E * 3 * s.d * 2);
+            rb[j] = grsrc(p.wr3, (uint32_t)s.E * p.rparts * s.d * 2);
         }
         boff[j] = b_row<MODE>(p, bk, c) + pc * 16;
     }
@@ -540,7 +551,7 @@ __device__ __forceinline__ void wave_pass(const GemmParams &p, const Blk &bk, in
             const LDS uint8_t *B = A + RG::ABYTES;
             uint4 af[2][NTW];
             if constexpr (C::kFp4) {
-                using BT = typename std::conditional<MODE == M_D2 && !SPLIT, f16x8_t, bf16x8_t>::type;
+                using BT = typename std::conditional<(MODE == M_D2 || MODE == M_G13H) && !SPLIT, f16x8_t, bf16x8_t>::type;
                 // this lane's two MX blocks (pieces 2 kh, 2 kh + 1) of each of its
                 // two columns, and their scale bytes (bytes 4 sa + 2 kh, + 1 of
                 // the column's scale row)
@@ -667,6 +678,19 @@ __device__ __forceinline__ void wave_pass(const GemmParams &p, const Blk &bk, in
             // of different values interleave; then the stores of the rows in
             // range
             float hv[NTW][16];
+            if constexpr (MODE == M_G13H) {
+                // the rows' input scales: lane i holds that of the wave's row
+                // 32 T0 + i (rows past the group take its last row's)
+                const float zl = p.zsc[p.w.pos_tok[bk.base + m0 + min(T0 * 32 + lane, mrows - 1)]];
+#pragma unroll
+                for (int mt = 0; mt < NTW; mt++)
+#pragma unroll
+                    for (int e = 0; e < 16; e++) {
+                        const float zr = __shfl(zl, mt * 32 + 8 * (e >> 2) + 4 * kh + (e & 3), 64);
+                        acc[mt][0][e] *= zr;
+                        acc[mt][1][e] *= zr;
+                    }
+            }
             if (s.act == MOE_ACT_SWIGLU) {
 #pragma unroll
                 for (int mt = 0; mt < NTW; mt++)
@@ -688,7 +712,7 @@ __device__ __forceinline__ void wave_pass(const GemmParams &p, const Blk &bk, in
                     const int r = (T0 + mt) * 32 + 8 * (e >> 2) + 4 * kh + (e & 3);
                     if (r >= mrows) continue;
                     const int m = m0 + r;
-                    if constexpr (MODE == M_G13) {
+                    if constexpr (MODE == M_G13 || MODE == M_G13H) {
                         // (32-bit offsets: the host keeps T k F below 2^31)
                         _Float16 *H = reinterpret_cast<_Float16 *>(p.w.H);
                         H[(uint32_t)(bk.base + m) * (uint32_t)s.F + (uint32_t)f] = (_Float16)hv[mt][e];
@@ -778,15 +802,15 @@ __global__ __launch_bounds__(GT) void k_ggemm(GemmParams p)
 
     b.base = 0;
     b.e = 0;
-    if constexpr (MODE == M_G13 || MODE == M_D2) {
+    if constexpr (C::kFp4) {
         if (b.group >= p.w.meta[0]) return;
         b.e = p.w.active[b.group];
         b.M = p.w.counts[b.e];
         b.base = p.w.offsets[b.e];
-        b.K = MODE == M_G13 ? s.d : s.F;
+        b.K = MODE == M_D2 ? s.F : s.d;
     } else {
         b.M = s.T;
-        b.K = MODE == M_S13 ? s.d : (MODE == M_S2 ? 2 * s.F : 3 * s.d);
+        b.K = MODE == M_S13 ? s.d : (MODE == M_S2 ? 2 * s.F : p.rparts * s.d);
     }
     if constexpr (MODE == M_R) b.K /= p.ksplit;  // (a multiple of the stage, see the launch)
     b.nS = b.K / C::KS;
@@ -797,15 +821,24 @@ __global__ __launch_bounds__(GT) void k_ggemm(GemmParams p)
     // barrier cover them: the copies land in order)
     if constexpr (C::kFp4) load_scales<MODE>(p, b, ring);
 
-    if constexpr (MODE == M_D2) {
-        // The down projection multiplies fp16 H by W2 decoded to fp16, which
-        // is exact for scale bytes 104..140 (and 255, which decodes to 0).
-        // A block whose W2 scales leave that range takes the exact split
-        // path (bf16 weights, H split into two bf16 parts) for all its rows.
+    if constexpr (MODE == M_D2 || MODE == M_G13H) {
+        // The down projection multiplies fp16 H by W2 decoded to fp16 (G13H:
+        // the fp16 input rows by W1 / W3 decoded to fp16), which is exact
+        // for scale bytes 104..140 (and 255, which decodes to 0).  A block
+        // whose weight scales leave that range takes the exact split path
+        // (bf16 weights, the fp16 operand split into two bf16 parts) for all
+        // its rows.
         bool ok = true;
         if (threadIdx.x < GN) {
-            const uint8_t *sc = p.w2s + ((size_t)b.e * s.d + b.tile * GN + threadIdx.x) * (s.F / 32);
-            for (int i = 0; i < s.F / 32; i += 4) {
+            const int K = MODE == M_D2 ? s.F : s.d;
+            const uint8_t *sc;
+            if constexpr (MODE == M_D2) {
+                sc = p.w2s + ((size_t)b.e * s.d + b.tile * GN + threadIdx.x) * (K / 32);
+            } else {
+                const uint8_t *m = threadIdx.x < 128 ? p.w1s : p.w3s;
+                sc = m + ((size_t)b.e * s.F + min(b.tile * 128 + (int)(threadIdx.x & 127), s.F - 1)) * (K / 32);
+            }
+            for (int i = 0; i < K / 32; i += 4) {
                 const uint32_t v = *reinterpret_cast<const uint32_t *>(sc + i);
 #pragma unroll
                 for (int k = 0; k < 4; k++) {
@@ -945,12 +978,12 @@ bool mfma_supported(const Shape &s)
 }
 
 // K slices of the router GEMM: its grid has only ceil(E / 256) * ceil(T /
-// 128) blocks, so small T splits K = 3d (in units of two 64-wide stages)
-// until about 256 blocks run, within kRouterPartRows rows of partials
-int router_ksplit(const Shape &s)
+// 128) blocks, so small T splits K = parts d (in units of two 64-wide
+// stages) until about 256 blocks run, within kRouterPartRows rows of partials
+int router_ksplit(const Shape &s, int parts = 3)
 {
     if (s.d % 256 != 0 || s.F % 256 != 0) return 1;
-    const int nk = 3 * s.d / 128;
+    const int nk = parts * s.d / 128;
     const int blocks = ((s.E + GN - 1) / GN) * ((s.T + GM - 1) / GM);
     const int cap = min(min((256 + blocks - 1) / blocks, kRouterPartRows / max(s.T, 1)), nk);
     int ks = 1;
@@ -960,11 +993,11 @@ int router_ksplit(const Shape &s)
 }
 
 // partial router logits of the MFMA path: [ksplit][T][E], ksplit * T <=
-// min(T * 3d / 128, kRouterPartRows) (non-decreasing in T)
-size_t router_part_workspace(const Shape &s)
+// min(T * parts d / 128, kRouterPartRows) (non-decreasing in T)
+size_t router_part_workspace(const Shape &s, int parts)
 {
     if (s.d % 256 != 0 || s.F % 256 != 0) return 0;
-    const size_t rows = min((size_t)s.T * (3 * s.d / 128), (size_t)kRouterPartRows);
+    const size_t rows = min((size_t)s.T * (parts * s.d / 128), (size_t)kRouterPartRows);
     return rows * s.E * 4;
 }
 
@@ -1016,6 +1049,9 @@ static GemmParams make_gemm_params(const Shape &s, const uint16_t *x, const Weig
     p.groups = p.n_tiles = p.m_blocks = 0;
     p.ksplit = 1;
     p.rpart = w.rpart;
+    p.rparts = 3;
+    p.zh = nullptr;
+    p.zsc = nullptr;
     return p;
 }
 
@@ -1051,6 +1087,84 @@ hipError_t launch_mfma_experts(const Shape &s, const uint16_t *x, const Weights 
     if (include_shared && s.S > 0) launch_mode<M_S2>(p, s.S, (s.d + GN - 1) / GN, mb, st);
     launch_mode<M_D2>(p, max_active, (s.d + GN - 1) / GN, 1, st);
     if (ev2) (void)hipEventRecord(ev2[1], st);
+    return hipGetLastError();
+}
+
+// ------------------------------------------------- latent layer (prefill)
+
+// out[T][N] (fp32) = x[T][K] (bf16) W[N][K]^T (bf16): the router mode with
+// one bf16 part per weight row (s.d = K, s.E = N); small T splits K over
+// blocks (partials summed in slice order)
+hipError_t launch_mfma_linear(const Shape &s, const uint16_t *x, const uint16_t *W, float *out,
+                              const Work &w, hipStream_t st)
+{
+    Work wl = w;
+    wl.logits = out;
+    GemmParams p = make_gemm_params(s, x, Weights{}, wl);
+    p.wr3 = W;
+    p.rparts = 1;
+    const int nt = (s.E + GN - 1) / GN, mb = (s.T + GM - 1) / GM;
+    const int ks = router_ksplit(s, 1);
+    launch_mode<M_R>(p, 1, nt, mb, st, ks);
+    if (ks > 1) {
+        const int n = s.T * s.E;
+        k_router_reduce<<<(n + 255) / 256, 256, 0, st>>>(n, ks, w.rpart, out);
+    }
+    return hipGetLastError();
+}
+
+// routed experts of the latent layer: gate/up on the fp16 rows zh (times
+// their scales zsc), then down + routing weight into the slot rows
+hipError_t launch_mfma_latent_experts(const Shape &s, const Weights &wt, const uint16_t *zh,
+                                      const float *zsc, const Work &w, hipStream_t st,
+                                      hipEvent_t const *ev2)
+{
+    GemmParams p = make_gemm_params(s, nullptr, wt, w);
+    p.zh = zh;
+    p.zsc = zsc;
+    const int max_active = min(s.E, s.T * s.k);
+    launch_mode<M_G13H>(p, max_active, (s.F + 127) / 128, 1, st);
+    if (ev2) (void)hipEventRecord(ev2[0], st);
+    launch_mode<M_D2>(p, max_active, (s.d + GN - 1) / GN, 1, st);
+    if (ev2) (void)hipEventRecord(ev2[1], st);
+    return hipGetLastError();
+}
+
+// shared experts' gate/up at the full width (H fp32 split into bf16 hi / lo
+// parts in w.Hs)
+hipError_t launch_mfma_shared_gateup(const Shape &s, const uint16_t *x, const Weights &wt,
+                                     const Work &w, hipStream_t st)
+{
+    GemmParams p = make_gemm_params(s, x, wt, w);
+    if (s.S > 0) launch_mode<M_S13>(p, s.S, (s.F + 127) / 128, (s.T + GM - 1) / GM, st);
+    return hipGetLastError();
+}
+
+// ysh[(S + 1)][T][d]: slot 0 = W_up n (n as bf16 hi / lo parts [T][L]),
+// slots 1 .. S = the shared experts' down projections (s.d = hidden width)
+hipError_t launch_mfma_up_shared(const Shape &s, int L, const uint16_t *up, const uint16_t *nhi,
+                                 const uint16_t *nlo, const Weights &wt, const Work &w, float *ysh,
+                                 hipStream_t st)
+{
+    const int mb = (s.T + GM - 1) / GM;
+    {
+        Shape su = s;
+        su.S = 1;
+        su.F = L;
+        Work wu = w;
+        wu.Ysh = ysh;
+        GemmParams p = make_gemm_params(su, nullptr, Weights{}, wu);
+        p.sh2 = up;
+        p.hs_hi = nhi;
+        p.hs_lo = nlo;
+        launch_mode<M_S2>(p, 1, (s.d + GN - 1) / GN, mb, st);
+    }
+    if (s.S > 0) {
+        Work ws = w;
+        ws.Ysh = ysh + (size_t)s.T * s.d;
+        GemmParams p = make_gemm_params(s, nullptr, wt, ws);
+        launch_mode<M_S2>(p, s.S, (s.d + GN - 1) / GN, mb, st);
+    }
     return hipGetLastError();
 }
 

@@ -1,0 +1,424 @@
+// Kimi-K3's Stable LatentMoE around the routed experts (kimi-k3-in-c
+// section 9, k3_moe): the router and the shared experts read the full-width
+// input x[T][H]; a bf16 projection takes x down into the experts' latent
+// width L; the chosen experts run there and their weighted outputs are
+// summed; that AGGREGATE (not each expert's output) is RMS-normalised
+// (section 5, k3_rmsnorm: double sum of squares, eps inside the root, the
+// inverse rounded to fp32, then two fp32 products); a bf16 projection takes
+// it back up to H; the shared experts' outputs are added unweighted.
+//
+// Precision: the latent z feeds the MXFP4 experts as fp16 rows, each scaled
+// by a power of two that puts its largest |z| in [2^14, 2^15) (11
+// significant bits; 8-bit formats such as bf16 alone would cost about
+// 2e-3 of the output).  The normed aggregate reaches the up projection in
+// fp32 (GEMV) or as two bf16 parts whose sum carries 16 significant bits
+// (MFMA).  Sums of squares are accumulated in double.
+//
+// Kernels of the small-T (GEMV) path:
+//   k_latent_front  router rows, down-projection rows and the shared
+//                   experts' gate/up pairs (all reading x), one launch
+//   k_quant_z       z -> fp16 rows + per-token scale
+//   k_latent_accum  the aggregate per token (fixed ascending-id order) and
+//                   partial sums of squares per 1024-element chunk
+//   k_latent_out    RMSNorm on the fly while staging the token's inputs in
+//                   LDS, then W_up n + sum_s W2s h_s per output row
+// The MFMA path shares k_quant_z and k_latent_accum and adds k_latent_split
+// (the normed aggregate as bf16 hi / lo parts for the up projection GEMM).
+#include <algorithm>
+
+#include "common.h"
+#include "router_dev.h"
+
+namespace moe {
+
+namespace {
+
+__device__ __forceinline__ uint4 ld16(const void *p) { return *reinterpret_cast<const uint4 *>(p); }
+
+struct FrontParams {
+    int T, E, H, L, F, S, act;
+    float b1, b2;
+    const uint16_t *x;               // [T][H]
+    const float *Wr;                 // [E][H]
+    const uint16_t *down;            // [L][H]
+    const uint16_t *sh1, *sh3;       // [S][F][H]
+    float *logits, *zf, *Hs;         // [T][E], [T][L], [T][S*F]
+    int n_sh, n_dn;                  // blocks of shared pairs, of down rows (router blocks follow)
+};
+
+// bf16 row of width H (nb = H / 8 pieces of 16 bytes) into registers: lane
+// holds pieces lane + 64 i
+template <int NP>
+__device__ __forceinline__ void load_row(uint4 (&w)[NP], const uint16_t *row, int nb)
+{
+    const int lane = threadIdx.x & 63;
+#pragma unroll
+    for (int i = 0; i < NP; i++) {
+        const int c = lane + 64 * i;
+        w[i] = c < nb ? ld16(row + (size_t)c * 8) : make_uint4(0, 0, 0, 0);
+    }
+}
+
+// NP = ceil(H / 512) pieces per lane; the router row takes 2 NP float4
+template <int NP>
+__global__ __launch_bounds__(256) void k_latent_front(FrontParams p)
+{
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const int nb = p.H / 8;
+    int b = blockIdx.x;
+    if (b < p.n_sh) {
+        // one (gate, up) row pair of a shared expert per wave
+        const int pair = b * 4 + wave;
+        if (pair >= p.S * p.F) return;
+        const int sidx = pair / p.F, f = pair % p.F;
+        uint4 wg[NP], wu[NP];
+        load_row<NP>(wg, p.sh1 + ((size_t)sidx * p.F + f) * p.H, nb);
+        load_row<NP>(wu, p.sh3 + ((size_t)sidx * p.F + f) * p.H, nb);
+        for (int t = 0; t < p.T; t++) {
+            const uint16_t *xr = p.x + (size_t)t * p.H;
+            float ga = 0.0f, ua = 0.0f;
+#pragma unroll
+            for (int i = 0; i < NP; i++) {
+                const int c = lane + 64 * i;
+                if (c < nb) {
+                    const uint4 v = ld16(xr + (size_t)c * 8);
+                    const uint32_t xp[4] = {v.x, v.y, v.z, v.w};
+                    ga = bf16x8_dot_bf16(wg[i], xp, ga);
+                    ua = bf16x8_dot_bf16(wu[i], xp, ua);
+                }
+            }
+            ga = group_sum<64>(ga);
+            ua = group_sum<64>(ua);
+            if (lane == 0) p.Hs[(size_t)t * p.S * p.F + pair] = gated_act(ga, ua, p.act, p.b1, p.b2);
+        }
+        return;
+    }
+    b -= p.n_sh;
+    if (b < p.n_dn) {
+        // one down-projection row per wave: z[t][r] = W_down[r] . x[t]
+        const int r = b * 4 + wave;
+        if (r >= p.L) return;
+        uint4 w[NP];
+        load_row<NP>(w, p.down + (size_t)r * p.H, nb);
+        for (int t = 0; t < p.T; t++) {
+            const uint16_t *xr = p.x + (size_t)t * p.H;
+            float a = 0.0f;
+#pragma unroll
+            for (int i = 0; i < NP; i++) {
+                const int c = lane + 64 * i;
+                if (c < nb) {
+                    const uint4 v = ld16(xr + (size_t)c * 8);
+                    const uint32_t xp[4] = {v.x, v.y, v.z, v.w};
+                    a = bf16x8_dot_bf16(w[i], xp, a);
+                }
+            }
+            a = group_sum<64>(a);
+            if (lane == 0) p.zf[(size_t)t * p.L + r] = a;
+        }
+        return;
+    }
+    b -= p.n_dn;
+    const int e = b * 4 + wave;
+    if (e < p.E) router_row<2 * NP>(p.T, p.E, p.H, p.x, p.Wr, p.logits, e);
+}
+
+// one wave per token: largest |z| -> scale 2^s with max |z| / 2^s in
+// [2^14, 2^15) (below the fp16 maximum after rounding), zh = rne_fp16(z / 2^s)
+__global__ __launch_bounds__(256) void k_quant_z(int T, int L, const float *__restrict__ zf,
+                                                 uint16_t *__restrict__ zh, float *__restrict__ zsc)
+{
+    const int t = blockIdx.x * 4 + (threadIdx.x >> 6);
+    if (t >= T) return;
+    const int lane = threadIdx.x & 63;
+    const float4 *row = reinterpret_cast<const float4 *>(zf + (size_t)t * L);
+    const int n4 = L / 4;
+    float amax = 0.0f;
+    for (int c = lane; c < n4; c += 64) {
+        const float4 v = row[c];
+        amax = fmaxf(amax, fmaxf(fmaxf(fabsf(v.x), fabsf(v.y)), fmaxf(fabsf(v.z), fabsf(v.w))));
+    }
+#pragma unroll
+    for (int m = 32; m >= 1; m >>= 1) amax = fmaxf(amax, __shfl_xor(amax, m, 64));
+    const int ea = amax > 0.0f ? (int)((__float_as_uint(amax) >> 23) & 0xff) - 127 : 14;
+    const int sh = min(max(ea - 14, -100), 100);
+    const float inv = ldexpf(1.0f, -sh);
+    uint2 *dst = reinterpret_cast<uint2 *>(zh + (size_t)t * L);
+    for (int c = lane; c < n4; c += 64) {
+        const float4 v = row[c];
+        const uint32_t a = (uint32_t)__builtin_bit_cast(uint16_t, (_Float16)(v.x * inv)) |
+                           ((uint32_t)__builtin_bit_cast(uint16_t, (_Float16)(v.y * inv)) << 16);
+        const uint32_t b = (uint32_t)__builtin_bit_cast(uint16_t, (_Float16)(v.z * inv)) |
+                           ((uint32_t)__builtin_bit_cast(uint16_t, (_Float16)(v.w * inv)) << 16);
+        dst[c] = make_uint2(a, b);
+    }
+    if (lane == 0) zsc[t] = ldexpf(1.0f, sh);
+}
+
+constexpr int kSlotChunk = 16;  // slot rows loaded together
+
+// block (t, chunk): aggregate[t][4 c .. 4 c + 3] = sum of the token's slot
+// rows in ascending expert id (positions tok_pos, -1 = none), and the
+// chunk's sum of squares in double (fixed order: lane butterfly, then waves)
+__global__ __launch_bounds__(256) void k_latent_accum(int T, int k, int L, int nch,
+                                                      const int32_t *__restrict__ tok_pos,
+                                                      const float *__restrict__ Y,
+                                                      float *__restrict__ accL,
+                                                      double *__restrict__ ssp)
+{
+    __shared__ double red[4];
+    const int t = blockIdx.x / nch, ch = blockIdx.x % nch;
+    const int L4 = L / 4;
+    const int c = ch * 256 + threadIdx.x;
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    double ss = 0.0;
+    if (c < L4) {
+        float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
+        const int32_t *tp = tok_pos + (size_t)t * k;
+        for (int r0 = 0; r0 < k; r0 += kSlotChunk) {
+            int pp[kSlotChunk];
+#pragma unroll
+            for (int r = 0; r < kSlotChunk; r++) pp[r] = r0 + r < k ? tp[r0 + r] : -1;
+            float4 v[kSlotChunk];
+#pragma unroll
+            for (int r = 0; r < kSlotChunk; r++)
+                v[r] = pp[r] >= 0 ? reinterpret_cast<const float4 *>(Y + (size_t)pp[r] * L)[c]
+                                  : make_float4(0.f, 0.f, 0.f, 0.f);
+#pragma unroll
+            for (int r = 0; r < kSlotChunk; r++) {
+                if (pp[r] >= 0) {
+                    acc.x += v[r].x;
+                    acc.y += v[r].y;
+                    acc.z += v[r].z;
+                    acc.w += v[r].w;
+                }
+            }
+        }
+        reinterpret_cast<float4 *>(accL + (size_t)t * L)[c] = acc;
+        ss = ((double)acc.x * acc.x + (double)acc.y * acc.y) + ((double)acc.z * acc.z + (double)acc.w * acc.w);
+    }
+#pragma unroll
+    for (int m = 32; m >= 1; m >>= 1) ss += __shfl_xor(ss, m, 64);
+    if (lane == 0) red[wave] = ss;
+    __syncthreads();
+    if (threadIdx.x == 0) ssp[(size_t)t * nch + ch] = (red[0] + red[1]) + (red[2] + red[3]);
+}
+
+// 1 / sqrt(ss / L + eps) rounded to fp32, ss = the token's partial sums in
+// chunk order (k3_rmsnorm's inverse)
+__device__ __forceinline__ float rms_inv(const double *ssp, int nch, int L, float eps)
+{
+    double ss = 0.0;
+    for (int c = 0; c < nch; c++) ss += ssp[c];
+    return (float)(1.0 / sqrt(ss / (double)L + (double)eps));
+}
+
+// block (t, chunk): n = aggregate * inv * norm_w (or the aggregate), as bf16
+// hi = rne(n), lo = rne(n - hi)
+__global__ __launch_bounds__(256) void k_latent_split(int T, int L, int nch, int do_norm, float eps,
+                                                      const float *__restrict__ nw,
+                                                      const float *__restrict__ accL,
+                                                      const double *__restrict__ ssp,
+                                                      uint16_t *__restrict__ nhi,
+                                                      uint16_t *__restrict__ nlo)
+{
+    const int t = blockIdx.x / nch, ch = blockIdx.x % nch;
+    const int c = ch * 256 + threadIdx.x;
+    if (c >= L / 4) return;
+    const float inv = do_norm ? rms_inv(ssp + (size_t)t * nch, nch, L, eps) : 1.0f;
+    const float4 a = reinterpret_cast<const float4 *>(accL + (size_t)t * L)[c];
+    const float v[4] = {a.x, a.y, a.z, a.w};
+    uint16_t h[4], l[4];
+#pragma unroll
+    for (int j = 0; j < 4; j++) {
+        const float n = do_norm ? v[j] * inv * (nw ? nw[4 * c + j] : 1.0f) : v[j];
+        h[j] = f32_to_bf16_rne(n);
+        l[j] = f32_to_bf16_rne(n - __uint_as_float((uint32_t)h[j] << 16));
+    }
+    reinterpret_cast<uint2 *>(nhi + (size_t)t * L)[c] =
+        make_uint2((uint32_t)h[0] | ((uint32_t)h[1] << 16), (uint32_t)h[2] | ((uint32_t)h[3] << 16));
+    reinterpret_cast<uint2 *>(nlo + (size_t)t * L)[c] =
+        make_uint2((uint32_t)l[0] | ((uint32_t)l[1] << 16), (uint32_t)l[2] | ((uint32_t)l[3] << 16));
+}
+
+constexpr int kOutRowsPerWave = 2;
+constexpr int kOutRows = 4 * kOutRowsPerWave;  // output rows per block
+constexpr int kOutMaxTok = 4;                  // tokens staged in LDS at once
+constexpr int kOutBatch = 8;                   // weight pieces per lane loaded together per row
+
+struct OutParams {
+    int T, H, L, F, S, do_norm, nch, ntok;
+    float eps;
+    const float *accL;    // [T][L]
+    const double *ssp;    // [T][nch]
+    const float *nw;      // [L] or null
+    const float *Hs;      // [T][S*F]
+    const uint16_t *up;   // [H][L]
+    const uint16_t *sh2;  // [S][H][F]
+    float *out_f32;
+    uint16_t *out_bf16;
+};
+
+// the wave's rows r0, r0 + 1 of one segment (weights wrow0 / wrow1, K wide)
+// dotted with the staged inputs xs + xoff of nt tokens (token stride W)
+__device__ __forceinline__ void seg_dot(const uint16_t *wrow0, const uint16_t *wrow1, bool two, int K,
+                                        const float *xs, int xoff, int W, int nt,
+                                        float (&acc)[kOutRowsPerWave][kOutMaxTok])
+{
+    const int lane = threadIdx.x & 63;
+    const int nb = K / 8;
+    for (int c0 = 0; c0 < nb; c0 += 64 * kOutBatch) {
+        uint4 w[kOutRowsPerWave][kOutBatch];
+#pragma unroll
+        for (int i = 0; i < kOutBatch; i++) {
+            const int c = c0 + lane + 64 * i;
+            w[0][i] = c < nb ? ld16(wrow0 + (size_t)c * 8) : make_uint4(0, 0, 0, 0);
+            w[1][i] = (two && c < nb) ? ld16(wrow1 + (size_t)c * 8) : make_uint4(0, 0, 0, 0);
+        }
+#pragma unroll
+        for (int i = 0; i < kOutBatch; i++) {
+            const int c = c0 + lane + 64 * i;
+            if (c < nb) {
+#pragma unroll
+                for (int tt = 0; tt < kOutMaxTok; tt++) {
+                    if (tt < nt) {
+                        const float *xv = xs + tt * W + xoff + c * 8;
+                        acc[0][tt] = bf16x8_dot_f32(w[0][i], xv, acc[0][tt]);
+                        acc[1][tt] = bf16x8_dot_f32(w[1][i], xv, acc[1][tt]);
+                    }
+                }
+            }
+        }
+    }
+}
+
+// out[t][r] = W_up[r] . n[t] + sum_s W2s[s][r] . h_s[t]: each block stages
+// up to ntok tokens' inputs (n computed from the aggregate on the way, then
+// the shared activations) in LDS; each wave then streams two output rows'
+// weights once per staged group and dots them with every staged token
+__global__ __launch_bounds__(256) void k_latent_out(OutParams p)
+{
+    extern __shared__ float4 lds4[];
+    float *xs = reinterpret_cast<float *>(lds4);
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const int r0 = blockIdx.x * kOutRows + wave * kOutRowsPerWave;
+    const int SF = p.S * p.F, W = p.L + SF;
+    for (int t0 = 0; t0 < p.T; t0 += p.ntok) {
+        const int nt = min(p.ntok, p.T - t0);
+        __syncthreads();  // the previous group's reads are done
+        for (int tt = 0; tt < nt; tt++) {
+            const int t = t0 + tt;
+            const float inv = p.do_norm ? rms_inv(p.ssp + (size_t)t * p.nch, p.nch, p.L, p.eps) : 1.0f;
+            float *dst = xs + tt * W;
+            for (int i = threadIdx.x; i < p.L; i += 256) {
+                const float a = p.accL[(size_t)t * p.L + i];
+                dst[i] = p.do_norm ? a * inv * (p.nw ? p.nw[i] : 1.0f) : a;
+            }
+            for (int i = threadIdx.x; i < SF; i += 256) dst[p.L + i] = p.Hs[(size_t)t * SF + i];
+        }
+        __syncthreads();
+        if (r0 < p.H) {
+            const bool two = r0 + 1 < p.H;
+            const int r1 = two ? r0 + 1 : r0;
+            float acc[kOutRowsPerWave][kOutMaxTok];
+#pragma unroll
+            for (int a = 0; a < kOutRowsPerWave; a++)
+#pragma unroll
+                for (int tt = 0; tt < kOutMaxTok; tt++) acc[a][tt] = 0.0f;
+            seg_dot(p.up + (size_t)r0 * p.L, p.up + (size_t)r1 * p.L, two, p.L, xs, 0, W, nt, acc);
+            for (int s = 0; s < p.S; s++)
+                seg_dot(p.sh2 + ((size_t)s * p.H + r0) * p.F, p.sh2 + ((size_t)s * p.H + r1) * p.F, two,
+                        p.F, xs, p.L + s * p.F, W, nt, acc);
+#pragma unroll
+            for (int tt = 0; tt < kOutMaxTok; tt++) {
+                if (tt < nt) {
+#pragma unroll
+                    for (int a = 0; a < kOutRowsPerWave; a++) {
+                        const float v = group_sum<64>(acc[a][tt]);
+                        const int r = r0 + a;
+                        if (lane == 0 && (a == 0 || two)) {
+                            const size_t o = (size_t)(t0 + tt) * p.H + r;
+                            if (p.out_f32) p.out_f32[o] = v;
+                            if (p.out_bf16) p.out_bf16[o] = f32_to_bf16_rne(v);
+                        }
+                    }
+                }
+            }
+        }
+    }
+}
+
+}  // namespace
+
+// LDS bytes of one staged token of k_latent_out
+static size_t out_token_bytes(int L, int S, int F) { return ((size_t)L + (size_t)S * F) * 4; }
+
+hipError_t launch_latent_front(const Shape &so, int L, const uint16_t *x, const Weights &wt,
+                               const uint16_t *down, const Work &w, const LatentBufs &b,
+                               hipStream_t st)
+{
+    FrontParams p;
+    p.T = so.T; p.E = so.E; p.H = so.d; p.L = L; p.F = so.F; p.S = so.S;
+    p.act = so.act; p.b1 = so.b1; p.b2 = so.b2;
+    p.x = x; p.Wr = wt.router_w; p.down = down; p.sh1 = wt.sh1; p.sh3 = wt.sh3;
+    p.logits = w.logits; p.zf = b.zf; p.Hs = w.Hs;
+    p.n_sh = (so.S * so.F + 3) / 4;
+    p.n_dn = (L + 3) / 4;
+    const int n_rt = (so.E + 3) / 4;
+    const int nblk = p.n_sh + p.n_dn + n_rt;
+    const int np = (so.d + 511) / 512;
+    if (np <= 1) k_latent_front<1><<<nblk, 256, 0, st>>>(p);
+    else if (np <= 2) k_latent_front<2><<<nblk, 256, 0, st>>>(p);
+    else if (np <= 4) k_latent_front<4><<<nblk, 256, 0, st>>>(p);
+    else if (np <= 8) k_latent_front<8><<<nblk, 256, 0, st>>>(p);
+    else if (np <= 14) k_latent_front<14><<<nblk, 256, 0, st>>>(p);
+    else k_latent_front<16><<<nblk, 256, 0, st>>>(p);
+    return hipGetLastError();
+}
+
+hipError_t launch_quant_z(int T, int L, const LatentBufs &b, hipStream_t st)
+{
+    if (T > 0) k_quant_z<<<(T + 3) / 4, 256, 0, st>>>(T, L, b.zf, b.zh, b.zsc);
+    return hipGetLastError();
+}
+
+hipError_t launch_latent_accum(int T, int k, int L, const Work &w, const LatentBufs &b,
+                               hipStream_t st)
+{
+    const int nch = latent_chunks(L);
+    if (T > 0) k_latent_accum<<<T * nch, 256, 0, st>>>(T, k, L, nch, w.tok_pos, w.Y, b.accL, b.ssp);
+    return hipGetLastError();
+}
+
+hipError_t launch_latent_split(int T, int L, int do_norm, float eps, const float *norm_w,
+                               const LatentBufs &b, hipStream_t st)
+{
+    const int nch = latent_chunks(L);
+    if (T > 0)
+        k_latent_split<<<T * nch, 256, 0, st>>>(T, L, nch, do_norm, eps, norm_w, b.accL, b.ssp, b.nhi,
+                                                b.nlo);
+    return hipGetLastError();
+}
+
+hipError_t launch_latent_out(const Shape &so, int L, int do_norm, float eps, const float *norm_w,
+                             const uint16_t *up, const Weights &wt, const Work &w,
+                             const LatentBufs &b, uint16_t *out_bf16, float *out_f32,
+                             hipStream_t st)
+{
+    OutParams p;
+    p.T = so.T; p.H = so.d; p.L = L; p.F = so.F; p.S = so.S;
+    p.do_norm = do_norm; p.nch = latent_chunks(L); p.eps = eps;
+    p.accL = b.accL; p.ssp = b.ssp; p.nw = norm_w; p.Hs = w.Hs;
+    p.up = up; p.sh2 = wt.sh2;
+    p.out_f32 = out_f32; p.out_bf16 = out_bf16;
+    const size_t tb = out_token_bytes(L, so.S, so.F);
+    p.ntok = (int)std::min<size_t>(std::max<size_t>((size_t)(48 << 10) / tb, 1), kOutMaxTok);
+    p.ntok = std::min(p.ntok, std::max(so.T, 1));
+    const int nblk = (so.d + kOutRows - 1) / kOutRows;
+    if (so.T > 0) k_latent_out<<<nblk, 256, p.ntok * tb, st>>>(p);
+    return hipGetLastError();
+}
+
+// the largest staged token k_latent_out takes (its LDS holds one at least)
+bool latent_out_fits(int L, int S, int F) { return out_token_bytes(L, S, F) <= (size_t)(64 << 10); }
+
+}  // namespace moe

@@ -224,6 +224,200 @@ moe_status run_layer(const moe_layer_desc *d, const Shape &s, const uint16_t *x,
     return MOE_OK;
 }
 
+// ------------------------------------------------------------ latent layer
+
+constexpr int32_t kMaxHidden = 8192;  // the front kernel's row registers (16 pieces per lane)
+
+moe_status check_latent_desc(const moe_latent_desc *d)
+{
+    if (!d) return MOE_EINVAL;
+    if (d->n_experts < 1 || d->top_k < 1 || d->top_k > d->n_experts) return MOE_EINVAL;
+    if (d->hidden < 32 || d->hidden % 32 || d->latent < 32 || d->latent % 32 || d->d_ffn < 32 ||
+        d->d_ffn % 32)
+        return MOE_EINVAL;
+    if (d->n_shared < 0) return MOE_EINVAL;
+    if (d->act != MOE_ACT_SITU && d->act != MOE_ACT_SWIGLU) return MOE_EINVAL;
+    if (d->path != MOE_PATH_AUTO && d->path != MOE_PATH_GEMV && d->path != MOE_PATH_MFMA)
+        return MOE_EINVAL;
+    if (d->renorm != 0 && d->renorm != 1) return MOE_EINVAL;
+    if (d->latent_norm != 0 && d->latent_norm != 1) return MOE_EINVAL;
+    if (!isfinite(d->routed_scale)) return MOE_EINVAL;
+    if (!(isfinite(d->rms_eps) && d->rms_eps >= 0.0f)) return MOE_EINVAL;
+    if (d->act == MOE_ACT_SITU &&
+        !(isfinite(d->situ_b1) && isfinite(d->situ_b2) && d->situ_b1 > 0 && d->situ_b2 > 0))
+        return MOE_EINVAL;
+    if (!d->router_w || !d->down || !d->up || !d->w1_q || !d->w1_s || !d->w3_q || !d->w3_s ||
+        !d->w2_q || !d->w2_s)
+        return MOE_EINVAL;
+    if (d->n_shared > 0 && (!d->sh_w1 || !d->sh_w3 || !d->sh_w2)) return MOE_EINVAL;
+    if (!aligned(d->router_w, 16) || !aligned(d->down, 16) || !aligned(d->up, 16) ||
+        !aligned(d->w1_q, 16) || !aligned(d->w3_q, 16) || !aligned(d->w2_q, 16))
+        return MOE_EINVAL;
+    if (d->norm_w && !aligned(d->norm_w, 4)) return MOE_EINVAL;
+    if (d->n_shared > 0 && (!aligned(d->sh_w1, 16) || !aligned(d->sh_w3, 16) || !aligned(d->sh_w2, 16)))
+        return MOE_EINVAL;
+    if (d->n_experts > moe::kMaxExperts || d->top_k > moe::kMaxTopK || d->hidden > kMaxHidden ||
+        d->latent > moe::kMaxDim || d->d_ffn > moe::kMaxDim || d->n_shared > moe::kMaxShared ||
+        !moe::latent_out_fits(d->latent, d->n_shared, d->d_ffn))
+        return MOE_EUNSUPPORTED;
+    return MOE_OK;
+}
+
+// full-width shape (router, shared experts: d = hidden) and the routed
+// experts' shape (d = latent, no shared experts)
+Shape latent_outer(const moe_latent_desc *d, int32_t T)
+{
+    Shape s;
+    s.T = T;
+    s.E = d->n_experts;
+    s.k = d->top_k;
+    s.d = d->hidden;
+    s.F = d->d_ffn;
+    s.S = d->n_shared;
+    s.act = d->act;
+    s.b1 = d->situ_b1;
+    s.b2 = d->situ_b2;
+    s.renorm = d->renorm;
+    s.routed_scale = d->routed_scale;
+    return s;
+}
+
+Shape latent_inner(const moe_latent_desc *d, int32_t T)
+{
+    Shape s = latent_outer(d, T);
+    s.d = d->latent;
+    s.S = 0;
+    return s;
+}
+
+bool latent_mfma_supported(const moe_latent_desc *d, int32_t T)
+{
+    return moe::mfma_supported(latent_outer(d, T)) && moe::mfma_supported(latent_inner(d, T));
+}
+
+int latent_path(const moe_latent_desc *d, int32_t T)
+{
+    if (d->path == MOE_PATH_GEMV || d->path == MOE_PATH_MFMA) return d->path;
+    return (T > kGemvMaxTokens && latent_mfma_supported(d, T)) ? MOE_PATH_MFMA : MOE_PATH_GEMV;
+}
+
+size_t carve_latent(const moe_latent_desc *d, int32_t T, char *base, Work *w, moe::LatentBufs *lb)
+{
+    const Shape so = latent_outer(d, T), si = latent_inner(d, T);
+    size_t off = 0;
+    auto take = [&](size_t bytes) -> char * {
+        char *p = base ? base + off : nullptr;
+        off += (bytes + 255) & ~(size_t)255;
+        return p;
+    };
+    const size_t Tz = (size_t)T, E = (size_t)so.E, k = (size_t)so.k, F = (size_t)so.F;
+    const size_t S = (size_t)so.S, H = (size_t)so.d, L = (size_t)si.d;
+    const size_t nblk = (Tz + moe::kDispatchTokens - 1) / moe::kDispatchTokens;
+    Work v = {};
+    v.logits = (float *)take(Tz * E * 4);
+    v.ids = (int32_t *)take(Tz * k * 4);
+    v.wts = (float *)take(Tz * k * 4);
+    v.counts = (int32_t *)take(E * 4);
+    v.offsets = (int32_t *)take((E + 1) * 4);
+    v.active = (int32_t *)take(E * 4);
+    v.meta = (int32_t *)take(16);
+    v.masks = (uint64_t *)take(nblk * E * 8);
+    v.blk_base = (int32_t *)take(nblk * E * 4);
+    v.pos_tok = (int32_t *)take(Tz * k * 4);
+    v.pos_w = (float *)take(Tz * k * 4);
+    v.tok_pos = (int32_t *)take(Tz * k * 4);
+    v.H = (void *)take(Tz * k * F * 4);
+    v.Hs = (float *)take(Tz * S * F * 4);
+    v.Y = (float *)take(Tz * k * L * 4);
+    v.extra = (void *)take(moe::mfma_extra_workspace(so));
+    Shape sd = so;  // the down projection as a router-mode GEMM: E = latent rows
+    sd.E = (int)L;
+    v.rpart = (float *)take(std::max(moe::router_part_workspace(so, 3), moe::router_part_workspace(sd, 1)));
+    moe::LatentBufs b;
+    b.zf = (float *)take(Tz * L * 4);
+    b.zh = (uint16_t *)take(Tz * L * 2);
+    b.zsc = (float *)take(Tz * 4);
+    b.accL = (float *)take(Tz * L * 4);
+    b.ssp = (double *)take(Tz * moe::latent_chunks((int)L) * 8);
+    b.nhi = (uint16_t *)take(Tz * L * 2);
+    b.nlo = (uint16_t *)take(Tz * L * 2);
+    b.ysh = (float *)take((S + 1) * Tz * H * 4);
+    if (w) *w = v;
+    if (lb) *lb = b;
+    return off;
+}
+
+moe_status check_latent_call(const moe_latent_desc *d, const uint16_t *x, int32_t T, void *ws,
+                             size_t ws_bytes)
+{
+    const moe_status st = check_latent_desc(d);
+    if (st != MOE_OK) return st;
+    if (T < 0) return MOE_EINVAL;
+    if (T > kMaxTokens) return MOE_EUNSUPPORTED;
+    if (T == 0) return MOE_OK;
+    if (!x || !aligned(x, 16)) return MOE_EINVAL;
+    if (!ws || !aligned(ws, 256)) return MOE_EINVAL;
+    if (latent_path(d, T) == MOE_PATH_MFMA && !latent_mfma_supported(d, T)) return MOE_EUNSUPPORTED;
+    if (ws_bytes < carve_latent(d, T, nullptr, nullptr, nullptr)) return MOE_EWORKSPACE;
+    return MOE_OK;
+}
+
+// route (full width) -> z -> experts in the latent -> aggregate -> norm ->
+// up projection + shared experts; ev (optional, 6 events) marks the phases
+moe_status run_latent(const moe_latent_desc *d, int32_t T, const uint16_t *x, int32_t *ids,
+                      float *wts, int32_t *counts_out, const Work &w, const moe::LatentBufs &b,
+                      int32_t out_mode, uint16_t *out_bf16, float *out_f32, hipStream_t st,
+                      hipEvent_t const *ev)
+{
+    const Shape so = latent_outer(d, T), si = latent_inner(d, T);
+    const int L = d->latent;
+    const int path = latent_path(d, T);
+    moe::Weights wt;
+    wt.router_w = d->router_w;
+    wt.router_bias = d->router_bias;
+    wt.w1q = d->w1_q; wt.w1s = d->w1_s; wt.w3q = d->w3_q; wt.w3s = d->w3_s;
+    wt.w2q = d->w2_q; wt.w2s = d->w2_s;
+    wt.sh1 = d->sh_w1; wt.sh3 = d->sh_w3; wt.sh2 = d->sh_w2;
+    uint16_t *ob = out_mode != MOE_OUT_F32 ? out_bf16 : nullptr;
+    float *of = out_mode != MOE_OUT_BF16 ? out_f32 : nullptr;
+    MOE_TRY(mark(ev, 0, st));
+    if (path == MOE_PATH_GEMV) {
+        MOE_TRY(moe::launch_latent_front(so, L, x, wt, d->down, w, b, st));
+    } else {
+        MOE_TRY(moe::launch_mfma_router(so, x, wt, w, st));
+        Shape sd = so;
+        sd.E = L;
+        MOE_TRY(moe::launch_mfma_linear(sd, x, d->down, b.zf, w, st));
+        MOE_TRY(moe::launch_mfma_shared_gateup(so, x, wt, w, st));
+    }
+    MOE_TRY(mark(ev, 1, st));
+    MOE_TRY(moe::launch_dispatch(si, 1, w.logits, d->router_bias, ids, wts, counts_out, w, st));
+    MOE_TRY(moe::launch_quant_z(T, L, b, st));
+    MOE_TRY(mark(ev, 2, st));
+    if (path == MOE_PATH_GEMV) {
+        MOE_TRY(moe::launch_gemv_experts(si, nullptr, wt, 0, w, st, ev ? ev + 3 : nullptr, b.zh, b.zsc));
+    } else {
+        MOE_TRY(moe::launch_mfma_latent_experts(si, wt, b.zh, b.zsc, w, st, ev ? ev + 3 : nullptr));
+    }
+    MOE_TRY(moe::launch_latent_accum(T, so.k, L, w, b, st));
+    if (path == MOE_PATH_GEMV) {
+        MOE_TRY(moe::launch_latent_out(so, L, d->latent_norm, d->rms_eps, d->norm_w, d->up, wt, w, b,
+                                       ob, of, st));
+    } else {
+        MOE_TRY(moe::launch_latent_split(T, L, d->latent_norm, d->rms_eps, d->norm_w, b, st));
+        MOE_TRY(moe::launch_mfma_up_shared(so, L, d->up, b.nhi, b.nlo, wt, w, b.ysh, st));
+        // out = slot 0 (W_up n) + slots 1 .. S (shared), in that order
+        Shape sc = so;
+        sc.k = 0;
+        sc.S = so.S + 1;
+        Work wc = w;
+        wc.Ysh = b.ysh;
+        MOE_TRY(moe::launch_combine(sc, 1, wc, ob, of, st));
+    }
+    MOE_TRY(mark(ev, 5, st));
+    return MOE_OK;
+}
+
 constexpr int kMaxDevices = 64;
 std::atomic<void *> g_scratch_dev[kMaxDevices];
 
@@ -351,6 +545,55 @@ moe_status moe_set_one_token_router_wait(int32_t microseconds)
     if (microseconds < 0) return MOE_EINVAL;
     moe::set_router_wait_us((uint32_t)microseconds);
     return MOE_OK;
+}
+
+size_t moe_latent_workspace_bytes(const moe_latent_desc *desc, int32_t max_tokens)
+{
+    if (check_latent_desc(desc) != MOE_OK || max_tokens < 0 || max_tokens > kMaxTokens) return 0;
+    return carve_latent(desc, max_tokens < 1 ? 1 : max_tokens, nullptr, nullptr, nullptr);
+}
+
+int32_t moe_latent_path_for(const moe_latent_desc *desc, int32_t T)
+{
+    const moe_status st = check_latent_desc(desc);
+    if (st != MOE_OK) return st;
+    return latent_path(desc, T);
+}
+
+moe_status moe_latent_layer(const moe_latent_desc *desc, const uint16_t *x, int32_t T,
+                            uint16_t *out_bf16, float *out_f32, int32_t out_mode, int32_t *ids_opt,
+                            float *weights_opt, int32_t *counts_opt, void *ws, size_t ws_bytes,
+                            void *stream)
+{
+    moe_status st = check_latent_call(desc, x, T, ws, ws_bytes);
+    if (st != MOE_OK) return st;
+    st = check_out(out_mode, out_bf16, out_f32);
+    if (st != MOE_OK || T == 0) return st;
+    (void)hipGetLastError();
+    Work w;
+    moe::LatentBufs b;
+    carve_latent(desc, T, (char *)ws, &w, &b);
+    return run_latent(desc, T, x, ids_opt ? ids_opt : w.ids, weights_opt ? weights_opt : w.wts,
+                      counts_opt, w, b, out_mode, out_bf16, out_f32, (hipStream_t)stream, nullptr);
+}
+
+moe_status moe_latent_layer_timed(const moe_latent_desc *desc, const uint16_t *x, int32_t T,
+                                  uint16_t *out_bf16, float *out_f32, int32_t out_mode, void *ws,
+                                  size_t ws_bytes, void *stream, void *const *events)
+{
+    moe_status st = check_latent_call(desc, x, T, ws, ws_bytes);
+    if (st != MOE_OK) return st;
+    st = check_out(out_mode, out_bf16, out_f32);
+    if (st != MOE_OK || T == 0) return st;
+    if (!events) return MOE_EINVAL;
+    for (int i = 0; i < MOE_TIMED_EVENTS; i++)
+        if (!events[i]) return MOE_EINVAL;
+    (void)hipGetLastError();
+    Work w;
+    moe::LatentBufs b;
+    carve_latent(desc, T, (char *)ws, &w, &b);
+    return run_latent(desc, T, x, w.ids, w.wts, nullptr, w, b, out_mode, out_bf16, out_f32,
+                      (hipStream_t)stream, reinterpret_cast<hipEvent_t const *>(events));
 }
 
 const char *moe_status_str(int32_t status)

@@ -94,8 +94,9 @@ __device__ __forceinline__ void topk_regs(int E, int k, const float *__restrict_
 }
 
 // One wave: logits of router row e for tokens [0, T) of x.  The row (d fp32,
-// d <= 4096) is loaded once into registers (16 float4 per lane at most) and
+// d <= 256 NC) is loaded once into registers (NC float4 per lane at most) and
 // reused for every token; x is read through the cache, 8 tokens at a time.
+template <int NC = 16>
 __device__ __forceinline__ void router_row(int T, int E, int d, const uint16_t *__restrict__ x,
                                            const float *__restrict__ Wr, float *__restrict__ logits,
                                            int e)
@@ -104,9 +105,9 @@ __device__ __forceinline__ void router_row(int T, int E, int d, const uint16_t *
     const int lane = threadIdx.x & 63;
     const int nc = d / 4;
     const float4 *row = reinterpret_cast<const float4 *>(Wr + (size_t)e * d);
-    float4 w[16];
+    float4 w[NC];
 #pragma unroll
-    for (int i = 0; i < 16; i++) {
+    for (int i = 0; i < NC; i++) {
         const int c = lane + 64 * i;
         w[i] = c < nc ? row[c] : make_float4(0.f, 0.f, 0.f, 0.f);
     }
@@ -116,7 +117,7 @@ __device__ __forceinline__ void router_row(int T, int E, int d, const uint16_t *
 #pragma unroll
         for (int t = 0; t < TT; t++) acc[t] = 0.0f;
 #pragma unroll
-        for (int i = 0; i < 16; i++) {
+        for (int i = 0; i < NC; i++) {
             const int c = lane + 64 * i;
             if (c < nc) {
 #pragma unroll

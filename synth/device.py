@@ -22,9 +22,12 @@ def _pinned(nbytes: int) -> torch.Tensor:
 
 def upload_layer(shape: synth.LayerShape, seed: int, layer: int, zipf: bool = False,
                  device: str = "cuda", chunk_bytes: int = 512 << 20,
-                 shared_host: Optional[tuple] = None) -> dict:
+                 shared_host: Optional[tuple] = None,
+                 outer: Optional[synth.LayerShape] = None) -> dict:
     """Device tensors keyed as the layer descriptor's fields (uint8 for MXFP4,
-    int16 holding bf16 bits, float32)."""
+    int16 holding bf16 bits, float32).  ``outer`` (default ``shape``) is the
+    shape of the router and the shared experts."""
+    outer = shape if outer is None else outer
     E = shape.n_experts
     out = {}
     for which in _NAMES:
@@ -44,10 +47,10 @@ def upload_layer(shape: synth.LayerShape, seed: int, layer: int, zipf: bool = Fa
             s[e0:e0 + ne].copy_(hs[: ne * sb].view(ne, rows, cols // 32))
         torch.cuda.synchronize()
         out[which + "_q"], out[which + "_s"] = q, s
-    sh = shared_host if shared_host is not None else synth.shared_weights(shape, seed, layer)
+    sh = shared_host if shared_host is not None else synth.shared_weights(outer, seed, layer)
     for name, a in zip(("sh_w1", "sh_w3", "sh_w2"), sh):
         out[name] = torch.from_numpy(a.view(np.int16)).to(device)
-    out["router_w"] = torch.from_numpy(synth.router_weight(shape, seed, layer)).to(device)
+    out["router_w"] = torch.from_numpy(synth.router_weight(outer, seed, layer)).to(device)
     out["router_bias"] = torch.from_numpy(synth.zipf_bias(shape, seed)).to(device) if zipf else None
     return out
 
@@ -66,3 +69,24 @@ def host_to_device(h: "synth.HostLayer", device: str = "cuda") -> dict:
 
 def tokens_to_device(x_bits: np.ndarray, device: str = "cuda") -> torch.Tensor:
     return torch.from_numpy(np.ascontiguousarray(x_bits).view(np.int16)).to(device)
+
+
+def upload_latent_layer(shape: "synth.LatentShape", seed: int, layer: int, zipf: bool = False,
+                        device: str = "cuda") -> dict:
+    """Device tensors of a latent layer, keyed as moe_latent_desc's fields."""
+    out = upload_layer(shape.inner, seed, layer, zipf=zipf, device=device, outer=shape.outer)
+    down, up, nw = synth.latent_projections(shape, seed, layer)
+    out["down"] = torch.from_numpy(down.view(np.int16)).to(device)
+    out["up"] = torch.from_numpy(up.view(np.int16)).to(device)
+    out["norm_w"] = torch.from_numpy(nw).to(device)
+    return out
+
+
+def latent_host_to_device(h: "synth.HostLatentLayer", device: str = "cuda") -> dict:
+    """Device copy of a HostLatentLayer that holds every expert."""
+    out = host_to_device(h.core, device)
+    t = lambda a: torch.from_numpy(np.ascontiguousarray(a)).to(device)
+    out["down"] = t(h.down.view(np.int16))
+    out["up"] = t(h.up.view(np.int16))
+    out["norm_w"] = t(h.norm_w)
+    return out

@@ -144,3 +144,93 @@ def check_routing(ids_gpu, w_gpu, cnt_gpu, ids_ref, w_ref, E, what=""):
     wg = np.take_along_axis(w_gpu, og, axis=1)
     wr = np.take_along_axis(w_ref, orf, axis=1)
     np.testing.assert_allclose(wg, wr, rtol=1e-5, atol=1e-7)
+
+
+# ------------------------------------------------------------------ latent layer
+
+@dataclass
+class GpuLatent:
+    shape: "synth.LatentShape"
+    seed: int
+    layer: int
+    zipf: bool
+    tensors: dict
+    desc: object
+    host: Optional["synth.HostLatentLayer"] = None  # small shapes: every tensor on the host too
+
+
+def make_gpu_latent(shape, seed: int, layer: int = 0, zipf: bool = False, act: int = 0,
+                    path: int = 0, host=None, latent_norm: int = 1, norm_w: bool = True,
+                    small: Optional[bool] = None) -> GpuLatent:
+    import quantized_expert_gemv_sigmoid_amd as moe
+    import synth.device as sdev
+    if small is None:
+        small = shape.n_experts * shape.inner.expert_bytes < (1 << 30)
+    if small:
+        if host is None:
+            host = synth.host_latent_layer(shape, seed, layer, zipf=zipf)
+        t = sdev.latent_host_to_device(host)
+    else:
+        t = sdev.upload_latent_layer(shape, seed, layer, zipf=zipf)
+    tt = dict(t)
+    if not norm_w:
+        tt["norm_w"] = None
+    d = moe.make_latent_desc(shape.n_experts, shape.top_k, shape.hidden, shape.latent, shape.d_ffn,
+                             shape.n_shared, tt, act=act, path=path, latent_norm=latent_norm)
+    return GpuLatent(shape, seed, layer, zipf, t, d, host)
+
+
+def latent_tokens(gl: GpuLatent, T: int, screened: bool = True, first_token: int = 0):
+    """Full-width workload tokens with the near-tie rule applied (on the
+    full-width router)."""
+    if gl.host is not None:
+        rw, bias = gl.host.core.router_w, gl.host.core.router_bias
+    else:
+        rw = synth.router_weight(gl.shape.outer, gl.seed, gl.layer)
+        bias = synth.zipf_bias(gl.shape.outer, gl.seed) if gl.zipf else None
+    if screened:
+        x, _ = oracle.screened_tokens(gl.shape.outer, gl.seed, gl.layer, T, rw, bias,
+                                      first_token=first_token)
+    else:
+        x = synth.x_tokens(gl.shape.outer, gl.seed, gl.layer, T, first_token=first_token)
+    return x, rw, bias
+
+
+def run_latent(gl: GpuLatent, x_bits: np.ndarray, out_mode: int = 2):
+    """moe_latent_layer on the GPU; returns numpy (out_f32, out_bf16, ids, weights, counts)."""
+    import torch
+    import quantized_expert_gemv_sigmoid_amd as moe
+    import synth.device as sdev
+    T, H = x_bits.shape
+    E, k = gl.shape.n_experts, gl.shape.top_k
+    x = sdev.tokens_to_device(x_bits)
+    out_f = torch.empty((T, H), dtype=torch.float32, device="cuda")
+    out_b = torch.empty((T, H), dtype=torch.int16, device="cuda")
+    ids = torch.empty((T, k), dtype=torch.int32, device="cuda")
+    w = torch.empty((T, k), dtype=torch.float32, device="cuda")
+    cnt = torch.empty(E, dtype=torch.int32, device="cuda")
+    ws = moe.latent_workspace(gl.desc, T)
+    moe.latent_layer(gl.desc, x, T, out_b if out_mode != 1 else None,
+                     out_f if out_mode != 0 else None, out_mode, ws, ids=ids, weights=w, counts=cnt)
+    torch.cuda.synchronize()
+    return (out_f.cpu().numpy(), out_b.cpu().numpy().view(np.uint16), ids.cpu().numpy(),
+            w.cpu().numpy(), cnt.cpu().numpy())
+
+
+def oracle_latent_outputs(gl: GpuLatent, x_bits: np.ndarray, rw, bias, sample: Sequence[int],
+                          act: int = 0, latent_norm: int = 1, norm_w: bool = True):
+    """Oracle ids/weights for every token and latent-layer outputs for the sampled tokens."""
+    ids, w, gap = oracle.route(x_bits, rw, bias, gl.shape.top_k)
+    sample = np.asarray(sample, dtype=np.int64)
+    need = np.unique(ids[sample])
+    if gl.host is not None:
+        h = gl.host
+        pos = {int(e): i for i, e in enumerate(h.core.experts)}
+    else:
+        h = synth.host_latent_layer(gl.shape, gl.seed, gl.layer, zipf=gl.zipf, experts=need)
+        pos = {int(e): i for i, e in enumerate(need)}
+    slot = np.vectorize(lambda e: pos[int(e)], otypes=[np.int32])(ids[sample])
+    out = oracle.latent_forward(x_bits[sample], slot, w[sample], oracle.held_arrays(h.core), h.down,
+                                h.up, h.norm_w if norm_w else None, oracle.shared_arrays(h.core),
+                                latent_norm, oracle.RMS_EPS, act)
+    return ids, w, gap, out
