@@ -299,6 +299,53 @@ __device__ __forceinline__ float bf16x8_dot_f32(const uint4 w, const float *h, f
 
 }  // namespace moe
 
+namespace moe {
+
+// The latent layer's experts read the latent z as fp16 rows, each divided by
+// a power of two 2^s that puts the row's largest |z| in [2^14, 2^15) (so the
+// rounding to fp16 cannot overflow); zsc[t] = 2^s.
+struct ZQuant {
+    const float *zf;  // [T][L] z (fp32), or null: nothing to do
+    uint16_t *zh;     // [T][L] fp16 bits
+    float *zsc;       // [T]
+    int L;
+};
+
+// one wave: token t's row
+__device__ __forceinline__ void quant_z_row(int t, const ZQuant &q)
+{
+    const int lane = threadIdx.x & 63;
+    const float4 *row = reinterpret_cast<const float4 *>(q.zf + (size_t)t * q.L);
+    const int n4 = q.L / 4;
+    float amax = 0.0f;
+#pragma unroll 8
+    for (int c = lane; c < n4; c += 64) {
+        const float4 v = row[c];
+        amax = fmaxf(amax, fmaxf(fmaxf(fabsf(v.x), fabsf(v.y)), fmaxf(fabsf(v.z), fabsf(v.w))));
+    }
+#pragma unroll
+    for (int m = 32; m >= 1; m >>= 1) amax = fmaxf(amax, __shfl_xor(amax, m, 64));
+    const int ea = amax > 0.0f ? (int)((__float_as_uint(amax) >> 23) & 0xff) - 127 : 14;
+    const int sh = min(max(ea - 14, -100), 100);
+    const float inv = ldexpf(1.0f, -sh);
+    uint2 *dst = reinterpret_cast<uint2 *>(q.zh + (size_t)t * q.L);
+#pragma unroll 8
+    for (int c = lane; c < n4; c += 64) {
+        const float4 v = row[c];
+        const uint32_t a = (uint32_t)__builtin_bit_cast(uint16_t, (_Float16)(v.x * inv)) |
+                           ((uint32_t)__builtin_bit_cast(uint16_t, (_Float16)(v.y * inv)) << 16);
+        const uint32_t b = (uint32_t)__builtin_bit_cast(uint16_t, (_Float16)(v.z * inv)) |
+                           ((uint32_t)__builtin_bit_cast(uint16_t, (_Float16)(v.w * inv)) << 16);
+        dst[c] = make_uint2(a, b);
+    }
+    if (lane == 0) q.zsc[t] = ldexpf(1.0f, sh);
+}
+
+// one wave per token row
+__global__ __launch_bounds__(256) void k_quant_z(int T, ZQuant q);
+
+}  // namespace moe
+
 // ------------------------------------------------------------ host launchers
 // Each returns hipGetLastError() after enqueueing on `stream`.
 
@@ -317,10 +364,11 @@ hipError_t launch_front(const Shape &s, const uint16_t *x, const Weights &wt, in
                         int include_shared, const Work &w, hipStream_t stream);
 
 // top-k + renormalised weights (do_topk), then histogram / scan / stable
-// permutation of the slots; do_topk = 0 takes ids/wts as given.
+// permutation of the slots; do_topk = 0 takes ids/wts as given.  zq
+// (optional, the latent layer): also the fp16 latent rows.
 hipError_t launch_dispatch(const Shape &s, int do_topk, const float *logits, const float *bias,
                            int32_t *ids, float *wts, int32_t *counts_out, const Work &w,
-                           hipStream_t stream);
+                           hipStream_t stream, const ZQuant &zq = ZQuant{nullptr, nullptr, nullptr, 0});
 
 // dequant-fused GEMV experts: shared down + routed gate/up + activation, then
 // routed down + weight.  ev2 (optional): events recorded after each launch.
@@ -379,8 +427,6 @@ inline int latent_chunks(int L) { return (L + kLatentChunk - 1) / kLatentChunk; 
 hipError_t launch_latent_front(const Shape &so, int L, const uint16_t *x, const Weights &wt,
                                const uint16_t *down, const Work &w, const LatentBufs &b,
                                hipStream_t st);
-// z -> fp16 rows with a power-of-two scale per token
-hipError_t launch_quant_z(int T, int L, const LatentBufs &b, hipStream_t st);
 // aggregate of each token's slot rows (ascending expert id) + partial sums of squares
 hipError_t launch_latent_accum(int T, int k, int L, const Work &w, const LatentBufs &b,
                                hipStream_t st);

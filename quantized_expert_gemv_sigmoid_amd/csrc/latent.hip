@@ -17,12 +17,13 @@
 // Kernels of the small-T (GEMV) path:
 //   k_latent_front  router rows, down-projection rows and the shared
 //                   experts' gate/up pairs (all reading x), one launch
-//   k_quant_z       z -> fp16 rows + per-token scale
+//   (the dispatch block's idle waves turn z into fp16 rows + a per-token
+//   scale meanwhile; k_quant_z for larger T)
 //   k_latent_accum  the aggregate per token (fixed ascending-id order) and
 //                   partial sums of squares per 1024-element chunk
 //   k_latent_out    RMSNorm on the fly while staging the token's inputs in
 //                   LDS, then W_up n + sum_s W2s h_s per output row
-// The MFMA path shares k_quant_z and k_latent_accum and adds k_latent_split
+// The MFMA path shares k_latent_accum and adds k_latent_split
 // (the normed aggregate as bf16 hi / lo parts for the up projection GEMM).
 #include <algorithm>
 
@@ -120,38 +121,6 @@ __global__ __launch_bounds__(256) void k_latent_front(FrontParams p)
     b -= p.n_dn;
     const int e = b * 4 + wave;
     if (e < p.E) router_row<2 * NP>(p.T, p.E, p.H, p.x, p.Wr, p.logits, e);
-}
-
-// one wave per token: largest |z| -> scale 2^s with max |z| / 2^s in
-// [2^14, 2^15) (below the fp16 maximum after rounding), zh = rne_fp16(z / 2^s)
-__global__ __launch_bounds__(256) void k_quant_z(int T, int L, const float *__restrict__ zf,
-                                                 uint16_t *__restrict__ zh, float *__restrict__ zsc)
-{
-    const int t = blockIdx.x * 4 + (threadIdx.x >> 6);
-    if (t >= T) return;
-    const int lane = threadIdx.x & 63;
-    const float4 *row = reinterpret_cast<const float4 *>(zf + (size_t)t * L);
-    const int n4 = L / 4;
-    float amax = 0.0f;
-    for (int c = lane; c < n4; c += 64) {
-        const float4 v = row[c];
-        amax = fmaxf(amax, fmaxf(fmaxf(fabsf(v.x), fabsf(v.y)), fmaxf(fabsf(v.z), fabsf(v.w))));
-    }
-#pragma unroll
-    for (int m = 32; m >= 1; m >>= 1) amax = fmaxf(amax, __shfl_xor(amax, m, 64));
-    const int ea = amax > 0.0f ? (int)((__float_as_uint(amax) >> 23) & 0xff) - 127 : 14;
-    const int sh = min(max(ea - 14, -100), 100);
-    const float inv = ldexpf(1.0f, -sh);
-    uint2 *dst = reinterpret_cast<uint2 *>(zh + (size_t)t * L);
-    for (int c = lane; c < n4; c += 64) {
-        const float4 v = row[c];
-        const uint32_t a = (uint32_t)__builtin_bit_cast(uint16_t, (_Float16)(v.x * inv)) |
-                           ((uint32_t)__builtin_bit_cast(uint16_t, (_Float16)(v.y * inv)) << 16);
-        const uint32_t b = (uint32_t)__builtin_bit_cast(uint16_t, (_Float16)(v.z * inv)) |
-                           ((uint32_t)__builtin_bit_cast(uint16_t, (_Float16)(v.w * inv)) << 16);
-        dst[c] = make_uint2(a, b);
-    }
-    if (lane == 0) zsc[t] = ldexpf(1.0f, sh);
 }
 
 constexpr int kSlotChunk = 16;  // slot rows loaded together
@@ -349,6 +318,12 @@ __global__ __launch_bounds__(256) void k_latent_out(OutParams p)
 
 }  // namespace
 
+__global__ __launch_bounds__(256) void k_quant_z(int T, ZQuant q)
+{
+    const int t = blockIdx.x * 4 + (threadIdx.x >> 6);
+    if (t < T) quant_z_row(t, q);
+}
+
 // LDS bytes of one staged token of k_latent_out
 static size_t out_token_bytes(int L, int S, int F) { return ((size_t)L + (size_t)S * F) * 4; }
 
@@ -372,12 +347,6 @@ hipError_t launch_latent_front(const Shape &so, int L, const uint16_t *x, const 
     else if (np <= 8) k_latent_front<8><<<nblk, 256, 0, st>>>(p);
     else if (np <= 14) k_latent_front<14><<<nblk, 256, 0, st>>>(p);
     else k_latent_front<16><<<nblk, 256, 0, st>>>(p);
-    return hipGetLastError();
-}
-
-hipError_t launch_quant_z(int T, int L, const LatentBufs &b, hipStream_t st)
-{
-    if (T > 0) k_quant_z<<<(T + 3) / 4, 256, 0, st>>>(T, L, b.zf, b.zh, b.zsc);
     return hipGetLastError();
 }
 

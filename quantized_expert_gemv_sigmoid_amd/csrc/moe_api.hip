@@ -391,8 +391,8 @@ moe_status run_latent(const moe_latent_desc *d, int32_t T, const uint16_t *x, in
         MOE_TRY(moe::launch_mfma_shared_gateup(so, x, wt, w, st));
     }
     MOE_TRY(mark(ev, 1, st));
-    MOE_TRY(moe::launch_dispatch(si, 1, w.logits, d->router_bias, ids, wts, counts_out, w, st));
-    MOE_TRY(moe::launch_quant_z(T, L, b, st));
+    const moe::ZQuant zq{b.zf, b.zh, b.zsc, L};
+    MOE_TRY(moe::launch_dispatch(si, 1, w.logits, d->router_bias, ids, wts, counts_out, w, st, zq));
     MOE_TRY(mark(ev, 2, st));
     if (path == MOE_PATH_GEMV) {
         MOE_TRY(moe::launch_gemv_experts(si, nullptr, wt, 0, w, st, ev ? ev + 3 : nullptr, b.zh, b.zsc));

@@ -143,26 +143,42 @@ __device__ __forceinline__ void write_tok_pos(int t, int slot_j, int E, int k,
     tok_pos[(size_t)t * k + r] = me_leads ? pos : -1;
 }
 
-// T <= 64 and T*k < 65536: one block of 1024 threads does top-k (optional),
-// the bitmaps, the counts/offsets scan and the scatter.
+// T <= 64 (so T*k <= 4096): one block of 1024 threads does top-k
+// (optional), the bitmaps, the counts/offsets scan and the scatter, with the
+// routing rows staged in LDS (the per-slot loops over a token's row then read
+// LDS, not a chain of global loads).  zq (optional, the latent layer): the
+// idle waves (the last ones first) turn the tokens' latent rows into fp16
+// rows with a scale meanwhile.
 template <int EPL>
 __global__ __launch_bounds__(1024) void k_dispatch_small(
     Shape s, int do_topk, const float *__restrict__ logits, const float *__restrict__ bias,
-    int32_t *__restrict__ ids, float *__restrict__ wts, int32_t *__restrict__ counts_out, Work w)
+    int32_t *__restrict__ ids, float *__restrict__ wts, int32_t *__restrict__ counts_out, Work w,
+    ZQuant zq)
 {
     __shared__ unsigned long long masks[kMaxExperts];
     __shared__ int offs[kMaxExperts];
     __shared__ int tmp16[16];
+    __shared__ int32_t s_ids[kDispatchTokens * kMaxTopK];
+    __shared__ float s_wts[kDispatchTokens * kMaxTopK];
     const int T = s.T, E = s.E, k = s.k;
+    const int wave = threadIdx.x >> 6;
     if (do_topk) {
-        for (int t = threadIdx.x >> 6; t < T; t += 16)
+        for (int t = wave; t < T; t += 16)
             topk_wave<EPL>(E, k, logits + (size_t)t * E, bias, s.renorm, s.routed_scale,
                            ids + (size_t)t * k, wts + (size_t)t * k);
+    }
+    if (zq.zf) {
+        for (int t = 15 - wave; t < T; t += 16) quant_z_row(t, zq);
     }
     for (int e = threadIdx.x; e < E; e += 1024) masks[e] = 0ull;
     __syncthreads();  // also publishes the top-k results to the block
     for (int sl = threadIdx.x; sl < T * k; sl += 1024) {
-        const int e = ids[sl];
+        s_ids[sl] = ids[sl];
+        s_wts[sl] = wts[sl];
+    }
+    __syncthreads();
+    for (int sl = threadIdx.x; sl < T * k; sl += 1024) {
+        const int e = s_ids[sl];
         if (valid_id(e, E)) atomicOr(&masks[e], 1ull << (sl / k));
     }
     __syncthreads();
@@ -173,13 +189,13 @@ __global__ __launch_bounds__(1024) void k_dispatch_small(
     __syncthreads();
     for (int sl = threadIdx.x; sl < T * k; sl += 1024) {
         const int t = sl / k, j = sl % k;
-        const int32_t *row = ids + (size_t)t * k;
+        const int32_t *row = s_ids + t * k;
         const int ee = row[j];
         int p = -1;
         if (leads(row, j, E)) {
             p = offs[ee] + __popcll(masks[ee] & ((1ull << t) - 1ull));
             w.pos_tok[p] = t;
-            w.pos_w[p] = merged_weight(row, wts + (size_t)t * k, j, k);
+            w.pos_w[p] = merged_weight(row, s_wts + t * k, j, k);
         }
         write_tok_pos(t, j, E, k, row, p, w.tok_pos);
     }
@@ -263,9 +279,9 @@ static void launch_topk(const Shape &s, const float *logits, const float *bias, 
 template <int EPL>
 static void launch_small(const Shape &s, int do_topk, const float *logits, const float *bias,
                          int32_t *ids, float *wts, int32_t *counts_out, const Work &w,
-                         hipStream_t stream)
+                         hipStream_t stream, const ZQuant &zq)
 {
-    k_dispatch_small<EPL><<<1, 1024, 0, stream>>>(s, do_topk, logits, bias, ids, wts, counts_out, w);
+    k_dispatch_small<EPL><<<1, 1024, 0, stream>>>(s, do_topk, logits, bias, ids, wts, counts_out, w, zq);
 }
 
 #define MOE_EPL_SWITCH(epl, CALL)       \
@@ -279,11 +295,11 @@ static void launch_small(const Shape &s, int do_topk, const float *logits, const
 
 hipError_t launch_dispatch(const Shape &s, int do_topk, const float *logits, const float *bias,
                            int32_t *ids, float *wts, int32_t *counts_out, const Work &w,
-                           hipStream_t stream)
+                           hipStream_t stream, const ZQuant &zq)
 {
     const int epl = (s.E + 63) / 64;
-    if (s.T <= kDispatchTokens && s.T * s.k < 65536 && s.T <= 16) {
-#define CALL_SMALL(N) launch_small<N>(s, do_topk, logits, bias, ids, wts, counts_out, w, stream)
+    if (s.T <= kDispatchTokens && s.T <= 16) {
+#define CALL_SMALL(N) launch_small<N>(s, do_topk, logits, bias, ids, wts, counts_out, w, stream, zq)
         MOE_EPL_SWITCH(epl, CALL_SMALL);
 #undef CALL_SMALL
         return hipGetLastError();
@@ -293,12 +309,13 @@ hipError_t launch_dispatch(const Shape &s, int do_topk, const float *logits, con
         MOE_EPL_SWITCH(epl, CALL_TOPK);
 #undef CALL_TOPK
     }
-    if (s.T <= kDispatchTokens && s.T * s.k < 65536) {
-#define CALL_SMALL0(N) launch_small<N>(s, 0, logits, bias, ids, wts, counts_out, w, stream)
+    if (s.T <= kDispatchTokens) {
+#define CALL_SMALL0(N) launch_small<N>(s, 0, logits, bias, ids, wts, counts_out, w, stream, zq)
         MOE_EPL_SWITCH(epl, CALL_SMALL0);
 #undef CALL_SMALL0
         return hipGetLastError();
     }
+    if (zq.zf) k_quant_z<<<(s.T + 3) / 4, 256, 0, stream>>>(s.T, zq);
     const int nblk = (s.T + kDispatchTokens - 1) / kDispatchTokens;
     k_dispatch_masks<<<nblk, 256, 0, stream>>>(s, ids, w);
     k_dispatch_scan<<<1, 1024, 0, stream>>>(s, nblk, counts_out, w);
