@@ -20,8 +20,14 @@ Prints one JSON line:
   the HIP events of moe_layer_timed on the launch stream) and the CPU oracle
   timed on a bounded sample of the same workload on this host;
 - ``configs``: the same measurements for the other workloads (tiny, decode
-  T=64, prefill T=4096, the 12-layer stack), each layer set freed before the
-  next is loaded.
+  T=64, prefill T=4096, the 12-layer stack) and for Kimi-K3's Stable
+  LatentMoE around the routed experts (full-width router and shared
+  experts, projections into and out of the latent, RMSNorm of the
+  aggregate) at decode T=1 and prefill T=4096, each layer set freed before
+  the next is loaded.
+
+``--latent-workload N`` makes latent workload N the headline instead (with
+``--configs '' --latent-configs ''`` a single-workload run, as for profiling).
 """
 import argparse
 import hashlib
@@ -61,14 +67,35 @@ KERNELS = {
 # steps per timed window of each workload when it is measured as an entry of
 # `configs` (about 10-50 ms of GPU time per window)
 CONFIG_STEPS = {0: 200, 1: 200, 2: 20, 3: 5, 4: 20}
+LATENT_STEPS = {0: 200, 1: 200, 2: 5}
+# phases of the latent layer (Kimi-K3's Stable LatentMoE) and their kernels
+LATENT_PHASES = ("front", "topk_dispatch_z", "expert_gate_up", "expert_down", "norm_up_shared_out")
+LATENT_KERNELS = {
+    "gemv": {"front": "k_latent_front (router + down projection + shared gate/up, full width)",
+             "topk_dispatch_z": "k_dispatch_small/k_topk+k_dispatch_* + k_quant_z",
+             "expert_gate_up": "k_gemv_gateup (fp16 latent rows)", "expert_down": "k_gemv_down",
+             "norm_up_shared_out": "k_latent_accum + k_latent_out (norm, up projection, shared down)"},
+    "mfma": {"front": "k_split_router + k_ggemm<M_R> (router) + k_ggemm<M_R> (down projection) + k_ggemm<M_S13>",
+             "topk_dispatch_z": "k_topk + k_dispatch_* + k_quant_z",
+             "expert_gate_up": "k_ggemm<M_G13H>", "expert_down": "k_ggemm<M_D2>",
+             "norm_up_shared_out": "k_latent_accum + k_latent_split + k_ggemm<M_S2> (up, shared down) + k_combine"},
+}
 WINDOWS = 3
 
 # HBM bytes per dispatch measured by rocprofv3 (FETCH_SIZE and WRITE_SIZE,
 # each scaled by what the counter reads for a plain 256 MiB copy) at decode
 # T=1, with the SHA-256 prefix of the kernel's source file when the counters
 # were taken: a kernel whose source has changed since reports traffic null.
-# The summary and the commands are in profiles/moe_layer_kernels__k3-moe-decode-T1.md.
-MEASURED_TRAFFIC = {}
+# The summaries and the commands are in profiles/moe_layer_kernels__k3-moe-decode-T1.md
+# and profiles/latent_kernels__k3-latent-moe-decode-T1.md.
+MEASURED_TRAFFIC = {
+    "k_dec1_gateup": {"bytes": 289326029, "source": "decode1.hip", "sha": "570544b9dbb5dcbf"},
+    "k_dec1_down": {"bytes": 139091304, "source": "decode1.hip", "sha": "570544b9dbb5dcbf"},
+    "k_latent_front": {"bytes": 253999253, "source": "latent.hip", "sha": "bae8c0c78d423e41"},
+    "k_latent_out": {"bytes": 140118160, "source": "latent.hip", "sha": "bae8c0c78d423e41"},
+    "k_gemv_gateup": {"bytes": 187593528, "source": "gemv.hip", "sha": "f5aeda5727b5bb2d"},
+    "k_gemv_down": {"bytes": 95553957, "source": "gemv.hip", "sha": "f5aeda5727b5bb2d"},
+}
 
 
 def log(*a):
@@ -158,6 +185,191 @@ def cpu_baseline(shape, seed, zipf, pools, budget_s):
             "sample": f"{done} token-layer passes of the workload, one at a time{stack} (router over all "
                       f"{shape.n_experts} experts + {shape.top_k} routed + {shape.n_shared} "
                       f"shared expert FFNs each), {spent:.1f} s of oracle time"}
+
+
+def latent_phase_bytes(ls, T, counts):
+    """Algorithmic HBM bytes of each latent-layer phase for one step."""
+    H, L, F, S, E = ls.hidden, ls.latent, ls.d_ffn, ls.n_shared, ls.n_experts
+    active = int((counts > 0).sum())
+    w13 = 2 * (F * L // 2 + F * L // 32)
+    w2 = L * F // 2 + L * F // 32
+    return {"front": E * H * 4 + L * H * 2 + S * 2 * F * H * 2 + T * H * 2, "topk_dispatch_z": 0,
+            "expert_gate_up": active * w13, "expert_down": active * w2,
+            "norm_up_shared_out": H * L * 2 + L * 4 + S * H * F * 2 + T * H * 2}
+
+
+def latent_phase_flops(ls, T):
+    H, L, F, S, E, k = ls.hidden, ls.latent, ls.d_ffn, ls.n_shared, ls.n_experts, ls.top_k
+    return {"front": 2 * T * (E * H + L * H + 2 * S * F * H), "topk_dispatch_z": 0,
+            "expert_gate_up": 4 * T * k * L * F, "expert_down": 2 * T * k * L * F,
+            "norm_up_shared_out": 2 * T * (H * L + S * H * F)}
+
+
+def latent_cpu_baseline(ls, seed, pool, budget_s):
+    """The oracle's latent layer, as it is, on a bounded sample of the
+    workload's tokens, one token at a time (routing on the full width,
+    projections, the 16 experts, norm, shared experts; expert generation
+    untimed)."""
+    import oracle
+    import synth
+    rw = synth.router_weight(ls.outer, seed, 0)
+    down, up, nw = synth.latent_projections(ls, seed, 0)
+    sh = synth.shared_weights(ls.outer, seed, 0)
+    toks = pool.reshape(-1, ls.hidden)
+    done, spent = 0, 0.0
+    for t in range(toks.shape[0]):
+        x = toks[t:t + 1]
+        t0 = time.perf_counter()
+        ids, w, _ = oracle.route(x, rw, None, ls.top_k)
+        spent += time.perf_counter() - t0
+        held = synth.host_layer(ls.inner, seed, 0, experts=np.unique(ids), outer=ls.outer)
+        pos = {int(e): i for i, e in enumerate(held.experts)}
+        slot = np.array([[pos[int(e)] for e in ids[0]]], dtype=np.int32)
+        t0 = time.perf_counter()
+        oracle.latent_forward(x, slot, w, oracle.held_arrays(held), down, up, nw, sh)
+        spent += time.perf_counter() - t0
+        done += 1
+        if spent >= budget_s:
+            break
+    return {"value": done / spent, "unit": "tok/s", "cores": oracle.threads(), "kind": "oracle",
+            "sample": f"{done} tokens of the workload, one at a time (full-width router over "
+                      f"{ls.n_experts} experts, down projection, {ls.top_k} routed expert FFNs in the "
+                      f"latent, RMSNorm of the aggregate, up projection, {ls.n_shared} full-width shared "
+                      f"experts), {spent:.1f} s of oracle time"}
+
+
+def measure_latent(lidx, steps, warmup, pool, use_graph, cpu_seconds, hbm_copy_gbs):
+    """One latent-layer workload (Kimi-K3's Stable LatentMoE around the routed
+    experts): as measure(), with the phases of moe_latent_layer_timed."""
+    import torch
+    import synth
+    import synth.device as sdev
+    import quantized_expert_gemv_sigmoid_amd as moe
+
+    wl = synth.LATENT_WORKLOADS[lidx]
+    ls = synth.K3_LATENT if lidx > 0 else synth.TINY_LATENT
+    T, H = wl.tokens, ls.hidden
+    t_load = time.perf_counter()
+    log(f"bench: {wl.name}: uploading {ls.n_experts} experts "
+        f"({ls.n_experts * ls.inner.expert_bytes / 1e9:.2f} GB MXFP4)")
+    t = sdev.upload_latent_layer(ls, wl.seed, 0)
+    desc = moe.make_latent_desc(ls.n_experts, ls.top_k, H, ls.latent, ls.d_ffn, ls.n_shared, t)
+    npool = max(1, min(pool, (1 << 16) // T))
+    xpool = synth.x_tokens(ls.outer, wl.seed, 0, npool * T).reshape(npool, T, H)
+    xs = sdev.tokens_to_device(xpool.reshape(npool * T, H)).view(npool, T, H)
+    ws = moe.latent_workspace(desc, T)
+    out = torch.empty((T, H), dtype=torch.int16, device="cuda")
+    ids = torch.empty((T, ls.top_k), dtype=torch.int32, device="cuda")
+    wts = torch.empty((T, ls.top_k), dtype=torch.float32, device="cuda")
+    cnt = torch.empty(ls.n_experts, dtype=torch.int32, device="cuda")
+    counts = []
+    for i in range(npool):
+        moe.latent_layer(desc, xs[i], T, out, None, moe.OUT_BF16, ws, ids=ids, weights=wts, counts=cnt)
+        torch.cuda.synchronize()
+        counts.append(cnt.cpu().numpy().copy())
+    load_s = time.perf_counter() - t_load
+    kind = {1: "gemv", 2: "mfma"}[moe.latent_path_for(desc, T)]
+
+    def step(i):
+        moe.latent_layer(desc, xs[i % npool], T, out, None, moe.OUT_BF16, ws)
+
+    stream = torch.cuda.current_stream()
+    for i in range(warmup):
+        step(i)
+    torch.cuda.synchronize()
+    K = steps
+    start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    graphs = None
+    if use_graph:
+        graphs = []
+        for i in range(npool):
+            g = torch.cuda.CUDAGraph()
+            with torch.cuda.graph(g):
+                step(i)
+            graphs.append(g)
+        for i in range(warmup):
+            graphs[i % npool].replay()
+        torch.cuda.synchronize()
+    windows = []
+    for wdx in range(WINDOWS):
+        torch.cuda.synchronize()
+        start.record(stream)
+        for i in range(K):
+            if graphs is not None:
+                graphs[(wdx * K + i) % npool].replay()
+            else:
+                step(wdx * K + i)
+        end.record(stream)
+        torch.cuda.synchronize()
+        windows.append(start.elapsed_time(end) / K)
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(moe.TIMED_EVENTS)] for _ in range(K)]
+    for row in evs:
+        for e in row:
+            e.record(stream)
+    torch.cuda.synchronize()
+    start.record(stream)
+    for i in range(K):
+        moe.latent_layer_timed(desc, xs[i % npool], T, out, None, moe.OUT_BF16, ws, evs[i], stream=stream)
+    end.record(stream)
+    torch.cuda.synchronize()
+    eager_ms = start.elapsed_time(end) / K
+    ph_ms = {p: float(np.mean([evs[i][j].elapsed_time(evs[i][j + 1]) for i in range(K)]))
+             for j, p in enumerate(LATENT_PHASES)}
+    ph_bytes = {p: float(np.mean([latent_phase_bytes(ls, T, counts[i % npool])[p] for i in range(K)]))
+                for p in LATENT_PHASES}
+    ph_flops = latent_phase_flops(ls, T)
+    step_bytes = sum(ph_bytes.values())
+    step_flops = sum(ph_flops.values())
+    dom = max(("front", "expert_gate_up", "expert_down", "norm_up_shared_out"), key=lambda p: ph_ms[p])
+    intensity = ph_flops[dom] / max(ph_bytes[dom], 1.0)
+    if kind == "mfma" and intensity >= 0.5 * PEAK_BF16_TFLOPS * 1e12 / (PEAK_HBM_GBS * 1e9):
+        achieved = ph_flops[dom] / (ph_ms[dom] * 1e-3) / 1e12
+        roofline = {"bound": "mfma", "achieved": round(achieved, 1), "peak": PEAK_BF16_TFLOPS,
+                    "unit": "TFLOP/s", "frac": round(achieved / PEAK_BF16_TFLOPS, 4), "traffic": None,
+                    "kernel": LATENT_KERNELS[kind][dom], "flops_per_launch": int(ph_flops[dom]),
+                    "avg_launch_us": round(ph_ms[dom] * 1e3, 2)}
+    else:
+        achieved = ph_bytes[dom] / (ph_ms[dom] * 1e-3) / 1e9
+        roofline = {"bound": "hbm", "achieved": round(achieved, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
+                    "frac": round(achieved / PEAK_HBM_GBS, 4),
+                    "traffic": measured_traffic(LATENT_KERNELS[kind][dom].split()[0]) if T == 1 else None,
+                    "kernel": LATENT_KERNELS[kind][dom], "bytes_per_launch": int(ph_bytes[dom]),
+                    "avg_launch_us": round(ph_ms[dom] * 1e3, 2),
+                    "frac_of_copy": round(achieved / hbm_copy_gbs, 4)}
+    med = float(np.median(windows))
+    res = {
+        "config": {"workload": wl.name, "layer": "Stable LatentMoE", "n_experts": ls.n_experts,
+                   "top_k": ls.top_k, "n_shared": ls.n_shared, "hidden": H, "latent": ls.latent,
+                   "d_ffn": ls.d_ffn, "tokens": T, "latent_norm": 1, "rms_eps": 1e-5,
+                   "weights": "mxfp4 (e2m1 + e8m0/32) routed, bf16 projections and shared, fp32 router",
+                   "path": kind, "token_pool": npool,
+                   "launch": "hip graph replay" if graphs is not None else "eager"},
+        "steps": K, "ms_per_step": round(windows[0], 5),
+        "ms_per_step_windows": [round(w, 5) for w in windows],
+        "ms_per_step_median": round(med, 5),
+        "ms_per_step_spread": round((max(windows) - min(windows)) / med, 4),
+        "tok_s": round(T / (windows[0] * 1e-3), 2), "tok_s_median": round(T / (med * 1e-3), 2),
+        "ms_per_step_eager": round(eager_ms, 5),
+        "step_hbm_gbs": round(step_bytes / (med * 1e-3) / 1e9, 1),
+        "step_hbm_frac": round(step_bytes / (med * 1e-3) / 1e9 / PEAK_HBM_GBS, 4),
+        "step_frac_of_copy": round(step_bytes / (med * 1e-3) / 1e9 / hbm_copy_gbs, 4),
+        "step_tflops": round(step_flops / (med * 1e-3) / 1e12, 3),
+        "step_mfma_frac": round(step_flops / (med * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 4),
+        "step_bytes": int(step_bytes), "step_flops": int(step_flops),
+        "distinct_experts": round(float(np.mean([(c > 0).sum() for c in counts])), 1),
+        "phase_us": {p: round(v * 1e3, 2) for p, v in ph_ms.items()},
+        "roofline": roofline,
+        "load_s": round(load_s, 1),
+    }
+    if cpu_seconds > 0:
+        log(f"bench: {wl.name}: timing the CPU oracle on a bounded sample")
+        res["cpu_baseline"] = latent_cpu_baseline(ls, wl.seed, xpool, cpu_seconds)
+    del graphs, t, desc, xs, ws, out, ids, wts, cnt, evs
+    import gc
+    gc.collect()
+    torch.cuda.synchronize()
+    torch.cuda.empty_cache()
+    return res
 
 
 def copy_gbs(torch, nbytes: int, reps: int) -> float:
@@ -354,6 +566,11 @@ def main():
                          "3: prefill T=4096, 4: 12 stacked layers with the Zipf selection bias, T=1)")
     ap.add_argument("--configs", default="0,2,3,4",
                     help="other workloads measured into `configs` (comma-separated indexes; '' for none)")
+    ap.add_argument("--latent-workload", type=int, default=-1,
+                    help="make this latent workload (index into synth.LATENT_WORKLOADS) the headline")
+    ap.add_argument("--latent-configs", default="1,2",
+                    help="latent-layer workloads (Kimi-K3's Stable LatentMoE) measured into `configs`: "
+                         "indexes into synth.LATENT_WORKLOADS (0: tiny, 1: decode T=1, 2: prefill T=4096)")
     ap.add_argument("--pool", type=int, default=32, help="distinct token batches cycled over")
     ap.add_argument("--cpu-seconds", type=float, default=15.0, help="oracle time of the headline's CPU sample")
     ap.add_argument("--config-cpu-seconds", type=float, default=4.0,
@@ -401,8 +618,12 @@ def main():
     # this GPU, reported beside the published peak
     hbm_copy_gbs = copy_gbs(torch, 1 << 30, 20)
     use_graph = not args.no_graph
-    head = measure(args.workload, args.steps, args.warmup, args.pool, use_graph,
-                   0.0 if args.no_cpu_baseline else args.cpu_seconds, hbm_copy_gbs)
+    if args.latent_workload >= 0:
+        head = measure_latent(args.latent_workload, args.steps, args.warmup, args.pool, use_graph,
+                              0.0 if args.no_cpu_baseline else args.cpu_seconds, hbm_copy_gbs)
+    else:
+        head = measure(args.workload, args.steps, args.warmup, args.pool, use_graph,
+                       0.0 if args.no_cpu_baseline else args.cpu_seconds, hbm_copy_gbs)
     result = {
         "metric": METRIC, "value": head["tok_s"], "unit": "tok/s", "n_gpus": 1, "steps": args.steps,
         "warmup": args.warmup, "ms_per_step": head["ms_per_step"], "higher_is_better": True,
@@ -424,10 +645,17 @@ def main():
     idx = [int(c) for c in args.configs.split(",") if c.strip() != ""]
     configs = []
     for c in idx:
-        if c == args.workload:
+        if c == args.workload and args.latent_workload < 0:
             continue
         r = measure(c, CONFIG_STEPS.get(c, 20), min(args.warmup, 5), args.pool, use_graph,
                     0.0 if args.no_cpu_baseline else args.config_cpu_seconds, hbm_copy_gbs)
+        log(f"bench: {r['config']['workload']}: {r['ms_per_step_median']} ms/step (median of {WINDOWS} windows)")
+        configs.append(r)
+    for c in [int(c) for c in args.latent_configs.split(",") if c.strip() != ""]:
+        if c == args.latent_workload:
+            continue
+        r = measure_latent(c, LATENT_STEPS.get(c, 20), min(args.warmup, 5), args.pool, use_graph,
+                           0.0 if args.no_cpu_baseline else args.config_cpu_seconds, hbm_copy_gbs)
         log(f"bench: {r['config']['workload']}: {r['ms_per_step_median']} ms/step (median of {WINDOWS} windows)")
         configs.append(r)
     if configs:
