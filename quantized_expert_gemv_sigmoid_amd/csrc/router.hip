@@ -4,9 +4,9 @@
 //
 // Selection: each candidate is a 64-bit key, the fp32 selection score mapped
 // to an order-preserving uint32 in the high half and ~id in the low half, so
-// the largest key is the largest score with ties to the lower id.  k rounds of
-// a wave-wide 64-bit max (DPP inside each row of 16 lanes, then readlane
-// across the four rows) pick the experts in descending order.
+// the largest key is the largest score with ties to the lower id.  One wave
+// per token finds the k-th largest score by a ballot bisection over its 32
+// bits, collects the k candidates and ranks them (topk_wave_select).
 //
 // Dispatch: positions group the (token, expert) pairs by expert (ascending
 // id) and, inside an expert, by token.  The pairs of expert e inside a
@@ -16,6 +16,8 @@
 // repeats of an id in a token's row share one position (one bit of the
 // bitmap), whose weight is the sum of their weights in slot order, so that
 // w1 FFN_e(x) + w2 FFN_e(x) = (w1 + w2) FFN_e(x) loses no contribution.
+// The scatter takes one wave per token, lane j holding slot j, so the merge
+// and the ascending-id order of the token's positions are O(k) readlanes.
 #include "common.h"
 #include "router_dev.h"
 
@@ -27,12 +29,12 @@ template <int EPL>
 __device__ __forceinline__ void topk_wave(int E, int k, const float *__restrict__ lrow,
                                           const float *__restrict__ bias, int renorm,
                                           float routed_scale, int32_t *__restrict__ ids_out,
-                                          float *__restrict__ w_out)
+                                          float *__restrict__ w_out, uint64_t *cand)
 {
     const int lane = threadIdx.x & 63;
     int id;
     float wt;
-    topk_regs<EPL>(E, k, lrow, bias, renorm, routed_scale, id, wt);
+    topk_wave_select<EPL>(E, k, lrow, bias, renorm, routed_scale, cand, id, wt);
     if (lane < k) {
         ids_out[lane] = id;
         w_out[lane] = wt;
@@ -45,19 +47,21 @@ __global__ __launch_bounds__(256) void k_topk(int T, int E, int k, const float *
                                               float routed_scale, int32_t *__restrict__ ids,
                                               float *__restrict__ wts)
 {
+    __shared__ uint64_t s_tk[4][2 * kMaxTopK];
     const int t = blockIdx.x * 4 + (threadIdx.x >> 6);
     if (t >= T) return;
     topk_wave<EPL>(E, k, logits + (size_t)t * E, bias, renorm, routed_scale,
-                   ids + (size_t)t * k, wts + (size_t)t * k);
+                   ids + (size_t)t * k, wts + (size_t)t * k, s_tk[threadIdx.x >> 6]);
 }
 
 // -------------------------------------------------------------- dispatch
 
 __device__ __forceinline__ bool valid_id(int e, int E) { return e >= 0 && e < E; }
 
-// exclusive scan of one int per thread over a block of 1024 threads (16
-// waves); returns the thread's exclusive prefix, *total gets the sum.
-__device__ __forceinline__ int block_scan_1024(int v, int *tmp16, int *total)
+// exclusive scan of one int per thread over a block of NW waves; returns
+// the thread's exclusive prefix, *total gets the sum.
+template <int NW>
+__device__ __forceinline__ int block_scan(int v, int *tmp, int *total)
 {
     const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
     int x = v;
@@ -66,12 +70,12 @@ __device__ __forceinline__ int block_scan_1024(int v, int *tmp16, int *total)
         const int y = __shfl_up(x, d, 64);
         if (lane >= d) x += y;
     }
-    if (lane == 63) tmp16[wv] = x;
+    if (lane == 63) tmp[wv] = x;
     __syncthreads();
     int base = 0, tot = 0;
 #pragma unroll
-    for (int i = 0; i < 16; i++) {
-        const int t = tmp16[i];
+    for (int i = 0; i < NW; i++) {
+        const int t = tmp[i];
         base += i < wv ? t : 0;
         tot += t;
     }
@@ -80,125 +84,121 @@ __device__ __forceinline__ int block_scan_1024(int v, int *tmp16, int *total)
     return base + x - v;
 }
 
-// per-expert counts (one thread per expert, given its count) -> counts,
-// offsets, active list, meta; returns the expert's offset
-__device__ __forceinline__ int write_offsets(int e, int E, int c, int *tmp16, int32_t *counts_out,
-                                             const Work &w)
+constexpr int kSmallThreads = 512;  // threads of the one-block dispatch (2 experts each)
+
+// per-expert counts, experts 2 i and 2 i + 1 with thread i (counts c0, c1)
+// -> counts, offsets (into offs[] too), active list, meta
+__device__ __forceinline__ void write_offsets2(int E, int c0, int c1, int *offs, int *tmp,
+                                               int32_t *counts_out, const Work &w)
 {
-    // low 16 bits: slots (<= T*k <= 65535 per call here), high: active experts
-    const int packed = (e < E) ? (c | ((c > 0) << 16)) : 0;
+    // low 16 bits: slots (<= T*k <= 4096 here), high: active experts
+    const int e0 = 2 * (int)threadIdx.x, e1 = e0 + 1;
+    const int p0 = e0 < E ? (c0 | ((c0 > 0) << 16)) : 0;
+    const int p1 = e1 < E ? (c1 | ((c1 > 0) << 16)) : 0;
     int total;
-    const int ex = block_scan_1024(packed, tmp16, &total);
-    const int off = ex & 0xffff, act = ex >> 16;
-    if (e < E) {
-        w.counts[e] = c;
-        w.offsets[e] = off;
-        if (counts_out) counts_out[e] = c;
-        if (c > 0) w.active[act] = e;
+    const int ex0 = block_scan<kSmallThreads / 64>(p0 + p1, tmp, &total);
+    const int ex1 = ex0 + p0;
+    if (e0 < E) {
+        w.counts[e0] = c0;
+        w.offsets[e0] = offs[e0] = ex0 & 0xffff;
+        if (counts_out) counts_out[e0] = c0;
+        if (c0 > 0) w.active[ex0 >> 16] = e0;
+    }
+    if (e1 < E) {
+        w.counts[e1] = c1;
+        w.offsets[e1] = offs[e1] = ex1 & 0xffff;
+        if (counts_out) counts_out[e1] = c1;
+        if (c1 > 0) w.active[ex1 >> 16] = e1;
     }
     if (threadIdx.x == 0) {
         w.offsets[E] = total & 0xffff;
         w.meta[0] = total >> 16;
     }
-    return off;
 }
 
-// the first slot of a token's row holding a valid id leads that id: it owns
-// the (token, expert) position; later slots with the same id follow it
-__device__ __forceinline__ bool leads(const int32_t *__restrict__ row, int j, int E)
+// One wave per token t: lane j < k holds slot j.  A slot leads its id if no
+// earlier slot of the row holds the same id; the leader owns the (token,
+// expert) position pos_of(id), whose weight is the sum of the weights of
+// every slot with that id in slot order (just its own when it has no
+// repeat).  tok_pos[t] lists the token's positions in ascending expert id,
+// then -1 for the rest (invalid ids and repeats).
+template <typename PosOf>
+__device__ __forceinline__ void dispatch_token(int t, int E, int k, const int32_t *__restrict__ ids,
+                                               const float *__restrict__ wts, PosOf &&pos_of,
+                                               const Work &w)
 {
-    const int o = row[j];
-    if (!valid_id(o, E)) return false;
-    for (int i = 0; i < j; i++)
-        if (row[i] == o) return false;
-    return true;
-}
-
-// the routing weight of a leading slot: the weights of every slot of the row
-// with its id, summed in slot order (just its own weight when it has no repeat)
-__device__ __forceinline__ float merged_weight(const int32_t *__restrict__ row,
-                                               const float *__restrict__ wrow, int j, int k)
-{
-    const int o = row[j];
-    float w = 0.0f;
-    for (int i = 0; i < k; i++)
-        if (row[i] == o) w += wrow[i];
-    return w;
-}
-
-// positions of token t's (token, expert) pairs in ascending expert id, one
-// entry per slot: leading slots first, then -1 for the rest (invalid ids and
-// repeats)
-__device__ __forceinline__ void write_tok_pos(int t, int slot_j, int E, int k,
-                                              const int32_t *__restrict__ row, int pos,
-                                              int32_t *__restrict__ tok_pos)
-{
-    const bool me_leads = leads(row, slot_j, E);
-    const int mk = me_leads ? row[slot_j] : 0x7fffffff;
-    int r = 0;
+    const int lane = threadIdx.x & 63;
+    const int id = lane < k ? ids[(size_t)t * k + lane] : -1;
+    const float wt = lane < k ? wts[(size_t)t * k + lane] : 0.0f;
+    bool lead = lane < k && valid_id(id, E);
+    float wsum = 0.0f;
     for (int j = 0; j < k; j++) {
-        const int ok = leads(row, j, E) ? row[j] : 0x7fffffff;
-        r += (ok < mk) || (ok == mk && j < slot_j);
+        const int o = __builtin_amdgcn_readlane(id, j);
+        const float ow = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(wt), j));
+        lead = lead && !(o == id && j < lane);
+        wsum += o == id ? ow : 0.0f;
     }
-    tok_pos[(size_t)t * k + r] = me_leads ? pos : -1;
+    const uint64_t leaders = __builtin_amdgcn_ballot_w64(lead);
+    int rank = 0;
+    for (int j = 0; j < k; j++) {
+        const int o = __builtin_amdgcn_readlane(id, j);
+        rank += (((leaders >> j) & 1ull) && o < id) ? 1 : 0;
+    }
+    int32_t *tp = w.tok_pos + (size_t)t * k;
+    if (lead) {
+        const int p = pos_of(id);
+        w.pos_tok[p] = t;
+        w.pos_w[p] = wsum;
+        tp[rank] = p;
+    }
+    const int nlead = __builtin_popcountll(leaders);
+    if (lane >= nlead && lane < k) tp[lane] = -1;
 }
 
-// T <= 64 (so T*k <= 4096): one block of 1024 threads does top-k
-// (optional), the bitmaps, the counts/offsets scan and the scatter, with the
-// routing rows staged in LDS (the per-slot loops over a token's row then read
-// LDS, not a chain of global loads).  zq (optional, the latent layer): the
-// idle waves (the last ones first) turn the tokens' latent rows into fp16
-// rows with a scale meanwhile.
+// T <= 64: one block of 512 threads (8 waves: at most 128 registers per
+// lane for 16 waves would spill the top-k) does top-k (optional; wave t % 8
+// for token t), the bitmaps, the counts/offsets scan (two experts per
+// thread) and the scatter (one wave per token).  zq (optional, the latent
+// layer): the waves without a top-k (the last ones first) turn the tokens'
+// latent rows into fp16 rows with a scale meanwhile.
 template <int EPL>
-__global__ __launch_bounds__(1024) void k_dispatch_small(
+__global__ __launch_bounds__(kSmallThreads) void k_dispatch_small(
     Shape s, int do_topk, const float *__restrict__ logits, const float *__restrict__ bias,
     int32_t *__restrict__ ids, float *__restrict__ wts, int32_t *__restrict__ counts_out, Work w,
     ZQuant zq)
 {
+    constexpr int NW = kSmallThreads / 64;
     __shared__ unsigned long long masks[kMaxExperts];
     __shared__ int offs[kMaxExperts];
-    __shared__ int tmp16[16];
-    __shared__ int32_t s_ids[kDispatchTokens * kMaxTopK];
-    __shared__ float s_wts[kDispatchTokens * kMaxTopK];
+    __shared__ int tmp[NW];
+    __shared__ uint64_t s_tk[NW][2 * kMaxTopK];
     const int T = s.T, E = s.E, k = s.k;
     const int wave = threadIdx.x >> 6;
     if (do_topk) {
-        for (int t = wave; t < T; t += 16)
+        for (int t = wave; t < T; t += NW)
             topk_wave<EPL>(E, k, logits + (size_t)t * E, bias, s.renorm, s.routed_scale,
-                           ids + (size_t)t * k, wts + (size_t)t * k);
+                           ids + (size_t)t * k, wts + (size_t)t * k, s_tk[wave]);
     }
     if (zq.zf) {
-        for (int t = 15 - wave; t < T; t += 16) quant_z_row(t, zq);
+        for (int t = NW - 1 - wave; t < T; t += NW) quant_z_row(t, zq);
     }
-    for (int e = threadIdx.x; e < E; e += 1024) masks[e] = 0ull;
+    for (int e = threadIdx.x; e < E; e += kSmallThreads) masks[e] = 0ull;
     __syncthreads();  // also publishes the top-k results to the block
-    for (int sl = threadIdx.x; sl < T * k; sl += 1024) {
-        s_ids[sl] = ids[sl];
-        s_wts[sl] = wts[sl];
-    }
-    __syncthreads();
-    for (int sl = threadIdx.x; sl < T * k; sl += 1024) {
-        const int e = s_ids[sl];
+    for (int sl = threadIdx.x; sl < T * k; sl += kSmallThreads) {
+        const int e = ids[sl];
         if (valid_id(e, E)) atomicOr(&masks[e], 1ull << (sl / k));
     }
     __syncthreads();
-    const int e = threadIdx.x;
-    const int c = e < E ? __popcll(masks[e]) : 0;
-    const int off = write_offsets(e, E, c, tmp16, counts_out, w);
-    if (e < E) offs[e] = off;
-    __syncthreads();
-    for (int sl = threadIdx.x; sl < T * k; sl += 1024) {
-        const int t = sl / k, j = sl % k;
-        const int32_t *row = s_ids + t * k;
-        const int ee = row[j];
-        int p = -1;
-        if (leads(row, j, E)) {
-            p = offs[ee] + __popcll(masks[ee] & ((1ull << t) - 1ull));
-            w.pos_tok[p] = t;
-            w.pos_w[p] = merged_weight(row, s_wts + t * k, j, k);
-        }
-        write_tok_pos(t, j, E, k, row, p, w.tok_pos);
+    {
+        const int e0 = 2 * (int)threadIdx.x;
+        const int c0 = e0 < E ? __popcll(masks[e0]) : 0;
+        const int c1 = e0 + 1 < E ? __popcll(masks[e0 + 1]) : 0;
+        write_offsets2(E, c0, c1, offs, tmp, counts_out, w);
     }
+    __syncthreads();
+    for (int t = wave; t < T; t += NW)
+        dispatch_token(t, E, k, ids, wts,
+                       [&](int e) { return offs[e] + __popcll(masks[e] & ((1ull << t) - 1ull)); }, w);
 }
 
 // Large T: bitmaps per 64-token block
@@ -233,9 +233,9 @@ __global__ __launch_bounds__(1024) void k_dispatch_scan(Shape s, int nblk, int32
     }
     // counts can exceed 16 bits here: scan slots and active flags separately
     int total;
-    const int off = block_scan_1024(e < E ? run : 0, tmp16, &total);
+    const int off = block_scan<16>(e < E ? run : 0, tmp16, &total);
     int nact;
-    const int act = block_scan_1024(e < E && run > 0 ? 1 : 0, tmp16, &nact);
+    const int act = block_scan<16>(e < E && run > 0 ? 1 : 0, tmp16, &nact);
     if (e < E) {
         w.counts[e] = run;
         w.offsets[e] = off;
@@ -248,24 +248,19 @@ __global__ __launch_bounds__(1024) void k_dispatch_scan(Shape s, int nblk, int32
     }
 }
 
-// Large T: scatter slots to positions (one thread per slot)
+// Large T: scatter the slots to positions (one wave per token)
 __global__ __launch_bounds__(256) void k_dispatch_scatter(Shape s, const int32_t *__restrict__ ids,
                                                           const float *__restrict__ wts, Work w)
 {
-    const int sl = blockIdx.x * blockDim.x + threadIdx.x;
-    if (sl >= s.T * s.k) return;
-    const int t = sl / s.k, j = sl % s.k;
-    const int32_t *row = ids + (size_t)t * s.k;
-    const int e = row[j];
-    int p = -1;
-    if (leads(row, j, s.E)) {
-        const int b = t / kDispatchTokens, tl = t % kDispatchTokens;
-        const unsigned long long m = w.masks[(size_t)b * s.E + e];
-        p = w.offsets[e] + w.blk_base[(size_t)b * s.E + e] + __popcll(m & ((1ull << tl) - 1ull));
-        w.pos_tok[p] = t;
-        w.pos_w[p] = merged_weight(row, wts + (size_t)t * s.k, j, s.k);
-    }
-    write_tok_pos(t, j, s.E, s.k, row, p, w.tok_pos);
+    const int t = blockIdx.x * 4 + (threadIdx.x >> 6);
+    if (t >= s.T) return;
+    const int b = t / kDispatchTokens, tl = t % kDispatchTokens;
+    dispatch_token(t, s.E, s.k, ids, wts,
+                   [&](int e) {
+                       const unsigned long long m = w.masks[(size_t)b * s.E + e];
+                       return w.offsets[e] + w.blk_base[(size_t)b * s.E + e] + __popcll(m & ((1ull << tl) - 1ull));
+                   },
+                   w);
 }
 
 template <int EPL>
@@ -281,7 +276,7 @@ static void launch_small(const Shape &s, int do_topk, const float *logits, const
                          int32_t *ids, float *wts, int32_t *counts_out, const Work &w,
                          hipStream_t stream, const ZQuant &zq)
 {
-    k_dispatch_small<EPL><<<1, 1024, 0, stream>>>(s, do_topk, logits, bias, ids, wts, counts_out, w, zq);
+    k_dispatch_small<EPL><<<1, kSmallThreads, 0, stream>>>(s, do_topk, logits, bias, ids, wts, counts_out, w, zq);
 }
 
 #define MOE_EPL_SWITCH(epl, CALL)       \
@@ -319,7 +314,7 @@ hipError_t launch_dispatch(const Shape &s, int do_topk, const float *logits, con
     const int nblk = (s.T + kDispatchTokens - 1) / kDispatchTokens;
     k_dispatch_masks<<<nblk, 256, 0, stream>>>(s, ids, w);
     k_dispatch_scan<<<1, 1024, 0, stream>>>(s, nblk, counts_out, w);
-    k_dispatch_scatter<<<(s.T * s.k + 255) / 256, 256, 0, stream>>>(s, ids, wts, w);
+    k_dispatch_scatter<<<(s.T + 3) / 4, 256, 0, stream>>>(s, ids, wts, w);
     return hipGetLastError();
 }
 

@@ -1,5 +1,6 @@
-// Device helpers of the router: the 64-bit selection key, a wave-wide 64-bit
-// max, and the logit rows (fp32 dot products of the router weights with x).
+// Device helpers of the router: the 64-bit selection key, the top-k of one
+// token by one wave, and the logit rows (fp32 dot products of the router
+// weights with x).
 #pragma once
 
 #include "common.h"
@@ -14,78 +15,72 @@ __device__ __forceinline__ uint64_t select_key(float ch, int e)
     return ((uint64_t)u << 32) | (uint32_t)(~(uint32_t)e);
 }
 
-template <int CTRL>
-__device__ __forceinline__ uint64_t dpp_u64(uint64_t v)
-{
-    const int lo = __builtin_amdgcn_update_dpp(0, (int)(uint32_t)v, CTRL, 0xF, 0xF, true);
-    const int hi = __builtin_amdgcn_update_dpp(0, (int)(uint32_t)(v >> 32), CTRL, 0xF, 0xF, true);
-    return ((uint64_t)(uint32_t)hi << 32) | (uint32_t)lo;
-}
-
-// max over the 64 lanes, returned (uniform) to every lane: a butterfly inside
-// each row of 16 lanes (quad_perm [1,0,3,2], [2,3,0,1], row_half_mirror,
-// row_mirror), then the four row results through readlane
-__device__ __forceinline__ uint64_t wave_max_u64(uint64_t v)
-{
-    uint64_t o;
-    o = dpp_u64<0xB1>(v);
-    v = o > v ? o : v;
-    o = dpp_u64<0x4E>(v);
-    v = o > v ? o : v;
-    o = dpp_u64<0x141>(v);
-    v = o > v ? o : v;
-    o = dpp_u64<0x140>(v);
-    v = o > v ? o : v;
-    uint64_t r = 0;
-#pragma unroll
-    for (int row = 0; row < 4; row++) {
-        const uint32_t lo = __builtin_amdgcn_readlane((int)(uint32_t)v, row * 16);
-        const uint32_t hi = __builtin_amdgcn_readlane((int)(uint32_t)(v >> 32), row * 16);
-        const uint64_t x = ((uint64_t)hi << 32) | lo;
-        r = x > r ? x : r;
-    }
-    return r;
-}
-
 // Top-k of one token's logits row by one wave (kimi-k3-in-c section 9,
 // "Picking 16 experts of 896"): lane j < k ends with the j-th pick (descending
 // selection score sigmoid(logit) + bias, ties to the lower id) in id and its
 // routing weight in wt: the unbiased score, renormalised over the k picks (fp32
-// sum in selection order) if renorm, times routed_scale.  Each lane keeps
-// EPL >= E / 64 keys; k rounds of a wave-wide 64-bit max.
+// sum in selection order) if renorm, times routed_scale.  Each lane keys
+// EPL >= E / 64 experts (expert 64 i + lane in slot i) with the 32-bit
+// order-preserving score; the k-th largest key t comes from a bisection over
+// its 32 bits (is #{key >= t | bit} >= k? counted with ballots), then the
+// keys above t and, in ascending id, the keys equal to t fill k candidates
+// (64-bit keys: score, then the inverted id), which are ranked by count.
+// cand: 2 kMaxTopK entries of LDS of the calling wave.
 template <int EPL>
-__device__ __forceinline__ void topk_regs(int E, int k, const float *__restrict__ lrow,
-                                          const float *__restrict__ bias, int renorm,
-                                          float routed_scale, int &id, float &wt)
+__device__ __forceinline__ void topk_wave_select(int E, int k, const float *__restrict__ lrow,
+                                                 const float *__restrict__ bias, int renorm,
+                                                 float routed_scale, uint64_t *cand, int &id, float &wt)
 {
     const int lane = threadIdx.x & 63;
-    uint64_t key[EPL];
+    uint32_t key[EPL];
 #pragma unroll
     for (int i = 0; i < EPL; i++) {
         // branch-free (a branch per element makes the compiler copy the whole array)
         const int e = lane + 64 * i;
         const int ec = e < E ? e : E - 1;
         const float sc = sigmoidf_(lrow[ec]);
-        const uint64_t kk = select_key(sc + (bias ? bias[ec] : 0.0f), e);
-        key[i] = e < E ? kk : 0ull;  // padding is never selected: real keys are > 0
+        const uint32_t kk = (uint32_t)(select_key(sc + (bias ? bias[ec] : 0.0f), e) >> 32);
+        key[i] = e < E ? kk : 0u;  // padding is never selected: real keys are > 0
     }
-    int my_id = 0;
+    uint32_t t = 0;
 #pragma unroll 1
-    for (int j = 0; j < k; j++) {
-        uint64_t best = 0;
+    for (int bit = 31; bit >= 0; bit--) {
+        const uint32_t c = t | (1u << bit);
+        int n = 0;
 #pragma unroll
-        for (int i = 0; i < EPL; i++) best = key[i] > best ? key[i] : best;
-        const uint64_t win = wave_max_u64(best);
-        const int e = (int)(~(uint32_t)win);
-        const bool mine = (e & 63) == lane;
-#pragma unroll
-        for (int i = 0; i < EPL; i++) key[i] = (mine && i == (e >> 6)) ? 0ull : key[i];
-        my_id = lane == j ? e : my_id;
+        for (int i = 0; i < EPL; i++) n += __builtin_popcountll(__builtin_amdgcn_ballot_w64(key[i] >= c));
+        t = n >= k ? c : t;
     }
+    int above = 0;
+#pragma unroll
+    for (int i = 0; i < EPL; i++) above += __builtin_popcountll(__builtin_amdgcn_ballot_w64(key[i] > t));
+    const int need_eq = k - above;
+    int pg = 0, pe = 0;
+#pragma unroll
+    for (int i = 0; i < EPL; i++) {
+        const uint64_t mg = __builtin_amdgcn_ballot_w64(key[i] > t);
+        const uint64_t me = __builtin_amdgcn_ballot_w64(key[i] == t);
+        const int bg = pg + (int)__builtin_amdgcn_mbcnt_hi((uint32_t)(mg >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)mg, 0u));
+        const int be = pe + (int)__builtin_amdgcn_mbcnt_hi((uint32_t)(me >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)me, 0u));
+        const uint64_t ck = ((uint64_t)key[i] << 32) | (uint32_t)(~(uint32_t)(lane + 64 * i));
+        if (key[i] > t) cand[bg] = ck;
+        if (key[i] == t && be < need_eq) cand[above + be] = ck;
+        pg += __builtin_popcountll(mg);
+        pe += __builtin_popcountll(me);
+    }
+    // (one wave: its LDS accesses are performed in issue order)
+    __builtin_amdgcn_wave_barrier();
+    const uint64_t c = lane < k ? cand[lane] : 0ull;
+    int r = 0;
+    for (int i = 0; i < k; i++) r += cand[i] > c ? 1 : 0;  // one address for all lanes: a broadcast
+    if (lane < k) cand[kMaxTopK + r] = c;  // distinct keys: the ranks are a permutation
+    __builtin_amdgcn_wave_barrier();
+    const uint64_t kk = lane < k ? cand[kMaxTopK + lane] : 0ull;
+    const int my_id = lane < k ? (int)(~(uint32_t)kk) : 0;
     // the unbiased score of each pick, recomputed from its logit (same fp32 op)
     const float my_s = lane < k ? sigmoidf_(lrow[my_id]) : 0.0f;
     float sum = 0.0f;  // fp32 sum in selection order
-    for (int j = 0; j < k; j++) sum += __shfl(my_s, j, 64);
+    for (int j = 0; j < k; j++) sum += __int_as_float(__builtin_amdgcn_readlane(__float_as_int(my_s), j));
     float wj = my_s;
     if (renorm && sum > 0.0f) wj = wj / sum;
     wj *= routed_scale;
