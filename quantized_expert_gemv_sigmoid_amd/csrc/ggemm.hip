@@ -477,9 +477,13 @@ __device__ __forceinline__ void wave_pass(const GemmParams &p, const Blk &bk, in
         return lds_ld16(B + (cg * 64 + nb * 32 + col) * C::BCOL + ((pc ^ sb_) << 4));
     };
 
-    // multiply stage i, in ring slot sl
-    auto compute = [&](int i, int sl) __attribute__((always_inline)) {
-        if constexpr (NTW > 0 && MODE == M_G13) {
+    // multiply stage i, in ring slot sl.  mid() (the next stage's copies) is
+    // called once the stage's first fragment reads are issued, so that their
+    // latency covers the copies' issue
+    auto compute = [&](int i, int sl, auto &&mid) __attribute__((always_inline)) {
+        if constexpr (NTW == 0) {
+            mid();
+        } else if constexpr (MODE == M_G13) {
             // Scaled MX MFMA (32x32x64, A fp8 e4m3, B fp4 e2m1).  In step stp
             // (0, 1) of the stage, lane (col, kh) holds for each of its two
             // columns MX block 2 stp + kh (K 64 stp + 32 kh .. + 31; B piece
@@ -495,28 +499,10 @@ __device__ __forceinline__ void wave_pass(const GemmParams &p, const Blk &bk, in
             const int sa = i + bk.kst0;
             typedef int i32x8_t __attribute__((ext_vector_type(8)));
             uint4 q[2][2];
+            uint32_t s4[2];
             int scb[2][2];
-#pragma unroll
-            for (int nb = 0; nb < 2; nb++) {
-                // the stage's 4 scale bytes of the column (blocks 0..3)
-                const int R = s_row_of<MODE>(cg * 64 + nb * 32 + col);
-                const uint32_t s4 = *reinterpret_cast<const LDS uint32_t *>(
-                    scl + R * 128 + (((sa >> 2) ^ (R & 7)) << 4) + 4 * (sa & 3));
-#pragma unroll
-                for (int stp = 0; stp < 2; stp++) {
-                    q[nb][stp] = b_piece(B, nb, 2 * stp + kh);
-                    // NaN scale (255): the block contributes 0
-                    const uint32_t sc = (s4 >> (8 * (2 * stp + kh))) & 0xffu;
-                    const uint32_t keep = sc == 255u ? 0u : ~0u;
-                    q[nb][stp].x &= keep; q[nb][stp].y &= keep; q[nb][stp].z &= keep; q[nb][stp].w &= keep;
-                    scb[nb][stp] = (int)(sc == 255u ? 127u : sc);
-                }
-            }
-            // (the MFMAs of a step run through all accumulators once per term,
-            // so that consecutive ones never depend on each other)
-#pragma unroll
-            for (int stp = 0; stp < 2; stp++) {
-                i32x8_t at[2][NTW];  // [term][tile]
+            // the step's A fragments of each term and tile
+            auto a_load = [&](i32x8_t (&at)[2][NTW], int stp) __attribute__((always_inline)) {
 #pragma unroll
                 for (int mt = 0; mt < NTW; mt++) {
                     const LDS uint8_t *arow = A + ((T0 + mt) * 32 + col) * AROW;
@@ -529,6 +515,38 @@ __device__ __forceinline__ void wave_pass(const GemmParams &p, const Blk &bk, in
                                                (int)u1.x, (int)u1.y, (int)u1.z, (int)u1.w};
                     }
                 }
+            };
+            // the stage's reads first: the 4 scale bytes of each column
+            // (blocks 0..3), its two MX blocks, step 0's A fragments
+#pragma unroll
+            for (int nb = 0; nb < 2; nb++) {
+                const int R = s_row_of<MODE>(cg * 64 + nb * 32 + col);
+                s4[nb] = *reinterpret_cast<const LDS uint32_t *>(
+                    scl + R * 128 + (((sa >> 2) ^ (R & 7)) << 4) + 4 * (sa & 3));
+#pragma unroll
+                for (int stp = 0; stp < 2; stp++) q[nb][stp] = b_piece(B, nb, 2 * stp + kh);
+            }
+            i32x8_t at0[2][NTW];
+            a_load(at0, 0);
+            mid();
+#pragma unroll
+            for (int nb = 0; nb < 2; nb++) {
+#pragma unroll
+                for (int stp = 0; stp < 2; stp++) {
+                    // NaN scale (255): the block contributes 0
+                    const uint32_t sc = (s4[nb] >> (8 * (2 * stp + kh))) & 0xffu;
+                    const uint32_t keep = sc == 255u ? 0u : ~0u;
+                    q[nb][stp].x &= keep; q[nb][stp].y &= keep; q[nb][stp].z &= keep; q[nb][stp].w &= keep;
+                    scb[nb][stp] = (int)(sc == 255u ? 127u : sc);
+                }
+            }
+            // (the MFMAs of a step run through all accumulators once per term,
+            // so that consecutive ones never depend on each other)
+#pragma unroll
+            for (int stp = 0; stp < 2; stp++) {
+                i32x8_t at1[2][NTW];
+                if (stp == 1) a_load(at1, 1);
+                auto &at = stp == 0 ? at0 : at1;
 #pragma unroll
                 for (int tm = 0; tm < 2; tm++)
 #pragma unroll
@@ -546,7 +564,7 @@ __device__ __forceinline__ void wave_pass(const GemmParams &p, const Blk &bk, in
                                     at[1][mt], bv, acc[mt][nb], 0, 4, 1, (int)sca[mt], 0, scb[nb][stp]);
                         }
             }
-        } else if constexpr (NTW > 0) {
+        } else {
             const LDS uint8_t *A = ring + sl * RG::STAGE;
             const LDS uint8_t *B = A + RG::ABYTES;
             uint4 af[2][NTW];
@@ -557,18 +575,27 @@ __device__ __forceinline__ void wave_pass(const GemmParams &p, const Blk &bk, in
                 // the column's scale row)
                 const int sa = i + bk.kst0;
                 uint4 q[2][2];
+                uint32_t s2[2];
                 float scf[2][2];
 #pragma unroll
                 for (int nb = 0; nb < 2; nb++) {
                     q[nb][0] = b_piece(B, nb, 2 * kh);
                     q[nb][1] = b_piece(B, nb, 2 * kh + 1);
                     const int R = s_row_of<MODE>(cg * 64 + nb * 32 + col);
-                    const uint32_t s2 = *reinterpret_cast<const LDS uint16_t *>(
+                    s2[nb] = *reinterpret_cast<const LDS uint16_t *>(
                         scl + R * 128 + (((sa >> 2) ^ (R & 7)) << 4) + 4 * (sa & 3) + 2 * kh);
+                }
+                if constexpr (!SPLIT) {
+#pragma unroll
+                    for (int mt = 0; mt < NTW; mt++) af[0][mt] = a_frag(A, mt, 0);
+                }
+                mid();
+#pragma unroll
+                for (int nb = 0; nb < 2; nb++) {
 #pragma unroll
                     for (int h = 0; h < 2; h++) {
                         // NaN scale (255): the block contributes 0
-                        const uint32_t sc = (s2 >> (8 * h)) & 0xffu;
+                        const uint32_t sc = (s2[nb] >> (8 * h)) & 0xffu;
                         const uint32_t keep = sc == 255u ? 0u : ~0u;
                         q[nb][h].x &= keep; q[nb][h].y &= keep; q[nb][h].z &= keep; q[nb][h].w &= keep;
                         scf[nb][h] = e8m0f(sc == 255u ? 127u : sc);
@@ -584,8 +611,6 @@ __device__ __forceinline__ void wave_pass(const GemmParams &p, const Blk &bk, in
                 };
                 if constexpr (!SPLIT) {
                     BT b[2][2];
-#pragma unroll
-                    for (int mt = 0; mt < NTW; mt++) af[0][mt] = a_frag(A, mt, 0);
                     decode(b[0], 0);
 #pragma unroll
                     for (int st = 0; st < STEPS; st++) {
@@ -625,6 +650,7 @@ __device__ __forceinline__ void wave_pass(const GemmParams &p, const Blk &bk, in
                 for (int mt = 0; mt < NTW; mt++) af[0][mt] = a_frag(A, mt, 0);
 #pragma unroll
                 for (int nb = 0; nb < 2; nb++) bf[0][nb] = b_piece(B, nb, kh * STEPS);
+                mid();
 #pragma unroll
                 for (int st = 0; st < STEPS; st++) {
                     const int cur = st & 1, nxt = cur ^ 1;
@@ -659,8 +685,8 @@ __device__ __forceinline__ void wave_pass(const GemmParams &p, const Blk &bk, in
         // copies may fill stage i - 1's slot
         wait_vm<IN_FLIGHT>();
         block_barrier();
-        issue(i + NST - 1, sl == 0 ? NST - 1 : sl - 1);
-        compute(i, sl);
+        const int nsl = sl == 0 ? NST - 1 : sl - 1;
+        compute(i, sl, [&] __attribute__((always_inline)) { issue(i + NST - 1, nsl); });
         sl = sl == NST - 1 ? 0 : sl + 1;
     }
     // the ring is reused by the next pass: every copy (past-the-end ones
