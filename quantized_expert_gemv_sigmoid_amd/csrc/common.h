@@ -344,6 +344,50 @@ __device__ __forceinline__ void quant_z_row(int t, const ZQuant &q)
 // one wave per token row
 __global__ __launch_bounds__(256) void k_quant_z(int T, ZQuant q);
 
+// ---------------------------------------- buffer resources, direct loads to LDS
+
+// LDS pointers keep their address space through every helper (generic
+// pointers would let the compiler fall back to flat instructions)
+#define LDS __attribute__((address_space(3)))
+typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
+__device__ __forceinline__ uint4 lds_ld16(const LDS uint8_t *p)
+{
+    return __builtin_bit_cast(uint4, *reinterpret_cast<const LDS u32x4_t *>(p));
+}
+
+// a buffer resource over [base, base + bytes) (wave-uniform: the copies
+// below take it in scalar registers)
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t grsrc(const void *base, uint32_t bytes)
+{
+    const uint64_t a = (uint64_t)(uintptr_t)base;
+    const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)a);
+    const uint32_t hi = __builtin_amdgcn_readfirstlane((uint32_t)(a >> 32));
+    void *ub = (void *)(uintptr_t)(((uint64_t)hi << 32) | lo);
+    return __builtin_amdgcn_make_buffer_rsrc(ub, (short)0, (int)__builtin_amdgcn_readfirstlane(bytes), 0x00020000);
+}
+__device__ __forceinline__ uint4 gbld16(__amdgpu_buffer_rsrc_t r, uint32_t voff)
+{
+    return __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(r, (int)voff, 0, 0));
+}
+__device__ __forceinline__ uint32_t gbld1(__amdgpu_buffer_rsrc_t r, uint32_t voff)
+{
+    return __builtin_amdgcn_raw_buffer_load_b8(r, (int)voff, 0, 0);
+}
+// Direct global -> LDS loads: lane i's bytes at voff of r go to LDS at
+// dst + size * i (dst wave-uniform, in M0).  Written out: the compiler,
+// which cannot tell such a copy from the LDS reads of another ring slot,
+// would otherwise wait for every copy in flight before each LDS read.  The
+// caller orders the copies with explicit waits (wait_vm) and barriers; M0 is
+// restored for the compiler's own uses.
+__device__ __forceinline__ void gbld16_lds(__amdgpu_buffer_rsrc_t r, LDS uint8_t *dst, uint32_t voff)
+{
+    const uint32_t m0v = (uint32_t)(uintptr_t)dst;
+    uint32_t save;
+    asm volatile("s_mov_b32 %0, m0\n\ts_mov_b32 m0, %1\n\tbuffer_load_dwordx4 %2, %3, 0 offen lds\n\ts_mov_b32 m0, %0"
+                 : "=&s"(save)
+                 : "s"(m0v), "v"(voff), "s"(r)
+                 : "memory");
+}
 }  // namespace moe
 
 // ------------------------------------------------------------ host launchers

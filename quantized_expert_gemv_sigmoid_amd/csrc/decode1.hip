@@ -777,17 +777,17 @@ struct DnLoads {
     uint32_t sc[2][kDnRows][2];
 };
 
-// Rows [14 rblk, 14 rblk + 14) of the output: waves 0-6 own two rows each
-// (other waves of the block only stage and wait at the barrier).  s_h: LDS
-// for the fp16 H of the picks [k][F] and the fp32 shared activations [S][F];
-// s_e / s_w: the picks in ascending id (-1: none) and their weights.  The
-// rows' weight loads go out first; wait_h() then returns once H is written
-// (the gate/up kernel has ended, or every block of the fused kernel has
-// raised its flag); H is staged with agent-coherent loads when COHERENT.
+// Rows [14 rblk, 14 rblk + 14) of the output, two per wave.  s_h: LDS for
+// the fp16 H of the picks [k][F] and the fp32 shared activations [S][F]
+// (rounded up to whole KB); s_e / s_w: the picks in ascending id (-1: none)
+// and their weights.  H goes to LDS first, by direct global -> LDS copies
+// (no registers), so that it is not queued behind the rows' first weight
+// loads, which go out next; the wave then waits for the copies only (loads
+// complete in issue order) and the block meets once.
 // SHC: 16-byte chunks per lane of a shared down row (ceil(F / 512)).
-template <int SHC, bool COHERENT, typename WaitH>
+template <int SHC>
 __device__ __forceinline__ void dec1_down_rows(const Dec1Params &p, int rblk, uint8_t *s_h, const int *s_e,
-                                               const float *s_w, WaitH &&wait_h)
+                                               const float *s_w)
 {
     const Shape &s = p.s;
     const int lane = threadIdx.x & 63;
@@ -804,7 +804,6 @@ __device__ __forceinline__ void dec1_down_rows(const Dec1Params &p, int rblk, ui
     const uint32_t voq0 = lane < nb ? (uint32_t)lane * 16 : kPast, voq1 = lane + 64 < nb ? (uint32_t)(lane + 64) * 16 : kPast;
     const uint32_t vos0 = lane < nb ? (uint32_t)lane : kPast, vos1 = lane + 64 < nb ? (uint32_t)(lane + 64) : kPast;
     const int hb0 = min(lane, nb - 1), hb1 = min(lane + 64, nb - 1);
-    const bool row_wave = wave < kDnWaves;
     const int n0 = rblk * kDnBlockRows + wave * kDnRows;
     // rows past d (last block) re-read row d - 1 and are not stored
     int rows[kDnRows];
@@ -817,8 +816,11 @@ __device__ __forceinline__ void dec1_down_rows(const Dec1Params &p, int rblk, ui
     // holding 16-byte chunks l + 64 c; chunks past the row re-read its last
     // chunk and are masked out
     const int nchf = F / 8;
+    // (si past the shared experts: a zero-sized resource, nothing read, so
+    // that the number of loads issued is fixed)
     auto load_shd = [&](uint4 (&w)[kDnRows][SHC], int si) __attribute__((always_inline)) {
-        const auto r = brsrc(p.sh2 + (size_t)si * d * F, (uint32_t)((size_t)d * F * 2));
+        const bool ok = si < S;
+        const auto r = brsrc(ok ? p.sh2 + (size_t)si * d * F : p.sh2, ok ? (uint32_t)((size_t)d * F * 2) : 0u);
 #pragma unroll
         for (int rr = 0; rr < kDnRows; rr++)
 #pragma unroll
@@ -827,13 +829,17 @@ __device__ __forceinline__ void dec1_down_rows(const Dec1Params &p, int rblk, ui
                 w[rr][c] = bld16(r, ch * 16, (uint32_t)rows[rr] * F * 2);
             }
     };
-    // the first two shared experts' rows are loaded now (one if the rows are
-    // so wide that two would not fit the registers), a later one into the
-    // registers of the one just multiplied
-    constexpr int NSH = SHC <= 6 ? 2 : 1;
-    uint4 shw[NSH][kDnRows][SHC];
-    if (row_wave && S > 0) load_shd(shw[0], 0);
-    if (row_wave && NSH > 1 && S > 1) load_shd(shw[NSH - 1], 1);
+    // H (k F 2 + S F 4 bytes, one region) into LDS, 1 KB per copy
+    // instruction, the copies spread over the waves; bytes past the region
+    // read 0 into the rounding
+    {
+        const int nbytes = k * F * 2 + S * F * 4;
+        const int nchunk = (nbytes + 1023) / 1024;
+        const int nw = (int)(blockDim.x >> 6);
+        const auto rh = grsrc(p.w.H, (uint32_t)nbytes);
+        LDS uint8_t *dst = (LDS uint8_t *)s_h;
+        for (int c = wave; c < nchunk; c += nw) gbld16_lds(rh, dst + c * 1024, (uint32_t)(c * 1024 + lane * 16));
+    }
 
     const int npair = (k + 1) / 2;
     // loads of pick pair q; past the end (or no pick) they re-read valid rows
@@ -855,33 +861,21 @@ __device__ __forceinline__ void dec1_down_rows(const Dec1Params &p, int rblk, ui
         }
     };
 
+    // then the first pick pair's rows and the first two shared experts'
+    // rows (one if the rows are so wide that two would not fit the
+    // registers; a later one goes into the registers of the one just
+    // multiplied): a fixed number of loads, kAfter
     DnLoads ga, gb;
-    if (row_wave) load(ga, 0);
-    wait_h();
-    // stage the fp16 H of all picks (k * F * 2 bytes) and the shared
-    // activations after it (S * F * 4 bytes), one contiguous region, into
-    // LDS: every load of a round is issued before its stores
-    {
-        constexpr int NB = 16;
-        const int nt = (int)blockDim.x;
-        const int n16 = (k * F * 2 + S * F * 4) / 16;
-        const auto rh = brsrc(p.w.H, (uint32_t)n16 * 16);
-        for (int i0 = 0; i0 < n16; i0 += NB * nt) {
-            uint4 v[NB];
-#pragma unroll
-            for (int b = 0; b < NB; b++) {
-                const uint32_t i = (uint32_t)min(i0 + b * nt + (int)threadIdx.x, n16 - 1);
-                // (sc1: agent-coherent, for H written by other blocks of this kernel)
-                v[b] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(rh, (int)(i * 16), 0, COHERENT ? 16 : 0));
-            }
-            // (indexes past the end store the last piece again, same value)
-#pragma unroll
-            for (int b = 0; b < NB; b++)
-                *reinterpret_cast<uint4 *>(s_h + (size_t)min(i0 + b * nt + (int)threadIdx.x, n16 - 1) * 16) = v[b];
-        }
-    }
+    load(ga, 0);
+    constexpr int NSH = SHC <= 6 ? 2 : 1;
+    uint4 shw[NSH][kDnRows][SHC];
+    load_shd(shw[0], 0);
+    if constexpr (NSH > 1) load_shd(shw[NSH - 1], 1);
+    constexpr int kAfter = 2 * kDnRows * 4 + NSH * kDnRows * SHC;
+    static_assert(kAfter < 64, "vmcnt field");
+    // this wave's copies have landed once at most kAfter loads are in flight
+    __builtin_amdgcn_s_waitcnt((kAfter & 15) | ((kAfter >> 4) << 14) | (7 << 4) | (0xF << 8));
     __syncthreads();
-    if (!row_wave) return;
 
     // the shared rows
     float ysh[kDnRows];
@@ -989,8 +983,8 @@ __global__ __launch_bounds__(kDnWaves * 64) void k_dec1_down(Dec1Params p)
         __hip_atomic_store(p.w.ctl + kCtlEpoch, ep + 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     }
     __syncthreads();
-    // (H was written by the gate/up kernel, which has ended: nothing to wait for)
-    dec1_down_rows<SHC, false>(p, (int)blockIdx.x, s_h, s_e, s_w, [] {});
+    // (H was written by the gate/up kernel, which has ended)
+    dec1_down_rows<SHC>(p, (int)blockIdx.x, s_h, s_e, s_w);
 }
 
 // ---------------------------------------------------------------- host
@@ -1071,7 +1065,8 @@ hipError_t launch_decode1(const Shape &s, const uint16_t *x, const Weights &wt, 
 #undef MOE_DEC1_GU
     if (ev2) (void)hipEventRecord(ev2[0], stream);
     const int nd = (s.d + kDnBlockRows - 1) / kDnBlockRows;
-    const size_t lds = (size_t)s.k * s.F * 2 + (size_t)(p.shared ? s.S : 0) * s.F * 4;
+    // (whole KB: the staging copies write 1 KB each)
+    const size_t lds = (((size_t)s.k * s.F * 2 + (size_t)(p.shared ? s.S : 0) * s.F * 4) + 1023) & ~(size_t)1023;
     const int shd = (s.F / 8 + 63) / 64;  // 16-byte chunks per lane of a shared down row
     if (shd <= 2) k_dec1_down<2><<<nd, kDnWaves * 64, lds, stream>>>(p);
     else if (shd <= 4) k_dec1_down<4><<<nd, kDnWaves * 64, lds, stream>>>(p);
