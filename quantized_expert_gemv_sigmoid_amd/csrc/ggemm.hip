@@ -435,217 +435,254 @@ __device__ __forceinline__ void wave_pass(const GemmParams &p, const Blk &bk, in
         return lds_ld16(B + (cg * 64 + nb * 32 + col) * C::BCOL + ((pc ^ sb_) << 4));
     };
 
-    // multiply stage i, in ring slot sl.  mid() (the next stage's copies) is
-    // called once the stage's first fragment reads are issued, so that their
-    // latency covers the copies' issue
-    auto compute = [&](int i, int sl, auto &&mid) __attribute__((always_inline)) {
-        if constexpr (NTW == 0) {
-            mid();
-        } else if constexpr (MODE == M_G13) {
-            // Scaled MX MFMA (32x32x64, A fp8 e4m3, B fp4 e2m1).  In step stp
-            // (0, 1) of the stage, lane (col, kh) holds for each of its two
-            // columns MX block 2 stp + kh (K 64 stp + 32 kh .. + 31; B piece
-            // 2 stp + kh) with its E8M0 scale, and of its token row the 16-byte
-            // runs K 64 stp + 16 kh .. + 15 and 64 stp + 32 + 16 kh .. + 15
-            // (A pieces 4 stp + kh and 4 stp + 2 + kh; the lo term's 8 later):
-            // the A lanes' 32 elements interleave in 16s against a B lane's
-            // contiguous block (measured on gfx950).  The token rows have one
-            // E8M0 scale per term.  The hi and lo terms are two MFMAs into one
-            // sum.
+    // ---- the stages.  Stage i is multiplied in two halves around one
+    // barrier: its first half's operands (B pieces, scale bytes, the first
+    // half of K's A fragments) were read from LDS during stage i - 1
+    // (prefetch); the first half reads the second half's A fragments and
+    // multiplies; then the barrier (stage i + 1 has landed for every wave,
+    // and every wave has read all of stage i); then stage i + NST's copies
+    // into stage i's slot, the reads of stage i + 1's first-half operands,
+    // and the second half's MFMAs, whose operands are all in registers, so
+    // that the matrix cores work while the barrier's wait and the next reads
+    // are in flight.  Operand registers are single-buffered: the prefetch of
+    // stage i + 1 overwrites registers whose last reader, an MFMA or the
+    // scale masking of stage i, precedes it.
+    //  - G13: half = MFMA step (K 64); the prefetch takes step 0's hi-term A
+    //  - fp16 weights (D2, G13H): half = K 64 (the lane's MX block 0 or 1)
+    //  - bf16 weights (shared experts, router): half = steps 0-1 / 2-3
+    //  - SPLIT (exact fallback): the whole stage in the first half
+    constexpr int HS = STEPS / 2;  // MFMA steps per half (fp16 / bf16)
+    uint4 fq[2][2];                // B: [nb][block or step] pieces
+    uint32_t fs[2];                // scale bytes of the lane's two columns
+    typedef int i32x8_t __attribute__((ext_vector_type(8)));
+    i32x8_t ga[NTW > 0 ? NTW : 1];               // G13: step 0's hi-term A, [tile]
+    uint4 fa[HS][NTW > 0 ? NTW : 1];             // fp16 / bf16: first half's A, [step][tile]
+    uint4 fb[HS][2];                             // bf16: first half's B, [step][nb]
+
+    // G13: the step's A fragments of each term and tile.  Lane (col, kh)
+    // takes, of its token row, the 16-byte runs K 64 stp + 16 kh .. + 15 and
+    // 64 stp + 32 + 16 kh .. + 15 (A pieces 4 stp + kh and 4 stp + 2 + kh;
+    // the lo term's 8 later): the A lanes' 32 elements interleave in 16s
+    // against a B lane's contiguous MX block (measured on gfx950).
+    auto g_load = [&](const LDS uint8_t *A, i32x8_t (&at)[NTW > 0 ? NTW : 1], int stp, int tm) __attribute__((always_inline)) {
+#pragma unroll
+        for (int mt = 0; mt < NTW; mt++) {
+            const LDS uint8_t *arow = A + ((T0 + mt) * 32 + col) * AROW;
+            const int q0 = 4 * stp + kh + 8 * tm, q1 = q0 + 2;
+            const uint4 u0 = lds_ld16(arow + ((q0 ^ sa_) << 4));
+            const uint4 u1 = lds_ld16(arow + ((q1 ^ sa_) << 4));
+            at[mt] = (i32x8_t){(int)u0.x, (int)u0.y, (int)u0.z, (int)u0.w,
+                               (int)u1.x, (int)u1.y, (int)u1.z, (int)u1.w};
+        }
+    };
+    // the scale word(s) of the lane's two columns for stage sa: G13 all 4
+    // bytes (MX blocks 0..3 of the stage), fp16 weights the 2 bytes of
+    // half kh (blocks 2 kh, 2 kh + 1)
+    auto scale_word = [&](int sa, int nb) __attribute__((always_inline)) -> uint32_t {
+        const int R = s_row_of<MODE>(cg * 64 + nb * 32 + col);
+        const LDS uint8_t *p = scl + R * 128 + (((sa >> 2) ^ (R & 7)) << 4) + 4 * (sa & 3);
+        if constexpr (MODE == M_G13) return *reinterpret_cast<const LDS uint32_t *>(p);
+        else return *reinterpret_cast<const LDS uint16_t *>(p + 2 * kh);
+    };
+
+    // stage i's first-half operands, from ring slot sl
+    auto prefetch = [&](int i, int sl) __attribute__((always_inline)) {
+        if constexpr (NTW > 0 && !SPLIT) {
             const LDS uint8_t *A = ring + sl * RG::STAGE;
             const LDS uint8_t *B = A + RG::ABYTES;
             const int sa = i + bk.kst0;
-            typedef int i32x8_t __attribute__((ext_vector_type(8)));
-            uint4 q[2][2];
-            uint32_t s4[2];
-            int scb[2][2];
-            // the step's A fragments of each term and tile
-            auto a_load = [&](i32x8_t (&at)[2][NTW], int stp) __attribute__((always_inline)) {
-#pragma unroll
-                for (int mt = 0; mt < NTW; mt++) {
-                    const LDS uint8_t *arow = A + ((T0 + mt) * 32 + col) * AROW;
-                    const int q0 = 4 * stp + kh, q1 = q0 + 2;
-#pragma unroll
-                    for (int tm = 0; tm < 2; tm++) {
-                        const uint4 u0 = lds_ld16(arow + (((q0 + 8 * tm) ^ sa_) << 4));
-                        const uint4 u1 = lds_ld16(arow + (((q1 + 8 * tm) ^ sa_) << 4));
-                        at[tm][mt] = (i32x8_t){(int)u0.x, (int)u0.y, (int)u0.z, (int)u0.w,
-                                               (int)u1.x, (int)u1.y, (int)u1.z, (int)u1.w};
-                    }
-                }
-            };
-            // the stage's reads first: the 4 scale bytes of each column
-            // (blocks 0..3), its two MX blocks, step 0's A fragments
-#pragma unroll
-            for (int nb = 0; nb < 2; nb++) {
-                const int R = s_row_of<MODE>(cg * 64 + nb * 32 + col);
-                s4[nb] = *reinterpret_cast<const LDS uint32_t *>(
-                    scl + R * 128 + (((sa >> 2) ^ (R & 7)) << 4) + 4 * (sa & 3));
-#pragma unroll
-                for (int stp = 0; stp < 2; stp++) q[nb][stp] = b_piece(B, nb, 2 * stp + kh);
-            }
-            i32x8_t at0[2][NTW];
-            a_load(at0, 0);
-            mid();
-#pragma unroll
-            for (int nb = 0; nb < 2; nb++) {
-#pragma unroll
-                for (int stp = 0; stp < 2; stp++) {
-                    // NaN scale (255): the block contributes 0
-                    const uint32_t sc = (s4[nb] >> (8 * (2 * stp + kh))) & 0xffu;
-                    const uint32_t keep = sc == 255u ? 0u : ~0u;
-                    q[nb][stp].x &= keep; q[nb][stp].y &= keep; q[nb][stp].z &= keep; q[nb][stp].w &= keep;
-                    scb[nb][stp] = (int)(sc == 255u ? 127u : sc);
-                }
-            }
-            // (the MFMAs of a step run through all accumulators once per term,
-            // so that consecutive ones never depend on each other)
-#pragma unroll
-            for (int stp = 0; stp < 2; stp++) {
-                i32x8_t at1[2][NTW];
-                if (stp == 1) a_load(at1, 1);
-                auto &at = stp == 0 ? at0 : at1;
-#pragma unroll
-                for (int tm = 0; tm < 2; tm++)
-#pragma unroll
-                    for (int mt = 0; mt < NTW; mt++)
-#pragma unroll
-                        for (int nb = 0; nb < 2; nb++) {
-                            const uint4 bq = q[nb][stp];
-                            const i32x8_t bv = {(int)bq.x, (int)bq.y, (int)bq.z, (int)bq.w, 0, 0, 0, 0};
-                            // (the token row's scale register: hi term byte 0, lo term byte 1)
-                            if (tm == 0)
-                                acc[mt][nb] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(
-                                    at[0][mt], bv, acc[mt][nb], 0, 4, 0, (int)sca[mt], 0, scb[nb][stp]);
-                            else
-                                acc[mt][nb] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(
-                                    at[1][mt], bv, acc[mt][nb], 0, 4, 1, (int)sca[mt], 0, scb[nb][stp]);
-                        }
-            }
-        } else {
-            const LDS uint8_t *A = ring + sl * RG::STAGE;
-            const LDS uint8_t *B = A + RG::ABYTES;
-            uint4 af[2][NTW];
             if constexpr (C::kFp4) {
-                using BT = typename std::conditional<(MODE == M_D2 || MODE == M_G13H) && !SPLIT, f16x8_t, bf16x8_t>::type;
-                // this lane's two MX blocks (pieces 2 kh, 2 kh + 1) of each of its
-                // two columns, and their scale bytes (bytes 4 sa + 2 kh, + 1 of
-                // the column's scale row)
-                const int sa = i + bk.kst0;
-                uint4 q[2][2];
-                uint32_t s2[2];
-                float scf[2][2];
 #pragma unroll
                 for (int nb = 0; nb < 2; nb++) {
-                    q[nb][0] = b_piece(B, nb, 2 * kh);
-                    q[nb][1] = b_piece(B, nb, 2 * kh + 1);
-                    const int R = s_row_of<MODE>(cg * 64 + nb * 32 + col);
-                    s2[nb] = *reinterpret_cast<const LDS uint16_t *>(
-                        scl + R * 128 + (((sa >> 2) ^ (R & 7)) << 4) + 4 * (sa & 3) + 2 * kh);
+                    fs[nb] = scale_word(sa, nb);
+                    // G13: the two steps' blocks 2 stp + kh; fp16: blocks 2 kh, 2 kh + 1
+#pragma unroll
+                    for (int h = 0; h < 2; h++) fq[nb][h] = b_piece(B, nb, MODE == M_G13 ? 2 * h + kh : 2 * kh + h);
                 }
-                if constexpr (!SPLIT) {
-#pragma unroll
-                    for (int mt = 0; mt < NTW; mt++) af[0][mt] = a_frag(A, mt, 0);
-                }
-                mid();
-#pragma unroll
-                for (int nb = 0; nb < 2; nb++) {
-#pragma unroll
-                    for (int h = 0; h < 2; h++) {
-                        // NaN scale (255): the block contributes 0
-                        const uint32_t sc = (s2[nb] >> (8 * h)) & 0xffu;
-                        const uint32_t keep = sc == 255u ? 0u : ~0u;
-                        q[nb][h].x &= keep; q[nb][h].y &= keep; q[nb][h].z &= keep; q[nb][h].w &= keep;
-                        scf[nb][h] = e8m0f(sc == 255u ? 127u : sc);
-                    }
-                }
-                auto decode = [&](BT (&bb)[2], int st) __attribute__((always_inline)) {
-#pragma unroll
-                    for (int nb = 0; nb < 2; nb++) {
-                        const uint32_t w = u4at(q[nb][st >> 2], st & 3);
-                        if constexpr (std::is_same<BT, f16x8_t>::value) bb[nb] = cvt8_f16(w, scf[nb][st >> 2]);
-                        else bb[nb] = cvt8_bf16(w, scf[nb][st >> 2]);
-                    }
-                };
-                if constexpr (!SPLIT) {
-                    BT b[2][2];
-                    decode(b[0], 0);
-#pragma unroll
-                    for (int st = 0; st < STEPS; st++) {
-                        const int cur = st & 1, nxt = cur ^ 1;
-                        if (st + 1 < STEPS) {
-#pragma unroll
-                            for (int mt = 0; mt < NTW; mt++) af[nxt][mt] = a_frag(A, mt, st + 1);
-                            decode(b[nxt], st + 1);
-                        }
-#pragma unroll
-                        for (int mt = 0; mt < NTW; mt++)
-#pragma unroll
-                            for (int nb = 0; nb < 2; nb++)
-                                acc[mt][nb] = mfma32(__builtin_bit_cast(BT, af[cur][mt]), b[cur][nb], acc[mt][nb]);
-                    }
+                if constexpr (MODE == M_G13) {
+                    g_load(A, ga, 0, 0);
                 } else {
-                    // exact fallback: bf16 weights, fp16 inputs split in two bf16 parts
 #pragma unroll
-                    for (int st = 0; st < STEPS; st++) {
-                        bf16x8_t b[2];
-                        decode(b, st);
+                    for (int st = 0; st < HS; st++)
 #pragma unroll
-                        for (int mt = 0; mt < NTW; mt++) {
-                            bf16x8_t ah, al;
-                            split_f16(__builtin_bit_cast(f16x8_t, a_frag(A, mt, st)), ah, al);
-#pragma unroll
-                            for (int nb = 0; nb < 2; nb++) {
-                                acc[mt][nb] = mfma32(ah, b[nb], acc[mt][nb]);
-                                acc[mt][nb] = mfma32(al, b[nb], acc[mt][nb]);
-                            }
-                        }
-                    }
+                        for (int mt = 0; mt < NTW; mt++) fa[st][mt] = a_frag(A, mt, st);
                 }
             } else {
-                uint4 bf[2][2];
 #pragma unroll
-                for (int mt = 0; mt < NTW; mt++) af[0][mt] = a_frag(A, mt, 0);
+                for (int st = 0; st < HS; st++) {
 #pragma unroll
-                for (int nb = 0; nb < 2; nb++) bf[0][nb] = b_piece(B, nb, kh * STEPS);
-                mid();
+                    for (int nb = 0; nb < 2; nb++) fb[st][nb] = b_piece(B, nb, kh * STEPS + st);
 #pragma unroll
-                for (int st = 0; st < STEPS; st++) {
-                    const int cur = st & 1, nxt = cur ^ 1;
-                    if (st + 1 < STEPS) {
-#pragma unroll
-                        for (int mt = 0; mt < NTW; mt++) af[nxt][mt] = a_frag(A, mt, st + 1);
-#pragma unroll
-                        for (int nb = 0; nb < 2; nb++) bf[nxt][nb] = b_piece(B, nb, kh * STEPS + st + 1);
-                    }
-#pragma unroll
-                    for (int mt = 0; mt < NTW; mt++)
-#pragma unroll
-                        for (int nb = 0; nb < 2; nb++)
-                            acc[mt][nb] = mfma32(__builtin_bit_cast(bf16x8_t, af[cur][mt]),
-                                                 __builtin_bit_cast(bf16x8_t, bf[cur][nb]), acc[mt][nb]);
+                    for (int mt = 0; mt < NTW; mt++) fa[st][mt] = a_frag(A, mt, st);
                 }
             }
         }
     };
 
-    // ---- K loop: stage i's copies are issued at the top of iteration
-    // i - (NST - 1) (the prologue issues stages 0 .. NST - 2), so before
-    // stage i is multiplied the copies of the NST - 2 stages after it may
-    // still be in flight
-    constexpr int IN_FLIGHT = (NST - 2) * (RG::NA + RG::NB);
+    // the MXFP4 blocks of the prefetched B pieces with their scales: a NaN
+    // scale (255) makes the block contribute 0
+    uint4 qm[2][2];
+    int scb[2][2];     // G13: E8M0 scale operands [nb][step]
+    float scf[2][2];   // fp16: decode scales [nb][block]
+    auto mask_blocks = [&]() __attribute__((always_inline)) {
 #pragma unroll
-    for (int i = 0; i < NST - 1; i++) issue(i, i);
+        for (int nb = 0; nb < 2; nb++) {
+#pragma unroll
+            for (int h = 0; h < 2; h++) {
+                const uint32_t sc = MODE == M_G13 ? (fs[nb] >> (8 * (2 * h + kh))) & 0xffu : (fs[nb] >> (8 * h)) & 0xffu;
+                const uint32_t keep = sc == 255u ? 0u : ~0u;
+                qm[nb][h] = make_uint4(fq[nb][h].x & keep, fq[nb][h].y & keep, fq[nb][h].z & keep, fq[nb][h].w & keep);
+                if constexpr (MODE == M_G13) scb[nb][h] = (int)(sc == 255u ? 127u : sc);
+                else scf[nb][h] = e8m0f(sc == 255u ? 127u : sc);
+            }
+        }
+    };
+    // G13: the MFMAs of term tm of step stp, over all accumulators (the
+    // four of a term never depend on each other); the token row's scale
+    // register holds the hi term's byte in byte 0 and the lo term's in byte 1
+    auto g_mfma = [&](const i32x8_t (&at)[NTW > 0 ? NTW : 1], int stp, int tm) __attribute__((always_inline)) {
+#pragma unroll
+        for (int mt = 0; mt < NTW; mt++)
+#pragma unroll
+            for (int nb = 0; nb < 2; nb++) {
+                const uint4 bq = qm[nb][stp];
+                const i32x8_t bv = {(int)bq.x, (int)bq.y, (int)bq.z, (int)bq.w, 0, 0, 0, 0};
+                if (tm == 0)
+                    acc[mt][nb] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(
+                        at[mt], bv, acc[mt][nb], 0, 4, 0, (int)sca[mt], 0, scb[nb][stp]);
+                else
+                    acc[mt][nb] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(
+                        at[mt], bv, acc[mt][nb], 0, 4, 1, (int)sca[mt], 0, scb[nb][stp]);
+            }
+    };
+    using BT = typename std::conditional<(MODE == M_D2 || MODE == M_G13H) && !SPLIT, f16x8_t, bf16x8_t>::type;
+    // fp16 weights: steps h HS .. h HS + HS - 1 (MX block h of each column),
+    // each step's B decoded one step ahead of its MFMAs
+    auto f_half = [&](const uint4 (&av)[HS][NTW > 0 ? NTW : 1], int h) __attribute__((always_inline)) {
+        BT b[2][2];
+        auto decode = [&](BT (&bb)[2], int st) __attribute__((always_inline)) {
+#pragma unroll
+            for (int nb = 0; nb < 2; nb++) {
+                const uint32_t w = u4at(qm[nb][h], st);
+                if constexpr (std::is_same<BT, f16x8_t>::value) bb[nb] = cvt8_f16(w, scf[nb][h]);
+                else bb[nb] = cvt8_bf16(w, scf[nb][h]);
+            }
+        };
+        decode(b[0], 0);
+#pragma unroll
+        for (int st = 0; st < HS; st++) {
+            const int cur = st & 1, nxt = cur ^ 1;
+            if (st + 1 < HS) decode(b[nxt], st + 1);
+#pragma unroll
+            for (int mt = 0; mt < NTW; mt++)
+#pragma unroll
+                for (int nb = 0; nb < 2; nb++)
+                    acc[mt][nb] = mfma32(__builtin_bit_cast(BT, av[st][mt]), b[cur][nb], acc[mt][nb]);
+        }
+    };
+    auto b_half = [&](const uint4 (&av)[HS][NTW > 0 ? NTW : 1], const uint4 (&bv)[HS][2]) __attribute__((always_inline)) {
+#pragma unroll
+        for (int st = 0; st < HS; st++)
+#pragma unroll
+            for (int mt = 0; mt < NTW; mt++)
+#pragma unroll
+                for (int nb = 0; nb < 2; nb++)
+                    acc[mt][nb] = mfma32(__builtin_bit_cast(bf16x8_t, av[st][mt]),
+                                         __builtin_bit_cast(bf16x8_t, bv[st][nb]), acc[mt][nb]);
+    };
+
+    // ---- K loop.  The prologue issues stages 0 .. NST - 1 (every slot);
+    // stage i + NST's copies are issued after iteration i's barrier, into
+    // stage i's slot, so at that barrier the copies of the NST - 2 stages
+    // after stage i + 1 may still be in flight
+    constexpr int NPS = RG::NA + RG::NB;  // copies per wave per stage
+#pragma unroll
+    for (int i = 0; i < NST; i++) issue(i, i);
+    wait_vm<(NST - 1) * NPS>();
+    block_barrier();
+    prefetch(0, 0);
     int sl = 0;  // ring slot of stage i
     for (int i = 0; i < nS; i++) {
-        // this wave's copies of stage i have landed and its reads of stage
-        // i - 1 are done; after the barrier every wave's are, so the next
-        // copies may fill stage i - 1's slot
-        wait_vm<IN_FLIGHT>();
+        const int sln = sl == NST - 1 ? 0 : sl + 1;
+        const LDS uint8_t *A = ring + sl * RG::STAGE;
+        // -- first half (and the reads of the second half's A)
+        i32x8_t g0l[NTW > 0 ? NTW : 1], g1h[NTW > 0 ? NTW : 1], g1l[NTW > 0 ? NTW : 1];
+        uint4 a2[HS][NTW > 0 ? NTW : 1], b2[HS][2];
+        if constexpr (NTW > 0) {
+            if constexpr (MODE == M_G13) {
+                g_load(A, g0l, 0, 1);
+                g_load(A, g1h, 1, 0);
+                g_load(A, g1l, 1, 1);
+                mask_blocks();
+                g_mfma(ga, 0, 0);
+                g_mfma(g0l, 0, 1);
+            } else if constexpr (C::kFp4 && !SPLIT) {
+#pragma unroll
+                for (int st = 0; st < HS; st++)
+#pragma unroll
+                    for (int mt = 0; mt < NTW; mt++) a2[st][mt] = a_frag(A, mt, HS + st);
+                mask_blocks();
+                f_half(fa, 0);
+            } else if constexpr (C::kFp4) {
+                // exact fallback: bf16 weights, fp16 inputs split in two bf16
+                // parts, the whole stage here
+                const LDS uint8_t *B = A + RG::ABYTES;
+                const int sa = i + bk.kst0;
+#pragma unroll
+                for (int nb = 0; nb < 2; nb++) {
+                    fs[nb] = scale_word(sa, nb);
+#pragma unroll
+                    for (int h = 0; h < 2; h++) fq[nb][h] = b_piece(B, nb, 2 * kh + h);
+                }
+                mask_blocks();
+#pragma unroll
+                for (int st = 0; st < STEPS; st++) {
+                    bf16x8_t b[2];
+#pragma unroll
+                    for (int nb = 0; nb < 2; nb++) b[nb] = cvt8_bf16(u4at(qm[nb][st / HS], st % HS), scf[nb][st / HS]);
+#pragma unroll
+                    for (int mt = 0; mt < NTW; mt++) {
+                        bf16x8_t ah, al;
+                        split_f16(__builtin_bit_cast(f16x8_t, a_frag(A, mt, st)), ah, al);
+#pragma unroll
+                        for (int nb = 0; nb < 2; nb++) {
+                            acc[mt][nb] = mfma32(ah, b[nb], acc[mt][nb]);
+                            acc[mt][nb] = mfma32(al, b[nb], acc[mt][nb]);
+                        }
+                    }
+                }
+            } else {
+                const LDS uint8_t *B = A + RG::ABYTES;
+#pragma unroll
+                for (int st = 0; st < HS; st++) {
+#pragma unroll
+                    for (int nb = 0; nb < 2; nb++) b2[st][nb] = b_piece(B, nb, kh * STEPS + HS + st);
+#pragma unroll
+                    for (int mt = 0; mt < NTW; mt++) a2[st][mt] = a_frag(A, mt, HS + st);
+                }
+                b_half(fa, fb);
+            }
+        }
+        // -- stage i + 1 has landed for every wave, and every wave has read
+        // all of stage i: its slot takes stage i + NST.  (The scheduling
+        // fences keep the first half's MFMAs ahead of the wait; the last
+        // iteration's prefetch reads a slot no stage uses, and is not used.)
+        __builtin_amdgcn_sched_barrier(0);
+        wait_vm<(NST - 2) * NPS>();
         block_barrier();
-        const int nsl = sl == 0 ? NST - 1 : sl - 1;
-        compute(i, sl, [&] __attribute__((always_inline)) { issue(i + NST - 1, nsl); });
-        sl = sl == NST - 1 ? 0 : sl + 1;
+        __builtin_amdgcn_sched_barrier(0);
+        issue(i + NST, sl);
+        prefetch(i + 1 < nS ? i + 1 : i, sln);
+        // -- second half, from registers
+        if constexpr (NTW > 0) {
+            if constexpr (MODE == M_G13) {
+                g_mfma(g1h, 1, 0);
+                g_mfma(g1l, 1, 1);
+            }
+            else if constexpr (C::kFp4 && !SPLIT) f_half(a2, 1);
+            else if constexpr (!C::kFp4) b_half(a2, b2);
+        }
+        sl = sln;
     }
     // the ring is reused by the next pass: every copy (past-the-end ones
     // included) must have landed, and every wave be done reading
