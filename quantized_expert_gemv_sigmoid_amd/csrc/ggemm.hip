@@ -282,8 +282,8 @@ __device__ __forceinline__ void load_scales(const GemmParams &p, const Blk &b, L
 // pass's MT), all stages of K, then its epilogue.  Every wave of the block
 // issues its share of every stage's copies and meets every barrier, whatever
 // its NTW (0 included).
-template <int MODE, int MT, int NTW, int T0, bool SPLIT>
-__device__ __forceinline__ void wave_pass(const GemmParams &p, const Blk &bk, int m0, int mrows, LDS uint8_t *lds)
+template <int MODE, int MT, int NTW, int T0, bool SPLIT, int NB>
+__device__ __forceinline__ bool wave_pass(const GemmParams &p, const Blk &bk, int m0, int mrows, LDS uint8_t *lds, bool check)
 {
     using C = Cfg<MODE>;
     using RG = Ring<MODE, MT>;
@@ -292,6 +292,10 @@ __device__ __forceinline__ void wave_pass(const GemmParams &p, const Blk &bk, in
     const int lane = threadIdx.x & 63, wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int col = lane & 31, kh = lane >> 5;
     const int cg = wave & 3;  // the SIMD's column group
+    // the wave's 32-column tile nb (0 .. NB - 1) is the SIMD's column tile
+    // nb (NB = 2) or wave / 4 (NB = 1: the SIMD's two waves split the
+    // columns, each taking every row tile of the pass)
+    auto cn = [&](int nb) __attribute__((always_inline)) { return NB == 2 ? nb : (wave >> 2); };
     const int nS = bk.nS;
     LDS uint8_t *ring = lds + RG::BASE;
     const LDS uint8_t *scl = lds;  // (MXFP4) the block's scale rows
@@ -418,21 +422,20 @@ __device__ __forceinline__ void wave_pass(const GemmParams &p, const Blk &bk, in
         }
     }
 
-    f32x16_t acc[NTW > 0 ? NTW : 1][2];
+    f32x16_t acc[NTW > 0 ? NTW : 1][NB];
 #pragma unroll
-    for (int i = 0; i < (NTW > 0 ? NTW : 1); i++) {
-        acc[i][0] = (f32x16_t)0.0f;
-        acc[i][1] = (f32x16_t)0.0f;
-    }
+    for (int i = 0; i < (NTW > 0 ? NTW : 1); i++)
+#pragma unroll
+        for (int nb = 0; nb < NB; nb++) acc[i][nb] = (f32x16_t)0.0f;
 
     const int sa_ = swz_a<MODE>(col), sb_ = swz_b<MODE>(col);
     // A fragment of pass tile T0 + mt, step st: row (T0 + mt) * 32 + col, piece kh * STEPS + st
     auto a_frag = [&](const LDS uint8_t *A, int mt, int st) __attribute__((always_inline)) -> uint4 {
         return lds_ld16(A + ((T0 + mt) * 32 + col) * AROW + (((kh * STEPS + st) ^ sa_) << 4));
     };
-    // B column of this lane for nb (0, 1): block column 64 cg + 32 nb + col
+    // B column of this lane for nb: block column 64 cg + 32 cn(nb) + col
     auto b_piece = [&](const LDS uint8_t *B, int nb, int pc) __attribute__((always_inline)) -> uint4 {
-        return lds_ld16(B + (cg * 64 + nb * 32 + col) * C::BCOL + ((pc ^ sb_) << 4));
+        return lds_ld16(B + (cg * 64 + cn(nb) * 32 + col) * C::BCOL + ((pc ^ sb_) << 4));
     };
 
     // ---- the stages.  Stage i is multiplied in two halves around one
@@ -452,12 +455,12 @@ __device__ __forceinline__ void wave_pass(const GemmParams &p, const Blk &bk, in
     //  - bf16 weights (shared experts, router): half = steps 0-1 / 2-3
     //  - SPLIT (exact fallback): the whole stage in the first half
     constexpr int HS = STEPS / 2;  // MFMA steps per half (fp16 / bf16)
-    uint4 fq[2][2];                // B: [nb][block or step] pieces
-    uint32_t fs[2];                // scale bytes of the lane's two columns
+    uint4 fq[NB][2];               // B: [nb][block or step] pieces
+    uint32_t fs[NB];               // scale bytes of the lane's columns
     typedef int i32x8_t __attribute__((ext_vector_type(8)));
     i32x8_t ga[NTW > 0 ? NTW : 1];               // G13: step 0's hi-term A, [tile]
     uint4 fa[HS][NTW > 0 ? NTW : 1];             // fp16 / bf16: first half's A, [step][tile]
-    uint4 fb[HS][2];                             // bf16: first half's B, [step][nb]
+    uint4 fb[HS][NB];                            // bf16: first half's B, [step][nb]
 
     // G13: the step's A fragments of each term and tile.  Lane (col, kh)
     // takes, of its token row, the 16-byte runs K 64 stp + 16 kh .. + 15 and
@@ -479,7 +482,7 @@ __device__ __forceinline__ void wave_pass(const GemmParams &p, const Blk &bk, in
     // bytes (MX blocks 0..3 of the stage), fp16 weights the 2 bytes of
     // half kh (blocks 2 kh, 2 kh + 1)
     auto scale_word = [&](int sa, int nb) __attribute__((always_inline)) -> uint32_t {
-        const int R = s_row_of<MODE>(cg * 64 + nb * 32 + col);
+        const int R = s_row_of<MODE>(cg * 64 + cn(nb) * 32 + col);
         const LDS uint8_t *p = scl + R * 128 + (((sa >> 2) ^ (R & 7)) << 4) + 4 * (sa & 3);
         if constexpr (MODE == M_G13) return *reinterpret_cast<const LDS uint32_t *>(p);
         else return *reinterpret_cast<const LDS uint16_t *>(p + 2 * kh);
@@ -493,7 +496,7 @@ __device__ __forceinline__ void wave_pass(const GemmParams &p, const Blk &bk, in
             const int sa = i + bk.kst0;
             if constexpr (C::kFp4) {
 #pragma unroll
-                for (int nb = 0; nb < 2; nb++) {
+                for (int nb = 0; nb < NB; nb++) {
                     fs[nb] = scale_word(sa, nb);
                     // G13: the two steps' blocks 2 stp + kh; fp16: blocks 2 kh, 2 kh + 1
 #pragma unroll
@@ -511,7 +514,7 @@ __device__ __forceinline__ void wave_pass(const GemmParams &p, const Blk &bk, in
 #pragma unroll
                 for (int st = 0; st < HS; st++) {
 #pragma unroll
-                    for (int nb = 0; nb < 2; nb++) fb[st][nb] = b_piece(B, nb, kh * STEPS + st);
+                    for (int nb = 0; nb < NB; nb++) fb[st][nb] = b_piece(B, nb, kh * STEPS + st);
 #pragma unroll
                     for (int mt = 0; mt < NTW; mt++) fa[st][mt] = a_frag(A, mt, st);
                 }
@@ -521,12 +524,12 @@ __device__ __forceinline__ void wave_pass(const GemmParams &p, const Blk &bk, in
 
     // the MXFP4 blocks of the prefetched B pieces with their scales: a NaN
     // scale (255) makes the block contribute 0
-    uint4 qm[2][2];
-    int scb[2][2];     // G13: E8M0 scale operands [nb][step]
-    float scf[2][2];   // fp16: decode scales [nb][block]
+    uint4 qm[NB][2];
+    int scb[NB][2];     // G13: E8M0 scale operands [nb][step]
+    float scf[NB][2];   // fp16: decode scales [nb][block]
     auto mask_blocks = [&]() __attribute__((always_inline)) {
 #pragma unroll
-        for (int nb = 0; nb < 2; nb++) {
+        for (int nb = 0; nb < NB; nb++) {
 #pragma unroll
             for (int h = 0; h < 2; h++) {
                 const uint32_t sc = MODE == M_G13 ? (fs[nb] >> (8 * (2 * h + kh))) & 0xffu : (fs[nb] >> (8 * h)) & 0xffu;
@@ -544,7 +547,7 @@ __device__ __forceinline__ void wave_pass(const GemmParams &p, const Blk &bk, in
 #pragma unroll
         for (int mt = 0; mt < NTW; mt++)
 #pragma unroll
-            for (int nb = 0; nb < 2; nb++) {
+            for (int nb = 0; nb < NB; nb++) {
                 const uint4 bq = qm[nb][stp];
                 const i32x8_t bv = {(int)bq.x, (int)bq.y, (int)bq.z, (int)bq.w, 0, 0, 0, 0};
                 if (tm == 0)
@@ -559,10 +562,10 @@ __device__ __forceinline__ void wave_pass(const GemmParams &p, const Blk &bk, in
     // fp16 weights: steps h HS .. h HS + HS - 1 (MX block h of each column),
     // each step's B decoded one step ahead of its MFMAs
     auto f_half = [&](const uint4 (&av)[HS][NTW > 0 ? NTW : 1], int h) __attribute__((always_inline)) {
-        BT b[2][2];
-        auto decode = [&](BT (&bb)[2], int st) __attribute__((always_inline)) {
+        BT b[2][NB];
+        auto decode = [&](BT (&bb)[NB], int st) __attribute__((always_inline)) {
 #pragma unroll
-            for (int nb = 0; nb < 2; nb++) {
+            for (int nb = 0; nb < NB; nb++) {
                 const uint32_t w = u4at(qm[nb][h], st);
                 if constexpr (std::is_same<BT, f16x8_t>::value) bb[nb] = cvt8_f16(w, scf[nb][h]);
                 else bb[nb] = cvt8_bf16(w, scf[nb][h]);
@@ -576,17 +579,17 @@ __device__ __forceinline__ void wave_pass(const GemmParams &p, const Blk &bk, in
 #pragma unroll
             for (int mt = 0; mt < NTW; mt++)
 #pragma unroll
-                for (int nb = 0; nb < 2; nb++)
+                for (int nb = 0; nb < NB; nb++)
                     acc[mt][nb] = mfma32(__builtin_bit_cast(BT, av[st][mt]), b[cur][nb], acc[mt][nb]);
         }
     };
-    auto b_half = [&](const uint4 (&av)[HS][NTW > 0 ? NTW : 1], const uint4 (&bv)[HS][2]) __attribute__((always_inline)) {
+    auto b_half = [&](const uint4 (&av)[HS][NTW > 0 ? NTW : 1], const uint4 (&bv)[HS][NB]) __attribute__((always_inline)) {
 #pragma unroll
         for (int st = 0; st < HS; st++)
 #pragma unroll
             for (int mt = 0; mt < NTW; mt++)
 #pragma unroll
-                for (int nb = 0; nb < 2; nb++)
+                for (int nb = 0; nb < NB; nb++)
                     acc[mt][nb] = mfma32(__builtin_bit_cast(bf16x8_t, av[st][mt]),
                                          __builtin_bit_cast(bf16x8_t, bv[st][nb]), acc[mt][nb]);
     };
@@ -600,6 +603,33 @@ __device__ __forceinline__ void wave_pass(const GemmParams &p, const Blk &bk, in
     for (int i = 0; i < NST; i++) issue(i, i);
     wait_vm<(NST - 1) * NPS>();
     block_barrier();
+    if constexpr ((MODE == M_D2 || MODE == M_G13H) && !SPLIT) {
+        // (the scale rows landed with stage 0's copies, which followed
+        // them): thread t checks scale row t; on a byte outside the fp16
+        // window the stages in flight are drained and the caller takes the
+        // split path
+        if (check) {
+            bool ok = true;
+            if (threadIdx.x < GN) {
+                const int R = threadIdx.x;
+                const int nbytes = (MODE == M_D2 ? s.F : s.d) / 32;
+                for (int q = 0; q * 16 < nbytes; q++) {
+                    const uint4 v = lds_ld16(scl + R * 128 + ((q ^ (R & 7)) << 4));
+                    const uint32_t w[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+                    for (int k = 0; k < 16; k++) {
+                        const uint32_t by = (w[k >> 2] >> (8 * (k & 3))) & 0xffu;
+                        ok = ok && (q * 16 + k >= nbytes || by == 255u || (by - 104u) <= 36u);
+                    }
+                }
+            }
+            if (!__syncthreads_and(ok)) {
+                wait_vm<0>();
+                block_barrier();
+                return false;
+            }
+        }
+    }
     prefetch(0, 0);
     int sl = 0;  // ring slot of stage i
     for (int i = 0; i < nS; i++) {
@@ -607,7 +637,7 @@ __device__ __forceinline__ void wave_pass(const GemmParams &p, const Blk &bk, in
         const LDS uint8_t *A = ring + sl * RG::STAGE;
         // -- first half (and the reads of the second half's A)
         i32x8_t g0l[NTW > 0 ? NTW : 1], g1h[NTW > 0 ? NTW : 1], g1l[NTW > 0 ? NTW : 1];
-        uint4 a2[HS][NTW > 0 ? NTW : 1], b2[HS][2];
+        uint4 a2[HS][NTW > 0 ? NTW : 1], b2[HS][NB];
         if constexpr (NTW > 0) {
             if constexpr (MODE == M_G13) {
                 g_load(A, g0l, 0, 1);
@@ -629,7 +659,7 @@ __device__ __forceinline__ void wave_pass(const GemmParams &p, const Blk &bk, in
                 const LDS uint8_t *B = A + RG::ABYTES;
                 const int sa = i + bk.kst0;
 #pragma unroll
-                for (int nb = 0; nb < 2; nb++) {
+                for (int nb = 0; nb < NB; nb++) {
                     fs[nb] = scale_word(sa, nb);
 #pragma unroll
                     for (int h = 0; h < 2; h++) fq[nb][h] = b_piece(B, nb, 2 * kh + h);
@@ -637,15 +667,15 @@ __device__ __forceinline__ void wave_pass(const GemmParams &p, const Blk &bk, in
                 mask_blocks();
 #pragma unroll
                 for (int st = 0; st < STEPS; st++) {
-                    bf16x8_t b[2];
+                    bf16x8_t b[NB];
 #pragma unroll
-                    for (int nb = 0; nb < 2; nb++) b[nb] = cvt8_bf16(u4at(qm[nb][st / HS], st % HS), scf[nb][st / HS]);
+                    for (int nb = 0; nb < NB; nb++) b[nb] = cvt8_bf16(u4at(qm[nb][st / HS], st % HS), scf[nb][st / HS]);
 #pragma unroll
                     for (int mt = 0; mt < NTW; mt++) {
                         bf16x8_t ah, al;
                         split_f16(__builtin_bit_cast(f16x8_t, a_frag(A, mt, st)), ah, al);
 #pragma unroll
-                        for (int nb = 0; nb < 2; nb++) {
+                        for (int nb = 0; nb < NB; nb++) {
                             acc[mt][nb] = mfma32(ah, b[nb], acc[mt][nb]);
                             acc[mt][nb] = mfma32(al, b[nb], acc[mt][nb]);
                         }
@@ -656,7 +686,7 @@ __device__ __forceinline__ void wave_pass(const GemmParams &p, const Blk &bk, in
 #pragma unroll
                 for (int st = 0; st < HS; st++) {
 #pragma unroll
-                    for (int nb = 0; nb < 2; nb++) b2[st][nb] = b_piece(B, nb, kh * STEPS + HS + st);
+                    for (int nb = 0; nb < NB; nb++) b2[st][nb] = b_piece(B, nb, kh * STEPS + HS + st);
 #pragma unroll
                     for (int mt = 0; mt < NTW; mt++) a2[st][mt] = a_frag(A, mt, HS + st);
                 }
@@ -694,6 +724,7 @@ __device__ __forceinline__ void wave_pass(const GemmParams &p, const Blk &bk, in
         // 8 (e / 4) + 4 kh + e % 4 of the tile, column nb * 32 + col of the
         // SIMD's 64)
         if constexpr (C::kGated) {
+            static_assert(NB == 2, "a gated tile's gate and up columns sit in one wave");
             // the activations first, all of them and without a branch (one
             // copy per activation, chosen once), so that the exp / rcp chains
             // of different values interleave; then the stores of the rows in
@@ -747,11 +778,16 @@ __device__ __forceinline__ void wave_pass(const GemmParams &p, const Blk &bk, in
                 }
             }
         } else {
-            // (down projection: lane i holds the routing weight of the wave's
-            // row 32 T0 + i, loaded once; a row's weight comes by a lane
-            // shuffle.  Rows past the group read its last row's.)
-            float wl = 1.0f;
-            if constexpr (MODE == M_D2) wl = p.w.pos_w[bk.base + m0 + min(T0 * 32 + lane, mrows - 1)];
+            // (down projection: lane i holds the routing weights of the wave's
+            // rows 32 T0 + i and 32 T0 + 64 + i, loaded once; a row's weight
+            // comes by a lane shuffle.  Rows past the group read its last
+            // row's.)
+            float wl[2] = {1.0f, 1.0f};
+            if constexpr (MODE == M_D2) {
+#pragma unroll
+                for (int h = 0; h < (NTW > 2 ? 2 : 1); h++)
+                    wl[h] = p.w.pos_w[bk.base + m0 + min(T0 * 32 + 64 * h + lane, mrows - 1)];
+            }
 #pragma unroll
             for (int mt = 0; mt < NTW; mt++) {
 #pragma unroll
@@ -759,12 +795,12 @@ __device__ __forceinline__ void wave_pass(const GemmParams &p, const Blk &bk, in
                     const int rl = mt * 32 + 8 * (e >> 2) + 4 * kh + (e & 3);  // row of the wave's tiles
                     const int r = T0 * 32 + rl;
                     float wrow = 1.0f;
-                    if constexpr (MODE == M_D2) wrow = __shfl(wl, rl, 64);
+                    if constexpr (MODE == M_D2) wrow = __shfl(wl[rl >> 6], rl & 63, 64);
                     if (r >= mrows) continue;
                     const int m = m0 + r;
 #pragma unroll
-                    for (int nb = 0; nb < 2; nb++) {
-                        const int n = bk.tile * GN + cg * 64 + nb * 32 + col;
+                    for (int nb = 0; nb < NB; nb++) {
+                        const int n = bk.tile * GN + cg * 64 + cn(nb) * 32 + col;
                         if (n >= bk.ncols) continue;
                         const float v = acc[mt][nb][e];
                         if constexpr (MODE == M_D2) p.w.Y[(size_t)(bk.base + m) * s.d + n] = v * wrow;
@@ -776,16 +812,25 @@ __device__ __forceinline__ void wave_pass(const GemmParams &p, const Blk &bk, in
             }
         }
     }
+    return true;
 }
 
-// One M pass of MT 32-row tiles (rows m0 .. m0 + mrows - 1 of the group):
-// the two waves of a SIMD take the first (MT + 1) / 2 tiles and the rest.
+// One M pass of MT 32-row tiles (rows m0 .. m0 + mrows - 1 of the group).
+// The two waves of a SIMD take the first (MT + 1) / 2 tiles and the rest,
+// both column tiles (a gated tile's gate and up columns are then in one
+// wave); in the routed down projection each wave instead takes every row
+// tile and one of the SIMD's two column tiles, so that the waves' MFMA work
+// is equal and each B column is decoded once.
 template <int MODE, int MT, bool SPLIT = false>
-__device__ __forceinline__ void gemm_pass(const GemmParams &p, const Blk &bk, int m0, int mrows, LDS uint8_t *lds)
+__device__ __forceinline__ bool gemm_pass(const GemmParams &p, const Blk &bk, int m0, int mrows, LDS uint8_t *lds, bool check)
 {
-    constexpr int N0 = (MT + 1) / 2, N1 = MT / 2;
-    if (__builtin_amdgcn_readfirstlane(threadIdx.x >> 6) < 4) wave_pass<MODE, MT, N0, 0, SPLIT>(p, bk, m0, mrows, lds);
-    else wave_pass<MODE, MT, N1, N0, SPLIT>(p, bk, m0, mrows, lds);
+    if constexpr (MODE != M_D2) {
+        constexpr int N0 = (MT + 1) / 2, N1 = MT / 2;
+        if (__builtin_amdgcn_readfirstlane(threadIdx.x >> 6) < 4) return wave_pass<MODE, MT, N0, 0, SPLIT, 2>(p, bk, m0, mrows, lds, check);
+        return wave_pass<MODE, MT, N1, N0, SPLIT, 2>(p, bk, m0, mrows, lds, check);
+    } else {
+        return wave_pass<MODE, MT, MT, 0, SPLIT, 1>(p, bk, m0, mrows, lds, check);
+    }
 }
 
 template <int MODE>
@@ -842,53 +887,33 @@ __global__ __launch_bounds__(GT) void k_ggemm(GemmParams p)
     // barrier cover them: the copies land in order)
     if constexpr (C::kFp4) load_scales<MODE>(p, b, ring);
 
-    if constexpr (MODE == M_D2 || MODE == M_G13H) {
-        // The down projection multiplies fp16 H by W2 decoded to fp16 (G13H:
-        // the fp16 input rows by W1 / W3 decoded to fp16), which is exact
-        // for scale bytes 104..140 (and 255, which decodes to 0).  A block
-        // whose weight scales leave that range takes the exact split path
-        // (bf16 weights, the fp16 operand split into two bf16 parts) for all
-        // its rows.
-        bool ok = true;
-        if (threadIdx.x < GN) {
-            const int K = MODE == M_D2 ? s.F : s.d;
-            const uint8_t *sc;
-            if constexpr (MODE == M_D2) {
-                sc = p.w2s + ((size_t)b.e * s.d + b.tile * GN + threadIdx.x) * (K / 32);
-            } else {
-                const uint8_t *m = threadIdx.x < 128 ? p.w1s : p.w3s;
-                sc = m + ((size_t)b.e * s.F + min(b.tile * 128 + (int)(threadIdx.x & 127), s.F - 1)) * (K / 32);
-            }
-            for (int i = 0; i < K / 32; i += 4) {
-                const uint32_t v = *reinterpret_cast<const uint32_t *>(sc + i);
-#pragma unroll
-                for (int k = 0; k < 4; k++) {
-                    const uint32_t by = (v >> (8 * k)) & 0xffu;
-                    ok = ok && (by == 255u || (by - 104u) <= 36u);
-                }
-            }
-        }
-        if (!__syncthreads_and(ok)) {
-            // (64-row passes: this rare path then needs few registers)
-            for (int m0 = 0; m0 < b.M; m0 += 64) gemm_pass<MODE, 2, true>(p, b, m0, min(64, b.M - m0), ring);
-            return;
-        }
-    }
     if constexpr (C::kFp4) {
-        // routed experts: all of the group's rows, in passes of up to 32 GMT4
-        for (int m0 = 0; m0 < b.M; m0 += 32 * GMT4) {
+        // routed experts: all of the group's rows, in passes of up to 32 GMT4.
+        // D2 / G13H multiply fp16 operands by weights decoded to fp16, exact
+        // for scale bytes 104..140 (and 255, which decodes to 0): the first
+        // pass checks the block's scale rows once they are in LDS, and a
+        // block whose scales leave that range takes the exact split path
+        // (bf16 weights, the fp16 operand split into two bf16 parts) for all
+        // its rows, in 64-row passes (this rare path then needs few
+        // registers).
+        bool fast = true;
+        for (int m0 = 0; m0 < b.M && fast; m0 += 32 * GMT4) {
             const int mrows = min(32 * GMT4, b.M - m0);
             switch ((mrows + 31) >> 5) {
-            case 1: gemm_pass<MODE, 1>(p, b, m0, mrows, ring); break;
-            case 2: gemm_pass<MODE, 2>(p, b, m0, mrows, ring); break;
-            default: gemm_pass<MODE, 3>(p, b, m0, mrows, ring); break;
+            case 1: fast = gemm_pass<MODE, 1>(p, b, m0, mrows, ring, m0 == 0); break;
+            case 2: fast = gemm_pass<MODE, 2>(p, b, m0, mrows, ring, m0 == 0); break;
+            default: fast = gemm_pass<MODE, 3>(p, b, m0, mrows, ring, m0 == 0); break;
             }
+        }
+        if constexpr (MODE == M_D2 || MODE == M_G13H) {
+            if (!fast)
+                for (int m0 = 0; m0 < b.M; m0 += 64) gemm_pass<MODE, 2, true>(p, b, m0, min(64, b.M - m0), ring, false);
         }
     } else {
         // shared experts / router: one pass of GM rows per block (rows past
         // the end read nothing and are never stored)
         const int m0 = b.mb * GM;
-        if (m0 < b.M) gemm_pass<MODE, GMT>(p, b, m0, min(GM, b.M - m0), ring);
+        if (m0 < b.M) gemm_pass<MODE, GMT>(p, b, m0, min(GM, b.M - m0), ring, false);
     }
 }
 
