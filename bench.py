@@ -51,13 +51,13 @@ DTYPE_DETAIL = ("routed weights MXFP4 (E2M1 + E8M0 per 32), decoded exactly to b
                 "(fp32 H) on the GEMV path; shared experts bf16; router fp32; every sum fp32; outputs bf16 "
                 "(round to nearest even of the fp32 sum)")
 PHASES = ("router_logits", "topk_dispatch", "expert_gate_up", "expert_down", "combine")
-# kernels of each phase, per path: the fused one-token path (top-k, dispatch
-# and combine folded into the expert kernels), the GEMV path (small T), the
-# MFMA path (grouped GEMM over expert-sorted tokens)
+# kernels of each phase, per path: the one-token path (one launch: router,
+# top-k, gate/up, down and combine in k_dec1_fused), the GEMV path (small T),
+# the MFMA path (grouped GEMM over expert-sorted tokens)
 KERNELS = {
-    "decode1": {"router_logits": "- (in k_dec1_gateup)", "topk_dispatch": "- (in k_dec1_gateup)",
-                "expert_gate_up": "k_dec1_gateup (router + top-k + shared and routed gate/up)",
-                "expert_down": "k_dec1_down (shared and routed down + combine)", "combine": "-"},
+    "decode1": {"router_logits": "- (in k_dec1_fused)", "topk_dispatch": "- (in k_dec1_fused)",
+                "expert_gate_up": "k_dec1_fused (router + top-k + shared and routed gate/up, down, combine)",
+                "expert_down": "- (in k_dec1_fused)", "combine": "-"},
     "gemv": {"router_logits": "k_front", "topk_dispatch": "k_dispatch_small/k_topk+k_dispatch_*",
              "expert_gate_up": "k_gemv_gateup", "expert_down": "k_gemv_down", "combine": "k_combine"},
     "mfma": {"router_logits": "k_split_router + k_ggemm<M_R>", "topk_dispatch": "k_topk + k_dispatch_*",
@@ -89,8 +89,6 @@ WINDOWS = 3
 # The summaries and the commands are in profiles/moe_layer_kernels__k3-moe-decode-T1.md
 # and profiles/latent_kernels__k3-latent-moe-decode-T1.md.
 MEASURED_TRAFFIC = {
-    "k_dec1_gateup": {"bytes": 289326029, "source": "decode1.hip", "sha": "570544b9dbb5dcbf"},
-    "k_dec1_down": {"bytes": 139091304, "source": "decode1.hip", "sha": "570544b9dbb5dcbf"},
     "k_latent_front": {"bytes": 253999253, "source": "latent.hip", "sha": "bae8c0c78d423e41"},
     "k_latent_out": {"bytes": 140118160, "source": "latent.hip", "sha": "bae8c0c78d423e41"},
     "k_gemv_gateup": {"bytes": 187593528, "source": "gemv.hip", "sha": "f5aeda5727b5bb2d"},
@@ -117,9 +115,8 @@ def measured_traffic(kernel: str):
 def phase_bytes(shape, T, counts, kind):
     """Algorithmic HBM bytes of each phase for one step (every touched expert
     read once; shared, router, tokens and outputs once; workspace excluded).
-    On the fused one-token path the router and the shared experts' gate/up
-    run in the gate/up kernel and the shared experts' down in the down
-    kernel."""
+    The one-token path is one kernel: all of its bytes count in the gate/up
+    phase, whose events enclose it."""
     d, F, S, E, k = shape.d_model, shape.d_ffn, shape.n_shared, shape.n_experts, shape.top_k
     active = int((counts > 0).sum())
     w13 = 2 * (F * d // 2 + F * d // 32)
@@ -127,8 +124,8 @@ def phase_bytes(shape, T, counts, kind):
     sh13, sh2 = S * 2 * F * d * 2, S * d * F * 2
     if kind == "decode1":
         return {"router_logits": 0, "topk_dispatch": 0,
-                "expert_gate_up": E * d * 4 + sh13 + active * w13 + T * d * 2,
-                "expert_down": active * w2 + sh2 + T * d * 2, "combine": 0}
+                "expert_gate_up": E * d * 4 + sh13 + active * w13 + active * w2 + sh2 + 2 * T * d * 2,
+                "expert_down": 0, "combine": 0}
     return {
         "router_logits": E * d * 4 + T * d * 2,
         "topk_dispatch": 0,

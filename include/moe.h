@@ -104,13 +104,14 @@ typedef struct {
 /* Workspace bytes a call with up to max_tokens tokens needs (0 if the
  * descriptor is invalid or unsupported).  Pass a buffer of at least this
  * size, 256-byte aligned, to the calls below.  Its contents need no
- * initialisation and carry nothing a caller reads.  (The one-token kernels
- * hand the router logits between their blocks through slots at the start of
- * the workspace, each tagged with the call's epoch, a counter kept there
- * that every call advances; a slot counts only with the running call's tag.
- * Slots earlier calls left never carry it, and other contents carry it only
- * by a coincidence of 1 in 2^32 per slot, so the workspace may start with
- * any bytes.) */
+ * initialisation and carry nothing a caller reads.  (The one-token kernel
+ * hands the router logits, and the signals that a block's activations are
+ * stored, between its blocks through slots at the start of the workspace,
+ * each tagged with the call's epoch, a counter kept there that every call
+ * advances; a slot counts only with the running call's tag.  Slots earlier
+ * calls left never carry it, and other contents carry it only by a
+ * coincidence of 1 in 2^32 per slot, so the workspace may start with any
+ * bytes.) */
 size_t moe_workspace_bytes(const moe_layer_desc *desc, int32_t max_tokens);
 
 /* The expert path (MOE_PATH_GEMV or MOE_PATH_MFMA) a call with T tokens
@@ -190,11 +191,12 @@ moe_status moe_layer_timed(const moe_layer_desc *desc, const uint16_t *x, int32_
                            uint16_t *out_bf16, float *out_f32, int32_t out_mode,
                            void *ws, size_t ws_bytes, void *stream, void *const *events);
 
-/* The one-token kernels' router hand-off: a block that has waited this many
- * microseconds for router logits other blocks compute (default 50) computes
- * the missing ones itself, the same sums, so the same bits; no wait depends
- * on another block being resident.  Process-wide; it applies to calls
- * enqueued after it returns (a captured graph keeps the value it was
+/* The one-token kernel's hand-offs between its blocks: a block that has
+ * waited this many microseconds (default 50) for router logits other blocks
+ * compute, or four times as long for another block's stored activations,
+ * computes the missing ones itself, the same sums, so the same bits; no wait
+ * depends on another block being resident.  Process-wide; it applies to
+ * calls enqueued after it returns (a captured graph keeps the value it was
  * captured with).  MOE_EINVAL for a negative value. */
 moe_status moe_set_one_token_router_wait(int32_t microseconds);
 

@@ -18,12 +18,12 @@ constexpr int kMaxExperts = 1024;  // router top-k keeps E/64 scores per lane
 constexpr int kMaxTopK = 64;
 constexpr int kMaxDim = 4096;      // d and F: GEMV lanes hold <= 2 MXFP4 blocks
 constexpr int kMaxShared = 8;
-constexpr size_t kWsControlBytes = 9 * 1024;  // workspace bytes [0, this): the one-token control block
+constexpr size_t kWsControlBytes = 13 * 1024;  // workspace bytes [0, this): the one-token control block
 constexpr int kDispatchTokens = 64;  // tokens per dispatch block (one 64-bit mask)
 
 // Device views of the workspace of one call (see carve_workspace).
 struct Work {
-    int32_t *ctl;      // control block of the one-token path (kWsControlBytes: router slots, epoch)
+    int32_t *ctl;      // control block of the one-token path (kWsControlBytes: router slots, epoch, block tags)
     float *logits;     // [T][E]  router logits
     int32_t *ids;      // [T][k]  routing (when the caller passed none)
     float *wts;        // [T][k]
@@ -384,6 +384,17 @@ __device__ __forceinline__ void gbld16_lds(__amdgpu_buffer_rsrc_t r, LDS uint8_t
     const uint32_t m0v = (uint32_t)(uintptr_t)dst;
     uint32_t save;
     asm volatile("s_mov_b32 %0, m0\n\ts_mov_b32 m0, %1\n\tbuffer_load_dwordx4 %2, %3, 0 offen lds\n\ts_mov_b32 m0, %0"
+                 : "=&s"(save)
+                 : "s"(m0v), "v"(voff), "s"(r)
+                 : "memory");
+}
+// the same copy, system coherent (sc0 sc1: served past the XCD's L2, so it
+// sees data another XCD wrote back)
+__device__ __forceinline__ void gbld16_lds_sys(__amdgpu_buffer_rsrc_t r, LDS uint8_t *dst, uint32_t voff)
+{
+    const uint32_t m0v = (uint32_t)(uintptr_t)dst;
+    uint32_t save;
+    asm volatile("s_mov_b32 %0, m0\n\ts_mov_b32 m0, %1\n\tbuffer_load_dwordx4 %2, %3, 0 offen sc0 sc1 lds\n\ts_mov_b32 m0, %0"
                  : "=&s"(save)
                  : "s"(m0v), "v"(voff), "s"(r)
                  : "memory");

@@ -1,26 +1,33 @@
-// Fused decode path for one token (T = 1), two launches in all:
+// Fused decode path for one token (T = 1), one launch (k_dec1_fused) when
+// one block per CU covers the output rows, else two (k_dec1_gateup then
+// k_dec1_down):
 //
-//   k_dec1_gateup  one block of 8 waves per CU.  Waves 0-3 compute the
-//                  router logits (four rows per block), wait until every row
-//                  is stored, and pick the top k (kimi-k3-in-c section 9,
-//                  "Picking 16 experts of 896"), recomputed by every block
-//                  from the logits; meanwhile waves 4-7 (and 0-3 while they
-//                  wait) stream the shared experts' gate/up rows.  Then all
-//                  waves take the routed experts' gate/up + activation -> H
-//                  (fp16, picks in ascending id)
-//   k_dec1_down    per output row: the shared experts' down rows, then the
-//                  routed down of every pick times its routing weight,
-//                  summed over the picks -> out (the weighted combine of
-//                  section 9, then the shared add)
+//   gate/up   one block of 8 waves per CU.  Waves 0-3 compute the router
+//             logits (four rows per block), wait until every row is stored,
+//             and pick the top k (kimi-k3-in-c section 9, "Picking 16
+//             experts of 896"), recomputed by every block from the logits;
+//             meanwhile waves 4-7 (and 0-3 while they wait) stream the
+//             shared experts' gate/up rows.  Then the waves take the routed
+//             experts' gate/up + activation -> H (fp16, picks in ascending
+//             id)
+//   down      per output row: the shared experts' down rows, then the routed
+//             down of every pick times its routing weight, summed over the
+//             picks -> out (the weighted combine of section 9, then the
+//             shared add)
 //
 // No dispatch kernel and no combine kernel: with one token the dispatch is
 // the ascending sort of 16 ids, and the combine is a sum over the picks that
-// the down kernel accumulates in registers.
+// the down rows accumulate in registers.
 //
-// The logits pass between the blocks of the gate/up kernel through slots in
-// the workspace's control block, tagged with the call's epoch (see
-// slot_store); the down kernel advances the epoch for the next call, so the
-// block needs no initialisation and nothing has to be cleared.
+// The logits pass between the blocks through slots in the workspace's
+// control block, tagged with the call's epoch (see slot_store).  In the one
+// launch a block goes on from its gate/up work to its 14 output rows: it
+// signals (epoch-tagged words) once its shared activations, then its routed
+// ones, are stored, and the down rows wait for the signals of every block
+// (see dec1_down_fused), so the shared rows run while slower blocks finish
+// their gate/up work.  The epoch moves on once every block has tagged (the
+// down kernel moves it in the two-launch form), so the control block needs
+// no initialisation and nothing has to be cleared.
 //
 // Weight streaming (kimi-k3-in-c section 4: MXFP4 = E2M1 codes two per byte,
 // low nibble first, one E8M0 scale per 32 weights): a row is spread over the
@@ -81,6 +88,13 @@ constexpr int kGuDynLds = kGuPartBytes + kXPad * 2 + 32 * 1024;
 // earlier calls never match it, and whatever the block held before its
 // first call (it is never cleared) matches only by a 32-bit coincidence.
 constexpr int kCtlEpoch = 2 * kMaxExperts + 64;  // int32 index
+// one-launch path: a 32-bit tag per block for "its shared activations are
+// stored" and one for "its routed activations are stored" (see
+// dec1_down_fused), after the epoch's line
+constexpr int kFusedMaxBlocks = 512;
+constexpr int kCtlShDone = kCtlEpoch + 64;
+constexpr int kCtlRtDone = kCtlShDone + kFusedMaxBlocks;
+static_assert((size_t)(kCtlRtDone + kFusedMaxBlocks) * 4 <= kWsControlBytes, "control block");
 constexpr uint32_t kHelpUsDefault = 50;  // wait (us) before a waiter computes missing router rows itself
 
 __device__ __forceinline__ uint4 gl16(const void *p) { return *reinterpret_cast<const uint4 *>(p); }
@@ -350,14 +364,33 @@ __device__ __forceinline__ float router_dot(const uint4 (&wv)[kRtChunks], const 
     return wave_sum(acc);
 }
 
+// Stores of the one-launch kernel's activations, written through to the
+// level all XCDs share (agent-scope atomic stores): once a wave's stores
+// are done (s_waitcnt), a tag stored after them publishes them, with no L2
+// writeback.
+__device__ __forceinline__ void st_through(_Float16 *q, _Float16 v)
+{
+    __hip_atomic_store(reinterpret_cast<uint16_t *>(q), __builtin_bit_cast(uint16_t, v), __ATOMIC_RELAXED,
+                       __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ void st_through(float *q, float v)
+{
+    __hip_atomic_store(reinterpret_cast<uint32_t *>(q), __float_as_uint(v), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+// the down rows of the one-launch kernel (defined with the down kernel)
+template <int SHD, class FS, class FR>
+__device__ void dec1_down_fused(const Dec1Params &p, uint32_t ep, uint8_t *s_h, const int *s_e, const float *s_w,
+                                bool sh_ready, FS &redo_shared, FR &redo_routed);
+
 // One block of 8 waves per CU.  Waves 0-3 compute their router rows, then
 // pick the experts (top-k) from the logits of the whole grid, while waves
 // 4-7 stream the shared experts' gate/up rows (a work queue of their own);
 // then every wave takes routed gate/up units from the block's queue.
 // SHC: 16-byte chunks per lane of a shared gate/up row (ceil(d / 512)).
 // SA: a row's scale bytes are 16-byte aligned (d % 512 == 0).
-template <int SHC, bool SA>
-__global__ __launch_bounds__(kGuWaves * 64) void k_dec1_gateup(Dec1Params p)
+template <int SHC, bool SA, bool FUSED, int SHD>
+__device__ __forceinline__ void dec1_gu(const Dec1Params &p)
 {
     __shared__ uint64_t s_cand[kTkWaves * kMaxTopK];
     __shared__ uint64_t s_sel[kMaxTopK];
@@ -377,8 +410,9 @@ __global__ __launch_bounds__(kGuWaves * 64) void k_dec1_gateup(Dec1Params p)
     // candidates are written; [3]: picks ready; [4]: keying waves whose
     // candidates are ranked; [5]: waves 4-7 whose part of the token is
     // staged; [6]: keying waves whose router row has arrived (or that have
-    // none)
-    __shared__ int s_ctl[7];
+    // none); [7]: (one launch) waves 4-7 done with the shared units; [8]:
+    // (one launch) 1 once the shared activations of every block are in LDS
+    __shared__ int s_ctl[9];
     const Shape &s = p.s;
     const int lane = threadIdx.x & 63;
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -464,7 +498,7 @@ __global__ __launch_bounds__(kGuWaves * 64) void k_dec1_gateup(Dec1Params p)
     // the queues and flags cleared: the one workgroup barrier before the
     // last (the loads above stay in flight; the shared queue starts past
     // the four units that waves 4-7 take first)
-    if (threadIdx.x < 7) s_ctl[threadIdx.x] = threadIdx.x == 1 ? kTkWaves * 64 : 0;
+    if (threadIdx.x < 9) s_ctl[threadIdx.x] = threadIdx.x == 1 ? kTkWaves * 64 : 0;
     lds_barrier();
 
     const uint32_t q_addr = (uint32_t)(uintptr_t)(__attribute__((address_space(3))) int *)&s_ctl[0];
@@ -623,6 +657,18 @@ __global__ __launch_bounds__(kGuWaves * 64) void k_dec1_gateup(Dec1Params p)
                 vb = vd;
             }
         }
+        if constexpr (FUSED) {
+            // one launch: the last of waves 4-7 to finish stores the block's
+            // shared activations and then its shared tag (after a release)
+            if (grab(q_addr + 28) == kGuWaves - kTkWaves - 1) {
+                float *hs = reinterpret_cast<float *>(reinterpret_cast<_Float16 *>(p.w.H) + (size_t)k * F);
+                for (int i = lane; i < nsloc; i += 64) st_through(&hs[sbeg + i], s_hsh[i]);
+                __builtin_amdgcn_s_waitcnt(0);
+                if (lane == 0)
+                    __hip_atomic_store(ctl + kCtlShDone + blockIdx.x, (int)slot_tag(ep, kFusedMaxBlocks + blockIdx.x),
+                                       __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            }
+        }
     }
     spin_until(&s_ctl[3], 1);
     spin_until(&s_ctl[5], kGuWaves - kTkWaves);
@@ -660,10 +706,9 @@ __global__ __launch_bounds__(kGuWaves * 64) void k_dec1_gateup(Dec1Params p)
     // loads of stage st of local unit v (past the block's range: zero-sized
     // resources, nothing read; still issued so that the waits count exactly)
     const int nitems = nloc * NS;
-    auto load = [&](GuStage<SA> &g, int item) __attribute__((always_inline)) {
-        const bool ok = item < nitems;
-        const int v = item / NS, st = item - v * NS;
-        const int u = ok ? (int)blockIdx.x + v * (int)gridDim.x : 0;
+    // loads of K slice st of unit u (ok false: zero-sized resources)
+    auto load_u = [&](GuStage<SA> &g, int u, int st, bool ok) __attribute__((always_inline)) {
+        u = ok ? u : 0;
         const int j = u / upr, f0 = (u % upr) * kGuFeat;
         const int e = max(__builtin_amdgcn_readlane(my_e, j), 0);  // no pick: expert 0, never used
         const uint32_t qbytes = ok ? (uint32_t)F * qrow : 0u, sbytes = ok ? (uint32_t)F * srow : 0u;
@@ -690,9 +735,14 @@ __global__ __launch_bounds__(kGuWaves * 64) void k_dec1_gateup(Dec1Params p)
         // (all of them issued before the arithmetic that follows)
         __builtin_amdgcn_sched_barrier(0);
     };
-    // multiply item `item` (valid) held in g, store its row sums
-    auto compute = [&](const GuStage<SA> &g, int item) __attribute__((always_inline)) {
+    auto load = [&](GuStage<SA> &g, int item) __attribute__((always_inline)) {
+        const bool ok = item < nitems;
         const int v = item / NS, st = item - v * NS;
+        load_u(g, (int)blockIdx.x + v * (int)gridDim.x, st, ok);
+    };
+    // the row sums of K slice st held in g: gate (x) and up (y) of row
+    // mrow, in every lane of the row
+    auto rowsum = [&](const GuStage<SA> &g, int st) __attribute__((always_inline)) -> float2 {
         float acc[2] = {0.0f, 0.0f};  // gate, up
 #pragma unroll
         for (int w = 0; w < kGuWin; w++) {
@@ -720,13 +770,45 @@ __global__ __launch_bounds__(kGuWaves * 64) void k_dec1_gateup(Dec1Params p)
             acc[m] += dppf<0xB1>(acc[m]);  // quad_perm [1,0,3,2]
             acc[m] += dppf<0x4E>(acc[m]);  // quad_perm [2,3,0,1]
         }
+        return make_float2(acc[0], acc[1]);
+    };
+    // multiply item `item` (valid) held in g, store its row sums
+    auto compute = [&](const GuStage<SA> &g, int item) __attribute__((always_inline)) {
+        const int v = item / NS, st = item - v * NS;
+        const float2 a = rowsum(g, st);
         if (grp == 0) {
-            s_part[v][st][mrow] = acc[0];
-            s_part[v][st][kGuFeat + mrow] = acc[1];
+            s_part[v][st][mrow] = a.x;
+            s_part[v][st][kGuFeat + mrow] = a.y;
         }
     };
 
-    {
+    // (one launch, a wide H: wave 7 instead waits for every block's shared
+    // activations (stored before their routed units) and stages them in LDS
+    // past the gate/up records, so that the down rows find them there)
+    const bool early_sh = FUSED && k * F * 2 >= kGuPartBytes + kXPad * 2 + 1024;
+    if (early_sh && wave == kGuWaves - 1) {
+        const int G = (int)gridDim.x;
+        const uint64_t t0 = __builtin_amdgcn_s_memrealtime();
+        bool all = false;
+        for (;;) {
+            bool miss = false;
+            for (int b = lane; b < G; b += 64)
+                miss = miss || (uint32_t)__hip_atomic_load(ctl + kCtlShDone + b, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) !=
+                                   slot_tag(ep, kFusedMaxBlocks + b);
+            all = !__builtin_amdgcn_ballot_w64(miss);
+            if (all || __builtin_amdgcn_s_memrealtime() - t0 >= 4 * p.help_ticks) break;
+            __builtin_amdgcn_s_sleep(4);
+        }
+        if (all) {
+            const int o = k * F * 2, n = S * F * 4;
+            const auto rh = grsrc(p.w.H, (uint32_t)(o + n));
+            LDS uint8_t *dst = (LDS uint8_t *)s_dyn;
+            for (int c = o / 1024; c * 1024 < o + n; c++)
+                gbld16_lds_sys(rh, dst + c * 1024, (uint32_t)(c * 1024 + lane * 16));
+            __builtin_amdgcn_s_waitcnt(0);
+            if (lane == 0) s_ctl[8] = 1;
+        }
+    } else {
         int ia = grab(q_addr);
         if (ia < nitems) {
             int ib = grab(q_addr);
@@ -762,12 +844,82 @@ __global__ __launch_bounds__(kGuWaves * 64) void k_dec1_gateup(Dec1Params p)
             g += s_part[v][st][f];
             up += s_part[v][st][kGuFeat + f];
         }
-        if (s_eid[u / upr] >= 0) H[(size_t)u * kGuFeat + f] = (_Float16)gated_act(g, up, s.act, s.b1, s.b2);
+        if (s_eid[u / upr] >= 0) {
+            const _Float16 hv = (_Float16)gated_act(g, up, s.act, s.b1, s.b2);
+            if constexpr (FUSED) st_through(&H[(size_t)u * kGuFeat + f], hv);
+            else H[(size_t)u * kGuFeat + f] = hv;
+        }
     }
     // (the shared activations follow the fp16 H of the picks: the down
     // kernel stages both in one copy)
     float *hs1 = reinterpret_cast<float *>(H + (size_t)k * F);
-    for (int i = threadIdx.x; i < nsloc; i += kGuWaves * 64) hs1[sbeg + i] = s_hsh[i];
+    if constexpr (!FUSED) {
+        for (int i = threadIdx.x; i < nsloc; i += kGuWaves * 64) hs1[sbeg + i] = s_hsh[i];
+    } else {
+        // ---- one launch: the block's routed tag once every wave's H stores
+        // (written through) are done, then the down rows
+        __builtin_amdgcn_s_waitcnt(0);
+        lds_barrier();
+        if (threadIdx.x == 0) {
+            __hip_atomic_store(ctl + kCtlRtDone + blockIdx.x, (int)slot_tag(ep, 2 * kFusedMaxBlocks + blockIdx.x),
+                               __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        }
+        // what a waiter computes for a block whose tag does not come (it
+        // may not be resident): the same sums in the same order, so the
+        // same bits as the block's own (a second store of equal values)
+        auto redo_shared = [&](int b) __attribute__((always_inline)) {
+            const int b0 = b * sper, bn = max(min(nsh - b0, sper), 0);
+            for (int v = wave; v < bn; v += kGuWaves) {
+                const int u = b0 + v;
+                const int si = u / F, f = u - si * F;
+                const auto r1 = brsrc(p.sh1 + (size_t)si * F * d, (uint32_t)((size_t)F * d * 2));
+                const auto r3 = brsrc(p.sh3 + (size_t)si * F * d, (uint32_t)((size_t)F * d * 2));
+                float ga = 0.0f, ua = 0.0f;
+#pragma unroll
+                for (int c = 0; c < SHC; c++) {
+                    const uint32_t ch = (uint32_t)min(lane + 64 * c, nch - 1);
+                    const uint4 w1 = bld16(r1, ch * 16, (uint32_t)f * d * 2);
+                    const uint4 w3 = bld16(r3, ch * 16, (uint32_t)f * d * 2);
+                    const uint4 xq = *reinterpret_cast<const uint4 *>(s_xb + (lane + 64 * c) * 8);
+                    const uint32_t xw[4] = {xq.x, xq.y, xq.z, xq.w};
+                    ga = bf16x8_dot_bf16(w1, xw, ga);
+                    ua = bf16x8_dot_bf16(w3, xw, ua);
+                }
+                const float g = wave_total(ga), up = wave_total(ua);
+                if (lane == 0) st_through(&hs1[u], gated_act(g, up, s.act, s.b1, s.b2));
+            }
+        };
+        auto redo_routed = [&](int b) __attribute__((always_inline)) {
+            const int nl = units > b ? (units - 1 - b) / (int)gridDim.x + 1 : 0;
+            for (int v = wave; v < nl; v += kGuWaves) {
+                const int u = b + v * (int)gridDim.x;
+                float g = 0.0f, up = 0.0f;
+                for (int st = 0; st < NS; st++) {
+                    GuStage<SA> gs;
+                    load_u(gs, u, st, true);
+                    const float2 a = rowsum(gs, st);
+                    g += a.x;
+                    up += a.y;
+                }
+                if (grp == 0 && s_eid[u / upr] >= 0)
+                    st_through(&H[(size_t)u * kGuFeat + mrow], (_Float16)gated_act(g, up, s.act, s.b1, s.b2));
+            }
+        };
+        dec1_down_fused<SHD>(p, ep, reinterpret_cast<uint8_t *>(s_dyn), s_eid, s_wt, s_ctl[8] == 1, redo_shared,
+                             redo_routed);
+    }
+}
+
+// the two kernels of the one-token path, and the one-launch kernel
+template <int SHC, bool SA>
+__global__ __launch_bounds__(kGuWaves * 64) void k_dec1_gateup(Dec1Params p)
+{
+    dec1_gu<SHC, SA, false, 2>(p);
+}
+template <int SHC, bool SA, int SHD>
+__global__ __launch_bounds__(kGuWaves * 64) void k_dec1_fused(Dec1Params p)
+{
+    dec1_gu<SHC, SA, true, SHD>(p);
 }
 
 // ------------------------------------------------------------ routed down + combine
@@ -963,6 +1115,252 @@ __device__ __forceinline__ void dec1_down_rows(const Dec1Params &p, int rblk, ui
     }
 }
 
+// ---- the down rows of the one-launch kernel.  After its gate/up work a
+// block (8 waves; waves 0-6 take two rows each, rows [14 b, 14 b + 14))
+// issues its rows' first weight loads, then waits until every block has
+// stored its shared activations (long done: they are stored before the
+// routed units), stages them and multiplies the shared experts' rows (so the
+// blocks that end their gate/up work early stream these rows while the
+// others finish), then waits until every block has stored its routed H,
+// stages it and runs the routed rows as k_dec1_down does (the same sums in
+// the same order: the same output bits).
+// A block's tags are 32-bit words in the control block, tagged with the
+// call's epoch (see slot_tag): no initialisation, nothing cleared.  A wait
+// longer than 4 help_ticks makes the waiter compute the missing blocks'
+// activations itself (redo_shared / redo_routed: the same bits), so no wait
+// depends on another block being resident.  H is read with system-coherent
+// copies (past this XCD's L2), after its producer's release.
+template <int SHD, class FS, class FR>
+__device__ void dec1_down_fused(const Dec1Params &p, uint32_t ep, uint8_t *s_h, const int *s_e, const float *s_w,
+                                bool sh_ready, FS &redo_shared, FR &redo_routed)
+{
+    constexpr int SHC = SHD;
+    __shared__ uint64_t s_miss[kGuWaves + 1];  // per wave: its lanes' missing tags; [8]: past the wait
+    const Shape &s = p.s;
+    const int lane = threadIdx.x & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int d = s.d, F = s.F, k = s.k;
+    const int S = p.shared ? s.S : 0;
+    const int G = (int)gridDim.x;
+    const bool has_rows = wave < kDnWaves;
+    int *ctl = p.w.ctl;
+    const int nb = F / 32;
+    constexpr uint32_t kPast = 0xF0000000u;
+    const size_t qrow = (size_t)F / 2, srow = (size_t)F / 32;
+    const uint32_t voq0 = lane < nb ? (uint32_t)lane * 16 : kPast, voq1 = lane + 64 < nb ? (uint32_t)(lane + 64) * 16 : kPast;
+    const uint32_t vos0 = lane < nb ? (uint32_t)lane : kPast, vos1 = lane + 64 < nb ? (uint32_t)(lane + 64) : kPast;
+    const int hb0 = min(lane, nb - 1), hb1 = min(lane + 64, nb - 1);
+    const int n0 = (int)blockIdx.x * kDnBlockRows + wave * kDnRows;
+    int rows[kDnRows];
+#pragma unroll
+    for (int r = 0; r < kDnRows; r++) rows[r] = min(n0 + r, d - 1);
+    const float *s_hs = reinterpret_cast<const float *>(s_h + (size_t)k * F * 2);
+    const int nchf = F / 8;
+    auto load_shd = [&](uint4 (&w)[kDnRows][SHC], int si) __attribute__((always_inline)) {
+        const bool ok = has_rows && si < S;
+        const auto r = brsrc(ok ? p.sh2 + (size_t)si * d * F : p.sh2, ok ? (uint32_t)((size_t)d * F * 2) : 0u);
+#pragma unroll
+        for (int rr = 0; rr < kDnRows; rr++)
+#pragma unroll
+            for (int c = 0; c < SHC; c++) {
+                const uint32_t ch = (uint32_t)min(lane + 64 * c, nchf - 1);
+                w[rr][c] = bld16(r, ch * 16, (uint32_t)rows[rr] * F * 2);
+            }
+    };
+    const int npair = (k + 1) / 2;
+    auto load = [&](DnLoads &g, int q) __attribute__((always_inline)) {
+#pragma unroll
+        for (int h = 0; h < 2; h++) {
+            const int j = min(2 * q + h, k - 1);
+            const int e = max(s_e[j], 0);
+            const uint32_t qbytes = has_rows ? (uint32_t)(d * qrow) : 0u, sbytes = has_rows ? (uint32_t)(d * srow) : 0u;
+            const auto rq = brsrc(p.w2q + (size_t)e * (d * qrow), qbytes), rs = brsrc(p.w2s + (size_t)e * (d * srow), sbytes);
+#pragma unroll
+            for (int r = 0; r < kDnRows; r++) {
+                const uint32_t so = (uint32_t)(rows[r] * qrow), ss = (uint32_t)(rows[r] * srow);
+                g.c[h][r][0] = bld16(rq, voq0, so);
+                g.c[h][r][1] = bld16(rq, voq1, so);
+                g.sc[h][r][0] = bld1(rs, vos0, ss);
+                g.sc[h][r][1] = bld1(rs, vos1, ss);
+            }
+        }
+    };
+    // wait until block b's tag (base + b) holds the call's tag, for every
+    // block; past 4 help_ticks, redo the missing blocks' work here.  Returns
+    // whether every tag was seen.
+    auto wait_tags = [&](int base, int tagoff, auto &redo) __attribute__((always_inline)) -> bool {
+        const uint64_t t0 = __builtin_amdgcn_s_memrealtime();
+        for (;;) {
+            bool miss = false;
+            for (int b = wave * 64 + lane; b < G; b += kGuWaves * 64) {
+                const uint32_t t = (uint32_t)__hip_atomic_load(ctl + base + b, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+                miss = miss || t != slot_tag(ep, tagoff + b);
+            }
+            const uint64_t m = __builtin_amdgcn_ballot_w64(miss);
+            if (lane == 0) s_miss[wave] = m;
+            // (one clock decides for the block)
+            if (threadIdx.x == 0) s_miss[kGuWaves] = __builtin_amdgcn_s_memrealtime() - t0 >= 4 * p.help_ticks;
+            __syncthreads();
+            uint64_t any = 0;
+#pragma unroll
+            for (int w = 0; w < kGuWaves; w++) any |= s_miss[w];
+            const bool late = s_miss[kGuWaves] != 0;
+            if (any == 0) return true;
+            if (late) {
+                // (one pass: the missing blocks' work, recomputed by this block)
+                for (int w = 0; w < kGuWaves; w++) {
+                    uint64_t mw = s_miss[w];
+                    while (mw) {
+                        const int l = __builtin_ctzll(mw);
+                        mw &= mw - 1;
+                        // (which blocks a lane polled: w * 64 + l, + 512 ...)
+                        for (int b = w * 64 + l; b < G; b += kGuWaves * 64) {
+                            const uint32_t t = (uint32_t)__hip_atomic_load(ctl + base + b, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+                            if (t != slot_tag(ep, tagoff + b)) redo(b);
+                        }
+                    }
+                }
+                // this block's own stores (written through): done before the
+                // coherent copies that read them
+                __builtin_amdgcn_s_waitcnt(0);
+                __syncthreads();
+                return false;
+            }
+            __builtin_amdgcn_s_sleep(2);
+            __syncthreads();
+        }
+    };
+    // bytes [o, o + n) of the H region into LDS at s_h + o (1 KB copies over
+    // the waves; the region ends on a whole KB of LDS)
+    auto stage = [&](int o, int n) __attribute__((always_inline)) {
+        const auto rh = grsrc(p.w.H, (uint32_t)(o + n));
+        LDS uint8_t *dst = (LDS uint8_t *)s_h;
+        for (int c = o / 1024 + wave; c * 1024 < o + n; c += kGuWaves)
+            gbld16_lds_sys(rh, dst + c * 1024, (uint32_t)(c * 1024 + lane * 16));
+    };
+
+    // ---- the rows' first weight loads (independent of H)
+    DnLoads ga, gb;
+    load(ga, 0);
+    constexpr int NSH = SHC <= 6 ? 2 : 1;
+    uint4 shw[NSH][kDnRows][SHC];
+    load_shd(shw[0], 0);
+    if constexpr (NSH > 1) load_shd(shw[NSH - 1], 1);
+
+    // ---- shared activations of every block (unless wave 7 staged them
+    // already), then the shared rows
+    if (!sh_ready) {
+        wait_tags(kCtlShDone, kFusedMaxBlocks, redo_shared);
+        // (the routed H precedes them: [k F fp16 | S F fp32])
+        stage(k * F * 2, S * F * 4);
+        __builtin_amdgcn_s_waitcnt(0);
+        __syncthreads();
+    }
+    float ysh[kDnRows];
+#pragma unroll
+    for (int r = 0; r < kDnRows; r++) ysh[r] = 0.0f;
+    auto dot_shd = [&](const uint4 (&w)[kDnRows][SHC], int si) __attribute__((always_inline)) {
+        float a[kDnRows];
+#pragma unroll
+        for (int r = 0; r < kDnRows; r++) a[r] = 0.0f;
+#pragma unroll
+        for (int c = 0; c < SHC; c++) {
+            const int ch = lane + 64 * c;
+            const bool ok = ch < nchf;
+            const float4 *h4 = reinterpret_cast<const float4 *>(s_hs + (size_t)si * F + (size_t)min(ch, nchf - 1) * 8);
+            const float4 h0 = h4[0], h1 = h4[1];
+            const float hv[8] = {h0.x, h0.y, h0.z, h0.w, h1.x, h1.y, h1.z, h1.w};
+#pragma unroll
+            for (int r = 0; r < kDnRows; r++) {
+                const float t = bf16x8_dot_f32(w[r][c], hv, 0.0f);
+                a[r] += ok ? t : 0.0f;
+            }
+        }
+#pragma unroll
+        for (int r = 0; r < kDnRows; r++) ysh[r] += wave_total(a[r]);
+    };
+    for (int si = 0; si < S; si++) {
+        if (NSH > 1 && (si & 1)) {
+            dot_shd(shw[NSH - 1], si);
+            if (si + 2 < S) load_shd(shw[NSH - 1], si + 2);
+        } else {
+            dot_shd(shw[0], si);
+            if (si + NSH < S) load_shd(shw[0], si + NSH);
+        }
+    }
+
+    // ---- the routed H of every block, then the routed rows.  Once every
+    // block's routed tag is seen, every block has read this call's epoch
+    // (it tagged its words with it): block 0 then sets the next call's.
+    const bool all_seen = wait_tags(kCtlRtDone, 2 * kFusedMaxBlocks, redo_routed);
+    if (blockIdx.x == 0 && threadIdx.x == 0 && all_seen)
+        __hip_atomic_store(ctl + kCtlEpoch, (int)ep, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    stage(0, k * F * 2);
+    __builtin_amdgcn_s_waitcnt(0);
+    __syncthreads();
+    float acc[kDnRows];
+#pragma unroll
+    for (int r = 0; r < kDnRows; r++) acc[r] = 0.0f;
+    auto compute = [&](const DnLoads &g, int q) __attribute__((always_inline)) {
+#pragma unroll
+        for (int h = 0; h < 2; h++) {
+            const int j = 2 * q + h;
+            const int jc = min(j, k - 1);
+            const bool use = j < k && s_e[jc] >= 0;
+            const float wj = s_w[jc];
+            uint32_t hr[32];
+            const uint4 *hs0 = reinterpret_cast<const uint4 *>(s_h + ((size_t)jc * F + (size_t)hb0 * 32) * 2);
+            const uint4 *hs1 = reinterpret_cast<const uint4 *>(s_h + ((size_t)jc * F + (size_t)hb1 * 32) * 2);
+#pragma unroll
+            for (int i = 0; i < 4; i++) {
+                const uint4 v = hs0[i], w = hs1[i];
+                hr[4 * i + 0] = v.x; hr[4 * i + 1] = v.y; hr[4 * i + 2] = v.z; hr[4 * i + 3] = v.w;
+                hr[16 + 4 * i + 0] = w.x; hr[16 + 4 * i + 1] = w.y; hr[16 + 4 * i + 2] = w.z; hr[16 + 4 * i + 3] = w.w;
+            }
+#pragma unroll
+            for (int r = 0; r < kDnRows; r++) {
+                const float a0 = fp4x32_dot_f16(g.c[h][r][0], hr);
+                const float a1 = fp4x32_dot_f16(g.c[h][r][1], hr + 16);
+                const float v = scaled2(a0, a1, (g.sc[h][r][0] & 0xFFu) | ((g.sc[h][r][1] & 0xFFu) << 8));
+                acc[r] = use ? fmaf(wj, v, acc[r]) : acc[r];
+            }
+        }
+    };
+    for (int q = 0;; q += 2) {
+        load(gb, min(q + 1, npair - 1));
+        compute(ga, q);
+        if (q + 1 >= npair) break;
+        load(ga, min(q + 2, npair - 1));
+        compute(gb, q + 1);
+        if (q + 2 >= npair) break;
+    }
+#pragma unroll
+    for (int r = 0; r < kDnRows; r++) {
+        const float v = wave_total(acc[r]) + ysh[r];
+        const int n = n0 + r;
+        if (has_rows && lane == 0 && n < d) {
+            if (p.out_f32) p.out_f32[n] = v;
+            if (p.out_bf16) p.out_bf16[n] = f32_to_bf16_rne(v);
+        }
+    }
+    // block 0 past the wait without seeing every tag: the epoch may move on
+    // only once every block has started (and tagged), which the other
+    // blocks' bounded waits let happen; the bound here only guards against a
+    // block that never runs
+    if (blockIdx.x == 0 && !all_seen && wave == 0) {
+        const uint64_t t0 = __builtin_amdgcn_s_memrealtime();
+        for (;;) {
+            bool miss = false;
+            for (int b = lane; b < G; b += 64)
+                miss = miss || (uint32_t)__hip_atomic_load(ctl + kCtlRtDone + b, __ATOMIC_RELAXED,
+                                                           __HIP_MEMORY_SCOPE_AGENT) != slot_tag(ep, 2 * kFusedMaxBlocks + b);
+            if (!__builtin_amdgcn_ballot_w64(miss) || __builtin_amdgcn_s_memrealtime() - t0 > (1ull << 27)) break;
+            __builtin_amdgcn_s_sleep(8);
+        }
+        if (lane == 0) __hip_atomic_store(ctl + kCtlEpoch, (int)ep, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    }
+}
+
 // SHC: 16-byte chunks per lane of a shared down row (ceil(F / 512))
 template <int SHC>
 __global__ __launch_bounds__(kDnWaves * 64) void k_dec1_down(Dec1Params p)
@@ -1057,6 +1455,42 @@ hipError_t launch_decode1(const Shape &s, const uint16_t *x, const Weights &wt, 
         if (sa) k_dec1_gateup<C, true><<<nblk, kGuWaves * 64, kGuDynLds, stream>>>(p);          \
         else k_dec1_gateup<C, false><<<nblk, kGuWaves * 64, kGuDynLds, stream>>>(p);           \
     } while (0)
+    const int shd = (s.F / 8 + 63) / 64;  // 16-byte chunks per lane of a shared down row
+    // (whole KB: the staging copies write 1 KB each)
+    const size_t lds = (((size_t)s.k * s.F * 2 + (size_t)(p.shared ? s.S : 0) * s.F * 4) + 1023) & ~(size_t)1023;
+    // one launch when one block per CU covers the output rows (so that in
+    // the usual case every block is resident at once: a wait for another
+    // block's tag then ends within microseconds; the bounded waits keep it
+    // correct otherwise)
+    const int nblk_f = max(nblk, (s.d + kDnBlockRows - 1) / kDnBlockRows);
+    if (nblk_f <= min(cu_count(), kFusedMaxBlocks)) {
+        const size_t lds_f = max(lds, (size_t)kGuDynLds);
+#define MOE_DEC1_F(C, D)                                                                                 \
+    do {                                                                                                 \
+        if (sa) k_dec1_fused<C, true, D><<<nblk_f, kGuWaves * 64, lds_f, stream>>>(p);                  \
+        else k_dec1_fused<C, false, D><<<nblk_f, kGuWaves * 64, lds_f, stream>>>(p);                   \
+    } while (0)
+#define MOE_DEC1_FD(C)                       \
+    do {                                     \
+        if (shd <= 2) MOE_DEC1_F(C, 2);      \
+        else if (shd <= 4) MOE_DEC1_F(C, 4); \
+        else if (shd <= 6) MOE_DEC1_F(C, 6); \
+        else MOE_DEC1_F(C, 8);               \
+    } while (0)
+        if (shc <= 2) MOE_DEC1_FD(2);
+        else if (shc <= 4) MOE_DEC1_FD(4);
+        else if (shc <= 6) MOE_DEC1_FD(6);
+        else if (shc <= 7) MOE_DEC1_FD(7);
+        else MOE_DEC1_FD(8);
+#undef MOE_DEC1_FD
+#undef MOE_DEC1_F
+        // (one kernel: both phase events after it)
+        if (ev2) {
+            (void)hipEventRecord(ev2[0], stream);
+            (void)hipEventRecord(ev2[1], stream);
+        }
+        return hipGetLastError();
+    }
     if (shc <= 2) MOE_DEC1_GU(2);
     else if (shc <= 4) MOE_DEC1_GU(4);
     else if (shc <= 6) MOE_DEC1_GU(6);
@@ -1065,9 +1499,6 @@ hipError_t launch_decode1(const Shape &s, const uint16_t *x, const Weights &wt, 
 #undef MOE_DEC1_GU
     if (ev2) (void)hipEventRecord(ev2[0], stream);
     const int nd = (s.d + kDnBlockRows - 1) / kDnBlockRows;
-    // (whole KB: the staging copies write 1 KB each)
-    const size_t lds = (((size_t)s.k * s.F * 2 + (size_t)(p.shared ? s.S : 0) * s.F * 4) + 1023) & ~(size_t)1023;
-    const int shd = (s.F / 8 + 63) / 64;  // 16-byte chunks per lane of a shared down row
     if (shd <= 2) k_dec1_down<2><<<nd, kDnWaves * 64, lds, stream>>>(p);
     else if (shd <= 4) k_dec1_down<4><<<nd, kDnWaves * 64, lds, stream>>>(p);
     else if (shd <= 6) k_dec1_down<6><<<nd, kDnWaves * 64, lds, stream>>>(p);
