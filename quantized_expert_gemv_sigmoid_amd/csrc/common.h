@@ -381,7 +381,7 @@ __device__ __forceinline__ uint32_t gbld1(__amdgpu_buffer_rsrc_t r, uint32_t vof
 // restored for the compiler's own uses.
 __device__ __forceinline__ void gbld16_lds(__amdgpu_buffer_rsrc_t r, LDS uint8_t *dst, uint32_t voff)
 {
-    const uint32_t m0v = (uint32_t)(uintptr_t)dst;
+    const uint32_t m0v = __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)dst);  // (wave-uniform)
     uint32_t save;
     asm volatile("s_mov_b32 %0, m0\n\ts_mov_b32 m0, %1\n\tbuffer_load_dwordx4 %2, %3, 0 offen lds\n\ts_mov_b32 m0, %0"
                  : "=&s"(save)
@@ -392,7 +392,7 @@ __device__ __forceinline__ void gbld16_lds(__amdgpu_buffer_rsrc_t r, LDS uint8_t
 // sees data another XCD wrote back)
 __device__ __forceinline__ void gbld16_lds_sys(__amdgpu_buffer_rsrc_t r, LDS uint8_t *dst, uint32_t voff)
 {
-    const uint32_t m0v = (uint32_t)(uintptr_t)dst;
+    const uint32_t m0v = __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)dst);  // (wave-uniform)
     uint32_t save;
     asm volatile("s_mov_b32 %0, m0\n\ts_mov_b32 m0, %1\n\tbuffer_load_dwordx4 %2, %3, 0 offen sc0 sc1 lds\n\ts_mov_b32 m0, %0"
                  : "=&s"(save)
