@@ -14,11 +14,14 @@ stacks 12 such layers (own weights, own tokens, one Zipf selection bias) in
 one HIP graph per step.
 
 Prints one JSON line:
-- the headline: tok/s over exactly K timed graph replays (``value``), two
-  more windows of K steps for the spread, the roofline of the dominant
-  kernel (algorithmic bytes or flops / its average duration, timed live with
-  the HIP events of moe_layer_timed on the launch stream) and the CPU oracle
-  timed on a bounded sample of the same workload on this host;
+- the headline: tok/s over exactly K timed steps (``value``), two more
+  windows of K steps for the spread, one window of the other launch form for
+  reference, the roofline of the dominant kernel (algorithmic bytes or flops
+  / its average duration, timed live with HIP events on the launch stream)
+  and the CPU oracle timed on a bounded sample of the same workload on this
+  host.  A step that is one kernel launch (the one-token path of one layer)
+  is timed as plain back-to-back launches, a step of several launches as a
+  replay of its HIP graph;
 - ``configs``: the same measurements for the other workloads (tiny, decode
   T=64, prefill T=4096, the 12-layer stack) and for Kimi-K3's Stable
   LatentMoE around the routed experts (full-width router and shared
@@ -61,7 +64,8 @@ KERNELS = {
     "gemv": {"router_logits": "k_front", "topk_dispatch": "k_dispatch_small/k_topk+k_dispatch_*",
              "expert_gate_up": "k_gemv_gateup", "expert_down": "k_gemv_down", "combine": "k_combine"},
     "mfma": {"router_logits": "k_split_router + k_ggemm<M_R>", "topk_dispatch": "k_topk + k_dispatch_*",
-             "expert_gate_up": "k_ggemm<M_S13> + k_ggemm<M_G13>", "expert_down": "k_ggemm<M_S2> + k_ggemm<M_D2>",
+             "expert_gate_up": "k_ggemm_pair<M_S13, M_G13> (K3 shape, T <= 1280; else k_ggemm<M_S13> + k_ggemm<M_G13>)",
+             "expert_down": "k_ggemm_pair<M_S2, M_D2> (K3 shape, T <= 2304; else k_ggemm<M_S2> + k_ggemm<M_D2>)",
              "combine": "k_combine"},
 }
 # steps per timed window of each workload when it is measured as an entry of
@@ -81,6 +85,35 @@ LATENT_KERNELS = {
              "norm_up_shared_out": "k_latent_accum + k_latent_split + k_ggemm<M_S2> (up, shared down) + k_combine"},
 }
 WINDOWS = 3
+
+
+def time_windows(torch, step, graphs, npool, K, stream, plain):
+    """WINDOWS windows of K steps (window 0 first: the headline's K steps),
+    each bracketed by events on the launch stream; then one window of the
+    other launch form for reference.  plain: the windows time the steps as
+    plain launches (the form for a step that is one kernel launch: a graph
+    replay adds a fixed cost per replay, about 5 us on this stack); else as
+    replays of the step's graph.  Returns (windows, reference window or None)."""
+    start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+
+    def window(w, use_graph):
+        torch.cuda.synchronize()
+        start.record(stream)
+        for i in range(K):
+            if use_graph:
+                graphs[(w * K + i) % npool].replay()
+            else:
+                step(w * K + i)
+        end.record(stream)
+        torch.cuda.synchronize()
+        return start.elapsed_time(end) / K
+
+    primary_graph = graphs is not None and not plain
+    windows = [window(w, primary_graph) for w in range(WINDOWS)]
+    ref = None
+    if graphs is not None:
+        ref = window(WINDOWS, not primary_graph)
+    return windows, ref
 
 # HBM bytes per dispatch measured by rocprofv3 (FETCH_SIZE and WRITE_SIZE,
 # each scaled by what the counter reads for a plain 256 MiB copy) at decode
@@ -288,18 +321,7 @@ def measure_latent(lidx, steps, warmup, pool, use_graph, cpu_seconds, hbm_copy_g
         for i in range(warmup):
             graphs[i % npool].replay()
         torch.cuda.synchronize()
-    windows = []
-    for wdx in range(WINDOWS):
-        torch.cuda.synchronize()
-        start.record(stream)
-        for i in range(K):
-            if graphs is not None:
-                graphs[(wdx * K + i) % npool].replay()
-            else:
-                step(wdx * K + i)
-        end.record(stream)
-        torch.cuda.synchronize()
-        windows.append(start.elapsed_time(end) / K)
+    windows, ref_ms = time_windows(torch, step, graphs, npool, K, stream, plain=False)
     evs = [[torch.cuda.Event(enable_timing=True) for _ in range(moe.TIMED_EVENTS)] for _ in range(K)]
     for row in evs:
         for e in row:
@@ -343,11 +365,12 @@ def measure_latent(lidx, steps, warmup, pool, use_graph, cpu_seconds, hbm_copy_g
                    "path": kind, "token_pool": npool,
                    "launch": "hip graph replay" if graphs is not None else "eager"},
         "steps": K, "ms_per_step": round(windows[0], 5),
+        "ms_per_step_other_launch": None if ref_ms is None else {"launch": "eager", "ms": round(ref_ms, 5)},
         "ms_per_step_windows": [round(w, 5) for w in windows],
         "ms_per_step_median": round(med, 5),
         "ms_per_step_spread": round((max(windows) - min(windows)) / med, 4),
         "tok_s": round(T / (windows[0] * 1e-3), 2), "tok_s_median": round(T / (med * 1e-3), 2),
-        "ms_per_step_eager": round(eager_ms, 5),
+        "ms_per_step_with_phase_events": round(eager_ms, 5),
         "step_hbm_gbs": round(step_bytes / (med * 1e-3) / 1e9, 1),
         "step_hbm_frac": round(step_bytes / (med * 1e-3) / 1e9 / PEAK_HBM_GBS, 4),
         "step_frac_of_copy": round(step_bytes / (med * 1e-3) / 1e9 / hbm_copy_gbs, 4),
@@ -440,7 +463,6 @@ def measure(widx, steps, warmup, pool, use_graph, cpu_seconds, hbm_copy_gbs):
 
     K = steps
     start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    windows = []
     graphs = None
     if use_graph:
         # one HIP graph per token batch of the pool, holding all L layers (the
@@ -455,17 +477,9 @@ def measure(widx, steps, warmup, pool, use_graph, cpu_seconds, hbm_copy_gbs):
         for i in range(warmup):
             graphs[i % npool].replay()
         torch.cuda.synchronize()
-    for wdx in range(WINDOWS):
-        torch.cuda.synchronize()
-        start.record(stream)
-        for i in range(K):
-            if graphs is not None:
-                graphs[(wdx * K + i) % npool].replay()
-            else:
-                step(wdx * K + i)
-        end.record(stream)
-        torch.cuda.synchronize()
-        windows.append(start.elapsed_time(end) / K)
+    # (the one-token path of a single layer is one kernel launch per step)
+    plain = kind == "decode1" and L == 1
+    windows, ref_ms = time_windows(torch, step, graphs, npool, K, stream, plain)
 
     # per-phase durations: every layer of every step with its own events
     evs = [[[torch.cuda.Event(enable_timing=True) for _ in range(moe.TIMED_EVENTS)] for _ in range(L)]
@@ -492,6 +506,12 @@ def measure(widx, steps, warmup, pool, use_graph, cpu_seconds, hbm_copy_gbs):
     ph_flops = phase_flops(shape, T)
     step_bytes = L * sum(ph_bytes.values())  # per step, all layers
     dom = max(("expert_gate_up", "expert_down"), key=lambda p: ph_ms[p])
+    # the dominant kernel's average duration: a step of plain launches of
+    # one kernel is that kernel, so the timed windows' events give it (the
+    # median window); else the events around its phase in every step
+    dom_ms = float(np.median(windows)) if plain else ph_ms[dom]
+    dom_timing = ("events around the timed windows' K back-to-back launches (median window)" if plain
+                  else "events around the phase, every step of a window")
     # the bound of the dominant phase: its flops per algorithmic HBM byte
     # against the machine balance (peak flops / peak bytes, 312 F/B); half of
     # it or more counts as matrix-core bound
@@ -499,18 +519,18 @@ def measure(widx, steps, warmup, pool, use_graph, cpu_seconds, hbm_copy_gbs):
     if kind == "mfma" and intensity >= 0.5 * PEAK_BF16_TFLOPS * 1e12 / (PEAK_HBM_GBS * 1e9):
         # a dense contraction on the matrix cores (bf16 after the in-register
         # MXFP4 decode): against the bf16 MFMA peak
-        achieved = ph_flops[dom] / (ph_ms[dom] * 1e-3) / 1e12
+        achieved = ph_flops[dom] / (dom_ms * 1e-3) / 1e12
         roofline = {"bound": "mfma", "achieved": round(achieved, 1), "peak": PEAK_BF16_TFLOPS,
                     "unit": "TFLOP/s", "frac": round(achieved / PEAK_BF16_TFLOPS, 4), "traffic": None,
                     "kernel": KERNELS[kind][dom], "flops_per_launch": int(ph_flops[dom]),
-                    "avg_launch_us": round(ph_ms[dom] * 1e3, 2)}
+                    "avg_launch_us": round(dom_ms * 1e3, 2), "timing": dom_timing}
     else:
-        achieved = ph_bytes[dom] / (ph_ms[dom] * 1e-3) / 1e9
+        achieved = ph_bytes[dom] / (dom_ms * 1e-3) / 1e9
         roofline = {"bound": "hbm", "achieved": round(achieved, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
                     "frac": round(achieved / PEAK_HBM_GBS, 4),
                     "traffic": measured_traffic(KERNELS[kind][dom].split()[0]) if T == 1 else None,
                     "kernel": KERNELS[kind][dom], "bytes_per_launch": int(ph_bytes[dom]),
-                    "avg_launch_us": round(ph_ms[dom] * 1e3, 2),
+                    "avg_launch_us": round(dom_ms * 1e3, 2), "timing": dom_timing,
                     "frac_of_copy": round(achieved / hbm_copy_gbs, 4)}
     ms = windows[0]
     med = float(np.median(windows))
@@ -520,14 +540,17 @@ def measure(widx, steps, warmup, pool, use_graph, cpu_seconds, hbm_copy_gbs):
               "tokens": T, "layers": L, "selection_bias": "zipf" if wl.zipf_bias else "none",
               "weights": "mxfp4 (e2m1 + e8m0/32) routed, bf16 shared",
               "path": kind, "token_pool": npool,
-              "launch": "hip graph replay" if graphs is not None else "eager"}
+              "launch": ("hip graph replay" if graphs is not None and not plain
+                         else "eager (one kernel launch per step)" if plain else "eager")}
     res = {
         "config": config, "steps": K, "ms_per_step": round(ms, 5),
+        "ms_per_step_other_launch": None if ref_ms is None else {
+            "launch": "hip graph replay" if plain else "eager", "ms": round(ref_ms, 5)},
         "ms_per_step_windows": [round(w, 5) for w in windows],
         "ms_per_step_median": round(med, 5),
         "ms_per_step_spread": round((max(windows) - min(windows)) / med, 4),
         "tok_s": round(T / (ms * 1e-3), 2), "tok_s_median": round(T / (med * 1e-3), 2),
-        "ms_per_step_eager": round(eager_ms, 5),
+        "ms_per_step_with_phase_events": round(eager_ms, 5),
         "step_hbm_gbs": round(step_bytes / (med * 1e-3) / 1e9, 1),
         "step_hbm_frac": round(step_bytes / (med * 1e-3) / 1e9 / PEAK_HBM_GBS, 4),
         "step_frac_of_copy": round(step_bytes / (med * 1e-3) / 1e9 / hbm_copy_gbs, 4),
@@ -633,7 +656,8 @@ def main():
         "ms_per_step_windows": head["ms_per_step_windows"],
         "ms_per_step_median": head["ms_per_step_median"],
         "ms_per_step_spread": head["ms_per_step_spread"],
-        "ms_per_step_eager": head["ms_per_step_eager"],
+        "ms_per_step_with_phase_events": head["ms_per_step_with_phase_events"],
+        "ms_per_step_other_launch": head["ms_per_step_other_launch"],
         "step_hbm_gbs": head["step_hbm_gbs"], "step_hbm_frac": head["step_hbm_frac"],
         "hbm_copy_gbs": round(hbm_copy_gbs, 1), "step_frac_of_copy": head["step_frac_of_copy"],
         "step_tflops": head["step_tflops"],

@@ -833,18 +833,18 @@ __device__ __forceinline__ bool gemm_pass(const GemmParams &p, const Blk &bk, in
     }
 }
 
+// Block x of a MODE grid (x counts from the first block of the grid's
+// MODE part; that part starts at a multiple of 8 blocks, so x % 8 is still
+// the XCD the block runs on).
 template <int MODE>
-__global__ __launch_bounds__(GT) void k_ggemm(GemmParams p)
+__device__ __forceinline__ void ggemm_block(const GemmParams &p, int x, LDS uint8_t *ring)
 {
     using C = Cfg<MODE>;
-    __shared__ __attribute__((aligned(1024))) uint8_t lds_blk[kLdsBytes];
-    LDS uint8_t *ring = (LDS uint8_t *)lds_blk;  // (MXFP4: the scale rows, then the ring)
     const Shape &s = p.s;
     Blk b;
     // ---- block -> (m block, group, column tile); consecutive groups of
     // tiles go to one XCD (blocks are dealt to the 8 XCDs round robin), so
     // the blocks of one group share its A rows in that XCD's L2
-    int x = blockIdx.x;
     const int gt = p.groups * p.n_tiles;
     b.mb = 0;
     b.ks = 0;
@@ -915,6 +915,29 @@ __global__ __launch_bounds__(GT) void k_ggemm(GemmParams p)
         const int m0 = b.mb * GM;
         if (m0 < b.M) gemm_pass<MODE, GMT>(p, b, m0, min(GM, b.M - m0), ring, false);
     }
+}
+
+template <int MODE>
+__global__ __launch_bounds__(GT) void k_ggemm(GemmParams p)
+{
+    __shared__ __attribute__((aligned(1024))) uint8_t lds_blk[kLdsBytes];
+    // (MXFP4: the scale rows, then the ring)
+    ggemm_block<MODE>(p, (int)blockIdx.x, (LDS uint8_t *)lds_blk);
+}
+
+// Two independent GEMMs in one grid: blocks [0, n1) run MODE1 with p1,
+// blocks [n1p, grid) MODE2 with p2 (n1p: n1 rounded up to a multiple of 8,
+// the blocks between do nothing).  The shared experts' GEMMs have few
+// blocks at small T (one per 256 columns and 128 tokens); as the head of
+// the routed GEMM's grid they run beside its blocks instead of holding the
+// GPU to a fraction of its CUs in a launch of their own.
+template <int MODE1, int MODE2>
+__global__ __launch_bounds__(GT) void k_ggemm_pair(GemmParams p1, GemmParams p2, int n1, int n1p)
+{
+    __shared__ __attribute__((aligned(1024))) uint8_t lds_blk[kLdsBytes];
+    const int x = (int)blockIdx.x;
+    if (x < n1) ggemm_block<MODE1>(p1, x, (LDS uint8_t *)lds_blk);
+    else if (x >= n1p) ggemm_block<MODE2>(p2, x - n1p, (LDS uint8_t *)lds_blk);
 }
 
 // Router weights fp32 -> three bf16 parts whose sum is exact: hi = rne(w),
@@ -1062,9 +1085,10 @@ size_t mfma_extra_workspace(const Shape &s)
     return (((size_t)s.E * 3 * s.d * 2) + 255) & ~(size_t)255;
 }
 
-template <int MODE>
-static void launch_mode(const GemmParams &p0, int groups, int n_tiles, int m_blocks, hipStream_t st,
-                        int ksplit = 1)
+// p0 with a grid of `groups` groups of n_tiles column tiles, m_blocks M
+// passes and ksplit K slices; *nblk gets the grid's block count
+static GemmParams mode_params(const GemmParams &p0, int groups, int n_tiles, int m_blocks, int ksplit,
+                              int *nblk)
 {
     GemmParams p = p0;
     p.groups = groups;
@@ -1072,8 +1096,33 @@ static void launch_mode(const GemmParams &p0, int groups, int n_tiles, int m_blo
     p.m_blocks = m_blocks;
     p.ksplit = ksplit;
     const int padded = groups >= 8 ? (groups + 7) / 8 * 8 : groups;
-    const int nblk = padded * n_tiles * m_blocks * ksplit;
+    *nblk = padded * n_tiles * m_blocks * ksplit;
+    return p;
+}
+
+template <int MODE>
+static void launch_mode(const GemmParams &p0, int groups, int n_tiles, int m_blocks, hipStream_t st,
+                        int ksplit = 1)
+{
+    int nblk;
+    const GemmParams p = mode_params(p0, groups, n_tiles, m_blocks, ksplit, &nblk);
     if (nblk > 0) k_ggemm<MODE><<<nblk, GT, 0, st>>>(p);
+}
+
+// the shared experts' GEMM (MODE1, n1 blocks) at the head of the routed one
+// (MODE2, n2 blocks) in one launch while it has too few blocks to fill the
+// GPU twice (small T); else two launches
+constexpr int kPairMaxHead = 512;
+template <int MODE1, int MODE2>
+static void launch_pair(const GemmParams &p1, int n1, const GemmParams &p2, int n2, hipStream_t st)
+{
+    if (n1 >= kPairMaxHead) {
+        k_ggemm<MODE1><<<n1, GT, 0, st>>>(p1);
+        if (n2 > 0) k_ggemm<MODE2><<<n2, GT, 0, st>>>(p2);
+        return;
+    }
+    const int n1p = (n1 + 7) / 8 * 8;
+    if (n1 + n2 > 0) k_ggemm_pair<MODE1, MODE2><<<n1p + n2, GT, 0, st>>>(p1, p2, n1, n1p);
 }
 
 static GemmParams make_gemm_params(const Shape &s, const uint16_t *x, const Weights &wt, const Work &w)
@@ -1127,11 +1176,17 @@ hipError_t launch_mfma_experts(const Shape &s, const uint16_t *x, const Weights 
     const int mb = (s.T + GM - 1) / GM;
     // the tokens as two fp8 terms (the routed gate/up's A operand)
     k_quant_x<<<(s.T + 3) / 4, 256, 0, st>>>(s.T, s.d, x, w.xq, const_cast<uint32_t *>(p.xs));
-    if (include_shared && s.S > 0) launch_mode<M_S13>(p, s.S, (s.F + 127) / 128, mb, st);
-    launch_mode<M_G13>(p, max_active, (s.F + 127) / 128, 1, st);
+    // the shared experts (when included) in the same launches as the routed
+    // gate/up and down
+    const bool sh = include_shared && s.S > 0;
+    int n_s13 = 0, n_g13, n_s2 = 0, n_d2;
+    const GemmParams p_s13 = mode_params(p, sh ? s.S : 0, (s.F + 127) / 128, mb, 1, &n_s13);
+    const GemmParams p_g13 = mode_params(p, max_active, (s.F + 127) / 128, 1, 1, &n_g13);
+    launch_pair<M_S13, M_G13>(p_s13, n_s13, p_g13, n_g13, st);
     if (ev2) (void)hipEventRecord(ev2[0], st);
-    if (include_shared && s.S > 0) launch_mode<M_S2>(p, s.S, (s.d + GN - 1) / GN, mb, st);
-    launch_mode<M_D2>(p, max_active, (s.d + GN - 1) / GN, 1, st);
+    const GemmParams p_s2 = mode_params(p, sh ? s.S : 0, (s.d + GN - 1) / GN, mb, 1, &n_s2);
+    const GemmParams p_d2 = mode_params(p, max_active, (s.d + GN - 1) / GN, 1, 1, &n_d2);
+    launch_pair<M_S2, M_D2>(p_s2, n_s2, p_d2, n_d2, st);
     if (ev2) (void)hipEventRecord(ev2[1], st);
     return hipGetLastError();
 }

@@ -172,6 +172,8 @@ __global__ __launch_bounds__(kSmallThreads) void k_dispatch_small(
     __shared__ int offs[kMaxExperts];
     __shared__ int tmp[NW];
     __shared__ uint64_t s_tk[NW][2 * kMaxTopK];
+    __shared__ int32_t s_ids[kDispatchTokens * kMaxTopK];
+    __shared__ float s_wts[kDispatchTokens * kMaxTopK];
     const int T = s.T, E = s.E, k = s.k;
     const int wave = threadIdx.x >> 6;
     if (do_topk) {
@@ -184,8 +186,12 @@ __global__ __launch_bounds__(kSmallThreads) void k_dispatch_small(
     }
     for (int e = threadIdx.x; e < E; e += kSmallThreads) masks[e] = 0ull;
     __syncthreads();  // also publishes the top-k results to the block
+    // every slot's id and weight into LDS at once (the per-token scatter
+    // below then waits on no global load)
     for (int sl = threadIdx.x; sl < T * k; sl += kSmallThreads) {
         const int e = ids[sl];
+        s_ids[sl] = e;
+        s_wts[sl] = wts[sl];
         if (valid_id(e, E)) atomicOr(&masks[e], 1ull << (sl / k));
     }
     __syncthreads();
@@ -197,7 +203,7 @@ __global__ __launch_bounds__(kSmallThreads) void k_dispatch_small(
     }
     __syncthreads();
     for (int t = wave; t < T; t += NW)
-        dispatch_token(t, E, k, ids, wts,
+        dispatch_token(t, E, k, s_ids, s_wts,
                        [&](int e) { return offs[e] + __popcll(masks[e] & ((1ull << t) - 1ull)); }, w);
 }
 
