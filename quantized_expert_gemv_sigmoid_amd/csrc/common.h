@@ -30,11 +30,14 @@ struct Work {
     int32_t *counts;   // [E]
     int32_t *offsets;  // [E+1]   exclusive scan of counts
     int32_t *active;   // [E]     experts with a nonzero count, ascending
+    int32_t *ginfo;    // [E][4]  per active expert (same order): {expert, count, offset, 0}
     int32_t *meta;     // [4]     meta[0] = number of active experts
     uint64_t *masks;   // [nblk][E] token bitmaps per 64-token block
     int32_t *blk_base; // [nblk][E]
     int32_t *pos_tok;  // [T*k]   token of the slot at each expert-grouped position
     float *pos_w;      // [T*k]   its routing weight
+    uint32_t *pos_xs;  // [T*k]   MFMA path: the E8M0 scales of its token's fp8 terms ...
+    const uint32_t *tok_xs;  // ... gathered from these [T] (null: not gathered)
     int32_t *tok_pos;  // [T][k]  positions of a token's slots, ascending expert id
     void *H;           // [T*k][F] gate/up activations (fp32 or fp16; one token: fp16, then the
                        // shared activations [S*F] fp32)
@@ -443,6 +446,8 @@ size_t router_part_workspace(const Shape &s, int parts = 3);
 constexpr int kRouterPartRows = 8192;  // rows of E partial logits (MFMA router K slices)
 hipError_t launch_mfma_router(const Shape &s, const uint16_t *x, const Weights &wt, const Work &w,
                               hipStream_t stream);
+const uint32_t *mfma_token_scales(const Shape &s, const Work &w);
+hipError_t launch_quant_x(const Shape &s, const uint16_t *x, const Work &w, hipStream_t stream);
 hipError_t launch_mfma_experts(const Shape &s, const uint16_t *x, const Weights &wt,
                                int include_shared, const Work &w, hipStream_t stream,
                                hipEvent_t const *ev2);

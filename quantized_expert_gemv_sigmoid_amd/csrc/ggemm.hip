@@ -46,13 +46,19 @@
 namespace moe {
 
 typedef float f32x16_t __attribute__((ext_vector_type(16)));
+typedef int i32x4_t __attribute__((ext_vector_type(4)));
+// Read-only view (address space 4) of data an earlier launch wrote: a
+// wave-uniform index then loads into scalar registers, through the scalar
+// memory path, so it waits behind none of the block's copies in flight
+#define KCONST __attribute__((address_space(4)))
 
 constexpr int GT = 512;              // threads per block: 8 waves, two per SIMD
 constexpr int GN = 256;              // output columns per block (64 per SIMD: two 32-column tiles)
 constexpr int GMT = 4;               // 32-row MFMA tiles per M pass, bf16 weights
 constexpr int GMT4 = 3;              // 32-row MFMA tiles per M pass (at most), MXFP4 weights
 constexpr int GM = GMT * 32;         // rows per M pass
-constexpr int kLdsBytes = 152 * 1024;   // LDS of a block (one block per CU)
+constexpr int kLdsBytes = 152 * 1024;   // LDS of a block's scale rows and stage ring (one block per CU)
+constexpr int kMetaBytes = 1024;        // and past them: the routed gate/up pass's token scales
 constexpr int kScaleBytes = 32 * 1024;  // MXFP4: the block's scale rows (256 of at most 128 bytes)
 constexpr uint32_t kPast = 0xF0000000u;  // a buffer offset past every resource: loads return 0, read nothing
 
@@ -330,20 +336,36 @@ __device__ __forceinline__ bool wave_pass(const GemmParams &p, const Blk &bk, in
         ra0 = grsrc(abase, abytes);
         ra1 = MODE == M_S2 ? grsrc(p.hs_lo, abytes) : ra0;
         constexpr int RPI = 1024 / AROW;
+        static_assert(RPI * C::ASLOTS == 64, "rows per copy");
 #pragma unroll
         for (int j = 0; j < RG::NA; j++) {
             const int r = RPI * (8 * j + wave) + lane / C::ASLOTS;
             const int q = (lane % C::ASLOTS) ^ swz_a<MODE>(r);
             const int m = m0 + min(r, mrows - 1);
+            // gathered rows (routed gate/up): the copy's RPI rows are the same
+            // for the whole wave, so their tokens come in by scalar loads
+            // (no round trip through the vector memory queue before the
+            // block's first copy), and each lane takes its row's
+            int tok = 0;
+            if constexpr (MODE == M_G13 || MODE == M_G13H) {
+                const KCONST int32_t *pt = (const KCONST int32_t *)p.w.pos_tok + bk.base + m0;
+                const int r0 = RPI * (8 * j + wave);
+                tok = pt[min(r0, mrows - 1)];
+#pragma unroll
+                for (int u = 1; u < RPI; u++) {
+                    const int tu = pt[min(r0 + u, mrows - 1)];
+                    tok = lane / C::ASLOTS == u ? tu : tok;
+                }
+            }
             uint32_t e;  // byte offset of the row, and of piece q in it
             if constexpr (MODE == M_G13) {
                 // pieces 0-7: the hi fp8 bytes of the stage, 8-15: the lo ones
-                e = (uint32_t)p.w.pos_tok[bk.base + m] * (2 * s.d) + (q >= 8 ? s.d : 0) + (q & 7) * 16;
+                e = (uint32_t)tok * (2 * s.d) + (q >= 8 ? s.d : 0) + (q & 7) * 16;
             } else {
                 uint32_t el;  // element offset
                 if constexpr (MODE == M_D2) el = (uint32_t)(bk.base + m) * s.F;
                 else if constexpr (MODE == M_S2) el = (uint32_t)m * s.S * s.F + (uint32_t)bk.group * s.F;
-                else if constexpr (MODE == M_G13H) el = (uint32_t)p.w.pos_tok[bk.base + m] * s.d;
+                else if constexpr (MODE == M_G13H) el = (uint32_t)tok * s.d;
                 else el = (uint32_t)m * s.d;
                 e = el * 2 + q * 16;
             }
@@ -409,18 +431,16 @@ __device__ __forceinline__ bool wave_pass(const GemmParams &p, const Blk &bk, in
             gbld16_lds(rb[j], st + RG::ABYTES + (8 * j + wave) * 1024, ok ? boff[j] + kb : kPast);
     };
 
-    // (G13) the E8M0 scales of this lane's token row in each of its tiles:
-    // hi term in byte 0, lo term in byte 1; loaded here, before the copies,
-    // and waited for at once
-    uint32_t sca[NTW > 0 ? NTW : 1];
+    // (G13) the E8M0 scales of the pass's token rows (hi term in byte 0, lo
+    // term in byte 1, gathered per position by the dispatch): wave 0 copies
+    // them to LDS past the ring ahead of the stage copies, so the first
+    // stage's wait covers them; the lanes read their rows' after it
+    const int xs0 = (bk.base + m0) & ~3;  // (16-byte aligned start of the copy)
     if constexpr (MODE == M_G13) {
-#pragma unroll
-        for (int mt = 0; mt < NTW; mt++) {
-            const int m = m0 + min((T0 + mt) * 32 + col, mrows - 1);
-            sca[mt] = p.xs[p.w.pos_tok[bk.base + m]];
-            asm volatile("" : "+v"(sca[mt]));
-        }
+        if (wave == 0)
+            gbld16_lds(grsrc(p.w.pos_xs, (uint32_t)s.T * s.k * 4), lds + kLdsBytes, (uint32_t)xs0 * 4 + lane * 16);
     }
+    uint32_t sca[NTW > 0 ? NTW : 1];
 
     f32x16_t acc[NTW > 0 ? NTW : 1][NB];
 #pragma unroll
@@ -629,6 +649,11 @@ __device__ __forceinline__ bool wave_pass(const GemmParams &p, const Blk &bk, in
                 return false;
             }
         }
+    }
+    if constexpr (MODE == M_G13) {
+        const LDS uint32_t *xsl = reinterpret_cast<const LDS uint32_t *>(lds + kLdsBytes);
+#pragma unroll
+        for (int mt = 0; mt < NTW; mt++) sca[mt] = xsl[bk.base + m0 - xs0 + min((T0 + mt) * 32 + col, mrows - 1)];
     }
     prefetch(0, 0);
     int sl = 0;  // ring slot of stage i
@@ -869,10 +894,13 @@ __device__ __forceinline__ void ggemm_block(const GemmParams &p, int x, LDS uint
     b.base = 0;
     b.e = 0;
     if constexpr (C::kFp4) {
-        if (b.group >= p.w.meta[0]) return;
-        b.e = p.w.active[b.group];
-        b.M = p.w.counts[b.e];
-        b.base = p.w.offsets[b.e];
+        // the group's record {expert, rows, first position}: one scalar load
+        // (b.group < E; the dispatch zeroes the records past the active ones)
+        const i32x4_t g = ((const KCONST i32x4_t *)p.w.ginfo)[b.group];
+        if (g.y <= 0) return;
+        b.e = g.x;
+        b.M = g.y;
+        b.base = g.z;
         b.K = MODE == M_D2 ? s.F : s.d;
     } else {
         b.M = s.T;
@@ -920,7 +948,7 @@ __device__ __forceinline__ void ggemm_block(const GemmParams &p, int x, LDS uint
 template <int MODE>
 __global__ __launch_bounds__(GT) void k_ggemm(GemmParams p)
 {
-    __shared__ __attribute__((aligned(1024))) uint8_t lds_blk[kLdsBytes];
+    __shared__ __attribute__((aligned(1024))) uint8_t lds_blk[kLdsBytes + kMetaBytes];
     // (MXFP4: the scale rows, then the ring)
     ggemm_block<MODE>(p, (int)blockIdx.x, (LDS uint8_t *)lds_blk);
 }
@@ -934,7 +962,7 @@ __global__ __launch_bounds__(GT) void k_ggemm(GemmParams p)
 template <int MODE1, int MODE2>
 __global__ __launch_bounds__(GT) void k_ggemm_pair(GemmParams p1, GemmParams p2, int n1, int n1p)
 {
-    __shared__ __attribute__((aligned(1024))) uint8_t lds_blk[kLdsBytes];
+    __shared__ __attribute__((aligned(1024))) uint8_t lds_blk[kLdsBytes + kMetaBytes];
     const int x = (int)blockIdx.x;
     if (x < n1) ggemm_block<MODE1>(p1, x, (LDS uint8_t *)lds_blk);
     else if (x >= n1p) ggemm_block<MODE2>(p2, x - n1p, (LDS uint8_t *)lds_blk);
@@ -1135,7 +1163,7 @@ static GemmParams make_gemm_params(const Shape &s, const uint16_t *x, const Weig
     p.w = w;
     p.wr3 = reinterpret_cast<const uint16_t *>(w.extra);
     p.xq = w.xq;
-    p.xs = reinterpret_cast<const uint32_t *>(w.xq + ((((size_t)s.T * 2 * s.d) + 255) & ~(size_t)255));
+    p.xs = mfma_token_scales(s, w);
     // the shared H (bf16 hi and lo parts) lives in the fp32 shared-H region
     p.hs_hi = reinterpret_cast<const uint16_t *>(w.Hs);
     p.hs_lo = p.hs_hi + (size_t)s.T * s.S * s.F;
@@ -1167,6 +1195,20 @@ hipError_t launch_mfma_router(const Shape &s, const uint16_t *x, const Weights &
     return hipGetLastError();
 }
 
+// the tokens' E8M0 scales of the MFMA path's token workspace
+const uint32_t *mfma_token_scales(const Shape &s, const Work &w)
+{
+    return reinterpret_cast<const uint32_t *>(w.xq + ((((size_t)s.T * 2 * s.d) + 255) & ~(size_t)255));
+}
+
+// the tokens as two fp8 terms and their scales (the routed gate/up's A
+// operand), ahead of the dispatch, which gathers the scales per position
+hipError_t launch_quant_x(const Shape &s, const uint16_t *x, const Work &w, hipStream_t st)
+{
+    k_quant_x<<<(s.T + 3) / 4, 256, 0, st>>>(s.T, s.d, x, w.xq, const_cast<uint32_t *>(mfma_token_scales(s, w)));
+    return hipGetLastError();
+}
+
 hipError_t launch_mfma_experts(const Shape &s, const uint16_t *x, const Weights &wt,
                                int include_shared, const Work &w, hipStream_t st,
                                hipEvent_t const *ev2)
@@ -1174,8 +1216,6 @@ hipError_t launch_mfma_experts(const Shape &s, const uint16_t *x, const Weights 
     GemmParams p = make_gemm_params(s, x, wt, w);
     const int max_active = min(s.E, s.T * s.k);
     const int mb = (s.T + GM - 1) / GM;
-    // the tokens as two fp8 terms (the routed gate/up's A operand)
-    k_quant_x<<<(s.T + 3) / 4, 256, 0, st>>>(s.T, s.d, x, w.xq, const_cast<uint32_t *>(p.xs));
     // the shared experts (when included) in the same launches as the routed
     // gate/up and down
     const bool sh = include_shared && s.S > 0;

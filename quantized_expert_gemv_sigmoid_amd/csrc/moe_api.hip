@@ -24,7 +24,16 @@ using moe::Work;
 constexpr int32_t kMaxTokens = 1 << 20;
 // AUTO: GEMV up to here, MFMA above (measured at the K3 layer shape: the
 // grouped GEMM is faster from about 32 tokens on, the GEMV below 24)
-constexpr int32_t kGemvMaxTokens = 24;
+// AUTO: the GEMV kernels up to kGemvMaxTokens tokens (at the Kimi-K3 shape
+// the grouped GEMM is faster from 4 tokens up: 0.33 against 0.36 ms at T = 4,
+// 0.91 against 1.22 ms at T = 16); the latent layer's switch is its own.
+// The MFMA path computes the router logits with the front kernel's fp32 rows
+// up to kFrontRouterMaxTokens tokens (one wave per expert row, the tokens in
+// turn: 19 us at T = 2 against 35 us for the router GEMM and its split and
+// reduce), with the router GEMM above.
+constexpr int32_t kGemvMaxTokens = 3;
+constexpr int32_t kLatentGemvMaxTokens = 24;
+constexpr int32_t kFrontRouterMaxTokens = 4;
 
 bool aligned(const void *p, size_t a) { return ((uintptr_t)p % a) == 0; }
 
@@ -102,11 +111,14 @@ size_t carve(const Shape &s, char *base, Work *w)
     v.counts = (int32_t *)take(E * 4);
     v.offsets = (int32_t *)take((E + 1) * 4);
     v.active = (int32_t *)take(E * 4);
+    v.ginfo = (int32_t *)take(E * 16);
     v.meta = (int32_t *)take(16);
     v.masks = (uint64_t *)take(nblk * E * 8);
     v.blk_base = (int32_t *)take(nblk * E * 4);
     v.pos_tok = (int32_t *)take(T * k * 4);
     v.pos_w = (float *)take(T * k * 4);
+    v.pos_xs = (uint32_t *)take(T * k * 4);
+    v.tok_xs = nullptr;
     v.tok_pos = (int32_t *)take(T * k * 4);
     // (one token: the fp16 H of the picks, then the fp32 shared activations)
     v.H = (void *)take(std::max(T * k * (size_t)s.F * 4, k * (size_t)s.F * 2 + (size_t)s.S * s.F * 4));
@@ -203,13 +215,20 @@ moe_status run_layer(const moe_layer_desc *d, const Shape &s, const uint16_t *x,
         return MOE_OK;
     }
     const int front_shared = experts && shared && path == MOE_PATH_GEMV;
-    if (do_router && path == MOE_PATH_MFMA) {
+    if (do_router && path == MOE_PATH_MFMA && s.T > kFrontRouterMaxTokens) {
         MOE_TRY(moe::launch_mfma_router(s, x, wt, w, st));
     } else if (do_router || front_shared) {
         MOE_TRY(moe::launch_front(s, x, wt, do_router, front_shared, w, st));
     }
     MOE_TRY(mark(ev, 1, st));
-    MOE_TRY(moe::launch_dispatch(s, do_router, w.logits, d->router_bias, ids, wts, counts_out, w,
+    // (MFMA path: the tokens' fp8 terms first; the dispatch gathers their
+    // scales per position)
+    Work wd = w;
+    if (experts && path == MOE_PATH_MFMA) {
+        MOE_TRY(moe::launch_quant_x(s, x, w, st));
+        wd.tok_xs = moe::mfma_token_scales(s, w);
+    }
+    MOE_TRY(moe::launch_dispatch(s, do_router, w.logits, d->router_bias, ids, wts, counts_out, wd,
                                  st));
     MOE_TRY(mark(ev, 2, st));
     if (!experts) return MOE_OK;
@@ -298,7 +317,7 @@ bool latent_mfma_supported(const moe_latent_desc *d, int32_t T)
 int latent_path(const moe_latent_desc *d, int32_t T)
 {
     if (d->path == MOE_PATH_GEMV || d->path == MOE_PATH_MFMA) return d->path;
-    return (T > kGemvMaxTokens && latent_mfma_supported(d, T)) ? MOE_PATH_MFMA : MOE_PATH_GEMV;
+    return (T > kLatentGemvMaxTokens && latent_mfma_supported(d, T)) ? MOE_PATH_MFMA : MOE_PATH_GEMV;
 }
 
 size_t carve_latent(const moe_latent_desc *d, int32_t T, char *base, Work *w, moe::LatentBufs *lb)
@@ -320,6 +339,7 @@ size_t carve_latent(const moe_latent_desc *d, int32_t T, char *base, Work *w, mo
     v.counts = (int32_t *)take(E * 4);
     v.offsets = (int32_t *)take((E + 1) * 4);
     v.active = (int32_t *)take(E * 4);
+    v.ginfo = (int32_t *)take(E * 16);
     v.meta = (int32_t *)take(16);
     v.masks = (uint64_t *)take(nblk * E * 8);
     v.blk_base = (int32_t *)take(nblk * E * 4);

@@ -86,6 +86,14 @@ __device__ __forceinline__ int block_scan(int v, int *tmp, int *total)
 
 constexpr int kSmallThreads = 512;  // threads of the one-block dispatch (2 experts each)
 
+// active expert number a is expert e with count c at offset o: the active
+// list, and the record a GEMM block of that group reads in one load
+__device__ __forceinline__ void set_active(const Work &w, int a, int e, int c, int o)
+{
+    w.active[a] = e;
+    *reinterpret_cast<int4 *>(w.ginfo + 4 * a) = make_int4(e, c, o, 0);
+}
+
 // per-expert counts, experts 2 i and 2 i + 1 with thread i (counts c0, c1)
 // -> counts, offsets (into offs[] too), active list, meta
 __device__ __forceinline__ void write_offsets2(int E, int c0, int c1, int *offs, int *tmp,
@@ -102,14 +110,18 @@ __device__ __forceinline__ void write_offsets2(int E, int c0, int c1, int *offs,
         w.counts[e0] = c0;
         w.offsets[e0] = offs[e0] = ex0 & 0xffff;
         if (counts_out) counts_out[e0] = c0;
-        if (c0 > 0) w.active[ex0 >> 16] = e0;
+        if (c0 > 0) set_active(w, ex0 >> 16, e0, c0, ex0 & 0xffff);
     }
     if (e1 < E) {
         w.counts[e1] = c1;
         w.offsets[e1] = offs[e1] = ex1 & 0xffff;
         if (counts_out) counts_out[e1] = c1;
-        if (c1 > 0) w.active[ex1 >> 16] = e1;
+        if (c1 > 0) set_active(w, ex1 >> 16, e1, c1, ex1 & 0xffff);
     }
+    // records past the active ones: zero rows (a GEMM block of such a
+    // group reads only its record)
+    for (int a = e0; a <= e1; a++)
+        if (a < E && a >= (total >> 16)) *reinterpret_cast<int4 *>(w.ginfo + 4 * a) = make_int4(0, 0, 0, 0);
     if (threadIdx.x == 0) {
         w.offsets[E] = total & 0xffff;
         w.meta[0] = total >> 16;
@@ -149,6 +161,7 @@ __device__ __forceinline__ void dispatch_token(int t, int E, int k, const int32_
         const int p = pos_of(id);
         w.pos_tok[p] = t;
         w.pos_w[p] = wsum;
+        if (w.tok_xs) w.pos_xs[p] = w.tok_xs[t];
         tp[rank] = p;
     }
     const int nlead = __builtin_popcountll(leaders);
@@ -246,7 +259,8 @@ __global__ __launch_bounds__(1024) void k_dispatch_scan(Shape s, int nblk, int32
         w.counts[e] = run;
         w.offsets[e] = off;
         if (counts_out) counts_out[e] = run;
-        if (run > 0) w.active[act] = e;
+        if (run > 0) set_active(w, act, e, run, off);
+        if (e >= nact) *reinterpret_cast<int4 *>(w.ginfo + 4 * e) = make_int4(0, 0, 0, 0);
     }
     if (threadIdx.x == 0) {
         w.offsets[E] = total;
