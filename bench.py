@@ -64,8 +64,10 @@ KERNELS = {
     "gemv": {"router_logits": "k_front", "topk_dispatch": "k_dispatch_small/k_topk+k_dispatch_*",
              "expert_gate_up": "k_gemv_gateup", "expert_down": "k_gemv_down", "combine": "k_combine"},
     "mfma": {"router_logits": "k_split_router + k_ggemm<M_R>", "topk_dispatch": "k_topk + k_dispatch_*",
-             "expert_gate_up": "k_ggemm_pair<M_S13, M_G13> (K3 shape, T <= 1280; else k_ggemm<M_S13> + k_ggemm<M_G13>)",
-             "expert_down": "k_ggemm_pair<M_S2, M_D2> (K3 shape, T <= 2304; else k_ggemm<M_S2> + k_ggemm<M_D2>)",
+             "expert_gate_up": "k_ggemm_pair<M_S13, M_G13> (K3 shape, T <= 1280, 4 column tiles per routed block "
+                               "for 32 <= T <= 256; else k_ggemm<M_S13> + k_ggemm<M_G13>)",
+             "expert_down": "k_ggemm_pair<M_S2, M_D2> (K3 shape, T <= 2304, 4 column tiles per routed block for "
+                            "T <= 256; else k_ggemm<M_S2> + k_ggemm<M_D2>)",
              "combine": "k_combine"},
 }
 # steps per timed window of each workload when it is measured as an entry of

@@ -58,7 +58,8 @@ constexpr int GMT = 4;               // 32-row MFMA tiles per M pass, bf16 weigh
 constexpr int GMT4 = 3;              // 32-row MFMA tiles per M pass (at most), MXFP4 weights
 constexpr int GM = GMT * 32;         // rows per M pass
 constexpr int kLdsBytes = 152 * 1024;   // LDS of a block's scale rows and stage ring (one block per CU)
-constexpr int kMetaBytes = 1024;        // and past them: the routed gate/up pass's token scales
+constexpr int kMetaBytes = 2048;        // and past them: the routed gate/up pass's token scales (1 KB), the
+                                        // target of placeholder copies (256 B)
 constexpr int kScaleBytes = 32 * 1024;  // MXFP4: the block's scale rows (256 of at most 128 bytes)
 constexpr uint32_t kPast = 0xF0000000u;  // a buffer offset past every resource: loads return 0, read nothing
 
@@ -190,6 +191,26 @@ struct Ring {
     static_assert(NST >= 3, "ring depth");
 };
 
+// The ring of the several-tiles-per-block GEMM (routed modes, one 32-row
+// tile per pass), after the scale region.  There a tile's scale bytes lie
+// as in memory, where they are contiguous: the K / 32 bytes of each of its
+// weight rows, the gate rows then the up rows of a gated tile (row
+// s_row_of(column)), one copy of 8 K / 32 KB per tile.
+template <int MODE>
+struct MRing {
+    using C = Cfg<MODE>;
+    static constexpr int BASE = kScaleBytes;
+    static constexpr int ABYTES = 32 * C::AROW;
+    static constexpr int BBYTES = GN * C::BCOL;
+    static constexpr int STAGE = ABYTES + BBYTES;
+    static constexpr int NMAX = (kLdsBytes - BASE) / STAGE;
+    static constexpr int NST = NMAX < 6 ? NMAX : 6;
+    static constexpr int NA = ABYTES / 1024 / 8;
+    static constexpr int NB = BBYTES / 1024 / 8;
+    static_assert(C::kFp4 && ABYTES % 8192 == 0 && BBYTES % 8192 == 0, "copies");
+    static_assert(NST >= 3, "ring depth");
+};
+
 // K order inside a stage: MFMA step st, lane half kh (lane / 32) and element
 // i (0..7) of a fragment multiply K index kh * KS / 2 + st * 8 + i of the
 // stage, for A and B alike.  A lane's A fragments of a row are then the
@@ -227,7 +248,37 @@ struct Blk {
     int group, tile, mb, ks;
     int M, base, e, K, nS, ncols;
     int kst0;  // first stage of the block's K range
+    int t;     // several tiles per block: group * n_tiles + tile
 };
+
+// Several column tiles per block (routed GEMMs at small T): the block's
+// tiles [t0, t_end) and, out, a bit per tile (from t0) whose W2 scales left
+// the fp16 window (those tiles' rows are computed again on the exact path).
+struct MultiJobs {
+    int t0, t_end;
+    uint32_t bad;
+};
+
+// The block of flattened routed tile t (group t / n_tiles) from its group's
+// record g = {expert, rows, first position}
+template <int MODE>
+__device__ __forceinline__ Blk tile_blk(const GemmParams &p, int t, i32x4_t g)
+{
+    Blk b;
+    b.t = t;
+    b.group = t / p.n_tiles;
+    b.tile = t - b.group * p.n_tiles;
+    b.mb = 0;
+    b.ks = 0;
+    b.e = g.x;
+    b.M = g.y;
+    b.base = g.z;
+    b.K = MODE == M_D2 ? p.s.F : p.s.d;
+    b.nS = b.K / Cfg<MODE>::KS;
+    b.kst0 = 0;
+    b.ncols = Cfg<MODE>::kGated ? p.s.F : p.s.d;
+    return b;
+}
 
 // block column c (0..255) of a gated tile -> feature: the SIMD's columns
 // 64 g .. 64 g + 63 hold features tile * 128 + g * 32 + 0..31, the gate ones
@@ -284,466 +335,19 @@ __device__ __forceinline__ void load_scales(const GemmParams &p, const Blk &b, L
     }
 }
 
-// The pass of one wave over its NTW tiles (tiles T0 .. T0 + NTW - 1 of the
-// pass's MT), all stages of K, then its epilogue.  Every wave of the block
-// issues its share of every stage's copies and meets every barrier, whatever
-// its NTW (0 included).
-template <int MODE, int MT, int NTW, int T0, bool SPLIT, int NB>
-__device__ __forceinline__ bool wave_pass(const GemmParams &p, const Blk &bk, int m0, int mrows, LDS uint8_t *lds, bool check)
+// The epilogue of a wave's NTW tiles (pass tiles T0 ..) of an M pass: the
+// activations into H (gated modes), or the outputs (times the routing
+// weight for the routed down) into their rows.
+template <int MODE, int NTW, int T0, int NB>
+__device__ __forceinline__ void pass_epilogue(const GemmParams &p, const Blk &bk, int m0, int mrows,
+                                              f32x16_t (&acc)[NTW > 0 ? NTW : 1][NB])
 {
     using C = Cfg<MODE>;
-    using RG = Ring<MODE, MT>;
-    constexpr int NST = RG::NST, STEPS = C::STEPS, AROW = C::AROW;
     const Shape &s = p.s;
     const int lane = threadIdx.x & 63, wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int col = lane & 31, kh = lane >> 5;
-    const int cg = wave & 3;  // the SIMD's column group
-    // the wave's 32-column tile nb (0 .. NB - 1) is the SIMD's column tile
-    // nb (NB = 2) or wave / 4 (NB = 1: the SIMD's two waves split the
-    // columns, each taking every row tile of the pass)
+    const int cg = wave & 3;
     auto cn = [&](int nb) __attribute__((always_inline)) { return NB == 2 ? nb : (wave >> 2); };
-    const int nS = bk.nS;
-    LDS uint8_t *ring = lds + RG::BASE;
-    const LDS uint8_t *scl = lds;  // (MXFP4) the block's scale rows
-
-    // ---- A copies: copy j of wave w fills rows RPI n .. RPI n + RPI - 1 of
-    // the stage, n = 8 j + w (RPI = 1024 / AROW rows per copy); lane i writes
-    // slot i % ASLOTS of row RPI n + i / ASLOTS, which holds piece
-    // slot ^ swz_a(row).  Rows past the group's end read nothing (zeros,
-    // never stored).  Byte offsets are 32-bit: the host checks that every A
-    // operand is below 2 GiB.
-    __amdgpu_buffer_rsrc_t ra0, ra1;  // (ra1: the shared down's lo half of K)
-    uint32_t aoff[RG::NA];
-    {
-        uint32_t abytes;
-        const uint8_t *abase;
-        if constexpr (MODE == M_G13) {
-            abase = p.xq;
-            abytes = (uint32_t)s.T * s.d * 2;
-        } else if constexpr (MODE == M_D2) {
-            abase = reinterpret_cast<const uint8_t *>(p.w.H);
-            abytes = (uint32_t)s.T * s.k * s.F * 2;
-        } else if constexpr (MODE == M_S2) {
-            abase = reinterpret_cast<const uint8_t *>(p.hs_hi);
-            abytes = (uint32_t)s.T * s.S * s.F * 2;
-        } else if constexpr (MODE == M_G13H) {
-            abase = reinterpret_cast<const uint8_t *>(p.zh);
-            abytes = (uint32_t)s.T * s.d * 2;
-        } else {
-            abase = reinterpret_cast<const uint8_t *>(p.x);
-            abytes = (uint32_t)s.T * s.d * 2;
-        }
-        ra0 = grsrc(abase, abytes);
-        ra1 = MODE == M_S2 ? grsrc(p.hs_lo, abytes) : ra0;
-        constexpr int RPI = 1024 / AROW;
-        static_assert(RPI * C::ASLOTS == 64, "rows per copy");
-#pragma unroll
-        for (int j = 0; j < RG::NA; j++) {
-            const int r = RPI * (8 * j + wave) + lane / C::ASLOTS;
-            const int q = (lane % C::ASLOTS) ^ swz_a<MODE>(r);
-            const int m = m0 + min(r, mrows - 1);
-            // gathered rows (routed gate/up): the copy's RPI rows are the same
-            // for the whole wave, so their tokens come in by scalar loads
-            // (no round trip through the vector memory queue before the
-            // block's first copy), and each lane takes its row's
-            int tok = 0;
-            if constexpr (MODE == M_G13 || MODE == M_G13H) {
-                const KCONST int32_t *pt = (const KCONST int32_t *)p.w.pos_tok + bk.base + m0;
-                const int r0 = RPI * (8 * j + wave);
-                tok = pt[min(r0, mrows - 1)];
-#pragma unroll
-                for (int u = 1; u < RPI; u++) {
-                    const int tu = pt[min(r0 + u, mrows - 1)];
-                    tok = lane / C::ASLOTS == u ? tu : tok;
-                }
-            }
-            uint32_t e;  // byte offset of the row, and of piece q in it
-            if constexpr (MODE == M_G13) {
-                // pieces 0-7: the hi fp8 bytes of the stage, 8-15: the lo ones
-                e = (uint32_t)tok * (2 * s.d) + (q >= 8 ? s.d : 0) + (q & 7) * 16;
-            } else {
-                uint32_t el;  // element offset
-                if constexpr (MODE == M_D2) el = (uint32_t)(bk.base + m) * s.F;
-                else if constexpr (MODE == M_S2) el = (uint32_t)m * s.S * s.F + (uint32_t)bk.group * s.F;
-                else if constexpr (MODE == M_G13H) el = (uint32_t)tok * s.d;
-                else el = (uint32_t)m * s.d;
-                e = el * 2 + q * 16;
-            }
-            aoff[j] = r < mrows ? e : kPast;
-        }
-    }
-    // ---- B copies: copy j of wave w fills the stage's B pieces 64 n .. 64 n
-    // + 63, n = 8 j + w: piece t is slot t % BP of column t / BP, holding piece
-    // slot ^ swz_b(column) of the column's run of the stage; the BP lanes of
-    // a column read one contiguous run.  The copy's columns share a matrix.
-    __amdgpu_buffer_rsrc_t rb[RG::NB];
-    uint32_t boff[RG::NB];
-#pragma unroll
-    for (int j = 0; j < RG::NB; j++) {
-        const int t = 64 * (8 * j + wave) + lane;
-        const int c = t / C::BP;
-        const int pc = (t % C::BP) ^ swz_b<MODE>(c);
-        const int c0 = 64 * (8 * j + wave) / C::BP;  // the copy's first column (uniform)
-        const bool up = (c0 >> 5) & 1;               // gated: the up matrix
-        if constexpr (MODE == M_G13 || MODE == M_G13H) {
-            const uint32_t qb = (uint32_t)s.F * (s.d / 2);
-            rb[j] = grsrc((up ? p.w3q : p.w1q) + (size_t)bk.e * qb, qb);
-        } else if constexpr (MODE == M_D2) {
-            const uint32_t qb = (uint32_t)s.d * (s.F / 2);
-            rb[j] = grsrc(p.w2q + (size_t)bk.e * qb, qb);
-        } else if constexpr (MODE == M_S13) {
-            const uint32_t qb = (uint32_t)s.F * s.d * 2;
-            rb[j] = grsrc(reinterpret_cast<const uint8_t *>(up ? p.sh3 : p.sh1) + (size_t)bk.group * qb, qb);
-        } else if constexpr (MODE == M_S2) {
-            const uint32_t qb = (uint32_t)s.d * s.F * 2;
-            rb[j] = grsrc(reinterpret_cast<const uint8_t *>(p.sh2) + (size_t)bk.group * qb, qb);
-        } else {
-            rb[j] = grsrc(p.wr3, (uint32_t)s.E * p.rparts * s.d * 2);
-        }
-        boff[j] = b_row<MODE>(p, bk, c) + pc * 16;
-    }
-
-    // stage i (of the block's range) into ring slot sl; past the end the
-    // copies read nothing and fill a slot no stage reads
-    auto issue = [&](int i, int sl) __attribute__((always_inline)) {
-        const int sa = i + bk.kst0;
-        const bool ok = i < nS;
-        LDS uint8_t *st = ring + sl * RG::STAGE;
-        // A
-        int kk = sa * C::KS;
-        bool hi = true;
-        if constexpr (MODE == M_S2) {
-            hi = kk < s.F;  // K runs over [hi parts | lo parts]
-            kk = hi ? kk : kk - s.F;
-        } else if constexpr (MODE == M_R) {
-            kk = kk % s.d;  // K runs over [x | x | x]
-        }
-        // (bytes per A element of a stage row: 1 for each fp8 term, else 2)
-        constexpr uint32_t EB = MODE == M_G13 ? 1 : 2;
-#pragma unroll
-        for (int j = 0; j < RG::NA; j++)
-            gbld16_lds(hi ? ra0 : ra1, st + (8 * j + wave) * 1024, ok ? aoff[j] + (uint32_t)kk * EB : kPast);
-        // B
-        uint32_t kb = (uint32_t)sa * C::BCOL;  // byte offset of the stage in a B row
-        if constexpr (MODE == M_S2) kb = (uint32_t)((sa * C::KS) % s.F) * 2;  // repeats for hi / lo
-#pragma unroll
-        for (int j = 0; j < RG::NB; j++)
-            gbld16_lds(rb[j], st + RG::ABYTES + (8 * j + wave) * 1024, ok ? boff[j] + kb : kPast);
-    };
-
-    // (G13) the E8M0 scales of the pass's token rows (hi term in byte 0, lo
-    // term in byte 1, gathered per position by the dispatch): wave 0 copies
-    // them to LDS past the ring ahead of the stage copies, so the first
-    // stage's wait covers them; the lanes read their rows' after it
-    const int xs0 = (bk.base + m0) & ~3;  // (16-byte aligned start of the copy)
-    if constexpr (MODE == M_G13) {
-        if (wave == 0)
-            gbld16_lds(grsrc(p.w.pos_xs, (uint32_t)s.T * s.k * 4), lds + kLdsBytes, (uint32_t)xs0 * 4 + lane * 16);
-    }
-    uint32_t sca[NTW > 0 ? NTW : 1];
-
-    f32x16_t acc[NTW > 0 ? NTW : 1][NB];
-#pragma unroll
-    for (int i = 0; i < (NTW > 0 ? NTW : 1); i++)
-#pragma unroll
-        for (int nb = 0; nb < NB; nb++) acc[i][nb] = (f32x16_t)0.0f;
-
-    const int sa_ = swz_a<MODE>(col), sb_ = swz_b<MODE>(col);
-    // A fragment of pass tile T0 + mt, step st: row (T0 + mt) * 32 + col, piece kh * STEPS + st
-    auto a_frag = [&](const LDS uint8_t *A, int mt, int st) __attribute__((always_inline)) -> uint4 {
-        return lds_ld16(A + ((T0 + mt) * 32 + col) * AROW + (((kh * STEPS + st) ^ sa_) << 4));
-    };
-    // B column of this lane for nb: block column 64 cg + 32 cn(nb) + col
-    auto b_piece = [&](const LDS uint8_t *B, int nb, int pc) __attribute__((always_inline)) -> uint4 {
-        return lds_ld16(B + (cg * 64 + cn(nb) * 32 + col) * C::BCOL + ((pc ^ sb_) << 4));
-    };
-
-    // ---- the stages.  Stage i is multiplied in two halves around one
-    // barrier: its first half's operands (B pieces, scale bytes, the first
-    // half of K's A fragments) were read from LDS during stage i - 1
-    // (prefetch); the first half reads the second half's A fragments and
-    // multiplies; then the barrier (stage i + 1 has landed for every wave,
-    // and every wave has read all of stage i); then stage i + NST's copies
-    // into stage i's slot, the reads of stage i + 1's first-half operands,
-    // and the second half's MFMAs, whose operands are all in registers, so
-    // that the matrix cores work while the barrier's wait and the next reads
-    // are in flight.  Operand registers are single-buffered: the prefetch of
-    // stage i + 1 overwrites registers whose last reader, an MFMA or the
-    // scale masking of stage i, precedes it.
-    //  - G13: half = MFMA step (K 64); the prefetch takes step 0's hi-term A
-    //  - fp16 weights (D2, G13H): half = K 64 (the lane's MX block 0 or 1)
-    //  - bf16 weights (shared experts, router): half = steps 0-1 / 2-3
-    //  - SPLIT (exact fallback): the whole stage in the first half
-    constexpr int HS = STEPS / 2;  // MFMA steps per half (fp16 / bf16)
-    uint4 fq[NB][2];               // B: [nb][block or step] pieces
-    uint32_t fs[NB];               // scale bytes of the lane's columns
-    typedef int i32x8_t __attribute__((ext_vector_type(8)));
-    i32x8_t ga[NTW > 0 ? NTW : 1];               // G13: step 0's hi-term A, [tile]
-    uint4 fa[HS][NTW > 0 ? NTW : 1];             // fp16 / bf16: first half's A, [step][tile]
-    uint4 fb[HS][NB];                            // bf16: first half's B, [step][nb]
-
-    // G13: the step's A fragments of each term and tile.  Lane (col, kh)
-    // takes, of its token row, the 16-byte runs K 64 stp + 16 kh .. + 15 and
-    // 64 stp + 32 + 16 kh .. + 15 (A pieces 4 stp + kh and 4 stp + 2 + kh;
-    // the lo term's 8 later): the A lanes' 32 elements interleave in 16s
-    // against a B lane's contiguous MX block (measured on gfx950).
-    auto g_load = [&](const LDS uint8_t *A, i32x8_t (&at)[NTW > 0 ? NTW : 1], int stp, int tm) __attribute__((always_inline)) {
-#pragma unroll
-        for (int mt = 0; mt < NTW; mt++) {
-            const LDS uint8_t *arow = A + ((T0 + mt) * 32 + col) * AROW;
-            const int q0 = 4 * stp + kh + 8 * tm, q1 = q0 + 2;
-            const uint4 u0 = lds_ld16(arow + ((q0 ^ sa_) << 4));
-            const uint4 u1 = lds_ld16(arow + ((q1 ^ sa_) << 4));
-            at[mt] = (i32x8_t){(int)u0.x, (int)u0.y, (int)u0.z, (int)u0.w,
-                               (int)u1.x, (int)u1.y, (int)u1.z, (int)u1.w};
-        }
-    };
-    // the scale word(s) of the lane's two columns for stage sa: G13 all 4
-    // bytes (MX blocks 0..3 of the stage), fp16 weights the 2 bytes of
-    // half kh (blocks 2 kh, 2 kh + 1)
-    auto scale_word = [&](int sa, int nb) __attribute__((always_inline)) -> uint32_t {
-        const int R = s_row_of<MODE>(cg * 64 + cn(nb) * 32 + col);
-        const LDS uint8_t *p = scl + R * 128 + (((sa >> 2) ^ (R & 7)) << 4) + 4 * (sa & 3);
-        if constexpr (MODE == M_G13) return *reinterpret_cast<const LDS uint32_t *>(p);
-        else return *reinterpret_cast<const LDS uint16_t *>(p + 2 * kh);
-    };
-
-    // stage i's first-half operands, from ring slot sl
-    auto prefetch = [&](int i, int sl) __attribute__((always_inline)) {
-        if constexpr (NTW > 0 && !SPLIT) {
-            const LDS uint8_t *A = ring + sl * RG::STAGE;
-            const LDS uint8_t *B = A + RG::ABYTES;
-            const int sa = i + bk.kst0;
-            if constexpr (C::kFp4) {
-#pragma unroll
-                for (int nb = 0; nb < NB; nb++) {
-                    fs[nb] = scale_word(sa, nb);
-                    // G13: the two steps' blocks 2 stp + kh; fp16: blocks 2 kh, 2 kh + 1
-#pragma unroll
-                    for (int h = 0; h < 2; h++) fq[nb][h] = b_piece(B, nb, MODE == M_G13 ? 2 * h + kh : 2 * kh + h);
-                }
-                if constexpr (MODE == M_G13) {
-                    g_load(A, ga, 0, 0);
-                } else {
-#pragma unroll
-                    for (int st = 0; st < HS; st++)
-#pragma unroll
-                        for (int mt = 0; mt < NTW; mt++) fa[st][mt] = a_frag(A, mt, st);
-                }
-            } else {
-#pragma unroll
-                for (int st = 0; st < HS; st++) {
-#pragma unroll
-                    for (int nb = 0; nb < NB; nb++) fb[st][nb] = b_piece(B, nb, kh * STEPS + st);
-#pragma unroll
-                    for (int mt = 0; mt < NTW; mt++) fa[st][mt] = a_frag(A, mt, st);
-                }
-            }
-        }
-    };
-
-    // the MXFP4 blocks of the prefetched B pieces with their scales: a NaN
-    // scale (255) makes the block contribute 0
-    uint4 qm[NB][2];
-    int scb[NB][2];     // G13: E8M0 scale operands [nb][step]
-    float scf[NB][2];   // fp16: decode scales [nb][block]
-    auto mask_blocks = [&]() __attribute__((always_inline)) {
-#pragma unroll
-        for (int nb = 0; nb < NB; nb++) {
-#pragma unroll
-            for (int h = 0; h < 2; h++) {
-                const uint32_t sc = MODE == M_G13 ? (fs[nb] >> (8 * (2 * h + kh))) & 0xffu : (fs[nb] >> (8 * h)) & 0xffu;
-                const uint32_t keep = sc == 255u ? 0u : ~0u;
-                qm[nb][h] = make_uint4(fq[nb][h].x & keep, fq[nb][h].y & keep, fq[nb][h].z & keep, fq[nb][h].w & keep);
-                if constexpr (MODE == M_G13) scb[nb][h] = (int)(sc == 255u ? 127u : sc);
-                else scf[nb][h] = e8m0f(sc == 255u ? 127u : sc);
-            }
-        }
-    };
-    // G13: the MFMAs of term tm of step stp, over all accumulators (the
-    // four of a term never depend on each other); the token row's scale
-    // register holds the hi term's byte in byte 0 and the lo term's in byte 1
-    auto g_mfma = [&](const i32x8_t (&at)[NTW > 0 ? NTW : 1], int stp, int tm) __attribute__((always_inline)) {
-#pragma unroll
-        for (int mt = 0; mt < NTW; mt++)
-#pragma unroll
-            for (int nb = 0; nb < NB; nb++) {
-                const uint4 bq = qm[nb][stp];
-                const i32x8_t bv = {(int)bq.x, (int)bq.y, (int)bq.z, (int)bq.w, 0, 0, 0, 0};
-                if (tm == 0)
-                    acc[mt][nb] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(
-                        at[mt], bv, acc[mt][nb], 0, 4, 0, (int)sca[mt], 0, scb[nb][stp]);
-                else
-                    acc[mt][nb] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(
-                        at[mt], bv, acc[mt][nb], 0, 4, 1, (int)sca[mt], 0, scb[nb][stp]);
-            }
-    };
-    using BT = typename std::conditional<(MODE == M_D2 || MODE == M_G13H) && !SPLIT, f16x8_t, bf16x8_t>::type;
-    // fp16 weights: steps h HS .. h HS + HS - 1 (MX block h of each column),
-    // each step's B decoded one step ahead of its MFMAs
-    auto f_half = [&](const uint4 (&av)[HS][NTW > 0 ? NTW : 1], int h) __attribute__((always_inline)) {
-        BT b[2][NB];
-        auto decode = [&](BT (&bb)[NB], int st) __attribute__((always_inline)) {
-#pragma unroll
-            for (int nb = 0; nb < NB; nb++) {
-                const uint32_t w = u4at(qm[nb][h], st);
-                if constexpr (std::is_same<BT, f16x8_t>::value) bb[nb] = cvt8_f16(w, scf[nb][h]);
-                else bb[nb] = cvt8_bf16(w, scf[nb][h]);
-            }
-        };
-        decode(b[0], 0);
-#pragma unroll
-        for (int st = 0; st < HS; st++) {
-            const int cur = st & 1, nxt = cur ^ 1;
-            if (st + 1 < HS) decode(b[nxt], st + 1);
-#pragma unroll
-            for (int mt = 0; mt < NTW; mt++)
-#pragma unroll
-                for (int nb = 0; nb < NB; nb++)
-                    acc[mt][nb] = mfma32(__builtin_bit_cast(BT, av[st][mt]), b[cur][nb], acc[mt][nb]);
-        }
-    };
-    auto b_half = [&](const uint4 (&av)[HS][NTW > 0 ? NTW : 1], const uint4 (&bv)[HS][NB]) __attribute__((always_inline)) {
-#pragma unroll
-        for (int st = 0; st < HS; st++)
-#pragma unroll
-            for (int mt = 0; mt < NTW; mt++)
-#pragma unroll
-                for (int nb = 0; nb < NB; nb++)
-                    acc[mt][nb] = mfma32(__builtin_bit_cast(bf16x8_t, av[st][mt]),
-                                         __builtin_bit_cast(bf16x8_t, bv[st][nb]), acc[mt][nb]);
-    };
-
-    // ---- K loop.  The prologue issues stages 0 .. NST - 1 (every slot);
-    // stage i + NST's copies are issued after iteration i's barrier, into
-    // stage i's slot, so at that barrier the copies of the NST - 2 stages
-    // after stage i + 1 may still be in flight
-    constexpr int NPS = RG::NA + RG::NB;  // copies per wave per stage
-#pragma unroll
-    for (int i = 0; i < NST; i++) issue(i, i);
-    wait_vm<(NST - 1) * NPS>();
-    block_barrier();
-    if constexpr ((MODE == M_D2 || MODE == M_G13H) && !SPLIT) {
-        // (the scale rows landed with stage 0's copies, which followed
-        // them): thread t checks scale row t; on a byte outside the fp16
-        // window the stages in flight are drained and the caller takes the
-        // split path
-        if (check) {
-            bool ok = true;
-            if (threadIdx.x < GN) {
-                const int R = threadIdx.x;
-                const int nbytes = (MODE == M_D2 ? s.F : s.d) / 32;
-                for (int q = 0; q * 16 < nbytes; q++) {
-                    const uint4 v = lds_ld16(scl + R * 128 + ((q ^ (R & 7)) << 4));
-                    const uint32_t w[4] = {v.x, v.y, v.z, v.w};
-#pragma unroll
-                    for (int k = 0; k < 16; k++) {
-                        const uint32_t by = (w[k >> 2] >> (8 * (k & 3))) & 0xffu;
-                        ok = ok && (q * 16 + k >= nbytes || by == 255u || (by - 104u) <= 36u);
-                    }
-                }
-            }
-            if (!__syncthreads_and(ok)) {
-                wait_vm<0>();
-                block_barrier();
-                return false;
-            }
-        }
-    }
-    if constexpr (MODE == M_G13) {
-        const LDS uint32_t *xsl = reinterpret_cast<const LDS uint32_t *>(lds + kLdsBytes);
-#pragma unroll
-        for (int mt = 0; mt < NTW; mt++) sca[mt] = xsl[bk.base + m0 - xs0 + min((T0 + mt) * 32 + col, mrows - 1)];
-    }
-    prefetch(0, 0);
-    int sl = 0;  // ring slot of stage i
-    for (int i = 0; i < nS; i++) {
-        const int sln = sl == NST - 1 ? 0 : sl + 1;
-        const LDS uint8_t *A = ring + sl * RG::STAGE;
-        // -- first half (and the reads of the second half's A)
-        i32x8_t g0l[NTW > 0 ? NTW : 1], g1h[NTW > 0 ? NTW : 1], g1l[NTW > 0 ? NTW : 1];
-        uint4 a2[HS][NTW > 0 ? NTW : 1], b2[HS][NB];
-        if constexpr (NTW > 0) {
-            if constexpr (MODE == M_G13) {
-                g_load(A, g0l, 0, 1);
-                g_load(A, g1h, 1, 0);
-                g_load(A, g1l, 1, 1);
-                mask_blocks();
-                g_mfma(ga, 0, 0);
-                g_mfma(g0l, 0, 1);
-            } else if constexpr (C::kFp4 && !SPLIT) {
-#pragma unroll
-                for (int st = 0; st < HS; st++)
-#pragma unroll
-                    for (int mt = 0; mt < NTW; mt++) a2[st][mt] = a_frag(A, mt, HS + st);
-                mask_blocks();
-                f_half(fa, 0);
-            } else if constexpr (C::kFp4) {
-                // exact fallback: bf16 weights, fp16 inputs split in two bf16
-                // parts, the whole stage here
-                const LDS uint8_t *B = A + RG::ABYTES;
-                const int sa = i + bk.kst0;
-#pragma unroll
-                for (int nb = 0; nb < NB; nb++) {
-                    fs[nb] = scale_word(sa, nb);
-#pragma unroll
-                    for (int h = 0; h < 2; h++) fq[nb][h] = b_piece(B, nb, 2 * kh + h);
-                }
-                mask_blocks();
-#pragma unroll
-                for (int st = 0; st < STEPS; st++) {
-                    bf16x8_t b[NB];
-#pragma unroll
-                    for (int nb = 0; nb < NB; nb++) b[nb] = cvt8_bf16(u4at(qm[nb][st / HS], st % HS), scf[nb][st / HS]);
-#pragma unroll
-                    for (int mt = 0; mt < NTW; mt++) {
-                        bf16x8_t ah, al;
-                        split_f16(__builtin_bit_cast(f16x8_t, a_frag(A, mt, st)), ah, al);
-#pragma unroll
-                        for (int nb = 0; nb < NB; nb++) {
-                            acc[mt][nb] = mfma32(ah, b[nb], acc[mt][nb]);
-                            acc[mt][nb] = mfma32(al, b[nb], acc[mt][nb]);
-                        }
-                    }
-                }
-            } else {
-                const LDS uint8_t *B = A + RG::ABYTES;
-#pragma unroll
-                for (int st = 0; st < HS; st++) {
-#pragma unroll
-                    for (int nb = 0; nb < NB; nb++) b2[st][nb] = b_piece(B, nb, kh * STEPS + HS + st);
-#pragma unroll
-                    for (int mt = 0; mt < NTW; mt++) a2[st][mt] = a_frag(A, mt, HS + st);
-                }
-                b_half(fa, fb);
-            }
-        }
-        // -- stage i + 1 has landed for every wave, and every wave has read
-        // all of stage i: its slot takes stage i + NST.  (The scheduling
-        // fences keep the first half's MFMAs ahead of the wait; the last
-        // iteration's prefetch reads a slot no stage uses, and is not used.)
-        __builtin_amdgcn_sched_barrier(0);
-        wait_vm<(NST - 2) * NPS>();
-        block_barrier();
-        __builtin_amdgcn_sched_barrier(0);
-        issue(i + NST, sl);
-        prefetch(i + 1 < nS ? i + 1 : i, sln);
-        // -- second half, from registers
-        if constexpr (NTW > 0) {
-            if constexpr (MODE == M_G13) {
-                g_mfma(g1h, 1, 0);
-                g_mfma(g1l, 1, 1);
-            }
-            else if constexpr (C::kFp4 && !SPLIT) f_half(a2, 1);
-            else if constexpr (!C::kFp4) b_half(a2, b2);
-        }
-        sl = sln;
-    }
-    // the ring is reused by the next pass: every copy (past-the-end ones
-    // included) must have landed, and every wave be done reading
-    wait_vm<0>();
-    block_barrier();
-
     if constexpr (NTW > 0) {
         // ---- epilogue (D lane layout: register e of tile (mt, nb) holds row
         // 8 (e / 4) + 4 kh + e % 4 of the tile, column nb * 32 + col of the
@@ -837,6 +441,621 @@ __device__ __forceinline__ bool wave_pass(const GemmParams &p, const Blk &bk, in
             }
         }
     }
+}
+
+// The pass of one wave over its NTW tiles (tiles T0 .. T0 + NTW - 1 of the
+// pass's MT), all stages of K, then its epilogue.  Every wave of the block
+// issues its share of every stage's copies and meets every barrier, whatever
+// its NTW (0 included).
+//
+// MULTI (routed modes, MT = 1): the passes of the block's tiles mj->t0 ..
+// mj->t_end - 1 (one per 32 rows of a tile; bk, m0, mrows: the first) run
+// as one sequence of stages through one ring, each pass's epilogue in the
+// stage after its last: the copies of the next pass's first stages are in
+// flight meanwhile.  The routed down checks each stage's scale bytes as it
+// multiplies them: a tile whose bytes leave the fp16 window stores nothing
+// and is marked in mj->bad for the exact path.
+template <int MODE, int MT, int NTW, int T0, bool SPLIT, int NB, bool MULTI = false>
+__device__ __forceinline__ bool wave_pass(const GemmParams &p, const Blk &bk_in, int m0_in, int mrows_in, LDS uint8_t *lds,
+                                          bool check, MultiJobs *mj = nullptr)
+{
+    using C = Cfg<MODE>;
+    using RG = typename std::conditional<MULTI, MRing<MODE>, Ring<MODE, MT>>::type;
+    static_assert(!MULTI || (MT == 1 && !SPLIT && C::kFp4 && MODE != M_G13H), "several tiles per block: routed, MT 1");
+    constexpr int NST = RG::NST, STEPS = C::STEPS, AROW = C::AROW;
+    Blk bk = bk_in;  // the pass being multiplied (MULTI: each in turn)
+    int m0 = m0_in, mrows = mrows_in;
+    const Shape &s = p.s;
+    const int lane = threadIdx.x & 63, wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int col = lane & 31, kh = lane >> 5;
+    const int cg = wave & 3;  // the SIMD's column group
+    // the wave's 32-column tile nb (0 .. NB - 1) is the SIMD's column tile
+    // nb (NB = 2) or wave / 4 (NB = 1: the SIMD's two waves split the
+    // columns, each taking every row tile of the pass)
+    auto cn = [&](int nb) __attribute__((always_inline)) { return NB == 2 ? nb : (wave >> 2); };
+    const int nS = bk.nS;
+    LDS uint8_t *ring = lds + RG::BASE;
+    const LDS uint8_t *scl = lds;  // (MXFP4) the block's scale rows
+
+    // ---- A copies: copy j of wave w fills rows RPI n .. RPI n + RPI - 1 of
+    // the stage, n = 8 j + w (RPI = 1024 / AROW rows per copy); lane i writes
+    // slot i % ASLOTS of row RPI n + i / ASLOTS, which holds piece
+    // slot ^ swz_a(row).  Rows past the group's end read nothing (zeros,
+    // never stored).  Byte offsets are 32-bit: the host checks that every A
+    // operand is below 2 GiB.
+    __amdgpu_buffer_rsrc_t ra0, ra1;  // (ra1: the shared down's lo half of K)
+    {
+        uint32_t abytes;
+        const uint8_t *abase;
+        if constexpr (MODE == M_G13) {
+            abase = p.xq;
+            abytes = (uint32_t)s.T * s.d * 2;
+        } else if constexpr (MODE == M_D2) {
+            abase = reinterpret_cast<const uint8_t *>(p.w.H);
+            abytes = (uint32_t)s.T * s.k * s.F * 2;
+        } else if constexpr (MODE == M_S2) {
+            abase = reinterpret_cast<const uint8_t *>(p.hs_hi);
+            abytes = (uint32_t)s.T * s.S * s.F * 2;
+        } else if constexpr (MODE == M_G13H) {
+            abase = reinterpret_cast<const uint8_t *>(p.zh);
+            abytes = (uint32_t)s.T * s.d * 2;
+        } else {
+            abase = reinterpret_cast<const uint8_t *>(p.x);
+            abytes = (uint32_t)s.T * s.d * 2;
+        }
+        ra0 = grsrc(abase, abytes);
+        ra1 = MODE == M_S2 ? grsrc(p.hs_lo, abytes) : ra0;
+    }
+    uint32_t aoff[RG::NA];
+    __amdgpu_buffer_rsrc_t rb[RG::NB];
+    uint32_t boff[RG::NB];
+    // the copies' sources for pass (b, bm0, bmrows)
+    auto set_addr = [&](const Blk &b, int bm0, int bmrows) __attribute__((always_inline)) {
+        constexpr int RPI = 1024 / AROW;
+        static_assert(RPI * C::ASLOTS == 64, "rows per copy");
+#pragma unroll
+        for (int j = 0; j < RG::NA; j++) {
+            const int r = RPI * (8 * j + wave) + lane / C::ASLOTS;
+            const int q = (lane % C::ASLOTS) ^ swz_a<MODE>(r);
+            const int m = bm0 + min(r, bmrows - 1);
+            // gathered rows (routed gate/up): the copy's RPI rows are the same
+            // for the whole wave, so their tokens come in by scalar loads
+            // (no round trip through the vector memory queue before the
+            // block's first copy), and each lane takes its row's
+            int tok = 0;
+            if constexpr (MODE == M_G13 || MODE == M_G13H) {
+                const KCONST int32_t *pt = (const KCONST int32_t *)p.w.pos_tok + b.base + bm0;
+                const int r0 = RPI * (8 * j + wave);
+                tok = pt[min(r0, bmrows - 1)];
+#pragma unroll
+                for (int u = 1; u < RPI; u++) {
+                    const int tu = pt[min(r0 + u, bmrows - 1)];
+                    tok = lane / C::ASLOTS == u ? tu : tok;
+                }
+            }
+            uint32_t e;  // byte offset of the row, and of piece q in it
+            if constexpr (MODE == M_G13) {
+                // pieces 0-7: the hi fp8 bytes of the stage, 8-15: the lo ones
+                e = (uint32_t)tok * (2 * s.d) + (q >= 8 ? s.d : 0) + (q & 7) * 16;
+            } else {
+                uint32_t el;  // element offset
+                if constexpr (MODE == M_D2) el = (uint32_t)(b.base + m) * s.F;
+                else if constexpr (MODE == M_S2) el = (uint32_t)m * s.S * s.F + (uint32_t)b.group * s.F;
+                else if constexpr (MODE == M_G13H) el = (uint32_t)tok * s.d;
+                else el = (uint32_t)m * s.d;
+                e = el * 2 + q * 16;
+            }
+            aoff[j] = r < bmrows ? e : kPast;
+        }
+        // ---- B copies: copy j of wave w fills the stage's B pieces 64 n ..
+        // 64 n + 63, n = 8 j + w: piece t is slot t % BP of column t / BP,
+        // holding piece slot ^ swz_b(column) of the column's run of the
+        // stage; the BP lanes of a column read one contiguous run.  The
+        // copy's columns share a matrix.
+#pragma unroll
+        for (int j = 0; j < RG::NB; j++) {
+            const int t = 64 * (8 * j + wave) + lane;
+            const int c = t / C::BP;
+            const int pc = (t % C::BP) ^ swz_b<MODE>(c);
+            const int c0 = 64 * (8 * j + wave) / C::BP;  // the copy's first column (uniform)
+            const bool up = (c0 >> 5) & 1;               // gated: the up matrix
+            if constexpr (MODE == M_G13 || MODE == M_G13H) {
+                const uint32_t qb = (uint32_t)s.F * (s.d / 2);
+                rb[j] = grsrc((up ? p.w3q : p.w1q) + (size_t)b.e * qb, qb);
+            } else if constexpr (MODE == M_D2) {
+                const uint32_t qb = (uint32_t)s.d * (s.F / 2);
+                rb[j] = grsrc(p.w2q + (size_t)b.e * qb, qb);
+            } else if constexpr (MODE == M_S13) {
+                const uint32_t qb = (uint32_t)s.F * s.d * 2;
+                rb[j] = grsrc(reinterpret_cast<const uint8_t *>(up ? p.sh3 : p.sh1) + (size_t)b.group * qb, qb);
+            } else if constexpr (MODE == M_S2) {
+                const uint32_t qb = (uint32_t)s.d * s.F * 2;
+                rb[j] = grsrc(reinterpret_cast<const uint8_t *>(p.sh2) + (size_t)b.group * qb, qb);
+            } else {
+                rb[j] = grsrc(p.wr3, (uint32_t)s.E * p.rparts * s.d * 2);
+            }
+            boff[j] = b_row<MODE>(p, b, c) + pc * 16;
+        }
+    };
+    set_addr(bk, m0, mrows);
+
+    // stage sa (of K) into ring slot sl from the sources set_addr set; not
+    // ok (past the end): the copies read nothing and fill a slot no stage
+    // reads
+    auto issue_at = [&](int sa, bool ok, int sl) __attribute__((always_inline)) {
+        LDS uint8_t *st = ring + sl * RG::STAGE;
+        // A
+        int kk = sa * C::KS;
+        bool hi = true;
+        if constexpr (MODE == M_S2) {
+            hi = kk < s.F;  // K runs over [hi parts | lo parts]
+            kk = hi ? kk : kk - s.F;
+        } else if constexpr (MODE == M_R) {
+            kk = kk % s.d;  // K runs over [x | x | x]
+        }
+        // (bytes per A element of a stage row: 1 for each fp8 term, else 2)
+        constexpr uint32_t EB = MODE == M_G13 ? 1 : 2;
+#pragma unroll
+        for (int j = 0; j < RG::NA; j++)
+            gbld16_lds(hi ? ra0 : ra1, st + (8 * j + wave) * 1024, ok ? aoff[j] + (uint32_t)kk * EB : kPast);
+        // B
+        uint32_t kb = (uint32_t)sa * C::BCOL;  // byte offset of the stage in a B row
+        if constexpr (MODE == M_S2) kb = (uint32_t)((sa * C::KS) % s.F) * 2;  // repeats for hi / lo
+#pragma unroll
+        for (int j = 0; j < RG::NB; j++)
+            gbld16_lds(rb[j], st + RG::ABYTES + (8 * j + wave) * 1024, ok ? boff[j] + kb : kPast);
+    };
+    // stage i of the pass into ring slot sl
+    auto issue = [&](int i, int sl) __attribute__((always_inline)) { issue_at(i + bk.kst0, i < nS, sl); };
+
+    // (G13) the E8M0 scales of the pass's token rows (hi term in byte 0, lo
+    // term in byte 1, gathered per position by the dispatch): wave 0 copies
+    // them to LDS past the ring ahead of the stage copies, so the first
+    // stage's wait covers them; the lanes read their rows' after it
+    auto xs_copy = [&](const Blk &b, int bm0) __attribute__((always_inline)) {
+        if constexpr (MODE == M_G13) {
+            if (wave == 0)
+                gbld16_lds(grsrc(p.w.pos_xs, (uint32_t)s.T * s.k * 4), lds + kLdsBytes,
+                           (uint32_t)((b.base + bm0) & ~3) * 4 + lane * 16);  // (from a 16-byte boundary)
+        }
+    };
+    xs_copy(bk, m0);
+    uint32_t sca[NTW > 0 ? NTW : 1];
+    auto read_sca = [&]() __attribute__((always_inline)) {
+        if constexpr (MODE == M_G13) {
+            const LDS uint32_t *xsl = reinterpret_cast<const LDS uint32_t *>(lds + kLdsBytes);
+            const int o = (bk.base + m0) & 3;
+#pragma unroll
+            for (int mt = 0; mt < NTW; mt++) sca[mt] = xsl[o + min((T0 + mt) * 32 + col, mrows - 1)];
+        }
+    };
+
+    // ---- MULTI: the pass whose stages are being issued (ib, im0, imrows)
+    // and its next stage ist; iok turns false once the last pass's are.
+    // Each pass has more stages than the ring holds, so the passes being
+    // issued and multiplied are the same or consecutive.
+    Blk ib = bk;
+    int im0 = m0, imrows = mrows, ist = 0;
+    bool iok = true;
+    // the pass after (b, bm0): the next 32 rows of its tile, else the next
+    // tile of the block with rows
+    auto next_pass = [&](Blk &b, int &bm0, int &bmrows) __attribute__((always_inline)) -> bool {
+        if (bm0 + 32 < b.M) {
+            bm0 += 32;
+            bmrows = min(32, b.M - bm0);
+            return true;
+        }
+        const int t = b.t + 1;
+        if (t >= mj->t_end) return false;
+        const i32x4_t g = ((const KCONST i32x4_t *)p.w.ginfo)[t / p.n_tiles];
+        if (g.y <= 0) return false;
+        b = tile_blk<MODE>(p, t, g);
+        bm0 = 0;
+        bmrows = min(32, b.M);
+        return true;
+    };
+    // a tile's scale bytes into the scale region (8 KB / 32 K per tile: 1 KB
+    // copies n = 8 j + w, those past the tile's bytes reading nothing)
+    int reg_t = -1;  // the tile whose scale bytes the region holds
+    auto tile_scales = [&](const Blk &b) __attribute__((always_inline)) {
+#pragma unroll
+        for (int j = 0; j < kScaleBytes / 8192; j++) {
+            const int n = 8 * j + wave;
+            __amdgpu_buffer_rsrc_t r;
+            uint32_t off = kPast;
+            if constexpr (C::kGated) {
+                const uint32_t half = 4u * (uint32_t)s.d;  // one matrix's rows of a tile: 128 (d / 32) bytes
+                const uint32_t sb = (uint32_t)s.F * (s.d / 32);
+                const bool up = (uint32_t)n * 1024 >= half;
+                r = grsrc((up ? p.w3s : p.w1s) + (size_t)b.e * sb, sb);
+                const uint32_t o = (uint32_t)n * 1024 - (up ? half : 0u);
+                if (o < half) off = (uint32_t)b.tile * half + o + lane * 16;
+            } else {
+                const uint32_t tot = 8u * (uint32_t)s.F;  // 256 rows of F / 32 bytes
+                const uint32_t sb = (uint32_t)s.d * (s.F / 32);
+                r = grsrc(p.w2s + (size_t)b.e * sb, sb);
+                if ((uint32_t)n * 1024 < tot) off = (uint32_t)b.tile * tot + (uint32_t)n * 1024 + lane * 16;
+            }
+            gbld16_lds(r, lds + n * 1024, off);
+        }
+        reg_t = b.t;
+    };
+    // the next stage of the issuing pass into slot sl (a new tile's scale
+    // bytes first; after the pass's last stage, the pass after it: its
+    // sources, and for the routed gate/up its token scales)
+    auto missue = [&](int sl) __attribute__((always_inline)) {
+        if (ist == 0 && iok && ib.t != reg_t) tile_scales(ib);
+        issue_at(ist, iok, sl);
+        if (iok && ++ist == nS) {
+            ist = 0;
+            iok = next_pass(ib, im0, imrows);
+            if (iok) {
+                set_addr(ib, im0, imrows);
+                xs_copy(ib, im0);
+            }
+        }
+    };
+
+    f32x16_t acc[NTW > 0 ? NTW : 1][NB];
+#pragma unroll
+    for (int i = 0; i < (NTW > 0 ? NTW : 1); i++)
+#pragma unroll
+        for (int nb = 0; nb < NB; nb++) acc[i][nb] = (f32x16_t)0.0f;
+
+    const int sa_ = swz_a<MODE>(col), sb_ = swz_b<MODE>(col);
+    // A fragment of pass tile T0 + mt, step st: row (T0 + mt) * 32 + col, piece kh * STEPS + st
+    auto a_frag = [&](const LDS uint8_t *A, int mt, int st) __attribute__((always_inline)) -> uint4 {
+        return lds_ld16(A + ((T0 + mt) * 32 + col) * AROW + (((kh * STEPS + st) ^ sa_) << 4));
+    };
+    // B column of this lane for nb: block column 64 cg + 32 cn(nb) + col
+    auto b_piece = [&](const LDS uint8_t *B, int nb, int pc) __attribute__((always_inline)) -> uint4 {
+        return lds_ld16(B + (cg * 64 + cn(nb) * 32 + col) * C::BCOL + ((pc ^ sb_) << 4));
+    };
+
+    // ---- the stages.  Stage i is multiplied in two halves around one
+    // barrier: its first half's operands (B pieces, scale bytes, the first
+    // half of K's A fragments) were read from LDS during stage i - 1
+    // (prefetch); the first half reads the second half's A fragments and
+    // multiplies; then the barrier (stage i + 1 has landed for every wave,
+    // and every wave has read all of stage i); then stage i + NST's copies
+    // into stage i's slot, the reads of stage i + 1's first-half operands,
+    // and the second half's MFMAs, whose operands are all in registers, so
+    // that the matrix cores work while the barrier's wait and the next reads
+    // are in flight.  Operand registers are single-buffered: the prefetch of
+    // stage i + 1 overwrites registers whose last reader, an MFMA or the
+    // scale masking of stage i, precedes it.
+    //  - G13: half = MFMA step (K 64); the prefetch takes step 0's hi-term A
+    //  - fp16 weights (D2, G13H): half = K 64 (the lane's MX block 0 or 1)
+    //  - bf16 weights (shared experts, router): half = steps 0-1 / 2-3
+    //  - SPLIT (exact fallback): the whole stage in the first half
+    constexpr int HS = STEPS / 2;  // MFMA steps per half (fp16 / bf16)
+    uint4 fq[NB][2];               // B: [nb][block or step] pieces
+    uint32_t fs[NB];               // scale bytes of the lane's columns
+    typedef int i32x8_t __attribute__((ext_vector_type(8)));
+    i32x8_t ga[NTW > 0 ? NTW : 1];               // G13: step 0's hi-term A, [tile]
+    uint4 fa[HS][NTW > 0 ? NTW : 1];             // fp16 / bf16: first half's A, [step][tile]
+    uint4 fb[HS][NB];                            // bf16: first half's B, [step][nb]
+
+    // G13: the step's A fragments of each term and tile.  Lane (col, kh)
+    // takes, of its token row, the 16-byte runs K 64 stp + 16 kh .. + 15 and
+    // 64 stp + 32 + 16 kh .. + 15 (A pieces 4 stp + kh and 4 stp + 2 + kh;
+    // the lo term's 8 later): the A lanes' 32 elements interleave in 16s
+    // against a B lane's contiguous MX block (measured on gfx950).
+    auto g_load = [&](const LDS uint8_t *A, i32x8_t (&at)[NTW > 0 ? NTW : 1], int stp, int tm) __attribute__((always_inline)) {
+#pragma unroll
+        for (int mt = 0; mt < NTW; mt++) {
+            const LDS uint8_t *arow = A + ((T0 + mt) * 32 + col) * AROW;
+            const int q0 = 4 * stp + kh + 8 * tm, q1 = q0 + 2;
+            const uint4 u0 = lds_ld16(arow + ((q0 ^ sa_) << 4));
+            const uint4 u1 = lds_ld16(arow + ((q1 ^ sa_) << 4));
+            at[mt] = (i32x8_t){(int)u0.x, (int)u0.y, (int)u0.z, (int)u0.w,
+                               (int)u1.x, (int)u1.y, (int)u1.z, (int)u1.w};
+        }
+    };
+    // the scale word(s) of the lane's two columns for stage sa: G13 all 4
+    // bytes (MX blocks 0..3 of the stage), fp16 weights the 2 bytes of
+    // half kh (blocks 2 kh, 2 kh + 1)
+    auto scale_word = [&](int sa, int nb) __attribute__((always_inline)) -> uint32_t {
+        const int R = s_row_of<MODE>(cg * 64 + cn(nb) * 32 + col);
+        const LDS uint8_t *p = scl + R * 128 + (((sa >> 2) ^ (R & 7)) << 4) + 4 * (sa & 3);
+        if constexpr (MODE == M_G13) return *reinterpret_cast<const LDS uint32_t *>(p);
+        else return *reinterpret_cast<const LDS uint16_t *>(p + 2 * kh);
+    };
+    // MULTI: the same from the scale region's rows as in memory; a tile's
+    // last NST - 1 stages' are read ahead into fsc when the next tile's
+    // bytes are due in the region (cached)
+    auto mscale_word = [&](int sa, int nb) __attribute__((always_inline)) -> uint32_t {
+        const int R = s_row_of<MODE>(cg * 64 + cn(nb) * 32 + col);
+        const LDS uint8_t *p = scl + R * (bk.K / 32) + 4 * sa;
+        if constexpr (MODE == M_G13) return *reinterpret_cast<const LDS uint32_t *>(p);
+        else return *reinterpret_cast<const LDS uint16_t *>(p + 2 * kh);
+    };
+    uint32_t fsc[NST - 1][NB];
+    bool cached = false;
+
+    // stage i's first-half operands, from ring slot sl
+    auto prefetch = [&](int i, int sl) __attribute__((always_inline)) {
+        if constexpr (NTW > 0 && !SPLIT) {
+            const LDS uint8_t *A = ring + sl * RG::STAGE;
+            const LDS uint8_t *B = A + RG::ABYTES;
+            const int sa = i + bk.kst0;
+            if constexpr (C::kFp4) {
+#pragma unroll
+                for (int nb = 0; nb < NB; nb++) {
+                    if constexpr (MULTI) fs[nb] = cached && i > nS - NST ? fsc[0][nb] : mscale_word(i, nb);
+                    else fs[nb] = scale_word(sa, nb);
+                    // G13: the two steps' blocks 2 stp + kh; fp16: blocks 2 kh, 2 kh + 1
+#pragma unroll
+                    for (int h = 0; h < 2; h++) fq[nb][h] = b_piece(B, nb, MODE == M_G13 ? 2 * h + kh : 2 * kh + h);
+                }
+                if constexpr (MULTI) {
+                    // (the read-ahead words go in stage order)
+#pragma unroll
+                    for (int k = 0; k + 1 < NST - 1; k++)
+#pragma unroll
+                        for (int nb = 0; nb < NB; nb++) fsc[k][nb] = fsc[k + 1][nb];
+                }
+                if constexpr (MODE == M_G13) {
+                    g_load(A, ga, 0, 0);
+                } else {
+#pragma unroll
+                    for (int st = 0; st < HS; st++)
+#pragma unroll
+                        for (int mt = 0; mt < NTW; mt++) fa[st][mt] = a_frag(A, mt, st);
+                }
+            } else {
+#pragma unroll
+                for (int st = 0; st < HS; st++) {
+#pragma unroll
+                    for (int nb = 0; nb < NB; nb++) fb[st][nb] = b_piece(B, nb, kh * STEPS + st);
+#pragma unroll
+                    for (int mt = 0; mt < NTW; mt++) fa[st][mt] = a_frag(A, mt, st);
+                }
+            }
+        }
+    };
+
+    // the MXFP4 blocks of the prefetched B pieces with their scales: a NaN
+    // scale (255) makes the block contribute 0
+    uint4 qm[NB][2];
+    int scb[NB][2];     // G13: E8M0 scale operands [nb][step]
+    float scf[NB][2];   // fp16: decode scales [nb][block]
+    bool bad = false;   // MULTI, routed down: a scale byte of the pass outside the fp16 window
+    auto mask_blocks = [&]() __attribute__((always_inline)) {
+#pragma unroll
+        for (int nb = 0; nb < NB; nb++) {
+#pragma unroll
+            for (int h = 0; h < 2; h++) {
+                const uint32_t sc = MODE == M_G13 ? (fs[nb] >> (8 * (2 * h + kh))) & 0xffu : (fs[nb] >> (8 * h)) & 0xffu;
+                if constexpr (MULTI && MODE == M_D2) bad = bad || !(sc == 255u || sc - 104u <= 36u);
+                const uint32_t keep = sc == 255u ? 0u : ~0u;
+                qm[nb][h] = make_uint4(fq[nb][h].x & keep, fq[nb][h].y & keep, fq[nb][h].z & keep, fq[nb][h].w & keep);
+                if constexpr (MODE == M_G13) scb[nb][h] = (int)(sc == 255u ? 127u : sc);
+                else scf[nb][h] = e8m0f(sc == 255u ? 127u : sc);
+            }
+        }
+    };
+    // G13: the MFMAs of term tm of step stp, over all accumulators (the
+    // four of a term never depend on each other); the token row's scale
+    // register holds the hi term's byte in byte 0 and the lo term's in byte 1
+    auto g_mfma = [&](const i32x8_t (&at)[NTW > 0 ? NTW : 1], int stp, int tm) __attribute__((always_inline)) {
+#pragma unroll
+        for (int mt = 0; mt < NTW; mt++)
+#pragma unroll
+            for (int nb = 0; nb < NB; nb++) {
+                const uint4 bq = qm[nb][stp];
+                const i32x8_t bv = {(int)bq.x, (int)bq.y, (int)bq.z, (int)bq.w, 0, 0, 0, 0};
+                if (tm == 0)
+                    acc[mt][nb] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(
+                        at[mt], bv, acc[mt][nb], 0, 4, 0, (int)sca[mt], 0, scb[nb][stp]);
+                else
+                    acc[mt][nb] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(
+                        at[mt], bv, acc[mt][nb], 0, 4, 1, (int)sca[mt], 0, scb[nb][stp]);
+            }
+    };
+    using BT = typename std::conditional<(MODE == M_D2 || MODE == M_G13H) && !SPLIT, f16x8_t, bf16x8_t>::type;
+    // fp16 weights: steps h HS .. h HS + HS - 1 (MX block h of each column),
+    // each step's B decoded one step ahead of its MFMAs
+    auto f_half = [&](const uint4 (&av)[HS][NTW > 0 ? NTW : 1], int h) __attribute__((always_inline)) {
+        BT b[2][NB];
+        auto decode = [&](BT (&bb)[NB], int st) __attribute__((always_inline)) {
+#pragma unroll
+            for (int nb = 0; nb < NB; nb++) {
+                const uint32_t w = u4at(qm[nb][h], st);
+                if constexpr (std::is_same<BT, f16x8_t>::value) bb[nb] = cvt8_f16(w, scf[nb][h]);
+                else bb[nb] = cvt8_bf16(w, scf[nb][h]);
+            }
+        };
+        decode(b[0], 0);
+#pragma unroll
+        for (int st = 0; st < HS; st++) {
+            const int cur = st & 1, nxt = cur ^ 1;
+            if (st + 1 < HS) decode(b[nxt], st + 1);
+#pragma unroll
+            for (int mt = 0; mt < NTW; mt++)
+#pragma unroll
+                for (int nb = 0; nb < NB; nb++)
+                    acc[mt][nb] = mfma32(__builtin_bit_cast(BT, av[st][mt]), b[cur][nb], acc[mt][nb]);
+        }
+    };
+    auto b_half = [&](const uint4 (&av)[HS][NTW > 0 ? NTW : 1], const uint4 (&bv)[HS][NB]) __attribute__((always_inline)) {
+#pragma unroll
+        for (int st = 0; st < HS; st++)
+#pragma unroll
+            for (int mt = 0; mt < NTW; mt++)
+#pragma unroll
+                for (int nb = 0; nb < NB; nb++)
+                    acc[mt][nb] = mfma32(__builtin_bit_cast(bf16x8_t, av[st][mt]),
+                                         __builtin_bit_cast(bf16x8_t, bv[st][nb]), acc[mt][nb]);
+    };
+
+    // ---- K loop.  The prologue issues stages 0 .. NST - 1 (every slot);
+    // stage i + NST's copies are issued after iteration i's barrier, into
+    // stage i's slot, so at that barrier the copies of the NST - 2 stages
+    // after stage i + 1 may still be in flight
+    constexpr int NPS = RG::NA + RG::NB;  // copies per wave per stage
+#pragma unroll
+    for (int i = 0; i < NST; i++) {
+        if constexpr (MULTI) missue(i);
+        else issue(i, i);
+    }
+    wait_vm<(NST - 1) * NPS>();
+    block_barrier();
+    if constexpr ((MODE == M_D2 || MODE == M_G13H) && !SPLIT && !MULTI) {
+        // (the scale rows landed with stage 0's copies, which followed
+        // them): thread t checks scale row t; on a byte outside the fp16
+        // window the stages in flight are drained and the caller takes the
+        // split path
+        if (check) {
+            bool ok = true;
+            if (threadIdx.x < GN) {
+                const int R = threadIdx.x;
+                const int nbytes = (MODE == M_D2 ? s.F : s.d) / 32;
+                for (int q = 0; q * 16 < nbytes; q++) {
+                    const uint4 v = lds_ld16(scl + R * 128 + ((q ^ (R & 7)) << 4));
+                    const uint32_t w[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+                    for (int k = 0; k < 16; k++) {
+                        const uint32_t by = (w[k >> 2] >> (8 * (k & 3))) & 0xffu;
+                        ok = ok && (q * 16 + k >= nbytes || by == 255u || (by - 104u) <= 36u);
+                    }
+                }
+            }
+            if (!__syncthreads_and(ok)) {
+                wait_vm<0>();
+                block_barrier();
+                return false;
+            }
+        }
+    }
+    read_sca();
+    prefetch(0, 0);
+    int sl = 0;   // ring slot of stage i
+    int cst = 0;  // MULTI: stage i's place in its pass
+    for (int i = 0; MULTI || i < nS; i++) {
+        const int sln = sl == NST - 1 ? 0 : sl + 1;
+        const LDS uint8_t *A = ring + sl * RG::STAGE;
+        // -- first half (and the reads of the second half's A)
+        i32x8_t g0l[NTW > 0 ? NTW : 1], g1h[NTW > 0 ? NTW : 1], g1l[NTW > 0 ? NTW : 1];
+        uint4 a2[HS][NTW > 0 ? NTW : 1], b2[HS][NB];
+        if constexpr (NTW > 0) {
+            if constexpr (MODE == M_G13) {
+                g_load(A, g0l, 0, 1);
+                g_load(A, g1h, 1, 0);
+                g_load(A, g1l, 1, 1);
+                mask_blocks();
+                g_mfma(ga, 0, 0);
+                g_mfma(g0l, 0, 1);
+            } else if constexpr (C::kFp4 && !SPLIT) {
+#pragma unroll
+                for (int st = 0; st < HS; st++)
+#pragma unroll
+                    for (int mt = 0; mt < NTW; mt++) a2[st][mt] = a_frag(A, mt, HS + st);
+                mask_blocks();
+                f_half(fa, 0);
+            } else if constexpr (C::kFp4) {
+                // exact fallback: bf16 weights, fp16 inputs split in two bf16
+                // parts, the whole stage here
+                const LDS uint8_t *B = A + RG::ABYTES;
+                const int sa = i + bk.kst0;
+#pragma unroll
+                for (int nb = 0; nb < NB; nb++) {
+                    fs[nb] = scale_word(sa, nb);
+#pragma unroll
+                    for (int h = 0; h < 2; h++) fq[nb][h] = b_piece(B, nb, 2 * kh + h);
+                }
+                mask_blocks();
+#pragma unroll
+                for (int st = 0; st < STEPS; st++) {
+                    bf16x8_t b[NB];
+#pragma unroll
+                    for (int nb = 0; nb < NB; nb++) b[nb] = cvt8_bf16(u4at(qm[nb][st / HS], st % HS), scf[nb][st / HS]);
+#pragma unroll
+                    for (int mt = 0; mt < NTW; mt++) {
+                        bf16x8_t ah, al;
+                        split_f16(__builtin_bit_cast(f16x8_t, a_frag(A, mt, st)), ah, al);
+#pragma unroll
+                        for (int nb = 0; nb < NB; nb++) {
+                            acc[mt][nb] = mfma32(ah, b[nb], acc[mt][nb]);
+                            acc[mt][nb] = mfma32(al, b[nb], acc[mt][nb]);
+                        }
+                    }
+                }
+            } else {
+                const LDS uint8_t *B = A + RG::ABYTES;
+#pragma unroll
+                for (int st = 0; st < HS; st++) {
+#pragma unroll
+                    for (int nb = 0; nb < NB; nb++) b2[st][nb] = b_piece(B, nb, kh * STEPS + HS + st);
+#pragma unroll
+                    for (int mt = 0; mt < NTW; mt++) a2[st][mt] = a_frag(A, mt, HS + st);
+                }
+                b_half(fa, fb);
+            }
+        }
+        // -- MULTI: the next tile's scale bytes are copied into the region
+        // after this barrier: the pass's remaining stages' words first
+        if constexpr (MULTI && NTW > 0) {
+            if (cst == nS - NST && iok && ib.t != bk.t) {
+#pragma unroll
+                for (int k = 0; k < NST - 1; k++)
+#pragma unroll
+                    for (int nb = 0; nb < NB; nb++) fsc[k][nb] = mscale_word(nS - NST + 1 + k, nb);
+                cached = true;
+            }
+        }
+        // -- stage i + 1 has landed for every wave, and every wave has read
+        // all of stage i: its slot takes stage i + NST.  (The scheduling
+        // fences keep the first half's MFMAs ahead of the wait; the last
+        // iteration's prefetch reads a slot no stage uses, and is not used.)
+        __builtin_amdgcn_sched_barrier(0);
+        wait_vm<(NST - 2) * NPS>();
+        block_barrier();
+        __builtin_amdgcn_sched_barrier(0);
+        if constexpr (MULTI) missue(sl);
+        else issue(i + NST, sl);
+        if constexpr (MULTI) prefetch(cst + 1 == nS ? 0 : cst + 1, sln);
+        else prefetch(i + 1 < nS ? i + 1 : i, sln);
+        // -- second half, from registers
+        if constexpr (NTW > 0) {
+            if constexpr (MODE == M_G13) {
+                g_mfma(g1h, 1, 0);
+                g_mfma(g1l, 1, 1);
+            }
+            else if constexpr (C::kFp4 && !SPLIT) f_half(a2, 1);
+            else if constexpr (!C::kFp4) b_half(a2, b2);
+        }
+        sl = sln;
+        if constexpr (MULTI) {
+            // -- the pass's last stage: its epilogue while the next pass's
+            // first stages are in flight, then the next pass (the one being
+            // issued), if any
+            if (++cst == nS) {
+                cst = 0;
+                bool lost = false;
+                if constexpr (MODE == M_D2) lost = __syncthreads_or(bad) != 0;
+                if (!lost) pass_epilogue<MODE, NTW, T0, NB>(p, bk, m0, mrows, acc);
+                else mj->bad |= 1u << (bk.t - mj->t0);
+                bad = false;
+                cached = false;
+#pragma unroll
+                for (int a = 0; a < (NTW > 0 ? NTW : 1); a++)
+#pragma unroll
+                    for (int nb = 0; nb < NB; nb++) acc[a][nb] = (f32x16_t)0.0f;
+                if (!iok) break;
+                bk = ib;
+                m0 = im0;
+                mrows = imrows;
+                read_sca();
+            }
+        }
+    }
+    // the ring is reused by the next pass: every copy (past-the-end ones
+    // included) must have landed, and every wave be done reading
+    wait_vm<0>();
+    block_barrier();
+
+    if constexpr (!MULTI) pass_epilogue<MODE, NTW, T0, NB>(p, bk, m0, mrows, acc);
     return true;
 }
 
@@ -945,6 +1164,39 @@ __device__ __forceinline__ void ggemm_block(const GemmParams &p, int x, LDS uint
     }
 }
 
+// The routed GEMMs at small T: block x takes the kMultiTiles flattened
+// tiles from x kMultiTiles (group t / n_tiles, column tile t % n_tiles),
+// all of their passes in one run of the ring (wave_pass MULTI); a routed
+// down tile whose W2 scales leave the fp16 window is then computed again on
+// the exact path.
+constexpr int kMultiTiles = 4;
+template <int MODE>
+__device__ __forceinline__ void ggemm_multi_block(const GemmParams &p, int x, LDS uint8_t *lds)
+{
+    const int t0 = x * kMultiTiles;
+    MultiJobs mj{t0, min(t0 + kMultiTiles, p.groups * p.n_tiles), 0u};
+    if (t0 >= mj.t_end) return;
+    const KCONST i32x4_t *gi = (const KCONST i32x4_t *)p.w.ginfo;
+    const i32x4_t g = gi[t0 / p.n_tiles];
+    if (g.y <= 0) return;
+    const Blk b = tile_blk<MODE>(p, t0, g);
+    const int mrows = min(32, b.M);
+    if constexpr (MODE == M_G13) {
+        if (__builtin_amdgcn_readfirstlane(threadIdx.x >> 6) < 4)
+            wave_pass<MODE, 1, 1, 0, false, 2, true>(p, b, 0, mrows, lds, false, &mj);
+        else
+            wave_pass<MODE, 1, 0, 1, false, 2, true>(p, b, 0, mrows, lds, false, &mj);
+    } else {
+        wave_pass<MODE, 1, 1, 0, false, 1, true>(p, b, 0, mrows, lds, false, &mj);
+        for (uint32_t m = mj.bad; m != 0; m &= m - 1) {
+            const int t = t0 + __builtin_ctz(m);
+            const Blk bt = tile_blk<MODE>(p, t, gi[t / p.n_tiles]);
+            load_scales<MODE>(p, bt, lds);
+            for (int m0 = 0; m0 < bt.M; m0 += 64) gemm_pass<MODE, 2, true>(p, bt, m0, min(64, bt.M - m0), lds, false);
+        }
+    }
+}
+
 template <int MODE>
 __global__ __launch_bounds__(GT) void k_ggemm(GemmParams p)
 {
@@ -959,13 +1211,17 @@ __global__ __launch_bounds__(GT) void k_ggemm(GemmParams p)
 // blocks at small T (one per 256 columns and 128 tokens); as the head of
 // the routed GEMM's grid they run beside its blocks instead of holding the
 // GPU to a fraction of its CUs in a launch of their own.
-template <int MODE1, int MODE2>
+// (MULTI2: the second GEMM's blocks take kMultiTiles tiles each)
+template <int MODE1, int MODE2, bool MULTI2>
 __global__ __launch_bounds__(GT) void k_ggemm_pair(GemmParams p1, GemmParams p2, int n1, int n1p)
 {
     __shared__ __attribute__((aligned(1024))) uint8_t lds_blk[kLdsBytes + kMetaBytes];
     const int x = (int)blockIdx.x;
     if (x < n1) ggemm_block<MODE1>(p1, x, (LDS uint8_t *)lds_blk);
-    else if (x >= n1p) ggemm_block<MODE2>(p2, x - n1p, (LDS uint8_t *)lds_blk);
+    else if (x >= n1p) {
+        if constexpr (MULTI2) ggemm_multi_block<MODE2>(p2, x - n1p, (LDS uint8_t *)lds_blk);
+        else ggemm_block<MODE2>(p2, x - n1p, (LDS uint8_t *)lds_blk);
+    }
 }
 
 // Router weights fp32 -> three bf16 parts whose sum is exact: hi = rne(w),
@@ -1141,16 +1397,32 @@ static void launch_mode(const GemmParams &p0, int groups, int n_tiles, int m_blo
 // (MODE2, n2 blocks) in one launch while it has too few blocks to fill the
 // GPU twice (small T); else two launches
 constexpr int kPairMaxHead = 512;
-template <int MODE1, int MODE2>
+template <int MODE1, int MODE2, bool MULTI2 = false>
 static void launch_pair(const GemmParams &p1, int n1, const GemmParams &p2, int n2, hipStream_t st)
 {
-    if (n1 >= kPairMaxHead) {
+    if (n1 >= kPairMaxHead && !MULTI2) {
         k_ggemm<MODE1><<<n1, GT, 0, st>>>(p1);
         if (n2 > 0) k_ggemm<MODE2><<<n2, GT, 0, st>>>(p2);
         return;
     }
     const int n1p = (n1 + 7) / 8 * 8;
-    if (n1 + n2 > 0) k_ggemm_pair<MODE1, MODE2><<<n1p + n2, GT, 0, st>>>(p1, p2, n1, n1p);
+    if (n1 + n2 > 0) k_ggemm_pair<MODE1, MODE2, MULTI2><<<n1p + n2, GT, 0, st>>>(p1, p2, n1, n1p);
+}
+
+// The routed GEMMs take kMultiTiles tiles per block up to kMultiMaxTokens
+// tokens (groups then hold a few rows: one 32-row pass per tile), where
+// every pass has more K stages than the ring holds.  Measured at the K3
+// shape: the routed down gains 10% at T = 64 (804 -> 727 us) and 8% at
+// T = 256; the routed gate/up, already at the HBM rate between its blocks'
+// first stages, 1% at T = 64 and loses 2% at T = 16, so it takes the form
+// from kMultiMinTokensG13 tokens only.
+constexpr int kMultiMaxTokens = 256;
+constexpr int kMultiMinTokensG13 = 32;
+static bool multi_tiles(const Shape &s, int mode)
+{
+    return s.T <= kMultiMaxTokens && (mode != M_G13 || s.T >= kMultiMinTokensG13) &&
+           s.d / 128 > MRing<M_G13>::NST && s.F / 128 > MRing<M_D2>::NST && 8 * s.d <= kScaleBytes &&
+           8 * s.F <= kScaleBytes;
 }
 
 static GemmParams make_gemm_params(const Shape &s, const uint16_t *x, const Weights &wt, const Work &w)
@@ -1221,12 +1493,24 @@ hipError_t launch_mfma_experts(const Shape &s, const uint16_t *x, const Weights 
     const bool sh = include_shared && s.S > 0;
     int n_s13 = 0, n_g13, n_s2 = 0, n_d2;
     const GemmParams p_s13 = mode_params(p, sh ? s.S : 0, (s.F + 127) / 128, mb, 1, &n_s13);
-    const GemmParams p_g13 = mode_params(p, max_active, (s.F + 127) / 128, 1, 1, &n_g13);
-    launch_pair<M_S13, M_G13>(p_s13, n_s13, p_g13, n_g13, st);
-    if (ev2) (void)hipEventRecord(ev2[0], st);
     const GemmParams p_s2 = mode_params(p, sh ? s.S : 0, (s.d + GN - 1) / GN, mb, 1, &n_s2);
+    // (several tiles per block: groups not padded, the blocks take
+    // consecutive flattened tiles)
+    const GemmParams p_g13 = mode_params(p, max_active, (s.F + 127) / 128, 1, 1, &n_g13);
+    if (multi_tiles(s, M_G13)) {
+        n_g13 = (max_active * p_g13.n_tiles + kMultiTiles - 1) / kMultiTiles;
+        launch_pair<M_S13, M_G13, true>(p_s13, n_s13, p_g13, n_g13, st);
+    } else {
+        launch_pair<M_S13, M_G13>(p_s13, n_s13, p_g13, n_g13, st);
+    }
+    if (ev2) (void)hipEventRecord(ev2[0], st);
     const GemmParams p_d2 = mode_params(p, max_active, (s.d + GN - 1) / GN, 1, 1, &n_d2);
-    launch_pair<M_S2, M_D2>(p_s2, n_s2, p_d2, n_d2, st);
+    if (multi_tiles(s, M_D2)) {
+        n_d2 = (max_active * p_d2.n_tiles + kMultiTiles - 1) / kMultiTiles;
+        launch_pair<M_S2, M_D2, true>(p_s2, n_s2, p_d2, n_d2, st);
+    } else {
+        launch_pair<M_S2, M_D2>(p_s2, n_s2, p_d2, n_d2, st);
+    }
     if (ev2) (void)hipEventRecord(ev2[1], st);
     return hipGetLastError();
 }
