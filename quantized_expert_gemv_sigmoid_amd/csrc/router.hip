@@ -85,6 +85,7 @@ __device__ __forceinline__ int block_scan(int v, int *tmp, int *total)
 }
 
 constexpr int kSmallThreads = 512;  // threads of the one-block dispatch (2 experts each)
+constexpr int kSmallScatterTokens = 16;  // tokens up to which the one block also scatters
 
 // active expert number a is expert e with count c at offset o: the active
 // list, and the record a GEMM block of that group reads in one load
@@ -134,9 +135,10 @@ __device__ __forceinline__ void write_offsets2(int E, int c0, int c1, int *offs,
 // every slot with that id in slot order (just its own when it has no
 // repeat).  tok_pos[t] lists the token's positions in ascending expert id,
 // then -1 for the rest (invalid ids and repeats).
+// xs_t: the token's fp8 scales, gathered to its positions when w.tok_xs is set
 template <typename PosOf>
 __device__ __forceinline__ void dispatch_token(int t, int E, int k, const int32_t *__restrict__ ids,
-                                               const float *__restrict__ wts, PosOf &&pos_of,
+                                               const float *__restrict__ wts, uint32_t xs_t, PosOf &&pos_of,
                                                const Work &w)
 {
     const int lane = threadIdx.x & 63;
@@ -161,7 +163,7 @@ __device__ __forceinline__ void dispatch_token(int t, int E, int k, const int32_
         const int p = pos_of(id);
         w.pos_tok[p] = t;
         w.pos_w[p] = wsum;
-        if (w.tok_xs) w.pos_xs[p] = w.tok_xs[t];
+        if (w.tok_xs) w.pos_xs[p] = xs_t;
         tp[rank] = p;
     }
     const int nlead = __builtin_popcountll(leaders);
@@ -187,6 +189,7 @@ __global__ __launch_bounds__(kSmallThreads) void k_dispatch_small(
     __shared__ uint64_t s_tk[NW][2 * kMaxTopK];
     __shared__ int32_t s_ids[kDispatchTokens * kMaxTopK];
     __shared__ float s_wts[kDispatchTokens * kMaxTopK];
+    __shared__ uint32_t s_xs[kDispatchTokens];
     const int T = s.T, E = s.E, k = s.k;
     const int wave = threadIdx.x >> 6;
     if (do_topk) {
@@ -198,9 +201,10 @@ __global__ __launch_bounds__(kSmallThreads) void k_dispatch_small(
         for (int t = NW - 1 - wave; t < T; t += NW) quant_z_row(t, zq);
     }
     for (int e = threadIdx.x; e < E; e += kSmallThreads) masks[e] = 0ull;
+    if (w.tok_xs && (int)threadIdx.x < T) s_xs[threadIdx.x] = w.tok_xs[threadIdx.x];
     __syncthreads();  // also publishes the top-k results to the block
-    // every slot's id and weight into LDS at once (the per-token scatter
-    // below then waits on no global load)
+    // every slot's id and weight (and the tokens' scales, above) into LDS at
+    // once: the per-token scatter below then waits on no global load
     for (int sl = threadIdx.x; sl < T * k; sl += kSmallThreads) {
         const int e = ids[sl];
         s_ids[sl] = e;
@@ -216,7 +220,7 @@ __global__ __launch_bounds__(kSmallThreads) void k_dispatch_small(
     }
     __syncthreads();
     for (int t = wave; t < T; t += NW)
-        dispatch_token(t, E, k, s_ids, s_wts,
+        dispatch_token(t, E, k, s_ids, s_wts, w.tok_xs ? s_xs[t] : 0u,
                        [&](int e) { return offs[e] + __popcll(masks[e] & ((1ull << t) - 1ull)); }, w);
 }
 
@@ -275,7 +279,7 @@ __global__ __launch_bounds__(256) void k_dispatch_scatter(Shape s, const int32_t
     const int t = blockIdx.x * 4 + (threadIdx.x >> 6);
     if (t >= s.T) return;
     const int b = t / kDispatchTokens, tl = t % kDispatchTokens;
-    dispatch_token(t, s.E, s.k, ids, wts,
+    dispatch_token(t, s.E, s.k, ids, wts, w.tok_xs ? w.tok_xs[t] : 0u,
                    [&](int e) {
                        const unsigned long long m = w.masks[(size_t)b * s.E + e];
                        return w.offsets[e] + w.blk_base[(size_t)b * s.E + e] + __popcll(m & ((1ull << tl) - 1ull));
@@ -313,7 +317,9 @@ hipError_t launch_dispatch(const Shape &s, int do_topk, const float *logits, con
                            hipStream_t stream, const ZQuant &zq)
 {
     const int epl = (s.E + 63) / 64;
-    if (s.T <= kDispatchTokens && s.T <= 16) {
+    // (up to one token per wave the one block takes the top-k too; beyond,
+    // a wave would key tokens in turn, and k_topk keys them in parallel)
+    if (s.T <= kDispatchTokens && s.T <= kSmallThreads / 64) {
 #define CALL_SMALL(N) launch_small<N>(s, do_topk, logits, bias, ids, wts, counts_out, w, stream, zq)
         MOE_EPL_SWITCH(epl, CALL_SMALL);
 #undef CALL_SMALL
@@ -324,7 +330,10 @@ hipError_t launch_dispatch(const Shape &s, int do_topk, const float *logits, con
         MOE_EPL_SWITCH(epl, CALL_TOPK);
 #undef CALL_TOPK
     }
-    if (s.T <= kDispatchTokens) {
+    // (the one block scatters every slot itself; from kSmallScatterTokens
+    // tokens on the many-block scatter is faster: one CU's stores of four
+    // scattered words per slot took 20 us at T = 64)
+    if (s.T <= kDispatchTokens && s.T <= kSmallScatterTokens) {
 #define CALL_SMALL0(N) launch_small<N>(s, 0, logits, bias, ids, wts, counts_out, w, stream, zq)
         MOE_EPL_SWITCH(epl, CALL_SMALL0);
 #undef CALL_SMALL0

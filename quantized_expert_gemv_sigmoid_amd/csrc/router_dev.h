@@ -33,13 +33,14 @@ __device__ __forceinline__ void topk_wave_select(int E, int k, const float *__re
 {
     const int lane = threadIdx.x & 63;
     uint32_t key[EPL];
+    float scs[EPL];  // the unbiased scores, kept for the picks' weights
 #pragma unroll
     for (int i = 0; i < EPL; i++) {
         // branch-free (a branch per element makes the compiler copy the whole array)
         const int e = lane + 64 * i;
         const int ec = e < E ? e : E - 1;
-        const float sc = sigmoidf_(lrow[ec]);
-        const uint32_t kk = (uint32_t)(select_key(sc + (bias ? bias[ec] : 0.0f), e) >> 32);
+        scs[i] = sigmoidf_(lrow[ec]);
+        const uint32_t kk = (uint32_t)(select_key(scs[i] + (bias ? bias[ec] : 0.0f), e) >> 32);
         key[i] = e < E ? kk : 0u;  // padding is never selected: real keys are > 0
     }
     uint32_t t = 0;
@@ -77,8 +78,15 @@ __device__ __forceinline__ void topk_wave_select(int E, int k, const float *__re
     __builtin_amdgcn_wave_barrier();
     const uint64_t kk = lane < k ? cand[kMaxTopK + lane] : 0ull;
     const int my_id = lane < k ? (int)(~(uint32_t)kk) : 0;
-    // the unbiased score of each pick, recomputed from its logit (same fp32 op)
-    const float my_s = lane < k ? sigmoidf_(lrow[my_id]) : 0.0f;
+    // the unbiased score of each pick: from the lane that keyed it (lane
+    // id % 64, slot id / 64), no second read of the logit
+    float my_s = 0.0f;
+#pragma unroll
+    for (int i = 0; i < EPL; i++) {
+        const float v = __int_as_float(__builtin_amdgcn_ds_bpermute((my_id & 63) << 2, __float_as_int(scs[i])));
+        my_s = (my_id >> 6) == i ? v : my_s;
+    }
+    my_s = lane < k ? my_s : 0.0f;
     float sum = 0.0f;  // fp32 sum in selection order
     for (int j = 0; j < k; j++) sum += __int_as_float(__builtin_amdgcn_readlane(__float_as_int(my_s), j));
     float wj = my_s;
