@@ -66,8 +66,8 @@ KERNELS = {
     "mfma": {"router_logits": "k_split_router + k_ggemm<M_R>", "topk_dispatch": "k_topk + k_dispatch_*",
              "expert_gate_up": "k_ggemm_pair<M_S13, M_G13> (K3 shape, T <= 1280, 4 column tiles per routed block "
                                "for 32 <= T <= 256; else k_ggemm<M_S13> + k_ggemm<M_G13>)",
-             "expert_down": "k_ggemm_pair<M_S2, M_D2> (K3 shape, T <= 2304, 4 column tiles per routed block for "
-                            "T <= 256; else k_ggemm<M_S2> + k_ggemm<M_D2>)",
+             "expert_down": "k_ggemm_pair<M_S2H, M_D2> (K3 shape, T <= 2304, 4 column tiles per routed block for "
+                            "T <= 256; else k_ggemm<M_S2H> + k_ggemm<M_D2>)",
              "combine": "k_combine"},
 }
 # steps per timed window of each workload when it is measured as an entry of
@@ -84,7 +84,7 @@ LATENT_KERNELS = {
     "mfma": {"front": "k_split_router + k_ggemm<M_R> (router) + k_ggemm<M_R> (down projection) + k_ggemm<M_S13>",
              "topk_dispatch_z": "k_topk + k_dispatch_* + k_quant_z",
              "expert_gate_up": "k_ggemm<M_G13H>", "expert_down": "k_ggemm<M_D2>",
-             "norm_up_shared_out": "k_latent_accum + k_latent_split + k_ggemm<M_S2> (up, shared down) + k_combine"},
+             "norm_up_shared_out": "k_latent_accum + k_latent_split + k_ggemm<M_S2> (up) + k_ggemm<M_S2H> (shared down) + k_combine"},
 }
 WINDOWS = 3
 

@@ -67,7 +67,7 @@ constexpr uint32_t kPast = 0xF0000000u;  // a buffer offset past every resource:
 // S13 / S2 shared gate/up and down (bf16); R router / plain linear (bf16
 // parts of the weights, fp32 out); G13H routed gate/up on fp16 input rows
 // with a power-of-two scale per row (the latent layer's experts)
-enum Mode { M_G13 = 0, M_D2 = 1, M_S13 = 2, M_S2 = 3, M_R = 4, M_G13H = 5 };
+enum Mode { M_G13 = 0, M_D2 = 1, M_S13 = 2, M_S2 = 3, M_R = 4, M_G13H = 5, M_S2H = 6 };
 
 struct GemmParams {
     Shape s;
@@ -148,6 +148,15 @@ __device__ __forceinline__ void split_f16(const f16x8_t a, bf16x8_t &hi, bf16x8_
         hi[i] = __builtin_bit_cast(__bf16, h);
         lo[i] = __builtin_bit_cast(__bf16, l);
     }
+}
+
+// bf16 x8 -> fp16 x8, round to nearest even (exact where fp16 holds the value)
+__device__ __forceinline__ f16x8_t bf16x8_to_f16(const uint4 v)
+{
+    typedef float f32x8_t __attribute__((ext_vector_type(8)));
+    const f32x8_t f = {bf16_lo(v.x), bf16_hi(v.x), bf16_lo(v.y), bf16_hi(v.y),
+                       bf16_lo(v.z), bf16_hi(v.z), bf16_lo(v.w), bf16_hi(v.w)};
+    return __builtin_convertvector(f, f16x8_t);
 }
 
 __device__ __forceinline__ f32x16_t mfma32(bf16x8_t a, bf16x8_t b, f32x16_t c)
@@ -295,7 +304,7 @@ __device__ __forceinline__ uint32_t b_row(const GemmParams &p, const Blk &b, int
     if constexpr (MODE == M_G13 || MODE == M_G13H) return (uint32_t)gated_feature(b.tile, c) * (s.d / 2);
     else if constexpr (MODE == M_D2) return (uint32_t)(b.tile * GN + c) * (s.F / 2);
     else if constexpr (MODE == M_S13) return (uint32_t)gated_feature(b.tile, c) * (s.d * 2);
-    else if constexpr (MODE == M_S2) return (uint32_t)(b.tile * GN + c) * (s.F * 2);
+    else if constexpr (MODE == M_S2 || MODE == M_S2H) return (uint32_t)(b.tile * GN + c) * (s.F * 2);
     else return (uint32_t)min(b.tile * GN + c, s.E - 1) * (p.rparts * s.d * 2);  // router: past E re-read row E - 1
 }
 // scale row of block column c (see the layout above)
@@ -398,11 +407,9 @@ __device__ __forceinline__ void pass_epilogue(const GemmParams &p, const Blk &bk
                         _Float16 *H = reinterpret_cast<_Float16 *>(p.w.H);
                         H[(uint32_t)(bk.base + m) * (uint32_t)s.F + (uint32_t)f] = (_Float16)hv[mt][e];
                     } else {
-                        const uint16_t hi = f32_to_bf16_rne(hv[mt][e]);
-                        const uint16_t lo = f32_to_bf16_rne(hv[mt][e] - __uint_as_float((uint32_t)hi << 16));
+                        // the shared experts' H, fp16 (in range: as for the routed H)
                         const size_t o = (size_t)m * s.S * s.F + (size_t)bk.group * s.F + f;
-                        p.hs_hi_w[o] = hi;
-                        p.hs_lo_w[o] = lo;
+                        reinterpret_cast<_Float16 *>(p.hs_hi_w)[o] = (_Float16)hv[mt][e];
                     }
                 }
             }
@@ -433,7 +440,7 @@ __device__ __forceinline__ void pass_epilogue(const GemmParams &p, const Blk &bk
                         if (n >= bk.ncols) continue;
                         const float v = acc[mt][nb][e];
                         if constexpr (MODE == M_D2) p.w.Y[(size_t)(bk.base + m) * s.d + n] = v * wrow;
-                        else if constexpr (MODE == M_S2) p.w.Ysh[((size_t)bk.group * s.T + m) * s.d + n] = v;
+                        else if constexpr (MODE == M_S2 || MODE == M_S2H) p.w.Ysh[((size_t)bk.group * s.T + m) * s.d + n] = v;
                         else if (p.ksplit > 1) p.rpart[((size_t)bk.ks * s.T + m) * s.E + n] = v;
                         else p.w.logits[(size_t)m * s.E + n] = v;
                     }
@@ -493,7 +500,7 @@ __device__ __forceinline__ bool wave_pass(const GemmParams &p, const Blk &bk_in,
         } else if constexpr (MODE == M_D2) {
             abase = reinterpret_cast<const uint8_t *>(p.w.H);
             abytes = (uint32_t)s.T * s.k * s.F * 2;
-        } else if constexpr (MODE == M_S2) {
+        } else if constexpr (MODE == M_S2 || MODE == M_S2H) {
             abase = reinterpret_cast<const uint8_t *>(p.hs_hi);
             abytes = (uint32_t)s.T * s.S * s.F * 2;
         } else if constexpr (MODE == M_G13H) {
@@ -540,7 +547,7 @@ __device__ __forceinline__ bool wave_pass(const GemmParams &p, const Blk &bk_in,
             } else {
                 uint32_t el;  // element offset
                 if constexpr (MODE == M_D2) el = (uint32_t)(b.base + m) * s.F;
-                else if constexpr (MODE == M_S2) el = (uint32_t)m * s.S * s.F + (uint32_t)b.group * s.F;
+                else if constexpr (MODE == M_S2 || MODE == M_S2H) el = (uint32_t)m * s.S * s.F + (uint32_t)b.group * s.F;
                 else if constexpr (MODE == M_G13H) el = (uint32_t)tok * s.d;
                 else el = (uint32_t)m * s.d;
                 e = el * 2 + q * 16;
@@ -568,7 +575,7 @@ __device__ __forceinline__ bool wave_pass(const GemmParams &p, const Blk &bk_in,
             } else if constexpr (MODE == M_S13) {
                 const uint32_t qb = (uint32_t)s.F * s.d * 2;
                 rb[j] = grsrc(reinterpret_cast<const uint8_t *>(up ? p.sh3 : p.sh1) + (size_t)b.group * qb, qb);
-            } else if constexpr (MODE == M_S2) {
+            } else if constexpr (MODE == M_S2 || MODE == M_S2H) {
                 const uint32_t qb = (uint32_t)s.d * s.F * 2;
                 rb[j] = grsrc(reinterpret_cast<const uint8_t *>(p.sh2) + (size_t)b.group * qb, qb);
             } else {
@@ -878,15 +885,30 @@ __device__ __forceinline__ bool wave_pass(const GemmParams &p, const Blk &bk_in,
                     acc[mt][nb] = mfma32(__builtin_bit_cast(BT, av[st][mt]), b[cur][nb], acc[mt][nb]);
         }
     };
+    // (M_S2H: fp16 A; the bf16 B converted to fp16, exact for every
+    // weight of magnitude in [2^-17, 65504], the rest rounded: tiny ones by
+    // at most 2^-25, huge ones to infinity, which the pass's check catches)
     auto b_half = [&](const uint4 (&av)[HS][NTW > 0 ? NTW : 1], const uint4 (&bv)[HS][NB]) __attribute__((always_inline)) {
 #pragma unroll
-        for (int st = 0; st < HS; st++)
+        for (int st = 0; st < HS; st++) {
+            if constexpr (MODE == M_S2H) {
+                f16x8_t bh[NB];
 #pragma unroll
-            for (int mt = 0; mt < NTW; mt++)
+                for (int nb = 0; nb < NB; nb++) bh[nb] = bf16x8_to_f16(bv[st][nb]);
 #pragma unroll
-                for (int nb = 0; nb < NB; nb++)
-                    acc[mt][nb] = mfma32(__builtin_bit_cast(bf16x8_t, av[st][mt]),
-                                         __builtin_bit_cast(bf16x8_t, bv[st][nb]), acc[mt][nb]);
+                for (int mt = 0; mt < NTW; mt++)
+#pragma unroll
+                    for (int nb = 0; nb < NB; nb++)
+                        acc[mt][nb] = mfma32(__builtin_bit_cast(f16x8_t, av[st][mt]), bh[nb], acc[mt][nb]);
+            } else {
+#pragma unroll
+                for (int mt = 0; mt < NTW; mt++)
+#pragma unroll
+                    for (int nb = 0; nb < NB; nb++)
+                        acc[mt][nb] = mfma32(__builtin_bit_cast(bf16x8_t, av[st][mt]),
+                                             __builtin_bit_cast(bf16x8_t, bv[st][nb]), acc[mt][nb]);
+            }
+        }
     };
 
     // ---- K loop.  The prologue issues stages 0 .. NST - 1 (every slot);
@@ -981,6 +1003,26 @@ __device__ __forceinline__ bool wave_pass(const GemmParams &p, const Blk &bk_in,
                         }
                     }
                 }
+            } else if constexpr (MODE == M_S2H && SPLIT) {
+                // exact redo: the bf16 weights as they are, the fp16 H split
+                // in two bf16 parts, the whole stage here
+                const LDS uint8_t *B = A + RG::ABYTES;
+#pragma unroll
+                for (int st = 0; st < STEPS; st++) {
+                    bf16x8_t b[NB];
+#pragma unroll
+                    for (int nb = 0; nb < NB; nb++) b[nb] = __builtin_bit_cast(bf16x8_t, b_piece(B, nb, kh * STEPS + st));
+#pragma unroll
+                    for (int mt = 0; mt < NTW; mt++) {
+                        bf16x8_t ah, al;
+                        split_f16(__builtin_bit_cast(f16x8_t, a_frag(A, mt, st)), ah, al);
+#pragma unroll
+                        for (int nb = 0; nb < NB; nb++) {
+                            acc[mt][nb] = mfma32(ah, b[nb], acc[mt][nb]);
+                            acc[mt][nb] = mfma32(al, b[nb], acc[mt][nb]);
+                        }
+                    }
+                }
             } else {
                 const LDS uint8_t *B = A + RG::ABYTES;
 #pragma unroll
@@ -1023,7 +1065,7 @@ __device__ __forceinline__ bool wave_pass(const GemmParams &p, const Blk &bk_in,
                 g_mfma(g1l, 1, 1);
             }
             else if constexpr (C::kFp4 && !SPLIT) f_half(a2, 1);
-            else if constexpr (!C::kFp4) b_half(a2, b2);
+            else if constexpr (!C::kFp4 && !SPLIT) b_half(a2, b2);
         }
         sl = sln;
         if constexpr (MULTI) {
@@ -1055,6 +1097,20 @@ __device__ __forceinline__ bool wave_pass(const GemmParams &p, const Blk &bk_in,
     wait_vm<0>();
     block_barrier();
 
+    // (M_S2H: a weight past fp16's range gave a non-finite sum; the caller
+    // then computes the pass again exactly)
+    if constexpr (MODE == M_S2H && !SPLIT) {
+        if (check) {
+            bool bad = false;
+#pragma unroll
+            for (int a = 0; a < NTW; a++)
+#pragma unroll
+                for (int nb = 0; nb < NB; nb++)
+#pragma unroll
+                    for (int e = 0; e < 16; e++) bad = bad || (__float_as_uint(acc[a][nb][e]) & 0x7f800000u) == 0x7f800000u;
+            if (__syncthreads_or(bad)) return false;
+        }
+    }
     if constexpr (!MULTI) pass_epilogue<MODE, NTW, T0, NB>(p, bk, m0, mrows, acc);
     return true;
 }
@@ -1123,7 +1179,7 @@ __device__ __forceinline__ void ggemm_block(const GemmParams &p, int x, LDS uint
         b.K = MODE == M_D2 ? s.F : s.d;
     } else {
         b.M = s.T;
-        b.K = MODE == M_S13 ? s.d : (MODE == M_S2 ? 2 * s.F : p.rparts * s.d);
+        b.K = MODE == M_S13 ? s.d : (MODE == M_S2 ? 2 * s.F : (MODE == M_S2H ? s.F : p.rparts * s.d));
     }
     if constexpr (MODE == M_R) b.K /= p.ksplit;  // (a multiple of the stage, see the launch)
     b.nS = b.K / C::KS;
@@ -1160,7 +1216,15 @@ __device__ __forceinline__ void ggemm_block(const GemmParams &p, int x, LDS uint
         // shared experts / router: one pass of GM rows per block (rows past
         // the end read nothing and are never stored)
         const int m0 = b.mb * GM;
-        if (m0 < b.M) gemm_pass<MODE, GMT>(p, b, m0, min(GM, b.M - m0), ring, false);
+        if (m0 < b.M) {
+            const int mr = min(GM, b.M - m0);
+            if constexpr (MODE == M_S2H) {
+                if (!gemm_pass<MODE, GMT>(p, b, m0, mr, ring, true))
+                    for (int r0 = 0; r0 < mr; r0 += 64) gemm_pass<MODE, 2, true>(p, b, m0 + r0, min(64, mr - r0), ring, false);
+            } else {
+                gemm_pass<MODE, GMT>(p, b, m0, mr, ring, false);
+            }
+        }
     }
 }
 
@@ -1436,7 +1500,8 @@ static GemmParams make_gemm_params(const Shape &s, const uint16_t *x, const Weig
     p.wr3 = reinterpret_cast<const uint16_t *>(w.extra);
     p.xq = w.xq;
     p.xs = mfma_token_scales(s, w);
-    // the shared H (bf16 hi and lo parts) lives in the fp32 shared-H region
+    // the shared experts' H (fp16, at hs_hi) lives in the fp32 shared-H
+    // region; hs_lo serves the latent up projection's two-part operand
     p.hs_hi = reinterpret_cast<const uint16_t *>(w.Hs);
     p.hs_lo = p.hs_hi + (size_t)s.T * s.S * s.F;
     p.hs_hi_w = reinterpret_cast<uint16_t *>(w.Hs);
@@ -1507,9 +1572,9 @@ hipError_t launch_mfma_experts(const Shape &s, const uint16_t *x, const Weights 
     const GemmParams p_d2 = mode_params(p, max_active, (s.d + GN - 1) / GN, 1, 1, &n_d2);
     if (multi_tiles(s, M_D2)) {
         n_d2 = (max_active * p_d2.n_tiles + kMultiTiles - 1) / kMultiTiles;
-        launch_pair<M_S2, M_D2, true>(p_s2, n_s2, p_d2, n_d2, st);
+        launch_pair<M_S2H, M_D2, true>(p_s2, n_s2, p_d2, n_d2, st);
     } else {
-        launch_pair<M_S2, M_D2>(p_s2, n_s2, p_d2, n_d2, st);
+        launch_pair<M_S2H, M_D2>(p_s2, n_s2, p_d2, n_d2, st);
     }
     if (ev2) (void)hipEventRecord(ev2[1], st);
     return hipGetLastError();
@@ -1555,8 +1620,7 @@ hipError_t launch_mfma_latent_experts(const Shape &s, const Weights &wt, const u
     return hipGetLastError();
 }
 
-// shared experts' gate/up at the full width (H fp32 split into bf16 hi / lo
-// parts in w.Hs)
+// shared experts' gate/up at the full width (H as fp16 in w.Hs)
 hipError_t launch_mfma_shared_gateup(const Shape &s, const uint16_t *x, const Weights &wt,
                                      const Work &w, hipStream_t st)
 {
@@ -1566,7 +1630,8 @@ hipError_t launch_mfma_shared_gateup(const Shape &s, const uint16_t *x, const We
 }
 
 // ysh[(S + 1)][T][d]: slot 0 = W_up n (n as bf16 hi / lo parts [T][L]),
-// slots 1 .. S = the shared experts' down projections (s.d = hidden width)
+// slots 1 .. S = the shared experts' down projections (fp16 H; s.d = hidden
+// width)
 hipError_t launch_mfma_up_shared(const Shape &s, int L, const uint16_t *up, const uint16_t *nhi,
                                  const uint16_t *nlo, const Weights &wt, const Work &w, float *ysh,
                                  hipStream_t st)
@@ -1588,7 +1653,7 @@ hipError_t launch_mfma_up_shared(const Shape &s, int L, const uint16_t *up, cons
         Work ws = w;
         ws.Ysh = ysh + (size_t)s.T * s.d;
         GemmParams p = make_gemm_params(s, nullptr, wt, ws);
-        launch_mode<M_S2>(p, s.S, (s.d + GN - 1) / GN, mb, st);
+        launch_mode<M_S2H>(p, s.S, (s.d + GN - 1) / GN, mb, st);
     }
     return hipGetLastError();
 }

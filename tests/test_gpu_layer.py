@@ -352,6 +352,36 @@ def test_mfma_down_projection_mixed_blocks():
     assert_close(out_f[:, 400:401], rout[:, 400:401], "column 400 (scale byte 141)")
 
 
+def test_mfma_shared_down_weights_past_fp16():
+    # The shared experts' down projection multiplies their fp16 H by the bf16
+    # weights converted to fp16.  Row 400 of shared expert 1's W2 is scaled
+    # by 2^24 (magnitudes past fp16's largest: they convert to infinity), so
+    # the passes over the column tile that holds output column 400 come out
+    # non-finite and are computed again exactly (the fp16 H in two bf16
+    # parts times the bf16 weights); every other tile keeps the fp16 pass.
+    # Column 400 is ~2^24 times larger than the rest and is compared on its
+    # own.  T = 300 runs two 128-row passes and a ragged one per tile.
+    import quantized_expert_gemv_sigmoid_amd as moe
+    h = synth.host_layer(MFMA_SHAPE, 66, 0)
+    row = h.sh_w2[1, 400, :].astype(np.uint32) << 16
+    big = (row.view(np.float32) * np.float32(2.0 ** 24)).view(np.uint32) >> 16
+    h.sh_w2[1, 400, :] = big.astype(np.uint16)
+    assert np.abs((big.astype(np.uint32) << 16).view(np.float32)).max() > 65520.0
+    gl = make_gpu_layer(MFMA_SHAPE, 66, host=h, path=moe.PATH_MFMA)
+    T = 300
+    log(f"case: MFMA E40 k6 S2 d512 F768 T={T}, a shared W2 row past fp16's range")
+    x, rw, bias = tokens(gl, T)
+    out_f, out_b, ids, w, cnt = run_layer(gl, x)
+    rids, rw_, gap, rout = oracle_outputs(gl, x, rw, bias, np.arange(T))
+    check_routing(ids, w, cnt, rids, rw_, gl.shape.n_experts, "routing")
+    assert np.isfinite(out_f).all()
+    other = np.ones(MFMA_SHAPE.d_model, dtype=bool)
+    other[400] = False
+    assert_close(out_f[:, other], rout[:, other], "columns other than 400")
+    assert_close(out_f[:, 400:401], rout[:, 400:401], "column 400 (weights times 2^24)")
+    assert np.array_equal(out_b, bf16_rne(out_f))
+
+
 def test_stacked_layers_in_one_graph():
     """The 12-layer workload's mechanics at a smaller shape: independent
     layers (own weights, own tokens, one Zipf selection bias) run one after
