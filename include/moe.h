@@ -63,7 +63,10 @@ typedef enum { MOE_OUT_BF16 = 0, MOE_OUT_F32 = 1, MOE_OUT_BOTH = 2 } moe_out_mod
  *
  * Precision of the activation H = act(g, u) between the gate/up and the down
  * products: the GEMV path keeps it in fp32; the one-token kernels and the
- * MFMA path store it in fp16 (relative rounding 2^-11).  SiTU bounds |h| by
+ * MFMA path store it in fp16 (relative rounding 2^-11), the MFMA path's
+ * shared experts included: their down product takes the bf16 weights as
+ * fp16 (exact in [2^-17, 65504]; smaller ones off by at most 2^-25; a pass
+ * that meets a larger one is computed again exactly).  SiTU bounds |h| by
  * b1*b2, which is why those two paths need b1*b2 <= 65504 (the largest
  * fp16).  SwiGLU is unbounded: the one-token kernels never take it, and on
  * the MFMA path an |h| above 65504 becomes inf in H, so that token's outputs
