@@ -212,15 +212,15 @@ def test_k3_decode_T1_zipf_bias():
     del gl
 
 
-def test_k3_decode_T64_sampled():
+def test_k3_decode_T64_every_token():
     w, gl = _k3(2)
     x, rw, bias = tokens(gl, w.tokens)
     out_f, out_b, ids, wts, cnt = run_layer(gl, x)
-    sample = np.array([0, 1, 7, 15, 16, 31, 32, 40, 47, 48, 55, 62, 63])
+    sample = np.arange(w.tokens)
     rids, rw_, gap, rout = oracle_outputs(gl, x, rw, bias, sample)
     check_routing(ids, wts, cnt, rids, rw_, w.shape.n_experts, "T64")
     log(f"  distinct experts touched: {(cnt > 0).sum()}")
-    assert_close(out_f[sample], rout, "T64 sampled")
+    assert_close(out_f, rout, "T64 every token")
     assert np.array_equal(out_b, bf16_rne(out_f))
     del gl
 
@@ -229,7 +229,8 @@ def test_k3_prefill_T4096_sampled():
     w, gl = _k3(3)
     x, rw, bias = tokens(gl, w.tokens)
     out_f, out_b, ids, wts, cnt = run_layer(gl, x)
-    sample = np.array([0, 1, 63, 64, 1000, 2047, 2048, 3001, 4030, 4095])
+    # 256 tokens spread over the batch, both ends included
+    sample = np.unique(np.r_[np.linspace(0, w.tokens - 1, 254).astype(np.int64), 63, 64])
     rids, rw_, gap, rout = oracle_outputs(gl, x, rw, bias, sample)
     check_routing(ids, wts, cnt, rids, rw_, w.shape.n_experts, "T4096")
     log(f"  experts touched: {(cnt > 0).sum()}, tokens/expert {cnt.mean():.1f} +- {cnt.std():.1f}")
