@@ -186,6 +186,8 @@ def test_latent_k3_decode_T1():
 
 def test_latent_k3_prefill_T4096_sampled():
     w, gl = _k3_latent(2)
-    _, out_f, _, _, _, cnt = _check(gl, w.tokens, sample=[0, 1, 63, 64, 1000, 2047, 2048, 3001, 4095])
+    # 256 tokens spread over the batch, both ends included
+    sample = np.unique(np.r_[np.linspace(0, w.tokens - 1, 254).astype(np.int64), 63, 64])
+    _, out_f, _, _, _, cnt = _check(gl, w.tokens, sample=sample)
     log(f"  experts touched: {(cnt > 0).sum()}, tokens/expert {cnt.mean():.1f}")
     del gl
