@@ -201,57 +201,45 @@ __device__ __forceinline__ void routed_gateup_tile(const GemvParams &p, int blk)
             sb[gi][i] = ok ? s3[row * srow + bc] : 255u;
         }
     }
-    for (int c0 = 0; c0 < n; c0 += NT) {
-        uint32_t xr[NT][BPL][16];
-        float xsc[NT];
-#pragma unroll
-        for (int tt = 0; tt < NT; tt++) {
-            const int i0 = c0 + tt;
-            const int tok = i0 < n ? p.w.pos_tok[base + i0] : 0;
-            xsc[tt] = XH ? p.zsc[tok] : 1.0f;
-            const uint16_t *src = i0 < n ? (XH ? p.zh : p.x) + (size_t)tok * d : nullptr;
-#pragma unroll
-            for (int i = 0; i < BPL; i++) {
-                const int bc = g + L * i;
-                if (src && bc < nb) {
-                    const uint4 *q = reinterpret_cast<const uint4 *>(src + bc * 32);
-#pragma unroll
-                    for (int c = 0; c < 4; c++) {
-                        const uint4 v = q[c];
-                        xr[tt][i][4 * c + 0] = v.x; xr[tt][i][4 * c + 1] = v.y;
-                        xr[tt][i][4 * c + 2] = v.z; xr[tt][i][4 * c + 3] = v.w;
-                    }
-                } else {
-#pragma unroll
-                    for (int c = 0; c < 16; c++) xr[tt][i][c] = 0u;
-                }
-            }
-        }
+    // The expert's tokens one at a time: the token (d 16-bit values) is
+    // staged in LDS for the block's waves, which read each MX block's 32
+    // values next to its use; the weights alone stay in registers, so more
+    // blocks fit a CU and more weight loads are in flight.
+    static_assert(NT == 1, "one token at a time");
+    __shared__ __attribute__((aligned(16))) uint16_t s_x[kMaxDim];
+    for (int c0 = 0; c0 < n; c0++) {
+        const int tok = p.w.pos_tok[base + c0];
+        const float xsc = XH ? p.zsc[tok] : 1.0f;
+        const uint4 *src = reinterpret_cast<const uint4 *>((XH ? p.zh : p.x) + (size_t)tok * d);
+        __syncthreads();  // (every wave is done with the previous token)
+        for (int c = threadIdx.x; c < d / 8; c += kWaves * 64) reinterpret_cast<uint4 *>(s_x)[c] = src[c];
+        __syncthreads();
 #pragma unroll
         for (int gi = 0; gi < G; gi++) {
             const int row = rw0 + gi * RPI + rsub;
-            float gv = 0.0f, uv = 0.0f;
+            float ga = 0.0f, ua = 0.0f;
 #pragma unroll
-            for (int tt = 0; tt < NT; tt++) {
-                float ga = 0.0f, ua = 0.0f;
+            for (int i = 0; i < BPL; i++) {
+                const int bc = g + L * i;
+                uint32_t xr[16];
+                const uint4 *q = reinterpret_cast<const uint4 *>(s_x + min(bc, nb - 1) * 32);
 #pragma unroll
-                for (int i = 0; i < BPL; i++) {
-                    const float pg = XH ? fp4x32_dot_f16(qa[gi][i], xr[tt][i]) : fp4x32_dot_bf16(qa[gi][i], xr[tt][i]);
-                    const float pu = XH ? fp4x32_dot_f16(qb[gi][i], xr[tt][i]) : fp4x32_dot_bf16(qb[gi][i], xr[tt][i]);
-                    ga = sa[gi][i] == 255u ? ga : fmaf(pg, e8m0_to_f32(sa[gi][i]), ga);
-                    ua = sb[gi][i] == 255u ? ua : fmaf(pu, e8m0_to_f32(sb[gi][i]), ua);
-                    // keep each block's decode next to its use (register pressure)
-                    __builtin_amdgcn_sched_barrier(0);
+                for (int c = 0; c < 4; c++) {
+                    const uint4 v = q[c];
+                    xr[4 * c + 0] = v.x; xr[4 * c + 1] = v.y; xr[4 * c + 2] = v.z; xr[4 * c + 3] = v.w;
                 }
-                ga = group_sum<L>(ga);
-                ua = group_sum<L>(ua);
-                if (g == tt) {
-                    gv = XH ? ga * xsc[tt] : ga;
-                    uv = XH ? ua * xsc[tt] : ua;
-                }
+                // (blocks past the row: zero codes and a 255 scale, adding nothing)
+                const float pg = XH ? fp4x32_dot_f16(qa[gi][i], xr) : fp4x32_dot_bf16(qa[gi][i], xr);
+                const float pu = XH ? fp4x32_dot_f16(qb[gi][i], xr) : fp4x32_dot_bf16(qb[gi][i], xr);
+                ga = sa[gi][i] == 255u ? ga : fmaf(pg, e8m0_to_f32(sa[gi][i]), ga);
+                ua = sb[gi][i] == 255u ? ua : fmaf(pu, e8m0_to_f32(sb[gi][i]), ua);
+                // keep each block's decode next to its use (register pressure)
+                __builtin_amdgcn_sched_barrier(0);
             }
-            if (g < NT && row < F && c0 + g < n)
-                H[(size_t)(base + c0 + g) * F + row] = gated_act(gv, uv, s.act, s.b1, s.b2);
+            ga = group_sum<L>(ga);
+            ua = group_sum<L>(ua);
+            if (g == 0 && row < F)
+                H[(size_t)(base + c0) * F + row] = gated_act(XH ? ga * xsc : ga, XH ? ua * xsc : ua, s.act, s.b1, s.b2);
         }
     }
 }
@@ -288,47 +276,43 @@ __device__ __forceinline__ void routed_down_tile(const GemvParams &p, int blk)
             sc[gi][i] = ok ? s2[row * srow + bc] : 255u;
         }
     }
-    for (int c0 = 0; c0 < n; c0 += NT) {
-        float hr[NT][BPL][32];
-        float wt[NT];
+    // the expert's tokens one at a time, the token's H row (F fp32) staged
+    // in LDS (as for the gate/up's token)
+    static_assert(NT == 1, "one token at a time");
+    __shared__ __attribute__((aligned(16))) float s_h[kMaxDim];
+    for (int c0 = 0; c0 < n; c0++) {
+        const float wt = p.w.pos_w[base + c0];
+        const float4 *src = reinterpret_cast<const float4 *>(H + (size_t)(base + c0) * F);
+        __syncthreads();  // (every wave is done with the previous token)
+        for (int c = threadIdx.x; c < F / 4; c += kWaves * 64) reinterpret_cast<float4 *>(s_h)[c] = src[c];
+        __syncthreads();
+        // (each H block read once, for all of the wave's row groups)
+        float a[G];
 #pragma unroll
-        for (int tt = 0; tt < NT; tt++) {
-            const int i0 = c0 + tt;
-            wt[tt] = i0 < n ? p.w.pos_w[base + i0] : 0.0f;
+        for (int gi = 0; gi < G; gi++) a[gi] = 0.0f;
 #pragma unroll
-            for (int i = 0; i < BPL; i++) {
-                const int bc = g + L * i;
-                if (i0 < n && bc < nb) {
-                    const float4 *src = reinterpret_cast<const float4 *>(H + (size_t)(base + i0) * F + bc * 32);
+        for (int i = 0; i < BPL; i++) {
+            const int bc = g + L * i;
+            float hr[32];
+            const float4 *h4 = reinterpret_cast<const float4 *>(s_h + min(bc, nb - 1) * 32);
 #pragma unroll
-                    for (int c = 0; c < 8; c++) {
-                        const float4 v = src[c];
-                        hr[tt][i][4 * c + 0] = v.x; hr[tt][i][4 * c + 1] = v.y;
-                        hr[tt][i][4 * c + 2] = v.z; hr[tt][i][4 * c + 3] = v.w;
-                    }
-                } else {
+            for (int c = 0; c < 8; c++) {
+                const float4 v = h4[c];
+                hr[4 * c + 0] = v.x; hr[4 * c + 1] = v.y; hr[4 * c + 2] = v.z; hr[4 * c + 3] = v.w;
+            }
 #pragma unroll
-                    for (int c = 0; c < 32; c++) hr[tt][i][c] = 0.0f;
-                }
+            for (int gi = 0; gi < G; gi++) {
+                // (blocks past the row: zero codes and a 255 scale, adding nothing)
+                const float pp = fp4x32_dot_f32(q[gi][i], hr);
+                a[gi] = sc[gi][i] == 255u ? a[gi] : fmaf(pp, e8m0_to_f32(sc[gi][i]), a[gi]);
+                __builtin_amdgcn_sched_barrier(0);
             }
         }
 #pragma unroll
         for (int gi = 0; gi < G; gi++) {
             const int row = rw0 + gi * RPI + rsub;
-            float yv = 0.0f;
-#pragma unroll
-            for (int tt = 0; tt < NT; tt++) {
-                float a = 0.0f;
-#pragma unroll
-                for (int i = 0; i < BPL; i++) {
-                    const float pp = fp4x32_dot_f32(q[gi][i], hr[tt][i]);
-                    a = sc[gi][i] == 255u ? a : fmaf(pp, e8m0_to_f32(sc[gi][i]), a);
-                    __builtin_amdgcn_sched_barrier(0);
-                }
-                a = group_sum<L>(a);
-                if (g == tt) yv = a * wt[tt];
-            }
-            if (g < NT && row < d && c0 + g < n) p.w.Y[(size_t)(base + c0 + g) * d + row] = yv;
+            const float v = group_sum<L>(a[gi]);
+            if (g == 0 && row < d) p.w.Y[(size_t)(base + c0) * d + row] = v * wt;
         }
     }
 }
@@ -347,12 +331,18 @@ __global__ __launch_bounds__(256) void k_front(GemvParams p)
     }
 }
 
-template <int NT, int L, int BPL, int G, bool XH>
+// (SH2: the grid starts with the shared experts' down rows; without them
+// the kernel holds only the routed tile's registers)
+template <int NT, int L, int BPL, int G, bool XH, bool SH2>
 __global__ __launch_bounds__(256) void k_gemv_gateup(GemvParams p)
 {
     const int blk = blockIdx.x;
-    if (blk < p.n_sh2) shared_down_tile<NT>(p, blk);
-    else routed_gateup_tile<NT, L, BPL, G, XH>(p, blk - p.n_sh2);
+    if constexpr (SH2) {
+        if (blk < p.n_sh2) shared_down_tile<NT>(p, blk);
+        else routed_gateup_tile<NT, L, BPL, G, XH>(p, blk - p.n_sh2);
+    } else {
+        routed_gateup_tile<NT, L, BPL, G, XH>(p, blk);
+    }
 }
 
 template <int NT, int L, int BPL, int G>
@@ -399,8 +389,13 @@ static void gateup_launch(GemvParams p, int max_active, hipStream_t stream)
     p.tiles13 = (p.s.F + RPB - 1) / RPB;
     const int nblk = p.n_sh2 + max_active * p.tiles13;
     if (nblk <= 0) return;
-    if (p.zh) k_gemv_gateup<NT, L, BPL, G, true><<<nblk, 256, 0, stream>>>(p);
-    else k_gemv_gateup<NT, L, BPL, G, false><<<nblk, 256, 0, stream>>>(p);
+    if (p.n_sh2 > 0) {
+        if (p.zh) k_gemv_gateup<NT, L, BPL, G, true, true><<<nblk, 256, 0, stream>>>(p);
+        else k_gemv_gateup<NT, L, BPL, G, false, true><<<nblk, 256, 0, stream>>>(p);
+    } else {
+        if (p.zh) k_gemv_gateup<NT, L, BPL, G, true, false><<<nblk, 256, 0, stream>>>(p);
+        else k_gemv_gateup<NT, L, BPL, G, false, false><<<nblk, 256, 0, stream>>>(p);
+    }
 }
 
 template <int NT, int L, int BPL, int G>
