@@ -52,7 +52,7 @@ typedef enum { MOE_ACT_SITU = 0, MOE_ACT_SWIGLU = 1 } moe_act;
 /* which outputs moe_expert_forward / moe_layer write */
 typedef enum { MOE_OUT_BF16 = 0, MOE_OUT_F32 = 1, MOE_OUT_BOTH = 2 } moe_out_mode;
 
-/* which expert kernels run: AUTO picks the dequant-fused GEMV for up to 3
+/* which expert kernels run: AUTO picks the dequant-fused GEMV for up to 12
  * tokens and the grouped MFMA GEMM above (moe_path_for reports it); one
  * token on the GEMV path takes fused one-token kernels where their limits
  * allow (SiTU with b1*b2 <= 65504 among them).

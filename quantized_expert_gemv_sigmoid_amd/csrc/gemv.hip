@@ -124,38 +124,32 @@ __device__ __forceinline__ void shared_down_tile(const GemvParams &p, int blk)
             wv[rr][b] = (row < d && bc < nb) ? ld16(w2 + (size_t)row * F + bc * 8) : make_uint4(0, 0, 0, 0);
         }
     }
-    for (int c0 = 0; c0 < T; c0 += NT) {
-        float hr[NT][kSB][8];
+    // the tokens one at a time, the token's shared H row (F fp32) staged
+    // in LDS for the block's waves and read per 16-byte block of W2
+    static_assert(NT == 1, "one token at a time");
+    __shared__ __attribute__((aligned(16))) float s_hs[kMaxDim];
+    for (int c0 = 0; c0 < T; c0++) {
+        const float4 *src = reinterpret_cast<const float4 *>(p.w.Hs + (size_t)c0 * SF + (size_t)sidx * F);
+        __syncthreads();  // (every wave is done with the previous token)
+        for (int c = threadIdx.x; c < F / 4; c += kWaves * 64) reinterpret_cast<float4 *>(s_hs)[c] = src[c];
+        __syncthreads();
+        float a[2] = {0.0f, 0.0f};
 #pragma unroll
-        for (int tt = 0; tt < NT; tt++) {
+        for (int b = 0; b < kSB; b++) {
+            const int bc = lane + 64 * b;
+            if (bc < nb) {
+                const float4 *h4 = reinterpret_cast<const float4 *>(s_hs + bc * 8);
+                const float4 v0 = h4[0], v1 = h4[1];
+                const float h[8] = {v0.x, v0.y, v0.z, v0.w, v1.x, v1.y, v1.z, v1.w};
 #pragma unroll
-            for (int b = 0; b < kSB; b++) {
-                const int bc = lane + 64 * b;
-                if (c0 + tt < T && bc < nb) {
-                    const float4 *src = reinterpret_cast<const float4 *>(
-                        p.w.Hs + (size_t)(c0 + tt) * SF + (size_t)sidx * F + bc * 8);
-                    const float4 v0 = src[0], v1 = src[1];
-                    hr[tt][b][0] = v0.x; hr[tt][b][1] = v0.y; hr[tt][b][2] = v0.z; hr[tt][b][3] = v0.w;
-                    hr[tt][b][4] = v1.x; hr[tt][b][5] = v1.y; hr[tt][b][6] = v1.z; hr[tt][b][7] = v1.w;
-                } else {
-#pragma unroll
-                    for (int c = 0; c < 8; c++) hr[tt][b][c] = 0.0f;
-                }
+                for (int rr = 0; rr < 2; rr++) a[rr] = bf16x8_dot_f32(wv[rr][b], h, a[rr]);
             }
         }
 #pragma unroll
         for (int rr = 0; rr < 2; rr++) {
             const int row = r0 + rr;
-            float yv = 0.0f;
-#pragma unroll
-            for (int tt = 0; tt < NT; tt++) {
-                float a = 0.0f;
-#pragma unroll
-                for (int b = 0; b < kSB; b++) a = bf16x8_dot_f32(wv[rr][b], hr[tt][b], a);
-                a = group_sum<64>(a);
-                if (lane == tt) yv = a;
-            }
-            if (lane < NT && row < d && c0 + lane < T) ysh[(size_t)(c0 + lane) * d + row] = yv;
+            const float v = group_sum<64>(a[rr]);
+            if (lane == 0 && row < d) ysh[(size_t)c0 * d + row] = v;
         }
     }
 }

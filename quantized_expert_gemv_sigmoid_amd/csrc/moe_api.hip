@@ -22,16 +22,15 @@ using moe::Shape;
 using moe::Work;
 
 constexpr int32_t kMaxTokens = 1 << 20;
-// AUTO: GEMV up to here, MFMA above (measured at the K3 layer shape: the
-// grouped GEMM is faster from about 32 tokens on, the GEMV below 24)
-// AUTO: the GEMV kernels up to kGemvMaxTokens tokens (at the Kimi-K3 shape
-// the grouped GEMM is faster from 4 tokens up: 0.33 against 0.36 ms at T = 4,
-// 0.91 against 1.22 ms at T = 16); the latent layer's switch is its own.
+// AUTO: the GEMV kernels up to kGemvMaxTokens tokens, the grouped GEMM above
+// (at the Kimi-K3 shape, the same box: 0.290 against 0.306 ms at T = 4,
+// 0.499 against 0.513 at T = 8, 0.699 against 0.703 at T = 12, 0.902
+// against 0.893 at T = 16); the latent layer's switch is its own.
 // The MFMA path computes the router logits with the front kernel's fp32 rows
 // up to kFrontRouterMaxTokens tokens (one wave per expert row, the tokens in
 // turn: 19 us at T = 2 against 35 us for the router GEMM and its split and
 // reduce), with the router GEMM above.
-constexpr int32_t kGemvMaxTokens = 3;
+constexpr int32_t kGemvMaxTokens = 12;
 constexpr int32_t kLatentGemvMaxTokens = 24;
 constexpr int32_t kFrontRouterMaxTokens = 4;
 

@@ -136,9 +136,9 @@ def test_workspace_monotone_and_paths(L):
     assert all(a <= b for a, b in zip(sizes, sizes[1:]))
     assert sizes[0] % 256 == 0
     assert moe.path_for(d, 1) == moe.PATH_GEMV
-    # AUTO at the Kimi-K3 shape: GEMV up to 3 tokens, the grouped GEMM from 4
-    assert moe.path_for(d, 3) == moe.PATH_GEMV
-    assert moe.path_for(d, 4) == moe.PATH_MFMA
+    # AUTO at the Kimi-K3 shape: GEMV up to 12 tokens, the grouped GEMM from 13
+    assert moe.path_for(d, 12) == moe.PATH_GEMV
+    assert moe.path_for(d, 13) == moe.PATH_MFMA
     assert moe.path_for(desc(path=moe.PATH_GEMV), 4096) == moe.PATH_GEMV
     assert moe.path_for(desc(path=moe.PATH_MFMA), 1) == moe.PATH_MFMA
 

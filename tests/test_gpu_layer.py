@@ -290,8 +290,8 @@ def test_mfma_auto_threshold_and_gemv_agree():
     h = synth.host_layer(MFMA_SHAPE, 62, 0)
     g_auto = make_gpu_layer(MFMA_SHAPE, 62, host=h)
     g_gemv = make_gpu_layer(MFMA_SHAPE, 62, host=h, path=moe.PATH_GEMV)
-    assert moe.path_for(g_auto.desc, 3) == moe.PATH_GEMV
-    assert moe.path_for(g_auto.desc, 4) == moe.PATH_MFMA
+    assert moe.path_for(g_auto.desc, 12) == moe.PATH_GEMV
+    assert moe.path_for(g_auto.desc, 13) == moe.PATH_MFMA
     T = 200
     x, rw, bias = tokens(g_auto, T)
     a = run_layer(g_auto, x)
