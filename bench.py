@@ -84,7 +84,7 @@ LATENT_KERNELS = {
     "mfma": {"front": "k_split_router + k_ggemm<M_R> (router) + k_ggemm<M_R> (down projection) + k_ggemm<M_S13>",
              "topk_dispatch_z": "k_topk + k_dispatch_* + k_quant_z",
              "expert_gate_up": "k_ggemm<M_G13H>", "expert_down": "k_ggemm<M_D2>",
-             "norm_up_shared_out": "k_latent_accum + k_latent_split + k_ggemm<M_S2> (up) + k_ggemm<M_S2H> (shared down) + k_combine"},
+             "norm_up_shared_out": "k_latent_accum + k_latent_split + k_ggemm<M_UPH> (up) + k_ggemm<M_S2H> (shared down) + k_combine"},
 }
 WINDOWS = 3
 

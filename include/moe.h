@@ -228,8 +228,10 @@ moe_status moe_set_one_token_router_wait(int32_t microseconds);
  *
  * Precision: the latent z reaches the MXFP4 experts as fp16 with one
  * power-of-two scale per token (11 significant bits); the normed aggregate
- * reaches W_up in fp32 (GEMV) or as two bf16 parts (16 bits, MFMA); every
- * product accumulates in fp32, sums of squares in double.
+ * reaches W_up in fp32 (GEMV) or in fp16 (MFMA, W_up taken as fp16; a pass
+ * whose sums come out non-finite, an element past fp16's range, is computed
+ * again on two bf16 parts, 16 bits); every product accumulates in fp32, sums
+ * of squares in double.
  *
  * The expert tensors are those of moe_layer_desc with d = latent (W1, W3
  * [E][F][L/2] + [E][F][L/32]; W2 [E][L][F/2] + [E][L][F/32]); router and

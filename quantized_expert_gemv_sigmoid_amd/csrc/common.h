@@ -465,9 +465,9 @@ hipError_t launch_mfma_latent_experts(const Shape &s, const Weights &wt, const u
                                       hipEvent_t const *ev2);
 hipError_t launch_mfma_shared_gateup(const Shape &s, const uint16_t *x, const Weights &wt,
                                      const Work &w, hipStream_t st);
-hipError_t launch_mfma_up_shared(const Shape &s, int L, const uint16_t *up, const uint16_t *nhi,
-                                 const uint16_t *nlo, const Weights &wt, const Work &w, float *ysh,
-                                 hipStream_t st);
+hipError_t launch_mfma_up_shared(const Shape &s, int L, const uint16_t *up, const uint16_t *n16,
+                                 const uint16_t *nhi, const uint16_t *nlo, const Weights &wt,
+                                 const Work &w, float *ysh, hipStream_t st);
 
 // the latent layer's own buffers (besides the routed part's Work)
 struct LatentBufs {
@@ -477,6 +477,7 @@ struct LatentBufs {
     float *accL;      // [T][L] weighted aggregate of the routed experts
     double *ssp;      // [T][nch] its partial sums of squares
     uint16_t *nhi, *nlo;  // [T][L] normed aggregate as bf16 hi + lo (MFMA path)
+    uint16_t *n16;        // [T][L] the same as fp16 (MFMA path)
     float *ysh;       // [S + 1][T][H] up projection, shared experts' downs (MFMA path)
 };
 constexpr int kLatentChunk = 1024;  // aggregate elements per block (one float4 per thread)

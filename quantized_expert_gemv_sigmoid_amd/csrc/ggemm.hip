@@ -67,7 +67,7 @@ constexpr uint32_t kPast = 0xF0000000u;  // a buffer offset past every resource:
 // S13 / S2 shared gate/up and down (bf16); R router / plain linear (bf16
 // parts of the weights, fp32 out); G13H routed gate/up on fp16 input rows
 // with a power-of-two scale per row (the latent layer's experts)
-enum Mode { M_G13 = 0, M_D2 = 1, M_S13 = 2, M_S2 = 3, M_R = 4, M_G13H = 5, M_S2H = 6 };
+enum Mode { M_G13 = 0, M_D2 = 1, M_S13 = 2, M_S2 = 3, M_R = 4, M_G13H = 5, M_S2H = 6, M_UPH = 7 };
 
 struct GemmParams {
     Shape s;
@@ -86,6 +86,7 @@ struct GemmParams {
     int ksplit;       // router: K slices over blocks (partial logits summed after)
     float *rpart;     // router: partial logits [ksplit][T][E] (ksplit > 1)
     int rparts;       // router: bf16 parts per weight row (3: fp32 weights; 1: bf16 weights)
+    const uint16_t *a16; // UPH: input rows [T][F] fp16 (their two-part form at hs_hi / hs_lo)
     const uint16_t *zh;  // G13H: input rows [T][d] fp16 ...
     const float *zsc;    // ... times their scales [T]
 };
@@ -304,7 +305,7 @@ __device__ __forceinline__ uint32_t b_row(const GemmParams &p, const Blk &b, int
     if constexpr (MODE == M_G13 || MODE == M_G13H) return (uint32_t)gated_feature(b.tile, c) * (s.d / 2);
     else if constexpr (MODE == M_D2) return (uint32_t)(b.tile * GN + c) * (s.F / 2);
     else if constexpr (MODE == M_S13) return (uint32_t)gated_feature(b.tile, c) * (s.d * 2);
-    else if constexpr (MODE == M_S2 || MODE == M_S2H) return (uint32_t)(b.tile * GN + c) * (s.F * 2);
+    else if constexpr (MODE == M_S2 || MODE == M_S2H || MODE == M_UPH) return (uint32_t)(b.tile * GN + c) * (s.F * 2);
     else return (uint32_t)min(b.tile * GN + c, s.E - 1) * (p.rparts * s.d * 2);  // router: past E re-read row E - 1
 }
 // scale row of block column c (see the layout above)
@@ -440,7 +441,7 @@ __device__ __forceinline__ void pass_epilogue(const GemmParams &p, const Blk &bk
                         if (n >= bk.ncols) continue;
                         const float v = acc[mt][nb][e];
                         if constexpr (MODE == M_D2) p.w.Y[(size_t)(bk.base + m) * s.d + n] = v * wrow;
-                        else if constexpr (MODE == M_S2 || MODE == M_S2H) p.w.Ysh[((size_t)bk.group * s.T + m) * s.d + n] = v;
+                        else if constexpr (MODE == M_S2 || MODE == M_S2H || MODE == M_UPH) p.w.Ysh[((size_t)bk.group * s.T + m) * s.d + n] = v;
                         else if (p.ksplit > 1) p.rpart[((size_t)bk.ks * s.T + m) * s.E + n] = v;
                         else p.w.logits[(size_t)m * s.E + n] = v;
                     }
@@ -503,6 +504,9 @@ __device__ __forceinline__ bool wave_pass(const GemmParams &p, const Blk &bk_in,
         } else if constexpr (MODE == M_S2 || MODE == M_S2H) {
             abase = reinterpret_cast<const uint8_t *>(p.hs_hi);
             abytes = (uint32_t)s.T * s.S * s.F * 2;
+        } else if constexpr (MODE == M_UPH) {
+            abase = reinterpret_cast<const uint8_t *>(p.a16);
+            abytes = (uint32_t)s.T * s.S * s.F * 2;
         } else if constexpr (MODE == M_G13H) {
             abase = reinterpret_cast<const uint8_t *>(p.zh);
             abytes = (uint32_t)s.T * s.d * 2;
@@ -547,7 +551,7 @@ __device__ __forceinline__ bool wave_pass(const GemmParams &p, const Blk &bk_in,
             } else {
                 uint32_t el;  // element offset
                 if constexpr (MODE == M_D2) el = (uint32_t)(b.base + m) * s.F;
-                else if constexpr (MODE == M_S2 || MODE == M_S2H) el = (uint32_t)m * s.S * s.F + (uint32_t)b.group * s.F;
+                else if constexpr (MODE == M_S2 || MODE == M_S2H || MODE == M_UPH) el = (uint32_t)m * s.S * s.F + (uint32_t)b.group * s.F;
                 else if constexpr (MODE == M_G13H) el = (uint32_t)tok * s.d;
                 else el = (uint32_t)m * s.d;
                 e = el * 2 + q * 16;
@@ -575,7 +579,7 @@ __device__ __forceinline__ bool wave_pass(const GemmParams &p, const Blk &bk_in,
             } else if constexpr (MODE == M_S13) {
                 const uint32_t qb = (uint32_t)s.F * s.d * 2;
                 rb[j] = grsrc(reinterpret_cast<const uint8_t *>(up ? p.sh3 : p.sh1) + (size_t)b.group * qb, qb);
-            } else if constexpr (MODE == M_S2 || MODE == M_S2H) {
+            } else if constexpr (MODE == M_S2 || MODE == M_S2H || MODE == M_UPH) {
                 const uint32_t qb = (uint32_t)s.d * s.F * 2;
                 rb[j] = grsrc(reinterpret_cast<const uint8_t *>(p.sh2) + (size_t)b.group * qb, qb);
             } else {
@@ -891,7 +895,7 @@ __device__ __forceinline__ bool wave_pass(const GemmParams &p, const Blk &bk_in,
     auto b_half = [&](const uint4 (&av)[HS][NTW > 0 ? NTW : 1], const uint4 (&bv)[HS][NB]) __attribute__((always_inline)) {
 #pragma unroll
         for (int st = 0; st < HS; st++) {
-            if constexpr (MODE == M_S2H) {
+            if constexpr (MODE == M_S2H || MODE == M_UPH) {
                 f16x8_t bh[NB];
 #pragma unroll
                 for (int nb = 0; nb < NB; nb++) bh[nb] = bf16x8_to_f16(bv[st][nb]);
@@ -1099,7 +1103,7 @@ __device__ __forceinline__ bool wave_pass(const GemmParams &p, const Blk &bk_in,
 
     // (M_S2H: a weight past fp16's range gave a non-finite sum; the caller
     // then computes the pass again exactly)
-    if constexpr (MODE == M_S2H && !SPLIT) {
+    if constexpr ((MODE == M_S2H || MODE == M_UPH) && !SPLIT) {
         if (check) {
             bool bad = false;
 #pragma unroll
@@ -1179,7 +1183,7 @@ __device__ __forceinline__ void ggemm_block(const GemmParams &p, int x, LDS uint
         b.K = MODE == M_D2 ? s.F : s.d;
     } else {
         b.M = s.T;
-        b.K = MODE == M_S13 ? s.d : (MODE == M_S2 ? 2 * s.F : (MODE == M_S2H ? s.F : p.rparts * s.d));
+        b.K = MODE == M_S13 ? s.d : (MODE == M_S2 ? 2 * s.F : (MODE == M_S2H || MODE == M_UPH ? s.F : p.rparts * s.d));
     }
     if constexpr (MODE == M_R) b.K /= p.ksplit;  // (a multiple of the stage, see the launch)
     b.nS = b.K / C::KS;
@@ -1221,6 +1225,15 @@ __device__ __forceinline__ void ggemm_block(const GemmParams &p, int x, LDS uint
             if constexpr (MODE == M_S2H) {
                 if (!gemm_pass<MODE, GMT>(p, b, m0, mr, ring, true))
                     for (int r0 = 0; r0 < mr; r0 += 64) gemm_pass<MODE, 2, true>(p, b, m0 + r0, min(64, mr - r0), ring, false);
+            } else if constexpr (MODE == M_UPH) {
+                // (a non-finite sum: the pass again on the rows' two bf16
+                // parts, which hold every fp32 value exactly)
+                if (!gemm_pass<MODE, GMT>(p, b, m0, mr, ring, true)) {
+                    Blk b2 = b;
+                    b2.K = 2 * s.F;
+                    b2.nS = b2.K / Cfg<M_S2>::KS;
+                    gemm_pass<M_S2, GMT>(p, b2, m0, mr, ring, false);
+                }
             } else {
                 gemm_pass<MODE, GMT>(p, b, m0, mr, ring, false);
             }
@@ -1512,6 +1525,7 @@ static GemmParams make_gemm_params(const Shape &s, const uint16_t *x, const Weig
     p.rparts = 3;
     p.zh = nullptr;
     p.zsc = nullptr;
+    p.a16 = nullptr;
     return p;
 }
 
@@ -1629,12 +1643,12 @@ hipError_t launch_mfma_shared_gateup(const Shape &s, const uint16_t *x, const We
     return hipGetLastError();
 }
 
-// ysh[(S + 1)][T][d]: slot 0 = W_up n (n as bf16 hi / lo parts [T][L]),
-// slots 1 .. S = the shared experts' down projections (fp16 H; s.d = hidden
-// width)
-hipError_t launch_mfma_up_shared(const Shape &s, int L, const uint16_t *up, const uint16_t *nhi,
-                                 const uint16_t *nlo, const Weights &wt, const Work &w, float *ysh,
-                                 hipStream_t st)
+// ysh[(S + 1)][T][d]: slot 0 = W_up n (n as fp16 [T][L], and as bf16 hi / lo
+// parts for passes whose fp16 sums are not finite), slots 1 .. S = the shared
+// experts' down projections (fp16 H; s.d = hidden width)
+hipError_t launch_mfma_up_shared(const Shape &s, int L, const uint16_t *up, const uint16_t *n16,
+                                 const uint16_t *nhi, const uint16_t *nlo, const Weights &wt,
+                                 const Work &w, float *ysh, hipStream_t st)
 {
     const int mb = (s.T + GM - 1) / GM;
     {
@@ -1645,9 +1659,10 @@ hipError_t launch_mfma_up_shared(const Shape &s, int L, const uint16_t *up, cons
         wu.Ysh = ysh;
         GemmParams p = make_gemm_params(su, nullptr, Weights{}, wu);
         p.sh2 = up;
+        p.a16 = n16;
         p.hs_hi = nhi;
         p.hs_lo = nlo;
-        launch_mode<M_S2>(p, 1, (s.d + GN - 1) / GN, mb, st);
+        launch_mode<M_UPH>(p, 1, (s.d + GN - 1) / GN, mb, st);
     }
     if (s.S > 0) {
         Work ws = w;

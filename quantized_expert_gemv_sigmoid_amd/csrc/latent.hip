@@ -182,13 +182,14 @@ __device__ __forceinline__ float rms_inv(const double *ssp, int nch, int L, floa
 }
 
 // block (t, chunk): n = aggregate * inv * norm_w (or the aggregate), as bf16
-// hi = rne(n), lo = rne(n - hi)
+// hi = rne(n), lo = rne(n - hi), and as fp16 rne(n)
 __global__ __launch_bounds__(256) void k_latent_split(int T, int L, int nch, int do_norm, float eps,
                                                       const float *__restrict__ nw,
                                                       const float *__restrict__ accL,
                                                       const double *__restrict__ ssp,
                                                       uint16_t *__restrict__ nhi,
-                                                      uint16_t *__restrict__ nlo)
+                                                      uint16_t *__restrict__ nlo,
+                                                      _Float16 *__restrict__ n16)
 {
     const int t = blockIdx.x / nch, ch = blockIdx.x % nch;
     const int c = ch * 256 + threadIdx.x;
@@ -197,12 +198,16 @@ __global__ __launch_bounds__(256) void k_latent_split(int T, int L, int nch, int
     const float4 a = reinterpret_cast<const float4 *>(accL + (size_t)t * L)[c];
     const float v[4] = {a.x, a.y, a.z, a.w};
     uint16_t h[4], l[4];
+    _Float16 f[4];
 #pragma unroll
     for (int j = 0; j < 4; j++) {
         const float n = do_norm ? v[j] * inv * (nw ? nw[4 * c + j] : 1.0f) : v[j];
         h[j] = f32_to_bf16_rne(n);
         l[j] = f32_to_bf16_rne(n - __uint_as_float((uint32_t)h[j] << 16));
+        f[j] = (_Float16)n;
     }
+    typedef _Float16 f16x4_t __attribute__((ext_vector_type(4)));
+    reinterpret_cast<f16x4_t *>(n16 + (size_t)t * L)[c] = (f16x4_t){f[0], f[1], f[2], f[3]};
     reinterpret_cast<uint2 *>(nhi + (size_t)t * L)[c] =
         make_uint2((uint32_t)h[0] | ((uint32_t)h[1] << 16), (uint32_t)h[2] | ((uint32_t)h[3] << 16));
     reinterpret_cast<uint2 *>(nlo + (size_t)t * L)[c] =
@@ -364,7 +369,7 @@ hipError_t launch_latent_split(int T, int L, int do_norm, float eps, const float
     const int nch = latent_chunks(L);
     if (T > 0)
         k_latent_split<<<T * nch, 256, 0, st>>>(T, L, nch, do_norm, eps, norm_w, b.accL, b.ssp, b.nhi,
-                                                b.nlo);
+                                                b.nlo, reinterpret_cast<_Float16 *>(b.n16));
     return hipGetLastError();
 }
 

@@ -360,6 +360,7 @@ size_t carve_latent(const moe_latent_desc *d, int32_t T, char *base, Work *w, mo
     b.ssp = (double *)take(Tz * moe::latent_chunks((int)L) * 8);
     b.nhi = (uint16_t *)take(Tz * L * 2);
     b.nlo = (uint16_t *)take(Tz * L * 2);
+    b.n16 = (uint16_t *)take(Tz * L * 2);
     b.ysh = (float *)take((S + 1) * Tz * H * 4);
     if (w) *w = v;
     if (lb) *lb = b;
@@ -424,7 +425,7 @@ moe_status run_latent(const moe_latent_desc *d, int32_t T, const uint16_t *x, in
                                        ob, of, st));
     } else {
         MOE_TRY(moe::launch_latent_split(T, L, d->latent_norm, d->rms_eps, d->norm_w, b, st));
-        MOE_TRY(moe::launch_mfma_up_shared(so, L, d->up, b.nhi, b.nlo, wt, w, b.ysh, st));
+        MOE_TRY(moe::launch_mfma_up_shared(so, L, d->up, b.n16, b.nhi, b.nlo, wt, w, b.ysh, st));
         // out = slot 0 (W_up n) + slots 1 .. S (shared), in that order
         Shape sc = so;
         sc.k = 0;

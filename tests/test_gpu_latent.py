@@ -106,6 +106,21 @@ def test_latent_mfma_weights_out_of_fp16_window():
     _check(gl, 120, screened=False)
 
 
+def test_latent_mfma_up_projection_past_fp16():
+    # The up projection multiplies the normed aggregate n in fp16.  Norm
+    # weight 37 of 10^6 puts n's element 37 past fp16's range (it converts to
+    # infinity), so every pass of the up projection comes out non-finite and
+    # is computed again on n's two bf16 parts; the outputs are all ~10^6
+    # times larger than usual and must match the oracle as they are.
+    h = synth.host_latent_layer(MID, 75, 0)
+    h.norm_w = h.norm_w.copy()
+    h.norm_w[37] = 1.0e6
+    log("case: latent MFMA, a normed-aggregate element past fp16's range")
+    gl = make_gpu_latent(MID, 75, host=h, path=2)
+    _, out_f, _, _, _, _ = _check(gl, 150)
+    assert np.isfinite(out_f).all() and np.abs(out_f).max() > 65504.0
+
+
 def test_latent_timed_equals_layer_and_zero_tokens():
     import quantized_expert_gemv_sigmoid_amd as moe
     import synth.device as sdev
