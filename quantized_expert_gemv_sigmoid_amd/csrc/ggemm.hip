@@ -1304,22 +1304,31 @@ __global__ __launch_bounds__(GT) void k_ggemm_pair(GemmParams p1, GemmParams p2,
 // Router weights fp32 -> three bf16 parts whose sum is exact: hi = rne(w),
 // mid = rne(w - hi), lo = rne(w - hi - mid); row e of the result is
 // [hi(d) | mid(d) | lo(d)] so that x . w = [x x x] . row.
+// (four weights per thread: d is a multiple of 4 on the MFMA path)
 __global__ __launch_bounds__(256) void k_split_router(int E, int d, const float *__restrict__ Wr,
                                                       uint16_t *__restrict__ wr3)
 {
-    const size_t i = (size_t)blockIdx.x * blockDim.x + threadIdx.x;
+    const size_t i = ((size_t)blockIdx.x * blockDim.x + threadIdx.x) * 4;
     if (i >= (size_t)E * d) return;
     const size_t e = i / d, c = i % d;
-    const float w = Wr[i];
-    const uint16_t hi = f32_to_bf16_rne(w);
-    const float r1 = w - __uint_as_float((uint32_t)hi << 16);
-    const uint16_t mid = f32_to_bf16_rne(r1);
-    const float r2 = r1 - __uint_as_float((uint32_t)mid << 16);
-    const uint16_t lo = f32_to_bf16_rne(r2);
+    const float4 w4 = *reinterpret_cast<const float4 *>(Wr + i);
+    const float w[4] = {w4.x, w4.y, w4.z, w4.w};
+    uint32_t hw[2] = {0u, 0u}, mw[2] = {0u, 0u}, lw[2] = {0u, 0u};
+#pragma unroll
+    for (int j = 0; j < 4; j++) {
+        const uint16_t hi = f32_to_bf16_rne(w[j]);
+        const float r1 = w[j] - __uint_as_float((uint32_t)hi << 16);
+        const uint16_t mid = f32_to_bf16_rne(r1);
+        const float r2 = r1 - __uint_as_float((uint32_t)mid << 16);
+        const uint16_t lo = f32_to_bf16_rne(r2);
+        hw[j >> 1] |= (uint32_t)hi << (16 * (j & 1));
+        mw[j >> 1] |= (uint32_t)mid << (16 * (j & 1));
+        lw[j >> 1] |= (uint32_t)lo << (16 * (j & 1));
+    }
     uint16_t *row = wr3 + e * 3 * d;
-    row[c] = hi;
-    row[d + c] = mid;
-    row[2 * d + c] = lo;
+    *reinterpret_cast<uint2 *>(row + c) = make_uint2(hw[0], hw[1]);
+    *reinterpret_cast<uint2 *>(row + d + c) = make_uint2(mw[0], mw[1]);
+    *reinterpret_cast<uint2 *>(row + 2 * d + c) = make_uint2(lw[0], lw[1]);
 }
 
 // The tokens as two fp8 (E4M3) terms for the scaled MFMA of the routed
@@ -1385,13 +1394,22 @@ __global__ __launch_bounds__(256) void k_quant_x(int T, int d, const uint16_t *_
 }
 
 // logits[t][e] = sum over the K slices, in slice order, of the partials
+// (loaded eight slices at a time, so that the loads are in flight together;
+// the sum keeps the slice order)
 __global__ __launch_bounds__(256) void k_router_reduce(int n, int ksplit, const float *__restrict__ rpart,
                                                        float *__restrict__ logits)
 {
     const int i = blockIdx.x * 256 + threadIdx.x;
     if (i >= n) return;
     float v = 0.0f;
-    for (int j = 0; j < ksplit; j++) v += rpart[(size_t)j * n + i];
+    for (int j0 = 0; j0 < ksplit; j0 += 8) {
+        float t[8];
+#pragma unroll
+        for (int u = 0; u < 8; u++) t[u] = j0 + u < ksplit ? rpart[(size_t)(j0 + u) * n + i] : 0.0f;
+#pragma unroll
+        for (int u = 0; u < 8; u++)
+            if (j0 + u < ksplit) v += t[u];
+    }
     logits[i] = v;
 }
 
@@ -1533,7 +1551,7 @@ hipError_t launch_mfma_router(const Shape &s, const uint16_t *x, const Weights &
                               hipStream_t st)
 {
     const size_t n = (size_t)s.E * s.d;
-    k_split_router<<<(unsigned)((n + 255) / 256), 256, 0, st>>>(s.E, s.d, wt.router_w,
+    k_split_router<<<(unsigned)((n / 4 + 255) / 256), 256, 0, st>>>(s.E, s.d, wt.router_w,
                                                                reinterpret_cast<uint16_t *>(w.extra));
     GemmParams p = make_gemm_params(s, x, wt, w);
     const int nt = (s.E + GN - 1) / GN, mb = (s.T + GM - 1) / GM;
