@@ -25,13 +25,16 @@ constexpr int32_t kMaxTokens = 1 << 20;
 // AUTO: the GEMV kernels up to kGemvMaxTokens tokens, the grouped GEMM above
 // (at the Kimi-K3 shape, the same box: 0.290 against 0.306 ms at T = 4,
 // 0.499 against 0.513 at T = 8, 0.699 against 0.703 at T = 12, 0.902
-// against 0.893 at T = 16); the latent layer's switch is its own.
+// against 0.893 at T = 16).  The latent layer's switch is its own: its GEMV
+// path up to kLatentGemvMaxTokens (at the Kimi-K3 latent shape, the same
+// box: 0.675 against 0.688 ms at T = 6; the MFMA path 0.797 against 0.859
+// at T = 8, 1.22 against 1.61 at T = 16).
 // The MFMA path computes the router logits with the front kernel's fp32 rows
 // up to kFrontRouterMaxTokens tokens (one wave per expert row, the tokens in
 // turn: 19 us at T = 2 against 35 us for the router GEMM and its split and
 // reduce), with the router GEMM above.
 constexpr int32_t kGemvMaxTokens = 12;
-constexpr int32_t kLatentGemvMaxTokens = 24;
+constexpr int32_t kLatentGemvMaxTokens = 6;
 constexpr int32_t kFrontRouterMaxTokens = 4;
 
 bool aligned(const void *p, size_t a) { return ((uintptr_t)p % a) == 0; }
