@@ -461,13 +461,12 @@ hipError_t launch_mfma_experts(const Shape &s, const uint16_t *x, const Weights 
 hipError_t launch_mfma_linear(const Shape &s, const uint16_t *x, const uint16_t *W, float *out,
                               const Work &w, hipStream_t st);
 hipError_t launch_mfma_latent_experts(const Shape &s, const Weights &wt, const uint16_t *zh,
-                                      const float *zsc, const Work &w, hipStream_t st,
+                                      const float *zsc, const Shape &so, const uint16_t *x,
+                                      float *ysh_sh, const Work &w, hipStream_t st,
                                       hipEvent_t const *ev2);
-hipError_t launch_mfma_shared_gateup(const Shape &s, const uint16_t *x, const Weights &wt,
-                                     const Work &w, hipStream_t st);
-hipError_t launch_mfma_up_shared(const Shape &s, int L, const uint16_t *up, const uint16_t *n16,
-                                 const uint16_t *nhi, const uint16_t *nlo, const Weights &wt,
-                                 const Work &w, float *ysh, hipStream_t st);
+hipError_t launch_mfma_up(const Shape &s, int L, const uint16_t *up, const uint16_t *n16,
+                          const uint16_t *nhi, const uint16_t *nlo, const Work &w, float *ysh,
+                          hipStream_t st);
 
 // the latent layer's own buffers (besides the routed part's Work)
 struct LatentBufs {

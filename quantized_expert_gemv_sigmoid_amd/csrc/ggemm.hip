@@ -1636,37 +1636,48 @@ hipError_t launch_mfma_linear(const Shape &s, const uint16_t *x, const uint16_t 
 }
 
 // routed experts of the latent layer: gate/up on the fp16 rows zh (times
-// their scales zsc), then down + routing weight into the slot rows
+// their scales zsc), then down + routing weight into the slot rows.  The
+// shared experts (shape so: the full width, on the tokens x) run in the same
+// two launches, their gate/up blocks at the head of the routed gate/up grid
+// (H as fp16 in w.Hs) and their down blocks at the head of the routed down
+// grid (outputs at ysh_sh [S][T][so.d]), as in the Kimi-K3 layer's
+// launches: alone they have few blocks at small T.
 hipError_t launch_mfma_latent_experts(const Shape &s, const Weights &wt, const uint16_t *zh,
-                                      const float *zsc, const Work &w, hipStream_t st,
+                                      const float *zsc, const Shape &so, const uint16_t *x,
+                                      float *ysh_sh, const Work &w, hipStream_t st,
                                       hipEvent_t const *ev2)
 {
     GemmParams p = make_gemm_params(s, nullptr, wt, w);
     p.zh = zh;
     p.zsc = zsc;
     const int max_active = min(s.E, s.T * s.k);
-    launch_mode<M_G13H>(p, max_active, (s.F + 127) / 128, 1, st);
+    int ng, nd, n13 = 0, n2 = 0;
+    const GemmParams pg = mode_params(p, max_active, (s.F + 127) / 128, 1, 1, &ng);
+    const GemmParams pd = mode_params(p, max_active, (s.d + GN - 1) / GN, 1, 1, &nd);
+    GemmParams p13 = pg, p2 = pd;
+    if (so.S > 0) {
+        const int mb = (so.T + GM - 1) / GM;
+        p13 = mode_params(make_gemm_params(so, x, wt, w), so.S, (so.F + 127) / 128, mb, 1, &n13);
+        Work ws = w;
+        ws.Ysh = ysh_sh;
+        p2 = mode_params(make_gemm_params(so, nullptr, wt, ws), so.S, (so.d + GN - 1) / GN, mb, 1, &n2);
+    }
+    if (n13 > 0) launch_pair<M_S13, M_G13H>(p13, n13, pg, ng, st);
+    else if (ng > 0) k_ggemm<M_G13H><<<ng, GT, 0, st>>>(pg);
     if (ev2) (void)hipEventRecord(ev2[0], st);
-    launch_mode<M_D2>(p, max_active, (s.d + GN - 1) / GN, 1, st);
+    if (n2 > 0) launch_pair<M_S2H, M_D2>(p2, n2, pd, nd, st);
+    else if (nd > 0) k_ggemm<M_D2><<<nd, GT, 0, st>>>(pd);
     if (ev2) (void)hipEventRecord(ev2[1], st);
     return hipGetLastError();
 }
 
-// shared experts' gate/up at the full width (H as fp16 in w.Hs)
-hipError_t launch_mfma_shared_gateup(const Shape &s, const uint16_t *x, const Weights &wt,
-                                     const Work &w, hipStream_t st)
-{
-    GemmParams p = make_gemm_params(s, x, wt, w);
-    if (s.S > 0) launch_mode<M_S13>(p, s.S, (s.F + 127) / 128, (s.T + GM - 1) / GM, st);
-    return hipGetLastError();
-}
-
-// ysh[(S + 1)][T][d]: slot 0 = W_up n (n as fp16 [T][L], and as bf16 hi / lo
-// parts for passes whose fp16 sums are not finite), slots 1 .. S = the shared
-// experts' down projections (fp16 H; s.d = hidden width)
-hipError_t launch_mfma_up_shared(const Shape &s, int L, const uint16_t *up, const uint16_t *n16,
-                                 const uint16_t *nhi, const uint16_t *nlo, const Weights &wt,
-                                 const Work &w, float *ysh, hipStream_t st)
+// ysh[(S + 1)][T][d] slot 0 = W_up n (n as fp16 [T][L], and as bf16 hi / lo
+// parts for passes whose fp16 sums are not finite; s.d = hidden width).
+// (Slots 1 .. S, the shared experts' down projections, come with the routed
+// down's launch.)
+hipError_t launch_mfma_up(const Shape &s, int L, const uint16_t *up, const uint16_t *n16,
+                          const uint16_t *nhi, const uint16_t *nlo, const Work &w, float *ysh,
+                          hipStream_t st)
 {
     const int mb = (s.T + GM - 1) / GM;
     {
@@ -1681,12 +1692,6 @@ hipError_t launch_mfma_up_shared(const Shape &s, int L, const uint16_t *up, cons
         p.hs_hi = nhi;
         p.hs_lo = nlo;
         launch_mode<M_UPH>(p, 1, (s.d + GN - 1) / GN, mb, st);
-    }
-    if (s.S > 0) {
-        Work ws = w;
-        ws.Ysh = ysh + (size_t)s.T * s.d;
-        GemmParams p = make_gemm_params(s, nullptr, wt, ws);
-        launch_mode<M_S2H>(p, s.S, (s.d + GN - 1) / GN, mb, st);
     }
     return hipGetLastError();
 }

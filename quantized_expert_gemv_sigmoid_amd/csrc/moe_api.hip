@@ -411,7 +411,6 @@ moe_status run_latent(const moe_latent_desc *d, int32_t T, const uint16_t *x, in
         Shape sd = so;
         sd.E = L;
         MOE_TRY(moe::launch_mfma_linear(sd, x, d->down, b.zf, w, st));
-        MOE_TRY(moe::launch_mfma_shared_gateup(so, x, wt, w, st));
     }
     MOE_TRY(mark(ev, 1, st));
     const moe::ZQuant zq{b.zf, b.zh, b.zsc, L};
@@ -420,7 +419,9 @@ moe_status run_latent(const moe_latent_desc *d, int32_t T, const uint16_t *x, in
     if (path == MOE_PATH_GEMV) {
         MOE_TRY(moe::launch_gemv_experts(si, nullptr, wt, 0, w, st, ev ? ev + 3 : nullptr, b.zh, b.zsc));
     } else {
-        MOE_TRY(moe::launch_mfma_latent_experts(si, wt, b.zh, b.zsc, w, st, ev ? ev + 3 : nullptr));
+        // (the shared experts' gate/up and down with the routed launches)
+        MOE_TRY(moe::launch_mfma_latent_experts(si, wt, b.zh, b.zsc, so, x, b.ysh + (size_t)T * so.d, w, st,
+                                                ev ? ev + 3 : nullptr));
     }
     MOE_TRY(moe::launch_latent_accum(T, so.k, L, w, b, st));
     if (path == MOE_PATH_GEMV) {
@@ -428,7 +429,7 @@ moe_status run_latent(const moe_latent_desc *d, int32_t T, const uint16_t *x, in
                                        ob, of, st));
     } else {
         MOE_TRY(moe::launch_latent_split(T, L, d->latent_norm, d->rms_eps, d->norm_w, b, st));
-        MOE_TRY(moe::launch_mfma_up_shared(so, L, d->up, b.n16, b.nhi, b.nlo, wt, w, b.ysh, st));
+        MOE_TRY(moe::launch_mfma_up(so, L, d->up, b.n16, b.nhi, b.nlo, w, b.ysh, st));
         // out = slot 0 (W_up n) + slots 1 .. S (shared), in that order
         Shape sc = so;
         sc.k = 0;
