@@ -81,10 +81,13 @@ LATENT_KERNELS = {
              "topk_dispatch_z": "k_dispatch_small/k_topk+k_dispatch_* + k_quant_z",
              "expert_gate_up": "k_gemv_gateup (fp16 latent rows)", "expert_down": "k_gemv_down",
              "norm_up_shared_out": "k_latent_accum + k_latent_out (norm, up projection, shared down)"},
-    "mfma": {"front": "k_split_router + k_ggemm<M_R> (router) + k_ggemm<M_R> (down projection) + k_ggemm<M_S13>",
+    "mfma": {"front": "k_split_router + k_ggemm<M_R> (router) + k_ggemm<M_R> (down projection)",
              "topk_dispatch_z": "k_topk + k_dispatch_* + k_quant_z",
-             "expert_gate_up": "k_ggemm<M_G13H>", "expert_down": "k_ggemm<M_D2>",
-             "norm_up_shared_out": "k_latent_accum + k_latent_split + k_ggemm<M_UPH> (up) + k_ggemm<M_S2H> (shared down) + k_combine"},
+             "expert_gate_up": "k_ggemm_pair<M_S13, M_G13H> (shared gate/up at the head below 512 shared blocks; "
+                               "else k_ggemm<M_S13> + k_ggemm<M_G13H>)",
+             "expert_down": "k_ggemm_pair<M_S2H, M_D2> (shared down at the head below 512 shared blocks; "
+                            "else k_ggemm<M_S2H> + k_ggemm<M_D2>)",
+             "norm_up_shared_out": "k_latent_accum + k_latent_split + k_ggemm<M_UPH> (up) + k_combine"},
 }
 WINDOWS = 3
 

@@ -222,7 +222,7 @@ moe_status moe_set_one_token_router_wait(int32_t microseconds);
  * Shapes: E, k, F, S as for moe_layer_desc; H = hidden, L = latent.
  * Supported: H a multiple of 32 in [32, 8192], L one in [32, 4096],
  * L + S*F <= 16384 and the moe_layer_desc limits on E, k, F and S;
- * otherwise MOE_EUNSUPPORTED.  The MFMA path (AUTO above 6 tokens) also needs H and
+ * otherwise MOE_EUNSUPPORTED.  The MFMA path (AUTO above 3 tokens) also needs H and
  * L multiples of 256 and the moe_layer_desc MFMA limits; AUTO falls back to
  * GEMV outside them.
  *

@@ -27,14 +27,14 @@ constexpr int32_t kMaxTokens = 1 << 20;
 // 0.499 against 0.513 at T = 8, 0.699 against 0.703 at T = 12, 0.902
 // against 0.893 at T = 16).  The latent layer's switch is its own: its GEMV
 // path up to kLatentGemvMaxTokens (at the Kimi-K3 latent shape, the same
-// box: 0.675 against 0.688 ms at T = 6; the MFMA path 0.797 against 0.859
-// at T = 8, 1.22 against 1.61 at T = 16).
+// box: 0.393 against 0.415 ms at T = 3; the MFMA path 0.456 against 0.488
+// at T = 4, 0.586 against 0.676 at T = 6).
 // The MFMA path computes the router logits with the front kernel's fp32 rows
 // up to kFrontRouterMaxTokens tokens (one wave per expert row, the tokens in
 // turn: 19 us at T = 2 against 35 us for the router GEMM and its split and
 // reduce), with the router GEMM above.
 constexpr int32_t kGemvMaxTokens = 12;
-constexpr int32_t kLatentGemvMaxTokens = 6;
+constexpr int32_t kLatentGemvMaxTokens = 3;
 constexpr int32_t kFrontRouterMaxTokens = 4;
 
 bool aligned(const void *p, size_t a) { return ((uintptr_t)p % a) == 0; }

@@ -1,7 +1,7 @@
 """C-ABI checks of the latent-layer entry points that need no GPU: the
 Python mirror of moe_latent_desc has the C layout, invalid descriptors and
 calls are refused on the host before any launch, workspace sizes grow with
-T and the AUTO path switches to MFMA above 6 tokens where it can."""
+T and the AUTO path switches to MFMA above 3 tokens where it can."""
 import ctypes
 import os
 import subprocess
@@ -98,8 +98,8 @@ def test_latent_workspace_monotone_and_paths(L):
     sizes = [L.moe_latent_workspace_bytes(ctypes.byref(d), t) for t in ts]
     assert all(a <= b for a, b in zip(sizes, sizes[1:]))
     assert moe.latent_path_for(d, 1) == moe.PATH_GEMV
-    assert moe.latent_path_for(d, 6) == moe.PATH_GEMV
-    assert moe.latent_path_for(d, 7) == moe.PATH_MFMA
+    assert moe.latent_path_for(d, 3) == moe.PATH_GEMV
+    assert moe.latent_path_for(d, 4) == moe.PATH_MFMA
     assert moe.latent_path_for(ldesc(path=moe.PATH_GEMV), 4096) == moe.PATH_GEMV
     # MFMA needs the hidden and latent widths to be multiples of 256
     assert moe.latent_path_for(ldesc(hidden=7200), 4096) == moe.PATH_GEMV

@@ -55,7 +55,7 @@ def test_latent_tiny_workload(path):
     assert np.array_equal(out_f, out_f2) and np.array_equal(ids, ids2)
 
 
-@pytest.mark.parametrize("T", [1, 5, 6, 7, 24, 37, 300])
+@pytest.mark.parametrize("T", [1, 3, 4, 5, 24, 37, 300])
 def test_latent_ragged_auto(T):
     import quantized_expert_gemv_sigmoid_amd as moe
     gl = make_gpu_latent(MID, 71)
