@@ -223,22 +223,30 @@ def cpu_baseline(shape, seed, zipf, pools, budget_s):
                       f"shared expert FFNs each), {spent:.1f} s of oracle time"}
 
 
-def latent_phase_bytes(ls, T, counts):
-    """Algorithmic HBM bytes of each latent-layer phase for one step."""
+def latent_phase_bytes(ls, T, counts, kind):
+    """Algorithmic HBM bytes of each latent-layer phase for one step.  The
+    GEMV path runs the shared experts' gate/up in its front kernel and their
+    down in its output kernel; the MFMA path runs them with the routed
+    gate/up and down."""
     H, L, F, S, E = ls.hidden, ls.latent, ls.d_ffn, ls.n_shared, ls.n_experts
     active = int((counts > 0).sum())
     w13 = 2 * (F * L // 2 + F * L // 32)
     w2 = L * F // 2 + L * F // 32
-    return {"front": E * H * 4 + L * H * 2 + S * 2 * F * H * 2 + T * H * 2, "topk_dispatch_z": 0,
-            "expert_gate_up": active * w13, "expert_down": active * w2,
-            "norm_up_shared_out": H * L * 2 + L * 4 + S * H * F * 2 + T * H * 2}
+    sh13, sh2 = S * 2 * F * H * 2, S * H * F * 2
+    m = kind == "mfma"
+    return {"front": E * H * 4 + L * H * 2 + (0 if m else sh13) + T * H * 2, "topk_dispatch_z": 0,
+            "expert_gate_up": active * w13 + (sh13 if m else 0), "expert_down": active * w2 + (sh2 if m else 0),
+            "norm_up_shared_out": H * L * 2 + L * 4 + (0 if m else sh2) + T * H * 2}
 
 
-def latent_phase_flops(ls, T):
+def latent_phase_flops(ls, T, kind):
     H, L, F, S, E, k = ls.hidden, ls.latent, ls.d_ffn, ls.n_shared, ls.n_experts, ls.top_k
-    return {"front": 2 * T * (E * H + L * H + 2 * S * F * H), "topk_dispatch_z": 0,
-            "expert_gate_up": 4 * T * k * L * F, "expert_down": 2 * T * k * L * F,
-            "norm_up_shared_out": 2 * T * (H * L + S * H * F)}
+    sh13, sh2 = 2 * T * 2 * S * F * H, 2 * T * S * H * F
+    m = kind == "mfma"
+    return {"front": 2 * T * (E * H + L * H) + (0 if m else sh13), "topk_dispatch_z": 0,
+            "expert_gate_up": 4 * T * k * L * F + (sh13 if m else 0),
+            "expert_down": 2 * T * k * L * F + (sh2 if m else 0),
+            "norm_up_shared_out": 2 * T * H * L + (0 if m else sh2)}
 
 
 def latent_cpu_baseline(ls, seed, pool, budget_s):
@@ -340,9 +348,9 @@ def measure_latent(lidx, steps, warmup, pool, use_graph, cpu_seconds, hbm_copy_g
     eager_ms = start.elapsed_time(end) / K
     ph_ms = {p: float(np.mean([evs[i][j].elapsed_time(evs[i][j + 1]) for i in range(K)]))
              for j, p in enumerate(LATENT_PHASES)}
-    ph_bytes = {p: float(np.mean([latent_phase_bytes(ls, T, counts[i % npool])[p] for i in range(K)]))
+    ph_bytes = {p: float(np.mean([latent_phase_bytes(ls, T, counts[i % npool], kind)[p] for i in range(K)]))
                 for p in LATENT_PHASES}
-    ph_flops = latent_phase_flops(ls, T)
+    ph_flops = latent_phase_flops(ls, T, kind)
     step_bytes = sum(ph_bytes.values())
     step_flops = sum(ph_flops.values())
     dom = max(("front", "expert_gate_up", "expert_down", "norm_up_shared_out"), key=lambda p: ph_ms[p])
