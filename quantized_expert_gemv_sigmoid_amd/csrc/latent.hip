@@ -60,29 +60,43 @@ __device__ __forceinline__ void load_row(uint4 (&w)[NP], const uint16_t *row, in
     }
 }
 
+constexpr int kFrontMaxH = 8192;  // the hidden width's bound (the token staged in LDS)
+
 // NP = ceil(H / 512) pieces per lane; the router row takes 2 NP float4
 template <int NP>
 __global__ __launch_bounds__(256) void k_latent_front(FrontParams p)
 {
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
     const int nb = p.H / 8;
+    // (shared pairs and down rows: the token staged in LDS once per block
+    // and read per 16-byte piece next to its use, so that only the weight
+    // rows stay in registers; the blocks' branches are uniform, and a wave
+    // past the last row still meets every barrier)
+    __shared__ __attribute__((aligned(16))) uint16_t s_x[kFrontMaxH];
+    auto stage_x = [&](int t) __attribute__((always_inline)) {
+        __syncthreads();  // (every wave is done with the previous token)
+        const uint4 *src = reinterpret_cast<const uint4 *>(p.x + (size_t)t * p.H);
+        for (int c = threadIdx.x; c < nb; c += 256) reinterpret_cast<uint4 *>(s_x)[c] = src[c];
+        __syncthreads();
+    };
     int b = blockIdx.x;
     if (b < p.n_sh) {
         // one (gate, up) row pair of a shared expert per wave
         const int pair = b * 4 + wave;
-        if (pair >= p.S * p.F) return;
-        const int sidx = pair / p.F, f = pair % p.F;
+        const bool has = pair < p.S * p.F;
+        const int pr = has ? pair : 0;
+        const int sidx = pr / p.F, f = pr % p.F;
         uint4 wg[NP], wu[NP];
-        load_row<NP>(wg, p.sh1 + ((size_t)sidx * p.F + f) * p.H, nb);
-        load_row<NP>(wu, p.sh3 + ((size_t)sidx * p.F + f) * p.H, nb);
+        load_row<NP>(wg, p.sh1 + ((size_t)sidx * p.F + f) * p.H, has ? nb : 0);
+        load_row<NP>(wu, p.sh3 + ((size_t)sidx * p.F + f) * p.H, has ? nb : 0);
         for (int t = 0; t < p.T; t++) {
-            const uint16_t *xr = p.x + (size_t)t * p.H;
+            stage_x(t);
             float ga = 0.0f, ua = 0.0f;
 #pragma unroll
             for (int i = 0; i < NP; i++) {
                 const int c = lane + 64 * i;
                 if (c < nb) {
-                    const uint4 v = ld16(xr + (size_t)c * 8);
+                    const uint4 v = *reinterpret_cast<const uint4 *>(s_x + (size_t)c * 8);
                     const uint32_t xp[4] = {v.x, v.y, v.z, v.w};
                     ga = bf16x8_dot_bf16(wg[i], xp, ga);
                     ua = bf16x8_dot_bf16(wu[i], xp, ua);
@@ -90,7 +104,7 @@ __global__ __launch_bounds__(256) void k_latent_front(FrontParams p)
             }
             ga = group_sum<64>(ga);
             ua = group_sum<64>(ua);
-            if (lane == 0) p.Hs[(size_t)t * p.S * p.F + pair] = gated_act(ga, ua, p.act, p.b1, p.b2);
+            if (has && lane == 0) p.Hs[(size_t)t * p.S * p.F + pair] = gated_act(ga, ua, p.act, p.b1, p.b2);
         }
         return;
     }
@@ -98,29 +112,61 @@ __global__ __launch_bounds__(256) void k_latent_front(FrontParams p)
     if (b < p.n_dn) {
         // one down-projection row per wave: z[t][r] = W_down[r] . x[t]
         const int r = b * 4 + wave;
-        if (r >= p.L) return;
+        const bool has = r < p.L;
         uint4 w[NP];
-        load_row<NP>(w, p.down + (size_t)r * p.H, nb);
+        load_row<NP>(w, p.down + (size_t)(has ? r : 0) * p.H, has ? nb : 0);
         for (int t = 0; t < p.T; t++) {
-            const uint16_t *xr = p.x + (size_t)t * p.H;
+            stage_x(t);
             float a = 0.0f;
 #pragma unroll
             for (int i = 0; i < NP; i++) {
                 const int c = lane + 64 * i;
                 if (c < nb) {
-                    const uint4 v = ld16(xr + (size_t)c * 8);
+                    const uint4 v = *reinterpret_cast<const uint4 *>(s_x + (size_t)c * 8);
                     const uint32_t xp[4] = {v.x, v.y, v.z, v.w};
                     a = bf16x8_dot_bf16(w[i], xp, a);
                 }
             }
             a = group_sum<64>(a);
-            if (lane == 0) p.zf[(size_t)t * p.L + r] = a;
+            if (has && lane == 0) p.zf[(size_t)t * p.L + r] = a;
         }
         return;
     }
     b -= p.n_dn;
+    // one router row per wave (fp32, H wide), in two halves of NP float4
+    // pieces per lane, each held across the tokens; a token's logit is the
+    // first half's sum (stored) plus the second half's, in that order
     const int e = b * 4 + wave;
-    if (e < p.E) router_row<2 * NP>(p.T, p.E, p.H, p.x, p.Wr, p.logits, e);
+    const bool has = e < p.E;
+    const int nc = p.H / 4, half = (nc + 1) / 2;  // float4 pieces of the row, of a half
+    const float4 *row = reinterpret_cast<const float4 *>(p.Wr + (size_t)(has ? e : 0) * p.H);
+    for (int h = 0; h < 2; h++) {
+        const int c0 = h * half, c1 = h ? nc : half;
+        float4 w[NP];
+#pragma unroll
+        for (int i = 0; i < NP; i++) {
+            const int c = c0 + lane + 64 * i;
+            w[i] = has && c < c1 ? row[c] : make_float4(0.f, 0.f, 0.f, 0.f);
+        }
+        for (int t = 0; t < p.T; t++) {
+            stage_x(t);
+            float a = 0.0f;
+#pragma unroll
+            for (int i = 0; i < NP; i++) {
+                const int c = c0 + lane + 64 * i;
+                if (c < c1) {
+                    const uint2 xv = *reinterpret_cast<const uint2 *>(s_x + (size_t)c * 4);
+                    a = fmaf(w[i].x, bf16_lo(xv.x), a);
+                    a = fmaf(w[i].y, bf16_hi(xv.x), a);
+                    a = fmaf(w[i].z, bf16_lo(xv.y), a);
+                    a = fmaf(w[i].w, bf16_hi(xv.y), a);
+                }
+            }
+            a = wave_sum(a);
+            float *dst = p.logits + (size_t)t * p.E + e;
+            if (has && lane == 0) *dst = h ? *dst + a : a;
+        }
+    }
 }
 
 constexpr int kSlotChunk = 16;  // slot rows loaded together
