@@ -278,6 +278,48 @@ struct OutParams {
     uint16_t *out_bf16;
 };
 
+constexpr int kStagePieces = 8;  // float4 pieces per thread loaded together while staging
+
+// stage token t's inputs [n (L values); shared activations (S*F values)] at
+// dst: each thread's pieces of a batch are all loaded before any is stored,
+// so one round trip to memory covers them (n = aggregate * inv * norm_w, the
+// products taken in the scalar staging's order)
+__device__ __forceinline__ void stage_token_vec(const OutParams &p, int t, float inv, float *dst)
+{
+    const int L4 = p.L >> 2, W4 = L4 + ((p.S * p.F) >> 2);
+    const float4 *a4 = reinterpret_cast<const float4 *>(p.accL + (size_t)t * p.L);
+    const float4 *h4 = reinterpret_cast<const float4 *>(p.Hs + (size_t)t * p.S * p.F);
+    const float4 *g4 = reinterpret_cast<const float4 *>(p.nw);
+    float4 *d4 = reinterpret_cast<float4 *>(dst);
+    for (int b = 0; b < W4; b += 256 * kStagePieces) {
+        float4 v[kStagePieces], g[kStagePieces];
+#pragma unroll
+        for (int k = 0; k < kStagePieces; k++) {
+            const int j = b + k * 256 + (int)threadIdx.x;
+            g[k] = make_float4(1.0f, 1.0f, 1.0f, 1.0f);
+            v[k] = make_float4(0.0f, 0.0f, 0.0f, 0.0f);
+            if (j < L4) {
+                v[k] = a4[j];
+                if (p.do_norm && g4) g[k] = g4[j];
+            } else if (j < W4) {
+                v[k] = h4[j - L4];
+            }
+        }
+#pragma unroll
+        for (int k = 0; k < kStagePieces; k++) {
+            const int j = b + k * 256 + (int)threadIdx.x;
+            float4 o = v[k];
+            if (j < L4 && p.do_norm) {
+                o.x = o.x * inv * g[k].x;
+                o.y = o.y * inv * g[k].y;
+                o.z = o.z * inv * g[k].z;
+                o.w = o.w * inv * g[k].w;
+            }
+            if (j < W4) d4[j] = o;
+        }
+    }
+}
+
 // the wave's rows r0, r0 + 1 of one segment (weights wrow0 / wrow1, K wide)
 // dotted with the staged inputs xs + xoff of nt tokens (token stride W)
 __device__ __forceinline__ void seg_dot(const uint16_t *wrow0, const uint16_t *wrow1, bool two, int K,
@@ -315,6 +357,7 @@ __device__ __forceinline__ void seg_dot(const uint16_t *wrow0, const uint16_t *w
 // up to ntok tokens' inputs (n computed from the aggregate on the way, then
 // the shared activations) in LDS; each wave then streams two output rows'
 // weights once per staged group and dots them with every staged token
+template <bool VEC>
 __global__ __launch_bounds__(256) void k_latent_out(OutParams p)
 {
     extern __shared__ float4 lds4[];
@@ -329,6 +372,10 @@ __global__ __launch_bounds__(256) void k_latent_out(OutParams p)
             const int t = t0 + tt;
             const float inv = p.do_norm ? rms_inv(p.ssp + (size_t)t * p.nch, p.nch, p.L, p.eps) : 1.0f;
             float *dst = xs + tt * W;
+            if constexpr (VEC) {
+                stage_token_vec(p, t, inv, dst);
+                continue;
+            }
             for (int i = threadIdx.x; i < p.L; i += 256) {
                 const float a = p.accL[(size_t)t * p.L + i];
                 dst[i] = p.do_norm ? a * inv * (p.nw ? p.nw[i] : 1.0f) : a;
@@ -430,11 +477,19 @@ hipError_t launch_latent_out(const Shape &so, int L, int do_norm, float eps, con
     p.accL = b.accL; p.ssp = b.ssp; p.nw = norm_w; p.Hs = w.Hs;
     p.up = up; p.sh2 = wt.sh2;
     p.out_f32 = out_f32; p.out_bf16 = out_bf16;
+    auto a16 = [](const void *q) { return ((uintptr_t)q & 15) == 0; };
+    const bool vec = L % 4 == 0 && (so.S * so.F) % 4 == 0 && a16(b.accL) && a16(w.Hs) && a16(norm_w);
     const size_t tb = out_token_bytes(L, so.S, so.F);
     p.ntok = (int)std::min<size_t>(std::max<size_t>((size_t)(48 << 10) / tb, 1), kOutMaxTok);
     p.ntok = std::min(p.ntok, std::max(so.T, 1));
     const int nblk = (so.d + kOutRows - 1) / kOutRows;
-    if (so.T > 0) k_latent_out<<<nblk, 256, p.ntok * tb, st>>>(p);
+    if (so.T > 0) {
+        // float4 staging when the inputs and sizes allow it
+        if (vec)
+            k_latent_out<true><<<nblk, 256, p.ntok * tb, st>>>(p);
+        else
+            k_latent_out<false><<<nblk, 256, p.ntok * tb, st>>>(p);
+    }
     return hipGetLastError();
 }
 
