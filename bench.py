@@ -81,6 +81,12 @@ LATENT_KERNELS = {
              "topk_dispatch_z": "k_dispatch_small/k_topk+k_dispatch_* + k_quant_z",
              "expert_gate_up": "k_gemv_gateup (fp16 latent rows)", "expert_down": "k_gemv_down",
              "norm_up_shared_out": "k_latent_accum + k_latent_out (norm, up projection, shared down)"},
+    "decode1": {"front": "k_latent_front (router + down projection + shared gate/up, full width)",
+                "topk_dispatch_z": "k_dispatch_small (top-k, dispatch, z as fp16 with a scale)",
+                "expert_gate_up": "k_dec1_fused (fp16 z row: routed gate/up, down, weighted sum into the aggregate)",
+                "expert_down": "- (in k_dec1_fused)",
+                "norm_up_shared_out": "k_latent_accum (sums of squares) + k_latent_out (norm, up projection, "
+                                      "shared down)"},
     "mfma": {"front": "k_split_router + k_ggemm<M_R> (router) + k_ggemm<M_R> (down projection)",
              "topk_dispatch_z": "k_topk + k_dispatch_* + k_quant_z",
              "expert_gate_up": "k_ggemm_pair<M_S13, M_G13H> (shared gate/up at the head below 512 shared blocks; "
@@ -227,13 +233,16 @@ def latent_phase_bytes(ls, T, counts, kind):
     """Algorithmic HBM bytes of each latent-layer phase for one step.  The
     GEMV path runs the shared experts' gate/up in its front kernel and their
     down in its output kernel; the MFMA path runs them with the routed
-    gate/up and down."""
+    gate/up and down.  At one token (decode1) the routed gate/up and down
+    are one kernel, all of whose bytes count in the gate/up phase."""
     H, L, F, S, E = ls.hidden, ls.latent, ls.d_ffn, ls.n_shared, ls.n_experts
     active = int((counts > 0).sum())
     w13 = 2 * (F * L // 2 + F * L // 32)
     w2 = L * F // 2 + L * F // 32
     sh13, sh2 = S * 2 * F * H * 2, S * H * F * 2
     m = kind == "mfma"
+    if kind == "decode1":
+        w13, w2 = w13 + w2, 0
     return {"front": E * H * 4 + L * H * 2 + (0 if m else sh13) + T * H * 2, "topk_dispatch_z": 0,
             "expert_gate_up": active * w13 + (sh13 if m else 0), "expert_down": active * w2 + (sh2 if m else 0),
             "norm_up_shared_out": H * L * 2 + L * 4 + (0 if m else sh2) + T * H * 2}
@@ -243,9 +252,10 @@ def latent_phase_flops(ls, T, kind):
     H, L, F, S, E, k = ls.hidden, ls.latent, ls.d_ffn, ls.n_shared, ls.n_experts, ls.top_k
     sh13, sh2 = 2 * T * 2 * S * F * H, 2 * T * S * H * F
     m = kind == "mfma"
+    one = kind == "decode1"
     return {"front": 2 * T * (E * H + L * H) + (0 if m else sh13), "topk_dispatch_z": 0,
-            "expert_gate_up": 4 * T * k * L * F + (sh13 if m else 0),
-            "expert_down": 2 * T * k * L * F + (sh2 if m else 0),
+            "expert_gate_up": (6 if one else 4) * T * k * L * F + (sh13 if m else 0),
+            "expert_down": (0 if one else 2 * T * k * L * F) + (sh2 if m else 0),
             "norm_up_shared_out": 2 * T * H * L + (0 if m else sh2)}
 
 
@@ -313,6 +323,11 @@ def measure_latent(lidx, steps, warmup, pool, use_graph, cpu_seconds, hbm_copy_g
         counts.append(cnt.cpu().numpy().copy())
     load_s = time.perf_counter() - t_load
     kind = {1: "gemv", 2: "mfma"}[moe.latent_path_for(desc, T)]
+    # (one token on the GEMV path: the routed experts run in the one-token
+    # kernel when the latent width is a multiple of 512 and the activation
+    # SiTU, as in this workload)
+    if kind == "gemv" and T == 1 and ls.latent % 512 == 0:
+        kind = "decode1"
 
     def step(i):
         moe.latent_layer(desc, xs[i % npool], T, out, None, moe.OUT_BF16, ws)
@@ -365,7 +380,8 @@ def measure_latent(lidx, steps, warmup, pool, use_graph, cpu_seconds, hbm_copy_g
         achieved = ph_bytes[dom] / (ph_ms[dom] * 1e-3) / 1e9
         roofline = {"bound": "hbm", "achieved": round(achieved, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
                     "frac": round(achieved / PEAK_HBM_GBS, 4),
-                    "traffic": measured_traffic(LATENT_KERNELS[kind][dom].split()[0]) if T == 1 else None,
+                    "traffic": measured_traffic(("latent:" if kind == "decode1" else "")
+                                                + LATENT_KERNELS[kind][dom].split()[0]) if T == 1 else None,
                     "kernel": LATENT_KERNELS[kind][dom], "bytes_per_launch": int(ph_bytes[dom]),
                     "avg_launch_us": round(ph_ms[dom] * 1e3, 2),
                     "frac_of_copy": round(achieved / hbm_copy_gbs, 4)}
@@ -391,7 +407,7 @@ def measure_latent(lidx, steps, warmup, pool, use_graph, cpu_seconds, hbm_copy_g
         "step_mfma_frac": round(step_flops / (med * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 4),
         "step_bytes": int(step_bytes), "step_flops": int(step_flops),
         "distinct_experts": round(float(np.mean([(c > 0).sum() for c in counts])), 1),
-        "phase_us": {p: round(v * 1e3, 2) for p, v in ph_ms.items()},
+        "phase_us": {p: (round(v * 1e3, 2) if LATENT_KERNELS[kind][p][0] != "-" else None) for p, v in ph_ms.items()},
         "roofline": roofline,
         "load_s": round(load_s, 1),
     }

@@ -487,9 +487,10 @@ inline int latent_chunks(int L) { return (L + kLatentChunk - 1) / kLatentChunk; 
 hipError_t launch_latent_front(const Shape &so, int L, const uint16_t *x, const Weights &wt,
                                const uint16_t *down, const Work &w, const LatentBufs &b,
                                hipStream_t st);
-// aggregate of each token's slot rows (ascending expert id) + partial sums of squares
+// aggregate of each token's slot rows (ascending expert id) + partial sums of
+// squares; given: the aggregate is already in b.accL, the sums of squares only
 hipError_t launch_latent_accum(int T, int k, int L, const Work &w, const LatentBufs &b,
-                               hipStream_t st);
+                               hipStream_t st, bool given = false);
 // MFMA path: n = RMSNorm(aggregate) * norm_w (or the aggregate) as bf16 hi / lo
 hipError_t launch_latent_split(int T, int L, int do_norm, float eps, const float *norm_w,
                                const LatentBufs &b, hipStream_t st);
@@ -513,10 +514,14 @@ void set_router_wait_us(uint32_t us);
 // fused one-token decode after launch_front: top-k (do_topk) or the given
 // ids / weights, routed gate/up (+ shared down), routed down + combine into
 // out_bf16 / out_f32.  ev2 (optional): events after each of the two launches.
+// zsc (optional): x holds fp16 values times the scale *zsc (the latent
+// layer's z row): the one-launch form on the given picks without shared
+// experts, when decode1_latent_supported (else hipErrorInvalidValue).
 bool decode1_supported(const Shape &s);
+bool decode1_latent_supported(const Shape &s);
 hipError_t launch_decode1(const Shape &s, const uint16_t *x, const Weights &wt, const float *bias,
                           int do_topk, int32_t *ids, float *wts, int32_t *counts_out, int shared,
                           const Work &w, uint16_t *out_bf16, float *out_f32, hipStream_t stream,
-                          hipEvent_t const *ev2);
+                          hipEvent_t const *ev2, const float *zsc = nullptr);
 
 }  // namespace moe

@@ -45,7 +45,8 @@ namespace moe {
 
 struct Dec1Params {
     Shape s;
-    const uint16_t *x;     // [d] bf16 token
+    const uint16_t *x;     // [d] bf16 token (zsc null) or fp16 values (zsc set)
+    const float *zsc;      // null, or the scale of the fp16 token (the latent layer's z row: z = x * zsc)
     const float *Wr;       // router weights [E][d] fp32
     const float *bias;     // router selection bias [E] or null
     const uint8_t *w1q, *w1s, *w3q, *w3s, *w2q, *w2s;
@@ -389,7 +390,10 @@ __device__ void dec1_down_fused(const Dec1Params &p, uint32_t ep, uint8_t *s_h, 
 // then every wave takes routed gate/up units from the block's queue.
 // SHC: 16-byte chunks per lane of a shared gate/up row (ceil(d / 512)).
 // SA: a row's scale bytes are 16-byte aligned (d % 512 == 0).
-template <int SHC, bool SA, bool FUSED, int SHD>
+// XH: the token is fp16 values times the scale *zsc (the routed gate/up
+// sums are taken on the fp16 values, then scaled; no router, no shared
+// experts)
+template <int SHC, bool SA, bool FUSED, int SHD, bool XH = false>
 __device__ __forceinline__ void dec1_gu(const Dec1Params &p)
 {
     __shared__ uint64_t s_cand[kTkWaves * kMaxTopK];
@@ -419,6 +423,8 @@ __device__ __forceinline__ void dec1_gu(const Dec1Params &p)
     const int d = s.d, F = s.F, E = s.E, k = s.k;
     const int S = p.shared ? s.S : 0;
     int *ctl = p.w.ctl;
+    // (the fp16 token's scale; 1 for a bf16 token: the products are exact)
+    const float xsc = XH ? *p.zsc : 1.0f;
     // this call's epoch (the previous call's down kernel wrote the one before)
     const uint32_t ep = (uint32_t)__hip_atomic_load(ctl + kCtlEpoch, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) + 1u;
 
@@ -761,7 +767,10 @@ __device__ __forceinline__ void dec1_gu(const Dec1Params &p)
             for (int m = 0; m < 2; m++) {
                 const uint32_t sb = g.scale(m, w, grp);
                 const float sc = (okb && sb != 255u) ? e8m0_to_f32(sb) : 0.0f;
-                acc[m] = fmaf(fp4x32_dot_bf16(g.c[m][w], xw), sc, acc[m]);
+                if constexpr (XH)
+                    acc[m] = fmaf(fp4x32_dot_f16(g.c[m][w], xw), sc, acc[m]);
+                else
+                    acc[m] = fmaf(fp4x32_dot_bf16(g.c[m][w], xw), sc, acc[m]);
             }
         }
         // the four lanes of a row
@@ -845,7 +854,7 @@ __device__ __forceinline__ void dec1_gu(const Dec1Params &p)
             up += s_part[v][st][kGuFeat + f];
         }
         if (s_eid[u / upr] >= 0) {
-            const _Float16 hv = (_Float16)gated_act(g, up, s.act, s.b1, s.b2);
+            const _Float16 hv = (_Float16)gated_act(g * xsc, up * xsc, s.act, s.b1, s.b2);
             if constexpr (FUSED) st_through(&H[(size_t)u * kGuFeat + f], hv);
             else H[(size_t)u * kGuFeat + f] = hv;
         }
@@ -902,7 +911,8 @@ __device__ __forceinline__ void dec1_gu(const Dec1Params &p)
                     up += a.y;
                 }
                 if (grp == 0 && s_eid[u / upr] >= 0)
-                    st_through(&H[(size_t)u * kGuFeat + mrow], (_Float16)gated_act(g, up, s.act, s.b1, s.b2));
+                    st_through(&H[(size_t)u * kGuFeat + mrow],
+                               (_Float16)gated_act(g * xsc, up * xsc, s.act, s.b1, s.b2));
             }
         };
         dec1_down_fused<SHD>(p, ep, reinterpret_cast<uint8_t *>(s_dyn), s_eid, s_wt, s_ctl[8] == 1, redo_shared,
@@ -916,10 +926,10 @@ __global__ __launch_bounds__(kGuWaves * 64) void k_dec1_gateup(Dec1Params p)
 {
     dec1_gu<SHC, SA, false, 2>(p);
 }
-template <int SHC, bool SA, int SHD>
+template <int SHC, bool SA, int SHD, bool XH = false>
 __global__ __launch_bounds__(kGuWaves * 64) void k_dec1_fused(Dec1Params p)
 {
-    dec1_gu<SHC, SA, true, SHD>(p);
+    dec1_gu<SHC, SA, true, SHD, XH>(p);
 }
 
 // ------------------------------------------------------------ routed down + combine
@@ -1418,14 +1428,33 @@ static int cu_count()
     return n;
 }
 
+// blocks of the one-launch form (one per CU, more when the gate/up units or
+// the output rows need them); the form runs when they fit the device's CUs
+static int fused_blocks(const Shape &s, bool shared)
+{
+    const int units = s.k * (s.F / kGuFeat);
+    const int sh_units = shared ? s.S * s.F : 0;
+    const int nblk = max(cu_count(), max((units + kGuMaxBlockUnits - 1) / kGuMaxBlockUnits,
+                                         (sh_units + kShMaxBlockUnits - 1) / kShMaxBlockUnits));
+    return max(nblk, (s.d + kDnBlockRows - 1) / kDnBlockRows);
+}
+
+bool decode1_latent_supported(const Shape &s)
+{
+    return decode1_supported(s) && s.d % 512 == 0 && fused_blocks(s, false) <= min(cu_count(), kFusedMaxBlocks);
+}
+
 hipError_t launch_decode1(const Shape &s, const uint16_t *x, const Weights &wt, const float *bias,
                           int do_topk, int32_t *ids, float *wts, int32_t *counts_out, int shared,
                           const Work &w, uint16_t *out_bf16, float *out_f32, hipStream_t stream,
-                          hipEvent_t const *ev2)
+                          hipEvent_t const *ev2, const float *zsc)
 {
+    // an fp16 token (zsc): the one-launch form on given picks, no shared experts
+    if (zsc && (do_topk || shared || !decode1_latent_supported(s))) return hipErrorInvalidValue;
     Dec1Params p;
     p.s = s;
     p.x = x;
+    p.zsc = zsc;
     p.bias = bias;
     p.w1q = wt.w1q; p.w1s = wt.w1s; p.w3q = wt.w3q; p.w3s = wt.w3s; p.w2q = wt.w2q; p.w2s = wt.w2s;
     p.Wr = wt.router_w;
@@ -1465,6 +1494,28 @@ hipError_t launch_decode1(const Shape &s, const uint16_t *x, const Weights &wt, 
     const int nblk_f = max(nblk, (s.d + kDnBlockRows - 1) / kDnBlockRows);
     if (nblk_f <= min(cu_count(), kFusedMaxBlocks)) {
         const size_t lds_f = max(lds, (size_t)kGuDynLds);
+        if (zsc) {
+#define MOE_DEC1_X(C, D) k_dec1_fused<C, true, D, true><<<nblk_f, kGuWaves * 64, lds_f, stream>>>(p)
+#define MOE_DEC1_XD(C)                        \
+    do {                                      \
+        if (shd <= 2) MOE_DEC1_X(C, 2);       \
+        else if (shd <= 4) MOE_DEC1_X(C, 4);  \
+        else if (shd <= 6) MOE_DEC1_X(C, 6);  \
+        else MOE_DEC1_X(C, 8);                \
+    } while (0)
+            if (shc <= 2) MOE_DEC1_XD(2);
+            else if (shc <= 4) MOE_DEC1_XD(4);
+            else if (shc <= 6) MOE_DEC1_XD(6);
+            else if (shc <= 7) MOE_DEC1_XD(7);
+            else MOE_DEC1_XD(8);
+#undef MOE_DEC1_XD
+#undef MOE_DEC1_X
+            if (ev2) {
+                (void)hipEventRecord(ev2[0], stream);
+                (void)hipEventRecord(ev2[1], stream);
+            }
+            return hipGetLastError();
+        }
 #define MOE_DEC1_F(C, D)                                                                                 \
     do {                                                                                                 \
         if (sa) k_dec1_fused<C, true, D><<<nblk_f, kGuWaves * 64, lds_f, stream>>>(p);                  \

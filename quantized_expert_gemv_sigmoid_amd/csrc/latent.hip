@@ -173,7 +173,9 @@ constexpr int kSlotChunk = 16;  // slot rows loaded together
 
 // block (t, chunk): aggregate[t][4 c .. 4 c + 3] = sum of the token's slot
 // rows in ascending expert id (positions tok_pos, -1 = none), and the
-// chunk's sum of squares in double (fixed order: lane butterfly, then waves)
+// chunk's sum of squares in double (fixed order: lane butterfly, then waves).
+// tok_pos null: the aggregate is given in accL (the one-token kernel wrote
+// it); only the sums of squares are taken.
 __global__ __launch_bounds__(256) void k_latent_accum(int T, int k, int L, int nch,
                                                       const int32_t *__restrict__ tok_pos,
                                                       const float *__restrict__ Y,
@@ -186,7 +188,10 @@ __global__ __launch_bounds__(256) void k_latent_accum(int T, int k, int L, int n
     const int c = ch * 256 + threadIdx.x;
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
     double ss = 0.0;
-    if (c < L4) {
+    if (c < L4 && !tok_pos) {
+        const float4 acc = reinterpret_cast<const float4 *>(accL + (size_t)t * L)[c];
+        ss = ((double)acc.x * acc.x + (double)acc.y * acc.y) + ((double)acc.z * acc.z + (double)acc.w * acc.w);
+    } else if (c < L4) {
         float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
         const int32_t *tp = tok_pos + (size_t)t * k;
         for (int r0 = 0; r0 < k; r0 += kSlotChunk) {
@@ -449,10 +454,11 @@ hipError_t launch_latent_front(const Shape &so, int L, const uint16_t *x, const 
 }
 
 hipError_t launch_latent_accum(int T, int k, int L, const Work &w, const LatentBufs &b,
-                               hipStream_t st)
+                               hipStream_t st, bool given)
 {
     const int nch = latent_chunks(L);
-    if (T > 0) k_latent_accum<<<T * nch, 256, 0, st>>>(T, k, L, nch, w.tok_pos, w.Y, b.accL, b.ssp);
+    if (T > 0)
+        k_latent_accum<<<T * nch, 256, 0, st>>>(T, k, L, nch, given ? nullptr : w.tok_pos, w.Y, b.accL, b.ssp);
     return hipGetLastError();
 }
 

@@ -335,6 +335,7 @@ size_t carve_latent(const moe_latent_desc *d, int32_t T, char *base, Work *w, mo
     const size_t S = (size_t)so.S, H = (size_t)so.d, L = (size_t)si.d;
     const size_t nblk = (Tz + moe::kDispatchTokens - 1) / moe::kDispatchTokens;
     Work v = {};
+    v.ctl = (int32_t *)take(moe::kWsControlBytes);  // the one-token kernel's control block, at offset 0
     v.logits = (float *)take(Tz * E * 4);
     v.ids = (int32_t *)take(Tz * k * 4);
     v.wts = (float *)take(Tz * k * 4);
@@ -416,14 +417,20 @@ moe_status run_latent(const moe_latent_desc *d, int32_t T, const uint16_t *x, in
     const moe::ZQuant zq{b.zf, b.zh, b.zsc, L};
     MOE_TRY(moe::launch_dispatch(si, 1, w.logits, d->router_bias, ids, wts, counts_out, w, st, zq));
     MOE_TRY(mark(ev, 2, st));
-    if (path == MOE_PATH_GEMV) {
+    // one token: the routed experts in the one-token kernel (gate/up on the
+    // fp16 z row, down, the weighted sum straight into the aggregate)
+    const bool one = path == MOE_PATH_GEMV && T == 1 && moe::decode1_latent_supported(si);
+    if (one) {
+        MOE_TRY(moe::launch_decode1(si, b.zh, wt, nullptr, 0, ids, wts, nullptr, 0, w, nullptr, b.accL, st,
+                                    ev ? ev + 3 : nullptr, b.zsc));
+    } else if (path == MOE_PATH_GEMV) {
         MOE_TRY(moe::launch_gemv_experts(si, nullptr, wt, 0, w, st, ev ? ev + 3 : nullptr, b.zh, b.zsc));
     } else {
         // (the shared experts' gate/up and down with the routed launches)
         MOE_TRY(moe::launch_mfma_latent_experts(si, wt, b.zh, b.zsc, so, x, b.ysh + (size_t)T * so.d, w, st,
                                                 ev ? ev + 3 : nullptr));
     }
-    MOE_TRY(moe::launch_latent_accum(T, so.k, L, w, b, st));
+    MOE_TRY(moe::launch_latent_accum(T, so.k, L, w, b, st, one));
     if (path == MOE_PATH_GEMV) {
         MOE_TRY(moe::launch_latent_out(so, L, d->latent_norm, d->rms_eps, d->norm_w, d->up, wt, w, b,
                                        ob, of, st));

@@ -121,6 +121,31 @@ def test_latent_mfma_up_projection_past_fp16():
     assert np.isfinite(out_f).all() and np.abs(out_f).max() > 65504.0
 
 
+def test_latent_out_unaligned_norm_weight():
+    # The output kernel stages each token's inputs as 16-byte pieces when the
+    # aggregate, the shared activations and the norm weight are 16-byte
+    # aligned, one value at a time otherwise.  A norm weight one element past
+    # an aligned address takes the second staging; the outputs must equal the
+    # aligned call's bit for bit (same products in the same order) and the
+    # oracle's within the tolerance.  T = 5 spans a staged group of four
+    # tokens and a ragged group of one.
+    T = 5
+    log(f"case: latent GEMV path, norm weight at a 4-byte offset, T={T}")
+    gl = make_gpu_latent(MID, 77, path=1)
+    x, out_f, out_b, ids, _, _ = _check(gl, T)
+    nw = gl.tensors["norm_w"]
+    buf = torch.empty(nw.numel() + 1, dtype=torch.float32, device="cuda")
+    buf[1:].copy_(nw)
+    moved = buf[1:]
+    assert moved.data_ptr() % 16 != 0
+    gl.desc.norm_w = moved.data_ptr()
+    out_f2, out_b2, ids2, _, _ = run_latent(gl, x)
+    gl.desc.norm_w = nw.data_ptr()
+    assert np.array_equal(ids, ids2)
+    assert np.array_equal(out_f, out_f2), "scalar staging differs from the 16-byte staging"
+    assert np.array_equal(out_b, out_b2)
+
+
 def test_latent_timed_equals_layer_and_zero_tokens():
     import quantized_expert_gemv_sigmoid_amd as moe
     import synth.device as sdev
