@@ -133,11 +133,12 @@ def time_windows(torch, step, graphs, npool, K, stream, plain):
 # The summaries and the commands are in profiles/moe_layer_kernels__k3-moe-decode-T1.md
 # and profiles/latent_kernels__k3-latent-moe-decode-T1.md.
 MEASURED_TRAFFIC = {
-    "k_dec1_fused": {"bytes": 428563011, "source": "decode1.hip", "sha": "85c974d86f77a426"},
-    "k_latent_front": {"bytes": 253999154, "source": "latent.hip", "sha": "bae8c0c78d423e41"},
-    "k_latent_out": {"bytes": 140118150, "source": "latent.hip", "sha": "bae8c0c78d423e41"},
-    "k_gemv_gateup": {"bytes": 187593892, "source": "gemv.hip", "sha": "f5aeda5727b5bb2d"},
-    "k_gemv_down": {"bytes": 95553960, "source": "gemv.hip", "sha": "f5aeda5727b5bb2d"},
+    "k_dec1_fused": {"bytes": 428568305, "source": "decode1.hip", "sha": "7c186e0d8586a0dd"},
+    "latent:k_dec1_fused": {"bytes": 282689003, "source": "decode1.hip", "sha": "7c186e0d8586a0dd"},
+    "k_latent_front": {"bytes": 253715405, "source": "latent.hip", "sha": "6229395c2b06c561"},
+    "k_latent_out": {"bytes": 140151932, "source": "latent.hip", "sha": "6229395c2b06c561"},
+    "k_gemv_gateup": {"bytes": 187593892, "source": "gemv.hip", "sha": "41cf35ee3e010d30"},
+    "k_gemv_down": {"bytes": 95553960, "source": "gemv.hip", "sha": "41cf35ee3e010d30"},
 }
 
 
