@@ -231,7 +231,10 @@ moe_status moe_set_one_token_router_wait(int32_t microseconds);
  * reaches W_up in fp32 (GEMV) or in fp16 (MFMA, W_up taken as fp16; a pass
  * whose sums come out non-finite, an element past fp16's range, is computed
  * again on two bf16 parts, 16 bits); every product accumulates in fp32, sums
- * of squares in double.
+ * of squares in double.  The experts' H is as for moe_layer: fp32 on the GEMV
+ * path; fp16 on the MFMA path and at one token on the GEMV path, whose
+ * routed experts then run in the one-token kernel (L a multiple of 512,
+ * SiTU with b1*b2 <= 65504).
  *
  * The expert tensors are those of moe_layer_desc with d = latent (W1, W3
  * [E][F][L/2] + [E][F][L/32]; W2 [E][L][F/2] + [E][L][F/32]); router and
